@@ -1,0 +1,156 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention operator.
+ *
+ * Pages cited (by title and section):
+ *   [XT] xutianle.me, "Kimi Linear：用 KDA 重写长上下文注意力"
+ *   [XD] xiudou.site, "Kimi Delta Attention：把遗忘门做到每个通道"
+ *   [DS] docsaid.org, "Kimi Linear" (逐通道的遺忘)
+ *   [RM] remio.ai, "Kimi Linear 以自己的方式击败了全注意力"
+ *
+ * The operator, per (sequence, head), token t = 1..L:
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_(t-1) + beta_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ * with S a d_k x d_v matrix whose ROWS are key channels, alpha_t = exp(g_t) a
+ * per-channel gate in (0,1] held in log space (g <= 0), beta_t a scalar per
+ * token and head, and q, k L2-normalised per head when qk_l2norm is set
+ * (q / sqrt(sum q^2 + 1e-6)).  [XT §3 boxed KDA update and its decay-then-
+ * correct split; XT §1 read-out o_t = S_t^T q_t; XT §6.2 L2 normalisation;
+ * DS §"KDA：把衰減拆到每個通道" state orientation and its two-channel table]
+ *
+ * Conventions common to every entry point:
+ *  - Tensor pointers are DEVICE pointers to dense row-major arrays (last
+ *    index fastest), 16-byte aligned.  The caller owns every buffer; the
+ *    library keeps no pointer after a call returns and never allocates device
+ *    memory (scratch comes in through `workspace`).
+ *  - Calls are asynchronous on `stream`; outputs are valid once the stream
+ *    has reached the point of the call.  Host-side validation never
+ *    synchronises the device; on any error nothing is launched, the status is
+ *    returned and kda_last_error() holds a message.  Launch failures return
+ *    KDA_ERR_HIP with the HIP error string.
+ *  - Results are bitwise deterministic for fixed inputs and descriptor.
+ *  - NaN or Inf in inputs propagate to outputs; no kernel waits on data, so
+ *    none can hang on them.
+ *  - g > 0 (alpha > 1) is outside the operator's domain; it is not checked on
+ *    the device and its results are unspecified (no fault, no hang).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad shape or value */
+  KDA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. dk = 96)   */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+  KDA_ERR_HIP = 4                 /* a HIP runtime call or launch failed         */
+} kda_status_t;
+
+/* Element type of q, k, v and o.  g, beta and every state are always fp32. */
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+/* Problem descriptor (plain old data, passed by pointer).
+ *   batch      B.  Dense layout: inputs are [B, T, H, d].  Must be 1 when
+ *              cu_seqlens is given (varlen packing).
+ *   seqlen     T: tokens per sequence (dense) or total packed tokens (varlen).
+ *              T = 0 is legal (nothing to compute; final = init).
+ *   num_seqs   N: = B (dense) or len(cu_seqlens) - 1 (varlen).  For decode,
+ *              the number of independent sequences.
+ *   heads      H >= 1.
+ *   dk, dv     key / value head dims; supported: dk = dv, 64 or 128.
+ *   dtype      element type of q, k, v, o.
+ *   chunk      must be 64 (the chunk size the pages' FLOP model uses,
+ *              [XT §5]).
+ *   qk_l2norm  1: normalise q and k inside the operator; 0: use as given.
+ *   scale      o = scale * S^T q (the pages use no query scale: 1.0).
+ *   ckpt_every 0 = no checkpoints; else a positive multiple of `chunk` that
+ *              divides T; dense layout only.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_seqs;
+  int64_t seqlen;
+  int32_t heads;
+  int32_t dk;
+  int32_t dv;
+  int32_t dtype;      /* kda_dtype_t */
+  int32_t chunk;
+  int32_t qk_l2norm;
+  float scale;
+  int32_t reserved0;  /* must be 0 */
+  int64_t ckpt_every;
+} kda_desc_t;
+
+/* Bytes of device workspace kda_chunk_fwd needs for this descriptor (an upper
+ * bound that does not read cu_seqlens).  Returns 0 for an invalid or
+ * unsupported descriptor (kda_last_error() then says why).  The workspace is
+ * scratch: its contents on entry do not matter and are undefined on exit. */
+size_t kda_chunk_fwd_workspace_bytes(const kda_desc_t* desc);
+
+/* Chunkwise prefill.  [XT §5: chunk-parallel within a chunk, recurrent across
+ * chunks; the UT transform turns a chunk of rank-1 transitions into dense
+ * products; the output adds an inter-chunk read of the entering state to an
+ * intra-chunk read of earlier in-chunk pseudo-values.  XT §4: the shared-key
+ * DPLR structure this relies on.]
+ *   q, k       [B, T, H, dk]  dtype          (raw; normalised inside if qk_l2norm)
+ *   v          [B, T, H, dv]  dtype
+ *   g          [B, T, H, dk]  fp32, log of the per-channel forget gate, <= 0
+ *   beta       [B, T, H]      fp32
+ *   init_state [N, H, dk, dv] fp32, or NULL for zeros
+ *   cu_seqlens [N + 1] int32 device array, cu[0] = 0, non-decreasing,
+ *              cu[N] = T; NULL for the dense layout.  Sequences are
+ *              independent; chunks restart at every sequence start and never
+ *              straddle two sequences.  Zero-length sequences are allowed
+ *              (their final state equals their initial state).  The values
+ *              are not checked on the host (that would need a sync).
+ *   o          [B, T, H, dv]  dtype, output; must not alias an input.
+ *   final_state [N, H, dk, dv] fp32 output or NULL; may equal init_state
+ *              (each (sequence, head) state is read before it is written).
+ *   state_ckpt [B, T / ckpt_every, H, dk, dv] fp32 output or NULL; slot j is
+ *              the state after (j + 1) * ckpt_every tokens of sequence b.
+ *   workspace  device scratch of at least kda_chunk_fwd_workspace_bytes().
+ */
+kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           const float* init_state, const int32_t* cu_seqlens, void* o,
+                           float* final_state, float* state_ckpt, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* One decode step for N independent sequences, state updated in place.
+ * [XT §3 decay-then-correct split; XT §5 recurrent form "S_(t-1) + current
+ * token -> S_t + output"; XD §"从推理成本看它省在哪": a fixed-size state read
+ * and written per step, independent of context length.]
+ *   q, k, g    [N, H, dk]   (q, k dtype; g fp32)
+ *   v          [N, H, dv]   dtype
+ *   beta       [N, H]       fp32
+ *   state      [N, H, dk, dv] fp32, read and overwritten with S_t
+ *   o          [N, H, dv]   dtype, output; must not alias an input.
+ * desc->seqlen, batch and ckpt_every are ignored; num_seqs = N.
+ * No workspace is needed. */
+kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* state,
+                             void* o, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kda_status_string(kda_status_t status);
+
+/* Detail message for the last non-OK status returned on this thread ("" if
+ * none).  The pointer stays valid until the next call on this thread. */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,274 @@
+/*
+ * kda_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of the Kimi Delta
+ * Attention (KDA) recurrence in double precision.  Only the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark may load this library; the
+ * product path (the HIP library under gated_delta_rule_54_amd/) never does,
+ * and the two share no code, header, table or helper.
+ *
+ * Pages cited (each by title and section):
+ *   [XT] xutianle.me, "Kimi Linear：用 KDA 重写长上下文注意力"
+ *   [XD] xiudou.site, "Kimi Delta Attention：把遗忘门做到每个通道"
+ *   [DS] docsaid.org, "Kimi Linear" (逐通道的遺忘)
+ *
+ * What is computed, per (sequence, head) chain, token by token:
+ *   1. q^ = q / sqrt(sum q^2 + eps), k^ likewise (eps = 1e-6), when
+ *      qk_l2norm is set.  [XT §6.2 "L2Norm 稳定 key 与 query"; XD, the
+ *      preprocessing list before the recurrence]  The pages give no eps; 1e-6
+ *      under the square root is this project's reading.
+ *   2. alpha = exp(g), one factor per key channel.  [XT §3: alpha_t is a
+ *      d_k-vector; the operator receives it in log space]
+ *   3. S~ = Diag(alpha) S : every ROW c of the d_k x d_v state is scaled by
+ *      alpha_c.  [XT §3, decay step; DS §"KDA：把衰減拆到每個通道", the state
+ *      is d_k x d_v and the matrices multiply on the left; its two-channel
+ *      table (8,6) -> (8,0.6) fixes that rows are key channels]
+ *   4. u = beta (v - S~^T k^)           [XT §2/§3, the error-correcting form]
+ *   5. S = S~ + k^ u^T                  [XT §3, boxed KDA update]
+ *   6. o = scale * S^T q^, with the UPDATED state.  [XT §1: o_t = S_t^T q_t]
+ * The decode oracle applies the same single-token step to a saved state;
+ * [XT §5] names the recurrent form S_(t-1) + current token -> S_t + output.
+ *
+ * Parity pins: every function here is pinned by tests under tests/ that do
+ * not re-type these formulas (worked example, GDN / delta-rule / linear
+ * attention special cases, brute-force transition products, the gradient
+ * identity, invariances).  No function is "parity unpinned".
+ *
+ * Data layout (all row-major, last index fastest):
+ *   q, k  [B, T, H, dk]    v [B, T, H, dv]     g [B, T, H, dk] (fp32)
+ *   beta  [B, T, H] (fp32) states [N, H, dk, dv] (fp32 in, fp64 out)
+ *   o     [B, T, H, dv] (fp64 out)
+ * q, k, v are fp32 (in_dtype 0) or bf16 bit patterns (in_dtype 1); a bf16
+ * value is widened exactly (its 16 bits become the top half of an fp32).
+ * Varlen: B = 1 and sequence n covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_EPS 1e-6
+
+/* Widen one stored input element to double.  bf16 -> fp32 is exact (the
+ * 16 bits are the high half of the fp32 pattern); fp32 -> fp64 is exact. */
+static double load_in(const void* base, int dtype, int64_t idx) {
+    if (dtype == 0) return (double)((const float*)base)[idx];
+    uint16_t h = ((const uint16_t*)base)[idx];
+    uint32_t w = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    /* problem */
+    int64_t batch, seqlen, num_seqs, heads, dk, dv;
+    int in_dtype, qk_l2norm;
+    double scale;
+    int64_t ckpt_every;
+    const void *q, *k, *v;
+    const float *g, *beta, *init_state;
+    const int32_t* cu_seqlens;
+    double *o, *final_state, *ckpt;
+    /* decode mode: steps > 0 means [steps, N, H, d] inputs, one token per step */
+    int64_t steps;
+    /* work split */
+    int64_t next_chain; /* guarded by mu */
+    pthread_mutex_t mu;
+} job_t;
+
+/* One token of the recurrence on state S (dk x dv, row-major).  qrow/krow/vrow
+ * are element offsets of this token's q, k, v vectors; grow of g; bidx of beta;
+ * orow is where o goes (fp64). */
+static void token_step(const job_t* J, double* S, double* qh, double* kh,
+                       double* u, int64_t qrow, int64_t vrow, int64_t grow,
+                       int64_t bidx, int64_t orow) {
+    const int64_t dk = J->dk, dv = J->dv;
+    /* step 1: read q, k, optionally L2-normalise */
+    double qq = 0.0, kk = 0.0;
+    for (int64_t c = 0; c < dk; ++c) {
+        qh[c] = load_in(J->q, J->in_dtype, qrow + c);
+        kh[c] = load_in(J->k, J->in_dtype, qrow + c);
+        qq += qh[c] * qh[c];
+        kk += kh[c] * kh[c];
+    }
+    if (J->qk_l2norm) {
+        double rq = 1.0 / sqrt(qq + ORACLE_EPS), rk = 1.0 / sqrt(kk + ORACLE_EPS);
+        for (int64_t c = 0; c < dk; ++c) { qh[c] *= rq; kh[c] *= rk; }
+    }
+    /* steps 2-3: per-channel decay of the state's rows */
+    for (int64_t c = 0; c < dk; ++c) {
+        double a = exp((double)J->g[grow + c]);
+        double* row = S + c * dv;
+        for (int64_t j = 0; j < dv; ++j) row[j] *= a;
+    }
+    /* step 4: u = beta * (v - S~^T k^) */
+    const double b = (double)J->beta[bidx];
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < dk; ++c) acc += S[c * dv + j] * kh[c];
+        u[j] = b * (load_in(J->v, J->in_dtype, vrow + j) - acc);
+    }
+    /* step 5: S = S~ + k^ u^T */
+    for (int64_t c = 0; c < dk; ++c) {
+        double* row = S + c * dv;
+        for (int64_t j = 0; j < dv; ++j) row[j] += kh[c] * u[j];
+    }
+    /* step 6: o = scale * S^T q^ (post-update state) */
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < dk; ++c) acc += S[c * dv + j] * qh[c];
+        J->o[orow + j] = J->scale * acc;
+    }
+}
+
+/* Run one (sequence, head) chain of the prefill problem. */
+static void run_fwd_chain(const job_t* J, int64_t n, int64_t h, double* S,
+                          double* qh, double* kh, double* u) {
+    const int64_t H = J->heads, dk = J->dk, dv = J->dv, sz = dk * dv;
+    /* token range of this sequence in the [B, T] token grid */
+    int64_t tok0, len;
+    if (J->cu_seqlens) {
+        tok0 = J->cu_seqlens[n];
+        len = (int64_t)J->cu_seqlens[n + 1] - tok0;
+    } else {
+        tok0 = n * J->seqlen;
+        len = J->seqlen;
+    }
+    const int64_t sidx = (n * H + h) * sz;
+    for (int64_t i = 0; i < sz; ++i)
+        S[i] = J->init_state ? (double)J->init_state[sidx + i] : 0.0;
+    const int64_t nck = (J->ckpt_every > 0) ? J->seqlen / J->ckpt_every : 0;
+    for (int64_t t = 0; t < len; ++t) {
+        const int64_t tok = tok0 + t;
+        token_step(J, S, qh, kh, u, (tok * H + h) * dk, (tok * H + h) * dv,
+                   (tok * H + h) * dk, tok * H + h, (tok * H + h) * dv);
+        if (J->ckpt && J->ckpt_every > 0 && (t + 1) % J->ckpt_every == 0) {
+            const int64_t j = (t + 1) / J->ckpt_every - 1;
+            double* dst = J->ckpt + (((n * nck) + j) * H + h) * sz;
+            memcpy(dst, S, (size_t)sz * sizeof(double));
+        }
+    }
+    if (J->final_state) memcpy(J->final_state + sidx, S, (size_t)sz * sizeof(double));
+}
+
+/* Run one (sequence, head) chain of the decode problem: steps tokens, each
+ * from its own [N, H, d] slab. */
+static void run_decode_chain(const job_t* J, int64_t n, int64_t h, double* S,
+                             double* qh, double* kh, double* u) {
+    const int64_t N = J->num_seqs, H = J->heads, dk = J->dk, dv = J->dv, sz = dk * dv;
+    const int64_t sidx = (n * H + h) * sz;
+    for (int64_t i = 0; i < sz; ++i)
+        S[i] = J->init_state ? (double)J->init_state[sidx + i] : 0.0;
+    for (int64_t s = 0; s < J->steps; ++s) {
+        const int64_t row = (s * N + n) * H + h;
+        token_step(J, S, qh, kh, u, row * dk, row * dv, row * dk, row, row * dv);
+    }
+    if (J->final_state) memcpy(J->final_state + sidx, S, (size_t)sz * sizeof(double));
+}
+
+static void* worker(void* arg) {
+    job_t* J = (job_t*)arg;
+    const int64_t sz = J->dk * J->dv;
+    double* S = (double*)malloc((size_t)sz * sizeof(double));
+    double* qh = (double*)malloc((size_t)J->dk * sizeof(double));
+    double* kh = (double*)malloc((size_t)J->dk * sizeof(double));
+    double* u = (double*)malloc((size_t)J->dv * sizeof(double));
+    if (!S || !qh || !kh || !u) { free(S); free(qh); free(kh); free(u); return (void*)1; }
+    const int64_t total = J->num_seqs * J->heads;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t c = J->next_chain++;
+        pthread_mutex_unlock(&J->mu);
+        if (c >= total) break;
+        const int64_t n = c / J->heads, h = c % J->heads;
+        if (J->steps > 0) run_decode_chain(J, n, h, S, qh, kh, u);
+        else run_fwd_chain(J, n, h, S, qh, kh, u);
+    }
+    free(S); free(qh); free(kh); free(u);
+    return NULL;
+}
+
+static int run_job(job_t* J, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t tid[256];
+    pthread_mutex_init(&J->mu, NULL);
+    J->next_chain = 0;
+    int started = 0, rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, worker, J) != 0) break;
+        ++started;
+    }
+    if (started == 0) {
+        void* r = worker(J);
+        rc = (r != NULL);
+    }
+    for (int i = 0; i < started; ++i) {
+        void* r = NULL;
+        pthread_join(tid[i], &r);
+        if (r != NULL) rc = 1;
+    }
+    pthread_mutex_destroy(&J->mu);
+    return rc;
+}
+
+/* Prefill oracle.  Returns 0 on success, nonzero on bad arguments or
+ * allocation failure.  final_state and ckpt may be NULL.  Checkpoint j
+ * (dense only) is the state after (j+1)*ckpt_every tokens of a sequence,
+ * stored at ckpt[b, j, h, :, :] with T/ckpt_every slots per sequence. */
+int kda_oracle_fwd_f64(int64_t batch, int64_t seqlen, int64_t num_seqs, int64_t heads,
+                       int64_t dk, int64_t dv, int in_dtype, const void* q, const void* k,
+                       const void* v, const float* g, const float* beta,
+                       const float* init_state, const int32_t* cu_seqlens, int qk_l2norm,
+                       double scale, int64_t ckpt_every, double* o, double* final_state,
+                       double* ckpt, int nthreads) {
+    if (batch < 1 || seqlen < 0 || heads < 1 || dk < 1 || dv < 1) return 2;
+    if (in_dtype != 0 && in_dtype != 1) return 2;
+    if (!q || !k || !v || !g || !beta || !o) return 2;
+    if (cu_seqlens) {
+        if (batch != 1 || num_seqs < 1) return 2;
+        if (cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != seqlen) return 2;
+        for (int64_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return 2;
+        if (ckpt_every > 0) return 2;
+    } else if (num_seqs != batch) {
+        return 2;
+    }
+    if (ckpt_every < 0) return 2;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.batch = batch; J.seqlen = seqlen; J.num_seqs = num_seqs; J.heads = heads;
+    J.dk = dk; J.dv = dv; J.in_dtype = in_dtype; J.qk_l2norm = qk_l2norm;
+    J.scale = scale; J.ckpt_every = ckpt_every;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.init_state = init_state;
+    J.cu_seqlens = cu_seqlens; J.o = o; J.final_state = final_state; J.ckpt = ckpt;
+    J.steps = 0;
+    return run_job(&J, nthreads) ? 3 : 0;
+}
+
+/* Decode oracle: `steps` single-token steps for N sequences x H heads.
+ * Inputs are [steps, N, H, d] (q,k,g: d = dk; v: d = dv), beta [steps, N, H];
+ * state_in [N, H, dk, dv] fp32 (NULL = zeros); o [steps, N, H, dv] fp64;
+ * state_out [N, H, dk, dv] fp64.  Chains are independent, so each one runs
+ * its steps back to back; the result equals the step-major order exactly. */
+int kda_oracle_decode_f64(int64_t steps, int64_t num_seqs, int64_t heads, int64_t dk,
+                          int64_t dv, int in_dtype, const void* q, const void* k,
+                          const void* v, const float* g, const float* beta,
+                          const float* state_in, int qk_l2norm, double scale, double* o,
+                          double* state_out, int nthreads) {
+    if (steps < 1 || num_seqs < 1 || heads < 1 || dk < 1 || dv < 1) return 2;
+    if (in_dtype != 0 && in_dtype != 1) return 2;
+    if (!q || !k || !v || !g || !beta || !o) return 2;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.batch = num_seqs; J.seqlen = 0; J.num_seqs = num_seqs; J.heads = heads;
+    J.dk = dk; J.dv = dv; J.in_dtype = in_dtype; J.qk_l2norm = qk_l2norm;
+    J.scale = scale; J.ckpt_every = 0;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.init_state = state_in;
+    J.o = o; J.final_state = state_out; J.steps = steps;
+    return run_job(&J, nthreads) ? 3 : 0;
+}
+
+int kda_oracle_abi_version(void) { return 1; }

@@ -1,0 +1,54 @@
+"""Planted mistakes in the oracle, on the CPU: every plausible slip (a dropped
+term, a wrong sign, a swapped operand or index) must fail at least one pin.
+Each mutant is a copy of oracle/kda_oracle.c with one textual change, built
+with gcc into a temporary directory."""
+import os
+
+import pytest
+
+import oracle_pins as P
+from oracle import oracle as O
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "kda_oracle.c")
+
+MUTANTS = {
+    "decay_dropped": ("for (int64_t j = 0; j < dv; ++j) row[j] *= a;",
+                      "for (int64_t j = 0; j < dv; ++j) row[j] *= 1.0;"),
+    "gate_sign": ("double a = exp((double)J->g[grow + c]);",
+                  "double a = exp(-(double)J->g[grow + c]);"),
+    "beta_dropped": ("u[j] = b * (", "u[j] = 1.0 * ("),
+    "error_sign": ("vrow + j) - acc);", "vrow + j) + acc);"),
+    "write_with_q": ("row[j] += kh[c] * u[j];", "row[j] += qh[c] * u[j];"),
+    "read_with_k": ("acc += S[c * dv + j] * qh[c];", "acc += S[c * dv + j] * kh[c];"),
+    "read_before_write": ("acc += S[c * dv + j] * qh[c];",
+                          "acc += (S[c * dv + j] - kh[c] * u[j]) * qh[c];"),
+    "transposed_correction": ("acc += S[c * dv + j] * kh[c];", "acc += S[j * dv + c] * kh[c];"),
+    "no_l2norm": ("if (J->qk_l2norm) {", "if (0) {"),
+    "norm_squared": ("double rq = 1.0 / sqrt(qq + ORACLE_EPS), rk = 1.0 / sqrt(kk + ORACLE_EPS);",
+                     "double rq = 1.0 / (qq + ORACLE_EPS), rk = 1.0 / (kk + ORACLE_EPS);"),
+    "gate_from_head0": ("(tok * H + h) * dk, tok * H + h,", "(tok * H) * dk, tok * H + h,"),
+    "varlen_offset": ("tok0 = J->cu_seqlens[n];", "tok0 = 0 * J->cu_seqlens[n];"),
+    "scale_ignored": ("J->o[orow + j] = J->scale * acc;", "J->o[orow + j] = acc;"),
+}
+
+
+def _caught(lib):
+    for pin in P.ALL_PINS:
+        try:
+            pin(lib=lib)
+        except (AssertionError, RuntimeError, ValueError):
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new, 1)
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(mutated)
+    lib = O.open_library(O.compile_source(str(path), str(tmp_path / f"lib_{name}.so")))
+    assert _caught(lib) is not None, f"mutant {name} passes every pin"

@@ -1,0 +1,13 @@
+"""The oracle against its pins (CPU only)."""
+import pytest
+
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_forgetting_licence():
+    P.pin_forgetting()
