@@ -1,0 +1,12 @@
+"""MI355X-native Kimi Delta Attention (KDA) operator.
+
+The operator runs in hand-written HIP kernels for gfx950 behind the C ABI
+of include/kda.h (libkda.so, built in-tree by
+``python -m gated_delta_rule_54_amd.build``).  This package is the thin
+Python binding over that ABI; torch provides device memory and streams.
+"""
+from .kda import (KdaDesc, KdaError, chunk_fwd_workspace_bytes, kda_chunk_fwd,  # noqa: F401
+                  kda_decode_step, load_library, make_desc)
+
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "chunk_fwd_workspace_bytes", "load_library",
+           "make_desc", "KdaDesc", "KdaError"]

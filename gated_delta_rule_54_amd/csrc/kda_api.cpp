@@ -1,0 +1,171 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: descriptor validation,
+// workspace sizing, status strings and dispatch to the HIP launchers.
+//
+// Validation is host-only and never synchronises the device; on error nothing
+// is launched.  The library allocates no device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kda_internal.h"
+
+#define KDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string t_last_error;
+
+kda_status_t fail(kda_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return st;
+}
+
+kda_status_t ok() {
+  t_last_error.clear();
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by both entry points: dims, dtype, chunk, scale.
+kda_status_t check_common(const kda_desc_t* d) {
+  if (!d) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->reserved0 != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "desc.reserved0 must be 0");
+  if (d->heads < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "heads must be >= 1 (got %d)", d->heads);
+  if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
+  if (d->dk < 1 || d->dv < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dk and dv must be positive (got %d, %d)", d->dk, d->dv);
+  if (d->dk != d->dv || (d->dk != 64 && d->dk != 128))
+    return fail(KDA_ERR_UNSUPPORTED, "supported head dims: dk = dv = 64 or 128 (got %d, %d)",
+                d->dk, d->dv);
+  if (!std::isfinite(d->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (d->qk_l2norm != 0 && d->qk_l2norm != 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "qk_l2norm must be 0 or 1");
+  return KDA_OK;
+}
+
+kda_status_t check_chunk_desc(const kda_desc_t* d) {
+  kda_status_t st = check_common(d);
+  if (st != KDA_OK) return st;
+  if (d->chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", d->chunk);
+  if (d->batch < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", d->batch);
+  if (d->num_seqs < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1 (got %d)", d->num_seqs);
+  if (d->seqlen < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
+  if (d->seqlen > (int64_t(1) << 40))
+    return fail(KDA_ERR_UNSUPPORTED, "seqlen %lld exceeds 2^40", (long long)d->seqlen);
+  if (d->ckpt_every < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt_every must be >= 0");
+  if (d->ckpt_every > 0) {
+    if (d->ckpt_every % d->chunk != 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt_every (%lld) must be a multiple of chunk",
+                  (long long)d->ckpt_every);
+    if (d->seqlen % d->ckpt_every != 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "ckpt_every (%lld) must divide seqlen (%lld)",
+                  (long long)d->ckpt_every, (long long)d->seqlen);
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT const char* kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_STATUS_UNKNOWN";
+}
+
+KDA_EXPORT const char* kda_last_error(void) { return t_last_error.c_str(); }
+
+KDA_EXPORT int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(const kda_desc_t* desc) {
+  if (check_chunk_desc(desc) != KDA_OK) return 0;
+  return kda::chunk_workspace_bytes(*desc);
+}
+
+KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
+                                      const void* v, const float* g, const float* beta,
+                                      const float* init_state, const int32_t* cu_seqlens,
+                                      void* o, float* final_state, float* state_ckpt,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  kda_status_t st = check_chunk_desc(desc);
+  if (st != KDA_OK) return st;
+  const kda_desc_t& d = *desc;
+  if (cu_seqlens) {
+    if (d.batch != 1)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "varlen (cu_seqlens != NULL) needs batch == 1");
+    if (d.ckpt_every > 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "state checkpoints need the dense layout");
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  } else if (d.num_seqs != d.batch) {
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dense layout needs num_seqs == batch (%d vs %d)",
+                d.num_seqs, d.batch);
+  }
+  if ((d.ckpt_every > 0) != (state_ckpt != nullptr))
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "state_ckpt must be given exactly when ckpt_every > 0");
+  const bool has_tokens = d.seqlen > 0;
+  const void* need[] = {q, k, v, g, beta, o};
+  const char* names[] = {"q", "k", "v", "g", "beta", "o"};
+  for (int i = 0; i < 6; ++i) {
+    if (has_tokens && !need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (need[i] && !aligned16(need[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  const void* opt[] = {init_state, final_state, state_ckpt, workspace};
+  const char* onames[] = {"init_state", "final_state", "state_ckpt", "workspace"};
+  for (int i = 0; i < 4; ++i)
+    if (opt[i] && !aligned16(opt[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", onames[i]);
+  if (o && (o == q || o == k || o == v || o == (const void*)g || o == (const void*)beta))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
+  const size_t need_ws = kda::chunk_workspace_bytes(d);
+  if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu%s", need_ws,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  hipError_t e = kda::launch_chunk_fwd(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                       final_state, state_ckpt, workspace, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_fwd launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+KDA_EXPORT kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, const void* k,
+                                        const void* v, const float* g, const float* beta,
+                                        float* state, void* o, hipStream_t stream) {
+  kda_status_t st = check_common(desc);
+  if (st != KDA_OK) return st;
+  const kda_desc_t& d = *desc;
+  if (d.num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+  if ((int64_t)d.num_seqs * d.heads > 0x7fffffffLL)
+    return fail(KDA_ERR_UNSUPPORTED, "num_seqs * heads exceeds 2^31 - 1");
+  if (d.num_seqs == 0) return ok();
+  const void* need[] = {q, k, v, g, beta, state, o};
+  const char* names[] = {"q", "k", "v", "g", "beta", "state", "o"};
+  for (int i = 0; i < 7; ++i) {
+    if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(need[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (o == q || o == k || o == v || o == (const void*)g || o == (const void*)beta ||
+      o == (const void*)state)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input or the state");
+  hipError_t e = kda::launch_decode(d, q, k, v, g, beta, state, o, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_decode_step launch: %s", hipGetErrorString(e));
+  return ok();
+}

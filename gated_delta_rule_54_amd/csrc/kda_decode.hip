@@ -1,0 +1,164 @@
+// kda_decode.hip -- fused single-token KDA decode step for gfx950.
+//
+// Pages cited (by title and section):
+//   [XT] xutianle.me, "Kimi Linear：用 KDA 重写长上下文注意力"
+//   [XD] xiudou.site, "Kimi Delta Attention：把遗忘门做到每个通道"
+//
+// Per (sequence, head), with S the d x d fp32 state (rows = key channels):
+//   k^, q^ = L2-normalised k, q                     [XT §6.2]
+//   S~ = Diag(exp g) S                              [XT §3, decay step]
+//   u  = beta (v - S~^T k^)                         [XT §3, correction]
+//   S  = S~ + k^ u^T                                [XT §3, boxed update]
+//   o  = scale S^T q^ = scale (S~^T q^ + u (k^.q^))  [XT §1 read-out, expanded]
+// The last line reads the updated state without a second pass over it: both
+// reductions (S~^T k^ and S~^T q^) are taken in the one pass that decays the
+// state, and the rank-1 term's contribution to the read-out is added from
+// the scalar k^.q^.  The step is a pure read-modify-write of the state
+// [XD §"从推理成本看它省在哪"]: 2 d^2 * 4 bytes of HBM traffic per head for
+// ~7 d^2 flops, so the kernel is laid out for bandwidth:
+//
+//   one 256-thread workgroup per (sequence, head); thread t owns 4 adjacent
+//   columns (a float4) of D/RG consecutive rows.  A wave's float4 loads cover
+//   whole 512-byte (D=128) row segments, so every state access is a fully
+//   coalesced 16-byte-per-lane load or store.  The state is read once into
+//   registers, decayed, reduced, updated and written back once.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kNormEps = 1e-6f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+__device__ __forceinline__ void store_out(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store_out(__hip_bfloat16* p, float x) { *p = __float2bfloat16(x); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void decode_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    T* __restrict__ o, int qk_l2norm, float scale) {
+  constexpr int CG = D / 4;            // float4 column groups per row
+  constexpr int RG = kThreads / CG;    // row groups
+  constexpr int RPG = D / RG;          // rows per thread
+  static_assert(CG * RG == kThreads && RPG * RG == D, "tile must cover the state");
+
+  __shared__ float s_k[D], s_q[D], s_a[D];
+  __shared__ float s_red_k[RG][D], s_red_q[RG][D];
+  __shared__ float s_u[D];
+  __shared__ float s_scal[2][kThreads / 64][2];
+
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, rg = tid / CG;
+  const int64_t head = blockIdx.x;  // flattened (sequence, head)
+  float* S = state + head * (int64_t)D * D;
+
+  // 1) Put the state's loads in flight first.
+  float4 s[RPG];
+#pragma unroll
+  for (int r = 0; r < RPG; ++r)
+    s[r] = reinterpret_cast<const float4*>(S + (int64_t)(rg * RPG + r) * D)[cg];
+
+  // 2) Per-channel vectors: raw k, q, and the gate.
+  const int64_t vb = head * D;
+  float kk = 0.f, qq = 0.f, kq = 0.f;
+  if (tid < D) {
+    const float kv = to_f32(k[vb + tid]), qv = to_f32(q[vb + tid]);
+    s_k[tid] = kv;
+    s_q[tid] = qv;
+    s_a[tid] = __expf(g[vb + tid]);
+    kk = kv * kv; qq = qv * qv; kq = kv * qv;
+  }
+  // wave reductions of |k|^2, |q|^2, k.q
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kk += __shfl_xor(kk, off);
+    qq += __shfl_xor(qq, off);
+    kq += __shfl_xor(kq, off);
+  }
+  const int wave = tid / 64, lane = tid % 64;
+  if (lane == 0) { s_scal[0][wave][0] = kk; s_scal[0][wave][1] = qq; s_scal[1][wave][0] = kq; }
+  __syncthreads();
+  float KK = 0.f, QQ = 0.f, KQ = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    KK += s_scal[0][w][0]; QQ += s_scal[0][w][1]; KQ += s_scal[1][w][0];
+  }
+  const float rk = qk_l2norm ? rsqrtf(KK + kNormEps) : 1.f;
+  const float rq = qk_l2norm ? rsqrtf(QQ + kNormEps) : 1.f;
+  const float kq_hat = KQ * rk * rq;
+
+  // 3) Decay the owned rows and form the partial reductions S~^T k^, S~^T q^.
+  float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+  float kr[RPG];
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    const int row = rg * RPG + r;
+    const float a = s_a[row];
+    const float kh = s_k[row] * rk, qh = s_q[row] * rq;
+    kr[r] = kh;
+    s[r].x *= a; s[r].y *= a; s[r].z *= a; s[r].w *= a;
+    pk[0] += s[r].x * kh; pk[1] += s[r].y * kh; pk[2] += s[r].z * kh; pk[3] += s[r].w * kh;
+    pq[0] += s[r].x * qh; pq[1] += s[r].y * qh; pq[2] += s[r].z * qh; pq[3] += s[r].w * qh;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s_red_k[rg][cg * 4 + j] = pk[j];
+    s_red_q[rg][cg * 4 + j] = pq[j];
+  }
+  __syncthreads();
+
+  // 4) Column-wise totals, the correction u and the read-out.
+  if (tid < D) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) { sk += s_red_k[i][tid]; sq += s_red_q[i][tid]; }
+    const float u = beta[head] * (to_f32(v[vb + tid]) - sk);
+    s_u[tid] = u;
+    store_out(o + vb + tid, scale * (sq + u * kq_hat));
+  }
+  __syncthreads();
+
+  // 5) Rank-1 write and store.
+  const float4 u4 = reinterpret_cast<const float4*>(s_u)[cg];
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    float4 t = s[r];
+    t.x += kr[r] * u4.x; t.y += kr[r] * u4.y; t.z += kr[r] * u4.z; t.w += kr[r] * u4.w;
+    reinterpret_cast<float4*>(S + (int64_t)(rg * RPG + r) * D)[cg] = t;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, float* state, void* o,
+                        hipStream_t stream) {
+  const int64_t blocks = (int64_t)d.num_seqs * d.heads;
+  hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                     static_cast<const T*>(v), g, beta, state, static_cast<T*>(o), d.qk_l2norm,
+                     d.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float* state, void* o,
+                         hipStream_t stream) {
+  if (d.num_seqs == 0) return hipSuccess;
+  const bool bf16 = d.dtype == KDA_DTYPE_BF16;
+  if (d.dk == 128) {
+    return bf16 ? launch_typed<__hip_bfloat16, 128>(d, q, k, v, g, beta, state, o, stream)
+                : launch_typed<float, 128>(d, q, k, v, g, beta, state, o, stream);
+  }
+  return bf16 ? launch_typed<__hip_bfloat16, 64>(d, q, k, v, g, beta, state, o, stream)
+              : launch_typed<float, 64>(d, q, k, v, g, beta, state, o, stream);
+}
+
+}  // namespace kda

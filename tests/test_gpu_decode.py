@@ -1,0 +1,89 @@
+"""Decode step on the GPU against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_54_amd import kda_decode_step
+from gated_delta_rule_54_amd import workloads as W
+from oracle import oracle as O
+from parity import TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(N, H, d, dtype, steps, seed, qk_l2norm=True, scale=1.0):
+    gen = W.make_generator(seed, DEV)
+    s0 = W.decode_initial_state(num_seqs=N, heads=H, dk=d, dv=d, gen=gen, device=DEV)
+    state = s0.clone()
+    ins, outs = [], []
+    for _ in range(steps):
+        x = W.decode_step_inputs(num_seqs=N, heads=H, dk=d, dv=d, dtype=dtype, gen=gen, device=DEV)
+        outs.append(kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state,
+                                    qk_l2norm=qk_l2norm, scale=scale).clone())
+        ins.append({k: t.cpu() for k, t in x.items()})
+    torch.cuda.synchronize()
+    st = lambda key: torch.stack([i[key] for i in ins])
+    o_ref, s_ref = O.kda_decode(st("q"), st("k"), st("v"), st("g"), st("beta"), s0.cpu(),
+                                qk_l2norm=qk_l2norm, scale=scale)
+    return torch.stack(outs), state, o_ref, s_ref
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_decode_small(d, dtype):
+    print(f"decode small d={d} {dtype}", flush=True)
+    o, s, o_ref, s_ref = _run(3, 2, d, dtype, steps=7, seed=7)
+    assert_close("o", o, o_ref, TOL[dtype])
+    assert_close("state", s, s_ref, TOL[dtype] / 10)
+
+
+def test_decode_options():
+    print("decode qk_l2norm=0 scale=0.5", flush=True)
+    o, s, o_ref, s_ref = _run(2, 3, 128, torch.float32, steps=4, seed=8, qk_l2norm=False,
+                              scale=0.5)
+    assert_close("o", o, o_ref, 1e-4)
+    assert_close("state", s, s_ref, 1e-5)
+
+
+def test_decode_zero_sequences():
+    q = torch.zeros((0, 2, 64), device=DEV)
+    st = torch.zeros((0, 2, 64, 64), device=DEV)
+    b = torch.zeros((0, 2), device=DEV)
+    o = kda_decode_step(q, q, q, q, b, st)
+    assert o.shape == (0, 2, 64)
+
+
+def test_decode_full_size_sampled():
+    """The 256-sequence x 32-head x d128 workload, 1024 steps, launched as the
+    benchmark launches it; a sample of whole (sequence, head) chains is
+    checked against the oracle step by step."""
+    w = W.DECODE_256
+    N, H, d = w.num_seqs, w.heads, w.dk
+    print(f"decode full size {w.describe()}", flush=True)
+    gen = W.make_generator(w.seed, DEV)
+    state = W.decode_initial_state(num_seqs=N, heads=H, dk=d, dv=d, gen=gen, device=DEV)
+    rng = np.random.default_rng(0)
+    pairs = sorted(set((int(a), int(b)) for a, b in zip(rng.integers(0, N, 40),
+                                                         rng.integers(0, H, 40))))
+    pairs += [(0, 0), (N - 1, H - 1)]
+    ns = torch.tensor([p[0] for p in pairs], device=DEV)
+    hs = torch.tensor([p[1] for p in pairs], device=DEV)
+    s0 = state[ns, hs].cpu()
+    keep = {key: [] for key in ("q", "k", "v", "g", "beta")}
+    o_keep = []
+    for step in range(w.steps):
+        x = W.decode_step_inputs(num_seqs=N, heads=H, dk=d, dv=d, dtype=w.dtype, gen=gen,
+                                 device=DEV)
+        o = kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state)
+        for key in keep:
+            keep[key].append(x[key][ns, hs])
+        o_keep.append(o[ns, hs])
+    torch.cuda.synchronize()
+    st = lambda key: torch.stack(keep[key]).cpu().unsqueeze(2)  # [steps, S, 1, d]
+    o_ref, s_ref = O.kda_decode(st("q"), st("k"), st("v"), st("g"), st("beta"),
+                                s0.unsqueeze(1))
+    o_gpu = torch.stack(o_keep).unsqueeze(2)
+    assert_close("o (sampled chains, all steps)", o_gpu, o_ref, TOL[w.dtype])
+    assert_close("state (sampled chains)", state[ns, hs].unsqueeze(1), s_ref, TOL[w.dtype] / 10)
+    assert torch.isfinite(state).all()
