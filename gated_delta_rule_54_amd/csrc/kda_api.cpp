@@ -32,7 +32,8 @@ kda_status_t ok() {
   return KDA_OK;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 // Checks shared by both entry points: dims, dtype, chunk, scale.
 kda_status_t check_common(const kda_desc_t* d) {
@@ -119,19 +120,25 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
   if ((d.ckpt_every > 0) != (state_ckpt != nullptr))
     return fail(KDA_ERR_INVALID_ARGUMENT,
                 "state_ckpt must be given exactly when ckpt_every > 0");
+  // q, k, v, o rows are moved with 16-byte vector accesses; everything else
+  // with 4-byte scalar accesses.
   const bool has_tokens = d.seqlen > 0;
   const void* need[] = {q, k, v, g, beta, o};
   const char* names[] = {"q", "k", "v", "g", "beta", "o"};
+  const uintptr_t align[] = {16, 16, 16, 4, 4, 16};
   for (int i = 0; i < 6; ++i) {
     if (has_tokens && !need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
-    if (need[i] && !aligned16(need[i]))
-      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+    if (need[i] && !aligned(need[i], align[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i],
+                  (int)align[i]);
   }
   const void* opt[] = {init_state, final_state, state_ckpt, workspace};
   const char* onames[] = {"init_state", "final_state", "state_ckpt", "workspace"};
+  const uintptr_t oalign[] = {4, 4, 4, 16};
   for (int i = 0; i < 4; ++i)
-    if (opt[i] && !aligned16(opt[i]))
-      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", onames[i]);
+    if (opt[i] && !aligned(opt[i], oalign[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", onames[i],
+                  (int)oalign[i]);
   if (o && (o == q || o == k || o == v || o == (const void*)g || o == (const void*)beta))
     return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
   const size_t need_ws = kda::chunk_workspace_bytes(d);
@@ -154,12 +161,16 @@ KDA_EXPORT kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, c
   if ((int64_t)d.num_seqs * d.heads > 0x7fffffffLL)
     return fail(KDA_ERR_UNSUPPORTED, "num_seqs * heads exceeds 2^31 - 1");
   if (d.num_seqs == 0) return ok();
+  // The state is moved with 16-byte vector accesses, the rest element-wise.
+  const uintptr_t el = d.dtype == KDA_DTYPE_BF16 ? 2 : 4;
   const void* need[] = {q, k, v, g, beta, state, o};
   const char* names[] = {"q", "k", "v", "g", "beta", "state", "o"};
+  const uintptr_t align[] = {el, el, el, 4, 4, 16, el};
   for (int i = 0; i < 7; ++i) {
     if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
-    if (!aligned16(need[i]))
-      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+    if (!aligned(need[i], align[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i],
+                  (int)align[i]);
   }
   if (o == q || o == k || o == v || o == (const void*)g || o == (const void*)beta ||
       o == (const void*)state)

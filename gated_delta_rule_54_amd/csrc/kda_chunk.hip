@@ -1,14 +1,919 @@
-// kda_chunk.hip -- chunkwise prefill (placeholder until the kernels land).
+// kda_chunk.hip -- chunkwise KDA prefill for gfx950 (MI355X).
+//
+// Pages cited (by title and section):
+//   [XT] xutianle.me, "Kimi Linear：用 KDA 重写长上下文注意力"
+//   [XD] xiudou.site, "Kimi Delta Attention：把遗忘门做到每个通道"
+//
+// Method.  [XT §5] splits the sequence into chunks of C = 64 tokens: work
+// inside a chunk is parallel, chunks are chained through the d x d state,
+// and the UT transform turns a chunk's rank-1 transitions into dense
+// products.  [XT §4] notes that the shared key of (I - beta k k^T) Diag(alpha)
+// is what keeps this cheap.  Written out for one chunk of n <= 64 rows with
+// entering state S (d_k x d_v, rows = key channels):
+//
+//   G_r   = sum_(s<=r) g_s            cumulative log-gate, per channel
+//   A_ri  = beta_r sum_c k_rc k_ic e^(G_rc - G_ic)          (i < r)
+//   T     = (I + A)^-1                unit lower triangular
+//   U     = T Diag(beta) V            Wk = T Diag(beta) (K o e^G)
+//   W     = U - Wk S                  the chunk's "pseudo-values"
+//   P_ri  = sum_c q_rc k_ic e^(G_rc - G_ic)                  (i <= r)
+//   O     = (Q o e^G) S + P W         inter-chunk + intra-chunk read-out
+//   S'    = Diag(e^gamma) S + (K o e^(gamma - G))^T W,   gamma = G_n
+//
+// This follows by induction from the per-token update
+// S_t = Diag(a_t) S_(t-1) + k_t u_t^T, u_t = beta_t (v_t - (Diag(a_t) S_(t-1))^T k_t)
+// [XT §3]: S_r = Diag(e^G_r) S + sum_(i<=r) Diag(e^(G_r - G_i)) k_i u_i^T, and
+// stacking the u_r gives (I + A) U_rows = Diag(beta)(V - (K o e^G) S).  It is
+// exact; only rounding separates it from the token-by-token recurrence.
+//
+// Kernels.
+//   K1 (kda_intra_chunk): one workgroup per (chunk, head), fully parallel.
+//     q/k L2 norm, the in-chunk prefix sum of g, A and P on MFMA, the
+//     triangular inverse T in fp32, then U and Wk on MFMA.  Writes the
+//     operands K2 consumes to the workspace.
+//   K2 (kda_state_pass): one workgroup per (sequence, head, d_v slice),
+//     sequential over that sequence's chunks.  The fp32 state slice lives in
+//     MFMA accumulators for the whole sequence; per chunk it forms W, the
+//     output and the next state with three MFMA chains.
+//   The d_v columns of the state never mix, so splitting d_v across
+//   workgroups lets one head's chain use several CUs; the slices of one head
+//   are placed on one XCD so their shared operand reads hit the same L2.
+//
+// Exponent handling.  g <= 0 makes G non-increasing inside a chunk.  The fast
+// path factors e^(G_r - G_i) = e^G_r * e^-G_i with the chunk start as the
+// reference: e^G <= 1 and e^-G <= e^80 when every channel's chunk decay
+// gamma >= -80, so nothing overflows fp32/bf16 (both have an 8-bit exponent)
+// and each product keeps the operands' relative precision.  [XT §4] names
+// the precision loss of this division as a design concern; a chunk whose
+// decay exceeds the bound takes an exact path that forms each
+// e^(G_r - G_i) <= 1 from its own difference (slow, but never overflows).
+//
+// Precision.  MFMA operands are the input dtype (bf16 or fp32); MFMA
+// accumulation, the state, T, G and gamma are fp32.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
+#include <algorithm>
+
 #include "kda_internal.h"
 
 namespace kda {
+namespace {
 
-size_t chunk_workspace_bytes(const kda_desc_t& d) { (void)d; return 0; }
+constexpr int kC = 64;            // chunk length
+constexpr int kThreads = 256;     // 4 waves
+constexpr float kNormEps = 1e-6f;
+constexpr float kFastDecayBound = -80.f;
+constexpr int64_t kSegSlots = 1024;    // chunk slots per K1/K2 launch pair (65536 tokens)
 
-hipError_t launch_chunk_fwd(const kda_desc_t&, const void*, const void*, const void*,
-                            const float*, const float*, const float*, const int32_t*, void*,
-                            float*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __hip_bfloat16 bf16;
+
+// ---------------------------------------------------------------------------
+// Element helpers.  bf16 values are handled as raw 16-bit patterns (no
+// class-typed objects in LDS or unions); rounding is round-to-nearest-even.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint16_t bf_bits(float x) {
+  return __bfloat16_as_ushort(__float2bfloat16(x));
+}
+__device__ __forceinline__ float bf_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float ld_f(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f(const bf16* p) {
+  return bf_val(*reinterpret_cast<const uint16_t*>(p));
+}
+__device__ __forceinline__ void st_f(float* p, float x) { *p = x; }
+__device__ __forceinline__ void st_f(bf16* p, float x) {
+  *reinterpret_cast<uint16_t*>(p) = bf_bits(x);
+}
+
+// Store 4 consecutive elements (8 bytes for bf16, 16 for fp32).
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+  uint2 u;
+  u.x = (uint32_t)bf_bits(a) | ((uint32_t)bf_bits(b) << 16);
+  u.y = (uint32_t)bf_bits(c) | ((uint32_t)bf_bits(d) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+// Load 4 consecutive elements as floats.
+__device__ __forceinline__ f32x4_t ld4(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  return f32x4_t{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ f32x4_t ld4(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4_t{bf_val(u.x & 0xffffu), bf_val(u.x >> 16), bf_val(u.y & 0xffffu),
+                 bf_val(u.y >> 16)};
+}
+// Load N consecutive elements (16-byte aligned, N a multiple of 8) as floats.
+template <int N>
+__device__ __forceinline__ void ld_seg(const float* p, float* out) {
+#pragma unroll
+  for (int j = 0; j < N; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p + j);
+    out[j] = v.x; out[j + 1] = v.y; out[j + 2] = v.z; out[j + 3] = v.w;
+  }
+}
+template <int N>
+__device__ __forceinline__ void ld_seg(const bf16* p, float* out) {
+#pragma unroll
+  for (int j = 0; j < N; j += 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      out[j + 2 * t] = bf_val(v[t] & 0xffffu);
+      out[j + 2 * t + 1] = bf_val(v[t] >> 16);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 tiles.  Lane l of a wave supplies, for operand A (M x K), row
+// l%16 and KPL consecutive k starting at KPL*(l/16); operand B (K x N) the
+// same with column l%16.  The accumulator holds rows 4*(l/16)+j, j = 0..3, of
+// column l%16.  Both operands are therefore read from buffers whose rows are
+// the tile's non-K index with k contiguous.
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+  static constexpr int KSTEP = 32, KPL = 8;
+  using frag = bf16x8_t;
+  static __device__ __forceinline__ frag load(const bf16* p) {
+    return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4_t*>(p));
+  }
+  static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KSTEP = 4, KPL = 1;
+  using frag = float;
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Fragment of rows [row0, row0+16) and k-step ks of a row-major buffer.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_at(const T* base, int ld, int row0, int ks,
+                                                         int lane) {
+  return Mma<T>::load(base + (int64_t)(row0 + (lane & 15)) * ld + ks * Mma<T>::KSTEP +
+                      Mma<T>::KPL * (lane >> 4));
+}
+
+// ---------------------------------------------------------------------------
+// Workspace record of one (head, chunk slot): the operands K2 reads.
+template <typename T, int D>
+struct Rec {
+  // element offsets inside a record (in units of T), then gamma (fp32)
+  static constexpr int64_t QG = 0;                 // [64][D]  q^ o e^G
+  static constexpr int64_t KT = QG + kC * D;       // [D][64]  (k^ o e^(gamma-G))^T
+  static constexpr int64_t WN = KT + D * kC;       // [64][D]  -Wk
+  static constexpr int64_t UT = WN + kC * D;       // [D][64]  U^T
+  static constexpr int64_t P = UT + D * kC;        // [64][64] P (zero above the diagonal)
+  static constexpr int64_t END = P + kC * kC;
+  static constexpr int64_t BYTES_T = END * (int64_t)sizeof(T);
+  static constexpr int64_t BYTES = ((BYTES_T + D * 4 + 255) / 256) * 256;  // + e^gamma
+};
+
+// Where a chunk slot lives in the token stream.  Slots number the chunks of
+// all sequences back to back: dense sequence b owns slots [b*spq, (b+1)*spq)
+// with spq = ceil(T/64); varlen sequence n owns [chunk_off[n], chunk_off[n+1]).
+struct ChunkGeom {
+  const int32_t* cu;          // varlen: sanitised cu_seqlens (device); dense: nullptr
+  const int32_t* chunk_off;   // varlen: [N+1] chunk offsets (device)
+  int64_t T;                  // dense: tokens per sequence
+  int64_t spq;                // dense: chunk slots per sequence
+  int32_t N;
+};
+
+struct ChunkLoc { int64_t tok0; int len; int seq; };
+
+// Slot range, first token and token count of sequence `seq`.
+struct SeqSpan { int64_t c0, c1, tok0, ntok; };
+__device__ __forceinline__ SeqSpan seq_span(const ChunkGeom& gm, int seq) {
+  if (gm.cu == nullptr)
+    return SeqSpan{(int64_t)seq * gm.spq, (int64_t)(seq + 1) * gm.spq, (int64_t)seq * gm.T, gm.T};
+  return SeqSpan{gm.chunk_off[seq], gm.chunk_off[seq + 1], gm.cu[seq],
+                 (int64_t)gm.cu[seq + 1] - gm.cu[seq]};
+}
+
+__device__ __forceinline__ bool locate(const ChunkGeom& gm, int64_t slot, ChunkLoc& L) {
+  int n;
+  if (gm.cu == nullptr) {
+    if (gm.spq == 0) return false;
+    n = (int)(slot / gm.spq);
+    if (n >= gm.N) return false;
+  } else {
+    if (slot >= gm.chunk_off[gm.N]) return false;
+    int lo = 0, hi = gm.N;  // find n with chunk_off[n] <= slot < chunk_off[n+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (gm.chunk_off[mid] <= slot) lo = mid; else hi = mid;
+    }
+    n = lo;
+  }
+  const SeqSpan sp = seq_span(gm, n);
+  const int64_t off = (slot - sp.c0) * kC;
+  L.seq = n;
+  L.tok0 = sp.tok0 + off;
+  L.len = (int)min<int64_t>(kC, sp.ntok - off);
+  return L.len > 0;
+}
+
+// Varlen chunk map, one workgroup.  The caller's cu_seqlens are not trusted:
+// each entry is clamped to [0, T] and made non-decreasing (a running max), so
+// no later kernel can address a token outside [0, T).  For valid input the
+// sanitised offsets equal cu_seqlens.  Then chunk_off[n] = sum_(m<n)
+// ceil(len_m / 64), the first chunk slot of sequence n.
+__global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restrict__ cu, int N,
+                                                          int64_t T, int32_t* __restrict__ cu_s,
+                                                          int32_t* __restrict__ chunk_off) {
+  __shared__ int32_t s_scan[kThreads];
+  __shared__ int32_t s_carry_max, s_carry_sum;
+  const int tid = threadIdx.x;
+  if (tid == 0) { s_carry_max = 0; s_carry_sum = 0; }
+  __syncthreads();
+  // pass 1: sanitised offsets (inclusive max-scan of clamped values)
+  for (int n0 = 0; n0 <= N; n0 += kThreads) {
+    const int n = n0 + tid;
+    int32_t x = 0;
+    if (n <= N) x = (int32_t)min<int64_t>(max<int64_t>((int64_t)cu[n], 0), T);
+    s_scan[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int32_t other = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] = max(s_scan[tid], other);
+      __syncthreads();
+    }
+    if (n <= N) cu_s[n] = max(s_scan[tid], s_carry_max);
+    __syncthreads();
+    if (tid == 0) s_carry_max = max(s_carry_max, s_scan[kThreads - 1]);
+    __syncthreads();
+  }
+  // pass 2: chunk offsets (exclusive sum-scan of per-sequence chunk counts)
+  for (int n0 = 0; n0 < N; n0 += kThreads) {
+    const int n = n0 + tid;
+    int32_t c = 0;
+    if (n < N) c = (cu_s[n + 1] - cu_s[n] + kC - 1) / kC;
+    s_scan[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int32_t add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    if (n < N) chunk_off[n + 1] = s_carry_sum + s_scan[tid];
+    __syncthreads();
+    if (tid == 0) s_carry_sum += s_scan[kThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) chunk_off[0] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// K1: intra-chunk transform.  LDS holds four equal regions, reused by phase:
+//   region 0: raw k -> K o e^G (row-major)          -> V^T       (U phase)
+//   region 1: raw q -> Q o e^G (row-major)          -> A (fp32)  -> T Diag(beta) (MFMA type)
+//   region 2: K o e^-G (row-major) / exact-path staging -> T (fp32)
+//   region 3: (K o e^G)^T
+template <typename T, int D>
+struct K1Lds {
+  static constexpr int LDR = D + 8;        // row-major leading dim (elements)
+  static constexpr int LDT = kC + 8;       // transposed leading dim
+  static constexpr int LDA = kC + 4;       // fp32 64x64 leading dim (16-byte rows)
+  static constexpr int RM = kC * LDR * (int)sizeof(T);
+  static constexpr int TR = D * LDT * (int)sizeof(T);
+  static constexpr int MX = RM > TR ? RM : TR;
+  static constexpr int FP = kC * LDA * 4;                     // fp32 A / T tile
+  static constexpr int REG = ((MX > FP ? MX : FP) + 255) / 256 * 256;
+  static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
+  static constexpr int NPART = kThreads / D;  // scan parts per channel
+  static constexpr int BYTES = 4 * REG + 4096 /*scratch*/ + 3 * kC * 4 + 16;
+};
+
+// fp32 operands at d = 128 need every VGPR of a one-workgroup-per-CU launch.
+template <typename T, int D>
+constexpr int k1_min_blocks() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_chunk(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
+    int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws) {
+  using L = K1Lds<T, D>;
+  using M = Mma<T>;
+  using R = Rec<T, D>;
+  constexpr int NPART = L::NPART, RPP = kC / NPART;  // rows per scan part
+  constexpr int QC = D / 4;                          // channels per thread in the norm phase
+  extern __shared__ __align__(16) char smem[];
+  T* r0 = reinterpret_cast<T*>(smem);
+  T* r1 = reinterpret_cast<T*>(smem + L::REG);
+  T* r2 = reinterpret_cast<T*>(smem + 2 * L::REG);
+  T* r3 = reinterpret_cast<T*>(smem + 3 * L::REG);
+  float* scratch = reinterpret_cast<float*>(smem + 4 * L::REG);           // 1024 floats
+  float* s_rk = scratch + 1024;
+  float* s_rq = s_rk + kC;
+  float* s_beta = s_rq + kC;
+
+  const int h = blockIdx.y;
+  const int64_t slot = slot_base + blockIdx.x;
+  ChunkLoc loc;
+  if (!locate(gm, slot, loc)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rowstride = (int64_t)H * D;  // elements between consecutive tokens
+  const T* qb = q + (loc.tok0 * H + h) * D;
+  const T* kb = k + (loc.tok0 * H + h) * D;
+  const T* vb = v + (loc.tok0 * H + h) * D;
+  const float* gb = g + (loc.tok0 * H + h) * D;
+  char* rec = ws + ((int64_t)h * nrec + (slot - slot_base)) * R::BYTES;
+  T* wQG = reinterpret_cast<T*>(rec) + R::QG;
+  T* wKT = reinterpret_cast<T*>(rec) + R::KT;
+  T* wWN = reinterpret_cast<T*>(rec) + R::WN;
+  T* wUT = reinterpret_cast<T*>(rec) + R::UT;
+  T* wP = reinterpret_cast<T*>(rec) + R::P;
+  float* wEG = reinterpret_cast<float*>(rec + R::BYTES_T);
+
+  // ---- issue the chunk's global loads ------------------------------------
+  // norm layout: thread = (row nr, quarter nq) covering QC channels
+  const int nr = tid >> 2, nq = tid & 3;
+  const bool nvalid = nr < loc.len;
+  float qraw[QC], kraw[QC];
+  if (nvalid) {
+    ld_seg<QC>(qb + nr * rowstride + nq * QC, qraw);
+    ld_seg<QC>(kb + nr * rowstride + nq * QC, kraw);
+  } else {
+#pragma unroll
+    for (int j = 0; j < QC; ++j) { qraw[j] = 0.f; kraw[j] = 0.f; }
+  }
+  // scan layout: thread = (channel sc, part sp) covering RPP rows
+  const int sc = tid % D, sp = tid / D;
+  float G[RPP];
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const int r = sp * RPP + j;
+    G[j] = r < loc.len ? gb[r * rowstride + sc] : 0.f;
+  }
+  if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
+
+  // ---- phase 1: row norms; raw q, k into regions 1, 0 ---------------------
+  {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < QC; ++j) { sq += qraw[j] * qraw[j]; sk += kraw[j] * kraw[j]; }
+    sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
+    sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
+    if (nq == 0) {
+      s_rq[nr] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
+      s_rk[nr] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
+    }
+#pragma unroll
+    for (int j = 0; j < QC; j += 4) {
+      st4(r1 + nr * L::LDR + nq * QC + j, qraw[j], qraw[j + 1], qraw[j + 2], qraw[j + 3]);
+      st4(r0 + nr * L::LDR + nq * QC + j, kraw[j], kraw[j + 1], kraw[j + 2], kraw[j + 3]);
+    }
+  }
+  // ---- phase 2: prefix sum of g within the chunk ---------------------------
+#pragma unroll
+  for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
+  scratch[sp * D + sc] = G[RPP - 1];
+  __syncthreads();
+  float off = 0.f, gamma = 0.f;
+#pragma unroll
+  for (int p = 0; p < NPART; ++p) {
+    const float t = scratch[p * D + sc];
+    off += p < sp ? t : 0.f;
+    gamma += t;
+  }
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) G[j] += off;
+  const bool exact = __syncthreads_or(gamma < kFastDecayBound) != 0;
+
+  // V rows: loaded now, consumed after phase 3 (as V^T in region 0)
+  float vraw[QC];
+  if (nvalid) {
+    ld_seg<QC>(vb + nr * rowstride + nq * QC, vraw);
+  } else {
+#pragma unroll
+    for (int j = 0; j < QC; ++j) vraw[j] = 0.f;
+  }
+
+  // operands, scan layout: each thread owns channel sc of rows sp*RPP ..
+  // (the exact path keeps raw q, k in regions 1, 0 for its staging)
+  const float eg_gamma = __expf(gamma);
+  if (sp == 0) wEG[sc] = eg_gamma;
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const int r = sp * RPP + j;
+    const float kh = ld_f(r0 + r * L::LDR + sc) * s_rk[r];
+    const float qh = ld_f(r1 + r * L::LDR + sc) * s_rq[r];
+    const float eg = __expf(G[j]);
+    st_f(r3 + sc * L::LDT + r, kh * eg);           // (K o e^G)^T
+    st_f(wQG + r * D + sc, qh * eg);
+    float ekt;
+    if (!exact) {
+      const float eng = __expf(-G[j]);
+      st_f(r0 + r * L::LDR + sc, kh * eg);         // K o e^G
+      st_f(r1 + r * L::LDR + sc, qh * eg);         // Q o e^G
+      st_f(r2 + r * L::LDR + sc, kh * eng);        // K o e^-G
+      ekt = eg_gamma * eng;
+    } else {
+      ekt = __expf(gamma - G[j]);
+    }
+    st_f(wKT + sc * kC + r, kh * ekt);             // (K o e^(gamma-G))^T
+  }
+  __syncthreads();
+
+  // ---- phase 3: A (strict lower, x beta_r) and P (lower) -------------------
+  // Tiles are computed transposed (A^T, P^T) so each lane's 4 accumulator
+  // rows are 4 consecutive columns of A / P: one vector store each.
+  // Block pairs (I, R), I <= R, dealt to waves.
+  const int pairI[4][3] = {{0, 0, 0}, {0, 1, 1}, {1, 2, -1}, {2, 3, -1}};
+  const int pairR[4][3] = {{0, 1, 2}, {3, 1, 2}, {3, 2, -1}, {3, 3, -1}};
+  f32x4_t accA[3], accP[3];
+  if (!exact) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      accA[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accP[p] = accA[p];
+      const int I = pairI[wave][p], Rb = pairR[wave][p];
+      if (I < 0) continue;
+#pragma unroll
+      for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+        const auto a = frag_at<T>(r2, L::LDR, I * 16, ks, lane);    // K o e^-G, rows I
+        const auto bk = frag_at<T>(r0, L::LDR, Rb * 16, ks, lane);  // K o e^G, rows R
+        const auto bq = frag_at<T>(r1, L::LDR, Rb * 16, ks, lane);  // Q o e^G, rows R
+        accA[p] = M::mma(a, bk, accA[p]);
+        accP[p] = M::mma(a, bq, accP[p]);
+      }
+    }
+  } else {
+    // Exact path: each entry from its own exponent difference (<= 0), with
+    // G, k^, q^ staged through region 2 in blocks of 16 channels.
+    constexpr int NE = (kC * (kC + 1) / 2 + kThreads - 1) / kThreads;
+    float ea[NE], ep[NE];
+    int er[NE], ei[NE];
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+      const int e = tid + m * kThreads;
+      int r = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
+      while ((r + 1) * (r + 2) / 2 <= e) ++r;
+      while (r * (r + 1) / 2 > e) --r;
+      er[m] = e < kC * (kC + 1) / 2 ? r : -1;
+      ei[m] = e - r * (r + 1) / 2;
+      ea[m] = 0.f; ep[m] = 0.f;
+    }
+    float* stG = reinterpret_cast<float*>(r2);
+    float* stK = stG + kC * 16;
+    float* stQ = stK + kC * 16;
+    for (int cb = 0; cb < D / 16; ++cb) {
+      if (sc / 16 == cb) {
+#pragma unroll
+        for (int j = 0; j < RPP; ++j) {
+          const int r = sp * RPP + j;
+          stG[r * 16 + sc % 16] = G[j];
+          stK[r * 16 + sc % 16] = ld_f(r0 + r * L::LDR + sc) * s_rk[r];
+          stQ[r * 16 + sc % 16] = ld_f(r1 + r * L::LDR + sc) * s_rq[r];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < NE; ++m) {
+        if (er[m] < 0) continue;
+        const int r = er[m], i = ei[m];
+        for (int c = 0; c < 16; ++c) {
+          const float e = __expf(stG[r * 16 + c] - stG[i * 16 + c]);
+          const float ki = stK[i * 16 + c] * e;
+          ea[m] += stK[r * 16 + c] * ki;
+          ep[m] += stQ[r * 16 + c] * ki;
+        }
+      }
+      __syncthreads();
+    }
+    // scatter into the same places the MFMA path writes
+    float* sA = reinterpret_cast<float*>(r1);
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+      if (er[m] < 0) continue;
+      const int r = er[m], i = ei[m];
+      sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[m] : 0.f;
+      st_f(wP + r * kC + i, ep[m]);
+    }
+  }
+  if (!exact) {
+    __syncthreads();  // all reads of regions 0..2 done; region 1 becomes A
+    float* sA = reinterpret_cast<float*>(r1);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int I = pairI[wave][p], Rb = pairR[wave][p];
+      if (I < 0) continue;
+      const int r = Rb * 16 + (lane & 15);
+      const int i0 = I * 16 + 4 * (lane >> 4);
+      const float br = s_beta[r];
+      float a4[4], p4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a4[j] = (i0 + j < r) ? br * accA[p][j] : 0.f;
+        p4[j] = (i0 + j <= r) ? accP[p][j] : 0.f;
+      }
+      *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+      st4(wP + r * kC + i0, p4[0], p4[1], p4[2], p4[3]);
+    }
+  }
+  // zeros of P above the diagonal (the MFMA path already wrote the upper
+  // triangles of the diagonal blocks)
+  for (int e = tid; e < kC * kC; e += kThreads) {
+    const int r = e >> 6, i = e & 63;
+    if (i > r && (exact || (i >> 4) > (r >> 4))) st_f(wP + r * kC + i, 0.f);
+  }
+  // V^T into region 0 (K o e^G row-major is dead now)
+#pragma unroll
+  for (int j = 0; j < QC; ++j) st_f(r0 + (nq * QC + j) * L::LDT + nr, vraw[j]);
+  __syncthreads();
+
+  // ---- phase 4: T = (I + A)^-1 in fp32 --------------------------------------
+  const float* sA = reinterpret_cast<const float*>(r1);
+  float* sT = reinterpret_cast<float*>(r2);
+  if (wave == 0) {
+    // diagonal 16x16 blocks by forward substitution; lane = (block, column)
+    const int b = lane >> 4, col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == col) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= sA[(b * 16 + r) * L::LDA + b * 16 + i] * x[i];
+      x[r] = acc;
+      sT[(b * 16 + r) * L::LDA + b * 16 + col] = acc;
+    }
+  }
+  __syncthreads();
+  // off-diagonal blocks by distance: T_RI = -T_RR sum_(J=I..R-1) A_RJ T_JI
+  for (int dist = 1; dist < 4; ++dist) {
+    if (wave < 4 - dist) {
+      const int I = wave, Rb = wave + dist;
+      const int rr = lane >> 2, cc = (lane & 3) * 4;
+      float m4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int J = I; J < Rb; ++J) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float a = sA[(Rb * 16 + rr) * L::LDA + J * 16 + kk];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) m4[j] += a * sT[(J * 16 + kk) * L::LDA + I * 16 + cc + j];
+        }
+      }
+      float* mscr = scratch + wave * 256;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mscr[rr * 16 + cc + j] = m4[j];
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      float t4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const float tr = sT[(Rb * 16 + rr) * L::LDA + Rb * 16 + kk];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t4[j] -= tr * mscr[kk * 16 + cc + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sT[(Rb * 16 + rr) * L::LDA + I * 16 + cc + j] = t4[j];
+    }
+    __syncthreads();
+  }
+  // T Diag(beta) in the MFMA type, lower triangle only, into region 1
+  T* sTb = r1;
+  for (int e = tid; e < kC * kC; e += kThreads) {
+    const int r = e >> 6, i = e & 63;
+    const float val = i <= r ? sT[r * L::LDA + i] * s_beta[i] : 0.f;
+    st_f(sTb + r * L::LDT + i, val);
+  }
+  __syncthreads();
+
+  // ---- phase 5: U = T Diag(beta) V and Wk^T = (K o e^G)^T (T Diag(beta))^T --
+  {
+    const int rb = wave;  // this wave's 16 rows of T
+    typename M::frag tb[kC / M::KSTEP];
+#pragma unroll
+    for (int ks = 0; ks < kC / M::KSTEP; ++ks) tb[ks] = frag_at<T>(sTb, L::LDT, rb * 16, ks, lane);
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      f32x4_t u = {0.f, 0.f, 0.f, 0.f}, wk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kC / M::KSTEP; ++ks) {
+        u = M::mma(tb[ks], frag_at<T>(r0, L::LDT, nb * 16, ks, lane), u);   // B = V^T rows
+        wk = M::mma(frag_at<T>(r3, L::LDT, nb * 16, ks, lane), tb[ks], wk);  // A = KG^T rows
+      }
+      // u: rows r = rb*16 + 4*(lane/16) + j, column n = nb*16 + lane%16  -> U^T[n][r..r+3]
+      const int n = nb * 16 + (lane & 15), r4 = rb * 16 + 4 * (lane >> 4);
+      st4(wUT + n * kC + r4, u[0], u[1], u[2], u[3]);
+      // wk: rows c = nb*16 + 4*(lane/16) + j of Wk^T, column r = rb*16 + lane%16
+      const int c4 = nb * 16 + 4 * (lane >> 4), r = rb * 16 + (lane & 15);
+      st4(wWN + r * D + c4, -wk[0], -wk[1], -wk[2], -wk[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: sequential state pass over one sequence's chunks for one d_v slice.
+template <typename T, int D, int WS>
+__global__ __launch_bounds__(kThreads) void kda_state_pass(
+    const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
+    int nseg, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
+    float* __restrict__ fin, float* __restrict__ ckpt, int64_t ckpt_every, int64_t nckpt,
+    float scale, T* __restrict__ o) {
+  using M = Mma<T>;
+  using R = Rec<T, D>;
+  constexpr int NB = WS / 16;          // 16-column blocks in the slice
+  constexpr int CBW = D / 16 / 4;      // 16-row blocks of S per wave
+  constexpr int KD = D / M::KSTEP;     // k-steps over d_k
+  constexpr int KC = kC / M::KSTEP;    // k-steps over the chunk
+  constexpr int LDS_S = D + 8, LDS_W = kC + 8;
+  __shared__ __align__(16) char lds_raw[(WS * LDS_S + WS * LDS_W) * sizeof(T)];
+  T* sSt = reinterpret_cast<T*>(lds_raw);                // S^T slice [n][c]
+  T* sWt = sSt + WS * LDS_S;                             // W^T slice [n][i]
+
+  // XCD-aware placement: workgroups of one (sequence, head) share id mod 8.
+  const int id = blockIdx.x;
+  const int nh = (id & 7) + 8 * (id / (8 * nslice));
+  const int slice = (id >> 3) % nslice;
+  if (nh >= NH) return;
+  const int seq = nh / H, h = nh % H;
+  const int n0 = slice * WS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // This sequence's chunks inside the segment's slot range [s0, s1).  The
+  // state enters from init_state at the sequence's first chunk, otherwise from
+  // the carry buffer the previous segment left; it leaves to final_state after
+  // the last chunk, otherwise to the carry buffer.
+  const SeqSpan sp = seq_span(gm, seq);
+  const int64_t nrec = s1 - s0;
+  if (sp.c0 == sp.c1) {  // empty sequence: final = init, once
+    if (seg != (int)min<int64_t>(sp.c0 / kSegSlots, nseg - 1) || fin == nullptr) return;
+    const int64_t base = (int64_t)nh * D * D;
+    for (int e = threadIdx.x; e < D * WS; e += kThreads) {
+      const int64_t idx = base + (int64_t)(e / WS) * D + n0 + e % WS;
+      fin[idx] = init ? init[idx] : 0.f;
+    }
+    return;
+  }
+  const int64_t slot0 = max(sp.c0, s0), slot1 = min(sp.c1, s1);
+  if (slot0 >= slot1) return;
+  const float* src = slot0 == sp.c0 ? init : carry;
+  float* dst = slot1 == sp.c1 ? fin : carry;
+
+  // state accumulators: wave owns rows (cb = wave*CBW + i) x all NB column blocks
+  f32x4_t S[CBW][NB];
+  const int64_t sbase = (int64_t)nh * D * D;
+#pragma unroll
+  for (int i = 0; i < CBW; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = (wave * CBW + i) * 16 + 4 * (lane >> 4) + j;
+        const int n = n0 + nb * 16 + (lane & 15);
+        S[i][nb][j] = src ? src[sbase + (int64_t)c * D + n] : 0.f;
+      }
+
+  for (int64_t slot = slot0; slot < slot1; ++slot) {
+    const char* rec = ws + ((int64_t)h * nrec + (slot - s0)) * R::BYTES;
+    const T* QG = reinterpret_cast<const T*>(rec) + R::QG;
+    const T* KT = reinterpret_cast<const T*>(rec) + R::KT;
+    const T* WN = reinterpret_cast<const T*>(rec) + R::WN;
+    const T* UT = reinterpret_cast<const T*>(rec) + R::UT;
+    const T* P = reinterpret_cast<const T*>(rec) + R::P;
+    const float* EG = reinterpret_cast<const float*>(rec + R::BYTES_T);
+    const int64_t off = (slot - sp.c0) * kC;  // first token of the chunk within the sequence
+    const int64_t tok0 = sp.tok0 + off;
+    const int len = (int)min<int64_t>(kC, sp.ntok - off);
+
+    // (a) S -> LDS as S^T in the MFMA type
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int c4 = (wave * CBW + i) * 16 + 4 * (lane >> 4);
+        const int n = nb * 16 + (lane & 15);
+        st4(sSt + n * LDS_S + c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
+      }
+    __syncthreads();
+
+    // (b) W = U + (-Wk) S  (rows of this wave's 16-row block) and O^T = S^T (Q o e^G)^T
+    f32x4_t W[NB], O[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = n0 + nb * 16 + (lane & 15);
+      W[nb] = ld4(UT + (int64_t)n * kC + wave * 16 + 4 * (lane >> 4));
+      O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      const auto wn = frag_at<T>(WN, D, wave * 16, ks, lane);
+      const auto qg = frag_at<T>(QG, D, wave * 16, ks, lane);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const auto s = frag_at<T>(sSt, LDS_S, nb * 16, ks, lane);
+        W[nb] = M::mma(wn, s, W[nb]);
+        O[nb] = M::mma(s, qg, O[nb]);
+      }
+    }
+    // (c) W -> LDS as W^T
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = nb * 16 + (lane & 15);
+      st4(sWt + n * LDS_W + wave * 16 + 4 * (lane >> 4), W[nb][0], W[nb][1], W[nb][2], W[nb][3]);
+    }
+    __syncthreads();
+
+    // (d) O^T += W^T P^T ;  S = Diag(e^gamma) S + K~^T W
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) {
+      const auto p = frag_at<T>(P, kC, wave * 16, ks, lane);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const auto wf = frag_at<T>(sWt, LDS_W, nb * 16, ks, lane);
+        O[nb] = M::mma(wf, p, O[nb]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+      const int cb = wave * CBW + i;
+      const f32x4_t eg = ld4(EG + cb * 16 + 4 * (lane >> 4));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[i][nb][j] *= eg[j];
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {
+        const auto kt = frag_at<T>(KT, kC, cb * 16, ks, lane);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const auto wf = frag_at<T>(sWt, LDS_W, nb * 16, ks, lane);
+          S[i][nb] = M::mma(kt, wf, S[i][nb]);
+        }
+      }
+    }
+
+    // (e) output rows of this wave's block: O^T[n][r] -> o[tok0 + r][h][n0 + n]
+    const int r = wave * 16 + (lane & 15);
+    if (r < len) {
+      T* orow = o + ((tok0 + r) * H + h) * D + n0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        st4(orow + nb * 16 + 4 * (lane >> 4), scale * O[nb][0], scale * O[nb][1],
+            scale * O[nb][2], scale * O[nb][3]);
+    }
+
+    // (f) checkpoint after every ckpt_every tokens (dense, chunk-aligned)
+    if (ckpt != nullptr) {
+      const int64_t done = off + len;  // tokens of this sequence so far
+      if (len == kC && done % ckpt_every == 0) {
+        const int64_t jslot = done / ckpt_every - 1;
+        float* dst = ckpt + (((int64_t)seq * nckpt + jslot) * H + h) * (int64_t)D * D;
+#pragma unroll
+        for (int i = 0; i < CBW; ++i)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int c = (wave * CBW + i) * 16 + 4 * (lane >> 4) + j;
+              dst[(int64_t)c * D + n0 + nb * 16 + (lane & 15)] = S[i][nb][j];
+            }
+      }
+    }
+    // No barrier here: the next chunk's sSt writes follow this chunk's
+    // second barrier (after every wave read sSt), and its sWt writes follow
+    // the next chunk's first barrier (after every wave read sWt).
+  }
+
+  if (dst != nullptr) {
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = (wave * CBW + i) * 16 + 4 * (lane >> 4) + j;
+          dst[sbase + (int64_t)c * D + n0 + nb * 16 + (lane & 15)] = S[i][nb][j];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: workspace plan and launches.
+//
+// Chunk slots are processed in segments of at most kSegSlots slots: K1 fills
+// the segment's records, then K2 advances every sequence through its chunks
+// inside the segment.  The workspace therefore holds one segment's records
+// (bounded for any T), the fp32 states carried between segments, and the
+// varlen chunk map.
+struct Plan {
+  int64_t slot_bound;   // upper bound on chunk slots (dense exact, varlen bound)
+  int64_t seg_slots;    // slots per segment
+  int64_t rec_bytes;
+  int64_t rec_total;    // bytes of one segment's records
+  int64_t carry_bytes;  // fp32 states carried between segments
+  int64_t map_bytes;    // varlen: sanitised cu_seqlens + chunk offsets
+};
+
+int64_t rec_bytes_for(const kda_desc_t& d) {
+  if (d.dtype == KDA_DTYPE_BF16)
+    return d.dk == 128 ? Rec<bf16, 128>::BYTES : Rec<bf16, 64>::BYTES;
+  return d.dk == 128 ? Rec<float, 128>::BYTES : Rec<float, 64>::BYTES;
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+Plan make_plan(const kda_desc_t& d, bool varlen) {
+  Plan p{};
+  const int64_t T = d.seqlen;
+  p.slot_bound = varlen ? (T + (int64_t)(kC - 1) * d.num_seqs) / kC
+                        : (int64_t)d.batch * ((T + kC - 1) / kC);
+  p.seg_slots = std::min<int64_t>(p.slot_bound, kSegSlots);
+  p.rec_bytes = rec_bytes_for(d);
+  p.rec_total = p.seg_slots * d.heads * p.rec_bytes;
+  p.carry_bytes = p.slot_bound > kSegSlots
+                      ? (int64_t)d.num_seqs * d.heads * d.dk * d.dv * 4 : 0;
+  p.map_bytes = varlen ? 2 * align256(((int64_t)d.num_seqs + 1) * 4) : 0;
+  return p;
+}
+
+template <typename T, int D>
+hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                     const float* g, const float* beta, const float* init_state,
+                     const int32_t* cu, void* o, float* final_state, float* ckpt, char* ws,
+                     hipStream_t stream) {
+  const bool varlen = cu != nullptr;
+  const Plan p = make_plan(d, varlen);
+  const int H = d.heads, NH = d.num_seqs * d.heads;
+  char* recs = ws;
+  float* carry = p.carry_bytes ? reinterpret_cast<float*>(ws + p.rec_total) : nullptr;
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.rec_total + p.carry_bytes);
+  int32_t* cu_s = chunk_off + (p.map_bytes / 2) / 4;  // sanitised cu_seqlens
+  constexpr int WS = 32;  // d_v slice per K2 workgroup
+  const int nslice = D / WS;
+  const int nhpad = (NH + 7) / 8 * 8;
+  const int k1_lds = K1Lds<T, D>::BYTES;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kda_intra_chunk<T, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t nck = d.ckpt_every > 0 ? d.seqlen / d.ckpt_every : 0;
+  ChunkGeom gm{nullptr, nullptr, d.seqlen, (d.seqlen + kC - 1) / kC, d.num_seqs};
+  if (varlen) {
+    hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, stream, cu, d.num_seqs,
+                       d.seqlen, cu_s, chunk_off);
+    gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
+  }
+  const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + kSegSlots - 1) / kSegSlots;
+  for (int64_t s = 0; s < nseg; ++s) {
+    const int64_t s0 = s * kSegSlots, s1 = std::min<int64_t>(p.slot_bound, s0 + kSegSlots);
+    if (s1 > s0)
+      hipLaunchKernelGGL((kda_intra_chunk<T, D>), dim3((unsigned)(s1 - s0), H), dim3(kThreads),
+                         k1_lds, stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H,
+                         s0, s1 - s0, d.qk_l2norm, recs);
+    hipLaunchKernelGGL((kda_state_pass<T, D, WS>), dim3(nhpad * nslice), dim3(kThreads), 0,
+                       stream, recs, gm, H, s0, s1, (int)s, (int)nseg, nslice, NH, init_state,
+                       carry, final_state, ckpt, d.ckpt_every, nck, d.scale, (T*)o);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t chunk_workspace_bytes(const kda_desc_t& d) {
+  // Whether cu_seqlens will be passed is not known here: size for the larger
+  // of the two layouts (they differ only in the slot bound and the map).
+  const Plan pv = make_plan(d, true), pd = make_plan(d, false);
+  const int64_t a = pv.rec_total + pv.carry_bytes + pv.map_bytes;
+  const int64_t b = pd.rec_total + pd.carry_bytes + pd.map_bytes;
+  return (size_t)(a > b ? a : b);
+}
+
+hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const float* init_state,
+                            const int32_t* cu_seqlens, void* o, float* final_state,
+                            float* state_ckpt, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const bool bf = d.dtype == KDA_DTYPE_BF16;
+  if (d.dk == 128)
+    return bf ? run_typed<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                     final_state, state_ckpt, ws, stream)
+              : run_typed<float, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                      final_state, state_ckpt, ws, stream);
+  return bf ? run_typed<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state,
+                                  state_ckpt, ws, stream)
+            : run_typed<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                   final_state, state_ckpt, ws, stream);
 }
 
 }  // namespace kda

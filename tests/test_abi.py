@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: the library loads, exports exactly what
+include/kda.h declares, and rejects invalid calls on the host (before any
+launch) with the documented status."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_54_amd as K
+from gated_delta_rule_54_amd import kda as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    out = subprocess.check_output(["nm", "-D", "--defined-only", B.LIB_PATH], text=True)
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == _declared(), (exported, _declared())
+    assert sorted(B.EXPORTED) == _declared()
+
+
+def test_abi_version_and_strings():
+    lib = K.load_library()
+    assert lib.kda_abi_version() == 1
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.kda_status_string(99) == b"KDA_STATUS_UNKNOWN"
+
+
+FAKE = 0x10000  # an aligned non-null address: validation fails before it is touched
+
+
+def _desc(**kw):
+    base = dict(batch=1, num_seqs=1, seqlen=128, heads=2, dk=64, dv=64, dtype=0)
+    base.update(kw)
+    return K.make_desc(**base)
+
+
+def _call_chunk(desc, *, q=FAKE, o=FAKE + 0x100, ws=None, ws_bytes=None, cu=None, ckpt=None,
+                misalign=None, shift=4):
+    """Every call here must fail validation: the fake addresses are never
+    dereferenced because nothing is launched."""
+    lib = K.load_library()
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc))
+    ptrs = dict(q=q, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=o)
+    if misalign:
+        ptrs[misalign] += shift
+    wsp = FAKE if ws is None else ws
+    wsb = need if ws_bytes is None else ws_bytes
+    return lib.kda_chunk_fwd(ctypes.byref(desc), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"],
+                             ptrs["beta"], None, cu, ptrs["o"], None, ckpt, wsp, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96, dv=96), B.KDA_ERR_UNSUPPORTED),
+    (dict(dk=64, dv=128), B.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=32), B.KDA_ERR_UNSUPPORTED),
+    (dict(heads=0), B.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.KDA_ERR_INVALID_ARGUMENT),
+    (dict(seqlen=-1), B.KDA_ERR_INVALID_ARGUMENT),
+    (dict(batch=2, num_seqs=1), B.KDA_ERR_INVALID_ARGUMENT),
+    (dict(ckpt_every=100), B.KDA_ERR_INVALID_ARGUMENT),
+    (dict(ckpt_every=96), B.KDA_ERR_INVALID_ARGUMENT),
+])
+def test_chunk_desc_errors(kw, status):
+    lib = K.load_library()
+    st = _call_chunk(_desc(**kw))
+    assert st == status, lib.kda_last_error()
+    assert lib.kda_last_error() != b""
+
+
+def test_chunk_pointer_errors():
+    lib = K.load_library()
+    assert _call_chunk(_desc(), q=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert b"q is NULL" in lib.kda_last_error()
+    assert _call_chunk(_desc(), misalign="q") == B.KDA_ERR_INVALID_ARGUMENT
+    assert b"q is not 16-byte aligned" in lib.kda_last_error()
+    assert _call_chunk(_desc(), misalign="g", shift=2) == B.KDA_ERR_INVALID_ARGUMENT
+    assert b"g is not 4-byte aligned" in lib.kda_last_error()
+    assert _call_chunk(_desc(), o=FAKE) == B.KDA_ERR_INVALID_ARGUMENT  # o aliases q
+    assert _call_chunk(_desc(), ws_bytes=16) == B.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert _call_chunk(_desc(ckpt_every=64)) == B.KDA_ERR_INVALID_ARGUMENT  # ckpt buffer missing
+    assert _call_chunk(_desc(), ckpt=FAKE) == B.KDA_ERR_INVALID_ARGUMENT    # ckpt without every
+    # varlen needs batch == 1 and no checkpoints
+    assert _call_chunk(_desc(batch=2, num_seqs=3), cu=FAKE) == B.KDA_ERR_INVALID_ARGUMENT
+    assert _call_chunk(_desc(num_seqs=3, ckpt_every=64), cu=FAKE, ckpt=FAKE) == \
+        B.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes():
+    lib = K.load_library()
+    ws = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(**kw)))
+    assert ws(dk=96, dv=96) == 0 and b"supported" in lib.kda_last_error()
+    small, big = ws(seqlen=64), ws(seqlen=8192)
+    assert 0 < small < big
+    # a 1M-token dense problem is processed in bounded time segments
+    assert ws(seqlen=1 << 20, dk=128, dv=128, dtype=1, heads=32) == \
+        ws(seqlen=1 << 16, dk=128, dv=128, dtype=1, heads=32) + 32 * 128 * 128 * 4
+    # the varlen bound leaves room for one partial chunk per sequence:
+    # 640 packed tokens in 10 sequences need up to (640 + 63*10)/64 = 19 slots
+    assert ws(seqlen=640, num_seqs=10) > ws(seqlen=640, num_seqs=1)
+
+
+def test_decode_errors():
+    lib = K.load_library()
+
+    def call(desc, **ptrs):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FAKE + 0x100)
+        p.update(ptrs)
+        return lib.kda_decode_step(ctypes.byref(desc), p["q"], p["k"], p["v"], p["g"],
+                                   p["beta"], p["state"], p["o"], None)
+
+    assert call(_desc(dk=32, dv=32)) == B.KDA_ERR_UNSUPPORTED
+    assert call(_desc(), state=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(_desc(), o=FAKE) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(_desc(), beta=FAKE + 2) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(_desc(), state=FAKE + 8) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(_desc(num_seqs=-1)) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(_desc(num_seqs=0)) == B.KDA_OK  # nothing to do, nothing launched
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        B.load_library(str(tmp_path / "missing.so"))
