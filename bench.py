@@ -1,0 +1,197 @@
+"""Benchmark of the KDA operator on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+One step is one chunkwise prefill (kda_chunk_fwd: q/k L2 norm, in-chunk
+gate prefix sum, intra-chunk UT transform, inter-chunk state pass) over the
+B=1, H=32, T=8192, d=128 bf16 workload.  The step is timed with HIP events on
+the stream the library launches on, K steps back to back between two device
+synchronisations; inputs are resident in HBM before timing starts.  The
+decode workload (256 sequences x 32 heads, d=128, 1024 sequential steps) is
+timed the same way and reported in the "decode" object.  The CPU oracle is
+timed on a bounded sample of the same prefill workload on this host's cores.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_delta_rule_54_amd import (chunk_fwd_workspace_bytes, kda_chunk_fwd,  # noqa: E402
+                                     kda_decode_step, make_desc)
+from gated_delta_rule_54_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+# Algorithmic (compulsory) bytes and flops per token-head, d = 128:
+#   prefill: q, k, v bf16 (3 x 256) + g fp32 (512) + beta (4) + o bf16 (256)
+#   decode:  prefill I/O + the fp32 state read and written (2 x 65536)
+#   prefill flops: 6 d^2 + 3 C d + C^2 per token-head at C = 64 (the
+#   chunkwise FLOP model of the pages; the dense count of the kernels'
+#   products is 6 d^2 + 10 C d + C^2 / 3)
+PREFILL_BYTES_PER_TH = 3 * 256 + 512 + 4 + 256
+DECODE_BYTES_PER_TH = PREFILL_BYTES_PER_TH + 2 * 128 * 128 * 4
+PREFILL_FLOPS_PER_TH = 6 * 128 ** 2 + 3 * 64 * 128 + 64 ** 2
+DECODE_FLOPS_PER_TH = 7 * 128 ** 2
+
+
+def _events():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_prefill(steps: int, warmup: int):
+    w = W.PREFILL_8K
+    inp = W.workload_inputs(w, "cuda")
+    B, T, H, d = inp["q"].shape
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    desc = make_desc(batch=B, num_seqs=B, seqlen=T, heads=H, dk=d, dv=d, dtype=w.dtype)
+    ws = torch.empty(chunk_fwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["init_state"],
+                      out=o, final_state=fs, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    th = B * T * H
+    sec = ms * 1e-3
+    achieved_gbs = PREFILL_BYTES_PER_TH * th / sec / 1e9
+    achieved_tf = PREFILL_FLOPS_PER_TH * th / sec / 1e12
+    return dict(w=w, inp=inp, ms=ms, wall=wall, tokens=B * T, token_heads=th,
+                achieved_gbs=achieved_gbs, achieved_tflops=achieved_tf,
+                ws_bytes=ws.numel())
+
+
+def bench_decode(warmup: int):
+    w = W.DECODE_256
+    N, H, d = w.num_seqs, w.heads, w.dk
+    gen = W.make_generator(w.seed, "cuda")
+    state = W.decode_initial_state(num_seqs=N, heads=H, dk=d, dv=d, gen=gen, device="cuda")
+    xs = [W.decode_step_inputs(num_seqs=N, heads=H, dk=d, dv=d, dtype=w.dtype, gen=gen,
+                               device="cuda") for _ in range(w.steps)]
+    o = torch.empty((N, H, d), dtype=w.dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    scratch = state.clone()  # warm-up runs on a copy; the timed run starts from the real state
+    for i in range(warmup):
+        x = xs[i]
+        kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], scratch, out=o, stream=stream)
+    del scratch
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for x in xs:
+        kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state, out=o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    sec_step = ms_total * 1e-3 / w.steps
+    th = N * H
+    achieved_gbs = DECODE_BYTES_PER_TH * th / sec_step / 1e9
+    return dict(w=w, ms_step=sec_step * 1e3, tokens_per_s=N * w.steps / (ms_total * 1e-3),
+                achieved_gbs=achieved_gbs,
+                achieved_tflops=DECODE_FLOPS_PER_TH * th / sec_step / 1e12)
+
+
+def cpu_baseline(inp, heads_sample: int):
+    """Time the fp64 oracle on a bounded sample of the prefill workload: all
+    T tokens of the first `heads_sample` heads (one thread per head)."""
+    sys.path.insert(0, os.path.join(ROOT))
+    from oracle import oracle as O
+    O.build()
+    sl = lambda x: x[:, :, :heads_sample].contiguous().cpu()
+    q, k, v, g, b = (sl(inp[key]) for key in ("q", "k", "v", "g", "beta"))
+    threads = min(O.default_threads(), heads_sample)
+    t0 = time.perf_counter()
+    O.kda_fwd(q, k, v, g, b, nthreads=threads)
+    dt = time.perf_counter() - t0
+    B, T, H, _ = q.shape
+    # tokens/s of the whole 32-head problem at this per-head rate and thread count
+    full_heads = inp["q"].shape[2]
+    return dict(value=B * T * heads_sample / full_heads / dt, unit="tokens/s", cores=threads,
+                kind="oracle",
+                sample=f"all {T} tokens of {heads_sample} of {full_heads} heads "
+                       f"(fp64, {dt:.1f} s wall); value scaled to all heads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are "
+                                   "not part of this build (--gpus must be 1)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    pf = bench_prefill(args.steps, args.warmup)
+    dc = bench_decode(min(args.warmup, 8))
+    w = pf["w"]
+    value = pf["tokens"] / (pf["ms"] * 1e-3)
+    line = {
+        "metric": "KDA prefill tokens/s (H32,d128) + decode tok/s; % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k,v ~ N(0,1) bf16, g = logsigmoid(N(0,1)+3), "
+                "beta = sigmoid(N(0,1)))",
+        "config": {"workload": "prefill B=1 H=32 T=8192 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/"
+                               "state, chunk 64", "global_batch": 1, "seq_len": 8192,
+                   "heads": 32, "head_dim": 128, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": pf["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": pf["achieved_gbs"] / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "kernel": "kda_chunk_fwd (intra-chunk + state-pass launches of one call)",
+                     "bytes_per_token_head": PREFILL_BYTES_PER_TH,
+                     "mfma_tflops": pf["achieved_tflops"],
+                     "mfma_frac": pf["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS},
+        "decode": {"workload": dc["w"].describe(), "value": dc["tokens_per_s"],
+                   "unit": "tokens/s", "ms_per_step": dc["ms_step"],
+                   "roofline": {"bound": "hbm", "achieved": dc["achieved_gbs"],
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dc["achieved_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                                "kernel": "decode_step_kernel<bf16,128>",
+                                "bytes_per_token_head": DECODE_BYTES_PER_TH}},
+        "wall_s_prefill_loop": pf["wall"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pf["inp"], args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,12 +120,12 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
   if ((d.ckpt_every > 0) != (state_ckpt != nullptr))
     return fail(KDA_ERR_INVALID_ARGUMENT,
                 "state_ckpt must be given exactly when ckpt_every > 0");
-  // q, k, v, o rows are moved with 16-byte vector accesses; everything else
-  // with 4-byte scalar accesses.
+  // q, k, v, g, o rows are moved with vector accesses (16-byte aligned rows);
+  // everything else with 4-byte scalar accesses.
   const bool has_tokens = d.seqlen > 0;
   const void* need[] = {q, k, v, g, beta, o};
   const char* names[] = {"q", "k", "v", "g", "beta", "o"};
-  const uintptr_t align[] = {16, 16, 16, 4, 4, 16};
+  const uintptr_t align[] = {16, 16, 16, 16, 4, 16};
   for (int i = 0; i < 6; ++i) {
     if (has_tokens && !need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
     if (need[i] && !aligned(need[i], align[i]))

@@ -54,6 +54,7 @@
 #include <hip/hip_bf16.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "kda_internal.h"
 
@@ -64,7 +65,7 @@ constexpr int kC = 64;            // chunk length
 constexpr int kThreads = 256;     // 4 waves
 constexpr float kNormEps = 1e-6f;
 constexpr float kFastDecayBound = -80.f;
-constexpr int64_t kSegSlots = 1024;    // chunk slots per K1/K2 launch pair (65536 tokens)
+constexpr int64_t kSegSlotsDefault = 1024;  // chunk slots per K1/K2 launch pair
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -108,6 +109,22 @@ __device__ __forceinline__ f32x4_t ld4(const bf16* p) {
   return f32x4_t{bf_val(u.x & 0xffffu), bf_val(u.x >> 16), bf_val(u.y & 0xffffu),
                  bf_val(u.y >> 16)};
 }
+// Four consecutive elements kept as raw bits until use (a prefetch must not
+// convert at load time: that would wait for the load).
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ f32x4_t get() const { return f32x4_t{v.x, v.y, v.z, v.w}; }
+};
+template <> struct Raw4<bf16> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ f32x4_t get() const {
+    return f32x4_t{bf_val(v.x & 0xffffu), bf_val(v.x >> 16), bf_val(v.y & 0xffffu),
+                   bf_val(v.y >> 16)};
+  }
+};
 // Load N consecutive elements (16-byte aligned, N a multiple of 8) as floats.
 template <int N>
 __device__ __forceinline__ void ld_seg(const float* p, float* out) {
@@ -278,10 +295,15 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restr
 
 // ---------------------------------------------------------------------------
 // K1: intra-chunk transform.  LDS holds four equal regions, reused by phase:
-//   region 0: raw k -> K o e^G (row-major)          -> V^T       (U phase)
-//   region 1: raw q -> Q o e^G (row-major)          -> A (fp32)  -> T Diag(beta) (MFMA type)
+//   region 0: K o e^G (row-major) [exact path: raw k]  -> V^T           (U phase)
+//   region 1: Q o e^G (row-major) [exact path: raw q]  -> A (fp32)     -> T Diag(beta)
 //   region 2: K o e^-G (row-major) / exact-path staging -> T (fp32)
 //   region 3: (K o e^G)^T
+// Thread layouts: "row" (tid = 4r + quarter) for the q/k norms, and
+// "channel pair" (tid = cp + (D/2) part): two adjacent channels of RPP
+// consecutive rows, for everything per-element.  A channel-pair thread holds
+// its rows contiguously, so the transposed buffers ((K o e^G)^T, V^T, K~^T)
+// are written 8 rows at a time with 16-byte stores.
 template <typename T, int D>
 struct K1Lds {
   static constexpr int LDR = D + 8;        // row-major leading dim (elements)
@@ -293,9 +315,53 @@ struct K1Lds {
   static constexpr int FP = kC * LDA * 4;                     // fp32 A / T tile
   static constexpr int REG = ((MX > FP ? MX : FP) + 255) / 256 * 256;
   static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
-  static constexpr int NPART = kThreads / D;  // scan parts per channel
+  static constexpr int NCP = D / 2;               // channel pairs
+  static constexpr int NPART = kThreads / NCP;    // row parts
+  static constexpr int RPP = kC / NPART;          // rows per part (16 or 8)
   static constexpr int BYTES = 4 * REG + 4096 /*scratch*/ + 3 * kC * 4 + 16;
 };
+
+// 16x16 fp32 tile product through MFMA: acc += A[ra.., ka..] * B[kb.., cb..],
+// A and B fp32 in LDS (row-major, leading dim lda / ldb), K = 16.
+__device__ __forceinline__ f32x4_t mm16_f32(const float* A, int lda, const float* B, int ldb,
+                                            f32x4_t acc, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const float a = A[(lane & 15) * lda + ks * 4 + (lane >> 4)];
+    const float b = B[(ks * 4 + (lane >> 4)) * ldb + (lane & 15)];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+// Store a 16x16 accumulator tile (rows 4*(l/16)+j, column l%16) into LDS.
+__device__ __forceinline__ void st_tile_f32(float* C, int ldc, f32x4_t v, float sgn, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) C[(4 * (lane >> 4) + j) * ldc + (lane & 15)] = sgn * v[j];
+}
+
+// Pack 8 values to the MFMA type and store 16 bytes (bf16) / 32 bytes (fp32).
+__device__ __forceinline__ void st8(bf16* p, const float* x) {
+  u32x4_t u;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) u[t] = (uint32_t)bf_bits(x[2 * t]) | ((uint32_t)bf_bits(x[2 * t + 1]) << 16);
+  *reinterpret_cast<u32x4_t*>(p) = u;
+}
+__device__ __forceinline__ void st8(float* p, const float* x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+// Two adjacent elements: load as floats / store from floats.
+__device__ __forceinline__ float2 ld2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ __forceinline__ float2 ld2(const bf16* p) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  return make_float2(bf_val(u & 0xffffu), bf_val(u >> 16));
+}
+__device__ __forceinline__ void st2(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+__device__ __forceinline__ void st2(bf16* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = (uint32_t)bf_bits(a) | ((uint32_t)bf_bits(b) << 16);
+}
 
 // fp32 operands at d = 128 need every VGPR of a one-workgroup-per-CU launch.
 template <typename T, int D>
@@ -309,8 +375,8 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   using L = K1Lds<T, D>;
   using M = Mma<T>;
   using R = Rec<T, D>;
-  constexpr int NPART = L::NPART, RPP = kC / NPART;  // rows per scan part
-  constexpr int QC = D / 4;                          // channels per thread in the norm phase
+  constexpr int NCP = L::NCP, NPART = L::NPART, RPP = L::RPP;
+  constexpr int QC = D / 4;  // channels per thread in the norm layout
   extern __shared__ __align__(16) char smem[];
   T* r0 = reinterpret_cast<T*>(smem);
   T* r1 = reinterpret_cast<T*>(smem + L::REG);
@@ -321,8 +387,10 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   float* s_rq = s_rk + kC;
   float* s_beta = s_rq + kC;
 
-  const int h = blockIdx.y;
-  const int64_t slot = slot_base + blockIdx.x;
+  // heads vary fastest across workgroups: concurrently resident workgroups
+  // then read whole token rows (all heads) of neighbouring tokens
+  const int h = blockIdx.x;
+  const int64_t slot = slot_base + blockIdx.y;
   ChunkLoc loc;
   if (!locate(gm, slot, loc)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -339,100 +407,101 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   T* wP = reinterpret_cast<T*>(rec) + R::P;
   float* wEG = reinterpret_cast<float*>(rec + R::BYTES_T);
 
-  // ---- issue the chunk's global loads ------------------------------------
-  // norm layout: thread = (row nr, quarter nq) covering QC channels
-  const int nr = tid >> 2, nq = tid & 3;
-  const bool nvalid = nr < loc.len;
-  float qraw[QC], kraw[QC];
-  if (nvalid) {
-    ld_seg<QC>(qb + nr * rowstride + nq * QC, qraw);
-    ld_seg<QC>(kb + nr * rowstride + nq * QC, kraw);
-  } else {
-#pragma unroll
-    for (int j = 0; j < QC; ++j) { qraw[j] = 0.f; kraw[j] = 0.f; }
-  }
-  // scan layout: thread = (channel sc, part sp) covering RPP rows
-  const int sc = tid % D, sp = tid / D;
-  float G[RPP];
+  // ---- global loads --------------------------------------------------------
+  // channel-pair layout: channels c0, c0+1 of rows r0p .. r0p+RPP-1
+  const int cp = tid % NCP, part = tid / NCP;
+  const int c0 = 2 * cp, r0p = part * RPP;
+  float2 G[RPP], kk[RPP], qq[RPP], vv[RPP];
 #pragma unroll
   for (int j = 0; j < RPP; ++j) {
-    const int r = sp * RPP + j;
-    G[j] = r < loc.len ? gb[r * rowstride + sc] : 0.f;
+    const int r = r0p + j;
+    const bool ok = r < loc.len;
+    G[j] = ok ? ld2(gb + r * rowstride + c0) : make_float2(0.f, 0.f);
+    kk[j] = ok ? ld2(kb + r * rowstride + c0) : make_float2(0.f, 0.f);
+    qq[j] = ok ? ld2(qb + r * rowstride + c0) : make_float2(0.f, 0.f);
+    vv[j] = ok ? ld2(vb + r * rowstride + c0) : make_float2(0.f, 0.f);
   }
   if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
-
-  // ---- phase 1: row norms; raw q, k into regions 1, 0 ---------------------
+  // row layout for the norms (a second, cache-served read of q and k rows)
   {
+    const int nr = tid >> 2, nq = tid & 3;
     float sq = 0.f, sk = 0.f;
+    if (nr < loc.len) {
+      float xq[QC], xk[QC];
+      ld_seg<QC>(qb + nr * rowstride + nq * QC, xq);
+      ld_seg<QC>(kb + nr * rowstride + nq * QC, xk);
 #pragma unroll
-    for (int j = 0; j < QC; ++j) { sq += qraw[j] * qraw[j]; sk += kraw[j] * kraw[j]; }
+      for (int j = 0; j < QC; ++j) { sq += xq[j] * xq[j]; sk += xk[j] * xk[j]; }
+    }
     sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
     sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
     if (nq == 0) {
       s_rq[nr] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
       s_rk[nr] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
     }
-#pragma unroll
-    for (int j = 0; j < QC; j += 4) {
-      st4(r1 + nr * L::LDR + nq * QC + j, qraw[j], qraw[j + 1], qraw[j + 2], qraw[j + 3]);
-      st4(r0 + nr * L::LDR + nq * QC + j, kraw[j], kraw[j + 1], kraw[j + 2], kraw[j + 3]);
-    }
   }
-  // ---- phase 2: prefix sum of g within the chunk ---------------------------
+  // ---- in-chunk prefix sum of g ---------------------------------------------
 #pragma unroll
-  for (int j = 1; j < RPP; ++j) G[j] += G[j - 1];
-  scratch[sp * D + sc] = G[RPP - 1];
+  for (int j = 1; j < RPP; ++j) { G[j].x += G[j - 1].x; G[j].y += G[j - 1].y; }
+  scratch[part * D + c0] = G[RPP - 1].x;
+  scratch[part * D + c0 + 1] = G[RPP - 1].y;
   __syncthreads();
-  float off = 0.f, gamma = 0.f;
+  float2 off = make_float2(0.f, 0.f), gamma = make_float2(0.f, 0.f);
 #pragma unroll
   for (int p = 0; p < NPART; ++p) {
-    const float t = scratch[p * D + sc];
-    off += p < sp ? t : 0.f;
-    gamma += t;
+    const float2 t = make_float2(scratch[p * D + c0], scratch[p * D + c0 + 1]);
+    if (p < part) { off.x += t.x; off.y += t.y; }
+    gamma.x += t.x; gamma.y += t.y;
   }
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) G[j] += off;
-  const bool exact = __syncthreads_or(gamma < kFastDecayBound) != 0;
+  for (int j = 0; j < RPP; ++j) { G[j].x += off.x; G[j].y += off.y; }
+  const bool exact =
+      __syncthreads_or(gamma.x < kFastDecayBound || gamma.y < kFastDecayBound) != 0;
 
-  // V rows: loaded now, consumed after phase 3 (as V^T in region 0)
-  float vraw[QC];
-  if (nvalid) {
-    ld_seg<QC>(vb + nr * rowstride + nq * QC, vraw);
-  } else {
+  // ---- operands ---------------------------------------------------------------
+  const float2 eg_gamma = make_float2(__expf(gamma.x), __expf(gamma.y));
+  if (part == 0) { wEG[c0] = eg_gamma.x; wEG[c0 + 1] = eg_gamma.y; }
+  {
+    float kgT[2][8], ktT[2][8];
 #pragma unroll
-    for (int j = 0; j < QC; ++j) vraw[j] = 0.f;
-  }
-
-  // operands, scan layout: each thread owns channel sc of rows sp*RPP ..
-  // (the exact path keeps raw q, k in regions 1, 0 for its staging)
-  const float eg_gamma = __expf(gamma);
-  if (sp == 0) wEG[sc] = eg_gamma;
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    const int r = sp * RPP + j;
-    const float kh = ld_f(r0 + r * L::LDR + sc) * s_rk[r];
-    const float qh = ld_f(r1 + r * L::LDR + sc) * s_rq[r];
-    const float eg = __expf(G[j]);
-    st_f(r3 + sc * L::LDT + r, kh * eg);           // (K o e^G)^T
-    st_f(wQG + r * D + sc, qh * eg);
-    float ekt;
-    if (!exact) {
-      const float eng = __expf(-G[j]);
-      st_f(r0 + r * L::LDR + sc, kh * eg);         // K o e^G
-      st_f(r1 + r * L::LDR + sc, qh * eg);         // Q o e^G
-      st_f(r2 + r * L::LDR + sc, kh * eng);        // K o e^-G
-      ekt = eg_gamma * eng;
-    } else {
-      ekt = __expf(gamma - G[j]);
+    for (int j = 0; j < RPP; ++j) {
+      const int r = r0p + j;
+      const float rk = s_rk[r], rq = s_rq[r];
+      const float khx = kk[j].x * rk, khy = kk[j].y * rk;
+      const float qhx = qq[j].x * rq, qhy = qq[j].y * rq;
+      const float egx = __expf(G[j].x), egy = __expf(G[j].y);
+      st2(wQG + r * D + c0, qhx * egx, qhy * egy);
+      kgT[0][j & 7] = khx * egx;
+      kgT[1][j & 7] = khy * egy;
+      if (!exact) {
+        const float enx = __expf(-G[j].x), eny = __expf(-G[j].y);
+        st2(r0 + r * L::LDR + c0, khx * egx, khy * egy);     // K o e^G
+        st2(r1 + r * L::LDR + c0, qhx * egx, qhy * egy);     // Q o e^G
+        st2(r2 + r * L::LDR + c0, khx * enx, khy * eny);     // K o e^-G
+        ktT[0][j & 7] = khx * (eg_gamma.x * enx);
+        ktT[1][j & 7] = khy * (eg_gamma.y * eny);
+      } else {
+        st2(r0 + r * L::LDR + c0, khx, khy);                 // k^ (staged later)
+        st2(r1 + r * L::LDR + c0, qhx, qhy);                 // q^
+        ktT[0][j & 7] = khx * __expf(gamma.x - G[j].x);
+        ktT[1][j & 7] = khy * __expf(gamma.y - G[j].y);
+      }
+      if ((j & 7) == 7) {
+        const int rb = r0p + (j & ~7);
+        st8(r3 + c0 * L::LDT + rb, kgT[0]);                  // (K o e^G)^T
+        st8(r3 + (c0 + 1) * L::LDT + rb, kgT[1]);
+        st8(wKT + c0 * kC + rb, ktT[0]);                     // (K o e^(gamma-G))^T
+        st8(wKT + (c0 + 1) * kC + rb, ktT[1]);
+      }
     }
-    st_f(wKT + sc * kC + r, kh * ekt);             // (K o e^(gamma-G))^T
   }
   __syncthreads();
 
-  // ---- phase 3: A (strict lower, x beta_r) and P (lower) -------------------
+  // ---- A (strict lower, x beta_r) and P (lower) ------------------------------
   // Tiles are computed transposed (A^T, P^T) so each lane's 4 accumulator
-  // rows are 4 consecutive columns of A / P: one vector store each.
-  // Block pairs (I, R), I <= R, dealt to waves.
+  // rows are 4 consecutive columns of A / P: one vector store each.  The 10
+  // block pairs (I <= R) and the 6 all-zero blocks of P above the diagonal
+  // are dealt to the waves.
   const int pairI[4][3] = {{0, 0, 0}, {0, 1, 1}, {1, 2, -1}, {2, 3, -1}};
   const int pairR[4][3] = {{0, 1, 2}, {3, 1, 2}, {3, 2, -1}, {3, 3, -1}};
   f32x4_t accA[3], accP[3];
@@ -472,13 +541,15 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
     float* stK = stG + kC * 16;
     float* stQ = stK + kC * 16;
     for (int cb = 0; cb < D / 16; ++cb) {
-      if (sc / 16 == cb) {
+      if (c0 / 16 == cb) {
 #pragma unroll
         for (int j = 0; j < RPP; ++j) {
-          const int r = sp * RPP + j;
-          stG[r * 16 + sc % 16] = G[j];
-          stK[r * 16 + sc % 16] = ld_f(r0 + r * L::LDR + sc) * s_rk[r];
-          stQ[r * 16 + sc % 16] = ld_f(r1 + r * L::LDR + sc) * s_rq[r];
+          const int r = r0p + j, cc = c0 % 16;
+          stG[r * 16 + cc] = G[j].x;
+          stG[r * 16 + cc + 1] = G[j].y;
+          const float2 kh = ld2(r0 + r * L::LDR + c0), qh = ld2(r1 + r * L::LDR + c0);
+          stK[r * 16 + cc] = kh.x; stK[r * 16 + cc + 1] = kh.y;
+          stQ[r * 16 + cc] = qh.x; stQ[r * 16 + cc + 1] = qh.y;
         }
       }
       __syncthreads();
@@ -495,7 +566,6 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       }
       __syncthreads();
     }
-    // scatter into the same places the MFMA path writes
     float* sA = reinterpret_cast<float*>(r1);
 #pragma unroll
     for (int m = 0; m < NE; ++m) {
@@ -503,6 +573,11 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       const int r = er[m], i = ei[m];
       sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[m] : 0.f;
       st_f(wP + r * kC + i, ep[m]);
+    }
+    // the exact path writes no upper-triangle entries of the diagonal blocks
+    for (int e = tid; e < kC * kC; e += kThreads) {
+      const int r = e >> 6, i = e & 63;
+      if (i > r && (i >> 4) == (r >> 4)) st_f(wP + r * kC + i, 0.f);
     }
   }
   if (!exact) {
@@ -525,18 +600,26 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       st4(wP + r * kC + i0, p4[0], p4[1], p4[2], p4[3]);
     }
   }
-  // zeros of P above the diagonal (the MFMA path already wrote the upper
-  // triangles of the diagonal blocks)
-  for (int e = tid; e < kC * kC; e += kThreads) {
-    const int r = e >> 6, i = e & 63;
-    if (i > r && (exact || (i >> 4) > (r >> 4))) st_f(wP + r * kC + i, 0.f);
+  {
+    // zero blocks of P above the diagonal: (R, I) = (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    const int zR[6] = {0, 0, 0, 1, 1, 2}, zI[6] = {1, 2, 3, 2, 3, 3};
+    for (int z = wave; z < 6; z += 4) {
+      const int r = zR[z] * 16 + (lane & 15), i0 = zI[z] * 16 + 4 * (lane >> 4);
+      st4(wP + r * kC + i0, 0.f, 0.f, 0.f, 0.f);
+    }
   }
-  // V^T into region 0 (K o e^G row-major is dead now)
+  // V^T into region 0 (its row-major content is dead now), 8 rows per store
 #pragma unroll
-  for (int j = 0; j < QC; ++j) st_f(r0 + (nq * QC + j) * L::LDT + nr, vraw[j]);
+  for (int j0 = 0; j0 < RPP; j0 += 8) {
+    float vx[8], vy[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) { vx[t] = vv[j0 + t].x; vy[t] = vv[j0 + t].y; }
+    st8(r0 + c0 * L::LDT + r0p + j0, vx);
+    st8(r0 + (c0 + 1) * L::LDT + r0p + j0, vy);
+  }
   __syncthreads();
 
-  // ---- phase 4: T = (I + A)^-1 in fp32 --------------------------------------
+  // ---- T = (I + A)^-1 in fp32 --------------------------------------------------
   const float* sA = reinterpret_cast<const float*>(r1);
   float* sT = reinterpret_cast<float*>(r2);
   if (wave == 0) {
@@ -553,47 +636,62 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
     }
   }
   __syncthreads();
-  // off-diagonal blocks by distance: T_RI = -T_RR sum_(J=I..R-1) A_RJ T_JI
-  for (int dist = 1; dist < 4; ++dist) {
-    if (wave < 4 - dist) {
-      const int I = wave, Rb = wave + dist;
-      const int rr = lane >> 2, cc = (lane & 3) * 4;
-      float m4[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int J = I; J < Rb; ++J) {
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const float a = sA[(Rb * 16 + rr) * L::LDA + J * 16 + kk];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) m4[j] += a * sT[(J * 16 + kk) * L::LDA + I * 16 + cc + j];
-        }
-      }
-      float* mscr = scratch + wave * 256;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mscr[rr * 16 + cc + j] = m4[j];
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      float t4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const float tr = sT[(Rb * 16 + rr) * L::LDA + Rb * 16 + kk];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t4[j] -= tr * mscr[kk * 16 + cc + j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sT[(Rb * 16 + rr) * L::LDA + I * 16 + cc + j] = t4[j];
-    }
-    __syncthreads();
+  // level 1: T_10 = -T_11 A_10 T_00 (wave 0), T_32 = -T_33 A_32 T_22 (wave 1)
+  if (wave < 2) {
+    const int b0 = wave * 32;  // the 32x32 diagonal block
+    float* xs = scratch + wave * 256;
+    f32x4_t x = mm16_f32(sA + (b0 + 16) * L::LDA + b0, L::LDA, sT + b0 * L::LDA + b0, L::LDA,
+                         f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
+    st_tile_f32(xs, 16, x, 1.f, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4_t y = mm16_f32(sT + (b0 + 16) * L::LDA + b0 + 16, L::LDA, xs, 16,
+                         f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
+    st_tile_f32(sT + (b0 + 16) * L::LDA + b0, L::LDA, y, -1.f, lane);
   }
-  // T Diag(beta) in the MFMA type, lower triangle only, into region 1
+  __syncthreads();
+  // level 2: T[32:64, 0:32] = -T_low A[32:64, 0:32] T_high; wave w owns one
+  // 16x16 output tile (rows 32 + 16*(w/2), cols 16*(w%2))
+  {
+    const int tr = 32 + 16 * (wave >> 1), tc = 16 * (wave & 1);
+    f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // X = A[tr.., 0:32] T_high[0:32, tc..]: T_high is lower triangular, so
+    // only k-blocks >= tc/16 contribute
+    for (int kb = tc / 16; kb < 2; ++kb)
+      x = mm16_f32(sA + tr * L::LDA + kb * 16, L::LDA, sT + (kb * 16) * L::LDA + tc, L::LDA, x,
+                   lane);
+    float* xs = scratch;  // 32x32 X, leading dim 32
+    st_tile_f32(xs + (tr - 32) * 32 + tc, 32, x, 1.f, lane);
+    __syncthreads();
+    // Y = T_low[tr.., 32:64] X[0:32, tc..]: T_low lower triangular, k-blocks <= tr
+    f32x4_t y = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb <= (tr - 32) / 16; ++kb)
+      y = mm16_f32(sT + tr * L::LDA + 32 + kb * 16, L::LDA, xs + (kb * 16) * 32 + tc, 32, y, lane);
+    st_tile_f32(sT + tr * L::LDA + tc, L::LDA, y, -1.f, lane);
+  }
+  __syncthreads();
+  // T Diag(beta) in the MFMA type, lower triangle only, into region 1:
+  // thread = (row, 16-column group)
   T* sTb = r1;
-  for (int e = tid; e < kC * kC; e += kThreads) {
-    const int r = e >> 6, i = e & 63;
-    const float val = i <= r ? sT[r * L::LDA + i] * s_beta[i] : 0.f;
-    st_f(sTb + r * L::LDT + i, val);
+  {
+    const int r = tid >> 2, i0 = (tid & 3) * 16;
+    float vals[16];
+#pragma unroll
+    for (int t = 0; t < 16; t += 4) {
+      const float4 tv = *reinterpret_cast<const float4*>(sT + r * L::LDA + i0 + t);
+      const float4 bv = *reinterpret_cast<const float4*>(s_beta + i0 + t);
+      vals[t] = (i0 + t <= r) ? tv.x * bv.x : 0.f;
+      vals[t + 1] = (i0 + t + 1 <= r) ? tv.y * bv.y : 0.f;
+      vals[t + 2] = (i0 + t + 2 <= r) ? tv.z * bv.z : 0.f;
+      vals[t + 3] = (i0 + t + 3 <= r) ? tv.w * bv.w : 0.f;
+    }
+    st8(sTb + r * L::LDT + i0, vals);  // region 1 held A: every read of it ended above
+    st8(sTb + r * L::LDT + i0 + 8, vals + 8);
   }
   __syncthreads();
 
-  // ---- phase 5: U = T Diag(beta) V and Wk^T = (K o e^G)^T (T Diag(beta))^T --
+  // ---- U = T Diag(beta) V and Wk^T = (K o e^G)^T (T Diag(beta))^T --------------
   {
     const int rb = wave;  // this wave's 16 rows of T
     typename M::frag tb[kC / M::KSTEP];
@@ -619,18 +717,59 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
 
 // ---------------------------------------------------------------------------
 // K2: sequential state pass over one sequence's chunks for one d_v slice.
+//
+// Per chunk, wave w owns output rows [16w, 16w+16) (W and O) and state rows
+// [16*CBW*w, 16*CBW*(w+1)) (S).  The fragments a wave needs from the chunk's
+// record -- rows of -Wk, Q o e^G and P, rows of K~^T, its U^T block and
+// e^gamma -- are private to the wave and go straight from memory into
+// registers; only S and W, which every wave reads in full, pass through LDS.
+// The next chunk's fragments are loaded while the current chunk computes
+// (two register sets, loop unrolled by two).
+template <typename T, int D, int WS>
+struct K2Frags {
+  using M = Mma<T>;
+  using R = Rec<T, D>;
+  static constexpr int NB = WS / 16, CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
+  typename M::frag wn[KD], qg[KD], p[KC], kt[CBW][KC];
+  Raw4<T> ut[NB];
+  Raw4<float> eg[CBW];
+
+  __device__ __forceinline__ void load(const char* rec, int wave, int lane, int n0) {
+    const T* QG = reinterpret_cast<const T*>(rec) + R::QG;
+    const T* KT = reinterpret_cast<const T*>(rec) + R::KT;
+    const T* WN = reinterpret_cast<const T*>(rec) + R::WN;
+    const T* UT = reinterpret_cast<const T*>(rec) + R::UT;
+    const T* P = reinterpret_cast<const T*>(rec) + R::P;
+    const float* EG = reinterpret_cast<const float*>(rec + R::BYTES_T);
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      wn[ks] = frag_at<T>(WN, D, wave * 16, ks, lane);
+      qg[ks] = frag_at<T>(QG, D, wave * 16, ks, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) p[ks] = frag_at<T>(P, kC, wave * 16, ks, lane);
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) kt[i][ks] = frag_at<T>(KT, kC, (wave * CBW + i) * 16, ks, lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      ut[nb].load(UT + (int64_t)(n0 + nb * 16 + (lane & 15)) * kC + wave * 16 + 4 * (lane >> 4));
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) eg[i].load(EG + (wave * CBW + i) * 16 + 4 * (lane >> 4));
+  }
+};
+
 template <typename T, int D, int WS>
 __global__ __launch_bounds__(kThreads) void kda_state_pass(
     const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
-    int nseg, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
+    int nseg, int64_t seg_slots, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
     float* __restrict__ fin, float* __restrict__ ckpt, int64_t ckpt_every, int64_t nckpt,
     float scale, T* __restrict__ o) {
   using M = Mma<T>;
   using R = Rec<T, D>;
-  constexpr int NB = WS / 16;          // 16-column blocks in the slice
-  constexpr int CBW = D / 16 / 4;      // 16-row blocks of S per wave
-  constexpr int KD = D / M::KSTEP;     // k-steps over d_k
-  constexpr int KC = kC / M::KSTEP;    // k-steps over the chunk
+  using F = K2Frags<T, D, WS>;
+  constexpr int NB = F::NB, CBW = F::CBW, KD = F::KD, KC = F::KC;
   constexpr int LDS_S = D + 8, LDS_W = kC + 8;
   __shared__ __align__(16) char lds_raw[(WS * LDS_S + WS * LDS_W) * sizeof(T)];
   T* sSt = reinterpret_cast<T*>(lds_raw);                // S^T slice [n][c]
@@ -652,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
   const SeqSpan sp = seq_span(gm, seq);
   const int64_t nrec = s1 - s0;
   if (sp.c0 == sp.c1) {  // empty sequence: final = init, once
-    if (seg != (int)min<int64_t>(sp.c0 / kSegSlots, nseg - 1) || fin == nullptr) return;
+    if (seg != (int)min<int64_t>(sp.c0 / seg_slots, nseg - 1) || fin == nullptr) return;
     const int64_t base = (int64_t)nh * D * D;
     for (int e = threadIdx.x; e < D * WS; e += kThreads) {
       const int64_t idx = base + (int64_t)(e / WS) * D + n0 + e % WS;
@@ -679,14 +818,9 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
         S[i][nb][j] = src ? src[sbase + (int64_t)c * D + n] : 0.f;
       }
 
-  for (int64_t slot = slot0; slot < slot1; ++slot) {
-    const char* rec = ws + ((int64_t)h * nrec + (slot - s0)) * R::BYTES;
-    const T* QG = reinterpret_cast<const T*>(rec) + R::QG;
-    const T* KT = reinterpret_cast<const T*>(rec) + R::KT;
-    const T* WN = reinterpret_cast<const T*>(rec) + R::WN;
-    const T* UT = reinterpret_cast<const T*>(rec) + R::UT;
-    const T* P = reinterpret_cast<const T*>(rec) + R::P;
-    const float* EG = reinterpret_cast<const float*>(rec + R::BYTES_T);
+  auto rec_of = [&](int64_t slot) { return ws + ((int64_t)h * nrec + (slot - s0)) * R::BYTES; };
+
+  auto step = [&](const F& f, int64_t slot) {
     const int64_t off = (slot - sp.c0) * kC;  // first token of the chunk within the sequence
     const int64_t tok0 = sp.tok0 + off;
     const int len = (int)min<int64_t>(kC, sp.ntok - off);
@@ -702,25 +836,18 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
       }
     __syncthreads();
 
-    // (b) W = U + (-Wk) S  (rows of this wave's 16-row block) and O^T = S^T (Q o e^G)^T
+    // (b) W = U + (-Wk) S (this wave's 16 rows) and O^T = S^T (Q o e^G)^T
     f32x4_t W[NB], O[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = n0 + nb * 16 + (lane & 15);
-      W[nb] = ld4(UT + (int64_t)n * kC + wave * 16 + 4 * (lane >> 4));
-      O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int nb = 0; nb < NB; ++nb) { W[nb] = f.ut[nb].get(); O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) {
-      const auto wn = frag_at<T>(WN, D, wave * 16, ks, lane);
-      const auto qg = frag_at<T>(QG, D, wave * 16, ks, lane);
+    for (int ks = 0; ks < KD; ++ks)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const auto s = frag_at<T>(sSt, LDS_S, nb * 16, ks, lane);
-        W[nb] = M::mma(wn, s, W[nb]);
-        O[nb] = M::mma(s, qg, O[nb]);
+        const auto sfr = frag_at<T>(sSt, LDS_S, nb * 16, ks, lane);
+        W[nb] = M::mma(f.wn[ks], sfr, W[nb]);
+        O[nb] = M::mma(sfr, f.qg[ks], O[nb]);
       }
-    }
     // (c) W -> LDS as W^T
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -729,34 +856,26 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
     }
     __syncthreads();
 
-    // (d) O^T += W^T P^T ;  S = Diag(e^gamma) S + K~^T W
+    // (d) S = Diag(e^gamma) S + K~^T W  (the chain's critical path) ; O^T += W^T P^T
+    typename M::frag wf[NB][KC];
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks) {
-      const auto p = frag_at<T>(P, kC, wave * 16, ks, lane);
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) wf[nb][ks] = frag_at<T>(sWt, LDS_W, nb * 16, ks, lane);
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const auto wf = frag_at<T>(sWt, LDS_W, nb * 16, ks, lane);
-        O[nb] = M::mma(wf, p, O[nb]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CBW; ++i) {
-      const int cb = wave * CBW + i;
-      const f32x4_t eg = ld4(EG + cb * 16 + 4 * (lane >> 4));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        const f32x4_t eg = f.eg[i].get();
 #pragma unroll
         for (int j = 0; j < 4; ++j) S[i][nb][j] *= eg[j];
 #pragma unroll
-      for (int ks = 0; ks < KC; ++ks) {
-        const auto kt = frag_at<T>(KT, kC, cb * 16, ks, lane);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const auto wf = frag_at<T>(sWt, LDS_W, nb * 16, ks, lane);
-          S[i][nb] = M::mma(kt, wf, S[i][nb]);
-        }
+        for (int ks = 0; ks < KC; ++ks) S[i][nb] = M::mma(f.kt[i][ks], wf[nb][ks], S[i][nb]);
       }
-    }
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(wf[nb][ks], f.p[ks], O[nb]);
 
     // (e) output rows of this wave's block: O^T[n][r] -> o[tok0 + r][h][n0 + n]
     const int r = wave * 16 + (lane & 15);
@@ -773,7 +892,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
       const int64_t done = off + len;  // tokens of this sequence so far
       if (len == kC && done % ckpt_every == 0) {
         const int64_t jslot = done / ckpt_every - 1;
-        float* dst = ckpt + (((int64_t)seq * nckpt + jslot) * H + h) * (int64_t)D * D;
+        float* cdst = ckpt + (((int64_t)seq * nckpt + jslot) * H + h) * (int64_t)D * D;
 #pragma unroll
         for (int i = 0; i < CBW; ++i)
 #pragma unroll
@@ -781,13 +900,26 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int c = (wave * CBW + i) * 16 + 4 * (lane >> 4) + j;
-              dst[(int64_t)c * D + n0 + nb * 16 + (lane & 15)] = S[i][nb][j];
+              cdst[(int64_t)c * D + n0 + nb * 16 + (lane & 15)] = S[i][nb][j];
             }
       }
     }
     // No barrier here: the next chunk's sSt writes follow this chunk's
     // second barrier (after every wave read sSt), and its sWt writes follow
     // the next chunk's first barrier (after every wave read sWt).
+  };
+
+  // The prefetch is unconditional (past the end it re-reads the last record)
+  // so no branch sits between a load and its use: the wait counter then only
+  // waits for the set being consumed.
+  F fa, fb;
+  fa.load(rec_of(slot0), wave, lane, n0);
+  for (int64_t slot = slot0; slot < slot1; slot += 2) {
+    fb.load(rec_of(min(slot + 1, slot1 - 1)), wave, lane, n0);
+    step(fa, slot);
+    if (slot + 1 >= slot1) break;
+    fa.load(rec_of(min(slot + 2, slot1 - 1)), wave, lane, n0);
+    step(fb, slot + 1);
   }
 
   if (dst != nullptr) {
@@ -806,7 +938,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
 // ---------------------------------------------------------------------------
 // Host side: workspace plan and launches.
 //
-// Chunk slots are processed in segments of at most kSegSlots slots: K1 fills
+// Chunk slots are processed in segments of at most seg_slots() slots: K1 fills
 // the segment's records, then K2 advances every sequence through its chunks
 // inside the segment.  The workspace therefore holds one segment's records
 // (bounded for any T), the fp32 states carried between segments, and the
@@ -828,15 +960,26 @@ int64_t rec_bytes_for(const kda_desc_t& d) {
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// Segment length in chunk slots; KDA_SEG_SLOTS (read once) overrides it for
+// tuning.  It fixes the workspace size, so it never changes after first use.
+int64_t seg_slots() {
+  static const int64_t v = [] {
+    const char* e = getenv("KDA_SEG_SLOTS");
+    const long long x = e ? atoll(e) : 0;
+    return x >= 8 && x <= (1 << 20) ? (int64_t)x : kSegSlotsDefault;
+  }();
+  return v;
+}
+
 Plan make_plan(const kda_desc_t& d, bool varlen) {
   Plan p{};
   const int64_t T = d.seqlen;
   p.slot_bound = varlen ? (T + (int64_t)(kC - 1) * d.num_seqs) / kC
                         : (int64_t)d.batch * ((T + kC - 1) / kC);
-  p.seg_slots = std::min<int64_t>(p.slot_bound, kSegSlots);
+  p.seg_slots = std::min<int64_t>(p.slot_bound, seg_slots());
   p.rec_bytes = rec_bytes_for(d);
   p.rec_total = p.seg_slots * d.heads * p.rec_bytes;
-  p.carry_bytes = p.slot_bound > kSegSlots
+  p.carry_bytes = p.slot_bound > seg_slots()
                       ? (int64_t)d.num_seqs * d.heads * d.dk * d.dv * 4 : 0;
   p.map_bytes = varlen ? 2 * align256(((int64_t)d.num_seqs + 1) * 4) : 0;
   return p;
@@ -872,15 +1015,16 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                        d.seqlen, cu_s, chunk_off);
     gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
   }
-  const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + kSegSlots - 1) / kSegSlots;
+  const int64_t SS = seg_slots();
+  const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + SS - 1) / SS;
   for (int64_t s = 0; s < nseg; ++s) {
-    const int64_t s0 = s * kSegSlots, s1 = std::min<int64_t>(p.slot_bound, s0 + kSegSlots);
+    const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
     if (s1 > s0)
-      hipLaunchKernelGGL((kda_intra_chunk<T, D>), dim3((unsigned)(s1 - s0), H), dim3(kThreads),
+      hipLaunchKernelGGL((kda_intra_chunk<T, D>), dim3(H, (unsigned)(s1 - s0)), dim3(kThreads),
                          k1_lds, stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H,
                          s0, s1 - s0, d.qk_l2norm, recs);
     hipLaunchKernelGGL((kda_state_pass<T, D, WS>), dim3(nhpad * nslice), dim3(kThreads), 0,
-                       stream, recs, gm, H, s0, s1, (int)s, (int)nseg, nslice, NH, init_state,
+                       stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,
                        carry, final_state, ckpt, d.ckpt_every, nck, d.scale, (T*)o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

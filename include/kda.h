@@ -19,7 +19,7 @@
  *
  * Conventions common to every entry point:
  *  - Tensor pointers are DEVICE pointers to dense row-major arrays (last
- *    index fastest).  Alignment: kda_chunk_fwd needs q, k, v, o and the
+ *    index fastest).  Alignment: kda_chunk_fwd needs q, k, v, g, o and the
  *    workspace 16-byte aligned and every other pointer 4-byte aligned;
  *    kda_decode_step needs the state 16-byte aligned and every other pointer
  *    aligned to its element size.  The caller owns every buffer; the

@@ -84,8 +84,10 @@ def test_chunk_pointer_errors():
     assert b"q is NULL" in lib.kda_last_error()
     assert _call_chunk(_desc(), misalign="q") == B.KDA_ERR_INVALID_ARGUMENT
     assert b"q is not 16-byte aligned" in lib.kda_last_error()
-    assert _call_chunk(_desc(), misalign="g", shift=2) == B.KDA_ERR_INVALID_ARGUMENT
-    assert b"g is not 4-byte aligned" in lib.kda_last_error()
+    assert _call_chunk(_desc(), misalign="g", shift=8) == B.KDA_ERR_INVALID_ARGUMENT
+    assert b"g is not 16-byte aligned" in lib.kda_last_error()
+    assert _call_chunk(_desc(), misalign="beta", shift=2) == B.KDA_ERR_INVALID_ARGUMENT
+    assert b"beta is not 4-byte aligned" in lib.kda_last_error()
     assert _call_chunk(_desc(), o=FAKE) == B.KDA_ERR_INVALID_ARGUMENT  # o aliases q
     assert _call_chunk(_desc(), ws_bytes=16) == B.KDA_ERR_WORKSPACE_TOO_SMALL
     assert _call_chunk(_desc(ckpt_every=64)) == B.KDA_ERR_INVALID_ARGUMENT  # ckpt buffer missing
