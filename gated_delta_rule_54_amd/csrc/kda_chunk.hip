@@ -125,6 +125,18 @@ template <> struct Raw4<bf16> {
                    bf_val(v.y >> 16)};
   }
 };
+// Two consecutive elements kept as raw bits until use.
+template <typename T> struct Raw2;
+template <> struct Raw2<float> {
+  float2 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ float2 get() const { return v; }
+};
+template <> struct Raw2<bf16> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
+};
 // Load N consecutive elements (16-byte aligned, N a multiple of 8) as floats.
 template <int N>
 __device__ __forceinline__ void ld_seg(const float* p, float* out) {
@@ -408,30 +420,53 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   float* wEG = reinterpret_cast<float*>(rec + R::BYTES_T);
 
   // ---- global loads --------------------------------------------------------
+  // Every load is unconditional (rows past the chunk's end re-read its last
+  // row and are masked afterwards) and keeps its raw bits until all loads
+  // are in flight: a load under a branch, or converted on arrival, makes the
+  // wave wait for it before issuing the next one.
   // channel-pair layout: channels c0, c0+1 of rows r0p .. r0p+RPP-1
   const int cp = tid % NCP, part = tid / NCP;
   const int c0 = 2 * cp, r0p = part * RPP;
+  Raw2<float> graw[RPP];
+  Raw2<T> kraw[RPP], qraw[RPP], vraw[RPP];
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const int r = min(r0p + j, loc.len - 1);
+    graw[j].load(gb + r * rowstride + c0);
+    kraw[j].load(kb + r * rowstride + c0);
+    qraw[j].load(qb + r * rowstride + c0);
+    vraw[j].load(vb + r * rowstride + c0);
+  }
+  // row layout for the norms (a second, cache-served read of q and k rows)
+  const int nr = tid >> 2, nq = tid & 3;
+  Raw4<T> nqr[QC / 4], nkr[QC / 4];
+  {
+    const int rr = min(nr, loc.len - 1);
+#pragma unroll
+    for (int j = 0; j < QC / 4; ++j) {
+      nqr[j].load(qb + rr * rowstride + nq * QC + 4 * j);
+      nkr[j].load(kb + rr * rowstride + nq * QC + 4 * j);
+    }
+  }
+  if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
   float2 G[RPP], kk[RPP], qq[RPP], vv[RPP];
 #pragma unroll
   for (int j = 0; j < RPP; ++j) {
-    const int r = r0p + j;
-    const bool ok = r < loc.len;
-    G[j] = ok ? ld2(gb + r * rowstride + c0) : make_float2(0.f, 0.f);
-    kk[j] = ok ? ld2(kb + r * rowstride + c0) : make_float2(0.f, 0.f);
-    qq[j] = ok ? ld2(qb + r * rowstride + c0) : make_float2(0.f, 0.f);
-    vv[j] = ok ? ld2(vb + r * rowstride + c0) : make_float2(0.f, 0.f);
+    const bool ok = r0p + j < loc.len;
+    G[j] = ok ? graw[j].get() : make_float2(0.f, 0.f);
+    kk[j] = ok ? kraw[j].get() : make_float2(0.f, 0.f);
+    qq[j] = ok ? qraw[j].get() : make_float2(0.f, 0.f);
+    vv[j] = ok ? vraw[j].get() : make_float2(0.f, 0.f);
   }
-  if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
-  // row layout for the norms (a second, cache-served read of q and k rows)
   {
-    const int nr = tid >> 2, nq = tid & 3;
     float sq = 0.f, sk = 0.f;
     if (nr < loc.len) {
-      float xq[QC], xk[QC];
-      ld_seg<QC>(qb + nr * rowstride + nq * QC, xq);
-      ld_seg<QC>(kb + nr * rowstride + nq * QC, xk);
 #pragma unroll
-      for (int j = 0; j < QC; ++j) { sq += xq[j] * xq[j]; sk += xk[j] * xk[j]; }
+      for (int j = 0; j < QC / 4; ++j) {
+        const f32x4_t a = nqr[j].get(), b = nkr[j].get();
+        sq += a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+        sk += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+      }
     }
     sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
     sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
@@ -725,43 +760,101 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
 // registers; only S and W, which every wave reads in full, pass through LDS.
 // The next chunk's fragments are loaded while the current chunk computes
 // (two register sets, loop unrolled by two).
+// Buffer-resource loads: one resource per head's records, a per-lane 32-bit
+// offset computed once, the slot's record offset in a scalar register and the
+// fragment's constant offset in the instruction -- no per-load address math.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <typename T> struct BufFrag;
+template <> struct BufFrag<bf16> {
+  static __device__ __forceinline__ bf16x8_t load(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                  uint32_t soff) {
+    return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+  }
+};
+template <> struct BufFrag<float> {
+  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+  }
+};
+// Four consecutive elements, raw bits.
+template <typename T> struct BufRaw4;
+template <> struct BufRaw4<bf16> {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  }
+  __device__ __forceinline__ f32x4_t get() const {
+    return f32x4_t{bf_val(v[0] & 0xffffu), bf_val(v[0] >> 16), bf_val(v[1] & 0xffffu),
+                   bf_val(v[1] >> 16)};
+  }
+};
+template <> struct BufRaw4<float> {
+  u32x4_t v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+  }
+  __device__ __forceinline__ f32x4_t get() const { return __builtin_bit_cast(f32x4_t, v); }
+};
+// Store 4 consecutive elements to LDS / global from floats.
+__device__ __forceinline__ void st4p(bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ void st4p(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// Per-wave fragments of one chunk's record (see kda_state_pass).
 template <typename T, int D, int WS>
 struct K2Frags {
   using M = Mma<T>;
   using R = Rec<T, D>;
   static constexpr int NB = WS / 16, CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
+  static constexpr uint32_t ES = sizeof(T);
   typename M::frag wn[KD], qg[KD], p[KC], kt[CBW][KC];
-  Raw4<T> ut[NB];
-  Raw4<float> eg[CBW];
+  BufRaw4<T> ut[NB];
+  BufRaw4<float> eg[CBW];
 
-  __device__ __forceinline__ void load(const char* rec, int wave, int lane, int n0) {
-    const T* QG = reinterpret_cast<const T*>(rec) + R::QG;
-    const T* KT = reinterpret_cast<const T*>(rec) + R::KT;
-    const T* WN = reinterpret_cast<const T*>(rec) + R::WN;
-    const T* UT = reinterpret_cast<const T*>(rec) + R::UT;
-    const T* P = reinterpret_cast<const T*>(rec) + R::P;
-    const float* EG = reinterpret_cast<const float*>(rec + R::BYTES_T);
+  // lane offsets (bytes within a record), computed once per workgroup
+  struct Offs { uint32_t wn, qg, p, kt, ut, eg; };
+  static __device__ __forceinline__ Offs offsets(int wave, int lane, int n0) {
+    const uint32_t row = wave * 16 + (lane & 15), kg = M::KPL * (lane >> 4);
+    Offs o;
+    o.wn = (uint32_t)(R::WN * ES) + (row * D + kg) * ES;
+    o.qg = (uint32_t)(R::QG * ES) + (row * D + kg) * ES;
+    o.p = (uint32_t)(R::P * ES) + (row * kC + kg) * ES;
+    o.kt = (uint32_t)(R::KT * ES) + ((wave * CBW * 16 + (lane & 15)) * kC + kg) * ES;
+    o.ut = (uint32_t)(R::UT * ES) + ((n0 + (lane & 15)) * kC + wave * 16 + 4 * (lane >> 4)) * ES;
+    o.eg = (uint32_t)R::BYTES_T + (wave * CBW * 16 + 4 * (lane >> 4)) * 4;
+    return o;
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
-      wn[ks] = frag_at<T>(WN, D, wave * 16, ks, lane);
-      qg[ks] = frag_at<T>(QG, D, wave * 16, ks, lane);
+      wn[ks] = BufFrag<T>::load(r, o.wn + ks * M::KSTEP * ES, soff);
+      qg[ks] = BufFrag<T>::load(r, o.qg + ks * M::KSTEP * ES, soff);
     }
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks) p[ks] = frag_at<T>(P, kC, wave * 16, ks, lane);
+    for (int ks = 0; ks < KC; ++ks) p[ks] = BufFrag<T>::load(r, o.p + ks * M::KSTEP * ES, soff);
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
 #pragma unroll
-      for (int ks = 0; ks < KC; ++ks) kt[i][ks] = frag_at<T>(KT, kC, (wave * CBW + i) * 16, ks, lane);
+      for (int ks = 0; ks < KC; ++ks)
+        kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * 16 * kC + ks * M::KSTEP) * ES, soff);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      ut[nb].load(UT + (int64_t)(n0 + nb * 16 + (lane & 15)) * kC + wave * 16 + 4 * (lane >> 4));
+    for (int nb = 0; nb < NB; ++nb) ut[nb].load(r, o.ut + nb * 16 * kC * ES, soff);
 #pragma unroll
-    for (int i = 0; i < CBW; ++i) eg[i].load(EG + (wave * CBW + i) * 16 + 4 * (lane >> 4));
+    for (int i = 0; i < CBW; ++i) eg[i].load(r, o.eg + i * 64, soff);
   }
 };
 
 template <typename T, int D, int WS>
-__global__ __launch_bounds__(kThreads) void kda_state_pass(
+__global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
     int nseg, int64_t seg_slots, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
     float* __restrict__ fin, float* __restrict__ ckpt, int64_t ckpt_every, int64_t nckpt,
@@ -818,12 +911,22 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
         S[i][nb][j] = src ? src[sbase + (int64_t)c * D + n] : 0.f;
       }
 
-  auto rec_of = [&](int64_t slot) { return ws + ((int64_t)h * nrec + (slot - s0)) * R::BYTES; };
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ws + (int64_t)h * nrec * R::BYTES), (short)0, (int)(nrec * R::BYTES), 0x00020000);
+  const typename F::Offs offs = F::offsets(wave, lane, n0);
+  auto soff_of = [&](int64_t slot) { return (uint32_t)((slot - s0) * R::BYTES); };
+
+  // Output row of this lane for the chunk at slot0; later chunks are whole
+  // chunks further on (kC tokens * H heads * D elements per chunk).
+  const int r_out = wave * 16 + (lane & 15);
+  T* const obase = o + ((sp.tok0 + (slot0 - sp.c0) * kC + r_out) * H + h) * D + n0;
+  const int64_t ostride = (int64_t)kC * H * D;
+  // checkpoints fall after every ck_chunks whole chunks of the sequence
+  const int ck_chunks = ckpt != nullptr ? (int)(ckpt_every / kC) : 1;
 
   auto step = [&](const F& f, int64_t slot) {
-    const int64_t off = (slot - sp.c0) * kC;  // first token of the chunk within the sequence
-    const int64_t tok0 = sp.tok0 + off;
-    const int len = (int)min<int64_t>(kC, sp.ntok - off);
+    const int ci = (int)(slot - sp.c0);  // chunk index within the sequence
+    const int len = (int)min<int64_t>(kC, sp.ntok - (int64_t)ci * kC);
 
     // (a) S -> LDS as S^T in the MFMA type
 #pragma unroll
@@ -832,7 +935,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
       for (int nb = 0; nb < NB; ++nb) {
         const int c4 = (wave * CBW + i) * 16 + 4 * (lane >> 4);
         const int n = nb * 16 + (lane & 15);
-        st4(sSt + n * LDS_S + c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
+        st4p(sSt + n * LDS_S + c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
       }
     __syncthreads();
 
@@ -852,7 +955,7 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = nb * 16 + (lane & 15);
-      st4(sWt + n * LDS_W + wave * 16 + 4 * (lane >> 4), W[nb][0], W[nb][1], W[nb][2], W[nb][3]);
+      st4p(sWt + n * LDS_W + wave * 16 + 4 * (lane >> 4), W[nb][0], W[nb][1], W[nb][2], W[nb][3]);
     }
     __syncthreads();
 
@@ -878,20 +981,18 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
       for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(wf[nb][ks], f.p[ks], O[nb]);
 
     // (e) output rows of this wave's block: O^T[n][r] -> o[tok0 + r][h][n0 + n]
-    const int r = wave * 16 + (lane & 15);
-    if (r < len) {
-      T* orow = o + ((tok0 + r) * H + h) * D + n0;
+    if (r_out < len) {
+      T* orow = obase + (slot - slot0) * ostride;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        st4(orow + nb * 16 + 4 * (lane >> 4), scale * O[nb][0], scale * O[nb][1],
-            scale * O[nb][2], scale * O[nb][3]);
+        st4p(orow + nb * 16 + 4 * (lane >> 4), scale * O[nb][0], scale * O[nb][1],
+             scale * O[nb][2], scale * O[nb][3]);
     }
 
     // (f) checkpoint after every ckpt_every tokens (dense, chunk-aligned)
     if (ckpt != nullptr) {
-      const int64_t done = off + len;  // tokens of this sequence so far
-      if (len == kC && done % ckpt_every == 0) {
-        const int64_t jslot = done / ckpt_every - 1;
+      if (len == kC && (ci + 1) % ck_chunks == 0) {
+        const int64_t jslot = (ci + 1) / ck_chunks - 1;
         float* cdst = ckpt + (((int64_t)seq * nckpt + jslot) * H + h) * (int64_t)D * D;
 #pragma unroll
         for (int i = 0; i < CBW; ++i)
@@ -909,17 +1010,23 @@ __global__ __launch_bounds__(kThreads) void kda_state_pass(
     // the next chunk's first barrier (after every wave read sWt).
   };
 
-  // The prefetch is unconditional (past the end it re-reads the last record)
-  // so no branch sits between a load and its use: the wait counter then only
+  // Fragments are prefetched two chunks ahead in three register sets (the
+  // loop is unrolled by three so each set stays in fixed registers).  Every
+  // prefetch is unconditional (past the end it re-reads the last record) so
+  // no branch sits between a load and its use: the wait counter then only
   // waits for the set being consumed.
-  F fa, fb;
-  fa.load(rec_of(slot0), wave, lane, n0);
-  for (int64_t slot = slot0; slot < slot1; slot += 2) {
-    fb.load(rec_of(min(slot + 1, slot1 - 1)), wave, lane, n0);
+  F fa, fb, fc;
+  fa.load(rsrc, soff_of(slot0), offs);
+  fb.load(rsrc, soff_of(min(slot0 + 1, slot1 - 1)), offs);
+  for (int64_t slot = slot0; slot < slot1; slot += 3) {
+    fc.load(rsrc, soff_of(min(slot + 2, slot1 - 1)), offs);
     step(fa, slot);
     if (slot + 1 >= slot1) break;
-    fa.load(rec_of(min(slot + 2, slot1 - 1)), wave, lane, n0);
+    fa.load(rsrc, soff_of(min(slot + 3, slot1 - 1)), offs);
     step(fb, slot + 1);
+    if (slot + 2 >= slot1) break;
+    fb.load(rsrc, soff_of(min(slot + 4, slot1 - 1)), offs);
+    step(fc, slot + 2);
   }
 
   if (dst != nullptr) {
