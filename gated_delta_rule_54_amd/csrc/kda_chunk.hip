@@ -79,6 +79,12 @@ __device__ __forceinline__ uint16_t bf_bits(float x) {
   return __bfloat16_as_ushort(__float2bfloat16(x));
 }
 __device__ __forceinline__ float bf_val(uint32_t b) { return __uint_as_float(b << 16); }
+// Two values to a bf16 pair (v_cvt_pk_bf16_f32, round-to-nearest-even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const bf16* p) {
@@ -94,10 +100,7 @@ __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 __device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
-  uint2 u;
-  u.x = (uint32_t)bf_bits(a) | ((uint32_t)bf_bits(b) << 16);
-  u.y = (uint32_t)bf_bits(c) | ((uint32_t)bf_bits(d) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 // Load 4 consecutive elements as floats.
 __device__ __forceinline__ f32x4_t ld4(const float* p) {
@@ -193,16 +196,85 @@ __device__ __forceinline__ typename Mma<T>::frag frag_at(const T* base, int ld, 
                       Mma<T>::KPL * (lane >> 4));
 }
 
+// The summed index k of a product may be permuted freely as long as both
+// operands use the same permutation.  Operands that K2 loads use the one
+// below inside each k-step: position kpos(k) holds index k.  It is chosen so
+// that the four consecutive accumulator rows 4*(l/16)+j a lane holds form
+// one contiguous piece of an operand fragment when the accumulator's rows
+// are the k index -- the intra-chunk kernel then stores its products
+// directly in operand order, and K2 loads each fragment as 64 lanes x KPL
+// contiguous elements.
+//   bf16 (k-step 32): position 8g+e holds k = 4g+e (e < 4), 16+4g+(e-4) (e >= 4)
+//   fp32 (k-step 4, blocks of 16): position 4s+g holds k = 4g+s
+template <typename T> __device__ __forceinline__ int kpos(int k);
+template <> __device__ __forceinline__ int kpos<bf16>(int k) {
+  const int cc = k & 31;
+  return (k & ~31) + ((cc & 15) >> 2) * 8 + (cc >> 4) * 4 + (cc & 3);
+}
+template <> __device__ __forceinline__ int kpos<float>(int k) {
+  const int cc = k & 15;
+  return (k & ~15) + (cc & 3) * 4 + (cc >> 2);
+}
+// Operand-order ("fragment-native") matrix with rows m and nks k-steps:
+// 16-row tile, then k-step, then the 64 lanes' KPL elements.  Element (m, k):
+template <typename T>
+__device__ __forceinline__ int fnat(int m, int k, int nks) {
+  using M = Mma<T>;
+  const int p = kpos<T>(k);
+  const int q = p % M::KSTEP;
+  return (((m >> 4) * nks + p / M::KSTEP) * 64 + (m & 15) + 16 * (q / M::KPL)) * M::KPL +
+         q % M::KPL;
+}
+// Stores of k-runs of row m into a fragment-native matrix (k0 % 4 == 0 for
+// runs of 4, k0 % 8 == 0 for runs of 8, k0 even for pairs).  For bf16 a run
+// of 4 is one 8-byte piece; fp32 scatters.
+__device__ __forceinline__ void st_fnat4(bf16* base, int nks, int m, int k0, float a, float b,
+                                         float c, float d) {
+  *reinterpret_cast<uint2*>(base + fnat<bf16>(m, k0, nks)) =
+      make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ void st_fnat4(float* base, int nks, int m, int k0, float a, float b,
+                                         float c, float d) {
+  base[fnat<float>(m, k0, nks)] = a;
+  base[fnat<float>(m, k0 + 1, nks)] = b;
+  base[fnat<float>(m, k0 + 2, nks)] = c;
+  base[fnat<float>(m, k0 + 3, nks)] = d;
+}
+template <typename T>
+__device__ __forceinline__ void st_fnat8(T* base, int nks, int m, int k0, const float* x) {
+  st_fnat4(base, nks, m, k0, x[0], x[1], x[2], x[3]);
+  st_fnat4(base, nks, m, k0 + 4, x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void st_fnat2(bf16* base, int nks, int m, int k0, float a, float b) {
+  *reinterpret_cast<uint32_t*>(base + fnat<bf16>(m, k0, nks)) = pack_bf16x2(a, b);
+}
+__device__ __forceinline__ void st_fnat2(float* base, int nks, int m, int k0, float a, float b) {
+  base[fnat<float>(m, k0, nks)] = a;
+  base[fnat<float>(m, k0 + 1, nks)] = b;
+}
+// Four consecutive k (k0 % 4 == 0) into an LDS row whose columns follow kpos.
+__device__ __forceinline__ void st_perm4(bf16* row, int k0, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(row + kpos<bf16>(k0)) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ void st_perm4(float* row, int k0, float a, float b, float c, float d) {
+  row[kpos<float>(k0)] = a;
+  row[kpos<float>(k0 + 1)] = b;
+  row[kpos<float>(k0 + 2)] = c;
+  row[kpos<float>(k0 + 3)] = d;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace record of one (head, chunk slot): the operands K2 reads.
 template <typename T, int D>
 struct Rec {
-  // element offsets inside a record (in units of T), then gamma (fp32)
-  static constexpr int64_t QG = 0;                 // [64][D]  q^ o e^G
-  static constexpr int64_t KT = QG + kC * D;       // [D][64]  (k^ o e^(gamma-G))^T
-  static constexpr int64_t WN = KT + D * kC;       // [64][D]  -Wk
-  static constexpr int64_t UT = WN + kC * D;       // [D][64]  U^T
-  static constexpr int64_t P = UT + D * kC;        // [64][64] P (zero above the diagonal)
+  // element offsets inside a record (in units of T), then gamma (fp32).
+  // QG, KT, WN and P are fragment-native (see fnat) with the k index named;
+  // U is stored as 16x16 accumulator tiles [n/16][r/16][lane][4].
+  static constexpr int64_t QG = 0;                 // rows r, k = channel: q^ o e^G
+  static constexpr int64_t KT = QG + kC * D;       // rows channel, k = r: k^ o e^(gamma-G)
+  static constexpr int64_t WN = KT + D * kC;       // rows r, k = channel: -Wk
+  static constexpr int64_t UT = WN + kC * D;       // U (rows r, columns n) as tiles
+  static constexpr int64_t P = UT + D * kC;        // rows r, k = i: P (zero for i > r)
   static constexpr int64_t END = P + kC * kC;
   static constexpr int64_t BYTES_T = END * (int64_t)sizeof(T);
   static constexpr int64_t BYTES = ((BYTES_T + D * 4 + 255) / 256) * 256;  // + e^gamma
@@ -355,7 +427,7 @@ __device__ __forceinline__ void st_tile_f32(float* C, int ldc, f32x4_t v, float 
 __device__ __forceinline__ void st8(bf16* p, const float* x) {
   u32x4_t u;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) u[t] = (uint32_t)bf_bits(x[2 * t]) | ((uint32_t)bf_bits(x[2 * t + 1]) << 16);
+  for (int t = 0; t < 4; ++t) u[t] = pack_bf16x2(x[2 * t], x[2 * t + 1]);
   *reinterpret_cast<u32x4_t*>(p) = u;
 }
 __device__ __forceinline__ void st8(float* p, const float* x) {
@@ -372,7 +444,7 @@ __device__ __forceinline__ void st2(float* p, float a, float b) {
   *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
 __device__ __forceinline__ void st2(bf16* p, float a, float b) {
-  *reinterpret_cast<uint32_t*>(p) = (uint32_t)bf_bits(a) | ((uint32_t)bf_bits(b) << 16);
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
 }
 
 // fp32 operands at d = 128 need every VGPR of a one-workgroup-per-CU launch.
@@ -505,7 +577,7 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       const float khx = kk[j].x * rk, khy = kk[j].y * rk;
       const float qhx = qq[j].x * rq, qhy = qq[j].y * rq;
       const float egx = __expf(G[j].x), egy = __expf(G[j].y);
-      st2(wQG + r * D + c0, qhx * egx, qhy * egy);
+      st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
       kgT[0][j & 7] = khx * egx;
       kgT[1][j & 7] = khy * egy;
       if (!exact) {
@@ -525,8 +597,8 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
         const int rb = r0p + (j & ~7);
         st8(r3 + c0 * L::LDT + rb, kgT[0]);                  // (K o e^G)^T
         st8(r3 + (c0 + 1) * L::LDT + rb, kgT[1]);
-        st8(wKT + c0 * kC + rb, ktT[0]);                     // (K o e^(gamma-G))^T
-        st8(wKT + (c0 + 1) * kC + rb, ktT[1]);
+        st_fnat8(wKT, kC / M::KSTEP, c0, rb, ktT[0]);       // K o e^(gamma-G), rows c
+        st_fnat8(wKT, kC / M::KSTEP, c0 + 1, rb, ktT[1]);
       }
     }
   }
@@ -607,12 +679,12 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       if (er[m] < 0) continue;
       const int r = er[m], i = ei[m];
       sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[m] : 0.f;
-      st_f(wP + r * kC + i, ep[m]);
+      st_f(wP + fnat<T>(r, i, kC / M::KSTEP), ep[m]);
     }
     // the exact path writes no upper-triangle entries of the diagonal blocks
     for (int e = tid; e < kC * kC; e += kThreads) {
       const int r = e >> 6, i = e & 63;
-      if (i > r && (i >> 4) == (r >> 4)) st_f(wP + r * kC + i, 0.f);
+      if (i > r && (i >> 4) == (r >> 4)) st_f(wP + fnat<T>(r, i, kC / M::KSTEP), 0.f);
     }
   }
   if (!exact) {
@@ -632,7 +704,7 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
         p4[j] = (i0 + j <= r) ? accP[p][j] : 0.f;
       }
       *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-      st4(wP + r * kC + i0, p4[0], p4[1], p4[2], p4[3]);
+      st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
     }
   }
   {
@@ -640,7 +712,7 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
     const int zR[6] = {0, 0, 0, 1, 1, 2}, zI[6] = {1, 2, 3, 2, 3, 3};
     for (int z = wave; z < 6; z += 4) {
       const int r = zR[z] * 16 + (lane & 15), i0 = zI[z] * 16 + 4 * (lane >> 4);
-      st4(wP + r * kC + i0, 0.f, 0.f, 0.f, 0.f);
+      st_fnat4(wP, kC / M::KSTEP, r, i0, 0.f, 0.f, 0.f, 0.f);
     }
   }
   // V^T into region 0 (its row-major content is dead now), 8 rows per store
@@ -740,12 +812,11 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
         u = M::mma(tb[ks], frag_at<T>(r0, L::LDT, nb * 16, ks, lane), u);   // B = V^T rows
         wk = M::mma(frag_at<T>(r3, L::LDT, nb * 16, ks, lane), tb[ks], wk);  // A = KG^T rows
       }
-      // u: rows r = rb*16 + 4*(lane/16) + j, column n = nb*16 + lane%16  -> U^T[n][r..r+3]
-      const int n = nb * 16 + (lane & 15), r4 = rb * 16 + 4 * (lane >> 4);
-      st4(wUT + n * kC + r4, u[0], u[1], u[2], u[3]);
+      // u: rows r = rb*16 + 4*(lane/16) + j, column n = nb*16 + lane%16 -> tile (nb, rb)
+      st4(wUT + ((nb * (kC / 16) + rb) * 64 + lane) * 4, u[0], u[1], u[2], u[3]);
       // wk: rows c = nb*16 + 4*(lane/16) + j of Wk^T, column r = rb*16 + lane%16
       const int c4 = nb * 16 + 4 * (lane >> 4), r = rb * 16 + (lane & 15);
-      st4(wWN + r * D + c4, -wk[0], -wk[1], -wk[2], -wk[3]);
+      st_fnat4(wWN, D / M::KSTEP, r, c4, -wk[0], -wk[1], -wk[2], -wk[3]);
     }
   }
 }
@@ -763,11 +834,6 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
 // Buffer-resource loads: one resource per head's records, a per-lane 32-bit
 // offset computed once, the slot's record offset in a scalar register and the
 // fragment's constant offset in the instruction -- no per-load address math.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2_t v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 template <typename T> struct BufFrag;
 template <> struct BufFrag<bf16> {
   static __device__ __forceinline__ bf16x8_t load(__amdgpu_buffer_rsrc_t r, uint32_t off,
@@ -801,21 +867,13 @@ template <> struct BufRaw4<float> {
   }
   __device__ __forceinline__ f32x4_t get() const { return __builtin_bit_cast(f32x4_t, v); }
 };
-// Store 4 consecutive elements to LDS / global from floats.
-__device__ __forceinline__ void st4p(bf16* p, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-}
-__device__ __forceinline__ void st4p(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
-
 // Per-wave fragments of one chunk's record (see kda_state_pass).
 template <typename T, int D, int WS>
 struct K2Frags {
   using M = Mma<T>;
   using R = Rec<T, D>;
   static constexpr int NB = WS / 16, CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
-  static constexpr uint32_t ES = sizeof(T);
+  static constexpr uint32_t ES = sizeof(T), FB = M::KPL * ES;  // bytes of a lane's fragment
   typename M::frag wn[KD], qg[KD], p[KC], kt[CBW][KC];
   BufRaw4<T> ut[NB];
   BufRaw4<float> eg[CBW];
@@ -823,31 +881,30 @@ struct K2Frags {
   // lane offsets (bytes within a record), computed once per workgroup
   struct Offs { uint32_t wn, qg, p, kt, ut, eg; };
   static __device__ __forceinline__ Offs offsets(int wave, int lane, int n0) {
-    const uint32_t row = wave * 16 + (lane & 15), kg = M::KPL * (lane >> 4);
     Offs o;
-    o.wn = (uint32_t)(R::WN * ES) + (row * D + kg) * ES;
-    o.qg = (uint32_t)(R::QG * ES) + (row * D + kg) * ES;
-    o.p = (uint32_t)(R::P * ES) + (row * kC + kg) * ES;
-    o.kt = (uint32_t)(R::KT * ES) + ((wave * CBW * 16 + (lane & 15)) * kC + kg) * ES;
-    o.ut = (uint32_t)(R::UT * ES) + ((n0 + (lane & 15)) * kC + wave * 16 + 4 * (lane >> 4)) * ES;
+    o.wn = (uint32_t)(R::WN * ES) + ((wave * KD) * 64 + lane) * FB;
+    o.qg = (uint32_t)(R::QG * ES) + ((wave * KD) * 64 + lane) * FB;
+    o.p = (uint32_t)(R::P * ES) + ((wave * KC) * 64 + lane) * FB;
+    o.kt = (uint32_t)(R::KT * ES) + ((wave * CBW * KC) * 64 + lane) * FB;
+    o.ut = (uint32_t)(R::UT * ES) + (((n0 / 16) * (kC / 16) + wave) * 64 + lane) * 4 * ES;
     o.eg = (uint32_t)R::BYTES_T + (wave * CBW * 16 + 4 * (lane >> 4)) * 4;
     return o;
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
-      wn[ks] = BufFrag<T>::load(r, o.wn + ks * M::KSTEP * ES, soff);
-      qg[ks] = BufFrag<T>::load(r, o.qg + ks * M::KSTEP * ES, soff);
+      wn[ks] = BufFrag<T>::load(r, o.wn + ks * 64 * FB, soff);
+      qg[ks] = BufFrag<T>::load(r, o.qg + ks * 64 * FB, soff);
     }
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks) p[ks] = BufFrag<T>::load(r, o.p + ks * M::KSTEP * ES, soff);
+    for (int ks = 0; ks < KC; ++ks) p[ks] = BufFrag<T>::load(r, o.p + ks * 64 * FB, soff);
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks)
-        kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * 16 * kC + ks * M::KSTEP) * ES, soff);
+        kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * KC + ks) * 64 * FB, soff);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ut[nb].load(r, o.ut + nb * 16 * kC * ES, soff);
+    for (int nb = 0; nb < NB; ++nb) ut[nb].load(r, o.ut + nb * (kC / 16) * 64 * 4 * ES, soff);
 #pragma unroll
     for (int i = 0; i < CBW; ++i) eg[i].load(r, o.eg + i * 64, soff);
   }
@@ -914,19 +971,25 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(ws + (int64_t)h * nrec * R::BYTES), (short)0, (int)(nrec * R::BYTES), 0x00020000);
   const typename F::Offs offs = F::offsets(wave, lane, n0);
-  auto soff_of = [&](int64_t slot) { return (uint32_t)((slot - s0) * R::BYTES); };
 
-  // Output row of this lane for the chunk at slot0; later chunks are whole
-  // chunks further on (kC tokens * H heads * D elements per chunk).
+  // The loop runs over 32-bit record indices j in [j0, j1) relative to the
+  // segment (64-bit scalar compares would need vector temporaries, whose
+  // reuse makes the compiler drain the prefetched loads).
+  const int j0 = (int)(slot0 - s0), j1 = (int)(slot1 - s0);
+  const int cdelta = (int)(s0 - sp.c0);             // chunk index = j + cdelta
+  const int ci_last = (int)((sp.ntok - 1) / kC);    // the sequence's last chunk
+  const int len_last = (int)(sp.ntok - (int64_t)ci_last * kC);
+  // Output row of this lane in the chunk at j0; each later chunk is kC
+  // tokens * H heads * D elements further on.
   const int r_out = wave * 16 + (lane & 15);
-  T* const obase = o + ((sp.tok0 + (slot0 - sp.c0) * kC + r_out) * H + h) * D + n0;
+  T* orow = o + ((sp.tok0 + (int64_t)(j0 + cdelta) * kC + r_out) * H + h) * D + n0;
   const int64_t ostride = (int64_t)kC * H * D;
   // checkpoints fall after every ck_chunks whole chunks of the sequence
   const int ck_chunks = ckpt != nullptr ? (int)(ckpt_every / kC) : 1;
 
-  auto step = [&](const F& f, int64_t slot) {
-    const int ci = (int)(slot - sp.c0);  // chunk index within the sequence
-    const int len = (int)min<int64_t>(kC, sp.ntok - (int64_t)ci * kC);
+  auto step = [&](const F& f, int j) {
+    const int ci = j + cdelta;  // chunk index within the sequence
+    const int len = ci == ci_last ? len_last : kC;
 
     // (a) S -> LDS as S^T in the MFMA type
 #pragma unroll
@@ -935,7 +998,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       for (int nb = 0; nb < NB; ++nb) {
         const int c4 = (wave * CBW + i) * 16 + 4 * (lane >> 4);
         const int n = nb * 16 + (lane & 15);
-        st4p(sSt + n * LDS_S + c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
+        st_perm4(sSt + n * LDS_S, c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
       }
     __syncthreads();
 
@@ -955,7 +1018,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = nb * 16 + (lane & 15);
-      st4p(sWt + n * LDS_W + wave * 16 + 4 * (lane >> 4), W[nb][0], W[nb][1], W[nb][2], W[nb][3]);
+      st_perm4(sWt + n * LDS_W, wave * 16 + 4 * (lane >> 4), W[nb][0], W[nb][1], W[nb][2], W[nb][3]);
     }
     __syncthreads();
 
@@ -982,10 +1045,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
 
     // (e) output rows of this wave's block: O^T[n][r] -> o[tok0 + r][h][n0 + n]
     if (r_out < len) {
-      T* orow = obase + (slot - slot0) * ostride;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        st4p(orow + nb * 16 + 4 * (lane >> 4), scale * O[nb][0], scale * O[nb][1],
+        st4(orow + nb * 16 + 4 * (lane >> 4), scale * O[nb][0], scale * O[nb][1],
              scale * O[nb][2], scale * O[nb][3]);
     }
 
@@ -1005,29 +1067,34 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
             }
       }
     }
+    orow += ostride;
     // No barrier here: the next chunk's sSt writes follow this chunk's
     // second barrier (after every wave read sSt), and its sWt writes follow
     // the next chunk's first barrier (after every wave read sWt).
   };
 
-  // Fragments are prefetched two chunks ahead in three register sets (the
-  // loop is unrolled by three so each set stays in fixed registers).  Every
-  // prefetch is unconditional (past the end it re-reads the last record) so
-  // no branch sits between a load and its use: the wait counter then only
-  // waits for the set being consumed.
+  // Fragments are prefetched two chunks ahead in three register sets; the
+  // loop body is three whole steps, so each set stays in fixed registers,
+  // and the one or two steps left over run after it.  Every prefetch is
+  // unconditional (past the end it re-reads the last record) and the loop
+  // has no early exit, so the in-order wait counter only ever waits for the
+  // set being consumed.
   F fa, fb, fc;
-  fa.load(rsrc, soff_of(slot0), offs);
-  fb.load(rsrc, soff_of(min(slot0 + 1, slot1 - 1)), offs);
-  for (int64_t slot = slot0; slot < slot1; slot += 3) {
-    fc.load(rsrc, soff_of(min(slot + 2, slot1 - 1)), offs);
-    step(fa, slot);
-    if (slot + 1 >= slot1) break;
-    fa.load(rsrc, soff_of(min(slot + 3, slot1 - 1)), offs);
-    step(fb, slot + 1);
-    if (slot + 2 >= slot1) break;
-    fb.load(rsrc, soff_of(min(slot + 4, slot1 - 1)), offs);
-    step(fc, slot + 2);
+  auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
+  fa.load(rsrc, soff(j0), offs);
+  __asm__ volatile("" ::: "memory");  // issue the first set's loads first
+  fb.load(rsrc, soff(min(j0 + 1, j1 - 1)), offs);
+  int j = j0;
+  for (; j + 3 <= j1; j += 3) {
+    fc.load(rsrc, soff(min(j + 2, j1 - 1)), offs);
+    step(fa, j);
+    fa.load(rsrc, soff(min(j + 3, j1 - 1)), offs);
+    step(fb, j + 1);
+    fb.load(rsrc, soff(min(j + 4, j1 - 1)), offs);
+    step(fc, j + 2);
   }
+  if (j < j1) step(fa, j);
+  if (j + 1 < j1) step(fb, j + 1);
 
   if (dst != nullptr) {
 #pragma unroll
