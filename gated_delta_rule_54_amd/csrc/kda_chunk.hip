@@ -65,7 +65,11 @@ constexpr int kC = 64;            // chunk length
 constexpr int kThreads = 256;     // 4 waves
 constexpr float kNormEps = 1e-6f;
 constexpr float kFastDecayBound = -80.f;
-constexpr int64_t kSegSlotsDefault = 1024;  // chunk slots per K1/K2 launch pair
+// One segment's records (all heads) are kept within kSegRecordBudget bytes,
+// so that they are still in the last-level cache (256 MB on MI355X) when the
+// state pass reads them right after the intra-chunk kernel wrote them.
+constexpr int64_t kSegRecordBudget = 160ll << 20;
+constexpr int64_t kSegSlotsMax = 1024;  // chunk slots per K1/K2 launch pair, at most
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -867,6 +871,25 @@ template <> struct BufRaw4<float> {
   }
   __device__ __forceinline__ f32x4_t get() const { return __builtin_bit_cast(f32x4_t, v); }
 };
+// Four consecutive elements from floats, as one buffer store.
+template <typename T> struct BufStore4;
+template <> struct BufStore4<bf16> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float a,
+                                               float b, float c, float d) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  }
+};
+template <> struct BufStore4<float> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float a,
+                                               float b, float c, float d) {
+    const u32x4_t v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c),
+                       __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  }
+};
+
 // Per-wave fragments of one chunk's record (see kda_state_pass).
 template <typename T, int D, int WS>
 struct K2Frags {
@@ -890,23 +913,39 @@ struct K2Frags {
     o.eg = (uint32_t)R::BYTES_T + (wave * CBW * 16 + 4 * (lane >> 4)) * 4;
     return o;
   }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
+  // The loads come in four groups so that a step can spread them between
+  // its phases: a CU's vector memory path takes ~1 KiB per 16 cycles, and
+  // a wave that issues a whole record at once stalls behind it.
+  template <int PART>
+  __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
+    // in the order a step consumes them: U and -Wk (W), Q o e^G (O), e^gamma
+    // and K~ (state update), P (O)
+    if constexpr (PART == 0) {
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) {
-      wn[ks] = BufFrag<T>::load(r, o.wn + ks * 64 * FB, soff);
-      qg[ks] = BufFrag<T>::load(r, o.qg + ks * 64 * FB, soff);
+      for (int nb = 0; nb < NB; ++nb) ut[nb].load(r, o.ut + nb * (kC / 16) * 64 * 4 * ES, soff);
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) wn[ks] = BufFrag<T>::load(r, o.wn + ks * 64 * FB, soff);
+    } else if constexpr (PART == 1) {
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) qg[ks] = BufFrag<T>::load(r, o.qg + ks * 64 * FB, soff);
+    } else if constexpr (PART == 2) {
+#pragma unroll
+      for (int i = 0; i < CBW; ++i) eg[i].load(r, o.eg + i * 64, soff);
+#pragma unroll
+      for (int i = 0; i < CBW; ++i)
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks)
+          kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * KC + ks) * 64 * FB, soff);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) p[ks] = BufFrag<T>::load(r, o.p + ks * 64 * FB, soff);
     }
-#pragma unroll
-    for (int ks = 0; ks < KC; ++ks) p[ks] = BufFrag<T>::load(r, o.p + ks * 64 * FB, soff);
-#pragma unroll
-    for (int i = 0; i < CBW; ++i)
-#pragma unroll
-      for (int ks = 0; ks < KC; ++ks)
-        kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * KC + ks) * 64 * FB, soff);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ut[nb].load(r, o.ut + nb * (kC / 16) * 64 * 4 * ES, soff);
-#pragma unroll
-    for (int i = 0; i < CBW; ++i) eg[i].load(r, o.eg + i * 64, soff);
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
+    load_part<0>(r, soff, o);
+    load_part<1>(r, soff, o);
+    load_part<2>(r, soff, o);
+    load_part<3>(r, soff, o);
   }
 };
 
@@ -979,15 +1018,39 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   const int cdelta = (int)(s0 - sp.c0);             // chunk index = j + cdelta
   const int ci_last = (int)((sp.ntok - 1) / kC);    // the sequence's last chunk
   const int len_last = (int)(sp.ntok - (int64_t)ci_last * kC);
-  // Output row of this lane in the chunk at j0; each later chunk is kC
-  // tokens * H heads * D elements further on.
-  const int r_out = wave * 16 + (lane & 15);
-  T* orow = o + ((sp.tok0 + (int64_t)(j0 + cdelta) * kC + r_out) * H + h) * D + n0;
-  const int64_t ostride = (int64_t)kC * H * D;
-  // checkpoints fall after every ck_chunks whole chunks of the sequence
+  const int r_out = wave * 16 + (lane & 15);  // this lane's output row in a chunk
+  const int64_t ostride = (int64_t)kC * H * D;  // elements from one chunk's rows to the next's
+  // Checkpoints fall after every ck_chunks whole chunks of the sequence;
+  // ck_left counts the chunks up to and including the next one.
   const int ck_chunks = ckpt != nullptr ? (int)(ckpt_every / kC) : 1;
+  int ck_left = ck_chunks - (j0 + cdelta) % ck_chunks;
 
-  auto step = [&](const F& f, int j) {
+  // Output of a chunk is stored during the next step (so the store never
+  // waits for the MFMA pipe): O holds the pending chunk's O^T, o_pend its
+  // first row for this lane's column block, len_pend its valid rows.  The
+  // store is a buffer store whose bound ends after row len_pend - 1, so rows
+  // past a sequence's end are dropped by the hardware, without a branch.
+  f32x4_t O[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  T* o_pend = o + ((sp.tok0 + (int64_t)(j0 + cdelta) * kC) * H + h) * D + n0;
+  int len_pend = 0;
+  const uint32_t o_voff = (uint32_t)((r_out * H * D + 4 * (lane >> 4)) * sizeof(T));
+  auto store_o = [&]() {
+    const int nbytes = len_pend > 0 ? ((len_pend - 1) * H * D + WS) * (int)sizeof(T) : 0;
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc((void*)o_pend, (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      BufStore4<T>::store(ro, o_voff + nb * 16 * sizeof(T), scale * O[nb][0], scale * O[nb][1],
+                          scale * O[nb][2], scale * O[nb][3]);
+  };
+
+  auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
+  // One chunk step: consumes the fragments in f and fills fn with those of
+  // record jn (clamped to the last record), the loads spread over the step.
+  auto step = [&](const F& f, F& fn, int j, int jn) {
+    const uint32_t son = soff(min(jn, j1 - 1));
     const int ci = j + cdelta;  // chunk index within the sequence
     const int len = ci == ci_last ? len_last : kC;
 
@@ -1002,18 +1065,34 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       }
     __syncthreads();
 
-    // (b) W = U + (-Wk) S (this wave's 16 rows) and O^T = S^T (Q o e^G)^T
-    f32x4_t W[NB], O[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) { W[nb] = f.ut[nb].get(); O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+    // (b) W = U + (-Wk) S for this wave's 16 rows -- the chain's critical
+    // path -- is issued first; then the previous chunk's output store and
+    // O^T = S^T (Q o e^G)^T, which overlap the W -> LDS hand-off.
+    typename M::frag sfr[NB][KD];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const auto sfr = frag_at<T>(sSt, LDS_S, nb * 16, ks, lane);
-        W[nb] = M::mma(f.wn[ks], sfr, W[nb]);
-        O[nb] = M::mma(sfr, f.qg[ks], O[nb]);
-      }
+      for (int nb = 0; nb < NB; ++nb) sfr[nb][ks] = frag_at<T>(sSt, LDS_S, nb * 16, ks, lane);
+    f32x4_t W[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) W[nb] = f.ut[nb].get();
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) W[nb] = M::mma(f.wn[ks], sfr[nb][ks], W[nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    fn.template load_part<0>(rsrc, son, offs);
+    store_o();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(sfr[nb][ks], f.qg[ks], O[nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    fn.template load_part<1>(rsrc, son, offs);
+    __builtin_amdgcn_sched_barrier(0);
+
     // (c) W -> LDS as W^T
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -1022,7 +1101,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     }
     __syncthreads();
 
-    // (d) S = Diag(e^gamma) S + K~^T W  (the chain's critical path) ; O^T += W^T P^T
+    // (d) S = Diag(e^gamma) S + K~^T W first (critical path), then O^T += W^T P^T
     typename M::frag wf[NB][KC];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -1038,22 +1117,21 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
 #pragma unroll
         for (int ks = 0; ks < KC; ++ks) S[i][nb] = M::mma(f.kt[i][ks], wf[nb][ks], S[i][nb]);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    fn.template load_part<2>(rsrc, son, offs);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(wf[nb][ks], f.p[ks], O[nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    fn.template load_part<3>(rsrc, son, offs);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // (e) output rows of this wave's block: O^T[n][r] -> o[tok0 + r][h][n0 + n]
-    if (r_out < len) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        st4(orow + nb * 16 + 4 * (lane >> 4), scale * O[nb][0], scale * O[nb][1],
-             scale * O[nb][2], scale * O[nb][3]);
-    }
-
-    // (f) checkpoint after every ckpt_every tokens (dense, chunk-aligned)
-    if (ckpt != nullptr) {
-      if (len == kC && (ci + 1) % ck_chunks == 0) {
+    // (e) checkpoint after every ckpt_every tokens (dense, chunk-aligned)
+    if (ckpt != nullptr && --ck_left == 0) {
+      ck_left = ck_chunks;
+      if (len == kC) {
         const int64_t jslot = (ci + 1) / ck_chunks - 1;
         float* cdst = ckpt + (((int64_t)seq * nckpt + jslot) * H + h) * (int64_t)D * D;
 #pragma unroll
@@ -1067,11 +1145,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
             }
       }
     }
-    orow += ostride;
+    // this chunk's output is now pending
+    o_pend = j == j0 ? o_pend : o_pend + ostride;
+    len_pend = len;
     // No barrier here: the next chunk's sSt writes follow this chunk's
     // second barrier (after every wave read sSt), and its sWt writes follow
     // the next chunk's first barrier (after every wave read sWt).
   };
+
 
   // Fragments are prefetched two chunks ahead in three register sets; the
   // loop body is three whole steps, so each set stays in fixed registers,
@@ -1080,21 +1161,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   // has no early exit, so the in-order wait counter only ever waits for the
   // set being consumed.
   F fa, fb, fc;
-  auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
   fa.load(rsrc, soff(j0), offs);
   __asm__ volatile("" ::: "memory");  // issue the first set's loads first
   fb.load(rsrc, soff(min(j0 + 1, j1 - 1)), offs);
   int j = j0;
   for (; j + 3 <= j1; j += 3) {
-    fc.load(rsrc, soff(min(j + 2, j1 - 1)), offs);
-    step(fa, j);
-    fa.load(rsrc, soff(min(j + 3, j1 - 1)), offs);
-    step(fb, j + 1);
-    fb.load(rsrc, soff(min(j + 4, j1 - 1)), offs);
-    step(fc, j + 2);
+    step(fa, fc, j, j + 2);
+    step(fb, fa, j + 1, j + 3);
+    step(fc, fb, j + 2, j + 4);
   }
-  if (j < j1) step(fa, j);
-  if (j + 1 < j1) step(fb, j + 1);
+  if (j < j1) step(fa, fc, j, j + 2);
+  if (j + 1 < j1) step(fb, fa, j + 1, j + 3);
+  store_o();
 
   if (dst != nullptr) {
 #pragma unroll
@@ -1134,15 +1212,20 @@ int64_t rec_bytes_for(const kda_desc_t& d) {
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// Segment length in chunk slots; KDA_SEG_SLOTS (read once) overrides it for
-// tuning.  It fixes the workspace size, so it never changes after first use.
-int64_t seg_slots() {
-  static const int64_t v = [] {
+// Segment length in chunk slots: the record budget over the records of one
+// slot (all heads), a multiple of 8 in [8, kSegSlotsMax].  KDA_SEG_SLOTS
+// (read once) overrides it for tuning.  It fixes the workspace size, so it
+// depends only on the descriptor.
+int64_t seg_slots(const kda_desc_t& d) {
+  static const int64_t env = [] {
     const char* e = getenv("KDA_SEG_SLOTS");
     const long long x = e ? atoll(e) : 0;
-    return x >= 8 && x <= (1 << 20) ? (int64_t)x : kSegSlotsDefault;
+    return x >= 8 && x <= (1 << 20) ? (int64_t)x : (int64_t)0;
   }();
-  return v;
+  if (env) return env;
+  const int64_t per_slot = (int64_t)d.heads * rec_bytes_for(d);
+  const int64_t s = (kSegRecordBudget / per_slot) & ~(int64_t)7;
+  return std::max<int64_t>(8, std::min<int64_t>(kSegSlotsMax, s));
 }
 
 Plan make_plan(const kda_desc_t& d, bool varlen) {
@@ -1150,10 +1233,10 @@ Plan make_plan(const kda_desc_t& d, bool varlen) {
   const int64_t T = d.seqlen;
   p.slot_bound = varlen ? (T + (int64_t)(kC - 1) * d.num_seqs) / kC
                         : (int64_t)d.batch * ((T + kC - 1) / kC);
-  p.seg_slots = std::min<int64_t>(p.slot_bound, seg_slots());
+  p.seg_slots = std::min<int64_t>(p.slot_bound, seg_slots(d));
   p.rec_bytes = rec_bytes_for(d);
   p.rec_total = p.seg_slots * d.heads * p.rec_bytes;
-  p.carry_bytes = p.slot_bound > seg_slots()
+  p.carry_bytes = p.slot_bound > seg_slots(d)
                       ? (int64_t)d.num_seqs * d.heads * d.dk * d.dv * 4 : 0;
   p.map_bytes = varlen ? 2 * align256(((int64_t)d.num_seqs + 1) * 4) : 0;
   return p;
@@ -1189,7 +1272,7 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                        d.seqlen, cu_s, chunk_off);
     gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
   }
-  const int64_t SS = seg_slots();
+  const int64_t SS = seg_slots(d);
   const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + SS - 1) / SS;
   for (int64_t s = 0; s < nseg; ++s) {
     const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
