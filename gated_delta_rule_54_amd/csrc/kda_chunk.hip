@@ -1254,7 +1254,11 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   float* carry = p.carry_bytes ? reinterpret_cast<float*>(ws + p.rec_total) : nullptr;
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.rec_total + p.carry_bytes);
   int32_t* cu_s = chunk_off + (p.map_bytes / 2) / 4;  // sanitised cu_seqlens
-  constexpr int WS = 32;  // d_v slice per K2 workgroup
+  // d_v columns per K2 workgroup: the smallest MFMA tile width.  A
+  // workgroup loads the same per-chunk operands whatever its width, so
+  // narrower slices spread the per-step math over more CUs at no extra
+  // per-CU traffic (one (sequence, head) chain then occupies D/16 CUs).
+  constexpr int WS = 16;
   const int nslice = D / WS;
   const int nhpad = (NH + 7) / 8 * 8;
   const int k1_lds = K1Lds<T, D>::BYTES;
