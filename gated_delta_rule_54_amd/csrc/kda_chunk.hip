@@ -392,6 +392,13 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restr
 // consecutive rows, for everything per-element.  A channel-pair thread holds
 // its rows contiguously, so the transposed buffers ((K o e^G)^T, V^T, K~^T)
 // are written 8 rows at a time with 16-byte stores.
+// K1 workgroup size.  LDS (~77 KiB per workgroup at d = 128) allows two
+// workgroups per CU; 512 threads per chunk then keep 16 waves per CU in
+// flight to hide the input loads, and halve each thread's rows and
+// registers.  fp32 operands keep 256 threads (their registers are full).
+template <typename T, int D>
+constexpr int k1_threads() { return (sizeof(T) == 2 && D == 128) ? 512 : 256; }
+
 template <typename T, int D>
 struct K1Lds {
   static constexpr int LDR = D + 8;        // row-major leading dim (elements)
@@ -403,9 +410,10 @@ struct K1Lds {
   static constexpr int FP = kC * LDA * 4;                     // fp32 A / T tile
   static constexpr int REG = ((MX > FP ? MX : FP) + 255) / 256 * 256;
   static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
-  static constexpr int NCP = D / 2;               // channel pairs
-  static constexpr int NPART = kThreads / NCP;    // row parts
-  static constexpr int RPP = kC / NPART;          // rows per part (16 or 8)
+  static constexpr int NCP = D / 2;                        // channel pairs
+  static constexpr int NPART = k1_threads<T, D>() / NCP;   // row parts
+  static constexpr int RPP = kC / NPART;                   // rows per part (8 or 16)
+  static_assert(RPP % 8 == 0, "transposed stores take 8 rows at a time");
   static constexpr int BYTES = 4 * REG + 4096 /*scratch*/ + 3 * kC * 4 + 16;
 };
 
@@ -456,7 +464,7 @@ template <typename T, int D>
 constexpr int k1_min_blocks() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_chunk(
+__global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void kda_intra_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
     int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws) {
@@ -464,7 +472,9 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   using M = Mma<T>;
   using R = Rec<T, D>;
   constexpr int NCP = L::NCP, NPART = L::NPART, RPP = L::RPP;
-  constexpr int QC = D / 4;  // channels per thread in the norm layout
+  constexpr int NT = k1_threads<T, D>(), NW = NT / 64;  // threads, waves
+  constexpr int NQ = NT / kC;  // threads per row in the norm layout
+  constexpr int QC = D / NQ;   // channels per thread in the norm layout
   extern __shared__ __align__(16) char smem[];
   T* r0 = reinterpret_cast<T*>(smem);
   T* r1 = reinterpret_cast<T*>(smem + L::REG);
@@ -514,7 +524,7 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
     vraw[j].load(vb + r * rowstride + c0);
   }
   // row layout for the norms (a second, cache-served read of q and k rows)
-  const int nr = tid >> 2, nq = tid & 3;
+  const int nr = tid / NQ, nq = tid % NQ;
   Raw4<T> nqr[QC / 4], nkr[QC / 4];
   {
     const int rr = min(nr, loc.len - 1);
@@ -544,8 +554,11 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
         sk += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
       }
     }
-    sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
-    sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
+#pragma unroll
+    for (int off = 1; off < NQ; off <<= 1) {
+      sq += __shfl_xor(sq, off);
+      sk += __shfl_xor(sk, off);
+    }
     if (nq == 0) {
       s_rq[nr] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
       s_rk[nr] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
@@ -611,36 +624,38 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   // ---- A (strict lower, x beta_r) and P (lower) ------------------------------
   // Tiles are computed transposed (A^T, P^T) so each lane's 4 accumulator
   // rows are 4 consecutive columns of A / P: one vector store each.  The 10
-  // block pairs (I <= R) and the 6 all-zero blocks of P above the diagonal
-  // are dealt to the waves.
-  const int pairI[4][3] = {{0, 0, 0}, {0, 1, 1}, {1, 2, -1}, {2, 3, -1}};
-  const int pairR[4][3] = {{0, 1, 2}, {3, 1, 2}, {3, 2, -1}, {3, 3, -1}};
-  f32x4_t accA[3], accP[3];
+  // block pairs (I <= R) are dealt to the waves round-robin (pair w, w+NW,
+  // ...), as are the 6 all-zero blocks of P above the diagonal.
+  constexpr int NPAIR = 10, PMAX = (NPAIR + NW - 1) / NW;
+  auto pair_I = [](int p) { return p < 4 ? 0 : p < 7 ? 1 : p < 9 ? 2 : 3; };
+  auto pair_R = [](int p) { return p < 4 ? p : p < 7 ? p - 3 : p < 9 ? p - 5 : 3; };
+  f32x4_t accA[PMAX], accP[PMAX];
   if (!exact) {
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      accA[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      accP[p] = accA[p];
-      const int I = pairI[wave][p], Rb = pairR[wave][p];
-      if (I < 0) continue;
+    for (int t = 0; t < PMAX; ++t) {
+      accA[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accP[t] = accA[t];
+      const int p = wave + t * NW;
+      if (p >= NPAIR) continue;
+      const int I = pair_I(p), Rb = pair_R(p);
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks) {
         const auto a = frag_at<T>(r2, L::LDR, I * 16, ks, lane);    // K o e^-G, rows I
         const auto bk = frag_at<T>(r0, L::LDR, Rb * 16, ks, lane);  // K o e^G, rows R
         const auto bq = frag_at<T>(r1, L::LDR, Rb * 16, ks, lane);  // Q o e^G, rows R
-        accA[p] = M::mma(a, bk, accA[p]);
-        accP[p] = M::mma(a, bq, accP[p]);
+        accA[t] = M::mma(a, bk, accA[t]);
+        accP[t] = M::mma(a, bq, accP[t]);
       }
     }
   } else {
     // Exact path: each entry from its own exponent difference (<= 0), with
     // G, k^, q^ staged through region 2 in blocks of 16 channels.
-    constexpr int NE = (kC * (kC + 1) / 2 + kThreads - 1) / kThreads;
+    constexpr int NE = (kC * (kC + 1) / 2 + NT - 1) / NT;
     float ea[NE], ep[NE];
     int er[NE], ei[NE];
 #pragma unroll
     for (int m = 0; m < NE; ++m) {
-      const int e = tid + m * kThreads;
+      const int e = tid + m * NT;
       int r = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
       while ((r + 1) * (r + 2) / 2 <= e) ++r;
       while (r * (r + 1) / 2 > e) --r;
@@ -686,7 +701,7 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       st_f(wP + fnat<T>(r, i, kC / M::KSTEP), ep[m]);
     }
     // the exact path writes no upper-triangle entries of the diagonal blocks
-    for (int e = tid; e < kC * kC; e += kThreads) {
+    for (int e = tid; e < kC * kC; e += NT) {
       const int r = e >> 6, i = e & 63;
       if (i > r && (i >> 4) == (r >> 4)) st_f(wP + fnat<T>(r, i, kC / M::KSTEP), 0.f);
     }
@@ -695,17 +710,18 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
     __syncthreads();  // all reads of regions 0..2 done; region 1 becomes A
     float* sA = reinterpret_cast<float*>(r1);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int I = pairI[wave][p], Rb = pairR[wave][p];
-      if (I < 0) continue;
+    for (int t = 0; t < PMAX; ++t) {
+      const int p = wave + t * NW;
+      if (p >= NPAIR) continue;
+      const int I = pair_I(p), Rb = pair_R(p);
       const int r = Rb * 16 + (lane & 15);
       const int i0 = I * 16 + 4 * (lane >> 4);
       const float br = s_beta[r];
       float a4[4], p4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a4[j] = (i0 + j < r) ? br * accA[p][j] : 0.f;
-        p4[j] = (i0 + j <= r) ? accP[p][j] : 0.f;
+        a4[j] = (i0 + j < r) ? br * accA[t][j] : 0.f;
+        p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
       }
       *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
       st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
@@ -714,7 +730,7 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
   {
     // zero blocks of P above the diagonal: (R, I) = (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
     const int zR[6] = {0, 0, 0, 1, 1, 2}, zI[6] = {1, 2, 3, 2, 3, 3};
-    for (int z = wave; z < 6; z += 4) {
+    for (int z = wave; z < 6; z += NW) {
       const int r = zR[z] * 16 + (lane & 15), i0 = zI[z] * 16 + 4 * (lane >> 4);
       st_fnat4(wP, kC / M::KSTEP, r, i0, 0.f, 0.f, 0.f, 0.f);
     }
@@ -762,34 +778,42 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
     st_tile_f32(sT + (b0 + 16) * L::LDA + b0, L::LDA, y, -1.f, lane);
   }
   __syncthreads();
-  // level 2: T[32:64, 0:32] = -T_low A[32:64, 0:32] T_high; wave w owns one
-  // 16x16 output tile (rows 32 + 16*(w/2), cols 16*(w%2))
+  // level 2: T[32:64, 0:32] = -T_low A[32:64, 0:32] T_high; waves 0..3 own
+  // one 16x16 output tile each (rows 32 + 16*(w/2), cols 16*(w%2)); every
+  // wave takes part in the barrier between the two products
   {
-    const int tr = 32 + 16 * (wave >> 1), tc = 16 * (wave & 1);
-    f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // X = A[tr.., 0:32] T_high[0:32, tc..]: T_high is lower triangular, so
-    // only k-blocks >= tc/16 contribute
-    for (int kb = tc / 16; kb < 2; ++kb)
-      x = mm16_f32(sA + tr * L::LDA + kb * 16, L::LDA, sT + (kb * 16) * L::LDA + tc, L::LDA, x,
-                   lane);
+    const bool active = wave < 4;
+    const int tr = 32 + 16 * ((wave & 3) >> 1), tc = 16 * (wave & 1);
     float* xs = scratch;  // 32x32 X, leading dim 32
-    st_tile_f32(xs + (tr - 32) * 32 + tc, 32, x, 1.f, lane);
+    if (active) {
+      f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // X = A[tr.., 0:32] T_high[0:32, tc..]: T_high is lower triangular, so
+      // only k-blocks >= tc/16 contribute
+      for (int kb = tc / 16; kb < 2; ++kb)
+        x = mm16_f32(sA + tr * L::LDA + kb * 16, L::LDA, sT + (kb * 16) * L::LDA + tc, L::LDA,
+                     x, lane);
+      st_tile_f32(xs + (tr - 32) * 32 + tc, 32, x, 1.f, lane);
+    }
     __syncthreads();
-    // Y = T_low[tr.., 32:64] X[0:32, tc..]: T_low lower triangular, k-blocks <= tr
-    f32x4_t y = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb <= (tr - 32) / 16; ++kb)
-      y = mm16_f32(sT + tr * L::LDA + 32 + kb * 16, L::LDA, xs + (kb * 16) * 32 + tc, 32, y, lane);
-    st_tile_f32(sT + tr * L::LDA + tc, L::LDA, y, -1.f, lane);
+    if (active) {
+      // Y = T_low[tr.., 32:64] X[0:32, tc..]: T_low lower triangular, k-blocks <= tr
+      f32x4_t y = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb <= (tr - 32) / 16; ++kb)
+        y = mm16_f32(sT + tr * L::LDA + 32 + kb * 16, L::LDA, xs + (kb * 16) * 32 + tc, 32, y,
+                     lane);
+      st_tile_f32(sT + tr * L::LDA + tc, L::LDA, y, -1.f, lane);
+    }
   }
   __syncthreads();
   // T Diag(beta) in the MFMA type, lower triangle only, into region 1:
-  // thread = (row, 16-column group)
+  // thread = (row, group of TW columns)
   T* sTb = r1;
   {
-    const int r = tid >> 2, i0 = (tid & 3) * 16;
-    float vals[16];
+    constexpr int TG = NT / kC, TW = kC / TG;  // threads per row, columns each
+    const int r = tid / TG, i0 = (tid % TG) * TW;
+    float vals[TW];
 #pragma unroll
-    for (int t = 0; t < 16; t += 4) {
+    for (int t = 0; t < TW; t += 4) {
       const float4 tv = *reinterpret_cast<const float4*>(sT + r * L::LDA + i0 + t);
       const float4 bv = *reinterpret_cast<const float4*>(s_beta + i0 + t);
       vals[t] = (i0 + t <= r) ? tv.x * bv.x : 0.f;
@@ -797,19 +821,24 @@ __global__ __launch_bounds__(kThreads, (k1_min_blocks<T, D>())) void kda_intra_c
       vals[t + 2] = (i0 + t + 2 <= r) ? tv.z * bv.z : 0.f;
       vals[t + 3] = (i0 + t + 3 <= r) ? tv.w * bv.w : 0.f;
     }
-    st8(sTb + r * L::LDT + i0, vals);  // region 1 held A: every read of it ended above
-    st8(sTb + r * L::LDT + i0 + 8, vals + 8);
+    // region 1 held A: every read of it ended above
+#pragma unroll
+    for (int t = 0; t < TW; t += 8) st8(sTb + r * L::LDT + i0 + t, vals + t);
   }
   __syncthreads();
 
   // ---- U = T Diag(beta) V and Wk^T = (K o e^G)^T (T Diag(beta))^T --------------
   {
-    const int rb = wave;  // this wave's 16 rows of T
+    // wave w: the 16 rows rb = w % 4 of T, and column blocks nb of its
+    // share (with 8 waves, waves 4..7 take the second half of the blocks)
+    const int rb = wave & 3;
+    constexpr int NBW = (D / 16) / (NW / 4);
+    const int nb0 = (wave >> 2) * NBW;
     typename M::frag tb[kC / M::KSTEP];
 #pragma unroll
     for (int ks = 0; ks < kC / M::KSTEP; ++ks) tb[ks] = frag_at<T>(sTb, L::LDT, rb * 16, ks, lane);
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
+    for (int nb = nb0; nb < nb0 + NBW; ++nb) {
       f32x4_t u = {0.f, 0.f, 0.f, 0.f}, wk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kC / M::KSTEP; ++ks) {
@@ -1281,7 +1310,8 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   for (int64_t s = 0; s < nseg; ++s) {
     const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
     if (s1 > s0)
-      hipLaunchKernelGGL((kda_intra_chunk<T, D>), dim3(H, (unsigned)(s1 - s0)), dim3(kThreads),
+      hipLaunchKernelGGL((kda_intra_chunk<T, D>), dim3(H, (unsigned)(s1 - s0)),
+                         dim3(k1_threads<T, D>()),
                          k1_lds, stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H,
                          s0, s1 - s0, d.qk_l2norm, recs);
     hipLaunchKernelGGL((kda_state_pass<T, D, WS>), dim3(nhpad * nslice), dim3(kThreads), 0,
