@@ -513,37 +513,34 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   // channel-pair layout: channels c0, c0+1 of rows r0p .. r0p+RPP-1
   const int cp = tid % NCP, part = tid / NCP;
   const int c0 = 2 * cp, r0p = part * RPP;
+  // Loads are issued tensor by tensor in the order they are consumed (g for
+  // the scan, k and the norm rows, then q, then v last, which is needed only
+  // after A and P): the wait counter is in-order, so each use then waits
+  // only for the loads it needs.
   Raw2<float> graw[RPP];
   Raw2<T> kraw[RPP], qraw[RPP], vraw[RPP];
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    const int r = min(r0p + j, loc.len - 1);
-    graw[j].load(gb + r * rowstride + c0);
-    kraw[j].load(kb + r * rowstride + c0);
-    qraw[j].load(qb + r * rowstride + c0);
-    vraw[j].load(vb + r * rowstride + c0);
-  }
-  // row layout for the norms (a second, cache-served read of q and k rows)
-  const int nr = tid / NQ, nq = tid % NQ;
+  const int nr = tid / NQ, nq = tid % NQ;  // row layout for the norms
+  const int rr = min(nr, loc.len - 1);
   Raw4<T> nqr[QC / 4], nkr[QC / 4];
-  {
-    const int rr = min(nr, loc.len - 1);
 #pragma unroll
-    for (int j = 0; j < QC / 4; ++j) {
-      nqr[j].load(qb + rr * rowstride + nq * QC + 4 * j);
-      nkr[j].load(kb + rr * rowstride + nq * QC + 4 * j);
-    }
-  }
+  for (int j = 0; j < RPP; ++j) graw[j].load(gb + min(r0p + j, loc.len - 1) * rowstride + c0);
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) kraw[j].load(kb + min(r0p + j, loc.len - 1) * rowstride + c0);
+  // the norm rows are a second, cache-served read of k and q
+#pragma unroll
+  for (int j = 0; j < QC / 4; ++j) nkr[j].load(kb + rr * rowstride + nq * QC + 4 * j);
+#pragma unroll
+  for (int j = 0; j < QC / 4; ++j) nqr[j].load(qb + rr * rowstride + nq * QC + 4 * j);
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) qraw[j].load(qb + min(r0p + j, loc.len - 1) * rowstride + c0);
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) vraw[j].load(vb + min(r0p + j, loc.len - 1) * rowstride + c0);
   if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
-  float2 G[RPP], kk[RPP], qq[RPP], vv[RPP];
+  // rows past the chunk's end read as zero (g = 0 keeps the prefix sum flat)
+  auto row_ok = [&](int j) { return r0p + j < loc.len; };
+  float2 G[RPP];
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    const bool ok = r0p + j < loc.len;
-    G[j] = ok ? graw[j].get() : make_float2(0.f, 0.f);
-    kk[j] = ok ? kraw[j].get() : make_float2(0.f, 0.f);
-    qq[j] = ok ? qraw[j].get() : make_float2(0.f, 0.f);
-    vv[j] = ok ? vraw[j].get() : make_float2(0.f, 0.f);
-  }
+  for (int j = 0; j < RPP; ++j) G[j] = row_ok(j) ? graw[j].get() : make_float2(0.f, 0.f);
   {
     float sq = 0.f, sk = 0.f;
     if (nr < loc.len) {
@@ -583,8 +580,22 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
       __syncthreads_or(gamma.x < kFastDecayBound || gamma.y < kFastDecayBound) != 0;
 
   // ---- operands ---------------------------------------------------------------
+  float2 kk[RPP], qq[RPP];
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    kk[j] = row_ok(j) ? kraw[j].get() : make_float2(0.f, 0.f);
+    qq[j] = row_ok(j) ? qraw[j].get() : make_float2(0.f, 0.f);
+  }
   const float2 eg_gamma = make_float2(__expf(gamma.x), __expf(gamma.y));
-  if (part == 0) { wEG[c0] = eg_gamma.x; wEG[c0 + 1] = eg_gamma.y; }
+  // bf16 records on the fast path take Q o e^G and K~ from LDS below, in
+  // whole operand fragments; otherwise every thread stores its own values
+  constexpr bool kStaged = sizeof(T) == 2;
+  const bool direct = !kStaged || exact;
+  float* s_eg = scratch;  // e^gamma per channel (the scan's partials are consumed)
+  if (part == 0) {
+    wEG[c0] = eg_gamma.x; wEG[c0 + 1] = eg_gamma.y;
+    s_eg[c0] = eg_gamma.x; s_eg[c0 + 1] = eg_gamma.y;
+  }
   {
     float kgT[2][8], ktT[2][8];
 #pragma unroll
@@ -594,7 +605,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
       const float khx = kk[j].x * rk, khy = kk[j].y * rk;
       const float qhx = qq[j].x * rq, qhy = qq[j].y * rq;
       const float egx = __expf(G[j].x), egy = __expf(G[j].y);
-      st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
+      if (direct) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
       kgT[0][j & 7] = khx * egx;
       kgT[1][j & 7] = khy * egy;
       if (!exact) {
@@ -614,12 +625,45 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
         const int rb = r0p + (j & ~7);
         st8(r3 + c0 * L::LDT + rb, kgT[0]);                  // (K o e^G)^T
         st8(r3 + (c0 + 1) * L::LDT + rb, kgT[1]);
-        st_fnat8(wKT, kC / M::KSTEP, c0, rb, ktT[0]);       // K o e^(gamma-G), rows c
-        st_fnat8(wKT, kC / M::KSTEP, c0 + 1, rb, ktT[1]);
+        if (direct) {
+          st_fnat8(wKT, kC / M::KSTEP, c0, rb, ktT[0]);     // K o e^(gamma-G), rows c
+          st_fnat8(wKT, kC / M::KSTEP, c0 + 1, rb, ktT[1]);
+        }
       }
     }
   }
   __syncthreads();
+
+  // Staged record writes (bf16, fast path): Q o e^G is region 1 and
+  // K o e^-G region 2, so every lane slot of the operand-order blocks is
+  // gathered from LDS and each wave writes whole 1 KiB blocks.  K~ = e^gamma
+  // (K o e^-G) per channel (a second bf16 rounding of the region-2 values).
+  if constexpr (kStaged) {
+    if (!exact) {
+      constexpr int QB = (kC / 16) * (D / 32), KB = (D / 16) * (kC / 32);  // blocks
+      for (int sidx = tid; sidx < (QB + KB) * 64; sidx += NT) {
+        const int b = sidx >> 6, L = sidx & 63, g = L >> 4;
+        float v[8];
+        if (b < QB) {  // Q o e^G: rows r, k = channel
+          const int r = (b / (D / 32)) * 16 + (L & 15), cb = (b % (D / 32)) * 32 + 4 * g;
+          const T* row = r1 + r * L::LDR;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[e] = ld_f(row + cb + e); v[4 + e] = ld_f(row + cb + 16 + e); }
+          st8(wQG + (b * 64 + L) * 8, v);
+        } else {       // K~: rows c, k = chunk row i
+          const int bk = b - QB;
+          const int c = (bk / (kC / 32)) * 16 + (L & 15), ib = (bk % (kC / 32)) * 32 + 4 * g;
+          const float eg = s_eg[c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = eg * ld_f(r2 + (ib + e) * L::LDR + c);
+            v[4 + e] = eg * ld_f(r2 + (ib + 16 + e) * L::LDR + c);
+          }
+          st8(wKT + (bk * 64 + L) * 8, v);
+        }
+      }
+    }
+  }
 
   // ---- A (strict lower, x beta_r) and P (lower) ------------------------------
   // Tiles are computed transposed (A^T, P^T) so each lane's 4 accumulator
@@ -740,7 +784,11 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   for (int j0 = 0; j0 < RPP; j0 += 8) {
     float vx[8], vy[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) { vx[t] = vv[j0 + t].x; vy[t] = vv[j0 + t].y; }
+    for (int t = 0; t < 8; ++t) {
+      const float2 vt = row_ok(j0 + t) ? vraw[j0 + t].get() : make_float2(0.f, 0.f);
+      vx[t] = vt.x;
+      vy[t] = vt.y;
+    }
     st8(r0 + c0 * L::LDT + r0p + j0, vx);
     st8(r0 + (c0 + 1) * L::LDT + r0p + j0, vy);
   }
