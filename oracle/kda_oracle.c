@@ -271,4 +271,37 @@ int kda_oracle_decode_f64(int64_t steps, int64_t num_seqs, int64_t heads, int64_
     return run_job(&J, nthreads) ? 3 : 0;
 }
 
+/* Output epilogue [XT §6.3 "Sigmoid output gate 控制读出"; XT §6 layer
+ * diagram: the operator's output passes an RMSNorm, then a sigmoid output
+ * gate, before the output projection].  The norm is head-wise: each (token,
+ * head) row of d_v outputs is divided by its root mean square.  The gate is
+ * a sigmoid of a value computed from the layer input, one per output
+ * element.  The pages give neither the norm's eps nor its weight; this
+ * project's reading: eps is a parameter (1e-6 in every workload) added to the
+ * mean square under the root, and w is one weight per d_v channel, shared by
+ * all heads (NULL means 1).  z is the gate's pre-activation.
+ *   y_j = o_j / sqrt(mean_i o_i^2 + eps) * w_j * sigmoid(z_j)
+ * o and z are fp32 (in_dtype 0) or bf16 bit patterns (in_dtype 1), rows x dv. */
+int kda_oracle_gate_norm_f64(int64_t rows, int64_t dv, int in_dtype, const void* o,
+                             const void* z, const float* w, double eps, double* y) {
+    if (rows < 0 || dv < 1 || (in_dtype != 0 && in_dtype != 1)) return 2;
+    if (rows > 0 && (!o || !z || !y)) return 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        double ms = 0.0;
+        for (int64_t j = 0; j < dv; ++j) {
+            const double x = load_in(o, in_dtype, r * dv + j);
+            ms += x * x;
+        }
+        ms /= (double)dv;
+        const double inv_rms = 1.0 / sqrt(ms + eps);
+        for (int64_t j = 0; j < dv; ++j) {
+            const double x = load_in(o, in_dtype, r * dv + j);
+            const double gate = 1.0 / (1.0 + exp(-load_in(z, in_dtype, r * dv + j)));
+            const double wj = w ? (double)w[j] : 1.0;
+            y[r * dv + j] = x * inv_rms * wj * gate;
+        }
+    }
+    return 0;
+}
+
 int kda_oracle_abi_version(void) { return 1; }

@@ -57,6 +57,8 @@ def open_library(path: str):
     lib.kda_oracle_decode_f64.argtypes = [i64, i64, i64, i64, i64, ip,
                                           vp, vp, vp, vp, vp, vp, ip, dp, vp, vp, ip]
     lib.kda_oracle_decode_f64.restype = ip
+    lib.kda_oracle_gate_norm_f64.argtypes = [i64, i64, ip, vp, vp, vp, dp, vp]
+    lib.kda_oracle_gate_norm_f64.restype = ip
     return lib
 
 
@@ -179,3 +181,26 @@ def kda_decode(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, nthreads=N
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode_f64 failed with code {rc}")
     return o, so
+
+
+def gate_norm(o, z, w=None, *, eps=1e-6, lib=None):
+    """fp64 output epilogue: head-wise RMSNorm of o times sigmoid(z).
+
+    o, z: [..., dv] (same dtype, fp32 or bf16); w: [dv] fp32 or None.
+    Returns y with o's shape as float64.
+    """
+    oa, dt = _as_np(o, "o")
+    za, dt2 = _as_np(z, "z")
+    if dt != dt2 or oa.shape != za.shape:
+        raise ValueError("o and z must have the same dtype and shape")
+    wa = _f32(w, "w")
+    dv = oa.shape[-1]
+    rows = int(np.prod(oa.shape[:-1])) if oa.ndim > 1 else 1
+    if wa is not None and wa.shape != (dv,):
+        raise ValueError("w must have shape [dv]")
+    y = np.zeros(oa.shape, dtype=np.float64)
+    rc = _load(lib).kda_oracle_gate_norm_f64(rows, dv, dt, _ptr(oa), _ptr(za), _ptr(wa),
+                                            float(eps), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_gate_norm_f64 failed with code {rc}")
+    return y

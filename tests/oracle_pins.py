@@ -399,7 +399,82 @@ def pin_contractivity(lib=None):
     assert np.max(np.abs(ck[-1] - s0)) > 1e-3
 
 
+# --- output epilogue: head-wise RMSNorm x sigmoid gate [XT §6.3] ----------------
+def pin_gate_norm_worked_example(lib=None):
+    """o = (3, 4): mean square 12.5; z = 0 gives the gate 1/2 exactly; w = (1, 2)."""
+    o = np.array([[3.0, 4.0]], dtype=f32)
+    z = np.zeros((1, 2), dtype=f32)
+    w = np.array([1.0, 2.0], dtype=f32)
+    y = O.gate_norm(o, z, w, eps=0.0, lib=lib)
+    r = np.sqrt(12.5)
+    _close(y, [[3.0 / r * 0.5, 4.0 / r * 2.0 * 0.5]], 1e-15, "gate-norm worked example")
+
+
+def pin_gate_norm_unit_rms(lib=None):
+    """With the gate saturated (z = 40: sigmoid = 1 - 4e-18), w = 1 and
+    eps = 0, every row comes out with mean square exactly 1, whatever its
+    scale; and the row's direction is kept."""
+    rng = np.random.default_rng(21)
+    o = (rng.standard_normal((6, 128)) * np.array([[1e-3], [1], [7], [1e3], [0.5], [2]])).astype(f32)
+    z = np.full(o.shape, 40.0, dtype=f32)
+    y = O.gate_norm(o, z, None, eps=0.0, lib=lib)
+    ms = np.mean(y * y, axis=1)
+    assert np.max(np.abs(ms - 1.0)) < 1e-13, f"rows not unit RMS: {ms}"
+    cos = np.sum(y * o, axis=1) / np.sqrt(np.sum(y * y, axis=1) * np.sum(o.astype(np.float64) ** 2, axis=1))
+    assert np.min(cos) > 1 - 1e-13, "normalisation changed a row's direction"
+
+
+def pin_gate_norm_scale_invariance(lib=None):
+    """RMSNorm ignores a positive scale of its row (eps = 0); the gate does not."""
+    rng = np.random.default_rng(22)
+    o = rng.standard_normal((8, 64)).astype(f32)
+    z = rng.standard_normal((8, 64)).astype(f32)
+    w = rng.uniform(0.5, 1.5, 64).astype(f32)
+    y1 = O.gate_norm(o, z, w, eps=0.0, lib=lib)
+    y2 = O.gate_norm((o * f32(8.0)).astype(f32), z, w, eps=0.0, lib=lib)  # exact power-of-2 scale
+    _close(y2, y1, 1e-14, "scale invariance")
+
+
+def pin_gate_norm_gate_symmetry(lib=None):
+    """sigmoid(z) + sigmoid(-z) = 1: y(z) + y(-z) is the ungated normalised row,
+    which the saturated gate (z = +40) also gives; sigmoid(0) = 1/2."""
+    rng = np.random.default_rng(23)
+    o = rng.standard_normal((5, 128)).astype(f32)
+    z = (3 * rng.standard_normal((5, 128))).astype(f32)
+    w = rng.uniform(0.5, 1.5, 128).astype(f32)
+    y_pos = O.gate_norm(o, z, w, eps=1e-6, lib=lib)
+    y_neg = O.gate_norm(o, -z, w, eps=1e-6, lib=lib)
+    y_one = O.gate_norm(o, np.full(o.shape, 40.0, dtype=f32), w, eps=1e-6, lib=lib)
+    y_half = O.gate_norm(o, np.zeros(o.shape, dtype=f32), w, eps=1e-6, lib=lib)
+    _close(y_pos + y_neg, y_one, 1e-14, "gate symmetry")
+    _close(2.0 * y_half, y_one, 1e-15, "sigmoid(0) = 1/2")
+
+
+def pin_gate_norm_special_rows(lib=None):
+    """A zero row stays zero with eps > 0; a constant row c gives
+    c / sqrt(c^2 + eps) before weight and gate; bf16 inputs widen exactly."""
+    o = np.zeros((3, 64), dtype=f32)
+    o[1, :] = 0.25
+    o[2, :] = -3.0
+    z = np.full(o.shape, 40.0, dtype=f32)
+    eps = 1e-2
+    y = O.gate_norm(o, z, None, eps=eps, lib=lib)
+    assert np.all(y[0] == 0.0), "zero row not zero"
+    _close(y[1], np.full(64, 0.25 / np.sqrt(0.0625 + eps)), 1e-14, "constant row")
+    _close(y[2], np.full(64, -3.0 / np.sqrt(9.0 + eps)), 1e-14, "negative constant row")
+    import torch
+    ob = torch.from_numpy(np.random.default_rng(24).standard_normal((4, 128)).astype(f32)).bfloat16()
+    zb = torch.zeros(4, 128).bfloat16()
+    yb = O.gate_norm(ob, zb, None, eps=1e-6, lib=lib)
+    yf = O.gate_norm(ob.float(), zb.float(), None, eps=1e-6, lib=lib)
+    assert np.array_equal(yb, yf), "bf16 inputs not widened exactly"
+
+
+GATE_NORM_PINS = [pin_gate_norm_worked_example, pin_gate_norm_unit_rms,
+                  pin_gate_norm_scale_invariance, pin_gate_norm_gate_symmetry,
+                  pin_gate_norm_special_rows]
+
 ALL_PINS = [pin_worked_example, pin_gdn, pin_delta_rule, pin_linear_attention,
             pin_l2_normalisation, pin_frozen_and_small_beta, pin_exact_retrieval,
             pin_transition_products, pin_gradient_step, pin_invariances,
-            pin_contractivity]
+            pin_contractivity] + GATE_NORM_PINS

@@ -30,6 +30,15 @@ MUTANTS = {
     "gate_from_head0": ("(tok * H + h) * dk, tok * H + h,", "(tok * H) * dk, tok * H + h,"),
     "varlen_offset": ("tok0 = J->cu_seqlens[n];", "tok0 = 0 * J->cu_seqlens[n];"),
     "scale_ignored": ("J->o[orow + j] = J->scale * acc;", "J->o[orow + j] = acc;"),
+    # output epilogue (head-wise RMSNorm x sigmoid gate)
+    "rms_sum_not_mean": ("ms /= (double)dv;", "ms /= 1.0;"),
+    "rms_eps_outside": ("1.0 / sqrt(ms + eps);", "1.0 / (sqrt(ms) + eps);"),
+    "rms_not_rooted": ("1.0 / sqrt(ms + eps);", "1.0 / (ms + eps);"),
+    "gate_swish": ("x * inv_rms * wj * gate;", "x * inv_rms * wj * gate * load_in(z, in_dtype, r * dv + j);"),
+    "out_gate_sign": ("exp(-load_in(z, in_dtype, r * dv + j))", "exp(load_in(z, in_dtype, r * dv + j))"),
+    "norm_weight_ignored": ("const double wj = w ? (double)w[j] : 1.0;", "const double wj = 1.0;"),
+    "norm_over_first_row": ("const double x = load_in(o, in_dtype, r * dv + j);\n            ms += x * x;",
+                            "const double x = load_in(o, in_dtype, j);\n            ms += x * x;"),
 }
 
 
