@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from gated_delta_rule_54_amd import (chunk_fwd_workspace_bytes, kda_chunk_fwd,  # noqa: E402
-                                     kda_decode_step, make_desc)
+                                     kda_decode_step, kda_output_gate_norm, make_desc)
 from gated_delta_rule_54_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -57,7 +57,10 @@ DECODE_FLOPS_PER_TH = 7 * 128 ** 2
 
 
 KERNEL_SOURCES = ("gated_delta_rule_54_amd/csrc/kda_chunk.hip",
-                  "gated_delta_rule_54_amd/csrc/kda_decode.hip")
+                  "gated_delta_rule_54_amd/csrc/kda_decode.hip",
+                  "gated_delta_rule_54_amd/csrc/kda_epilogue.hip")
+# output epilogue bytes per element (bf16): o read + gate read + y written
+EPILOGUE_BYTES_PER_EL = 2 + 2 + 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_hbm_traffic.json")
 
 
@@ -70,16 +73,16 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per prefill call / decode step from the committed counter
-    passes, or (None, None) when the kernels changed since they were taken."""
+    """HBM bytes per prefill call / decode step / epilogue call from the
+    committed counter passes, or None when the kernels changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None, None
+        return None, None, None
     if t.get("kernel_source_sha256") != kernel_source_hash():
-        return None, None
-    return t.get("prefill_call_bytes"), t.get("decode_step_bytes")
+        return None, None, None
+    return t.get("prefill_call_bytes"), t.get("decode_step_bytes"), t.get("epilogue_call_bytes")
 
 
 def probe():
@@ -106,6 +109,39 @@ def probe():
                                  dtype=dw.dtype, gen=gen, device="cuda")
         kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state)
     torch.cuda.synchronize()
+    del state
+    o, z, w = epilogue_inputs()
+    for _ in range(2):
+        kda_output_gate_norm(o, z, w)
+    torch.cuda.synchronize()
+
+
+def epilogue_inputs():
+    """Synthetic epilogue operands at the prefill output's size."""
+    gen = torch.Generator(device="cuda").manual_seed(1005)
+    rows, dv = 8192 * 32, 128
+    o = torch.randn(rows, dv, generator=gen, device="cuda").bfloat16()
+    z = (2.0 * torch.randn(rows, dv, generator=gen, device="cuda")).bfloat16()
+    w = 0.5 + torch.rand(dv, generator=gen, device="cuda")
+    return o, z, w
+
+
+def bench_epilogue(steps: int, warmup: int):
+    o, z, w = epilogue_inputs()
+    y = torch.empty_like(o)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        kda_output_gate_norm(o, z, w, out=y, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        kda_output_gate_norm(o, z, w, out=y, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = o.numel() * EPILOGUE_BYTES_PER_EL + w.numel() * 4
+    return dict(ms=ms, rows=o.shape[0], achieved_gbs=nbytes / (ms * 1e-3) / 1e9, nbytes=nbytes)
 
 
 def _events():
@@ -224,8 +260,9 @@ def main():
         probe()
         return
     pf = bench_prefill(args.steps, args.warmup)
-    tr_prefill, tr_decode = measured_traffic()
+    tr_prefill, tr_decode, tr_epi = measured_traffic()
     dc = bench_decode(min(args.warmup, 8))
+    ep = bench_epilogue(args.steps, args.warmup)
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -263,6 +300,15 @@ def main():
                                 "traffic_bytes_per_step": tr_decode,
                                 "kernel": "decode_step_kernel<bf16,128>",
                                 "bytes_per_token_head": DECODE_BYTES_PER_TH}},
+        "epilogue": {"workload": "head-wise RMSNorm x sigmoid gate on the prefill output: "
+                                 "262144 rows (8192 tokens x 32 heads) x 128, bf16",
+                     "us_per_call": ep["ms"] * 1e3,
+                     "roofline": {"bound": "hbm", "achieved": ep["achieved_gbs"],
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": ep["achieved_gbs"] / HBM_PEAK_GBS,
+                                  "traffic": (tr_epi / (ep["ms"] * 1e-3) / 1e9) if tr_epi else None,
+                                  "kernel": "gate_norm_kernel<bf16,128>",
+                                  "bytes_per_element": EPILOGUE_BYTES_PER_EL}},
         "wall_s_prefill_loop": pf["wall"],
     }
     if not args.no_cpu_baseline:

@@ -180,3 +180,35 @@ KDA_EXPORT kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, c
     return fail(KDA_ERR_HIP, "kda_decode_step launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+KDA_EXPORT kda_status_t kda_output_gate_norm(int64_t rows, int32_t dv, int32_t dtype,
+                                             const void* o, const void* z, const float* w,
+                                             float eps, void* y, hipStream_t stream) {
+  if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+  if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
+  if (dv != 64 && dv != 128) return fail(KDA_ERR_UNSUPPORTED, "dv must be 64 or 128 (got %d)", dv);
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (rows == 0) return ok();
+  const void* need[] = {o, z, y};
+  const char* names[] = {"o", "z", "y"};
+  for (int i = 0; i < 3; ++i) {
+    if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(need[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (w && !aligned(w, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "w is not 4-byte aligned");
+  const uintptr_t bytes = (uintptr_t)rows * dv * (dtype == KDA_DTYPE_BF16 ? 2 : 4);
+  auto overlap = [&](const void* a, const void* b) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + bytes && pb < pa + bytes;
+  };
+  if (overlap(y, z)) return fail(KDA_ERR_INVALID_ARGUMENT, "y must not overlap z");
+  if (y != o && overlap(y, o))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "y must equal o or not overlap it");
+  hipError_t e = kda::launch_gate_norm(rows, dv, dtype, o, z, w, eps, y, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_output_gate_norm launch: %s", hipGetErrorString(e));
+  return ok();
+}

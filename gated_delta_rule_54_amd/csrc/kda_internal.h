@@ -21,4 +21,8 @@ hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, c
                             const int32_t* cu_seqlens, void* o, float* final_state,
                             float* state_ckpt, void* workspace, hipStream_t stream);
 
+// Output epilogue: head-wise RMSNorm x sigmoid gate over [rows, dv].
+hipError_t launch_gate_norm(int64_t rows, int dv, int dtype, const void* o, const void* z,
+                            const float* w, float eps, void* y, hipStream_t stream);
+
 }  // namespace kda

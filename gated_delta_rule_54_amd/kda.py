@@ -29,7 +29,7 @@ KDA_DTYPE_BF16 = 1
 
 # Names every build of the library must export (the declarations of kda.h).
 EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_decode_step",
-            "kda_status_string", "kda_last_error", "kda_abi_version")
+            "kda_output_gate_norm", "kda_status_string", "kda_last_error", "kda_abi_version")
 
 
 class KdaDesc(ctypes.Structure):
@@ -77,6 +77,9 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_fwd.restype = i32
     lib.kda_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = i32
+    lib.kda_output_gate_norm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, ctypes.c_float,
+                                         vp, vp]
+    lib.kda_output_gate_norm.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -209,4 +212,25 @@ def kda_decode_step(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, out=N
     st = lib.kda_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(state), _ptr(out), _stream_handle(stream, q.device))
     _check(lib, st, "kda_decode_step")
+    return out
+
+
+def kda_output_gate_norm(o, z, w=None, *, eps=1e-6, out=None, stream=None):
+    """Output epilogue through the C ABI: head-wise RMSNorm of o times
+    sigmoid(z).  o, z: [..., dv] (same dtype and shape, contiguous); w: [dv]
+    fp32 or None.  out may be o itself (in place).  Returns out."""
+    lib = load_library()
+    dt = o.dtype
+    dv = o.shape[-1]
+    _need(o, "o", dt, tuple(o.shape))
+    _need(z, "z", dt, tuple(o.shape))
+    if w is not None:
+        _need(w, "w", torch.float32, (dv,))
+    if out is None:
+        out = torch.empty_like(o)
+    _need(out, "out", dt, tuple(o.shape))
+    rows = o.numel() // dv if dv else 0
+    st = lib.kda_output_gate_norm(rows, dv, _dtype_code(dt), _ptr(o), _ptr(z), _ptr(w),
+                                  float(eps), _ptr(out), _stream_handle(stream, o.device))
+    _check(lib, st, "kda_output_gate_norm")
     return out

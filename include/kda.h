@@ -142,6 +142,26 @@ kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, const void* 
                              const void* v, const float* g, const float* beta, float* state,
                              void* o, hipStream_t stream);
 
+/* Output epilogue: head-wise RMSNorm times a sigmoid output gate, the two
+ * steps that follow the operator in the layer.  [XT §6 layer diagram: KDA ->
+ * RMSNorm -> sigmoid output gate -> output projection; XT §6.3: the output is
+ * normalised per head, then multiplied by a sigmoid gate computed from the
+ * input.]  Per row r (one (token, head) pair) and channel j:
+ *   y[r, j] = o[r, j] / sqrt(mean_i o[r, i]^2 + eps) * w[j] * sigmoid(z[r, j])
+ *   rows     number of rows: B*T*H after kda_chunk_fwd, N*H after
+ *            kda_decode_step (0 is a no-op)
+ *   dv       64 or 128
+ *   dtype    KDA_DTYPE_F32 or KDA_DTYPE_BF16, the element type of o, z and y
+ *   o, z, y  [rows, dv] row-major, device, 16-byte aligned; y may equal o
+ *            (in place) but must not otherwise overlap o or z
+ *   w        [dv] fp32 device, one weight per channel shared by all heads,
+ *            or NULL for weight 1
+ *   eps      finite and >= 0 (the pages give none; 1e-6 in the workloads)
+ * Asynchronous on `stream`; on a validation error nothing is launched. */
+kda_status_t kda_output_gate_norm(int64_t rows, int32_t dv, int32_t dtype, const void* o,
+                                  const void* z, const float* w, float eps, void* y,
+                                  hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kda_status_string(kda_status_t status);
 

@@ -132,6 +132,30 @@ def test_decode_errors():
     assert call(_desc(num_seqs=0)) == B.KDA_OK  # nothing to do, nothing launched
 
 
+def test_gate_norm_errors():
+    """Every invalid epilogue call fails on the host; the fake pointers are
+    never dereferenced because nothing is launched."""
+    lib = K.load_library()
+    Z, Y = FAKE + 0x100000, FAKE + 0x200000  # disjoint 16-byte-aligned regions
+
+    def call(rows=4, dv=128, dtype=1, o=FAKE, z=Z, w=None, eps=1e-6, y=Y):
+        return lib.kda_output_gate_norm(rows, dv, dtype, o, z, w, eps, y, None)
+
+    assert call(rows=-1) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(dtype=7) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(dv=96) == B.KDA_ERR_UNSUPPORTED
+    assert call(eps=-1.0) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(eps=float("nan")) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(o=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(z=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(y=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(o=FAKE + 8) == B.KDA_ERR_INVALID_ARGUMENT        # not 16-byte aligned
+    assert call(w=FAKE + 2) == B.KDA_ERR_INVALID_ARGUMENT        # w not 4-byte aligned
+    assert call(y=Z) == B.KDA_ERR_INVALID_ARGUMENT               # y overlaps z
+    assert call(y=FAKE + 256) == B.KDA_ERR_INVALID_ARGUMENT      # partial overlap with o
+    assert call(rows=0, o=None, z=None, y=None) == B.KDA_OK      # nothing to do
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         B.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,108 @@
+"""The output epilogue (head-wise RMSNorm x sigmoid gate) on the GPU against
+the fp64 oracle: synthetic seeded o, z and w (none taken from the HIP path),
+all dtypes and head dims, ragged row counts, in place, and the whole path
+prefill -> epilogue against oracle prefill -> oracle epilogue."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_54_amd import kda_chunk_fwd, kda_decode_step, kda_output_gate_norm
+from gated_delta_rule_54_amd import workloads as W
+from oracle import oracle as O
+from parity import TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(rows, dv, dtype, seed, with_w=True, o_scale=1.0):
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    o = (o_scale * torch.randn(rows, dv, generator=gen, device=DEV)).to(dtype)
+    z = (2.0 * torch.randn(rows, dv, generator=gen, device=DEV)).to(dtype)
+    w = (0.5 + torch.rand(dv, generator=gen, device=DEV)) if with_w else None
+    return o, z, w
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("rows", [1, 3, 17, 1000])
+def test_gate_norm_parity(dtype, dv, rows):
+    o, z, w = _inputs(rows, dv, dtype, seed=100 + rows + dv)
+    y = kda_output_gate_norm(o, z, w, eps=1e-6)
+    torch.cuda.synchronize()
+    ref = O.gate_norm(o.cpu(), z.cpu(), w.cpu(), eps=1e-6)
+    print(f"gate_norm rows={rows} dv={dv} {dtype}", flush=True)
+    assert_close("y", y, ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_gate_norm_options(dtype):
+    # no weight, large eps, tiny and huge row scales, a zero row
+    for scale, eps in ((1e-4, 1e-2), (1e3, 0.0), (1.0, 1e-6)):
+        o, z, _ = _inputs(64, 128, dtype, seed=7, with_w=False, o_scale=scale)
+        o[5].zero_()
+        y = kda_output_gate_norm(o, z, None, eps=eps if eps > 0 else 1e-30)
+        torch.cuda.synchronize()
+        ref = O.gate_norm(o.cpu(), z.cpu(), None, eps=eps if eps > 0 else 1e-30)
+        print(f"options scale={scale} eps={eps} {dtype}", flush=True)
+        assert_close("y", y, ref, TOL[dtype])
+        assert torch.isfinite(y).all()
+
+
+def test_gate_norm_in_place_and_empty():
+    o, z, w = _inputs(300, 128, torch.bfloat16, seed=11)
+    ref = O.gate_norm(o.cpu(), z.cpu(), w.cpu(), eps=1e-6)
+    out = kda_output_gate_norm(o, z, w, eps=1e-6, out=o)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == o.data_ptr()
+    assert_close("in place", o, ref, TOL[torch.bfloat16])
+    e = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    kda_output_gate_norm(e, e.clone(), None)  # zero rows: nothing launched
+
+
+def test_gate_norm_prefill_rows_sampled():
+    """The prefill output's full size (8192 x 32 rows of 128, bf16), checked
+    on sampled rows that the oracle evaluates one by one."""
+    rows, dv = 8192 * 32, 128
+    o, z, w = _inputs(rows, dv, torch.bfloat16, seed=12)
+    y = kda_output_gate_norm(o, z, w, eps=1e-6)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(np.random.default_rng(3).choice(rows, 2000, replace=False)).to(DEV)
+    ref = O.gate_norm(o[idx].cpu(), z[idx].cpu(), w.cpu(), eps=1e-6)
+    assert_close("sampled rows", y[idx], ref, TOL[torch.bfloat16])
+
+
+def test_prefill_then_epilogue():
+    """The path as the layer runs it: prefill, then the epilogue on its output,
+    against the oracle's prefill followed by the oracle's epilogue."""
+    inp = W.prefill_inputs(batch=1, seqlen=300, heads=4, dk=128, dv=128, dtype=torch.bfloat16,
+                           device=DEV, seed=31, init="normal")
+    gen = torch.Generator(device=DEV).manual_seed(32)
+    z = (2.0 * torch.randn(1, 300, 4, 128, generator=gen, device=DEV)).bfloat16()
+    w = 0.5 + torch.rand(128, generator=gen, device=DEV)
+    o, _, _ = kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["init_state"])
+    y = kda_output_gate_norm(o, z, w, eps=1e-6)
+    torch.cuda.synchronize()
+    host = [inp[x].cpu() for x in ("q", "k", "v", "g", "beta", "init_state")]
+    o_ref, _, _ = O.kda_fwd(*host)
+    # the oracle epilogue on the oracle's own (fp64) operator output
+    y_ref = O.gate_norm(torch.from_numpy(o_ref.astype(np.float32)), z.float().cpu(), w.cpu(),
+                        eps=1e-6)
+    assert_close("prefill + epilogue", y, y_ref, TOL[torch.bfloat16])
+
+
+def test_decode_then_epilogue():
+    gen = W.make_generator(41, DEV)
+    N, H, d = 8, 4, 128
+    state = W.decode_initial_state(num_seqs=N, heads=H, dk=d, dv=d, gen=gen, device=DEV)
+    x = W.decode_step_inputs(num_seqs=N, heads=H, dk=d, dv=d, dtype=torch.bfloat16, gen=gen,
+                             device=DEV)
+    z = (2.0 * torch.randn(N, H, d, generator=gen, device=DEV)).bfloat16()
+    s0 = state.cpu().clone()
+    o = kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state)
+    y = kda_output_gate_norm(o, z, None, eps=1e-6)
+    torch.cuda.synchronize()
+    o_ref, _ = O.kda_decode(*(x[k].cpu().unsqueeze(0) for k in ("q", "k", "v", "g", "beta")), s0)
+    y_ref = O.gate_norm(torch.from_numpy(o_ref[0].astype(np.float32)), z.float().cpu(), None,
+                        eps=1e-6)
+    assert_close("decode + epilogue", y, y_ref, TOL[torch.bfloat16])
