@@ -144,6 +144,38 @@ def bench_epilogue(steps: int, warmup: int):
     return dict(ms=ms, rows=o.shape[0], achieved_gbs=nbytes / (ms * 1e-3) / 1e9, nbytes=nbytes)
 
 
+def bench_gate_modes(reps: int = 5):
+    """Prefill at the shape of the pages' kernel comparison (batch 1, 16
+    heads, 2K..64K tokens), d = 128 bf16: per-channel gates (KDA) against one
+    gate per token and head (Gated DeltaNet), microseconds per call."""
+    rows = []
+    stream = torch.cuda.current_stream()
+    for T in (2048, 4096, 8192, 16384, 32768, 65536):
+        row = {"T": T}
+        for mode, per_head in (("kda_us", False), ("gdn_us", True)):
+            inp = W.prefill_inputs(batch=1, seqlen=T, heads=16, dk=128, dv=128,
+                                   dtype=torch.bfloat16, device="cuda", seed=1006 + T,
+                                   gate_per_head=per_head)
+            o = torch.empty_like(inp["v"])
+            fs = torch.empty((1, 16, 128, 128), dtype=torch.float32, device="cuda")
+            run = lambda: kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                        out=o, final_state=fs, stream=stream)
+            for _ in range(2):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = _events()
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            row[mode] = e0.elapsed_time(e1) / reps * 1e3
+            del inp, o, fs
+        row["kda_over_gdn"] = row["kda_us"] / row["gdn_us"]
+        rows.append(row)
+    return rows
+
+
 def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -263,6 +295,7 @@ def main():
     tr_prefill, tr_decode, tr_epi = measured_traffic()
     dc = bench_decode(min(args.warmup, 8))
     ep = bench_epilogue(args.steps, args.warmup)
+    gm = bench_gate_modes()
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -309,6 +342,9 @@ def main():
                                   "traffic": (tr_epi / (ep["ms"] * 1e-3) / 1e9) if tr_epi else None,
                                   "kernel": "gate_norm_kernel<bf16,128>",
                                   "bytes_per_element": EPILOGUE_BYTES_PER_EL}},
+        "gate_modes": {"workload": "prefill B=1 H=16 d=128 bf16, T = 2K..64K: per-channel "
+                                   "gates (KDA) vs one gate per token and head (GDN)",
+                       "rows": gm},
         "wall_s_prefill_loop": pf["wall"],
     }
     if not args.no_cpu_baseline:

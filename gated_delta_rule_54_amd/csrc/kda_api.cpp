@@ -38,7 +38,8 @@ bool aligned16(const void* p) { return aligned(p, 16); }
 // Checks shared by both entry points: dims, dtype, chunk, scale.
 kda_status_t check_common(const kda_desc_t* d) {
   if (!d) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
-  if (d->reserved0 != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "desc.reserved0 must be 0");
+  if (d->gate_per_head != 0 && d->gate_per_head != 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "gate_per_head must be 0 or 1");
   if (d->heads < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "heads must be >= 1 (got %d)", d->heads);
   if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16)
     return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
@@ -121,11 +122,11 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
     return fail(KDA_ERR_INVALID_ARGUMENT,
                 "state_ckpt must be given exactly when ckpt_every > 0");
   // q, k, v, g, o rows are moved with vector accesses (16-byte aligned rows);
-  // everything else with 4-byte scalar accesses.
+  // everything else, and per-head gates, with 4-byte scalar accesses.
   const bool has_tokens = d.seqlen > 0;
   const void* need[] = {q, k, v, g, beta, o};
   const char* names[] = {"q", "k", "v", "g", "beta", "o"};
-  const uintptr_t align[] = {16, 16, 16, 16, 4, 16};
+  const uintptr_t align[] = {16, 16, 16, uintptr_t(d.gate_per_head ? 4 : 16), 4, 16};
   for (int i = 0; i < 6; ++i) {
     if (has_tokens && !need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
     if (need[i] && !aligned(need[i], align[i]))

@@ -463,7 +463,9 @@ __device__ __forceinline__ void st2(bf16* p, float a, float b) {
 template <typename T, int D>
 constexpr int k1_min_blocks() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
 
-template <typename T, int D>
+// GS: one gate per (token, head), broadcast over the key channels (Gated
+// DeltaNet) instead of one per channel.
+template <typename T, int D, bool GS>
 __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void kda_intra_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
@@ -496,7 +498,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   const T* qb = q + (loc.tok0 * H + h) * D;
   const T* kb = k + (loc.tok0 * H + h) * D;
   const T* vb = v + (loc.tok0 * H + h) * D;
-  const float* gb = g + (loc.tok0 * H + h) * D;
+  const float* gb = GS ? g + loc.tok0 * H + h : g + (loc.tok0 * H + h) * D;
   char* rec = ws + ((int64_t)h * nrec + (slot - slot_base)) * R::BYTES;
   T* wQG = reinterpret_cast<T*>(rec) + R::QG;
   T* wKT = reinterpret_cast<T*>(rec) + R::KT;
@@ -518,12 +520,18 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   // after A and P): the wait counter is in-order, so each use then waits
   // only for the loads it needs.
   Raw2<float> graw[RPP];
+  float gsc[RPP];  // GS: the row's one gate
   Raw2<T> kraw[RPP], qraw[RPP], vraw[RPP];
   const int nr = tid / NQ, nq = tid % NQ;  // row layout for the norms
   const int rr = min(nr, loc.len - 1);
   Raw4<T> nqr[QC / 4], nkr[QC / 4];
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) graw[j].load(gb + min(r0p + j, loc.len - 1) * rowstride + c0);
+  for (int j = 0; j < RPP; ++j) {
+    if constexpr (GS)
+      gsc[j] = gb[min(r0p + j, loc.len - 1) * H];
+    else
+      graw[j].load(gb + min(r0p + j, loc.len - 1) * rowstride + c0);
+  }
 #pragma unroll
   for (int j = 0; j < RPP; ++j) kraw[j].load(kb + min(r0p + j, loc.len - 1) * rowstride + c0);
   // the norm rows are a second, cache-served read of k and q
@@ -540,7 +548,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   auto row_ok = [&](int j) { return r0p + j < loc.len; };
   float2 G[RPP];
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) G[j] = row_ok(j) ? graw[j].get() : make_float2(0.f, 0.f);
+  for (int j = 0; j < RPP; ++j) {
+    const float2 gj = GS ? make_float2(gsc[j], gsc[j]) : graw[j].get();
+    G[j] = row_ok(j) ? gj : make_float2(0.f, 0.f);
+  }
   {
     float sq = 0.f, sk = 0.f;
     if (nr < loc.len) {
@@ -1341,9 +1352,11 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   const int k1_lds = K1Lds<T, D>::BYTES;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kda_intra_chunk<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
-    if (e != hipSuccess) return e;
+    for (const void* fn : {(const void*)kda_intra_chunk<T, D, false>,
+                           (const void*)kda_intra_chunk<T, D, true>}) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   const int64_t nck = d.ckpt_every > 0 ? d.seqlen / d.ckpt_every : 0;
@@ -1357,11 +1370,12 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + SS - 1) / SS;
   for (int64_t s = 0; s < nseg; ++s) {
     const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
-    if (s1 > s0)
-      hipLaunchKernelGGL((kda_intra_chunk<T, D>), dim3(H, (unsigned)(s1 - s0)),
-                         dim3(k1_threads<T, D>()),
-                         k1_lds, stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H,
-                         s0, s1 - s0, d.qk_l2norm, recs);
+    if (s1 > s0) {
+      auto k1 = d.gate_per_head ? kda_intra_chunk<T, D, true> : kda_intra_chunk<T, D, false>;
+      hipLaunchKernelGGL(k1, dim3(H, (unsigned)(s1 - s0)), dim3(k1_threads<T, D>()), k1_lds,
+                         stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
+                         s1 - s0, d.qk_l2norm, recs);
+    }
     hipLaunchKernelGGL((kda_state_pass<T, D, WS>), dim3(nhpad * nslice), dim3(kThreads), 0,
                        stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,
                        carry, final_state, ckpt, d.ckpt_every, nck, d.scale, (T*)o);

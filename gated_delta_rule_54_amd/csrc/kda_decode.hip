@@ -7,6 +7,7 @@
 // Per (sequence, head), with S the d x d fp32 state (rows = key channels):
 //   k^, q^ = L2-normalised k, q                     [XT §6.2]
 //   S~ = Diag(exp g) S                              [XT §3, decay step]
+//        (g per key channel, or one g per head broadcast: Gated DeltaNet)
 //   u  = beta (v - S~^T k^)                         [XT §3, correction]
 //   S  = S~ + k^ u^T                                [XT §3, boxed update]
 //   o  = scale S^T q^ = scale (S~^T q^ + u (k^.q^))  [XT §1 read-out, expanded]
@@ -46,7 +47,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    T* __restrict__ o, int qk_l2norm, float scale) {
+    T* __restrict__ o, int qk_l2norm, float scale, int gate_per_head) {
   constexpr int CG = D / 4;            // float4 column groups per row
   constexpr int RG = kThreads / CG;    // row groups
   constexpr int RPG = D / RG;          // rows per thread
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const float kv = to_f32(k[vb + tid]), qv = to_f32(q[vb + tid]);
     s_k[tid] = kv;
     s_q[tid] = qv;
-    s_a[tid] = __expf(g[vb + tid]);
+    s_a[tid] = __expf(gate_per_head ? g[head] : g[vb + tid]);
     kk = kv * kv; qq = qv * qv; kq = kv * qv;
   }
   // wave reductions of |k|^2, |q|^2, k.q
@@ -147,7 +148,7 @@ hipError_t launch_typed(const kda_desc_t& d, const void* q, const void* k, const
   hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), g, beta, state, static_cast<T*>(o), d.qk_l2norm,
-                     d.scale);
+                     d.scale, d.gate_per_head);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ class KdaDesc(ctypes.Structure):
         ("chunk", ctypes.c_int32),
         ("qk_l2norm", ctypes.c_int32),
         ("scale", ctypes.c_float),
-        ("reserved0", ctypes.c_int32),
+        ("gate_per_head", ctypes.c_int32),
         ("ckpt_every", ctypes.c_int64),
     ]
 
@@ -127,11 +127,11 @@ def _stream_handle(stream, device):
 
 
 def make_desc(*, batch, num_seqs, seqlen, heads, dk, dv, dtype, qk_l2norm=True, scale=1.0,
-              ckpt_every=0, chunk=64) -> KdaDesc:
+              ckpt_every=0, chunk=64, gate_per_head=False) -> KdaDesc:
     return KdaDesc(batch=batch, num_seqs=num_seqs, seqlen=seqlen, heads=heads, dk=dk, dv=dv,
                    dtype=_dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype),
                    chunk=chunk, qk_l2norm=int(bool(qk_l2norm)), scale=float(scale),
-                   reserved0=0, ckpt_every=int(ckpt_every))
+                   gate_per_head=int(gate_per_head), ckpt_every=int(ckpt_every))
 
 
 def chunk_fwd_workspace_bytes(desc: KdaDesc) -> int:
@@ -145,7 +145,8 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
     """Chunkwise KDA prefill through the C ABI.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (float32 or bfloat16); g: [B, T, H, dk]
-    fp32; beta: [B, T, H] fp32; init_state: [N, H, dk, dv] fp32 or None;
+    fp32 (per-channel gates, KDA) or [B, T, H] (one gate per token and head,
+    Gated DeltaNet); beta: [B, T, H] fp32; init_state: [N, H, dk, dv] fp32 or None;
     cu_seqlens: int32 [N + 1] device tensor (B must be 1) or None.
     Returns (o, final_state, state_ckpt); final_state may be passed in (it may
     be the init_state tensor itself).
@@ -158,7 +159,8 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
     _need(q, "q", dt, (B, T, H, dk))
     _need(k, "k", dt, (B, T, H, dk))
     _need(v, "v", dt, (B, T, H, dv))
-    _need(g, "g", torch.float32, (B, T, H, dk))
+    per_head = g.dim() == 3
+    _need(g, "g", torch.float32, (B, T, H) if per_head else (B, T, H, dk))
     _need(beta, "beta", torch.float32, (B, T, H))
     if init_state is not None:
         _need(init_state, "init_state", torch.float32, (N, H, dk, dv))
@@ -175,7 +177,8 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
     if ckpt_every and state_ckpt is None:
         state_ckpt = torch.empty((B, T // ckpt_every, H, dk, dv), dtype=torch.float32, device=dev)
     desc = make_desc(batch=B, num_seqs=N, seqlen=T, heads=H, dk=dk, dv=dv, dtype=dt,
-                     qk_l2norm=qk_l2norm, scale=scale, ckpt_every=ckpt_every)
+                     qk_l2norm=qk_l2norm, scale=scale, ckpt_every=ckpt_every,
+                     gate_per_head=per_head)
     ws_bytes = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
     if ws_bytes == 0 and lib.kda_last_error():
         _check(lib, KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_workspace_bytes")
@@ -193,7 +196,8 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
 def kda_decode_step(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, out=None,
                     stream=None):
     """One KDA decode step through the C ABI; `state` [N, H, dk, dv] fp32 is
-    updated in place.  q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H]."""
+    updated in place.  q, k: [N, H, dk]; g: [N, H, dk] (per-channel) or
+    [N, H] (per head, Gated DeltaNet); v: [N, H, dv]; beta: [N, H]."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -201,14 +205,15 @@ def kda_decode_step(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, out=N
     _need(q, "q", dt, (N, H, dk))
     _need(k, "k", dt, (N, H, dk))
     _need(v, "v", dt, (N, H, dv))
-    _need(g, "g", torch.float32, (N, H, dk))
+    per_head = g.dim() == 2
+    _need(g, "g", torch.float32, (N, H) if per_head else (N, H, dk))
     _need(beta, "beta", torch.float32, (N, H))
     _need(state, "state", torch.float32, (N, H, dk, dv))
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=q.device)
     _need(out, "out", dt, (N, H, dv))
     desc = make_desc(batch=max(N, 1), num_seqs=N, seqlen=1, heads=H, dk=dk, dv=dv, dtype=dt,
-                     qk_l2norm=qk_l2norm, scale=scale)
+                     qk_l2norm=qk_l2norm, scale=scale, gate_per_head=per_head)
     st = lib.kda_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(state), _ptr(out), _stream_handle(stream, q.device))
     _check(lib, st, "kda_decode_step")

@@ -101,8 +101,10 @@ def cu_from_lengths(lengths: torch.Tensor) -> torch.Tensor:
 def prefill_inputs(*, batch: int, seqlen: int, heads: int, dk: int, dv: int,
                    dtype: torch.dtype, device, seed: int, init: str = "zeros",
                    num_seqs: Optional[int] = None, lengths: Optional[list] = None,
-                   len_range: Optional[tuple] = None, gate_shift: float = 3.0) -> dict:
-    """Draw one prefill input set.
+                   len_range: Optional[tuple] = None, gate_shift: float = 3.0,
+                   gate_per_head: bool = False) -> dict:
+    """Draw one prefill input set.  gate_per_head draws one log-gate per
+    (token, head), [B, T, H] (Gated DeltaNet), instead of one per channel.
 
     Dense: [batch, seqlen, H, d].  Varlen: pass `len_range` (lengths drawn
     from the generator first) or explicit `lengths`; inputs are packed as
@@ -125,7 +127,7 @@ def prefill_inputs(*, batch: int, seqlen: int, heads: int, dk: int, dv: int,
     q = _randn(shp_k, gen, device).to(dtype)
     k = _randn(shp_k, gen, device).to(dtype)
     v = _randn(shp_v, gen, device).to(dtype)
-    g = draw_gate(shp_k, gen, device, gate_shift)
+    g = draw_gate((batch, seqlen, heads) if gate_per_head else shp_k, gen, device, gate_shift)
     beta = draw_beta((batch, seqlen, heads), gen, device)
     if init == "zeros":
         s0 = None
@@ -137,12 +139,13 @@ def prefill_inputs(*, batch: int, seqlen: int, heads: int, dk: int, dv: int,
 
 
 def decode_step_inputs(*, num_seqs: int, heads: int, dk: int, dv: int, dtype: torch.dtype,
-                       gen: torch.Generator, device) -> dict:
-    """One decode step's fresh q, k, v, g, beta ([N, H, d] / [N, H])."""
+                       gen: torch.Generator, device, gate_per_head: bool = False) -> dict:
+    """One decode step's fresh q, k, v, g, beta ([N, H, d] / [N, H]); g is
+    [N, H] with gate_per_head."""
     q = _randn((num_seqs, heads, dk), gen, device).to(dtype)
     k = _randn((num_seqs, heads, dk), gen, device).to(dtype)
     v = _randn((num_seqs, heads, dv), gen, device).to(dtype)
-    g = draw_gate((num_seqs, heads, dk), gen, device)
+    g = draw_gate((num_seqs, heads) if gate_per_head else (num_seqs, heads, dk), gen, device)
     beta = draw_beta((num_seqs, heads), gen, device)
     return dict(q=q, k=k, v=v, g=g, beta=beta)
 

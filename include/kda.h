@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -76,6 +76,11 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
  *   scale      o = scale * S^T q (the pages use no query scale: 1.0).
  *   ckpt_every 0 = no checkpoints; else a positive multiple of `chunk` that
  *              divides T; dense layout only.
+ *   gate_per_head  0 (KDA): g holds one log-gate per key channel, [.., dk].
+ *              1 (Gated DeltaNet): g holds one log-gate per (token, head),
+ *              broadcast over the key channels, [..] without the dk axis.
+ *              [XT §3: GDN's scalar forget gate is the special case of KDA's
+ *              per-channel gate with all channels equal.]
  */
 typedef struct {
   int32_t batch;
@@ -88,7 +93,7 @@ typedef struct {
   int32_t chunk;
   int32_t qk_l2norm;
   float scale;
-  int32_t reserved0;  /* must be 0 */
+  int32_t gate_per_head;  /* 0: per-channel gates; 1: one gate per (token, head) */
   int64_t ckpt_every;
 } kda_desc_t;
 
@@ -106,6 +111,7 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_desc_t* desc);
  *   q, k       [B, T, H, dk]  dtype          (raw; normalised inside if qk_l2norm)
  *   v          [B, T, H, dv]  dtype
  *   g          [B, T, H, dk]  fp32, log of the per-channel forget gate, <= 0
+ *              ([B, T, H] when desc->gate_per_head = 1)
  *   beta       [B, T, H]      fp32
  *   init_state [N, H, dk, dv] fp32, or NULL for zeros
  *   cu_seqlens [N + 1] int32 device array, cu[0] = 0, non-decreasing,
@@ -131,7 +137,8 @@ kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
  * [XT §3 decay-then-correct split; XT §5 recurrent form "S_(t-1) + current
  * token -> S_t + output"; XD §"从推理成本看它省在哪": a fixed-size state read
  * and written per step, independent of context length.]
- *   q, k, g    [N, H, dk]   (q, k dtype; g fp32)
+ *   q, k, g    [N, H, dk]   (q, k dtype; g fp32; g is [N, H] when
+ *              desc->gate_per_head = 1)
  *   v          [N, H, dv]   dtype
  *   beta       [N, H]       fp32
  *   state      [N, H, dk, dv] fp32, read and overwritten with S_t

@@ -30,7 +30,7 @@ def test_exports_match_header():
 
 def test_abi_version_and_strings():
     lib = K.load_library()
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
     assert lib.kda_status_string(99) == b"KDA_STATUS_UNKNOWN"
@@ -70,6 +70,7 @@ def _call_chunk(desc, *, q=FAKE, o=FAKE + 0x100, ws=None, ws_bytes=None, cu=None
     (dict(batch=2, num_seqs=1), B.KDA_ERR_INVALID_ARGUMENT),
     (dict(ckpt_every=100), B.KDA_ERR_INVALID_ARGUMENT),
     (dict(ckpt_every=96), B.KDA_ERR_INVALID_ARGUMENT),
+    (dict(gate_per_head=2), B.KDA_ERR_INVALID_ARGUMENT),
 ])
 def test_chunk_desc_errors(kw, status):
     lib = K.load_library()
