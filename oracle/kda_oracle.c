@@ -304,4 +304,52 @@ int kda_oracle_gate_norm_f64(int64_t rows, int64_t dv, int in_dtype, const void*
     return 0;
 }
 
+/* ShortConv + Swish prologue [XT §6 layer diagram: the q, k and v
+ * projections pass a ShortConv and a Swish before the operator (q and k then
+ * the L2 norm); XT §6.1; XD, the preprocessing list: a small-window causal
+ * convolution that mixes each position with the few tokens just before it].
+ * The pages give no window; this project's reading: W taps (4 in every
+ * workload), one filter per channel (depthwise), an optional bias, and
+ * Swish(x) = x * sigmoid(x).  Per sequence n, channel c, token t:
+ *   y_t[c] = swish(bias[c] + sum_{i<W} w[c][i] * x~[t - (W-1) + i][c])
+ * where x~ is the sequence's own input, preceded by the carried state
+ * state[n][c][0..W-2] (the W-1 inputs before the sequence, oldest first) or by
+ * zeros when no state is given.  state_out[n][c][:] = the last W-1 entries of
+ * x~ (carried state followed by the sequence's inputs).
+ * x, y: [B, T, C] row-major (x fp32 or bf16; y fp64 out); varlen: B = 1 and
+ * sequence n covers tokens cu[n] .. cu[n+1]-1.  w: [C][W] fp32; bias [C] fp32
+ * or NULL; state [N][C][W-1] fp32 or NULL; state_out [N][C][W-1] fp64 or NULL. */
+int kda_oracle_short_conv_f64(int64_t batch, int64_t seqlen, int64_t num_seqs, int64_t C,
+                              int64_t W, int in_dtype, const void* x, const float* w,
+                              const float* bias, const float* state, const int32_t* cu_seqlens,
+                              double* y, double* state_out) {
+    if (batch < 1 || seqlen < 0 || num_seqs < 0 || C < 1 || W < 1) return 2;
+    if (in_dtype != 0 && in_dtype != 1) return 2;
+    if (!w || (seqlen > 0 && (!x || !y))) return 2;
+    const int64_t nseq = cu_seqlens ? num_seqs : batch;
+    const int64_t H = W - 1;  /* carried inputs per channel */
+    double* ext = (double*)malloc((size_t)(H + (seqlen > 0 ? seqlen : 1)) * sizeof(double));
+    if (!ext) return 3;
+    for (int64_t n = 0; n < nseq; ++n) {
+        const int64_t t0 = cu_seqlens ? cu_seqlens[n] : 0;
+        const int64_t len = cu_seqlens ? cu_seqlens[n + 1] - cu_seqlens[n] : seqlen;
+        const int64_t rowbase = cu_seqlens ? 0 : n * seqlen;  /* token rows before sequence n */
+        for (int64_t c = 0; c < C; ++c) {
+            /* the extended input: carried state (or zeros), then the sequence */
+            for (int64_t i = 0; i < H; ++i) ext[i] = state ? (double)state[(n * C + c) * H + i] : 0.0;
+            for (int64_t t = 0; t < len; ++t)
+                ext[H + t] = load_in(x, in_dtype, (rowbase + t0 + t) * C + c);
+            for (int64_t t = 0; t < len; ++t) {
+                double acc = bias ? (double)bias[c] : 0.0;
+                for (int64_t i = 0; i < W; ++i) acc += (double)w[c * W + i] * ext[t + i];
+                y[(rowbase + t0 + t) * C + c] = acc / (1.0 + exp(-acc));
+            }
+            if (state_out)
+                for (int64_t i = 0; i < H; ++i) state_out[(n * C + c) * H + i] = ext[len + i];
+        }
+    }
+    free(ext);
+    return 0;
+}
+
 int kda_oracle_abi_version(void) { return 1; }

@@ -59,6 +59,9 @@ def open_library(path: str):
     lib.kda_oracle_decode_f64.restype = ip
     lib.kda_oracle_gate_norm_f64.argtypes = [i64, i64, ip, vp, vp, vp, dp, vp]
     lib.kda_oracle_gate_norm_f64.restype = ip
+    lib.kda_oracle_short_conv_f64.argtypes = [i64, i64, i64, i64, i64, ip, vp, vp, vp, vp, vp,
+                                              vp, vp]
+    lib.kda_oracle_short_conv_f64.restype = ip
     return lib
 
 
@@ -204,3 +207,30 @@ def gate_norm(o, z, w=None, *, eps=1e-6, lib=None):
     if rc != 0:
         raise RuntimeError(f"kda_oracle_gate_norm_f64 failed with code {rc}")
     return y
+
+
+def short_conv(x, w, bias=None, state=None, cu_seqlens=None, *, want_state=True, lib=None):
+    """fp64 ShortConv + Swish: causal depthwise convolution of width W then
+    x * sigmoid(x).  x: [B, T, C] (fp32 or bf16); w: [C, W] fp32; bias: [C]
+    or None; state: [N, C, W-1] fp32 carried inputs (oldest first) or None for
+    zeros; cu_seqlens: int32 [N+1] (B must be 1) or None.
+    Returns (y [B, T, C], state_out [N, C, W-1] or None) as float64."""
+    xa, dt = _as_np(x, "x")
+    wa = _f32(w, "w")
+    ba = _f32(bias, "bias")
+    sa = _f32(state, "state")
+    B, T, C = xa.shape
+    W = wa.shape[1]
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.size - 1
+    else:
+        N = B
+    y = np.zeros((B, T, C), dtype=np.float64)
+    so = np.zeros((N, C, W - 1), dtype=np.float64) if want_state else None
+    rc = _load(lib).kda_oracle_short_conv_f64(B, T, N, C, W, dt, _ptr(xa), _ptr(wa), _ptr(ba),
+                                             _ptr(sa), _ptr(cu), _ptr(y), _ptr(so))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_short_conv_f64 failed with code {rc}")
+    return y, so

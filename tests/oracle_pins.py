@@ -470,6 +470,89 @@ def pin_gate_norm_special_rows(lib=None):
     assert np.array_equal(yb, yf), "bf16 inputs not widened exactly"
 
 
+# --- ShortConv + Swish prologue [XT §6, §6.1; XD preprocessing list] ----------
+def _silu(a):
+    import torch
+    return torch.nn.functional.silu(torch.from_numpy(np.asarray(a, np.float64))).numpy()
+
+
+def pin_conv_shift(lib=None):
+    """A filter with one tap at position W-1-s passes x_{t-s}: the output is
+    swish of the input delayed by s tokens, zeros before the sequence."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((1, 12, 5)).astype(f32)
+    for s_ in range(4):
+        w = np.zeros((5, 4), dtype=f32)
+        w[:, 3 - s_] = 1.0
+        y, st = O.short_conv(x, w, lib=lib)
+        ref = np.zeros_like(y)
+        ref[:, s_:] = _silu(x[:, :12 - s_].astype(np.float64))
+        _close(y, ref, 1e-15, f"shift by {s_}")
+        _close(st, x[0, -3:].T, 0.0 + 1e-300, "carried state = last 3 inputs")
+
+
+def pin_conv_numpy(lib=None):
+    """Pre-activation = numpy's full convolution of each zero-padded channel
+    with the reversed filter (a library routine), then SiLU; with bias."""
+    rng = np.random.default_rng(32)
+    B, T, C, W = 2, 37, 6, 4
+    x = rng.standard_normal((B, T, C)).astype(f32)
+    w = rng.standard_normal((C, W)).astype(f32)
+    bias = rng.standard_normal(C).astype(f32)
+    y, _ = O.short_conv(x, w, bias, lib=lib)
+    pre = np.zeros((B, T, C))
+    for b in range(B):
+        for c in range(C):
+            pre[b, :, c] = np.convolve(x[b, :, c].astype(np.float64),
+                                       w[c, ::-1].astype(np.float64))[:T] + bias[c]
+    _close(y, _silu(pre), 1e-14, "convolution + SiLU")
+
+
+def pin_conv_continuation(lib=None):
+    """Splitting a sequence and carrying the state reproduces the whole run;
+    token-by-token steps (decode) do too; varlen packing (with an empty and a
+    one-token sequence) equals separate runs with their own states."""
+    rng = np.random.default_rng(33)
+    T, C = 50, 8
+    x = rng.standard_normal((1, T, C)).astype(f32)
+    w = rng.standard_normal((C, 4)).astype(f32)
+    s0 = rng.standard_normal((1, C, 3)).astype(f32)
+    y, sf = O.short_conv(x, w, None, s0, lib=lib)
+    y1, s1 = O.short_conv(x[:, :21], w, None, s0, lib=lib)
+    y2, s2 = O.short_conv(x[:, 21:], w, None, s1.astype(f32), lib=lib)
+    _close(np.concatenate([y1, y2], axis=1), y, 1e-15, "split and carry")
+    _close(s2, sf, 1e-300, "carried state after split")
+    st = s0
+    ys = []
+    for t in range(5):
+        yt, st = O.short_conv(x[:, t:t + 1], w, None, st, lib=lib)
+        st = st.astype(f32)
+        ys.append(yt)
+    _close(np.concatenate(ys, axis=1), y[:, :5], 1e-15, "token-by-token steps")
+    lens = [7, 0, 1, 30]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    xs = rng.standard_normal((1, int(cu[-1]), C)).astype(f32)
+    ss = rng.standard_normal((4, C, 3)).astype(f32)
+    yv, sv = O.short_conv(xs, w, None, ss, cu, lib=lib)
+    for n in range(4):
+        a, b = cu[n], cu[n + 1]
+        yn, sn = O.short_conv(xs[:, a:b], w, None, ss[n:n + 1], lib=lib)
+        _close(yv[:, a:b], yn, 1e-300, f"varlen sequence {n}") if b > a else None
+        _close(sv[n:n + 1], sn, 1e-300, f"varlen state {n}")
+
+
+def pin_conv_bf16(lib=None):
+    """bf16 inputs widen exactly."""
+    import torch
+    xb = torch.from_numpy(np.random.default_rng(34).standard_normal((1, 9, 16)).astype(f32)).bfloat16()
+    w = np.random.default_rng(35).standard_normal((16, 4)).astype(f32)
+    yb, _ = O.short_conv(xb, w, lib=lib)
+    yf, _ = O.short_conv(xb.float(), w, lib=lib)
+    assert np.array_equal(yb, yf), "bf16 not widened exactly"
+
+
+CONV_PINS = [pin_conv_shift, pin_conv_numpy, pin_conv_continuation, pin_conv_bf16]
+
 GATE_NORM_PINS = [pin_gate_norm_worked_example, pin_gate_norm_unit_rms,
                   pin_gate_norm_scale_invariance, pin_gate_norm_gate_symmetry,
                   pin_gate_norm_special_rows]
@@ -477,4 +560,4 @@ GATE_NORM_PINS = [pin_gate_norm_worked_example, pin_gate_norm_unit_rms,
 ALL_PINS = [pin_worked_example, pin_gdn, pin_delta_rule, pin_linear_attention,
             pin_l2_normalisation, pin_frozen_and_small_beta, pin_exact_retrieval,
             pin_transition_products, pin_gradient_step, pin_invariances,
-            pin_contractivity] + GATE_NORM_PINS
+            pin_contractivity] + GATE_NORM_PINS + CONV_PINS

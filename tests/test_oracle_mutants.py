@@ -37,6 +37,22 @@ MUTANTS = {
     "gate_swish": ("x * inv_rms * wj * gate;", "x * inv_rms * wj * gate * load_in(z, in_dtype, r * dv + j);"),
     "out_gate_sign": ("exp(-load_in(z, in_dtype, r * dv + j))", "exp(load_in(z, in_dtype, r * dv + j))"),
     "norm_weight_ignored": ("const double wj = w ? (double)w[j] : 1.0;", "const double wj = 1.0;"),
+    # ShortConv + Swish
+    "conv_taps_reversed": ("acc += (double)w[c * W + i] * ext[t + i];",
+                           "acc += (double)w[c * W + (W - 1 - i)] * ext[t + i];"),
+    "conv_state_ignored": ("ext[i] = state ? (double)state[(n * C + c) * H + i] : 0.0;",
+                           "ext[i] = 0.0;"),
+    "conv_state_reversed": ("ext[i] = state ? (double)state[(n * C + c) * H + i] : 0.0;",
+                            "ext[i] = state ? (double)state[(n * C + c) * H + (H - 1 - i)] : 0.0;"),
+    "conv_no_swish": ("y[(rowbase + t0 + t) * C + c] = acc / (1.0 + exp(-acc));",
+                      "y[(rowbase + t0 + t) * C + c] = acc;"),
+    "conv_sigmoid_not_swish": ("y[(rowbase + t0 + t) * C + c] = acc / (1.0 + exp(-acc));",
+                               "y[(rowbase + t0 + t) * C + c] = 1.0 / (1.0 + exp(-acc));"),
+    "conv_bias_ignored": ("double acc = bias ? (double)bias[c] : 0.0;", "double acc = 0.0;"),
+    "conv_state_out_first": ("state_out[(n * C + c) * H + i] = ext[len + i];",
+                             "state_out[(n * C + c) * H + i] = ext[i];"),
+    "conv_varlen_rows": ("ext[H + t] = load_in(x, in_dtype, (rowbase + t0 + t) * C + c);",
+                         "ext[H + t] = load_in(x, in_dtype, (rowbase + t) * C + c);"),
     "norm_over_first_row": ("const double x = load_in(o, in_dtype, r * dv + j);\n            ms += x * x;",
                             "const double x = load_in(o, in_dtype, j);\n            ms += x * x;"),
 }
