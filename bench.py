@@ -38,7 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from gated_delta_rule_54_amd import (chunk_fwd_workspace_bytes, kda_chunk_fwd,  # noqa: E402
-                                     kda_decode_step, kda_output_gate_norm, make_desc)
+                                     kda_decode_step, kda_output_gate_norm,
+                                     kda_short_conv_swish, make_desc)
 from gated_delta_rule_54_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -58,7 +59,10 @@ DECODE_FLOPS_PER_TH = 7 * 128 ** 2
 
 KERNEL_SOURCES = ("gated_delta_rule_54_amd/csrc/kda_chunk.hip",
                   "gated_delta_rule_54_amd/csrc/kda_decode.hip",
-                  "gated_delta_rule_54_amd/csrc/kda_epilogue.hip")
+                  "gated_delta_rule_54_amd/csrc/kda_epilogue.hip",
+                  "gated_delta_rule_54_amd/csrc/kda_conv.hip")
+# prologue bytes per element (bf16): x read + y written (the state is negligible)
+PROLOGUE_BYTES_PER_EL = 2 + 2
 # output epilogue bytes per element (bf16): o read + gate read + y written
 EPILOGUE_BYTES_PER_EL = 2 + 2 + 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_hbm_traffic.json")
@@ -142,6 +146,38 @@ def bench_epilogue(steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
     nbytes = o.numel() * EPILOGUE_BYTES_PER_EL + w.numel() * 4
     return dict(ms=ms, rows=o.shape[0], achieved_gbs=nbytes / (ms * 1e-3) / 1e9, nbytes=nbytes)
+
+
+def prologue_inputs():
+    """Synthetic ShortConv + Swish operands at one projection of the prefill
+    workload: [1, 8192, 32 heads x 128] bf16, width 4."""
+    gen = torch.Generator(device="cuda").manual_seed(1007)
+    C = 32 * 128
+    x = torch.randn(1, 8192, C, generator=gen, device="cuda").bfloat16()
+    w = 0.5 * torch.randn(C, 4, generator=gen, device="cuda")
+    b = 0.1 * torch.randn(C, generator=gen, device="cuda")
+    s = torch.randn(1, C, 3, generator=gen, device="cuda")
+    return x, w, b, s
+
+
+def bench_prologue(steps: int, warmup: int):
+    x, w, b, s = prologue_inputs()
+    y = torch.empty_like(x)
+    so = torch.empty_like(s)
+    stream = torch.cuda.current_stream()
+    run = lambda: kda_short_conv_swish(x, w, b, s, state_out=so, out=y, stream=stream)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = x.numel() * PROLOGUE_BYTES_PER_EL
+    return dict(ms=ms, achieved_gbs=nbytes / (ms * 1e-3) / 1e9)
 
 
 def bench_gate_modes(reps: int = 5):
@@ -296,6 +332,7 @@ def main():
     dc = bench_decode(min(args.warmup, 8))
     ep = bench_epilogue(args.steps, args.warmup)
     gm = bench_gate_modes()
+    pl = bench_prologue(args.steps, args.warmup)
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -342,6 +379,14 @@ def main():
                                   "traffic": (tr_epi / (ep["ms"] * 1e-3) / 1e9) if tr_epi else None,
                                   "kernel": "gate_norm_kernel<bf16,128>",
                                   "bytes_per_element": EPILOGUE_BYTES_PER_EL}},
+        "prologue": {"workload": "ShortConv (width 4) + Swish on one projection of the prefill "
+                                 "workload: [1, 8192, 4096] bf16, carried state in and out",
+                     "us_per_call": pl["ms"] * 1e3,
+                     "roofline": {"bound": "hbm", "achieved": pl["achieved_gbs"],
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": pl["achieved_gbs"] / HBM_PEAK_GBS,
+                                  "traffic": None, "kernel": "short_conv_kernel<bf16,4>",
+                                  "bytes_per_element": PROLOGUE_BYTES_PER_EL}},
         "gate_modes": {"workload": "prefill B=1 H=16 d=128 bf16, T = 2K..64K: per-channel "
                                    "gates (KDA) vs one gate per token and head (GDN)",
                        "rows": gm},

@@ -6,7 +6,8 @@ of include/kda.h (libkda.so, built in-tree by
 Python binding over that ABI; torch provides device memory and streams.
 """
 from .kda import (KdaDesc, KdaError, chunk_fwd_workspace_bytes, kda_chunk_fwd,  # noqa: F401
-                  kda_decode_step, kda_output_gate_norm, load_library, make_desc)
+                  kda_decode_step, kda_output_gate_norm, kda_short_conv_swish, load_library,
+                  make_desc)
 
-__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_output_gate_norm",
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_output_gate_norm", "kda_short_conv_swish",
            "chunk_fwd_workspace_bytes", "load_library", "make_desc", "KdaDesc", "KdaError"]

@@ -213,3 +213,69 @@ KDA_EXPORT kda_status_t kda_output_gate_norm(int64_t rows, int32_t dv, int32_t d
     return fail(KDA_ERR_HIP, "kda_output_gate_norm launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+KDA_EXPORT kda_status_t kda_short_conv_swish(int32_t batch, int64_t seqlen, int32_t num_seqs,
+                                             int32_t channels, int32_t width, int32_t dtype,
+                                             const void* x, const float* w, const float* bias,
+                                             const float* state_in, const int32_t* cu_seqlens,
+                                             void* y, float* state_out, hipStream_t stream) {
+  if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_DTYPE_F32 or KDA_DTYPE_BF16");
+  if (width < 1 || width > 4)
+    return fail(KDA_ERR_UNSUPPORTED, "width must be 1 ... 4 (got %d)", width);
+  const int el = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  if (channels < 1 || channels % (16 / el) != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "channels must be a positive multiple of %d (got %d)",
+                16 / el, channels);
+  if (batch < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
+  if (seqlen < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
+  if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+  if (cu_seqlens) {
+    if (batch != 1)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "varlen (cu_seqlens != NULL) needs batch == 1");
+    if (!aligned(cu_seqlens, 4))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  } else if (num_seqs != batch) {
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dense layout needs num_seqs == batch (%d vs %d)",
+                num_seqs, batch);
+  }
+  if ((double)batch * (double)seqlen * channels > 9.0e18)
+    return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
+  if (!w) return fail(KDA_ERR_INVALID_ARGUMENT, "w is NULL");
+  if (width == 4 && !aligned16(w))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "w must be 16-byte aligned for width 4");
+  const void* p4[] = {w, bias, state_in, state_out};
+  const char* n4[] = {"w", "bias", "state_in", "state_out"};
+  for (int i = 0; i < 4; ++i)
+    if (p4[i] && !aligned(p4[i], 4))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", n4[i]);
+  const bool has_tokens = seqlen > 0;
+  if (has_tokens) {
+    if (!x || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", x ? "y" : "x");
+    if (!aligned16(x) || !aligned16(y))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned");
+    const uintptr_t bytes = (uintptr_t)batch * (uintptr_t)seqlen * channels * el;
+    const uintptr_t px = reinterpret_cast<uintptr_t>(x), py = reinterpret_cast<uintptr_t>(y);
+    if (px < py + bytes && py < px + bytes)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "y must not overlap x");
+  }
+  if (state_in && state_out && width > 1) {
+    const uintptr_t sb = (uintptr_t)num_seqs * channels * (width - 1) * 4;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(state_in);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(state_out);
+    const bool same = pa == pb;
+    const bool in_place_ok = cu_seqlens == nullptr && seqlen <= kda::kConvInPlaceMaxTokens;
+    if (same ? !in_place_ok : (pa < pb + sb && pb < pa + sb))
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "state_out may equal state_in only in the dense layout with seqlen <= %d, "
+                  "and must not otherwise overlap it",
+                  (int)kda::kConvInPlaceMaxTokens);
+  }
+  if (num_seqs == 0 || (channels == 0)) return ok();
+  const kda::kda_conv_args a{batch, seqlen, num_seqs, channels, width, dtype, x, w, bias,
+                             state_in, cu_seqlens, y, width > 1 ? state_out : nullptr};
+  hipError_t e = kda::launch_short_conv(a, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_short_conv_swish launch: %s", hipGetErrorString(e));
+  return ok();
+}

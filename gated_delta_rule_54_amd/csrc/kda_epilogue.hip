@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kEpiThreads) void gate_norm_kernel(
       for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
       const float inv = rsqrtf(ss * (1.f / DV) + eps);
 #pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = x[e] * inv * wv[e] / (1.f + __expf(-g[e]));
+      for (int e = 0; e < E; ++e)
+        x[e] = x[e] * inv * wv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-g[e]));
       if (r < rows) *reinterpret_cast<u32x4e_t*>(y + off[u]) = V::pack(x);
     }
   }

@@ -21,6 +21,27 @@ hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, c
                             const int32_t* cu_seqlens, void* o, float* final_state,
                             float* state_ckpt, void* workspace, hipStream_t stream);
 
+// ShortConv + Swish prologue.  Shapes are validated by the caller.
+struct kda_conv_args {
+  int32_t batch;
+  int64_t seqlen;
+  int32_t num_seqs;
+  int32_t channels;
+  int32_t width;
+  int32_t dtype;
+  const void* x;
+  const float* w;
+  const float* bias;
+  const float* state_in;
+  const int32_t* cu;
+  void* y;
+  float* state_out;
+};
+hipError_t launch_short_conv(const kda_conv_args& a, hipStream_t stream);
+// Largest seqlen for which one thread covers a whole sequence (the carried
+// state may then be updated in place).
+constexpr int64_t kConvInPlaceMaxTokens = 32;
+
 // Output epilogue: head-wise RMSNorm x sigmoid gate over [rows, dv].
 hipError_t launch_gate_norm(int64_t rows, int dv, int dtype, const void* o, const void* z,
                             const float* w, float eps, void* y, hipStream_t stream);

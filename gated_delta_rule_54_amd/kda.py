@@ -29,7 +29,8 @@ KDA_DTYPE_BF16 = 1
 
 # Names every build of the library must export (the declarations of kda.h).
 EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_decode_step",
-            "kda_output_gate_norm", "kda_status_string", "kda_last_error", "kda_abi_version")
+            "kda_output_gate_norm", "kda_short_conv_swish", "kda_status_string",
+            "kda_last_error", "kda_abi_version")
 
 
 class KdaDesc(ctypes.Structure):
@@ -80,6 +81,9 @@ def load_library(path: Optional[str] = None):
     lib.kda_output_gate_norm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, ctypes.c_float,
                                          vp, vp]
     lib.kda_output_gate_norm.restype = i32
+    lib.kda_short_conv_swish.argtypes = [i32, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp, vp,
+                                         vp, vp, vp, vp]
+    lib.kda_short_conv_swish.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -239,3 +243,37 @@ def kda_output_gate_norm(o, z, w=None, *, eps=1e-6, out=None, stream=None):
                                   float(eps), _ptr(out), _stream_handle(stream, o.device))
     _check(lib, st, "kda_output_gate_norm")
     return out
+
+
+def kda_short_conv_swish(x, w, bias=None, state=None, cu_seqlens=None, *, want_state=True,
+                         state_out=None, out=None, stream=None):
+    """ShortConv + Swish through the C ABI.  x: [B, T, C] (float32 or
+    bfloat16, contiguous); w: [C, W] fp32; bias: [C] fp32 or None; state:
+    [N, C, W-1] fp32 carried-in inputs or None (zeros); cu_seqlens: int32
+    [N + 1] (B must be 1) or None.  Returns (y, state_out); state_out may be
+    passed as `state` itself for decode-sized calls (T <= 32, dense)."""
+    lib = load_library()
+    B, T, C = x.shape
+    W = w.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dt = x.dtype
+    _need(x, "x", dt, (B, T, C))
+    _need(w, "w", torch.float32, (C, W))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (C,))
+    if state is not None:
+        _need(state, "state", torch.float32, (N, C, W - 1))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", dt, (B, T, C))
+    if state_out is None and want_state and W > 1:
+        state_out = torch.empty((N, C, W - 1), dtype=torch.float32, device=x.device)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (N, C, W - 1))
+    st = lib.kda_short_conv_swish(B, T, N, C, W, _dtype_code(dt), _ptr(x), _ptr(w), _ptr(bias),
+                                  _ptr(state), _ptr(cu_seqlens), _ptr(out), _ptr(state_out),
+                                  _stream_handle(stream, x.device))
+    _check(lib, st, "kda_short_conv_swish")
+    return out, state_out

@@ -149,6 +149,39 @@ kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, const void* 
                              const void* v, const float* g, const float* beta, float* state,
                              void* o, hipStream_t stream);
 
+/* ShortConv + Swish prologue, the step before q, k and v enter the
+ * operator.  [XT §6 layer diagram: the q, k, v projections pass ShortConv ->
+ * Swish (q, k then the L2 norm, which kda_chunk_fwd / kda_decode_step apply);
+ * XT §6.1; XD preprocessing list: a small-window causal convolution mixing
+ * each position with the few tokens just before it, then Swish.]  One filter
+ * of `width` taps per channel; per sequence n, channel c, token t:
+ *   y[t, c] = swish(bias[c] + sum_{i<width} w[c, i] * x~[t - (width-1) + i, c])
+ * where x~ is the sequence's input preceded by state_in[n, c, :] (its previous
+ * width-1 inputs, oldest first) or by zeros when state_in is NULL, and
+ * swish(a) = a * sigmoid(a).  state_out[n, c, :] receives the last width-1
+ * entries of x~.  For decode, call it with seqlen = 1 and batch = N.
+ *   batch, seqlen, num_seqs  as in kda_desc_t: x, y are [B, T, C]; varlen
+ *              (cu_seqlens != NULL) needs batch == 1, dense needs
+ *              num_seqs == batch
+ *   channels   C >= 1, a multiple of 8 (bf16) or 4 (fp32); for q/k/v of H
+ *              heads, C = H * d
+ *   width      1 ... 4 (the pages give none; 4 in every workload)
+ *   dtype      element type of x and y
+ *   x, y       device, 16-byte aligned; y must not overlap x
+ *   w          [C, width] fp32 (16-byte aligned when width = 4); bias [C]
+ *              fp32 or NULL
+ *   state_in, state_out  [N, C, width-1] fp32 or NULL; state_out may equal
+ *              state_in only in the dense layout with seqlen <= 32 (then one
+ *              thread covers each sequence, e.g. decode steps); otherwise
+ *              they must not overlap
+ *   cu_seqlens as in kda_chunk_fwd (int32 [N+1], not checked on the host)
+ * Asynchronous on `stream`; on a validation error nothing is launched. */
+kda_status_t kda_short_conv_swish(int32_t batch, int64_t seqlen, int32_t num_seqs,
+                                  int32_t channels, int32_t width, int32_t dtype, const void* x,
+                                  const float* w, const float* bias, const float* state_in,
+                                  const int32_t* cu_seqlens, void* y, float* state_out,
+                                  hipStream_t stream);
+
 /* Output epilogue: head-wise RMSNorm times a sigmoid output gate, the two
  * steps that follow the operator in the layer.  [XT §6 layer diagram: KDA ->
  * RMSNorm -> sigmoid output gate -> output projection; XT §6.3: the output is

@@ -157,6 +157,35 @@ def test_gate_norm_errors():
     assert call(rows=0, o=None, z=None, y=None) == B.KDA_OK      # nothing to do
 
 
+def test_short_conv_errors():
+    """Every invalid ShortConv call fails on the host (nothing is launched)."""
+    lib = K.load_library()
+    X, Y, S = FAKE, FAKE + 0x100000, FAKE + 0x200000
+
+    def call(batch=1, seqlen=64, num_seqs=1, channels=64, width=4, dtype=1, x=X, w=FAKE,
+             bias=None, si=None, cu=None, y=Y, so=None):
+        return lib.kda_short_conv_swish(batch, seqlen, num_seqs, channels, width, dtype, x, w,
+                                        bias, si, cu, y, so, None)
+
+    assert call(dtype=7) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(width=0) == B.KDA_ERR_UNSUPPORTED
+    assert call(width=5) == B.KDA_ERR_UNSUPPORTED
+    assert call(channels=12) == B.KDA_ERR_UNSUPPORTED          # bf16 needs a multiple of 8
+    assert call(batch=0) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(seqlen=-1) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(num_seqs=2) == B.KDA_ERR_INVALID_ARGUMENT      # dense: num_seqs == batch
+    assert call(batch=2, num_seqs=3, cu=FAKE) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(w=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(x=None) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(x=X + 8) == B.KDA_ERR_INVALID_ARGUMENT          # not 16-byte aligned
+    assert call(bias=FAKE + 2) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(y=X + 1024) == B.KDA_ERR_INVALID_ARGUMENT      # y overlaps x
+    assert call(si=S, so=S) == B.KDA_ERR_INVALID_ARGUMENT      # in place needs seqlen <= 32
+    assert call(seqlen=8, si=S, so=S, cu=FAKE, num_seqs=1) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(seqlen=8, si=S, so=S + 16) == B.KDA_ERR_INVALID_ARGUMENT  # partial overlap
+    assert call(num_seqs=0, cu=FAKE) == B.KDA_OK                # nothing to do
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         B.load_library(str(tmp_path / "missing.so"))
