@@ -387,11 +387,13 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restr
 //   region 1: Q o e^G (row-major) [exact path: raw q]  -> A (fp32)     -> T Diag(beta)
 //   region 2: K o e^-G (row-major) / exact-path staging -> T (fp32)
 //   region 3: (K o e^G)^T
-// Thread layouts: "row" (tid = 4r + quarter) for the q/k norms, and
-// "channel pair" (tid = cp + (D/2) part): two adjacent channels of RPP
+// Thread layouts: "row" (NQ consecutive threads per row) for the q/k norms,
+// and "channel pair" (tid = cp + (D/2) part): two adjacent channels of RPP
 // consecutive rows, for everything per-element.  A channel-pair thread holds
-// its rows contiguously, so the transposed buffers ((K o e^G)^T, V^T, K~^T)
-// are written 8 rows at a time with 16-byte stores.
+// its rows contiguously, so the transposed LDS tiles ((K o e^G)^T, V^T) are
+// written 8 rows at a time with 16-byte stores.  The operand-order record
+// blocks of Q o e^G and K~ are gathered from LDS on the bf16 fast path (whole
+// 1 KiB blocks per wave) and stored per thread otherwise.
 // K1 workgroup size.  LDS (~77 KiB per workgroup at d = 128) allows two
 // workgroups per CU; 512 threads per chunk then keep 16 waves per CU in
 // flight to hide the input loads, and halve each thread's rows and
@@ -918,11 +920,12 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
 //
 // Per chunk, wave w owns output rows [16w, 16w+16) (W and O) and state rows
 // [16*CBW*w, 16*CBW*(w+1)) (S).  The fragments a wave needs from the chunk's
-// record -- rows of -Wk, Q o e^G and P, rows of K~^T, its U^T block and
+// record -- its rows of -Wk, Q o e^G and P, its rows of K~, its U tiles and
 // e^gamma -- are private to the wave and go straight from memory into
-// registers; only S and W, which every wave reads in full, pass through LDS.
-// The next chunk's fragments are loaded while the current chunk computes
-// (two register sets, loop unrolled by two).
+// registers (the record is stored in operand order, so each fragment is one
+// contiguous 1 KiB wave load); only S and W, which every wave reads in full,
+// pass through LDS.  Fragments are prefetched two chunks ahead into three
+// register sets (see the loop at the end of the kernel).
 // Buffer-resource loads: one resource per head's records, a per-lane 32-bit
 // offset computed once, the slot's record offset in a scalar register and the
 // fragment's constant offset in the instruction -- no per-load address math.
