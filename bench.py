@@ -17,11 +17,16 @@ Prints ONE JSON line.
 
 runs, for hardware-counter passes (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE),
 one 1 GiB device-to-device copy (the calibration kernel: 1 GiB read, 1 GiB
-written), then 2 prefill calls and 2 decode steps, and prints nothing.  The
-per-dispatch counters of those kernels, scaled by the copy's, are recorded
-in profiles/kda_hbm_traffic.json together with a hash of the kernel sources;
-the benchmark reports them as the roofline "traffic" only while the sources
-still match.
+written), then 2 prefill calls, 2 decode steps, 2 epilogue and 2 prologue
+calls, and prints nothing.
+
+    python bench.py --write-traffic FETCH_CSV WRITE_CSV
+
+turns the two passes' counter_collection.csv files into per-call bytes
+(scaled by the copy's counters) and records them in
+profiles/kda_hbm_traffic.json together with a hash of the kernel sources; the
+benchmark reports them as the roofline "traffic" only while the sources still
+match.
 """
 from __future__ import annotations
 
@@ -83,10 +88,11 @@ def measured_traffic():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None, None, None
+        return None, None, None, None
     if t.get("kernel_source_sha256") != kernel_source_hash():
-        return None, None, None
-    return t.get("prefill_call_bytes"), t.get("decode_step_bytes"), t.get("epilogue_call_bytes")
+        return None, None, None, None
+    return (t.get("prefill_call_bytes"), t.get("decode_step_bytes"), t.get("epilogue_call_bytes"),
+            t.get("prologue_call_bytes"))
 
 
 def probe():
@@ -118,6 +124,63 @@ def probe():
     for _ in range(2):
         kda_output_gate_norm(o, z, w)
     torch.cuda.synchronize()
+    del o, z, w
+    x, w, b, s = prologue_inputs()
+    for _ in range(2):
+        kda_short_conv_swish(x, w, b, s)
+    torch.cuda.synchronize()
+
+
+# kernel-name fragment -> (key in the traffic file, calls the probe makes)
+_PROBE_KERNELS = (("kda_intra_chunk", "prefill", 2), ("kda_state_pass", "prefill", 2),
+                  ("decode_step_kernel", "decode", 2), ("gate_norm_kernel", "epilogue", 2),
+                  ("short_conv_kernel", "prologue", 2))
+
+
+def write_traffic(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> dict:
+    """Turn the two counter passes over `--probe` (rocprofv3 --pmc FETCH_SIZE,
+    then WRITE_SIZE; csv output) into HBM bytes per call.  Each counter reads
+    KiB per dispatch; it is scaled by what it reads for the 1 GiB copy."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if len(copy) != 1:
+            raise SystemExit(f"{path}: expected one calibration copy, found {len(copy)}")
+        sums, parts = {}, {}
+        for r in rows:
+            for frag, key, _ in _PROBE_KERNELS:
+                if frag in r["Kernel_Name"]:
+                    sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+                    parts[frag] = parts.get(frag, 0.0) + float(r["Counter_Value"])
+        return copy[0], sums, parts
+
+    gib = 1 << 30
+    f_copy, f_sum, f_parts = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_copy, w_sum, w_parts = per_kernel(write_csv, "WRITE_SIZE")
+    fs, wsc = gib / (f_copy * 1024), gib / (w_copy * 1024)
+    calls = {key: n for _, key, n in _PROBE_KERNELS}
+    t = {"what": "HBM-side bytes (TCC FETCH_SIZE + WRITE_SIZE, each scaled by what it reads "
+                 "for a 1 GiB device copy) per prefill call (B1 H32 T8192 d128 bf16), per "
+                 "decode step (256 x 32 heads, d128), per epilogue call (262144 x 128 bf16) "
+                 "and per prologue call ([1, 8192, 4096] bf16, width 4)",
+         "kernel_source_sha256": kernel_source_hash(),
+         "calibration": {"copy_bytes": gib, "fetch_kib_read": f_copy, "write_kib_read": w_copy,
+                         "fetch_scale": fs, "write_scale": wsc}}
+    for key in calls:
+        if key not in f_sum or key not in w_sum:
+            raise SystemExit(f"no {key} dispatches in the counter files")
+        unit = "step" if key == "decode" else "call"
+        t[f"{key}_{unit}_bytes"] = (f_sum[key] * fs + w_sum[key] * wsc) * 1024 / calls[key]
+    t["breakdown_bytes_per_call"] = {
+        f"{frag}_{kind}": parts[frag] * scale * 1024 / n
+        for frag, _, n in _PROBE_KERNELS
+        for kind, parts, scale in (("fetch", f_parts, fs), ("write", w_parts, wsc))}
+    with open(out, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    return t
 
 
 def epilogue_inputs():
@@ -315,7 +378,13 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--probe", action="store_true",
                     help="run the kernels for hardware-counter passes and exit")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from the two counter passes over --probe")
     args = ap.parse_args()
+    if args.write_traffic:
+        t = write_traffic(*args.write_traffic)
+        print(json.dumps({k: v for k, v in t.items() if k.endswith("_bytes")}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are "
                                    "not part of this build (--gpus must be 1)"}))
@@ -328,7 +397,7 @@ def main():
         probe()
         return
     pf = bench_prefill(args.steps, args.warmup)
-    tr_prefill, tr_decode, tr_epi = measured_traffic()
+    tr_prefill, tr_decode, tr_epi, tr_pro = measured_traffic()
     dc = bench_decode(min(args.warmup, 8))
     ep = bench_epilogue(args.steps, args.warmup)
     gm = bench_gate_modes()
@@ -385,7 +454,8 @@ def main():
                      "roofline": {"bound": "hbm", "achieved": pl["achieved_gbs"],
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": pl["achieved_gbs"] / HBM_PEAK_GBS,
-                                  "traffic": None, "kernel": "short_conv_kernel<bf16,4>",
+                                  "traffic": (tr_pro / (pl["ms"] * 1e-3) / 1e9) if tr_pro else None,
+                                  "kernel": "short_conv_kernel<bf16,4>",
                                   "bytes_per_element": PROLOGUE_BYTES_PER_EL}},
         "gate_modes": {"workload": "prefill B=1 H=16 d=128 bf16, T = 2K..64K: per-channel "
                                    "gates (KDA) vs one gate per token and head (GDN)",
