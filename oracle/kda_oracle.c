@@ -28,11 +28,15 @@
  *   6. o = scale * S^T q^, with the UPDATED state.  [XT §1: o_t = S_t^T q_t]
  * The decode oracle applies the same single-token step to a saved state;
  * [XT §5] names the recurrent form S_(t-1) + current token -> S_t + output.
+ * The backward oracle (kda_oracle_bwd_f64) is the reverse-mode derivative of
+ * the same token steps; its derivation is written above the function.
  *
  * Parity pins: every function here is pinned by tests under tests/ that do
  * not re-type these formulas (worked example, GDN / delta-rule / linear
  * attention special cases, brute-force transition products, the gradient
- * identity, invariances).  No function is "parity unpinned".
+ * identity, invariances; for the backward: central differences of the
+ * forward, the frozen-state and linear-attention closed forms, Euler's
+ * identity).  No function is "parity unpinned".
  *
  * Data layout (all row-major, last index fastest):
  *   q, k  [B, T, H, dk]    v [B, T, H, dv]     g [B, T, H, dk] (fp32)
@@ -73,6 +77,11 @@ typedef struct {
     double *o, *final_state, *ckpt;
     /* decode mode: steps > 0 means [steps, N, H, d] inputs, one token per step */
     int64_t steps;
+    /* backward mode (bwd != 0): upstream gradients in, input gradients out */
+    int bwd;
+    const void* d_o;
+    const float* dfinal;
+    double *grad_q, *grad_k, *grad_v, *grad_g, *grad_beta, *grad_init;
     /* work split */
     int64_t next_chain; /* guarded by mu */
     pthread_mutex_t mu;
@@ -168,6 +177,205 @@ static void run_decode_chain(const job_t* J, int64_t n, int64_t h, double* S,
     if (J->final_state) memcpy(J->final_state + sidx, S, (size_t)sz * sizeof(double));
 }
 
+/* ---------------------------------------------------------------------------
+ * Backward (gradient) oracle.
+ *
+ * [XT §5] has training run the chunkwise form of the same recurrence and
+ * gives no gradient algorithm.  The gradient itself has a plain definition:
+ * the vector-Jacobian product of steps 1-6 above with the upstream gradients
+ * do_t (of every output) and dS_T (of the final state).  It is formed here by
+ * reverse-mode differentiation of the token recurrence, last token first.
+ * With dS = dL/dS_t (everything after token t) on entry:
+ *   a. o = scale S^T q^        dS += scale q^ do^T        dq^ = scale S do
+ *   b. S = S~ + k^ u^T         dk^ = dS u                 du  = dS^T k^
+ *   c. u = beta e,             dv = beta du   dbeta = du . e
+ *      e = v - S~^T k^         dS~ = dS - k^ (beta du)^T  dk^ -= S~ (beta du)
+ *   d. S~ = Diag(a) S_(t-1),   dg_c = sum_j dS~_cj S~_cj  (a = e^g: da/dg = a)
+ *      a = exp(g)              dS_(t-1) = Diag(a) dS~
+ *   e. x^ = x r, r = (|x|^2 + eps)^(-1/2)   dx = r dx^ - r^3 (x . dx^) x
+ *      for q and k when qk_l2norm is set (dx = dx^ otherwise)
+ * Step a uses the updated state S_t, as the forward's read-out does.  The
+ * sweep needs S_(t-1) at every token: the forward pass keeps the state at
+ * every BWD_BLOCK-th token of the chain, and each block's states are
+ * recomputed from the kept one by the same token step, so they are the
+ * identical numbers a full store would hold.
+ */
+#define BWD_BLOCK 64
+
+/* One forward token (steps 1-5) on S in place; no output. */
+static void advance_state(const job_t* J, double* S, double* qh, double* kh, double* u,
+                          int64_t row_k, int64_t row_v, int64_t bidx) {
+    const int64_t dk = J->dk, dv = J->dv;
+    double kk = 0.0;
+    for (int64_t c = 0; c < dk; ++c) {
+        kh[c] = load_in(J->k, J->in_dtype, row_k + c);
+        kk += kh[c] * kh[c];
+    }
+    if (J->qk_l2norm) {
+        const double rk = 1.0 / sqrt(kk + ORACLE_EPS);
+        for (int64_t c = 0; c < dk; ++c) kh[c] *= rk;
+    }
+    for (int64_t c = 0; c < dk; ++c) {
+        const double a = exp((double)J->g[row_k + c]);
+        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= a;
+    }
+    const double b = (double)J->beta[bidx];
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < dk; ++c) acc += S[c * dv + j] * kh[c];
+        u[j] = b * (load_in(J->v, J->in_dtype, row_v + j) - acc);
+    }
+    for (int64_t c = 0; c < dk; ++c)
+        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kh[c] * u[j];
+    (void)qh;
+}
+
+/* Reverse step of one token.  Sp = S_(t-1), Sn = S_t; dS holds dL/dS_t on
+ * entry and dL/dS_(t-1) on exit.  w is scratch of dk*dv + 4*dk + 3*dv. */
+static void reverse_token(const job_t* J, const double* Sp, const double* Sn, double* dS,
+                          double* w, int64_t row_k, int64_t row_v, int64_t bidx) {
+    const int64_t dk = J->dk, dv = J->dv;
+    double* St = w;               /* S~ = Diag(a) S_(t-1)   dk x dv */
+    double* qx = St + dk * dv;    /* raw q, then q^          dk */
+    double* kx = qx + dk;         /* raw k, then k^          dk */
+    double* dqh = kx + dk;        /* dL/dq^                  dk */
+    double* dkh = dqh + dk;       /* dL/dk^                  dk */
+    double* e = dkh + dk;         /* v - S~^T k^             dv */
+    double* du = e + dv;          /* dL/du                   dv */
+    double* don = du + dv;        /* do_t                    dv */
+    double qq = 0.0, kk = 0.0;
+    for (int64_t c = 0; c < dk; ++c) {
+        qx[c] = load_in(J->q, J->in_dtype, row_k + c);
+        kx[c] = load_in(J->k, J->in_dtype, row_k + c);
+        qq += qx[c] * qx[c];
+        kk += kx[c] * kx[c];
+    }
+    const double rq = J->qk_l2norm ? 1.0 / sqrt(qq + ORACLE_EPS) : 1.0;
+    const double rk = J->qk_l2norm ? 1.0 / sqrt(kk + ORACLE_EPS) : 1.0;
+    double qh_c, kh_c;
+    for (int64_t c = 0; c < dk; ++c) {
+        const double a = exp((double)J->g[row_k + c]);
+        for (int64_t j = 0; j < dv; ++j) St[c * dv + j] = a * Sp[c * dv + j];
+    }
+    const double b = (double)J->beta[bidx];
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < dk; ++c) acc += St[c * dv + j] * (kx[c] * rk);
+        e[j] = load_in(J->v, J->in_dtype, row_v + j) - acc;
+        don[j] = load_in(J->d_o, J->in_dtype, row_v + j);
+    }
+    /* a. read-out */
+    for (int64_t c = 0; c < dk; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < dv; ++j) acc += Sn[c * dv + j] * don[j];
+        dqh[c] = J->scale * acc;
+        qh_c = qx[c] * rq;
+        for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] += J->scale * qh_c * don[j];
+    }
+    /* b. rank-1 write (u = beta e) */
+    for (int64_t c = 0; c < dk; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < dv; ++j) acc += dS[c * dv + j] * (b * e[j]);
+        dkh[c] = acc;
+    }
+    for (int64_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < dk; ++c) acc += dS[c * dv + j] * (kx[c] * rk);
+        du[j] = acc;
+    }
+    /* c. correction */
+    double db = 0.0;
+    for (int64_t j = 0; j < dv; ++j) {
+        J->grad_v[row_v + j] = b * du[j];
+        db += du[j] * e[j];
+    }
+    J->grad_beta[bidx] = db;
+    for (int64_t c = 0; c < dk; ++c) {
+        kh_c = kx[c] * rk;
+        double acc = 0.0;
+        for (int64_t j = 0; j < dv; ++j) {
+            dS[c * dv + j] -= kh_c * (b * du[j]);
+            acc += St[c * dv + j] * (b * du[j]);
+        }
+        dkh[c] -= acc;
+    }
+    /* d. decay */
+    for (int64_t c = 0; c < dk; ++c) {
+        const double a = exp((double)J->g[row_k + c]);
+        double acc = 0.0;
+        for (int64_t j = 0; j < dv; ++j) acc += dS[c * dv + j] * St[c * dv + j];
+        J->grad_g[row_k + c] = acc;
+        for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] *= a;
+    }
+    /* e. L2 normalisation */
+    double qd = 0.0, kd = 0.0;
+    for (int64_t c = 0; c < dk; ++c) { qd += qx[c] * dqh[c]; kd += kx[c] * dkh[c]; }
+    for (int64_t c = 0; c < dk; ++c) {
+        if (J->qk_l2norm) {
+            J->grad_q[row_k + c] = rq * dqh[c] - rq * rq * rq * qd * qx[c];
+            J->grad_k[row_k + c] = rk * dkh[c] - rk * rk * rk * kd * kx[c];
+        } else {
+            J->grad_q[row_k + c] = dqh[c];
+            J->grad_k[row_k + c] = dkh[c];
+        }
+    }
+}
+
+/* Gradients of one (sequence, head) chain.  Returns nonzero on allocation
+ * failure. */
+static int run_bwd_chain(const job_t* J, int64_t n, int64_t h) {
+    const int64_t H = J->heads, dk = J->dk, dv = J->dv, sz = dk * dv;
+    int64_t tok0, len;
+    if (J->cu_seqlens) {
+        tok0 = J->cu_seqlens[n];
+        len = (int64_t)J->cu_seqlens[n + 1] - tok0;
+    } else {
+        tok0 = n * J->seqlen;
+        len = J->seqlen;
+    }
+    const int64_t nblk = (len + BWD_BLOCK - 1) / BWD_BLOCK;
+    double* kept = (double*)malloc((size_t)(nblk > 0 ? nblk : 1) * sz * sizeof(double));
+    double* blk = (double*)malloc((size_t)(BWD_BLOCK + 1) * sz * sizeof(double));
+    double* dS = (double*)malloc((size_t)sz * sizeof(double));
+    double* w = (double*)malloc((size_t)(sz + 4 * dk + 3 * dv) * sizeof(double));
+    double* vec = (double*)malloc((size_t)(2 * dk + dv) * sizeof(double));
+    if (!kept || !blk || !dS || !w || !vec) {
+        free(kept); free(blk); free(dS); free(w); free(vec);
+        return 1;
+    }
+    double *qh = vec, *kh = vec + dk, *u = vec + 2 * dk;
+    const int64_t sidx = (n * H + h) * sz;
+    /* forward sweep: keep the state entering every block */
+    double* S = blk;
+    for (int64_t i = 0; i < sz; ++i) S[i] = J->init_state ? (double)J->init_state[sidx + i] : 0.0;
+    for (int64_t t = 0; t < len; ++t) {
+        if (t % BWD_BLOCK == 0) memcpy(kept + (t / BWD_BLOCK) * sz, S, (size_t)sz * sizeof(double));
+        const int64_t tok = tok0 + t;
+        advance_state(J, S, qh, kh, u, (tok * H + h) * dk, (tok * H + h) * dv, tok * H + h);
+    }
+    /* reverse sweep */
+    for (int64_t i = 0; i < sz; ++i) dS[i] = J->dfinal ? (double)J->dfinal[sidx + i] : 0.0;
+    for (int64_t b = nblk - 1; b >= 0; --b) {
+        const int64_t t0 = b * BWD_BLOCK;
+        const int64_t t1 = (t0 + BWD_BLOCK < len) ? t0 + BWD_BLOCK : len;
+        memcpy(blk, kept + b * sz, (size_t)sz * sizeof(double));
+        for (int64_t t = t0; t < t1; ++t) {
+            double* nxt = blk + (t - t0 + 1) * sz;
+            memcpy(nxt, blk + (t - t0) * sz, (size_t)sz * sizeof(double));
+            const int64_t tok = tok0 + t;
+            advance_state(J, nxt, qh, kh, u, (tok * H + h) * dk, (tok * H + h) * dv, tok * H + h);
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            const int64_t tok = tok0 + t;
+            reverse_token(J, blk + (t - t0) * sz, blk + (t - t0 + 1) * sz, dS, w,
+                          (tok * H + h) * dk, (tok * H + h) * dv, tok * H + h);
+        }
+    }
+    if (J->grad_init) memcpy(J->grad_init + sidx, dS, (size_t)sz * sizeof(double));
+    free(kept); free(blk); free(dS); free(w); free(vec);
+    return 0;
+}
+
 static void* worker(void* arg) {
     job_t* J = (job_t*)arg;
     const int64_t sz = J->dk * J->dv;
@@ -177,17 +385,23 @@ static void* worker(void* arg) {
     double* u = (double*)malloc((size_t)J->dv * sizeof(double));
     if (!S || !qh || !kh || !u) { free(S); free(qh); free(kh); free(u); return (void*)1; }
     const int64_t total = J->num_seqs * J->heads;
+    int failed = 0;
     for (;;) {
         pthread_mutex_lock(&J->mu);
         int64_t c = J->next_chain++;
         pthread_mutex_unlock(&J->mu);
         if (c >= total) break;
         const int64_t n = c / J->heads, h = c % J->heads;
-        if (J->steps > 0) run_decode_chain(J, n, h, S, qh, kh, u);
-        else run_fwd_chain(J, n, h, S, qh, kh, u);
+        if (J->bwd) {
+            if (run_bwd_chain(J, n, h)) { failed = 1; break; }
+        } else if (J->steps > 0) {
+            run_decode_chain(J, n, h, S, qh, kh, u);
+        } else {
+            run_fwd_chain(J, n, h, S, qh, kh, u);
+        }
     }
     free(S); free(qh); free(kh); free(u);
-    return NULL;
+    return failed ? (void*)1 : NULL;
 }
 
 static int run_job(job_t* J, int nthreads) {
@@ -268,6 +482,43 @@ int kda_oracle_decode_f64(int64_t steps, int64_t num_seqs, int64_t heads, int64_
     J.scale = scale; J.ckpt_every = 0;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.init_state = state_in;
     J.o = o; J.final_state = state_out; J.steps = steps;
+    return run_job(&J, nthreads) ? 3 : 0;
+}
+
+/* Backward oracle: input gradients of the prefill operator for upstream
+ * gradients d_o [B, T, H, dv] (in_dtype, like q/k/v) and dfinal [N, H, dk, dv]
+ * (fp32; NULL = zero).  Outputs (fp64, all required except dinit): dq, dk
+ * [B, T, H, dk], dv [B, T, H, dv], dg [B, T, H, dk], dbeta [B, T, H], dinit
+ * [N, H, dk, dv] or NULL.  Other arguments as kda_oracle_fwd_f64.  Returns 0
+ * on success, 2 on bad arguments, 3 on allocation failure. */
+int kda_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t num_seqs, int64_t heads,
+                       int64_t dk, int64_t dv, int in_dtype, const void* q, const void* k,
+                       const void* v, const float* g, const float* beta,
+                       const float* init_state, const int32_t* cu_seqlens, int qk_l2norm,
+                       double scale, const void* d_o, const float* dfinal, double* dq,
+                       double* dkk, double* dvv, double* dg, double* dbeta, double* dinit,
+                       int nthreads) {
+    if (batch < 1 || seqlen < 0 || heads < 1 || dk < 1 || dv < 1) return 2;
+    if (in_dtype != 0 && in_dtype != 1) return 2;
+    if (!q || !k || !v || !g || !beta || !d_o || !dq || !dkk || !dvv || !dg || !dbeta) return 2;
+    if (cu_seqlens) {
+        if (batch != 1 || num_seqs < 1) return 2;
+        if (cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != seqlen) return 2;
+        for (int64_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return 2;
+    } else if (num_seqs != batch) {
+        return 2;
+    }
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.batch = batch; J.seqlen = seqlen; J.num_seqs = num_seqs; J.heads = heads;
+    J.dk = dk; J.dv = dv; J.in_dtype = in_dtype; J.qk_l2norm = qk_l2norm;
+    J.scale = scale;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.init_state = init_state;
+    J.cu_seqlens = cu_seqlens;
+    J.bwd = 1; J.d_o = d_o; J.dfinal = dfinal;
+    J.grad_q = dq; J.grad_k = dkk; J.grad_v = dvv; J.grad_g = dg; J.grad_beta = dbeta;
+    J.grad_init = dinit;
     return run_job(&J, nthreads) ? 3 : 0;
 }
 
@@ -352,4 +603,4 @@ int kda_oracle_short_conv_f64(int64_t batch, int64_t seqlen, int64_t num_seqs, i
     return 0;
 }
 
-int kda_oracle_abi_version(void) { return 1; }
+int kda_oracle_abi_version(void) { return 2; }

@@ -62,6 +62,10 @@ def open_library(path: str):
     lib.kda_oracle_short_conv_f64.argtypes = [i64, i64, i64, i64, i64, ip, vp, vp, vp, vp, vp,
                                               vp, vp]
     lib.kda_oracle_short_conv_f64.restype = ip
+    lib.kda_oracle_bwd_f64.argtypes = [i64, i64, i64, i64, i64, i64, ip,
+                                       vp, vp, vp, vp, vp, vp, vp, ip, dp,
+                                       vp, vp, vp, vp, vp, vp, vp, vp, ip]
+    lib.kda_oracle_bwd_f64.restype = ip
     return lib
 
 
@@ -157,6 +161,55 @@ def kda_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2norm=Tru
     if rc != 0:
         raise RuntimeError(f"kda_oracle_fwd_f64 failed with code {rc}")
     return o, fs, ck
+
+
+def kda_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens=None, *,
+            qk_l2norm=True, scale=1.0, nthreads=None, lib=None):
+    """fp64 gradients of the KDA prefill (reverse sweep of the token recurrence).
+
+    q, k, v, g, beta, init_state, cu_seqlens as :func:`kda_fwd`; do: [B, T, H, dv]
+    with q's dtype; dfinal: [N, H, dk, dv] float32 or None (zero).
+    Returns (dq, dk, dv, dg, dbeta, dinit) as float64 arrays of the inputs'
+    shapes (dinit [N, H, dk, dv]).
+    """
+    qa, dt = _as_np(q, "q")
+    ka, dt2 = _as_np(k, "k")
+    va, dt3 = _as_np(v, "v")
+    da, dt4 = _as_np(do, "do")
+    if not (dt == dt2 == dt3 == dt4):
+        raise ValueError("q, k, v, do must share a dtype")
+    ga = _f32(g, "g")
+    ba = _f32(beta, "beta")
+    sa = _f32(init_state, "init_state")
+    fa = _f32(dfinal, "dfinal")
+    B, T, H, dk = qa.shape
+    dv = va.shape[-1]
+    if ka.shape != (B, T, H, dk) or va.shape != (B, T, H, dv) or ga.shape != (B, T, H, dk) \
+            or ba.shape != (B, T, H) or da.shape != (B, T, H, dv):
+        raise ValueError("shape mismatch")
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        N = B
+    for a, what in ((sa, "init_state"), (fa, "dfinal")):
+        if a is not None and a.shape != (N, H, dk, dv):
+            raise ValueError(f"{what} shape mismatch")
+    dq = np.zeros((B, T, H, dk), dtype=np.float64)
+    dkk = np.zeros((B, T, H, dk), dtype=np.float64)
+    dvv = np.zeros((B, T, H, dv), dtype=np.float64)
+    dg = np.zeros((B, T, H, dk), dtype=np.float64)
+    db = np.zeros((B, T, H), dtype=np.float64)
+    ds0 = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = _load(lib).kda_oracle_bwd_f64(B, T, N, H, dk, dv, dt, _ptr(qa), _ptr(ka), _ptr(va),
+                                    _ptr(ga), _ptr(ba), _ptr(sa), _ptr(cu), int(bool(qk_l2norm)),
+                                    float(scale), _ptr(da), _ptr(fa), _ptr(dq), _ptr(dkk),
+                                    _ptr(dvv), _ptr(dg), _ptr(db), _ptr(ds0),
+                                    int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_bwd_f64 failed with code {rc}")
+    return dq, dkk, dvv, dg, db, ds0
 
 
 def kda_decode(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, nthreads=None,

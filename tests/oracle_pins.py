@@ -551,6 +551,162 @@ def pin_conv_bf16(lib=None):
     assert np.array_equal(yb, yf), "bf16 not widened exactly"
 
 
+# --- backward (gradient) pins ----------------------------------------------------
+# [XT §5]: training runs the chunkwise form; the gradient of the operator is
+# the vector-Jacobian product of its forward map.  These pins fix it from
+# outside the reverse sweep: central differences of the (pinned) forward
+# oracle, closed forms where the recurrence reduces to a read-out of a frozen
+# state or to linear attention, and Euler's identity for the parts of the map
+# that are homogeneous.
+
+def _loss(q, k, v, g, beta, s0, do, dfin, cu=None, *, l2, scale, lib):
+    o, fs, _ = O.kda_fwd(q, k, v, g, beta, s0, cu, qk_l2norm=l2, scale=scale, nthreads=1,
+                         lib=lib)
+    return float(np.sum(o * do) + np.sum(fs * dfin))
+
+
+def _fd_check(inp, cu, *, l2, scale, lib, samples=None, seed=0, h=2.0 ** -12, tol=1e-6):
+    """Central differences of the forward oracle against kda_bwd, every
+    component of every input (or `samples` random ones per input)."""
+    q, k, v, g, beta, s0, do, dfin = inp
+    grads = O.kda_bwd(q, k, v, g, beta, do, s0, dfin, cu, qk_l2norm=l2, scale=scale,
+                      nthreads=1, lib=lib)
+    rng = np.random.default_rng(seed)
+    args = [q, k, v, g, beta, s0]
+    for ai, name in enumerate(("q", "k", "v", "g", "beta", "init_state")):
+        x, grad = args[ai], grads[ai]
+        if samples is None:
+            idxs = list(np.ndindex(*x.shape))
+        else:
+            idxs = [tuple(int(rng.integers(0, n)) for n in x.shape) for _ in range(samples)]
+        gmax = max(np.max(np.abs(grad)), 1e-30)
+        for idx in idxs:
+            plus, minus = list(args), list(args)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += f32(h)
+            xm[idx] -= f32(h)
+            plus[ai], minus[ai] = xp, xm
+            fd = (_loss(*plus, do, dfin, cu, l2=l2, scale=scale, lib=lib) -
+                  _loss(*minus, do, dfin, cu, l2=l2, scale=scale, lib=lib)) / (2 * h)
+            err = abs(fd - grad[idx]) / gmax
+            assert err <= tol, f"d{name}{idx}: fd {fd:.9e} vs {grad[idx]:.9e} ({err:.2e})"
+
+
+def _bwd_problem(rng, B, T, H, dk, dv, N=None):
+    q, k, v, g, beta = _rand_problem(rng, B, T, H, dk, dv)
+    N = B if N is None else N
+    s0 = (0.5 * rng.standard_normal((N, H, dk, dv))).astype(f32)
+    do = rng.standard_normal((B, T, H, dv)).astype(f32)
+    dfin = rng.standard_normal((N, H, dk, dv)).astype(f32)
+    return q, k, v, g, beta, s0, do, dfin
+
+
+def pin_bwd_finite_differences(lib=None):
+    """Every input gradient equals the central difference of the forward map
+    (error O(h^2) ~ 1e-8 at h = 2^-12): dense with the L2 norm and a read-out
+    scale, varlen with an empty sequence and no norm, and one chain longer
+    than the sweep's 64-token recompute block."""
+    rng = np.random.default_rng(41)
+    _fd_check(_bwd_problem(rng, 2, 5, 2, 4, 3), None, l2=True, scale=0.6, lib=lib)
+    cu = np.array([0, 3, 3, 9], np.int32)
+    _fd_check(_bwd_problem(rng, 1, 9, 1, 3, 2, N=3), cu, l2=False, scale=1.0, lib=lib)
+    _fd_check(_bwd_problem(rng, 1, 70, 1, 3, 2), None, l2=True, scale=1.0, lib=lib,
+              samples=25, seed=3)
+
+
+def pin_bwd_frozen_state(lib=None):
+    """beta = 0: nothing is written, S_t = Diag(prod_(s<=t) a_s) S_0 and
+    o_t = scale S_t^T q_t.  With G_t = dL/dS_t = scale sum_(t'>=t) D(t,t') q_t' do_t'^T
+    + D(t,T) dS_T (D the decay between the two tokens), the closed forms are
+    dq_t = scale S_t do_t, dk = dv = 0, dg_t = rowsum(G_t o S_t),
+    dbeta_t = (G_t^T k_t) . (v_t - S_t^T k_t) and dS_0 = Diag(a_0) G_0."""
+    rng = np.random.default_rng(43)
+    T, dk, dv, scale = 7, 5, 4, 0.8
+    q, k, v, g, _ = (x[0, :, 0] for x in _rand_problem(rng, 1, T, 1, dk, dv, gate_shift=0.5))
+    beta = np.zeros(T, f32)
+    s0 = rng.standard_normal((dk, dv)).astype(f32)
+    do = rng.standard_normal((T, dv)).astype(f32)
+    dfin = rng.standard_normal((dk, dv)).astype(f32)
+    r = O.kda_bwd(q.reshape(1, T, 1, dk), k.reshape(1, T, 1, dk), v.reshape(1, T, 1, dv),
+                  g.reshape(1, T, 1, dk), beta.reshape(1, T, 1), do.reshape(1, T, 1, dv),
+                  s0.reshape(1, 1, dk, dv), dfin.reshape(1, 1, dk, dv), qk_l2norm=False,
+                  scale=scale, nthreads=1, lib=lib)
+    dq, dkk, dvv, dg = (x[0, :, 0] for x in r[:4])
+    db = r[4][0, :, 0]
+    ds0 = r[5][0, 0]
+    Q, K, V, Gl, S0, DO, DF = (x.astype(np.float64) for x in (q, k, v, g, s0, do, dfin))
+    cum = np.cumsum(Gl, axis=0)                     # log decay from 0 through t
+    S = [np.exp(cum[t])[:, None] * S0 for t in range(T)]
+    Gt = []
+    for t in range(T):
+        acc = np.exp(cum[-1] - cum[t])[:, None] * DF
+        for t2 in range(t, T):
+            acc = acc + scale * np.exp(cum[t2] - cum[t])[:, None] * np.outer(Q[t2], DO[t2])
+        Gt.append(acc)
+    _close(dq, np.stack([scale * S[t] @ DO[t] for t in range(T)]), 1e-12, "frozen dq")
+    assert np.max(np.abs(dkk)) == 0.0 and np.max(np.abs(dvv)) == 0.0, "frozen dk, dv"
+    _close(dg, np.stack([np.sum(Gt[t] * S[t], axis=1) for t in range(T)]), 1e-12, "frozen dg")
+    _close(db, np.array([(Gt[t].T @ K[t]) @ (V[t] - S[t].T @ K[t]) for t in range(T)]),
+           1e-12, "frozen dbeta")
+    _close(ds0, np.exp(cum[0])[:, None] * Gt[0], 1e-12, "frozen dS_0")
+
+
+def pin_bwd_linear_attention(lib=None):
+    """Orthonormal keys, alpha = 1, S_0 = 0, no norm: o_t = scale sum_(i<=t)
+    beta_i v_i (k_i . q_t) (linear attention, [XT §1]), and every correction and
+    its derivative in v, beta, q vanish, so dv_i = scale beta_i sum_(t>=i)
+    (k_i . q_t) do_t + beta_i dS_T^T k_i, dq_t = scale sum_(i<=t) beta_i k_i (v_i . do_t),
+    dbeta_i = scale sum_(t>=i) (k_i . q_t)(v_i . do_t) + k_i^T dS_T v_i."""
+    rng = np.random.default_rng(47)
+    T, dk, dv, scale = 6, 16, 5, 0.9
+    k = _orthonormal(T, dk, rng).astype(f32)
+    q = rng.standard_normal((T, dk)).astype(f32)
+    v = rng.standard_normal((T, dv)).astype(f32)
+    beta = rng.uniform(0.2, 1.0, T).astype(f32)
+    g = np.zeros((T, dk), f32)
+    do = rng.standard_normal((T, dv)).astype(f32)
+    dfin = rng.standard_normal((dk, dv)).astype(f32)
+    r = O.kda_bwd(q.reshape(1, T, 1, dk), k.reshape(1, T, 1, dk), v.reshape(1, T, 1, dv),
+                  g.reshape(1, T, 1, dk), beta.reshape(1, T, 1), do.reshape(1, T, 1, dv),
+                  None, dfin.reshape(1, 1, dk, dv), qk_l2norm=False, scale=scale, nthreads=1,
+                  lib=lib)
+    dq, dvv = r[0][0, :, 0], r[2][0, :, 0]
+    db = r[4][0, :, 0]
+    Q, K, V, Bt, DO, DF = (x.astype(np.float64) for x in (q, k, v, beta, do, dfin))
+    M = np.triu(K @ Q.T)                               # M[i, t] = k_i . q_t for t >= i
+    _close(dvv, scale * Bt[:, None] * (M @ DO) + Bt[:, None] * (K @ DF), 1e-12, "linear dv")
+    _close(dq, scale * np.tril(DO @ V.T * Bt[None, :]) @ K, 1e-12, "linear dq")
+    _close(db, scale * np.sum(M * (V @ DO.T), axis=1) + np.einsum("ic,cj,ij->i", K, DF, V),
+           1e-12, "linear dbeta")
+
+
+def pin_bwd_homogeneity(lib=None):
+    """Euler's identity on homogeneous parts of the map: the recurrence is
+    linear in (v, S_0) jointly, so sum v dv + sum S_0 dS_0 = L; without the
+    norm o is linear in q, so sum q dq = sum do . o; with the norm o is
+    unchanged by rescaling one token's q or k, so q_t . dq_t = k_t . dk_t = 0
+    (up to the eps under the root)."""
+    rng = np.random.default_rng(53)
+    q, k, v, g, beta, s0, do, dfin = _bwd_problem(rng, 2, 40, 2, 8, 6)
+    for l2 in (False, True):
+        dq, dkk, dvv, _, _, ds0 = O.kda_bwd(q, k, v, g, beta, do, s0, dfin, qk_l2norm=l2,
+                                            scale=0.7, lib=lib)
+        o, fs, _ = O.kda_fwd(q, k, v, g, beta, s0, qk_l2norm=l2, scale=0.7, lib=lib)
+        L = np.sum(o * do) + np.sum(fs * dfin)
+        _close(np.sum(v * dvv) + np.sum(s0 * ds0), L, 1e-11, f"Euler in (v, S_0), l2={l2}")
+        if not l2:
+            _close(np.sum(q * dq), np.sum(o * do), 1e-11, "Euler in q")
+        else:
+            tq = np.sum(q.astype(np.float64) * dq, axis=-1)
+            tk = np.sum(k.astype(np.float64) * dkk, axis=-1)
+            ref = np.max(np.abs(q)) * np.max(np.abs(dq)) + np.max(np.abs(k)) * np.max(np.abs(dkk))
+            assert np.max(np.abs(tq)) <= 1e-5 * ref and np.max(np.abs(tk)) <= 1e-5 * ref, \
+                "scale invariance of the L2 norm"
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_frozen_state, pin_bwd_linear_attention,
+            pin_bwd_homogeneity]
+
 CONV_PINS = [pin_conv_shift, pin_conv_numpy, pin_conv_continuation, pin_conv_bf16]
 
 GATE_NORM_PINS = [pin_gate_norm_worked_example, pin_gate_norm_unit_rms,
@@ -560,4 +716,4 @@ GATE_NORM_PINS = [pin_gate_norm_worked_example, pin_gate_norm_unit_rms,
 ALL_PINS = [pin_worked_example, pin_gdn, pin_delta_rule, pin_linear_attention,
             pin_l2_normalisation, pin_frozen_and_small_beta, pin_exact_retrieval,
             pin_transition_products, pin_gradient_step, pin_invariances,
-            pin_contractivity] + GATE_NORM_PINS + CONV_PINS
+            pin_contractivity] + GATE_NORM_PINS + CONV_PINS + BWD_PINS

@@ -55,6 +55,31 @@ MUTANTS = {
                          "ext[H + t] = load_in(x, in_dtype, (rowbase + t) * C + c);"),
     "norm_over_first_row": ("const double x = load_in(o, in_dtype, r * dv + j);\n            ms += x * x;",
                             "const double x = load_in(o, in_dtype, j);\n            ms += x * x;"),
+    # backward (reverse sweep)
+    "bwd_readout_old_state": ("for (int64_t j = 0; j < dv; ++j) acc += Sn[c * dv + j] * don[j];",
+                              "for (int64_t j = 0; j < dv; ++j) acc += Sp[c * dv + j] * don[j];"),
+    "bwd_readout_scale": ("dqh[c] = J->scale * acc;", "dqh[c] = acc;"),
+    "bwd_state_from_q_dropped": ("dS[c * dv + j] += J->scale * qh_c * don[j];",
+                                 "dS[c * dv + j] += 0.0 * qh_c * don[j];"),
+    "bwd_dk_write_dropped": ("acc += dS[c * dv + j] * (b * e[j]);",
+                             "acc += 0.0 * dS[c * dv + j] * (b * e[j]);"),
+    "bwd_dbeta_uses_u": ("db += du[j] * e[j];", "db += du[j] * b * e[j];"),
+    "bwd_dv_no_beta": ("J->grad_v[row_v + j] = b * du[j];", "J->grad_v[row_v + j] = du[j];"),
+    "bwd_correction_sign": ("dS[c * dv + j] -= kh_c * (b * du[j]);",
+                            "dS[c * dv + j] += kh_c * (b * du[j]);"),
+    "bwd_dk_correction_dropped": ("dkh[c] -= acc;", "dkh[c] -= 0.0 * acc;"),
+    "bwd_dg_prev_state": ("acc += dS[c * dv + j] * St[c * dv + j];",
+                          "acc += dS[c * dv + j] * Sp[c * dv + j];"),
+    "bwd_no_decay_back": ("for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] *= a;",
+                          "for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] *= 1.0;"),
+    "bwd_norm_no_projection": ("J->grad_k[row_k + c] = rk * dkh[c] - rk * rk * rk * kd * kx[c];",
+                               "J->grad_k[row_k + c] = rk * dkh[c];"),
+    "bwd_norm_q_with_k": ("J->grad_q[row_k + c] = rq * dqh[c] - rq * rq * rq * qd * qx[c];",
+                          "J->grad_q[row_k + c] = rq * dqh[c] - rq * rq * rq * qd * kx[c];"),
+    "bwd_dfinal_ignored": ("dS[i] = J->dfinal ? (double)J->dfinal[sidx + i] : 0.0;",
+                           "dS[i] = 0.0;"),
+    "bwd_block_restart": ("memcpy(blk, kept + b * sz, (size_t)sz * sizeof(double));",
+                          "memcpy(blk, kept, (size_t)sz * sizeof(double));"),
 }
 
 
