@@ -147,7 +147,7 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu%s", need_ws,
                 workspace_bytes, workspace ? "" : " (NULL)");
   hipError_t e = kda::launch_chunk_fwd(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                       final_state, state_ckpt, workspace, stream);
+                                       final_state, state_ckpt, nullptr, workspace, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_fwd launch: %s", hipGetErrorString(e));
   return ok();
 }

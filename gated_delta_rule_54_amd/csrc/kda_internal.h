@@ -15,11 +15,25 @@ hipError_t launch_decode(const kda_desc_t& d, const void* q, const void* k, cons
                          hipStream_t stream);
 
 // Chunkwise prefill.  Workspace size and launch plan live in kda_chunk.hip.
+// chunk_states (or nullptr): the state entering every chunk slot,
+// [slot][H][dk][dv] fp32, for the backward; o may then be nullptr.
 size_t chunk_workspace_bytes(const kda_desc_t& d);
 hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* init_state,
                             const int32_t* cu_seqlens, void* o, float* final_state,
-                            float* state_ckpt, void* workspace, hipStream_t stream);
+                            float* state_ckpt, float* chunk_states, void* workspace,
+                            hipStream_t stream);
+// Chunk slots of a batch (dense: B * ceil(T/64); varlen: an upper bound that
+// does not read cu_seqlens, T/64 + N).
+int64_t chunk_slot_bound(const kda_desc_t& d, bool varlen);
+
+// Chunkwise backward (kda_chunk_bwd.hip).
+size_t chunk_bwd_workspace_bytes(const kda_desc_t& d);
+hipError_t launch_chunk_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const float* init_state,
+                            const int32_t* cu_seqlens, const void* d_o, const float* d_final,
+                            void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                            float* d_init, void* workspace, hipStream_t stream);
 
 // ShortConv + Swish prologue.  Shapes are validated by the caller.
 struct kda_conv_args {
