@@ -152,6 +152,76 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
   return ok();
 }
 
+namespace {
+// Backward support: the forward's shapes, except fp32 operands at d = 128.
+kda_status_t check_bwd_desc(const kda_desc_t* d) {
+  kda_status_t st = check_chunk_desc(d);
+  if (st != KDA_OK) return st;
+  if (d->dtype == KDA_DTYPE_F32 && d->dk == 128)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_bwd: fp32 operands need dk = dv = 64");
+  return KDA_OK;
+}
+}  // namespace
+
+KDA_EXPORT size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc) {
+  if (check_bwd_desc(desc) != KDA_OK) return 0;
+  return kda::chunk_bwd_workspace_bytes(*desc);
+}
+
+KDA_EXPORT kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, const void* k,
+                                      const void* v, const float* g, const float* beta,
+                                      const float* init_state, const int32_t* cu_seqlens,
+                                      const void* d_o, const float* d_final_state, void* dq,
+                                      void* dk, void* dv, float* dg, float* dbeta,
+                                      float* d_init_state, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  kda_status_t st = check_bwd_desc(desc);
+  if (st != KDA_OK) return st;
+  const kda_desc_t& d = *desc;
+  if (cu_seqlens) {
+    if (d.batch != 1)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "varlen (cu_seqlens != NULL) needs batch == 1");
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  } else if (d.num_seqs != d.batch) {
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dense layout needs num_seqs == batch (%d vs %d)",
+                d.num_seqs, d.batch);
+  }
+  const bool has_tokens = d.seqlen > 0;
+  const void* need[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta};
+  const char* names[] = {"q", "k", "v", "g", "beta", "d_o", "dq", "dk", "dv", "dg", "dbeta"};
+  const uintptr_t align[] = {16, 16, 16, uintptr_t(d.gate_per_head ? 4 : 16), 4, 16,
+                             16, 16, 16, 4, 4};
+  for (int i = 0; i < 11; ++i) {
+    if (has_tokens && !need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (need[i] && !aligned(need[i], align[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i],
+                  (int)align[i]);
+  }
+  const void* opt[] = {init_state, d_final_state, d_init_state, workspace};
+  const char* onames[] = {"init_state", "d_final_state", "d_init_state", "workspace"};
+  const uintptr_t oalign[] = {4, 4, 4, 16};
+  for (int i = 0; i < 4; ++i)
+    if (opt[i] && !aligned(opt[i], oalign[i]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", onames[i],
+                  (int)oalign[i]);
+  // outputs never alias an input
+  const void* ins[] = {q, k, v, g, beta, init_state, d_o, d_final_state};
+  const void* outs[] = {dq, dk, dv, dg, dbeta, d_init_state};
+  for (const void* o : outs)
+    for (const void* in : ins)
+      if (o && o == in) return fail(KDA_ERR_INVALID_ARGUMENT, "gradients must not alias inputs");
+  const size_t need_ws = kda::chunk_bwd_workspace_bytes(d);
+  if (!workspace || workspace_bytes < need_ws)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu%s", need_ws,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  hipError_t e = kda::launch_chunk_bwd(d, q, k, v, g, beta, init_state, cu_seqlens, d_o,
+                                       d_final_state, dq, dk, dv, dg, dbeta, d_init_state,
+                                       workspace, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_bwd launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 KDA_EXPORT kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, const void* k,
                                         const void* v, const float* g, const float* beta,
                                         float* state, void* o, hipStream_t stream) {

@@ -753,8 +753,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   // first row for this lane's column block, len_pend its valid rows.  The
   // store is a buffer store whose bound ends after row len_pend - 1, so rows
   // past a sequence's end are dropped by the hardware, without a branch.
-  // Without o (the forward pass run inside the backward) the bound is 0 and
-  // the hardware drops every store.
+  // Without o (the forward pass run inside the backward) every store is
+  // dropped the same way.
   f32x4_t O[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -764,8 +764,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   auto store_o = [&]() {
     const int nbytes =
         (o_pend != nullptr && len_pend > 0) ? ((len_pend - 1) * H * D + WS) * (int)sizeof(T) : 0;
-    const __amdgpu_buffer_rsrc_t ro =
-        __builtin_amdgcn_make_buffer_rsrc((void*)o_pend, (short)0, nbytes, 0x00020000);
+    // (a bound of 0 on a real address when there is no o: every store dropped)
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        o_pend ? (void*)o_pend : (void*)ws, (short)0, nbytes, 0x00020000);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       BufStore4<T>::store(ro, o_voff + nb * 16 * sizeof(T), scale * O[nb][0], scale * O[nb][1],

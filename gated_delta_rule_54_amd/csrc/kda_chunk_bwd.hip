@@ -1,0 +1,977 @@
+// kda_chunk_bwd.hip -- chunkwise KDA backward (input gradients) for gfx950.
+//
+// Pages cited (by title and section):
+//   [XT] xutianle.me, "Kimi Linear：用 KDA 重写长上下文注意力"
+//
+// [XT §5] has training run the same chunkwise form as prefill but gives no
+// gradient algorithm; what follows is the vector-Jacobian product of the
+// chunk form written out in kda_chunk.hip (same notation, one chunk of n <= 64
+// rows, entering state S, leaving state S', scale folded into dO' = scale dO):
+//
+//   Kp = K^ o e^G   Km = K^ o e^-G   Qp = Q^ o e^G   K~ = K^ o e^(gamma-G)
+//   A  = Diag(beta) tril_-1(Kp Km^T)   T = (I + A)^-1   P = tril(Qp Km^T)
+//   W  = T Diag(beta) (V - Kp S)        O = scale (Qp S + P W)
+//   S' = Diag(e^gamma) S + K~^T W
+//
+// Given dO and dS' = dL/dS', with dW = P^T dO' + K~ dS' (what reaches W) and
+// L = T^T dW (the adjoint of the triangular solve (I + A) W = beta (V - Kp S)):
+//   dV     = Diag(beta) L
+//   dbeta  = rowsum(L o (V - Kp S)) + rowsum(dA o Kp Km^T),  dA = -tril_-1(L W^T)
+//   dQp    = dO' S^T + dP Km,                                dP = tril(dO' W^T)
+//   dKp    = -Diag(beta) L S^T + dB Km,                      dB = Diag(beta) dA
+//   dKm    = dB^T Kp + dP^T Qp
+//   dK~    = W dS'^T
+//   dgamma = colsum(dK~ o K~) + e^gamma o rowsum(S o dS')
+//   dS     = Diag(e^gamma) dS' + Qp^T dO' - Kp^T Diag(beta) L
+//          = M dS' + Z^T dO',   M = Diag(e^gamma) - Wk^T K~,  Z = Qp - P Wk,
+//                               Wk = T Diag(beta) Kp
+// and through the gates and the norm (per element, then per row / column):
+//   dk^ = dKp o e^G + dKm o e^-G + dK~ o e^(gamma-G)      dq^ = dQp o e^G
+//   dG  = k^ o (dKp o e^G - dKm o e^-G - dK~ o e^(gamma-G)) + q^ o dq^
+//         (+ dgamma on the chunk's last row: gamma = G_63, rows past the
+//          sequence's end carry g = 0)
+//   dg_r = sum_(s>=r) dG_s      (the in-chunk prefix sum, reversed)
+//   dk  = r_k (dk^ - (k^ . dk^) k^),  r_k = (|k|^2 + eps)^(-1/2)   (q alike)
+// Gated DeltaNet mode (one gate per token and head) sums dg over channels.
+//
+// Launches, all on the caller's stream:
+//   1. the forward (kda_chunk.hip) with o off and every chunk's entering
+//      state S written to the workspace;
+//   2. kda_bwd_prep, one workgroup per (chunk, head): M and Z^T in operand
+//      order for the reverse pass;
+//   3. kda_bwd_state_pass, one workgroup per (sequence, head, 16 columns of
+//      d_v), sequential over the sequence's chunks from the last: dS' of every
+//      chunk to the workspace, dS of the first to d_init_state;
+//   4. kda_bwd_intra, one workgroup per (chunk, head): every gradient above.
+// The per-chunk kernels recompute the chunk's operands (norms, G, A, T, P)
+// rather than store them.
+//
+// Operand layouts.  A workgroup of D/16 waves gives wave w the 16 columns
+// [16w, 16w+16) of every chunk x d matrix, all 64 rows, in MFMA accumulator
+// layout (lane: column l%16, rows 16t + 4(l/16) + j).  A product whose summed
+// index is the chunk row can take such an accumulator straight as an operand
+// (see acc_frag) when the other operand is read with the same row order
+// (the kpos permutation of kda_chunk_common.h); everything else is staged in
+// LDS in the MFMA type.
+//
+// Domain: the split exponentials e^G, e^-G need every chunk's per-channel
+// decay gamma >= -80 (the forward's fast-path bound); beyond it the backward's
+// results are unspecified (no fault, no hang).  fp32 operands at d = 128 do
+// not fit one workgroup's LDS and are not supported.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
+#include <algorithm>
+
+#include "kda_internal.h"
+#include "kda_chunk_common.h"
+
+namespace kda {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Operand fragments beyond frag_at (k contiguous along rows):
+//   frag_cm       element (m, k) = X[k * ld + m]        (k strided)
+//   frag_rm_perm  element (m, k) = X[m * ld + k], k in kpos order
+//   frag_cm_perm  element (m, k) = X[k * ld + m], k in kpos order
+//   acc_frag      operand whose k index is the row index of four stacked
+//                 16-row accumulator tiles, in kpos order (no data movement)
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_cm(const T* X, int ld, int m0, int ks,
+                                                         int lane);
+template <>
+__device__ __forceinline__ bf16x8_t frag_cm<bf16>(const bf16* X, int ld, int m0, int ks,
+                                                  int lane) {
+  const uint16_t* p =
+      reinterpret_cast<const uint16_t*>(X) + (ks * 32 + 8 * (lane >> 4)) * ld + m0 + (lane & 15);
+  u32x4_t u;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    u[t] = (uint32_t)p[(2 * t) * ld] | ((uint32_t)p[(2 * t + 1) * ld] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+template <>
+__device__ __forceinline__ float frag_cm<float>(const float* X, int ld, int m0, int ks, int lane) {
+  return X[(ks * 4 + (lane >> 4)) * ld + m0 + (lane & 15)];
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_rm_perm(const T* X, int ld, int m0, int ks,
+                                                              int lane);
+template <>
+__device__ __forceinline__ bf16x8_t frag_rm_perm<bf16>(const bf16* X, int ld, int m0, int ks,
+                                                       int lane) {
+  const bf16* row = X + (m0 + (lane & 15)) * ld + ks * 32 + 4 * (lane >> 4);
+  const uint2 a = *reinterpret_cast<const uint2*>(row);
+  const uint2 b = *reinterpret_cast<const uint2*>(row + 16);
+  return __builtin_bit_cast(bf16x8_t, (u32x4_t{a.x, a.y, b.x, b.y}));
+}
+template <>
+__device__ __forceinline__ float frag_rm_perm<float>(const float* X, int ld, int m0, int ks,
+                                                     int lane) {
+  return X[(m0 + (lane & 15)) * ld + 16 * (ks >> 2) + 4 * (lane >> 4) + (ks & 3)];
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_cm_perm(const T* X, int ld, int m0, int ks,
+                                                              int lane);
+template <>
+__device__ __forceinline__ bf16x8_t frag_cm_perm<bf16>(const bf16* X, int ld, int m0, int ks,
+                                                       int lane) {
+  const uint16_t* p =
+      reinterpret_cast<const uint16_t*>(X) + (ks * 32 + 4 * (lane >> 4)) * ld + m0 + (lane & 15);
+  u32x4_t u;
+  u[0] = (uint32_t)p[0] | ((uint32_t)p[ld] << 16);
+  u[1] = (uint32_t)p[2 * ld] | ((uint32_t)p[3 * ld] << 16);
+  u[2] = (uint32_t)p[16 * ld] | ((uint32_t)p[17 * ld] << 16);
+  u[3] = (uint32_t)p[18 * ld] | ((uint32_t)p[19 * ld] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+template <>
+__device__ __forceinline__ float frag_cm_perm<float>(const float* X, int ld, int m0, int ks,
+                                                     int lane) {
+  return X[(16 * (ks >> 2) + 4 * (lane >> 4) + (ks & 3)) * ld + m0 + (lane & 15)];
+}
+
+// Eight (bf16) or one (fp32) fp32 values to an operand fragment.
+__device__ __forceinline__ bf16x8_t to_frag(const float* x, bf16) {
+  const u32x4_t u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ float to_frag(const float* x, float) { return x[0]; }
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag acc_frag(const f32x4_t* tiles, int ks) {
+  if constexpr (sizeof(T) == 2) {
+    const float x[8] = {tiles[2 * ks][0],     tiles[2 * ks][1],     tiles[2 * ks][2],
+                        tiles[2 * ks][3],     tiles[2 * ks + 1][0], tiles[2 * ks + 1][1],
+                        tiles[2 * ks + 1][2], tiles[2 * ks + 1][3]};
+    return to_frag(x, T{});
+  } else {
+    return tiles[ks >> 2][ks & 3];
+  }
+}
+
+// B operand (k = rows of a row-major fp32 matrix X, n = column n) read from
+// memory: element (k, n) = X[k * ld + n], k natural order.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag gfrag_cm(const float* X, int ld, int n, int ks,
+                                                          int lane) {
+  using M = Mma<T>;
+  float x[M::KPL];
+#pragma unroll
+  for (int e = 0; e < M::KPL; ++e) x[e] = X[(int64_t)(ks * M::KSTEP + M::KPL * (lane >> 4) + e) * ld + n];
+  return to_frag(x, T{});
+}
+// The KPL consecutive fp32 values of row m at k-step ks (k contiguous).
+template <typename T>
+__device__ __forceinline__ void grow_vals(const float* X, int ld, int m, int ks, int lane,
+                                          float* x) {
+  using M = Mma<T>;
+  const float* p = X + (int64_t)m * ld + ks * M::KSTEP + M::KPL * (lane >> 4);
+  if constexpr (M::KPL == 8) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    x[0] = p[0];
+  }
+}
+
+// Sum over the 16 lanes of a lane group (the 16 columns of an accumulator).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// LDS of the per-chunk backward kernels (bytes).
+template <typename T, int D>
+struct BwdLds {
+  static constexpr int NW = D / 16, NT = 64 * NW;  // waves (one per 16 columns), threads
+  static constexpr int PAD = 16 / (int)sizeof(T);
+  static constexpr int LDX = D + PAD, LDC = kC + PAD;  // leading dims: C x D, C x C
+  static constexpr int XB = kC * LDX * (int)sizeof(T);
+  static constexpr int CB = kC * LDC * (int)sizeof(T);
+  static constexpr int FB = kC * kTriLd * 4;  // fp32 A or T of the inverse
+  static constexpr int UB = 2 * (XB > FB ? XB : FB);
+  static_assert(CB >= 4096, "the inverse's scratch lives in the dB buffer");
+  // regions: Kp, Km, Qp, K~ (later L); union {A, T fp32} then {W, dO'};
+  // T, P (later dP), dB; small fp32 arrays
+  static constexpr int KP = 0, KM = XB, QP = 2 * XB, KT = 3 * XB, U = 4 * XB;
+  static constexpr int TB = U + UB, PB = TB + CB, DB = PB + CB;
+  static constexpr int SM = DB + CB;
+  // small: beta, rk, rq, x0, x1, x2 [kC] and red [2][NW][kC]
+  static constexpr int BYTES = SM + (6 * kC + 2 * NW * kC) * 4;
+  static_assert(BYTES <= 160 * 1024, "per-chunk backward LDS exceeds a CU");
+};
+
+template <typename T, int D>
+struct BwdSmem {
+  using L = BwdLds<T, D>;
+  T *kp, *km, *qp, *kt, *tb, *pb, *db, *wb, *dob;
+  float *sA, *sT, *scratch, *beta, *rk, *rq, *x0, *x1, *x2, *red;
+  __device__ explicit BwdSmem(char* s) {
+    kp = reinterpret_cast<T*>(s + L::KP);
+    km = reinterpret_cast<T*>(s + L::KM);
+    qp = reinterpret_cast<T*>(s + L::QP);
+    kt = reinterpret_cast<T*>(s + L::KT);
+    sA = reinterpret_cast<float*>(s + L::U);
+    sT = sA + kC * kTriLd;
+    wb = reinterpret_cast<T*>(s + L::U);
+    dob = reinterpret_cast<T*>(s + L::U + L::XB);
+    tb = reinterpret_cast<T*>(s + L::TB);
+    pb = reinterpret_cast<T*>(s + L::PB);
+    db = reinterpret_cast<T*>(s + L::DB);
+    scratch = reinterpret_cast<float*>(s + L::DB);
+    beta = reinterpret_cast<float*>(s + L::SM);
+    rk = beta + kC;
+    rq = rk + kC;
+    x0 = rq + kC;
+    x1 = x0 + kC;
+    x2 = x1 + kC;
+    red = x2 + kC;
+  }
+};
+
+// Registers the prologue leaves to its kernel, in accumulator layout (wave w:
+// column c = 16w + l%16, rows 16t + 4(l/16) + j).
+struct BwdRegs {
+  float G[4][4];   // in-chunk prefix sum of g
+  float kh[4][4];  // k^ (0 past the chunk's end)
+  float qh[4][4];  // q^
+  float gam;       // gamma of this lane's column
+};
+
+// Prologue shared by the per-chunk backward kernels: loads, q/k norms, G,
+// the four gated operands in LDS, A and P, T = (I + A)^-1 (times Diag(beta)
+// when TBETA) in the MFMA type.  Bm receives this wave's tiles of Kp Km^T
+// (tile p = wave + NW * tt: rows 16(p/4), columns 16(p%4)).
+template <typename T, int D, bool GS, bool TBETA>
+__device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
+                                             const float* __restrict__ g,
+                                             const float* __restrict__ beta, const ChunkLoc& loc,
+                                             int H, int h, int qk_l2norm, BwdSmem<T, D>& sm,
+                                             BwdRegs& R, f32x4_t* Bm) {
+  using L = BwdLds<T, D>;
+  using M = Mma<T>;
+  constexpr int NW = L::NW, NT = L::NT, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+  const int c = 16 * wave + (lane & 15);
+  float gr[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * t + 4 * grp + j;
+      const int64_t row = (loc.tok0 + min(r, loc.len - 1)) * H + h;
+      const bool ok = r < loc.len;
+      R.kh[t][j] = ok ? ld_f(k + row * D + c) : 0.f;
+      R.qh[t][j] = ok ? ld_f(q + row * D + c) : 0.f;
+      gr[t][j] = ok ? (GS ? g[row] : g[row * D + c]) : 0.f;
+    }
+  if (tid < kC) sm.beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
+  // row norms: over this wave's 16 columns, then over the waves
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sk = sum16(R.kh[t][j] * R.kh[t][j]);
+      const float sq = sum16(R.qh[t][j] * R.qh[t][j]);
+      if ((lane & 15) == 0) {
+        const int r = 16 * t + 4 * grp + j;
+        sm.red[wave * kC + r] = sk;
+        sm.red[(NW + wave) * kC + r] = sq;
+      }
+    }
+  __syncthreads();
+  if (tid < kC) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      sk += sm.red[w * kC + tid];
+      sq += sm.red[(NW + w) * kC + tid];
+    }
+    sm.rk[tid] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
+    sm.rq[tid] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
+  }
+  // G: prefix sum down the 64 rows of this lane's column -- within the
+  // lane's 4 rows, then across the 4 lane groups, then across the tiles
+  float carry = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float loc4[4];
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { run += gr[t][j]; loc4[j] = run; }
+    float x = run;
+    float y = __shfl_up(x, 16);
+    if (grp >= 1) x += y;
+    y = __shfl_up(x, 32);
+    if (grp >= 2) x += y;
+    const float excl = x - run;
+    const float total = __shfl(x, 48 + (lane & 15));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.G[t][j] = carry + excl + loc4[j];
+    carry += total;
+  }
+  R.gam = carry;
+  __syncthreads();
+  // gated operands
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * t + 4 * grp + j;
+      R.kh[t][j] *= sm.rk[r];
+      R.qh[t][j] *= sm.rq[r];
+      const float G = R.G[t][j];
+      const float eg = __expf(G), en = __expf(-G), et = __expf(R.gam - G);
+      st_f(sm.kp + r * LDX + c, R.kh[t][j] * eg);
+      st_f(sm.km + r * LDX + c, R.kh[t][j] * en);
+      st_f(sm.qp + r * LDX + c, R.qh[t][j] * eg);
+      st_f(sm.kt + r * LDX + c, R.kh[t][j] * et);
+    }
+  __syncthreads();
+  // A = Diag(beta) tril_-1(Kp Km^T) (fp32) and P = tril(Qp Km^T)
+#pragma unroll
+  for (int tt = 0; tt < NTW; ++tt) {
+    const int p = wave + NW * tt, rb = p >> 2, ib = p & 3;
+    f32x4_t ab = {0.f, 0.f, 0.f, 0.f}, ap = ab;
+#pragma unroll
+    for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+      const auto bk = frag_at<T>(sm.km, LDX, 16 * ib, ks, lane);
+      ab = M::mma(frag_at<T>(sm.kp, LDX, 16 * rb, ks, lane), bk, ab);
+      ap = M::mma(frag_at<T>(sm.qp, LDX, 16 * rb, ks, lane), bk, ap);
+    }
+    Bm[tt] = ab;
+    const int i = 16 * ib + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * rb + 4 * grp + j;
+      sm.sA[r * kTriLd + i] = i < r ? sm.beta[r] * ab[j] : 0.f;
+      st_f(sm.pb + r * LDC + i, i <= r ? ap[j] : 0.f);
+    }
+  }
+  __syncthreads();
+  tri_inv64(sm.sA, sm.sT, sm.scratch, wave, lane);
+  for (int e = tid; e < kC * kC; e += NT) {
+    const int r = e >> 6, i = e & 63;
+    const float t = i <= r ? sm.sT[r * kTriLd + i] : 0.f;
+    st_f(sm.tb + r * LDC + i, TBETA ? t * sm.beta[i] : t);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Reverse-pass record of one (head, chunk slot): M and Z^T in operand order
+// (see fnat), rows = key channel c, k = c' (M) or chunk row r (Z^T).
+template <typename T, int D>
+struct BRec {
+  static constexpr int64_t MF = 0;
+  static constexpr int64_t ZF = MF + (int64_t)D * D;
+  static constexpr int64_t END = ZF + (int64_t)D * kC;
+  static constexpr int64_t BYTES = (END * (int64_t)sizeof(T) + 255) / 256 * 256;
+};
+
+template <typename T, int D, bool GS>
+__global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_prep(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, ChunkGeom gm, int H, int64_t nslot, int qk_l2norm,
+    char* __restrict__ brec) {
+  using L = BwdLds<T, D>;
+  using M = Mma<T>;
+  using RC = BRec<T, D>;
+  constexpr int NW = L::NW, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
+  constexpr int KC = kC / M::KSTEP, KD = D / M::KSTEP;
+  extern __shared__ __align__(16) char smem[];
+  const int h = blockIdx.x;
+  const int64_t slot = blockIdx.y;
+  ChunkLoc loc;
+  if (!locate(gm, slot, loc)) return;
+  BwdSmem<T, D> sm(smem);
+  BwdRegs R;
+  f32x4_t Bm[NTW];
+  bwd_prologue<T, D, GS, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
+  const int c = 16 * wave + (lane & 15);
+  T* rec = reinterpret_cast<T*>(brec + ((int64_t)h * nslot + slot) * RC::BYTES);
+
+  // Wk = T Diag(beta) Kp for this wave's columns, B = Kp from registers
+  f32x4_t kpa[4], wk[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kpa[t][j] = R.kh[t][j] * __expf(R.G[t][j]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    wk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+      wk[t] = M::mma(frag_rm_perm<T>(sm.tb, LDC, 16 * t, ks, lane), acc_frag<T>(kpa, ks), wk[t]);
+  }
+  // Z = Qp - P Wk, stored as Z^T (rows c, k = r): each lane's 4 rows are 4
+  // consecutive k
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4_t pw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+      pw = M::mma(frag_rm_perm<T>(sm.pb, LDC, 16 * t, ks, lane), acc_frag<T>(wk, ks), pw);
+    float z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = R.qh[t][j] * __expf(R.G[t][j]) - pw[j];
+    st_fnat4(rec + RC::ZF, KC, c, 16 * t + 4 * grp, z[0], z[1], z[2], z[3]);
+  }
+  // M^T tiles (rows c', column c) = Diag(e^gamma) - K~^T Wk, stored as M
+  // (rows c, k = c')
+  const float egam = __expf(R.gam);
+#pragma unroll
+  for (int cb = 0; cb < NW; ++cb) {
+    f32x4_t mt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+      mt = M::mma(frag_cm_perm<T>(sm.kt, LDX, 16 * cb, ks, lane), acc_frag<T>(wk, ks), mt);
+    float m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c2 = 16 * cb + 4 * grp + j;
+      m[j] = (c2 == c ? egam : 0.f) - mt[j];
+    }
+    st_fnat4(rec + RC::MF, KD, c, 16 * cb + 4 * grp, m[0], m[1], m[2], m[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state pass: dS = M dS' + Z^T dO' chunk by chunk from the last, one
+// workgroup per (sequence, head, 16 columns of d_v).  Wave w owns rows
+// [16 CBW w, 16 CBW (w+1)) of dS in accumulators; dS' crosses LDS once per
+// chunk (double-buffered, so one barrier per chunk).  Each chunk's dS' (the
+// gradient of the state leaving it) goes to dstates for kda_bwd_intra.
+constexpr int kBwdSliceW = 16;
+constexpr int kBwdPassThreads = 256;
+
+template <typename T, int D>
+struct BwdPassFrags {
+  using M = Mma<T>;
+  static constexpr int CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
+  typename M::frag mf[CBW][KD], zf[CBW][KC], of[KC];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
+    const char* __restrict__ brec, int64_t nslot, ChunkGeom gm, int H, int NH, int nslice,
+    const T* __restrict__ d_o, const float* __restrict__ dfinal, float* __restrict__ dstates,
+    float* __restrict__ dinit, float scale) {
+  using M = Mma<T>;
+  using RC = BRec<T, D>;
+  using F = BwdPassFrags<T, D>;
+  constexpr int CBW = F::CBW, KD = F::KD, KC = F::KC, LDS_S = D + 8;
+  __shared__ __align__(16) T sD[2][kBwdSliceW * LDS_S];
+  const int id = blockIdx.x;
+  const int nh = (id & 7) + 8 * (id / (8 * nslice));
+  const int slice = (id >> 3) % nslice;
+  if (nh >= NH) return;
+  const int seq = nh / H, h = nh % H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
+  const int n0 = slice * kBwdSliceW, n = n0 + (lane & 15);
+  const int64_t sidx = (int64_t)nh * D * D;
+  const SeqSpan sp = seq_span(gm, seq);
+  if (sp.c0 == sp.c1) {  // empty sequence: d_init = d_final
+    if (dinit == nullptr) return;
+    for (int e = threadIdx.x; e < D * kBwdSliceW; e += kBwdPassThreads) {
+      const int64_t idx = sidx + (int64_t)(e / kBwdSliceW) * D + n0 + e % kBwdSliceW;
+      dinit[idx] = dfinal ? dfinal[idx] : 0.f;
+    }
+    return;
+  }
+  f32x4_t dS[CBW];
+#pragma unroll
+  for (int i = 0; i < CBW; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = (wave * CBW + i) * 16 + 4 * grp + j;
+      dS[i][j] = dfinal ? dfinal[sidx + (int64_t)c * D + n] : 0.f;
+    }
+  const int nch = (int)(sp.c1 - sp.c0);
+  const int len_last = (int)(sp.ntok - (int64_t)(nch - 1) * kC);
+
+  auto load = [&](F& f, int ci) {
+    const T* rec = reinterpret_cast<const T*>(brec + ((int64_t)h * nslot + sp.c0 + ci) * RC::BYTES);
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks)
+        f.mf[i][ks] = M::load(rec + RC::MF + (((wave * CBW + i) * KD + ks) * 64 + lane) * M::KPL);
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks)
+        f.zf[i][ks] = M::load(rec + RC::ZF + (((wave * CBW + i) * KC + ks) * 64 + lane) * M::KPL);
+    }
+    // dO' rows in kpos order (the k index of Z^T)
+    const int len = ci == nch - 1 ? len_last : kC;
+    const T* ob = d_o + ((sp.tok0 + (int64_t)ci * kC) * H + h) * D + n;
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) {
+      float x[M::KPL];
+#pragma unroll
+      for (int e = 0; e < M::KPL; ++e) {
+        int r;
+        if constexpr (M::KPL == 8)
+          r = ks * 32 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+        else
+          r = 16 * (ks >> 2) + 4 * grp + (ks & 3);
+        x[e] = r < len ? scale * ld_f(ob + (int64_t)r * H * D) : 0.f;
+      }
+      f.of[ks] = to_frag(x, T{});
+    }
+  };
+  auto step = [&](const F& f, int ci, int buf) {
+    const int64_t slot = sp.c0 + ci;
+    float* dst = dstates + (slot * H + h) * (int64_t)D * D + n;
+    T* sb = sD[buf];
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+      const int c4 = (wave * CBW + i) * 16 + 4 * grp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[(int64_t)(c4 + j) * D] = dS[i][j];
+      st_perm4(sb + (lane & 15) * LDS_S, c4, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
+    }
+    __syncthreads();
+    typename M::frag bfr[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) bfr[ks] = frag_at<T>(sb, LDS_S, 0, ks, lane);
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) acc = M::mma(f.zf[i][ks], f.of[ks], acc);
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) acc = M::mma(f.mf[i][ks], bfr[ks], acc);
+      dS[i] = acc;
+    }
+    // No second barrier: the next chunk writes the other buffer, and this
+    // buffer is rewritten only after the next chunk's barrier, which every
+    // wave reaches after its reads of this one.
+  };
+  // two register sets, each chunk's record prefetched one chunk ahead
+  F fa, fb;
+  load(fa, nch - 1);
+  int s = 0;
+  for (; s + 2 <= nch; s += 2) {
+    const int ci = nch - 1 - s;
+    load(fb, ci - 1);
+    step(fa, ci, 0);
+    load(fa, max(ci - 2, 0));
+    step(fb, ci - 1, 1);
+  }
+  if (s < nch) step(fa, nch - 1 - s, 0);
+  if (dinit != nullptr) {
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = (wave * CBW + i) * 16 + 4 * grp + j;
+        dinit[sidx + (int64_t)c * D + n] = dS[i][j];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Every gradient of one (chunk, head), given the entering state S and the
+// gradient dS' of the leaving state.
+template <typename T, int D, bool GS>
+__global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ d_o,
+    const float* __restrict__ states, const float* __restrict__ dstates, ChunkGeom gm, int H,
+    int qk_l2norm, float scale, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
+  using L = BwdLds<T, D>;
+  using M = Mma<T>;
+  constexpr int NW = L::NW, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
+  constexpr int KC = kC / M::KSTEP, KD = D / M::KSTEP, KPL = M::KPL;
+  extern __shared__ __align__(16) char smem[];
+  const int h = blockIdx.x;
+  const int64_t slot = blockIdx.y;
+  ChunkLoc loc;
+  if (!locate(gm, slot, loc)) return;
+  BwdSmem<T, D> sm(smem);
+  BwdRegs R;
+  f32x4_t Bm[NTW];
+  bwd_prologue<T, D, GS, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+  const int c = 16 * wave + (lane & 15);  // this lane's column (d_k or d_v)
+  const float* S = states + (slot * H + h) * (int64_t)D * D;
+  const float* dS = dstates + (slot * H + h) * (int64_t)D * D;
+  auto tok = [&](int r) { return (loc.tok0 + r) * H + h; };
+
+  // ---- value side: columns n = c --------------------------------------------
+  // Kp S, then R = Diag(beta)(V - Kp S) and W = T R
+  f32x4_t vmk[4], acc[4], w[4];
+  {
+    typename M::frag sb[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) sb[ks] = gfrag_cm<T>(S, D, c, ks, lane);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) a = M::mma(frag_at<T>(sm.kp, LDX, 16 * t, ks, lane), sb[ks], a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * t + 4 * grp + j;
+        const float vv = r < loc.len ? ld_f(v + tok(r) * D + c) : 0.f;
+        vmk[t][j] = vv - a[j];
+        acc[t][j] = sm.beta[r] * vmk[t][j];
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    w[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+      w[t] = M::mma(frag_rm_perm<T>(sm.tb, LDC, 16 * t, ks, lane), acc_frag<T>(acc, ks), w[t]);
+  }
+  // dO' (kept for P^T dO') ; W and dO' into LDS
+  f32x4_t dov[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * t + 4 * grp + j;
+      dov[t][j] = r < loc.len ? scale * ld_f(d_o + tok(r) * D + c) : 0.f;
+      st_f(sm.wb + r * LDX + c, w[t][j]);
+      st_f(sm.dob + r * LDX + c, dov[t][j]);
+    }
+  // dW = P^T dO' + K~ dS'
+  {
+    typename M::frag dsb[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) dsb[ks] = gfrag_cm<T>(dS, D, c, ks, lane);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks)
+        a = M::mma(frag_cm_perm<T>(sm.pb, LDC, 16 * t, ks, lane), acc_frag<T>(dov, ks), a);
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) a = M::mma(frag_at<T>(sm.kt, LDX, 16 * t, ks, lane), dsb[ks], a);
+      acc[t] = a;
+    }
+  }
+  // L = T^T dW; dV = Diag(beta) L; dbeta, first part: rowsum(L o (V - Kp S))
+  f32x4_t lam[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    lam[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+      lam[t] = M::mma(frag_cm_perm<T>(sm.tb, LDC, 16 * t, ks, lane), acc_frag<T>(acc, ks), lam[t]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * t + 4 * grp + j;
+      if (r < loc.len) st_f(dv + tok(r) * D + c, sm.beta[r] * lam[t][j]);
+      const float part = sum16(lam[t][j] * vmk[t][j]);
+      if ((lane & 15) == 0) sm.red[wave * kC + r] = part;
+    }
+  }
+  __syncthreads();  // every read of K~ is done: its region becomes L
+  T* lb = sm.kt;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st_f(lb + (16 * t + 4 * grp + j) * LDX + c, lam[t][j]);
+  __syncthreads();
+
+  // ---- chunk x chunk: dP = tril(dO' W^T), dA = -tril_-1(L W^T), dB ------------
+#pragma unroll
+  for (int tt = 0; tt < NTW; ++tt) {
+    const int p = wave + NW * tt, rb = p >> 2, ib = p & 3;
+    f32x4_t ap = {0.f, 0.f, 0.f, 0.f}, aa = ap;
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      const auto bw = frag_at<T>(sm.wb, LDX, 16 * ib, ks, lane);
+      ap = M::mma(frag_at<T>(sm.dob, LDX, 16 * rb, ks, lane), bw, ap);
+      aa = M::mma(frag_at<T>(lb, LDX, 16 * rb, ks, lane), bw, aa);
+    }
+    const int i = 16 * ib + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * rb + 4 * grp + j;
+      const float da = i < r ? -aa[j] : 0.f;
+      st_f(sm.pb + r * LDC + i, i <= r ? ap[j] : 0.f);
+      st_f(sm.db + r * LDC + i, sm.beta[r] * da);
+      const float part = sum16(da * Bm[tt][j]);
+      if ((lane & 15) == 0) sm.red[(NW + ib) * kC + r] = part;  // one tile per (ib, r)
+    }
+  }
+  __syncthreads();
+  if (tid < kC) {
+    float b = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) b += sm.red[w2 * kC + tid];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) b += sm.red[(NW + ib) * kC + tid];
+    sm.x0[tid] = b;
+  }
+
+  // ---- key side: columns c --------------------------------------------------
+  float rs = 0.f;  // rowsum(S o dS') of row c
+  typename M::frag st[KD], dst[KD];
+#pragma unroll
+  for (int ks = 0; ks < KD; ++ks) {
+    float xs[KPL], xd[KPL];
+    grow_vals<T>(S, D, c, ks, lane, xs);
+    grow_vals<T>(dS, D, c, ks, lane, xd);
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) rs += xs[e] * xd[e];
+    st[ks] = to_frag(xs, T{});
+    dst[ks] = to_frag(xd, T{});
+  }
+  rs += __shfl_xor(rs, 16);
+  rs += __shfl_xor(rs, 32);
+  f32x4_t dqp[4], dkp[4], dkm[4], dkt[4];
+  {
+    typename M::frag kmc[KC], kpc[KC], qpc[KC];
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) {
+      kmc[ks] = frag_cm<T>(sm.km, LDX, 16 * wave, ks, lane);
+      kpc[ks] = frag_cm<T>(sm.kp, LDX, 16 * wave, ks, lane);
+      qpc[ks] = frag_cm<T>(sm.qp, LDX, 16 * wave, ks, lane);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f}, x = a, b = a, m = a, kt = a;
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) {
+        a = M::mma(frag_at<T>(sm.dob, LDX, 16 * t, ks, lane), st[ks], a);   // dO' S^T
+        x = M::mma(frag_at<T>(lb, LDX, 16 * t, ks, lane), st[ks], x);       // L S^T
+        kt = M::mma(frag_at<T>(sm.wb, LDX, 16 * t, ks, lane), dst[ks], kt); // W dS'^T
+      }
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {
+        a = M::mma(frag_at<T>(sm.pb, LDC, 16 * t, ks, lane), kmc[ks], a);   // dP Km
+        b = M::mma(frag_at<T>(sm.db, LDC, 16 * t, ks, lane), kmc[ks], b);   // dB Km
+        m = M::mma(frag_cm<T>(sm.db, LDC, 16 * t, ks, lane), kpc[ks], m);   // dB^T Kp
+        m = M::mma(frag_cm<T>(sm.pb, LDC, 16 * t, ks, lane), qpc[ks], m);   // dP^T Qp
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] -= sm.beta[16 * t + 4 * grp + j] * x[j];
+      dqp[t] = a; dkp[t] = b; dkm[t] = m; dkt[t] = kt;
+    }
+  }
+
+  // ---- gates, prefix-sum reversal, norms -------------------------------------
+  float dkh[4][4], dqh[4][4], dG[4][4];
+  float dgam = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float G = R.G[t][j];
+      const float a = dkp[t][j] * __expf(G), b = dkm[t][j] * __expf(-G);
+      const float e = dkt[t][j] * __expf(R.gam - G);
+      dkh[t][j] = a + b + e;
+      dqh[t][j] = dqp[t][j] * __expf(G);
+      dG[t][j] = R.kh[t][j] * (a - b - e) + R.qh[t][j] * dqh[t][j];
+      dgam += R.kh[t][j] * e;
+    }
+  dgam += __shfl_xor(dgam, 16);
+  dgam += __shfl_xor(dgam, 32);
+  dgam += __expf(R.gam) * rs;
+  if (grp == 3) dG[3][3] += dgam;  // gamma = G of row 63
+  // dg_r = sum_(s >= r) dG_s: within the lane's 4 rows, across the lane
+  // groups, then across the tiles from the last
+  float dgo[4][4];
+  {
+    float carry = 0.f;
+#pragma unroll
+    for (int t = 3; t >= 0; --t) {
+      float suf[4];
+      float run = 0.f;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) { run += dG[t][j]; suf[j] = run; }
+      float x = run;
+      float y = __shfl_down(x, 16);
+      if (grp <= 2) x += y;
+      y = __shfl_down(x, 32);
+      if (grp <= 1) x += y;
+      const float excl = x - run;
+      const float total = __shfl(x, lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dgo[t][j] = carry + excl + suf[j];
+      carry += total;
+    }
+  }
+  // row dots k^ . dk^, q^ . dq^ (and, per head, the row's dg) over all columns
+  __syncthreads();  // red is free again (x0 was formed from it above)
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * t + 4 * grp + j;
+      const float a = sum16(R.kh[t][j] * dkh[t][j]);
+      const float b = sum16(R.qh[t][j] * dqh[t][j]);
+      if ((lane & 15) == 0) {
+        sm.red[wave * kC + r] = a;
+        sm.red[(NW + wave) * kC + r] = b;
+      }
+    }
+  __syncthreads();
+  if (tid < kC) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      a += sm.red[w2 * kC + tid];
+      b += sm.red[(NW + w2) * kC + tid];
+    }
+    sm.x1[tid] = a;
+    sm.x2[tid] = b;
+    if (tid < loc.len) dbeta[tok(tid)] = sm.x0[tid];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * t + 4 * grp + j;
+      float gk = dkh[t][j], gq = dqh[t][j];
+      if (qk_l2norm) {
+        gk = sm.rk[r] * (gk - sm.x1[r] * R.kh[t][j]);
+        gq = sm.rq[r] * (gq - sm.x2[r] * R.qh[t][j]);
+      }
+      if (r < loc.len) {
+        st_f(dk + tok(r) * D + c, gk);
+        st_f(dq + tok(r) * D + c, gq);
+        if (!GS) dg[tok(r) * D + c] = dgo[t][j];
+      }
+    }
+  if constexpr (GS) {
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = sum16(dgo[t][j]);
+        if ((lane & 15) == 0) sm.red[wave * kC + 16 * t + 4 * grp + j] = a;
+      }
+    __syncthreads();
+    if (tid < loc.len) {
+      float a = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) a += sm.red[w2 * kC + tid];
+      dg[tok(tid)] = a;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Workspace: [forward workspace | S per slot | dS' per slot | M, Z^T records |
+// chunk map].  Slots are sized for the larger of the dense and varlen bounds.
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+struct BwdPlan {
+  int64_t slots, fwd, states, recs, map, total;
+};
+
+BwdPlan bwd_plan(const kda_desc_t& d) {
+  BwdPlan p{};
+  p.slots = std::max(chunk_slot_bound(d, true), chunk_slot_bound(d, false));
+  kda_desc_t df = d;
+  df.ckpt_every = 0;
+  p.fwd = align256((int64_t)chunk_workspace_bytes(df));
+  p.states = align256(p.slots * d.heads * (int64_t)d.dk * d.dv * 4);
+  const int64_t rb = d.dtype == KDA_DTYPE_BF16
+                         ? (d.dk == 128 ? BRec<bf16, 128>::BYTES : BRec<bf16, 64>::BYTES)
+                         : (d.dk == 128 ? BRec<float, 128>::BYTES : BRec<float, 64>::BYTES);
+  p.recs = p.slots * d.heads * rb;
+  p.map = 2 * align256(((int64_t)d.num_seqs + 1) * 4);
+  p.total = p.fwd + 2 * p.states + p.recs + p.map;
+  return p;
+}
+
+template <typename T, int D>
+hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* init_state, const int32_t* cu,
+                   const void* d_o, const float* d_final, void* dq, void* dk, void* dv,
+                   float* dg, float* dbeta, float* d_init, char* ws, hipStream_t stream) {
+  using L = BwdLds<T, D>;
+  const BwdPlan p = bwd_plan(d);
+  const bool varlen = cu != nullptr;
+  const int H = d.heads, NH = d.num_seqs * d.heads;
+  float* states = reinterpret_cast<float*>(ws + p.fwd);
+  float* dstates = reinterpret_cast<float*>(ws + p.fwd + p.states);
+  char* recs = ws + p.fwd + 2 * p.states;
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.fwd + 2 * p.states + p.recs);
+  int32_t* cu_s = chunk_off + (p.map / 2) / 4;
+  const int64_t nslot = chunk_slot_bound(d, varlen);
+
+  kda_desc_t df = d;
+  df.ckpt_every = 0;
+  hipError_t e = launch_chunk_fwd(df, q, k, v, g, beta, init_state, cu, nullptr, nullptr,
+                                  nullptr, states, ws, stream);
+  if (e != hipSuccess) return e;
+  ChunkGeom gm{nullptr, nullptr, d.seqlen, (d.seqlen + kC - 1) / kC, d.num_seqs};
+  if (varlen) {
+    hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, stream, cu, d.num_seqs,
+                       d.seqlen, cu_s, chunk_off);
+    gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
+  }
+  static bool attr_set = false;
+  if (!attr_set) {
+    for (const void* fn : {(const void*)kda_bwd_prep<T, D, false>,
+                           (const void*)kda_bwd_prep<T, D, true>,
+                           (const void*)kda_bwd_intra<T, D, false>,
+                           (const void*)kda_bwd_intra<T, D, true>}) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+      if (e != hipSuccess) return e;
+    }
+    attr_set = true;
+  }
+  if (nslot > 0) {
+    auto prep = d.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
+    hipLaunchKernelGGL(prep, dim3(H, (unsigned)nslot), dim3(L::NT), L::BYTES, stream,
+                       (const T*)q, (const T*)k, g, beta, gm, H, nslot, d.qk_l2norm, recs);
+  }
+  const int nslice = D / kBwdSliceW;
+  const int nhpad = (NH + 7) / 8 * 8;
+  hipLaunchKernelGGL((kda_bwd_state_pass<T, D>), dim3(nhpad * nslice), dim3(kBwdPassThreads), 0,
+                     stream, recs, nslot, gm, H, NH, nslice, (const T*)d_o, d_final, dstates,
+                     d_init, d.scale);
+  if (nslot > 0) {
+    auto intra = d.gate_per_head ? kda_bwd_intra<T, D, true> : kda_bwd_intra<T, D, false>;
+    hipLaunchKernelGGL(intra, dim3(H, (unsigned)nslot), dim3(L::NT), L::BYTES, stream,
+                       (const T*)q, (const T*)k, (const T*)v, g, beta, (const T*)d_o, states,
+                       dstates, gm, H, d.qk_l2norm, d.scale, (T*)dq, (T*)dk, (T*)dv, dg, dbeta);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace_bytes(const kda_desc_t& d) { return (size_t)bwd_plan(d).total; }
+
+hipError_t launch_chunk_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const float* init_state,
+                            const int32_t* cu_seqlens, const void* d_o, const float* d_final,
+                            void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                            float* d_init, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  if (d.dtype == KDA_DTYPE_BF16) {
+    if (d.dk == 128)
+      return run_bwd<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, d_o, d_final, dq,
+                                dk, dv, dg, dbeta, d_init, ws, stream);
+    return run_bwd<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, d_o, d_final, dq, dk,
+                             dv, dg, dbeta, d_init, ws, stream);
+  }
+  if (d.dk == 64)
+    return run_bwd<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, d_o, d_final, dq, dk,
+                              dv, dg, dbeta, d_init, ws, stream);
+  return hipErrorInvalidValue;  // fp32 at d = 128: rejected by the caller
+}
+
+}  // namespace kda

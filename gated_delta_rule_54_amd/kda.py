@@ -28,7 +28,8 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
 # Names every build of the library must export (the declarations of kda.h).
-EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_decode_step",
+EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_bwd_workspace_bytes",
+            "kda_chunk_bwd", "kda_decode_step",
             "kda_output_gate_norm", "kda_short_conv_swish", "kda_status_string",
             "kda_last_error", "kda_abi_version")
 
@@ -76,6 +77,10 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [dp]
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 16 + [sz, vp]
+    lib.kda_chunk_bwd.restype = i32
     lib.kda_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_output_gate_norm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, ctypes.c_float,
@@ -195,6 +200,61 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
                            _stream_handle(stream, dev))
     _check(lib, st, "kda_chunk_fwd")
     return out, final_state, state_ckpt
+
+
+def chunk_bwd_workspace_bytes(desc: KdaDesc) -> int:
+    """Workspace bytes kda_chunk_bwd needs for `desc` (0 if unsupported)."""
+    return int(load_library().kda_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens=None, *,
+                  qk_l2norm=True, scale=1.0, want_dinit=True, workspace=None, stream=None):
+    """Gradients of the chunkwise KDA prefill through the C ABI.
+
+    Inputs as kda_chunk_fwd, plus do: [B, T, H, dv] (q's dtype), the gradient
+    of o, and dfinal: [N, H, dk, dv] fp32 or None (zero), the gradient of the
+    final state.  Returns (dq, dk, dv, dg, dbeta, dinit): dq, dk, dv in q's
+    dtype, dg fp32 shaped like g, dbeta [B, T, H] fp32, dinit [N, H, dk, dv]
+    fp32 (None unless want_dinit).
+    """
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    for t, name, shape in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)),
+                           (v, "v", (B, T, H, dv)), (do, "do", (B, T, H, dv))):
+        _need(t, name, dt, shape)
+    per_head = g.dim() == 3
+    _need(g, "g", torch.float32, (B, T, H) if per_head else (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    for t, name in ((init_state, "init_state"), (dfinal, "dfinal")):
+        if t is not None:
+            _need(t, name, torch.float32, (N, H, dk, dv))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    dev = q.device
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    db = torch.empty_like(beta)
+    dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dinit else None
+    desc = make_desc(batch=B, num_seqs=N, seqlen=T, heads=H, dk=dk, dv=dv, dtype=dt,
+                     qk_l2norm=qk_l2norm, scale=scale, gate_per_head=per_head)
+    ws_bytes = int(lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+    if ws_bytes == 0:
+        _check(lib, KDA_ERR_UNSUPPORTED if lib.kda_last_error() else KDA_ERR_INVALID_ARGUMENT,
+               "kda_chunk_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(init_state), _ptr(cu_seqlens), _ptr(do), _ptr(dfinal), _ptr(dq),
+                           _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dinit),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream, dev))
+    _check(lib, st, "kda_chunk_bwd")
+    return dq, dkk, dvv, dg, db, dinit
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, out=None,

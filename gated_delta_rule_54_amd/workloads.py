@@ -138,6 +138,16 @@ def prefill_inputs(*, batch: int, seqlen: int, heads: int, dk: int, dv: int,
     return dict(q=q, k=k, v=v, g=g, beta=beta, init_state=s0, cu_seqlens=cu)
 
 
+def upstream_grads(*, batch: int, seqlen: int, heads: int, dk: int, dv: int, num_seqs: int,
+                   dtype: torch.dtype, device, seed: int, final: bool = True) -> dict:
+    """Upstream gradients for the backward: do ~ N(0,1) [B, T, H, dv] in the
+    operand dtype and d_final ~ N(0,1) [N, H, dk, dv] fp32 (None unless final)."""
+    gen = make_generator(seed, device)
+    do = _randn((batch, seqlen, heads, dv), gen, device).to(dtype)
+    dfin = _randn((num_seqs, heads, dk, dv), gen, device) if final else None
+    return dict(do=do, dfinal=dfin)
+
+
 def decode_step_inputs(*, num_seqs: int, heads: int, dk: int, dv: int, dtype: torch.dtype,
                        gen: torch.Generator, device, gate_per_head: bool = False) -> dict:
     """One decode step's fresh q, k, v, g, beta ([N, H, d] / [N, H]); g is

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -131,6 +131,44 @@ kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
                            const void* v, const float* g, const float* beta,
                            const float* init_state, const int32_t* cu_seqlens, void* o,
                            float* final_state, float* state_ckpt, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace kda_chunk_bwd needs for this descriptor (an upper
+ * bound that does not read cu_seqlens); 0 for an invalid or unsupported
+ * descriptor.  It holds a forward workspace plus, per chunk slot and head,
+ * the entering state and its gradient (2 x dk x dv x 4 bytes) and the
+ * reverse pass's operands ((dk + 64) x dk elements of dtype). */
+size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
+
+/* Gradients of kda_chunk_fwd (training).  [XT §5: training runs the
+ * chunkwise form; the pages give no gradient algorithm.  What is computed is
+ * the exact vector-Jacobian product of the operator's map
+ * (q, k, v, g, beta, init_state) -> (o, final_state) with the upstream
+ * gradients (d_o, d_final_state), formed chunkwise: a forward pass that keeps
+ * every chunk's entering state, a reverse pass over the chunks for the state
+ * gradients, then every chunk's input gradients in parallel.]
+ *   q, k, v, g, beta, init_state, cu_seqlens   as kda_chunk_fwd (the same
+ *              values the forward ran on; desc->ckpt_every is ignored)
+ *   d_o        [B, T, H, dv]  dtype, gradient of o
+ *   d_final_state [N, H, dk, dv] fp32 or NULL (zero)
+ *   dq, dk     [B, T, H, dk]  dtype, outputs (gradients of the raw q, k:
+ *              through the L2 norm when qk_l2norm is set)
+ *   dv         [B, T, H, dv]  dtype, output
+ *   dg         fp32, output shaped like g ([B, T, H] when gate_per_head = 1:
+ *              the sum over the key channels)
+ *   dbeta      [B, T, H]      fp32, output
+ *   d_init_state [N, H, dk, dv] fp32 output or NULL
+ *   workspace  device scratch of at least kda_chunk_bwd_workspace_bytes().
+ * Supported: bf16 with dk = dv = 64 or 128, fp32 with dk = dv = 64
+ * (KDA_ERR_UNSUPPORTED otherwise).  Alignment as kda_chunk_fwd (d_o, dq, dk,
+ * dv 16-byte; dg, dbeta 4-byte).  Outputs must not alias inputs.  Every
+ * chunk's per-channel decay (the sum of its 64 log-gates) must be >= -80;
+ * beyond that the results are unspecified (no fault, no hang). */
+kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           const float* init_state, const int32_t* cu_seqlens, const void* d_o,
+                           const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                           float* dbeta, float* d_init_state, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
 /* One decode step for N independent sequences, state updated in place.

@@ -30,7 +30,7 @@ def test_exports_match_header():
 
 def test_abi_version_and_strings():
     lib = K.load_library()
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
     assert lib.kda_status_string(99) == b"KDA_STATUS_UNKNOWN"
@@ -189,3 +189,49 @@ def test_short_conv_errors():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         B.load_library(str(tmp_path / "missing.so"))
+
+
+def _call_bwd(desc, *, ws=None, ws_bytes=None, nulls=(), misalign=None, alias=None):
+    """Backward calls that must fail host validation (nothing launched)."""
+    lib = K.load_library()
+    need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc))
+    names = ("q", "k", "v", "g", "beta", "d_o", "dq", "dk", "dv", "dg", "dbeta")
+    ptrs = {n: FAKE + 0x1000 * i for i, n in enumerate(names)}
+    for n in nulls:
+        ptrs[n] = None
+    if misalign:
+        ptrs[misalign] += 4
+    if alias:
+        ptrs[alias[0]] = ptrs[alias[1]]
+    wsp = FAKE + 0x100000 if ws is None else ws
+    wsb = need if ws_bytes is None else ws_bytes
+    return lib.kda_chunk_bwd(ctypes.byref(desc), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"],
+                             ptrs["beta"], None, None, ptrs["d_o"], None, ptrs["dq"], ptrs["dk"],
+                             ptrs["dv"], ptrs["dg"], ptrs["dbeta"], None, wsp, wsb, None)
+
+
+def test_bwd_workspace_and_support():
+    lib = K.load_library()
+    # fp32 operands at d = 128 are not supported by the backward
+    d = _desc(dk=128, dv=128, dtype=0)
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    assert _call_bwd(d) == B.KDA_ERR_UNSUPPORTED
+    for dt, dk in ((0, 64), (1, 64), (1, 128)):
+        d = _desc(dk=dk, dv=dk, dtype=dt)
+        need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d))
+        # at least the entering states and their gradients for every chunk slot
+        assert need >= 2 * 2 * 2 * dk * dk * 4
+    d = _desc(dk=64, dv=64, dtype=1)
+    assert _call_bwd(d, ws_bytes=1) == B.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert _call_bwd(d, ws=0) == B.KDA_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("case", [
+    dict(nulls=("d_o",)), dict(nulls=("dg",)), dict(nulls=("dbeta",)),
+    dict(misalign="dq"), dict(misalign="d_o"), dict(alias=("dq", "q")),
+    dict(alias=("dv", "d_o")),
+])
+def test_bwd_pointer_errors(case):
+    lib = K.load_library()
+    st = _call_bwd(_desc(dk=64, dv=64, dtype=1), **case)
+    assert st == B.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error()
