@@ -8,8 +8,10 @@ B=1, H=32, T=8192, d=128 bf16 workload.  The step is timed with HIP events on
 the stream the library launches on, K steps back to back between two device
 synchronisations; inputs are resident in HBM before timing starts.  The
 decode workload (256 sequences x 32 heads, d=128, 1024 sequential steps) is
-timed the same way and reported in the "decode" object.  The CPU oracle is
-timed on a bounded sample of the same prefill workload on this host's cores.
+timed the same way and reported in the "decode" object; the output epilogue,
+the ShortConv prologue, the gate-mode sweep and the backward (gradients of
+the same prefill workload) in objects of their own.  The CPU oracle is timed
+on a bounded sample of the same prefill workload on this host's cores.
 
 Prints ONE JSON line.
 
@@ -17,8 +19,8 @@ Prints ONE JSON line.
 
 runs, for hardware-counter passes (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE),
 one 1 GiB device-to-device copy (the calibration kernel: 1 GiB read, 1 GiB
-written), then 2 prefill calls, 2 decode steps, 2 epilogue and 2 prologue
-calls, and prints nothing.
+written), then 2 prefill calls, 2 decode steps, 2 epilogue, 2 prologue and
+2 backward calls, and prints nothing.
 
     python bench.py --write-traffic FETCH_CSV WRITE_CSV
 
@@ -42,7 +44,8 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from gated_delta_rule_54_amd import (chunk_fwd_workspace_bytes, kda_chunk_fwd,  # noqa: E402
+from gated_delta_rule_54_amd import (chunk_bwd_workspace_bytes,  # noqa: E402
+                                     chunk_fwd_workspace_bytes, kda_chunk_bwd, kda_chunk_fwd,
                                      kda_decode_step, kda_output_gate_norm,
                                      kda_short_conv_swish, make_desc)
 from gated_delta_rule_54_amd import workloads as W  # noqa: E402
@@ -57,12 +60,19 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 #   chunkwise FLOP model of the pages; the dense count of the kernels'
 #   products is 6 d^2 + 10 C d + C^2 / 3)
 PREFILL_BYTES_PER_TH = 3 * 256 + 512 + 4 + 256
+#   backward: reads q, k, v, do bf16 (4 x 256), g (512), beta (4); writes dq,
+#   dk, dv bf16 (3 x 256), dg (512), dbeta (4).  The per-sequence states
+#   (init_state, d_final, d_init: 3 x 64 KiB per head) are left out, as the
+#   prefill figure leaves out init and final states.
+BACKWARD_BYTES_PER_TH = 4 * 256 + 512 + 4 + 3 * 256 + 512 + 4
 DECODE_BYTES_PER_TH = PREFILL_BYTES_PER_TH + 2 * 128 * 128 * 4
 PREFILL_FLOPS_PER_TH = 6 * 128 ** 2 + 3 * 64 * 128 + 64 ** 2
 DECODE_FLOPS_PER_TH = 7 * 128 ** 2
 
 
-KERNEL_SOURCES = ("gated_delta_rule_54_amd/csrc/kda_chunk.hip",
+KERNEL_SOURCES = ("gated_delta_rule_54_amd/csrc/kda_chunk_common.h",
+                  "gated_delta_rule_54_amd/csrc/kda_chunk.hip",
+                  "gated_delta_rule_54_amd/csrc/kda_chunk_bwd.hip",
                   "gated_delta_rule_54_amd/csrc/kda_decode.hip",
                   "gated_delta_rule_54_amd/csrc/kda_epilogue.hip",
                   "gated_delta_rule_54_amd/csrc/kda_conv.hip")
@@ -88,11 +98,11 @@ def measured_traffic():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None, None, None, None
+        return None, None, None, None, None
     if t.get("kernel_source_sha256") != kernel_source_hash():
-        return None, None, None, None
+        return None, None, None, None, None
     return (t.get("prefill_call_bytes"), t.get("decode_step_bytes"), t.get("epilogue_call_bytes"),
-            t.get("prologue_call_bytes"))
+            t.get("prologue_call_bytes"), t.get("backward_call_bytes"))
 
 
 def probe():
@@ -129,12 +139,30 @@ def probe():
     for _ in range(2):
         kda_short_conv_swish(x, w, b, s)
     torch.cuda.synchronize()
+    del x, w, b, s
+    inp, up = backward_inputs()
+    for _ in range(2):
+        kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                      inp["init_state"], up["dfinal"])
+    torch.cuda.synchronize()
 
 
-# kernel-name fragment -> (key in the traffic file, calls the probe makes)
+# kernel-name fragment -> (key in the traffic file, calls the probe makes).
+# The backward runs the forward's kernels too: those dispatched after the
+# last prologue dispatch belong to the backward.
 _PROBE_KERNELS = (("kda_intra_chunk", "prefill", 2), ("kda_state_pass", "prefill", 2),
                   ("decode_step_kernel", "decode", 2), ("gate_norm_kernel", "epilogue", 2),
-                  ("short_conv_kernel", "prologue", 2))
+                  ("short_conv_kernel", "prologue", 2), ("kda_bwd_prep", "backward", 2),
+                  ("kda_bwd_state_pass", "backward", 2), ("kda_bwd_intra", "backward", 2))
+
+
+def _probe_key(name: str, after_prologue: bool):
+    for frag, key, _ in _PROBE_KERNELS:
+        if frag in name:
+            if key == "prefill" and after_prologue:
+                return f"backward_fwd_{frag}", "backward"
+            return frag, key
+    return None, None
 
 
 def write_traffic(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> dict:
@@ -145,15 +173,18 @@ def write_traffic(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> di
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if len(copy) != 1:
             raise SystemExit(f"{path}: expected one calibration copy, found {len(copy)}")
+        last_pro = max((i for i, r in enumerate(rows) if "short_conv_kernel" in r["Kernel_Name"]),
+                       default=len(rows))
         sums, parts = {}, {}
-        for r in rows:
-            for frag, key, _ in _PROBE_KERNELS:
-                if frag in r["Kernel_Name"]:
-                    sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
-                    parts[frag] = parts.get(frag, 0.0) + float(r["Counter_Value"])
+        for i, r in enumerate(rows):
+            part, key = _probe_key(r["Kernel_Name"], i > last_pro)
+            if key is not None:
+                sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+                parts[part] = parts.get(part, 0.0) + float(r["Counter_Value"])
         return copy[0], sums, parts
 
     gib = 1 << 30
@@ -163,8 +194,9 @@ def write_traffic(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> di
     calls = {key: n for _, key, n in _PROBE_KERNELS}
     t = {"what": "HBM-side bytes (TCC FETCH_SIZE + WRITE_SIZE, each scaled by what it reads "
                  "for a 1 GiB device copy) per prefill call (B1 H32 T8192 d128 bf16), per "
-                 "decode step (256 x 32 heads, d128), per epilogue call (262144 x 128 bf16) "
-                 "and per prologue call ([1, 8192, 4096] bf16, width 4)",
+                 "decode step (256 x 32 heads, d128), per epilogue call (262144 x 128 bf16), "
+                 "per prologue call ([1, 8192, 4096] bf16, width 4) and per backward call "
+                 "(B1 H32 T8192 d128 bf16, its forward recompute included)",
          "kernel_source_sha256": kernel_source_hash(),
          "calibration": {"copy_bytes": gib, "fetch_kib_read": f_copy, "write_kib_read": w_copy,
                          "fetch_scale": fs, "write_scale": wsc}}
@@ -174,8 +206,8 @@ def write_traffic(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> di
         unit = "step" if key == "decode" else "call"
         t[f"{key}_{unit}_bytes"] = (f_sum[key] * fs + w_sum[key] * wsc) * 1024 / calls[key]
     t["breakdown_bytes_per_call"] = {
-        f"{frag}_{kind}": parts[frag] * scale * 1024 / n
-        for frag, _, n in _PROBE_KERNELS
+        f"{part}_{kind}": parts[part] * scale * 1024 / 2
+        for part in sorted(f_parts)
         for kind, parts, scale in (("fetch", f_parts, fs), ("write", w_parts, wsc))}
     with open(out, "w") as f:
         json.dump(t, f, indent=1)
@@ -241,6 +273,40 @@ def bench_prologue(steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
     nbytes = x.numel() * PROLOGUE_BYTES_PER_EL
     return dict(ms=ms, achieved_gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
+def backward_inputs():
+    """The prefill workload (B1 H32 T8192 d128 bf16, nonzero initial state)
+    with seeded upstream gradients do and d_final."""
+    w = W.PREFILL_8K
+    inp = W.prefill_inputs(batch=w.batch, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
+                           dtype=w.dtype, device="cuda", seed=w.seed, init="normal")
+    up = W.upstream_grads(batch=w.batch, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
+                          num_seqs=w.batch, dtype=w.dtype, device="cuda", seed=w.seed + 7)
+    return inp, up
+
+
+def bench_backward(steps: int, warmup: int):
+    inp, up = backward_inputs()
+    B, T, H, d = inp["q"].shape
+    desc = make_desc(batch=B, num_seqs=B, seqlen=T, heads=H, dk=d, dv=d, dtype=inp["q"].dtype)
+    ws = torch.empty(chunk_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                                inp["init_state"], up["dfinal"], workspace=ws, stream=stream)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    th = B * T * H
+    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), ws_bytes=ws.numel(),
+                achieved_gbs=BACKWARD_BYTES_PER_TH * th / (ms * 1e-3) / 1e9)
 
 
 def bench_gate_modes(reps: int = 5):
@@ -397,11 +463,12 @@ def main():
         probe()
         return
     pf = bench_prefill(args.steps, args.warmup)
-    tr_prefill, tr_decode, tr_epi, tr_pro = measured_traffic()
+    tr_prefill, tr_decode, tr_epi, tr_pro, tr_bwd = measured_traffic()
     dc = bench_decode(min(args.warmup, 8))
     ep = bench_epilogue(args.steps, args.warmup)
     gm = bench_gate_modes()
     pl = bench_prologue(args.steps, args.warmup)
+    bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 2))
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -457,6 +524,19 @@ def main():
                                   "traffic": (tr_pro / (pl["ms"] * 1e-3) / 1e9) if tr_pro else None,
                                   "kernel": "short_conv_kernel<bf16,4>",
                                   "bytes_per_element": PROLOGUE_BYTES_PER_EL}},
+        "backward": {"workload": "gradients of the prefill workload (B=1 H=32 T=8192 "
+                                 "d=128 bf16, nonzero initial state, seeded do and d_final): "
+                                 "dq, dk, dv, dg, dbeta, d_init",
+                     "us_per_call": bw["ms"] * 1e3, "value": bw["tokens_per_s"],
+                     "unit": "tokens/s",
+                     "roofline": {"bound": "hbm", "achieved": bw["achieved_gbs"],
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": bw["achieved_gbs"] / HBM_PEAK_GBS,
+                                  "traffic": (tr_bwd / (bw["ms"] * 1e-3) / 1e9) if tr_bwd else None,
+                                  "traffic_bytes_per_call": tr_bwd,
+                                  "kernel": "kda_chunk_bwd (forward recompute + kda_bwd_prep + "
+                                            "kda_bwd_state_pass + kda_bwd_intra)",
+                                  "bytes_per_token_head": BACKWARD_BYTES_PER_TH}},
         "gate_modes": {"workload": "prefill B=1 H=16 d=128 bf16, T = 2K..64K: per-channel "
                                    "gates (KDA) vs one gate per token and head (GDN)",
                        "rows": gm},

@@ -161,7 +161,7 @@ __device__ __forceinline__ typename Mma<T>::frag gfrag_cm(const float* X, int ld
   using M = Mma<T>;
   float x[M::KPL];
 #pragma unroll
-  for (int e = 0; e < M::KPL; ++e) x[e] = X[(int64_t)(ks * M::KSTEP + M::KPL * (lane >> 4) + e) * ld + n];
+  for (int e = 0; e < M::KPL; ++e) x[e] = X[(ks * M::KSTEP + M::KPL * (lane >> 4) + e) * ld + n];
   return to_frag(x, T{});
 }
 // The KPL consecutive fp32 values of row m at k-step ks (k contiguous).
@@ -169,7 +169,7 @@ template <typename T>
 __device__ __forceinline__ void grow_vals(const float* X, int ld, int m, int ks, int lane,
                                           float* x) {
   using M = Mma<T>;
-  const float* p = X + (int64_t)m * ld + ks * M::KSTEP + M::KPL * (lane >> 4);
+  const float* p = X + m * ld + ks * M::KSTEP + M::KPL * (lane >> 4);
   if constexpr (M::KPL == 8) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -188,8 +188,11 @@ __device__ __forceinline__ float sum16(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS of the per-chunk backward kernels (bytes).
-template <typename T, int D>
+// LDS of the per-chunk backward kernels (bytes).  kda_bwd_intra (COMPACT =
+// false) keeps every operand for the whole kernel; kda_bwd_prep (COMPACT)
+// needs Kp, Km, Qp only until A and P are formed, so the fp32 A and T of the
+// inverse, and then K~, reuse their region, and two workgroups fit a CU.
+template <typename T, int D, bool COMPACT = false>
 struct BwdLds {
   static constexpr int NW = D / 16, NT = 64 * NW;  // waves (one per 16 columns), threads
   static constexpr int PAD = 16 / (int)sizeof(T);
@@ -199,19 +202,26 @@ struct BwdLds {
   static constexpr int FB = kC * kTriLd * 4;  // fp32 A or T of the inverse
   static constexpr int UB = 2 * (XB > FB ? XB : FB);
   static_assert(CB >= 4096, "the inverse's scratch lives in the dB buffer");
-  // regions: Kp, Km, Qp, K~ (later L); union {A, T fp32} then {W, dO'};
+  // full layout: Kp, Km, Qp, K~ (later L); union {A, T fp32} then {W, dO'};
   // T, P (later dP), dB; small fp32 arrays
-  static constexpr int KP = 0, KM = XB, QP = 2 * XB, KT = 3 * XB, U = 4 * XB;
-  static constexpr int TB = U + UB, PB = TB + CB, DB = PB + CB;
-  static constexpr int SM = DB + CB;
+  // compact layout: {Kp, Km, Qp} then {A, T, scratch} then {K~}; T, P; small
+  static constexpr int R0 = (3 * XB > 2 * FB + 4096) ? 3 * XB : 2 * FB + 4096;
+  static constexpr int KP = 0, KM = XB, QP = 2 * XB;
+  static constexpr int KT = COMPACT ? 0 : 3 * XB;
+  static constexpr int U = COMPACT ? 0 : 4 * XB;
+  static constexpr int TB = COMPACT ? R0 : U + UB;
+  static constexpr int PB = TB + CB;
+  static constexpr int DB = COMPACT ? -1 : PB + CB;
+  static constexpr int SCR = COMPACT ? 2 * FB : DB;
+  static constexpr int SM = COMPACT ? PB + CB : DB + CB;
   // small: beta, rk, rq, x0, x1, x2 [kC] and red [2][NW][kC]
   static constexpr int BYTES = SM + (6 * kC + 2 * NW * kC) * 4;
   static_assert(BYTES <= 160 * 1024, "per-chunk backward LDS exceeds a CU");
 };
 
-template <typename T, int D>
+template <typename T, int D, bool COMPACT = false>
 struct BwdSmem {
-  using L = BwdLds<T, D>;
+  using L = BwdLds<T, D, COMPACT>;
   T *kp, *km, *qp, *kt, *tb, *pb, *db, *wb, *dob;
   float *sA, *sT, *scratch, *beta, *rk, *rq, *x0, *x1, *x2, *red;
   __device__ explicit BwdSmem(char* s) {
@@ -225,8 +235,8 @@ struct BwdSmem {
     dob = reinterpret_cast<T*>(s + L::U + L::XB);
     tb = reinterpret_cast<T*>(s + L::TB);
     pb = reinterpret_cast<T*>(s + L::PB);
-    db = reinterpret_cast<T*>(s + L::DB);
-    scratch = reinterpret_cast<float*>(s + L::DB);
+    db = COMPACT ? nullptr : reinterpret_cast<T*>(s + L::DB);
+    scratch = reinterpret_cast<float*>(s + L::SCR);
     beta = reinterpret_cast<float*>(s + L::SM);
     rk = beta + kC;
     rq = rk + kC;
@@ -246,33 +256,73 @@ struct BwdRegs {
   float gam;       // gamma of this lane's column
 };
 
-// Prologue shared by the per-chunk backward kernels: loads, q/k norms, G,
-// the four gated operands in LDS, A and P, T = (I + A)^-1 (times Diag(beta)
-// when TBETA) in the MFMA type.  Bm receives this wave's tiles of Kp Km^T
-// (tile p = wave + NW * tt: rows 16(p/4), columns 16(p%4)).
-template <typename T, int D, bool GS, bool TBETA>
-__device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
-                                             const float* __restrict__ g,
-                                             const float* __restrict__ beta, const ChunkLoc& loc,
-                                             int H, int h, int qk_l2norm, BwdSmem<T, D>& sm,
-                                             BwdRegs& R, f32x4_t* Bm) {
-  using L = BwdLds<T, D>;
-  using M = Mma<T>;
-  constexpr int NW = L::NW, NT = L::NT, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
-  const int c = 16 * wave + (lane & 15);
-  float gr[4][4];
+// Raw k, q, g of this lane's column and rows (zero past the chunk's end).
+template <typename T, int D, bool GS>
+__device__ __forceinline__ void load_cols(const T* __restrict__ q, const T* __restrict__ k,
+                                          const float* __restrict__ g, const ChunkLoc& loc, int H,
+                                          int h, int c, int grp, BwdRegs& R, float (&gr)[4][4]) {
+  // uniform bases (the chunk's first row) and 32-bit per-lane offsets
+  const int64_t row0 = loc.tok0 * H + h;
+  const T* kb = k + row0 * D;
+  const T* qb = q + row0 * D;
+  const float* gb = GS ? g + row0 : g + row0 * D;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      const int64_t row = (loc.tok0 + min(r, loc.len - 1)) * H + h;
+      const int off = min(r, loc.len - 1) * H * D + c;
       const bool ok = r < loc.len;
-      R.kh[t][j] = ok ? ld_f(k + row * D + c) : 0.f;
-      R.qh[t][j] = ok ? ld_f(q + row * D + c) : 0.f;
-      gr[t][j] = ok ? (GS ? g[row] : g[row * D + c]) : 0.f;
+      R.kh[t][j] = ok ? ld_f(kb + off) : 0.f;
+      R.qh[t][j] = ok ? ld_f(qb + off) : 0.f;
+      gr[t][j] = ok ? (GS ? gb[min(r, loc.len - 1) * H] : gb[off]) : 0.f;
     }
+}
+
+// G = prefix sum of gr down the 64 rows of this lane's column -- within the
+// lane's 4 rows, then across the 4 lane groups, then across the tiles -- and
+// gamma = G of the last row.
+__device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdRegs& R) {
+  const int grp = lane >> 4;
+  float carry = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float loc4[4];
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { run += gr[t][j]; loc4[j] = run; }
+    float x = run;
+    float y = __shfl_up(x, 16);
+    if (grp >= 1) x += y;
+    y = __shfl_up(x, 32);
+    if (grp >= 2) x += y;
+    const float excl = x - run;
+    const float total = __shfl(x, 48 + (lane & 15));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) R.G[t][j] = carry + excl + loc4[j];
+    carry += total;
+  }
+  R.gam = carry;
+}
+
+// Prologue shared by the per-chunk backward kernels: loads, q/k norms, G,
+// the gated operands in LDS (K~ left to the caller in the compact layout), A
+// and P, T = (I + A)^-1 (times Diag(beta) when TBETA) in the MFMA type.  Bm receives this wave's tiles of Kp Km^T
+// (tile p = wave + NW * tt: rows 16(p/4), columns 16(p%4)).
+template <typename T, int D, bool GS, bool TBETA, bool COMPACT>
+__device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
+                                             const float* __restrict__ g,
+                                             const float* __restrict__ beta, const ChunkLoc& loc,
+                                             int H, int h, int qk_l2norm,
+                                             BwdSmem<T, D, COMPACT>& sm, BwdRegs& R,
+                                             f32x4_t* Bm) {
+  using L = BwdLds<T, D, COMPACT>;
+  using M = Mma<T>;
+  constexpr int NW = L::NW, NT = L::NT, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+  const int c = 16 * wave + (lane & 15);
+  float gr[4][4];
+  load_cols<T, D, GS>(q, k, g, loc, H, h, c, grp, R, gr);
   if (tid < kC) sm.beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
   // row norms: over this wave's 16 columns, then over the waves
 #pragma unroll
@@ -298,27 +348,7 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
     sm.rk[tid] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
     sm.rq[tid] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
   }
-  // G: prefix sum down the 64 rows of this lane's column -- within the
-  // lane's 4 rows, then across the 4 lane groups, then across the tiles
-  float carry = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float loc4[4];
-    float run = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { run += gr[t][j]; loc4[j] = run; }
-    float x = run;
-    float y = __shfl_up(x, 16);
-    if (grp >= 1) x += y;
-    y = __shfl_up(x, 32);
-    if (grp >= 2) x += y;
-    const float excl = x - run;
-    const float total = __shfl(x, 48 + (lane & 15));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) R.G[t][j] = carry + excl + loc4[j];
-    carry += total;
-  }
-  R.gam = carry;
+  prefix_G(gr, lane, R);
   __syncthreads();
   // gated operands
 #pragma unroll
@@ -333,7 +363,7 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
       st_f(sm.kp + r * LDX + c, R.kh[t][j] * eg);
       st_f(sm.km + r * LDX + c, R.kh[t][j] * en);
       st_f(sm.qp + r * LDX + c, R.qh[t][j] * eg);
-      st_f(sm.kt + r * LDX + c, R.kh[t][j] * et);
+      if constexpr (!COMPACT) st_f(sm.kt + r * LDX + c, R.kh[t][j] * et);
     }
   __syncthreads();
   // A = Diag(beta) tril_-1(Kp Km^T) (fp32) and P = tril(Qp Km^T)
@@ -350,10 +380,19 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
     Bm[tt] = ab;
     const int i = 16 * ib + (lane & 15);
 #pragma unroll
+    for (int j = 0; j < 4; ++j) st_f(sm.pb + (16 * rb + 4 * grp + j) * LDC + i, i <= 16 * rb + 4 * grp + j ? ap[j] : 0.f);
+  }
+  // A from the kept Bm tiles; in the compact layout A overlays Kp and Km, so
+  // every wave must be done reading them first
+  if constexpr (COMPACT) __syncthreads();
+#pragma unroll
+  for (int tt = 0; tt < NTW; ++tt) {
+    const int p = wave + NW * tt, rb = p >> 2, ib = p & 3;
+    const int i = 16 * ib + (lane & 15);
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * rb + 4 * grp + j;
-      sm.sA[r * kTriLd + i] = i < r ? sm.beta[r] * ab[j] : 0.f;
-      st_f(sm.pb + r * LDC + i, i <= r ? ap[j] : 0.f);
+      sm.sA[r * kTriLd + i] = i < r ? sm.beta[r] * Bm[tt][j] : 0.f;
     }
   }
   __syncthreads();
@@ -367,8 +406,8 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
 }
 
 // ---------------------------------------------------------------------------
-// Reverse-pass record of one (head, chunk slot): M and Z^T in operand order
-// (see fnat), rows = key channel c, k = c' (M) or chunk row r (Z^T).
+// Reverse-pass record of one (head, chunk slot): M and scale Z^T in operand
+// order (see fnat), rows = key channel c, k = c' (M) or chunk row r (Z^T).
 template <typename T, int D>
 struct BRec {
   static constexpr int64_t MF = 0;
@@ -378,11 +417,12 @@ struct BRec {
 };
 
 template <typename T, int D, bool GS>
-__global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_prep(
+__global__ __launch_bounds__((BwdLds<T, D>::NT), 1)
+__attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, ChunkGeom gm, int H, int64_t nslot, int qk_l2norm,
-    char* __restrict__ brec) {
-  using L = BwdLds<T, D>;
+    float scale, char* __restrict__ brec) {
+  using L = BwdLds<T, D, true>;
   using M = Mma<T>;
   using RC = BRec<T, D>;
   constexpr int NW = L::NW, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
@@ -392,12 +432,19 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_prep(
   const int64_t slot = blockIdx.y;
   ChunkLoc loc;
   if (!locate(gm, slot, loc)) return;
-  BwdSmem<T, D> sm(smem);
+  BwdSmem<T, D, true> sm(smem);
   BwdRegs R;
   f32x4_t Bm[NTW];
-  bwd_prologue<T, D, GS, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  bwd_prologue<T, D, GS, true, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
+  // K~ into the region the inverse has finished with
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      st_f(sm.kt + (16 * t + 4 * grp + j) * LDX + c, R.kh[t][j] * __expf(R.gam - R.G[t][j]));
+  __syncthreads();
   T* rec = reinterpret_cast<T*>(brec + ((int64_t)h * nslot + slot) * RC::BYTES);
 
   // Wk = T Diag(beta) Kp for this wave's columns, B = Kp from registers
@@ -413,8 +460,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_prep(
     for (int ks = 0; ks < KC; ++ks)
       wk[t] = M::mma(frag_rm_perm<T>(sm.tb, LDC, 16 * t, ks, lane), acc_frag<T>(kpa, ks), wk[t]);
   }
-  // Z = Qp - P Wk, stored as Z^T (rows c, k = r): each lane's 4 rows are 4
-  // consecutive k
+  // Z = Qp - P Wk, stored as scale Z^T (rows c, k = r; the reverse pass then
+  // takes dO as it is): each lane's 4 rows are 4 consecutive k
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     f32x4_t pw = {0.f, 0.f, 0.f, 0.f};
@@ -423,7 +470,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_prep(
       pw = M::mma(frag_rm_perm<T>(sm.pb, LDC, 16 * t, ks, lane), acc_frag<T>(wk, ks), pw);
     float z[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = R.qh[t][j] * __expf(R.G[t][j]) - pw[j];
+    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] * __expf(R.G[t][j]) - pw[j]);
     st_fnat4(rec + RC::ZF, KC, c, 16 * t + 4 * grp, z[0], z[1], z[2], z[3]);
   }
   // M^T tiles (rows c', column c) = Diag(e^gamma) - K~^T Wk, stored as M
@@ -446,7 +493,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_prep(
 }
 
 // ---------------------------------------------------------------------------
-// Reverse state pass: dS = M dS' + Z^T dO' chunk by chunk from the last, one
+// Reverse state pass: dS = M dS' + (scale Z)^T dO chunk by chunk from the last, one
 // workgroup per (sequence, head, 16 columns of d_v).  Wave w owns rows
 // [16 CBW w, 16 CBW (w+1)) of dS in accumulators; dS' crosses LDS once per
 // chunk (double-buffered, so one barrier per chunk).  Each chunk's dS' (the
@@ -458,14 +505,24 @@ template <typename T, int D>
 struct BwdPassFrags {
   using M = Mma<T>;
   static constexpr int CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
-  typename M::frag mf[CBW][KD], zf[CBW][KC], of[KC];
+  typename M::frag mf[CBW][KD], zf[CBW][KC];
+  uint32_t od[KC][M::KPL];  // raw dO elements, packed into fragments at use
+  __device__ __forceinline__ typename M::frag dof(int ks) const {
+    if constexpr (M::KPL == 8) {
+      const u32x4_t u = {od[ks][0] | (od[ks][1] << 16), od[ks][2] | (od[ks][3] << 16),
+                         od[ks][4] | (od[ks][5] << 16), od[ks][6] | (od[ks][7] << 16)};
+      return __builtin_bit_cast(bf16x8_t, u);
+    } else {
+      return __builtin_bit_cast(float, od[ks][0]);
+    }
+  }
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     const char* __restrict__ brec, int64_t nslot, ChunkGeom gm, int H, int NH, int nslice,
     const T* __restrict__ d_o, const float* __restrict__ dfinal, float* __restrict__ dstates,
-    float* __restrict__ dinit, float scale) {
+    float* __restrict__ dinit) {
   using M = Mma<T>;
   using RC = BRec<T, D>;
   using F = BwdPassFrags<T, D>;
@@ -510,12 +567,15 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
       for (int ks = 0; ks < KC; ++ks)
         f.zf[i][ks] = M::load(rec + RC::ZF + (((wave * CBW + i) * KC + ks) * 64 + lane) * M::KPL);
     }
-    // dO' rows in kpos order (the k index of Z^T)
+    // dO rows in kpos order (the k index of Z^T), as raw bits: the buffer's
+    // bound ends after the chunk's last valid row, so rows past a
+    // sequence's end read as zero without a branch
     const int len = ci == nch - 1 ? len_last : kC;
-    const T* ob = d_o + ((sp.tok0 + (int64_t)ci * kC) * H + h) * D + n;
+    const T* ob = d_o + ((sp.tok0 + (int64_t)ci * kC) * H + h) * D + n0;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)ob, (short)0, (int)(((len - 1) * H * D + kBwdSliceW) * sizeof(T)), 0x00020000);
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks) {
-      float x[M::KPL];
+    for (int ks = 0; ks < KC; ++ks)
 #pragma unroll
       for (int e = 0; e < M::KPL; ++e) {
         int r;
@@ -523,10 +583,12 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
           r = ks * 32 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
         else
           r = 16 * (ks >> 2) + 4 * grp + (ks & 3);
-        x[e] = r < len ? scale * ld_f(ob + (int64_t)r * H * D) : 0.f;
+        const uint32_t off = (uint32_t)((r * H * D + (lane & 15)) * sizeof(T));
+        if constexpr (M::KPL == 8)
+          f.od[ks][e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
+        else
+          f.od[ks][e] = __builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0);
       }
-      f.of[ks] = to_frag(x, T{});
-    }
   };
   auto step = [&](const F& f, int ci, int buf) {
     const int64_t slot = sp.c0 + ci;
@@ -536,7 +598,7 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     for (int i = 0; i < CBW; ++i) {
       const int c4 = (wave * CBW + i) * 16 + 4 * grp;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(int64_t)(c4 + j) * D] = dS[i][j];
+      for (int j = 0; j < 4; ++j) dst[(c4 + j) * D] = dS[i][j];
       st_perm4(sb + (lane & 15) * LDS_S, c4, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
     }
     __syncthreads();
@@ -547,7 +609,7 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     for (int i = 0; i < CBW; ++i) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KC; ++ks) acc = M::mma(f.zf[i][ks], f.of[ks], acc);
+      for (int ks = 0; ks < KC; ++ks) acc = M::mma(f.zf[i][ks], f.dof(ks), acc);
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) acc = M::mma(f.mf[i][ks], bfr[ks], acc);
       dS[i] = acc;
@@ -599,14 +661,25 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   ChunkLoc loc;
   if (!locate(gm, slot, loc)) return;
   BwdSmem<T, D> sm(smem);
-  BwdRegs R;
   f32x4_t Bm[NTW];
-  bwd_prologue<T, D, GS, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  {
+    BwdRegs R0;  // recomputed at the end rather than kept live (registers)
+    bwd_prologue<T, D, GS, false, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R0, Bm);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);  // this lane's column (d_k or d_v)
   const float* S = states + (slot * H + h) * (int64_t)D * D;
   const float* dS = dstates + (slot * H + h) * (int64_t)D * D;
-  auto tok = [&](int r) { return (loc.tok0 + r) * H + h; };
+  // per-token tensors: uniform bases at the chunk's first row, 32-bit offsets
+  const int64_t row0 = loc.tok0 * H + h;
+  const T* vb = v + row0 * D;
+  const T* ob = d_o + row0 * D;
+  T* dqb = dq + row0 * D;
+  T* dkb = dk + row0 * D;
+  T* dvb = dv + row0 * D;
+  float* dgb = GS ? dg + row0 : dg + row0 * D;
+  float* dbb = dbeta + row0;
+  auto tok = [&](int r) { return r * H; };  // row offset, in rows of D elements
 
   // ---- value side: columns n = c --------------------------------------------
   // Kp S, then R = Diag(beta)(V - Kp S) and W = T R
@@ -617,13 +690,14 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     for (int ks = 0; ks < KD; ++ks) sb[ks] = gfrag_cm<T>(S, D, c, ks, lane);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
       f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) a = M::mma(frag_at<T>(sm.kp, LDX, 16 * t, ks, lane), sb[ks], a);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * t + 4 * grp + j;
-        const float vv = r < loc.len ? ld_f(v + tok(r) * D + c) : 0.f;
+        const float vv = r < loc.len ? ld_f(vb + tok(r) * D + c) : 0.f;
         vmk[t][j] = vv - a[j];
         acc[t][j] = sm.beta[r] * vmk[t][j];
       }
@@ -631,6 +705,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
+    __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
     w[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks)
@@ -643,7 +718,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      dov[t][j] = r < loc.len ? scale * ld_f(d_o + tok(r) * D + c) : 0.f;
+      dov[t][j] = r < loc.len ? scale * ld_f(ob + tok(r) * D + c) : 0.f;
       st_f(sm.wb + r * LDX + c, w[t][j]);
       st_f(sm.dob + r * LDX + c, dov[t][j]);
     }
@@ -654,6 +729,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     for (int ks = 0; ks < KD; ++ks) dsb[ks] = gfrag_cm<T>(dS, D, c, ks, lane);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
       f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks)
@@ -667,6 +743,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   f32x4_t lam[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
+    __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
     lam[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks)
@@ -674,7 +751,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      if (r < loc.len) st_f(dv + tok(r) * D + c, sm.beta[r] * lam[t][j]);
+      if (r < loc.len) st_f(dvb + tok(r) * D + c, sm.beta[r] * lam[t][j]);
       const float part = sum16(lam[t][j] * vmk[t][j]);
       if ((lane & 15) == 0) sm.red[wave * kC + r] = part;
     }
@@ -719,67 +796,111 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     sm.x0[tid] = b;
   }
 
-  // ---- key side: columns c --------------------------------------------------
-  float rs = 0.f;  // rowsum(S o dS') of row c
-  typename M::frag st[KD], dst[KD];
-#pragma unroll
-  for (int ks = 0; ks < KD; ++ks) {
-    float xs[KPL], xd[KPL];
-    grow_vals<T>(S, D, c, ks, lane, xs);
-    grow_vals<T>(dS, D, c, ks, lane, xd);
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) rs += xs[e] * xd[e];
-    st[ks] = to_frag(xs, T{});
-    dst[ks] = to_frag(xd, T{});
-  }
-  rs += __shfl_xor(rs, 16);
-  rs += __shfl_xor(rs, 32);
-  f32x4_t dqp[4], dkp[4], dkm[4], dkt[4];
+  __syncthreads();  // red is free again (x0 was formed from it)
+
+  // ---- key side: columns c, then the gates ----------------------------------
+  // (the scheduler fences between phases keep each phase's loads in it:
+  // hoisted early, they would hold registers across the phases before)
+  __builtin_amdgcn_sched_barrier(0);
+  // G, k^, q^ again (the chunk's k, q, g are still in the cache)
+  BwdRegs R;
   {
-    typename M::frag kmc[KC], kpc[KC], qpc[KC];
+    float gr[4][4];
+    load_cols<T, D, GS>(q, k, g, loc, H, h, c, grp, R, gr);
+    prefix_G(gr, lane, R);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * t + 4 * grp + j;
+        R.kh[t][j] *= sm.rk[r];
+        R.qh[t][j] *= sm.rq[r];
+      }
+  }
+  // Two passes, each with its own B operands, the gate factors applied per
+  // tile so that one tile's accumulators are live at a time:
+  //   1. dQp = dO' S^T + dP Km,  dKp = dB Km - Diag(beta) L S^T
+  //   2. dKm = dB^T Kp + dP^T Qp,  dK~ = W dS'^T,  rowsum(S o dS')
+  // (q^ is read again for the norm's projection at the end rather than kept)
+  float dkh[4][4], dqh[4][4], dG[4][4];  // dkh holds dKp o e^G after pass 1
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    typename M::frag st[KD], kmc[KC];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      float xs[KPL];
+      grow_vals<T>(S, D, c, ks, lane, xs);
+      st[ks] = to_frag(xs, T{});
+    }
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) kmc[ks] = frag_cm<T>(sm.km, LDX, 16 * wave, ks, lane);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f}, x = a, b = a;
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) {
+        a = M::mma(frag_at<T>(sm.dob, LDX, 16 * t, ks, lane), st[ks], a);  // dO' S^T
+        x = M::mma(frag_at<T>(lb, LDX, 16 * t, ks, lane), st[ks], x);      // L S^T
+      }
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {
+        a = M::mma(frag_at<T>(sm.pb, LDC, 16 * t, ks, lane), kmc[ks], a);  // dP Km
+        b = M::mma(frag_at<T>(sm.db, LDC, 16 * t, ks, lane), kmc[ks], b);  // dB Km
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float eg = __expf(R.G[t][j]);
+        dqh[t][j] = a[j] * eg;
+        dkh[t][j] = (b[j] - sm.beta[16 * t + 4 * grp + j] * x[j]) * eg;
+        dG[t][j] = R.qh[t][j] * dqh[t][j];  // q^ is not needed again until the end
+        const float qd = sum16(R.qh[t][j] * dqh[t][j]);  // row dot q^ . dq^, this wave's part
+        if ((lane & 15) == 0) sm.red[(NW + wave) * kC + 16 * t + 4 * grp + j] = qd;
+      }
+    }
+  }
+  float rs = 0.f, dgam = 0.f;  // rowsum(S o dS') of row c
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    typename M::frag dst[KD], kpc[KC], qpc[KC];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      float xs[KPL], xd[KPL];
+      grow_vals<T>(S, D, c, ks, lane, xs);
+      grow_vals<T>(dS, D, c, ks, lane, xd);
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) rs += xs[e] * xd[e];
+      dst[ks] = to_frag(xd, T{});
+    }
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks) {
-      kmc[ks] = frag_cm<T>(sm.km, LDX, 16 * wave, ks, lane);
       kpc[ks] = frag_cm<T>(sm.kp, LDX, 16 * wave, ks, lane);
       qpc[ks] = frag_cm<T>(sm.qp, LDX, 16 * wave, ks, lane);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      f32x4_t a = {0.f, 0.f, 0.f, 0.f}, x = a, b = a, m = a, kt = a;
+      __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f}, kt = m;
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) {
-        a = M::mma(frag_at<T>(sm.dob, LDX, 16 * t, ks, lane), st[ks], a);   // dO' S^T
-        x = M::mma(frag_at<T>(lb, LDX, 16 * t, ks, lane), st[ks], x);       // L S^T
-        kt = M::mma(frag_at<T>(sm.wb, LDX, 16 * t, ks, lane), dst[ks], kt); // W dS'^T
-      }
+      for (int ks = 0; ks < KD; ++ks)
+        kt = M::mma(frag_at<T>(sm.wb, LDX, 16 * t, ks, lane), dst[ks], kt);  // W dS'^T
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) {
-        a = M::mma(frag_at<T>(sm.pb, LDC, 16 * t, ks, lane), kmc[ks], a);   // dP Km
-        b = M::mma(frag_at<T>(sm.db, LDC, 16 * t, ks, lane), kmc[ks], b);   // dB Km
-        m = M::mma(frag_cm<T>(sm.db, LDC, 16 * t, ks, lane), kpc[ks], m);   // dB^T Kp
-        m = M::mma(frag_cm<T>(sm.pb, LDC, 16 * t, ks, lane), qpc[ks], m);   // dP^T Qp
+        m = M::mma(frag_cm<T>(sm.db, LDC, 16 * t, ks, lane), kpc[ks], m);  // dB^T Kp
+        m = M::mma(frag_cm<T>(sm.pb, LDC, 16 * t, ks, lane), qpc[ks], m);  // dP^T Qp
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] -= sm.beta[16 * t + 4 * grp + j] * x[j];
-      dqp[t] = a; dkp[t] = b; dkm[t] = m; dkt[t] = kt;
+      for (int j = 0; j < 4; ++j) {
+        const float G = R.G[t][j];
+        const float a = dkh[t][j], bm = m[j] * __expf(-G), e = kt[j] * __expf(R.gam - G);
+        dkh[t][j] = a + bm + e;
+        dG[t][j] += R.kh[t][j] * (a - bm - e);
+        dgam += R.kh[t][j] * e;
+      }
     }
   }
-
-  // ---- gates, prefix-sum reversal, norms -------------------------------------
-  float dkh[4][4], dqh[4][4], dG[4][4];
-  float dgam = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float G = R.G[t][j];
-      const float a = dkp[t][j] * __expf(G), b = dkm[t][j] * __expf(-G);
-      const float e = dkt[t][j] * __expf(R.gam - G);
-      dkh[t][j] = a + b + e;
-      dqh[t][j] = dqp[t][j] * __expf(G);
-      dG[t][j] = R.kh[t][j] * (a - b - e) + R.qh[t][j] * dqh[t][j];
-      dgam += R.kh[t][j] * e;
-    }
+  rs += __shfl_xor(rs, 16);
+  rs += __shfl_xor(rs, 32);
   dgam += __shfl_xor(dgam, 16);
   dgam += __shfl_xor(dgam, 32);
   dgam += __expf(R.gam) * rs;
@@ -807,19 +928,13 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       carry += total;
     }
   }
-  // row dots k^ . dk^, q^ . dq^ (and, per head, the row's dg) over all columns
-  __syncthreads();  // red is free again (x0 was formed from it above)
+  // row dots k^ . dk^ (q^ . dq^ was taken in pass 1) over all columns
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 16 * t + 4 * grp + j;
       const float a = sum16(R.kh[t][j] * dkh[t][j]);
-      const float b = sum16(R.qh[t][j] * dqh[t][j]);
-      if ((lane & 15) == 0) {
-        sm.red[wave * kC + r] = a;
-        sm.red[(NW + wave) * kC + r] = b;
-      }
+      if ((lane & 15) == 0) sm.red[wave * kC + 16 * t + 4 * grp + j] = a;
     }
   __syncthreads();
   if (tid < kC) {
@@ -831,9 +946,10 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     }
     sm.x1[tid] = a;
     sm.x2[tid] = b;
-    if (tid < loc.len) dbeta[tok(tid)] = sm.x0[tid];
+    if (tid < loc.len) dbb[tok(tid)] = sm.x0[tid];
   }
   __syncthreads();
+  const T* qrow = q + row0 * D;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -841,13 +957,14 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       const int r = 16 * t + 4 * grp + j;
       float gk = dkh[t][j], gq = dqh[t][j];
       if (qk_l2norm) {
+        const float qn = r < loc.len ? ld_f(qrow + tok(r) * D + c) * sm.rq[r] : 0.f;
         gk = sm.rk[r] * (gk - sm.x1[r] * R.kh[t][j]);
-        gq = sm.rq[r] * (gq - sm.x2[r] * R.qh[t][j]);
+        gq = sm.rq[r] * (gq - sm.x2[r] * qn);
       }
       if (r < loc.len) {
-        st_f(dk + tok(r) * D + c, gk);
-        st_f(dq + tok(r) * D + c, gq);
-        if (!GS) dg[tok(r) * D + c] = dgo[t][j];
+        st_f(dkb + tok(r) * D + c, gk);
+        st_f(dqb + tok(r) * D + c, gq);
+        if (!GS) dgb[tok(r) * D + c] = dgo[t][j];
       }
     }
   if constexpr (GS) {
@@ -864,7 +981,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       float a = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) a += sm.red[w2 * kC + tid];
-      dg[tok(tid)] = a;
+      dgb[tok(tid)] = a;
     }
   }
 }
@@ -921,11 +1038,15 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
                        d.seqlen, cu_s, chunk_off);
     gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
   }
+  using LP = BwdLds<T, D, true>;
   static bool attr_set = false;
   if (!attr_set) {
     for (const void* fn : {(const void*)kda_bwd_prep<T, D, false>,
-                           (const void*)kda_bwd_prep<T, D, true>,
-                           (const void*)kda_bwd_intra<T, D, false>,
+                           (const void*)kda_bwd_prep<T, D, true>}) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LP::BYTES);
+      if (e != hipSuccess) return e;
+    }
+    for (const void* fn : {(const void*)kda_bwd_intra<T, D, false>,
                            (const void*)kda_bwd_intra<T, D, true>}) {
       e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
       if (e != hipSuccess) return e;
@@ -934,14 +1055,15 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   }
   if (nslot > 0) {
     auto prep = d.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
-    hipLaunchKernelGGL(prep, dim3(H, (unsigned)nslot), dim3(L::NT), L::BYTES, stream,
-                       (const T*)q, (const T*)k, g, beta, gm, H, nslot, d.qk_l2norm, recs);
+    hipLaunchKernelGGL(prep, dim3(H, (unsigned)nslot), dim3(LP::NT), LP::BYTES, stream,
+                       (const T*)q, (const T*)k, g, beta, gm, H, nslot, d.qk_l2norm, d.scale,
+                       recs);
   }
   const int nslice = D / kBwdSliceW;
   const int nhpad = (NH + 7) / 8 * 8;
   hipLaunchKernelGGL((kda_bwd_state_pass<T, D>), dim3(nhpad * nslice), dim3(kBwdPassThreads), 0,
                      stream, recs, nslot, gm, H, NH, nslice, (const T*)d_o, d_final, dstates,
-                     d_init, d.scale);
+                     d_init);
   if (nslot > 0) {
     auto intra = d.gate_per_head ? kda_bwd_intra<T, D, true> : kda_bwd_intra<T, D, false>;
     hipLaunchKernelGGL(intra, dim3(H, (unsigned)nslot), dim3(L::NT), L::BYTES, stream,
