@@ -180,6 +180,18 @@ __device__ __forceinline__ void grow_vals(const float* X, int ld, int m, int ks,
   }
 }
 
+// One element as raw bits (a load whose value is converted only at use does
+// not make the wave wait where it is issued), and its value.
+__device__ __forceinline__ uint32_t ld_raw(const bf16* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+__device__ __forceinline__ uint32_t ld_raw(const float* p) { return __float_as_uint(*p); }
+template <typename T>
+__device__ __forceinline__ float raw_val(uint32_t b) {
+  if constexpr (sizeof(T) == 2) return bf_val(b);
+  else return __uint_as_float(b);
+}
+
 // Sum over the 16 lanes of a lane group (the 16 columns of an accumulator).
 __device__ __forceinline__ float sum16(float x) {
 #pragma unroll
@@ -682,12 +694,34 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   auto tok = [&](int r) { return r * H; };  // row offset, in rows of D elements
 
   // ---- value side: columns n = c --------------------------------------------
+  // Every global read of this phase is issued at once, as raw bits converted
+  // at use, so the phase waits for memory once: the S and dS' columns of the
+  // two B operands (k = c), and v and dO of this column (rows past the
+  // chunk's end re-read its last row and are masked at use).
+  float sraw[KD][KPL], draw[KD][KPL];
+  uint32_t vraw[4][4], oraw[4][4];
+#pragma unroll
+  for (int ks = 0; ks < KD; ++ks)
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+      const int cc = ks * M::KSTEP + KPL * grp + e;
+      sraw[ks][e] = S[cc * D + c];
+      draw[ks][e] = dS[cc * D + c];
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = tok(min(16 * t + 4 * grp + j, loc.len - 1)) * D + c;
+      vraw[t][j] = ld_raw(vb + off);
+      oraw[t][j] = ld_raw(ob + off);
+    }
   // Kp S, then R = Diag(beta)(V - Kp S) and W = T R
   f32x4_t vmk[4], acc[4], w[4];
   {
     typename M::frag sb[KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) sb[ks] = gfrag_cm<T>(S, D, c, ks, lane);
+    for (int ks = 0; ks < KD; ++ks) sb[ks] = to_frag(sraw[ks], T{});
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
@@ -697,7 +731,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * t + 4 * grp + j;
-        const float vv = r < loc.len ? ld_f(vb + tok(r) * D + c) : 0.f;
+        const float vv = r < loc.len ? raw_val<T>(vraw[t][j]) : 0.f;
         vmk[t][j] = vv - a[j];
         acc[t][j] = sm.beta[r] * vmk[t][j];
       }
@@ -718,7 +752,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      dov[t][j] = r < loc.len ? scale * ld_f(ob + tok(r) * D + c) : 0.f;
+      dov[t][j] = r < loc.len ? scale * raw_val<T>(oraw[t][j]) : 0.f;
       st_f(sm.wb + r * LDX + c, w[t][j]);
       st_f(sm.dob + r * LDX + c, dov[t][j]);
     }
@@ -726,7 +760,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   {
     typename M::frag dsb[KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) dsb[ks] = gfrag_cm<T>(dS, D, c, ks, lane);
+    for (int ks = 0; ks < KD; ++ks) dsb[ks] = to_frag(draw[ks], T{});
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
