@@ -614,7 +614,7 @@ template <> struct BufStore4<float> {
 };
 
 // Per-wave fragments of one chunk's record (see kda_state_pass).
-template <typename T, int D, int WS>
+template <typename T, int D, int WS, bool OUT>
 struct K2Frags {
   using M = Mma<T>;
   using R = Rec<T, D>;
@@ -666,13 +666,15 @@ struct K2Frags {
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
     load_part<0>(r, soff, o);
-    load_part<1>(r, soff, o);
+    if constexpr (OUT) load_part<1>(r, soff, o);
     load_part<2>(r, soff, o);
-    load_part<3>(r, soff, o);
+    if constexpr (OUT) load_part<3>(r, soff, o);
   }
 };
 
-template <typename T, int D, int WS>
+// OUT = false (the forward run inside the backward): no output, so neither
+// Q o e^G nor P is loaded and O is not formed.
+template <typename T, int D, int WS, bool OUT>
 __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
     int nseg, int64_t seg_slots, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
@@ -680,7 +682,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     float* __restrict__ states, float scale, T* __restrict__ o) {
   using M = Mma<T>;
   using R = Rec<T, D>;
-  using F = K2Frags<T, D, WS>;
+  using F = K2Frags<T, D, WS, OUT>;
   constexpr int NB = F::NB, CBW = F::CBW, KD = F::KD, KC = F::KC;
   constexpr int LDS_S = D + 8, LDS_W = kC + 8;
   __shared__ __align__(16) char lds_raw[(WS * LDS_S + WS * LDS_W) * sizeof(T)];
@@ -774,6 +776,21 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   };
 
   auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
+  // For the backward: the state entering chunk slot s0 + j, [slot][H][dk][dv]
+  // fp32.  Written at the end of the step before (after that step's
+  // prefetch loads: the wait counter is in order, so a store issued before
+  // them would hold up every wait for them).
+  auto store_state = [&](int j) {
+    float* sd = states + ((s0 + j) * H + h) * (int64_t)D * D + n0 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sd[((wave * CBW + i) * 16 + 4 * (lane >> 4) + e) * D + nb * 16] = S[i][nb][e];
+  };
+  if (states != nullptr) store_state(j0);
   // One chunk step: consumes the fragments in f and fills fn with those of
   // record jn (clamped to the last record), the loads spread over the step.
   auto step = [&](const F& f, F& fn, int j, int jn) {
@@ -781,8 +798,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     const int ci = j + cdelta;  // chunk index within the sequence
     const int len = ci == ci_last ? len_last : kC;
 
-    // (a) S -> LDS as S^T in the MFMA type (and, for the backward, the
-    // state entering every chunk to `states`, [slot][H][dk][dv] fp32)
+    // (a) S -> LDS as S^T in the MFMA type
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
 #pragma unroll
@@ -791,16 +807,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
         const int n = nb * 16 + (lane & 15);
         st_perm4(sSt + n * LDS_S, c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
       }
-    if (states != nullptr) {
-      float* sd = states + ((s0 + j) * H + h) * (int64_t)D * D + n0 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < CBW; ++i)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sd[((wave * CBW + i) * 16 + 4 * (lane >> 4) + e) * D + nb * 16] = S[i][nb][e];
-    }
     __syncthreads();
 
     // (b) W = U + (-Wk) S for this wave's 16 rows -- the chain's critical
@@ -820,15 +826,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       for (int nb = 0; nb < NB; ++nb) W[nb] = M::mma(f.wn[ks], sfr[nb][ks], W[nb]);
     __builtin_amdgcn_sched_barrier(0);
     fn.template load_part<0>(rsrc, son, offs);
-    store_o();
+    if constexpr (OUT) {
+      store_o();
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks)
+      for (int ks = 0; ks < KD; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(sfr[nb][ks], f.qg[ks], O[nb]);
-    __builtin_amdgcn_sched_barrier(0);
-    fn.template load_part<1>(rsrc, son, offs);
+        for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(sfr[nb][ks], f.qg[ks], O[nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      fn.template load_part<1>(rsrc, son, offs);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // (c) W -> LDS as W^T
@@ -858,13 +866,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     __builtin_amdgcn_sched_barrier(0);
     fn.template load_part<2>(rsrc, son, offs);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (OUT) {
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks)
+      for (int ks = 0; ks < KC; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(wf[nb][ks], f.p[ks], O[nb]);
-    __builtin_amdgcn_sched_barrier(0);
-    fn.template load_part<3>(rsrc, son, offs);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int nb = 0; nb < NB; ++nb) O[nb] = M::mma(wf[nb][ks], f.p[ks], O[nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      fn.template load_part<3>(rsrc, son, offs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (states != nullptr && j + 1 < j1) store_state(j + 1);
 
     // (e) checkpoint after every ckpt_every tokens (dense, chunk-aligned)
     if (ckpt != nullptr && --ck_left == 0) {
@@ -910,7 +921,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   }
   if (j < j1) step(fa, fc, j, j + 2);
   if (j + 1 < j1) step(fb, fa, j + 1, j + 3);
-  store_o();
+  if constexpr (OUT) store_o();
 
   if (dst != nullptr) {
 #pragma unroll
@@ -1026,7 +1037,8 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                          stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
                          s1 - s0, d.qk_l2norm, recs);
     }
-    hipLaunchKernelGGL((kda_state_pass<T, D, WS>), dim3(nhpad * nslice), dim3(kThreads), 0,
+    auto k2 = o ? kda_state_pass<T, D, WS, true> : kda_state_pass<T, D, WS, false>;
+    hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(kThreads), 0,
                        stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,
                        carry, final_state, ckpt, d.ckpt_every, nck, states, d.scale, (T*)o);
     hipError_t e = hipGetLastError();

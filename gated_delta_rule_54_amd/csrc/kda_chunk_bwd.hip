@@ -602,15 +602,21 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
           f.od[ks][e] = __builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0);
       }
   };
+  // dS' of chunk ci (the gradient of the state leaving it) for kda_bwd_intra:
+  // stored once it is formed, after the step's prefetch loads were issued
+  // (the wait counter is in order; an earlier store would hold up the waits)
+  auto store_ds = [&](int ci) {
+    float* dst = dstates + ((sp.c0 + ci) * H + h) * (int64_t)D * D + n;
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[((wave * CBW + i) * 16 + 4 * grp + j) * D] = dS[i][j];
+  };
   auto step = [&](const F& f, int ci, int buf) {
-    const int64_t slot = sp.c0 + ci;
-    float* dst = dstates + (slot * H + h) * (int64_t)D * D + n;
     T* sb = sD[buf];
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       const int c4 = (wave * CBW + i) * 16 + 4 * grp;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(c4 + j) * D] = dS[i][j];
       st_perm4(sb + (lane & 15) * LDS_S, c4, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
     }
     __syncthreads();
@@ -626,22 +632,31 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
       for (int ks = 0; ks < KD; ++ks) acc = M::mma(f.mf[i][ks], bfr[ks], acc);
       dS[i] = acc;
     }
+    if (ci > 0) store_ds(ci - 1);
     // No second barrier: the next chunk writes the other buffer, and this
     // buffer is rewritten only after the next chunk's barrier, which every
     // wave reaches after its reads of this one.
   };
-  // two register sets, each chunk's record prefetched one chunk ahead
-  F fa, fb;
+  // Three register sets: each chunk's record is prefetched two chunks ahead
+  // (clamped at the first chunk, so every load is unconditional), and the
+  // loop body is three whole steps so each set stays in fixed registers.
+  // Steps alternate the two LDS buffers.
+  F fa, fb, fc;
   load(fa, nch - 1);
+  load(fb, max(nch - 2, 0));
+  store_ds(nch - 1);
   int s = 0;
-  for (; s + 2 <= nch; s += 2) {
+  for (; s + 3 <= nch; s += 3) {
     const int ci = nch - 1 - s;
-    load(fb, ci - 1);
-    step(fa, ci, 0);
-    load(fa, max(ci - 2, 0));
-    step(fb, ci - 1, 1);
+    load(fc, max(ci - 2, 0));
+    step(fa, ci, s & 1);
+    load(fa, max(ci - 3, 0));
+    step(fb, ci - 1, (s + 1) & 1);
+    load(fb, max(ci - 4, 0));
+    step(fc, ci - 2, s & 1);
   }
-  if (s < nch) step(fa, nch - 1 - s, 0);
+  if (s < nch) step(fa, nch - 1 - s, s & 1);
+  if (s + 1 < nch) step(fb, nch - 2 - s, (s + 1) & 1);
   if (dinit != nullptr) {
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
