@@ -116,3 +116,23 @@ def test_bwd_8k_windows():
             assert_close(f"{name} window {a}", gx, r[:, warm:warm + win], TOL[w.dtype])
     for x in got:
         assert torch.isfinite(x).all()
+
+
+def test_bwd_no_tokens():
+    """T = 0: nothing flows to the inputs; d_init_state = d_final_state."""
+    inp = _inputs(2, 0, 2, 64, torch.bfloat16, seed=2801)
+    up = _up(inp, 2802)
+    dq, dk, dv, dg, db, dinit = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"],
+                                              inp["beta"], up["do"], inp["init_state"],
+                                              up["dfinal"])
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and dg.numel() == 0 and db.numel() == 0
+    assert torch.equal(dinit, up["dfinal"])
+
+
+def test_bwd_fp32_gate_per_head_varlen():
+    """fp32 operands, one gate per (token, head), varlen packing with a
+    sequence boundary inside a chunk."""
+    inp = _inputs(1, 0, 3, 64, torch.float32, seed=2901, lengths=[37, 91, 64],
+                  gate_per_head=True)
+    _run(inp, _up(inp, 2902), torch.float32, per_head=True, label="fp32 GDN varlen")
