@@ -453,7 +453,7 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are "
-                                   "not part of this build (--gpus must be 1)"}))
+                                   "not supported by this benchmark (--gpus must be 1)"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
