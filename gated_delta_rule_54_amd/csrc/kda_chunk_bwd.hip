@@ -432,8 +432,8 @@ template <typename T, int D, bool GS>
 __global__ __launch_bounds__((BwdLds<T, D>::NT), 1)
 __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, ChunkGeom gm, int H, int64_t nslot, int qk_l2norm,
-    float scale, char* __restrict__ brec) {
+    const float* __restrict__ beta, ChunkGeom gm, int H, int64_t nslot, int64_t slot_base,
+    int qk_l2norm, float scale, char* __restrict__ brec) {
   using L = BwdLds<T, D, true>;
   using M = Mma<T>;
   using RC = BRec<T, D>;
@@ -441,7 +441,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
   constexpr int KC = kC / M::KSTEP, KD = D / M::KSTEP;
   extern __shared__ __align__(16) char smem[];
   const int h = blockIdx.x;
-  const int64_t slot = blockIdx.y;
+  const int64_t slot = slot_base + blockIdx.y;
   ChunkLoc loc;
   if (!locate(gm, slot, loc)) return;
   BwdSmem<T, D, true> sm(smem);
@@ -676,7 +676,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ d_o,
     const float* __restrict__ states, const float* __restrict__ dstates, ChunkGeom gm, int H,
-    int qk_l2norm, float scale, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    int64_t slot_base, int qk_l2norm, float scale, T* __restrict__ dq, T* __restrict__ dk,
+    T* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta) {
   using L = BwdLds<T, D>;
   using M = Mma<T>;
@@ -684,7 +685,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   constexpr int KC = kC / M::KSTEP, KD = D / M::KSTEP, KPL = M::KPL;
   extern __shared__ __align__(16) char smem[];
   const int h = blockIdx.x;
-  const int64_t slot = blockIdx.y;
+  const int64_t slot = slot_base + blockIdx.y;
   ChunkLoc loc;
   if (!locate(gm, slot, loc)) return;
   BwdSmem<T, D> sm(smem);
@@ -1102,22 +1103,25 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
     }
     attr_set = true;
   }
-  if (nslot > 0) {
-    auto prep = d.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
-    hipLaunchKernelGGL(prep, dim3(H, (unsigned)nslot), dim3(LP::NT), LP::BYTES, stream,
-                       (const T*)q, (const T*)k, g, beta, gm, H, nslot, d.qk_l2norm, d.scale,
-                       recs);
+  // chunk slots go in the grid's y dimension, at most kMaxGridY per launch
+  constexpr int64_t kMaxGridY = 32768;
+  auto prep = d.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
+  for (int64_t sb = 0; sb < nslot; sb += kMaxGridY) {
+    const unsigned ny = (unsigned)std::min<int64_t>(kMaxGridY, nslot - sb);
+    hipLaunchKernelGGL(prep, dim3(H, ny), dim3(LP::NT), LP::BYTES, stream, (const T*)q,
+                       (const T*)k, g, beta, gm, H, nslot, sb, d.qk_l2norm, d.scale, recs);
   }
   const int nslice = D / kBwdSliceW;
   const int nhpad = (NH + 7) / 8 * 8;
   hipLaunchKernelGGL((kda_bwd_state_pass<T, D>), dim3(nhpad * nslice), dim3(kBwdPassThreads), 0,
                      stream, recs, nslot, gm, H, NH, nslice, (const T*)d_o, d_final, dstates,
                      d_init);
-  if (nslot > 0) {
-    auto intra = d.gate_per_head ? kda_bwd_intra<T, D, true> : kda_bwd_intra<T, D, false>;
-    hipLaunchKernelGGL(intra, dim3(H, (unsigned)nslot), dim3(L::NT), L::BYTES, stream,
-                       (const T*)q, (const T*)k, (const T*)v, g, beta, (const T*)d_o, states,
-                       dstates, gm, H, d.qk_l2norm, d.scale, (T*)dq, (T*)dk, (T*)dv, dg, dbeta);
+  auto intra = d.gate_per_head ? kda_bwd_intra<T, D, true> : kda_bwd_intra<T, D, false>;
+  for (int64_t sb = 0; sb < nslot; sb += kMaxGridY) {
+    const unsigned ny = (unsigned)std::min<int64_t>(kMaxGridY, nslot - sb);
+    hipLaunchKernelGGL(intra, dim3(H, ny), dim3(L::NT), L::BYTES, stream, (const T*)q,
+                       (const T*)k, (const T*)v, g, beta, (const T*)d_o, states, dstates, gm, H,
+                       sb, d.qk_l2norm, d.scale, (T*)dq, (T*)dk, (T*)dv, dg, dbeta);
   }
   return hipGetLastError();
 }

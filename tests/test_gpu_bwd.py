@@ -136,3 +136,87 @@ def test_bwd_fp32_gate_per_head_varlen():
     inp = _inputs(1, 0, 3, 64, torch.float32, seed=2901, lengths=[37, 91, 64],
                   gate_per_head=True)
     _run(inp, _up(inp, 2902), torch.float32, per_head=True, label="fp32 GDN varlen")
+
+
+def test_bwd_varlen_full_size():
+    """16 sequences, lengths U[1024, 32768], 32 heads, d = 128, bf16, nonzero
+    initial states: one whole (sequence, head) chain per sequence through the
+    oracle's gradients (every token of those chains compared)."""
+    w = W.VARLEN_16
+    inp = W.workload_inputs(w, DEV)
+    up = _up(inp, 3001)
+    cu = inp["cu_seqlens"]
+    got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                        inp["init_state"], up["dfinal"], cu)
+    torch.cuda.synchronize()
+    cuh = cu.cpu().numpy().astype(np.int64)
+    N, H = w.num_seqs, w.heads
+    heads = np.random.default_rng(11).integers(0, H, N)
+    print(f"  total tokens {cuh[-1]}, heads {heads.tolist()}", flush=True)
+    keys = ("q", "k", "v", "g", "beta")
+    parts = {key: [] for key in keys + ("do",)}
+    for n in range(N):
+        a, b, h = int(cuh[n]), int(cuh[n + 1]), int(heads[n])
+        for key in keys:
+            parts[key].append(inp[key][:, a:b, h:h + 1].cpu())
+        parts["do"].append(up["do"][:, a:b, h:h + 1].cpu())
+    cat = {key: torch.cat(v, dim=1).contiguous() for key, v in parts.items()}
+    pick = lambda x: torch.stack([x[n, int(heads[n])] for n in range(N)]).unsqueeze(1).cpu()
+    ref = O.kda_bwd(*(cat[key] for key in keys), cat["do"], pick(inp["init_state"]),
+                    pick(up["dfinal"]), cuh.astype(np.int32))
+    for i, (name, x) in enumerate(zip(NAMES, got)):
+        if name == "dinit":
+            gx = torch.stack([x[n, int(heads[n])] for n in range(N)]).unsqueeze(1)
+        else:
+            gx = torch.cat([x[:, int(cuh[n]):int(cuh[n + 1]), int(heads[n]):int(heads[n]) + 1]
+                            for n in range(N)], dim=1)
+        assert torch.isfinite(x).all(), name
+        assert_close(f"{name} (16 whole chains)", gx, ref[i], TOL[w.dtype])
+
+
+def test_bwd_1m_windows():
+    """B=1, H=32, T=1,048,576, d=128, bf16 (16 forward segments, a 16384-chunk
+    reverse pass): gradients of two 256-token windows on four heads against
+    the oracle run on [a-2048, a+256+2048) with zero state and zero final
+    gradient (the forgetting licence covers both truncations)."""
+    w = W.PREFILL_1M
+    inp = W.workload_inputs(w, DEV)
+    up = W.upstream_grads(batch=1, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
+                          num_seqs=1, dtype=w.dtype, device=DEV, seed=3101, final=False)
+    got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                        want_dinit=False)
+    torch.cuda.synchronize()
+    heads = [3, 17, 30]
+    warm, win = 2048, 256
+    for a in (200_000 + 37, w.seqlen - 3000):
+        lo, hi = a - warm, min(a + win + warm, w.seqlen)
+        print(f"  window [{a}, {a + win}) on heads {heads}", flush=True)
+        sl = lambda x: x[:, lo:hi][:, :, heads].contiguous().cpu()
+        ref = O.kda_bwd(*(sl(inp[key]) for key in ("q", "k", "v", "g", "beta")), sl(up["do"]))
+        for name, x, r in zip(NAMES[:5], got[:5], ref[:5]):
+            gx = x[:, a:a + win][:, :, heads]
+            assert_close(f"{name} window {a}", gx, r[:, warm:warm + win], TOL[w.dtype])
+    for x in got[:5]:
+        assert torch.isfinite(x).all()
+
+
+def test_bwd_more_chunks_than_one_launch():
+    """One head, d = 64, T = 2,105,000 tokens: 32,891 chunk slots, more than
+    one launch of the per-chunk kernels covers (32,768).  A window straddling
+    slot 32,768 and one at the end, against the oracle on a 2048-token
+    margin each side."""
+    T = 2_105_000
+    inp = _inputs(1, T, 1, 64, torch.bfloat16, seed=3201, init="zeros")
+    up = _up(inp, 3202, final=False)
+    got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                        want_dinit=False)
+    torch.cuda.synchronize()
+    warm, win = 2048, 256
+    for a in (32768 * 64 - 100, T - 300):
+        lo, hi = a - warm, min(a + win + warm, T)
+        print(f"  window [{a}, {a + win})", flush=True)
+        sl = lambda x: x[:, lo:hi].contiguous().cpu()
+        ref = O.kda_bwd(*(sl(inp[key]) for key in ("q", "k", "v", "g", "beta")), sl(up["do"]))
+        for name, x, r in zip(NAMES[:5], got[:5], ref[:5]):
+            assert_close(f"{name} window {a}", x[:, a:a + win], r[:, warm:warm + win],
+                         TOL[torch.bfloat16])
