@@ -91,6 +91,25 @@ template <> struct Raw2<bf16> {
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
 };
+// Two consecutive elements as raw bits through a non-temporal load: for
+// inputs read once, so that they do not displace data that is read again
+// soon (the chunk records the state pass reads right after) in the caches.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <typename T> struct RawNt2;
+template <> struct RawNt2<float> {
+  f32x2_t v;
+  __device__ __forceinline__ void load(const float* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const f32x2_t*>(p));
+  }
+  __device__ __forceinline__ float2 get() const { return make_float2(v[0], v[1]); }
+};
+template <> struct RawNt2<bf16> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const bf16* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+  __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
+};
 // Load N consecutive elements (16-byte aligned, N a multiple of 8) as floats.
 template <int N>
 __device__ __forceinline__ void ld_seg(const float* p, float* out) {
