@@ -186,11 +186,25 @@ __device__ __forceinline__ uint32_t ld_raw(const bf16* p) {
   return *reinterpret_cast<const uint16_t*>(p);
 }
 __device__ __forceinline__ uint32_t ld_raw(const float* p) { return __float_as_uint(*p); }
+__device__ __forceinline__ uint32_t ld_raw_nt(const bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+__device__ __forceinline__ uint32_t ld_raw_nt(const float* p) {
+  return __float_as_uint(__builtin_nontemporal_load(p));
+}
 template <typename T>
 __device__ __forceinline__ float raw_val(uint32_t b) {
   if constexpr (sizeof(T) == 2) return bf_val(b);
   else return __uint_as_float(b);
 }
+
+// Gradient outputs are written once and read by nobody here: non-temporal
+// stores, so they do not push out of the caches the chunk's S, dS', k, q and
+// g that the workgroup reads again.
+__device__ __forceinline__ void st_nt(bf16* p, float x) {
+  __builtin_nontemporal_store(bf_bits(x), reinterpret_cast<uint16_t*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, float x) { __builtin_nontemporal_store(x, p); }
 
 // Sum over the 16 lanes of a lane group (the 16 columns of an accumulator).
 __device__ __forceinline__ float sum16(float x) {
@@ -269,7 +283,8 @@ struct BwdRegs {
 };
 
 // Raw k, q, g of this lane's column and rows (zero past the chunk's end).
-template <typename T, int D, bool GS>
+// NTL: read non-temporally (the caller reads them once).
+template <typename T, int D, bool GS, bool NTL = false>
 __device__ __forceinline__ void load_cols(const T* __restrict__ q, const T* __restrict__ k,
                                           const float* __restrict__ g, const ChunkLoc& loc, int H,
                                           int h, int c, int grp, BwdRegs& R, float (&gr)[4][4]) {
@@ -285,9 +300,16 @@ __device__ __forceinline__ void load_cols(const T* __restrict__ q, const T* __re
       const int r = 16 * t + 4 * grp + j;
       const int off = min(r, loc.len - 1) * H * D + c;
       const bool ok = r < loc.len;
-      R.kh[t][j] = ok ? ld_f(kb + off) : 0.f;
-      R.qh[t][j] = ok ? ld_f(qb + off) : 0.f;
-      gr[t][j] = ok ? (GS ? gb[min(r, loc.len - 1) * H] : gb[off]) : 0.f;
+      const float* gp = GS ? gb + min(r, loc.len - 1) * H : gb + off;
+      if constexpr (NTL) {
+        R.kh[t][j] = ok ? raw_val<T>(ld_raw_nt(kb + off)) : 0.f;
+        R.qh[t][j] = ok ? raw_val<T>(ld_raw_nt(qb + off)) : 0.f;
+        gr[t][j] = ok ? __builtin_nontemporal_load(gp) : 0.f;
+      } else {
+        R.kh[t][j] = ok ? ld_f(kb + off) : 0.f;
+        R.qh[t][j] = ok ? ld_f(qb + off) : 0.f;
+        gr[t][j] = ok ? *gp : 0.f;
+      }
     }
 }
 
@@ -321,7 +343,7 @@ __device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdR
 // the gated operands in LDS (K~ left to the caller in the compact layout), A
 // and P, T = (I + A)^-1 (times Diag(beta) when TBETA) in the MFMA type.  Bm receives this wave's tiles of Kp Km^T
 // (tile p = wave + NW * tt: rows 16(p/4), columns 16(p%4)).
-template <typename T, int D, bool GS, bool TBETA, bool COMPACT>
+template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false>
 __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
                                              const float* __restrict__ g,
                                              const float* __restrict__ beta, const ChunkLoc& loc,
@@ -334,7 +356,7 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
   float gr[4][4];
-  load_cols<T, D, GS>(q, k, g, loc, H, h, c, grp, R, gr);
+  load_cols<T, D, GS, NTL>(q, k, g, loc, H, h, c, grp, R, gr);
   if (tid < kC) sm.beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
   // row norms: over this wave's 16 columns, then over the waves
 #pragma unroll
@@ -447,7 +469,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
   BwdSmem<T, D, true> sm(smem);
   BwdRegs R;
   f32x4_t Bm[NTW];
-  bwd_prologue<T, D, GS, true, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  bwd_prologue<T, D, GS, true, true, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
   // K~ into the region the inverse has finished with
@@ -729,8 +751,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = tok(min(16 * t + 4 * grp + j, loc.len - 1)) * D + c;
-      vraw[t][j] = ld_raw(vb + off);
-      oraw[t][j] = ld_raw(ob + off);
+      vraw[t][j] = ld_raw_nt(vb + off);
+      oraw[t][j] = ld_raw_nt(ob + off);
     }
   // Kp S, then R = Diag(beta)(V - Kp S) and W = T R
   f32x4_t vmk[4], acc[4], w[4];
@@ -801,7 +823,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      if (r < loc.len) st_f(dvb + tok(r) * D + c, sm.beta[r] * lam[t][j]);
+      if (r < loc.len) st_nt(dvb + tok(r) * D + c, sm.beta[r] * lam[t][j]);
       const float part = sum16(lam[t][j] * vmk[t][j]);
       if ((lane & 15) == 0) sm.red[wave * kC + r] = part;
     }
@@ -996,7 +1018,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     }
     sm.x1[tid] = a;
     sm.x2[tid] = b;
-    if (tid < loc.len) dbb[tok(tid)] = sm.x0[tid];
+    if (tid < loc.len) st_nt(dbb + tok(tid), sm.x0[tid]);
   }
   __syncthreads();
   const T* qrow = q + row0 * D;
@@ -1012,9 +1034,9 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
         gq = sm.rq[r] * (gq - sm.x2[r] * qn);
       }
       if (r < loc.len) {
-        st_f(dkb + tok(r) * D + c, gk);
-        st_f(dqb + tok(r) * D + c, gq);
-        if (!GS) dgb[tok(r) * D + c] = dgo[t][j];
+        st_nt(dkb + tok(r) * D + c, gk);
+        st_nt(dqb + tok(r) * D + c, gq);
+        if (!GS) st_nt(dgb + tok(r) * D + c, dgo[t][j]);
       }
     }
   if constexpr (GS) {
@@ -1031,7 +1053,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       float a = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) a += sm.red[w2 * kC + tid];
-      dgb[tok(tid)] = a;
+      st_nt(dgb + tok(tid), a);
     }
   }
 }
