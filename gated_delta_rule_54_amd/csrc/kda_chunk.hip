@@ -91,9 +91,10 @@ struct Rec {
 //   region 1: Q o e^G (row-major) [exact path: raw q]  -> A (fp32)     -> T Diag(beta)
 //   region 2: K o e^-G (row-major) / exact-path staging -> T (fp32)
 //   region 3: (K o e^G)^T
-// Thread layouts: "row" (NQ consecutive threads per row) for the q/k norms,
-// and "channel pair" (tid = cp + (D/2) part): two adjacent channels of RPP
-// consecutive rows, for everything per-element.  A channel-pair thread holds
+// Thread layout "channel pair" (tid = cp + (D/2) part): two adjacent channels
+// of RPP consecutive rows.  The D/2 threads of a part hold whole rows (one
+// wave at d = 128, half a wave at d = 64), so the q/k row norms are reduced
+// across lanes without a second read of q and k.  A channel-pair thread holds
 // its rows contiguously, so the transposed LDS tiles ((K o e^G)^T, V^T) are
 // written 8 rows at a time with 16-byte stores.  The operand-order record
 // blocks of Q o e^G and K~ are gathered from LDS on the bf16 fast path (whole
@@ -163,8 +164,6 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   using R = Rec<T, D>;
   constexpr int NCP = L::NCP, NPART = L::NPART, RPP = L::RPP;
   constexpr int NT = k1_threads<T, D>(), NW = NT / 64;  // threads, waves
-  constexpr int NQ = NT / kC;  // threads per row in the norm layout
-  constexpr int QC = D / NQ;   // channels per thread in the norm layout
   extern __shared__ __align__(16) char smem[];
   T* r0 = reinterpret_cast<T*>(smem);
   T* r1 = reinterpret_cast<T*>(smem + L::REG);
@@ -204,20 +203,16 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   const int cp = tid % NCP, part = tid / NCP;
   const int c0 = 2 * cp, r0p = part * RPP;
   // Loads are issued tensor by tensor in the order they are consumed (g for
-  // the scan, k and the norm rows, then q, then v last, which is needed only
-  // after A and P): the wait counter is in-order, so each use then waits
-  // only for the loads it needs.  g and v, read once, are loaded
-  // non-temporally: the chunk records this kernel writes are what the state
-  // pass reads next, and these inputs streaming past would otherwise push
-  // them out of the last-level cache (measured: the state pass 67 -> 60 us
-  // per segment).  q and k stay cached for the norm rows' second read.
+  // the scan, k and q for the norms, then v last, which is needed only after
+  // A and P): the wait counter is in-order, so each use then waits only for
+  // the loads it needs.  g and v are loaded non-temporally: the chunk
+  // records this kernel writes are what the state pass reads next, and these
+  // inputs streaming past would otherwise push them out of the last-level
+  // cache (measured: the state pass 67 -> 60 us per segment).
   RawNt2<float> graw[RPP];
   float gsc[RPP];  // GS: the row's one gate
   Raw2<T> kraw[RPP], qraw[RPP];
   RawNt2<T> vraw[RPP];
-  const int nr = tid / NQ, nq = tid % NQ;  // row layout for the norms
-  const int rr = min(nr, loc.len - 1);
-  Raw4<T> nqr[QC / 4], nkr[QC / 4];
 #pragma unroll
   for (int j = 0; j < RPP; ++j) {
     if constexpr (GS)
@@ -227,17 +222,11 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   }
 #pragma unroll
   for (int j = 0; j < RPP; ++j) kraw[j].load(kb + min(r0p + j, loc.len - 1) * rowstride + c0);
-  // the norm rows are a second, cache-served read of k and q
-#pragma unroll
-  for (int j = 0; j < QC / 4; ++j) nkr[j].load(kb + rr * rowstride + nq * QC + 4 * j);
-#pragma unroll
-  for (int j = 0; j < QC / 4; ++j) nqr[j].load(qb + rr * rowstride + nq * QC + 4 * j);
 #pragma unroll
   for (int j = 0; j < RPP; ++j) qraw[j].load(qb + min(r0p + j, loc.len - 1) * rowstride + c0);
 #pragma unroll
   for (int j = 0; j < RPP; ++j) vraw[j].load(vb + min(r0p + j, loc.len - 1) * rowstride + c0);
   if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
-  // rows past the chunk's end read as zero (g = 0 keeps the prefix sum flat)
   auto row_ok = [&](int j) { return r0p + j < loc.len; };
   float2 G[RPP];
 #pragma unroll
@@ -245,24 +234,48 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
     const float2 gj = GS ? make_float2(gsc[j], gsc[j]) : graw[j].get();
     G[j] = row_ok(j) ? gj : make_float2(0.f, 0.f);
   }
-  {
-    float sq = 0.f, sk = 0.f;
-    if (nr < loc.len) {
+  float2 kk[RPP], qq[RPP];
 #pragma unroll
-      for (int j = 0; j < QC / 4; ++j) {
-        const f32x4_t a = nqr[j].get(), b = nkr[j].get();
-        sq += a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
-        sk += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+  for (int j = 0; j < RPP; ++j) {
+    kk[j] = row_ok(j) ? kraw[j].get() : make_float2(0.f, 0.f);
+    qq[j] = row_ok(j) ? qraw[j].get() : make_float2(0.f, 0.f);
+  }
+  // Row norms: the 2 RPP squared partial sums (q rows, then k rows) of the
+  // D/2 lanes of a part, reduced by a butterfly that halves the values each
+  // lane keeps at every step (reduce-scatter) and then sums the last one
+  // over the remaining lanes; lane bits name the value a lane ends with.
+  {
+    constexpr int V = 2 * RPP;
+    static_assert(V <= NCP, "one value per lane after the reduce-scatter");
+    float x[V];
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) {
+      x[j] = qq[j].x * qq[j].x + qq[j].y * qq[j].y;
+      x[RPP + j] = kk[j].x * kk[j].x + kk[j].y * kk[j].y;
+    }
+    int idx = 0;
+#pragma unroll
+    for (int s = 0; (NCP >> (s + 1)) >= 1; ++s) {
+      const int o = NCP >> (s + 1);
+      const int cnt = (V >> s) >= 2 ? (V >> s) : 1;
+      if (cnt > 1) {
+        const int half = cnt / 2;
+        const bool up = (lane & o) != 0;
+#pragma unroll
+        for (int t = 0; t < half; ++t) {
+          const float send = up ? x[t] : x[half + t];
+          const float keep = up ? x[half + t] : x[t];
+          x[t] = keep + __shfl_xor(send, o);
+        }
+        if (up) idx += half;
+      } else {
+        x[0] += __shfl_xor(x[0], o);
       }
     }
-#pragma unroll
-    for (int off = 1; off < NQ; off <<= 1) {
-      sq += __shfl_xor(sq, off);
-      sk += __shfl_xor(sk, off);
-    }
-    if (nq == 0) {
-      s_rq[nr] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
-      s_rk[nr] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
+    constexpr int LOWMASK = NCP / V - 1;
+    if ((lane & LOWMASK) == 0) {
+      const float rn = qk_l2norm ? rsqrtf(x[0] + kNormEps) : 1.f;
+      if (idx < RPP) s_rq[r0p + idx] = rn; else s_rk[r0p + idx - RPP] = rn;
     }
   }
   // ---- in-chunk prefix sum of g ---------------------------------------------
@@ -284,12 +297,6 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
       __syncthreads_or(gamma.x < kFastDecayBound || gamma.y < kFastDecayBound) != 0;
 
   // ---- operands ---------------------------------------------------------------
-  float2 kk[RPP], qq[RPP];
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    kk[j] = row_ok(j) ? kraw[j].get() : make_float2(0.f, 0.f);
-    qq[j] = row_ok(j) ? qraw[j].get() : make_float2(0.f, 0.f);
-  }
   const float2 eg_gamma = make_float2(__expf(gamma.x), __expf(gamma.y));
   // bf16 records on the fast path take Q o e^G and K~ from LDS below, in
   // whole operand fragments; otherwise every thread stores its own values
