@@ -86,43 +86,51 @@ struct Rec {
 };
 
 // ---------------------------------------------------------------------------
-// K1: intra-chunk transform.  LDS holds four equal regions, reused by phase:
-//   region 0: K o e^G (row-major) [exact path: raw k]  -> V^T           (U phase)
-//   region 1: Q o e^G (row-major) [exact path: raw q]  -> A (fp32)     -> T Diag(beta)
-//   region 2: K o e^-G (row-major) / exact-path staging -> T (fp32)
-//   region 3: (K o e^G)^T
+// K1: intra-chunk transform.  LDS holds three equal regions, reused by phase:
+//   region 0: K o e^G (row-major) [exact path: raw k]  -> V^T          (U phase)
+//   region 1: Q o e^G (row-major) [exact path: raw q]  -> A (fp32)    -> (K o e^G)^T
+//   region 2: scan partials -> K o e^-G (row-major) / exact-path staging
+//             -> T (fp32) -> T Diag(beta)
+// (K o e^G)^T is computed with the other operands but held in registers
+// until A is dead.  Three regions (~52 KiB at d = 128) let three workgroups
+// share a CU, where four allowed two.
 // Thread layout "channel pair" (tid = cp + (D/2) part): two adjacent channels
 // of RPP consecutive rows.  The D/2 threads of a part hold whole rows (one
 // wave at d = 128, half a wave at d = 64), so the q/k row norms are reduced
 // across lanes without a second read of q and k.  A channel-pair thread holds
 // its rows contiguously, so the transposed LDS tiles ((K o e^G)^T, V^T) are
-// written 8 rows at a time with 16-byte stores.  The operand-order record
-// blocks of Q o e^G and K~ are gathered from LDS on the bf16 fast path (whole
-// 1 KiB blocks per wave) and stored per thread otherwise.
-// K1 workgroup size.  LDS (~77 KiB per workgroup at d = 128) allows two
-// workgroups per CU; 512 threads per chunk then keep 16 waves per CU in
-// flight to hide the input loads, and halve each thread's rows and
-// registers.  fp32 operands keep 256 threads (their registers are full).
+// written 8 rows at a time.  The operand-order record blocks of Q o e^G and
+// K~ are gathered from LDS on the bf16 fast path (whole 1 KiB blocks per
+// wave) and stored per thread otherwise.
+// K1 workgroup size: 512 threads for bf16 at d = 128 (more waves in flight to
+// hide the input loads, and half the rows and registers per thread); fp32
+// operands keep 256 threads (their registers are full).
 template <typename T, int D>
 constexpr int k1_threads() { return (sizeof(T) == 2 && D == 128) ? 512 : 256; }
 
 template <typename T, int D>
 struct K1Lds {
-  static constexpr int LDR = D + 8;        // row-major leading dim (elements)
-  static constexpr int LDT = kC + 8;       // transposed leading dim
+  static constexpr int LDR = D + 16 / (int)sizeof(T);  // row-major leading dim (16-byte pad)
+  // Transposed tiles (rows = channel or chunk row, 64 wide): 68 elements,
+  // so bf16 rows are only 8-byte aligned and are accessed 8 bytes at a time.
+  static constexpr int LDT = kC + 4;
   static constexpr int LDA = kC + 4;       // fp32 64x64 leading dim (16-byte rows)
   static constexpr int RM = kC * LDR * (int)sizeof(T);
   static constexpr int TR = D * LDT * (int)sizeof(T);
   static constexpr int MX = RM > TR ? RM : TR;
   static constexpr int FP = kC * LDA * 4;                     // fp32 A / T tile
   static constexpr int REG = ((MX > FP ? MX : FP) + 255) / 256 * 256;
-  static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
   static constexpr int NCP = D / 2;                        // channel pairs
   static constexpr int NPART = k1_threads<T, D>() / NCP;   // row parts
   static constexpr int RPP = kC / NPART;                   // rows per part (8 or 16)
   static_assert(RPP % 8 == 0, "transposed stores take 8 rows at a time");
-  static constexpr int BYTES = 4 * REG + 4096 /*scratch*/ + 3 * kC * 4 + 16;
+  static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
+  static_assert(NPART * D * 4 <= REG, "the scan partials must fit a region");
+  // + per row: 1/|k|, 1/|q|, beta; per channel: e^gamma
+  static constexpr int BYTES = 3 * REG + (3 * kC + D) * 4;
 };
+
+constexpr float kLog2eF = 1.44269504088896341f;  // log2(e), rounded to fp32
 
 // Pack 8 values to the MFMA type and store 16 bytes (bf16) / 32 bytes (fp32).
 __device__ __forceinline__ void st8(bf16* p, const float* x) {
@@ -134,6 +142,48 @@ __device__ __forceinline__ void st8(bf16* p, const float* x) {
 __device__ __forceinline__ void st8(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+// Eight values of one transposed-tile row segment, packed to the MFMA type
+// when computed and stored later (8-byte aligned for bf16).
+template <typename T> struct Tr8;
+template <> struct Tr8<bf16> {
+  uint32_t u[4];
+  __device__ __forceinline__ void set2(int t, float a, float b) { u[t] = pack_bf16x2(a, b); }
+  __device__ __forceinline__ void set(const float* x) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) set2(t, x[2 * t], x[2 * t + 1]);
+  }
+  __device__ __forceinline__ void store(bf16* p) const {
+    reinterpret_cast<uint2*>(p)[0] = make_uint2(u[0], u[1]);
+    reinterpret_cast<uint2*>(p)[1] = make_uint2(u[2], u[3]);
+  }
+};
+template <> struct Tr8<float> {
+  float x[8];
+  __device__ __forceinline__ void set2(int t, float a, float b) { x[2 * t] = a; x[2 * t + 1] = b; }
+  __device__ __forceinline__ void set(const float* v) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] = v[t];
+  }
+  __device__ __forceinline__ void store(float* p) const { st8(p, x); }
+};
+template <typename T>
+__device__ __forceinline__ void st8t(T* p, const float* x) {
+  Tr8<T> h;
+  h.set(x);
+  h.store(p);
+}
+// MFMA fragment of a transposed tile (rows 8-byte aligned for bf16).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_t(const T* base, int ld, int row0, int ks,
+                                                        int lane) {
+  const T* p = base + (row0 + (lane & 15)) * ld + ks * Mma<T>::KSTEP + Mma<T>::KPL * (lane >> 4);
+  if constexpr (sizeof(T) == 2) {
+    const uint2 a = reinterpret_cast<const uint2*>(p)[0], b = reinterpret_cast<const uint2*>(p)[1];
+    return __builtin_bit_cast(typename Mma<T>::frag, u32x4_t{a.x, a.y, b.x, b.y});
+  } else {
+    return Mma<T>::load(p);
+  }
 }
 // Two adjacent elements: load as floats / store from floats.
 __device__ __forceinline__ float2 ld2(const float* p) { return *reinterpret_cast<const float2*>(p); }
@@ -148,14 +198,98 @@ __device__ __forceinline__ void st2(bf16* p, float a, float b) {
   *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
 }
 
-// fp32 operands at d = 128 need every VGPR of a one-workgroup-per-CU launch.
+// Waves per SIMD the kernel is built for: three workgroups per CU (LDS
+// allows it) except fp32 at d = 128, whose registers fill a CU alone.
 template <typename T, int D>
-constexpr int k1_min_blocks() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
+constexpr int k1_waves_per_simd() {
+  return (sizeof(T) == 4 && D == 128) ? 1 : 3 * k1_threads<T, D>() / 256;
+}
+
+// Exact-decay path of A and P: each entry from its own exponent difference
+// (<= 0), with G, k^ and q^ staged in blocks of 16 channels.  k^ and q^ are
+// the row-major LDS tiles khat and qhat; G is formed again from g (as the
+// kernel forms it: the prefix sum over the thread's rows, plus the part
+// offset).  Out of line: few chunks take it, and inlined it would set the
+// register budget of the common path.  Every thread of the workgroup calls it.
+template <typename T, int D, bool GS>
+__device__ __attribute__((noinline)) void k1_exact_ap(
+    const T* khat, const T* qhat, float* stage, float* sA, const float* s_beta, T* wP,
+    const float* gb, int64_t rowstride, int H, int len, float offx, float offy) {
+  using L = K1Lds<T, D>;
+  using M = Mma<T>;
+  constexpr int NCP = L::NCP, RPP = L::RPP, NT = k1_threads<T, D>();
+  const int tid = threadIdx.x, cp = tid % NCP, part = tid / NCP;
+  const int c0 = 2 * cp, r0p = part * RPP;
+  // Thread tid takes the lower-triangle entries e = tid + m NT, e = r(r+1)/2 + i
+  // (row and column are formed again at each use, to keep registers free).
+  constexpr int NE = (kC * (kC + 1) / 2 + NT - 1) / NT;
+  auto entry_r = [&](int m) {
+    const int e = tid + m * NT;
+    int r = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= e) ++r;
+    while (r * (r + 1) / 2 > e) --r;
+    return e < kC * (kC + 1) / 2 ? r : -1;
+  };
+  auto entry_i = [&](int m, int r) { return tid + m * NT - r * (r + 1) / 2; };
+  float ea[NE], ep[NE];
+#pragma unroll
+  for (int m = 0; m < NE; ++m) { ea[m] = 0.f; ep[m] = 0.f; }
+  float* stG = stage;
+  float* stK = stG + kC * 16;
+  float* stQ = stK + kC * 16;
+  for (int cb = 0; cb < D / 16; ++cb) {
+    if (c0 / 16 == cb) {
+      float2 run = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < RPP; ++j) {
+        const int r = r0p + j, cc = c0 % 16;
+        const int rr = min(r, len - 1);
+        const float2 gj = GS ? make_float2(gb[rr * H], gb[rr * H]) : ld2(gb + rr * rowstride + c0);
+        const float2 gm = r < len ? gj : make_float2(0.f, 0.f);
+        run = j == 0 ? gm : make_float2(gm.x + run.x, gm.y + run.y);
+        stG[r * 16 + cc] = run.x + offx;
+        stG[r * 16 + cc + 1] = run.y + offy;
+        const float2 kh = ld2(khat + r * L::LDR + c0), qh = ld2(qhat + r * L::LDR + c0);
+        stK[r * 16 + cc] = kh.x; stK[r * 16 + cc + 1] = kh.y;
+        stQ[r * 16 + cc] = qh.x; stQ[r * 16 + cc + 1] = qh.y;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+      const int r = entry_r(m);
+      if (r < 0) continue;
+      const int i = entry_i(m, r);
+#pragma unroll 1
+      for (int c = 0; c < 16; ++c) {
+        const float e = __expf(stG[r * 16 + c] - stG[i * 16 + c]);
+        const float ki = stK[i * 16 + c] * e;
+        ea[m] += stK[r * 16 + c] * ki;
+        ep[m] += stQ[r * 16 + c] * ki;
+      }
+    }
+    __syncthreads();
+  }
+  // sA aliases qhat: every read of it ended at the barrier above
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int r = entry_r(m);
+    if (r < 0) continue;
+    const int i = entry_i(m, r);
+    sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[m] : 0.f;
+    st_f(wP + fnat<T>(r, i, kC / M::KSTEP), ep[m]);
+  }
+  // the exact path writes no upper-triangle entries of the diagonal blocks
+  for (int e = tid; e < kC * kC; e += NT) {
+    const int r = e >> 6, i = e & 63;
+    if (i > r && (i >> 4) == (r >> 4)) st_f(wP + fnat<T>(r, i, kC / M::KSTEP), 0.f);
+  }
+}
 
 // GS: one gate per (token, head), broadcast over the key channels (Gated
 // DeltaNet) instead of one per channel.
 template <typename T, int D, bool GS>
-__global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void kda_intra_chunk(
+__global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) void kda_intra_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
     int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws) {
@@ -168,11 +302,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   T* r0 = reinterpret_cast<T*>(smem);
   T* r1 = reinterpret_cast<T*>(smem + L::REG);
   T* r2 = reinterpret_cast<T*>(smem + 2 * L::REG);
-  T* r3 = reinterpret_cast<T*>(smem + 3 * L::REG);
-  float* scratch = reinterpret_cast<float*>(smem + 4 * L::REG);           // 1024 floats
-  float* s_rk = scratch + 1024;
+  float* s_rk = reinterpret_cast<float*>(smem + 3 * L::REG);
   float* s_rq = s_rk + kC;
   float* s_beta = s_rq + kC;
+  float* s_eg = s_beta + kC;  // e^gamma per channel
 
   // heads vary fastest across workgroups: concurrently resident workgroups
   // then read whole token rows (all heads) of neighbouring tokens
@@ -195,20 +328,34 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   float* wEG = reinterpret_cast<float*>(rec + R::BYTES_T);
 
   // ---- global loads --------------------------------------------------------
-  // Every load is unconditional (rows past the chunk's end re-read its last
-  // row and are masked afterwards) and keeps its raw bits until all loads
-  // are in flight: a load under a branch, or converted on arrival, makes the
-  // wave wait for it before issuing the next one.
+  // Every load is unconditional and keeps its raw bits until all loads are in
+  // flight: a load under a branch, or converted on arrival, makes the wave
+  // wait for it before issuing the next one.  Each input is read through a
+  // buffer resource over this chunk's rows, bounded at the end of its last
+  // valid row: rows past the chunk's end read as zero (as the method wants
+  // them), and a load's address is one 32-bit offset.
   // channel-pair layout: channels c0, c0+1 of rows r0p .. r0p+RPP-1
   const int cp = tid % NCP, part = tid / NCP;
   const int c0 = 2 * cp, r0p = part * RPP;
   // Loads are issued tensor by tensor in the order they are consumed (g for
-  // the scan, k and q for the norms, then v last, which is needed only after
-  // A and P): the wait counter is in-order, so each use then waits only for
-  // the loads it needs.  g and v are loaded non-temporally: the chunk
-  // records this kernel writes are what the state pass reads next, and these
-  // inputs streaming past would otherwise push them out of the last-level
-  // cache (measured: the state pass 67 -> 60 us per segment).
+  // the scan, then k and q for the norms; v, needed only after A and P, is
+  // loaded after the operands): the wait counter is in-order, so each use
+  // then waits only for the loads it needs.  g and v are loaded
+  // non-temporally: the chunk records this kernel writes are what the state
+  // pass reads next, and these inputs streaming past would otherwise push
+  // them out of the last-level cache (measured: the state pass 67 -> 60 us
+  // per segment).
+  const int rs = H * D;  // elements between consecutive tokens
+  const int span = (loc.len - 1) * rs + D;  // elements from the first to the last valid
+  auto rsrc = [](const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qb, span * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kb, span * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vb, span * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t rg = rsrc(gb, GS ? ((loc.len - 1) * H + 1) * 4 : span * 4);
+  const uint32_t offT = (uint32_t)((r0p * rs + c0) * (int)sizeof(T));   // row r0p, channel c0
+  const uint32_t rowT = (uint32_t)(rs * (int)sizeof(T));                // bytes per token
   RawNt2<float> graw[RPP];
   float gsc[RPP];  // GS: the row's one gate
   Raw2<T> kraw[RPP], qraw[RPP];
@@ -216,30 +363,19 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
 #pragma unroll
   for (int j = 0; j < RPP; ++j) {
     if constexpr (GS)
-      gsc[j] = gb[min(r0p + j, loc.len - 1) * H];
+      gsc[j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)((r0p + j) * H * 4), 0, 2));
     else
-      graw[j].load(gb + min(r0p + j, loc.len - 1) * rowstride + c0);
+      graw[j].load(rg, (uint32_t)((r0p * rs + c0) * 4) + (uint32_t)j * (uint32_t)(rs * 4));
   }
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) kraw[j].load(kb + min(r0p + j, loc.len - 1) * rowstride + c0);
+  for (int j = 0; j < RPP; ++j) kraw[j].load(rk, offT + (uint32_t)j * rowT);
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) qraw[j].load(qb + min(r0p + j, loc.len - 1) * rowstride + c0);
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) vraw[j].load(vb + min(r0p + j, loc.len - 1) * rowstride + c0);
+  for (int j = 0; j < RPP; ++j) qraw[j].load(rq, offT + (uint32_t)j * rowT);
   if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
-  auto row_ok = [&](int j) { return r0p + j < loc.len; };
   float2 G[RPP];
 #pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    const float2 gj = GS ? make_float2(gsc[j], gsc[j]) : graw[j].get();
-    G[j] = row_ok(j) ? gj : make_float2(0.f, 0.f);
-  }
-  float2 kk[RPP], qq[RPP];
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    kk[j] = row_ok(j) ? kraw[j].get() : make_float2(0.f, 0.f);
-    qq[j] = row_ok(j) ? qraw[j].get() : make_float2(0.f, 0.f);
-  }
+  for (int j = 0; j < RPP; ++j) G[j] = GS ? make_float2(gsc[j], gsc[j]) : graw[j].get();
   // Row norms: the 2 RPP squared partial sums (q rows, then k rows) of the
   // D/2 lanes of a part, reduced by a butterfly that halves the values each
   // lane keeps at every step (reduce-scatter) and then sums the last one
@@ -250,8 +386,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
     float x[V];
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
-      x[j] = qq[j].x * qq[j].x + qq[j].y * qq[j].y;
-      x[RPP + j] = kk[j].x * kk[j].x + kk[j].y * kk[j].y;
+      // rows past the chunk's end read as zero (their norms are never used)
+      const float2 qj = qraw[j].get(), kj = kraw[j].get();
+      x[j] = qj.x * qj.x + qj.y * qj.y;
+      x[RPP + j] = kj.x * kj.x + kj.y * kj.y;
     }
     int idx = 0;
 #pragma unroll
@@ -278,16 +416,24 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
       if (idx < RPP) s_rq[r0p + idx] = rn; else s_rk[r0p + idx - RPP] = rn;
     }
   }
+  // The operands convert q and k from the raw bits again: holding the
+  // converted values instead would double their registers through the scan.
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    __asm__ volatile("" : "+v"(kraw[j].v));
+    __asm__ volatile("" : "+v"(qraw[j].v));
+  }
   // ---- in-chunk prefix sum of g ---------------------------------------------
+  float* scan = reinterpret_cast<float*>(r2);  // part totals; region 2 is free until the operands
 #pragma unroll
   for (int j = 1; j < RPP; ++j) { G[j].x += G[j - 1].x; G[j].y += G[j - 1].y; }
-  scratch[part * D + c0] = G[RPP - 1].x;
-  scratch[part * D + c0 + 1] = G[RPP - 1].y;
+  scan[part * D + c0] = G[RPP - 1].x;
+  scan[part * D + c0 + 1] = G[RPP - 1].y;
   __syncthreads();
   float2 off = make_float2(0.f, 0.f), gamma = make_float2(0.f, 0.f);
 #pragma unroll
   for (int p = 0; p < NPART; ++p) {
-    const float2 t = make_float2(scratch[p * D + c0], scratch[p * D + c0 + 1]);
+    const float2 t = make_float2(scan[p * D + c0], scan[p * D + c0 + 1]);
     if (p < part) { off.x += t.x; off.y += t.y; }
     gamma.x += t.x; gamma.y += t.y;
   }
@@ -302,48 +448,67 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   // whole operand fragments; otherwise every thread stores its own values
   constexpr bool kStaged = sizeof(T) == 2;
   const bool direct = !kStaged || exact;
-  float* s_eg = scratch;  // e^gamma per channel (the scan's partials are consumed)
   if (part == 0) {
     wEG[c0] = eg_gamma.x; wEG[c0 + 1] = eg_gamma.y;
     s_eg[c0] = eg_gamma.x; s_eg[c0 + 1] = eg_gamma.y;
   }
-  {
-    float kgT[2][8], ktT[2][8];
+  // (K o e^G)^T, 8 rows of channels c0 and c0+1 per entry, stored after the
+  // inverse.  Rows are taken in pairs, so that each pair goes straight into
+  // the held tile and K~ leaves as pairs (few values live at a time).
+  Tr8<T> kgh[RPP / 8][2];
 #pragma unroll
-    for (int j = 0; j < RPP; ++j) {
-      const int r = r0p + j;
+  for (int j = 0; j < RPP; j += 2) {
+    float kgx[2], kgy[2], ktx[2] = {0.f, 0.f}, kty[2] = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int jj = j + e, r = r0p + jj;
       const float rk = s_rk[r], rq = s_rq[r];
-      const float khx = kk[j].x * rk, khy = kk[j].y * rk;
-      const float qhx = qq[j].x * rq, qhy = qq[j].y * rq;
-      const float egx = __expf(G[j].x), egy = __expf(G[j].y);
+      const float2 kk = kraw[jj].get(), qq = qraw[jj].get();  // zero past the end
+      const float khx = kk.x * rk, khy = kk.y * rk;
+      const float qhx = qq.x * rq, qhy = qq.y * rq;
+      // e^(+-G) as 2^(+-G log2 e): one scaling for both signs (the same
+      // operations as __expf, so the same values)
+      const float gsx = G[jj].x * kLog2eF, gsy = G[jj].y * kLog2eF;
+      const float egx = __builtin_amdgcn_exp2f(gsx), egy = __builtin_amdgcn_exp2f(gsy);
       if (direct) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
-      kgT[0][j & 7] = khx * egx;
-      kgT[1][j & 7] = khy * egy;
+      kgx[e] = khx * egx;
+      kgy[e] = khy * egy;
       if (!exact) {
-        const float enx = __expf(-G[j].x), eny = __expf(-G[j].y);
+        const float enx = __builtin_amdgcn_exp2f(-gsx), eny = __builtin_amdgcn_exp2f(-gsy);
         st2(r0 + r * L::LDR + c0, khx * egx, khy * egy);     // K o e^G
         st2(r1 + r * L::LDR + c0, qhx * egx, qhy * egy);     // Q o e^G
         st2(r2 + r * L::LDR + c0, khx * enx, khy * eny);     // K o e^-G
-        ktT[0][j & 7] = khx * (eg_gamma.x * enx);
-        ktT[1][j & 7] = khy * (eg_gamma.y * eny);
+        if constexpr (!kStaged) {
+          ktx[e] = khx * (eg_gamma.x * enx);
+          kty[e] = khy * (eg_gamma.y * eny);
+        }
       } else {
         st2(r0 + r * L::LDR + c0, khx, khy);                 // k^ (staged later)
         st2(r1 + r * L::LDR + c0, qhx, qhy);                 // q^
-        ktT[0][j & 7] = khx * __expf(gamma.x - G[j].x);
-        ktT[1][j & 7] = khy * __expf(gamma.y - G[j].y);
+        ktx[e] = khx * __expf(gamma.x - G[jj].x);
+        kty[e] = khy * __expf(gamma.y - G[jj].y);
       }
-      if ((j & 7) == 7) {
-        const int rb = r0p + (j & ~7);
-        st8(r3 + c0 * L::LDT + rb, kgT[0]);                  // (K o e^G)^T
-        st8(r3 + (c0 + 1) * L::LDT + rb, kgT[1]);
-        if (direct) {
-          st_fnat8(wKT, kC / M::KSTEP, c0, rb, ktT[0]);     // K o e^(gamma-G), rows c
-          st_fnat8(wKT, kC / M::KSTEP, c0 + 1, rb, ktT[1]);
-        }
-      }
+    }
+    kgh[j / 8][0].set2((j & 7) / 2, kgx[0], kgx[1]);
+    kgh[j / 8][1].set2((j & 7) / 2, kgy[0], kgy[1]);
+    if (direct) {  // K o e^(gamma-G), rows c, k = chunk rows r0p+j, r0p+j+1
+      st_fnat2(wKT, kC / M::KSTEP, c0, r0p + j, ktx[0], ktx[1]);
+      st_fnat2(wKT, kC / M::KSTEP, c0 + 1, r0p + j, kty[0], kty[1]);
     }
   }
   __syncthreads();
+  // v is needed only after A and P: loading it here keeps its registers free
+  // through the operands, and the staged writes and A, P cover its latency
+  // (the exact path loads it after its own A and P).  Its row offsets are
+  // formed again: they equal the first loads' and would otherwise be held
+  // in registers until now.
+  auto load_v = [&]() {
+    uint32_t ov = offT;
+    __asm__ volatile("" : "+v"(ov));
+#pragma unroll
+    for (int j = 0; j < RPP; ++j) vraw[j].load(rv, ov + (uint32_t)j * rowT);
+  };
+  if (!exact) load_v();
 
   // Staged record writes (bf16, fast path): Q o e^G is region 1 and
   // K o e^-G region 2, so every lane slot of the operand-order blocks is
@@ -403,63 +568,9 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
       }
     }
   } else {
-    // Exact path: each entry from its own exponent difference (<= 0), with
-    // G, k^, q^ staged through region 2 in blocks of 16 channels.
-    constexpr int NE = (kC * (kC + 1) / 2 + NT - 1) / NT;
-    float ea[NE], ep[NE];
-    int er[NE], ei[NE];
-#pragma unroll
-    for (int m = 0; m < NE; ++m) {
-      const int e = tid + m * NT;
-      int r = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
-      while ((r + 1) * (r + 2) / 2 <= e) ++r;
-      while (r * (r + 1) / 2 > e) --r;
-      er[m] = e < kC * (kC + 1) / 2 ? r : -1;
-      ei[m] = e - r * (r + 1) / 2;
-      ea[m] = 0.f; ep[m] = 0.f;
-    }
-    float* stG = reinterpret_cast<float*>(r2);
-    float* stK = stG + kC * 16;
-    float* stQ = stK + kC * 16;
-    for (int cb = 0; cb < D / 16; ++cb) {
-      if (c0 / 16 == cb) {
-#pragma unroll
-        for (int j = 0; j < RPP; ++j) {
-          const int r = r0p + j, cc = c0 % 16;
-          stG[r * 16 + cc] = G[j].x;
-          stG[r * 16 + cc + 1] = G[j].y;
-          const float2 kh = ld2(r0 + r * L::LDR + c0), qh = ld2(r1 + r * L::LDR + c0);
-          stK[r * 16 + cc] = kh.x; stK[r * 16 + cc + 1] = kh.y;
-          stQ[r * 16 + cc] = qh.x; stQ[r * 16 + cc + 1] = qh.y;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < NE; ++m) {
-        if (er[m] < 0) continue;
-        const int r = er[m], i = ei[m];
-        for (int c = 0; c < 16; ++c) {
-          const float e = __expf(stG[r * 16 + c] - stG[i * 16 + c]);
-          const float ki = stK[i * 16 + c] * e;
-          ea[m] += stK[r * 16 + c] * ki;
-          ep[m] += stQ[r * 16 + c] * ki;
-        }
-      }
-      __syncthreads();
-    }
-    float* sA = reinterpret_cast<float*>(r1);
-#pragma unroll
-    for (int m = 0; m < NE; ++m) {
-      if (er[m] < 0) continue;
-      const int r = er[m], i = ei[m];
-      sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[m] : 0.f;
-      st_f(wP + fnat<T>(r, i, kC / M::KSTEP), ep[m]);
-    }
-    // the exact path writes no upper-triangle entries of the diagonal blocks
-    for (int e = tid; e < kC * kC; e += NT) {
-      const int r = e >> 6, i = e & 63;
-      if (i > r && (i >> 4) == (r >> 4)) st_f(wP + fnat<T>(r, i, kC / M::KSTEP), 0.f);
-    }
+    k1_exact_ap<T, D, GS>(r0, r1, reinterpret_cast<float*>(r2), reinterpret_cast<float*>(r1),
+                          s_beta, wP, gb, rowstride, H, loc.len, off.x, off.y);
+    load_v();
   }
   if (!exact) {
     __syncthreads();  // all reads of regions 0..2 done; region 1 becomes A
@@ -496,12 +607,12 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
     float vx[8], vy[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const float2 vt = row_ok(j0 + t) ? vraw[j0 + t].get() : make_float2(0.f, 0.f);
+      const float2 vt = vraw[j0 + t].get();  // zero past the chunk's end
       vx[t] = vt.x;
       vy[t] = vt.y;
     }
-    st8(r0 + c0 * L::LDT + r0p + j0, vx);
-    st8(r0 + (c0 + 1) * L::LDT + r0p + j0, vy);
+    st8t(r0 + c0 * L::LDT + r0p + j0, vx);
+    st8t(r0 + (c0 + 1) * L::LDT + r0p + j0, vy);
   }
   __syncthreads();
 
@@ -509,10 +620,11 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
   const float* sA = reinterpret_cast<const float*>(r1);
   float* sT = reinterpret_cast<float*>(r2);
   static_assert(L::LDA == kTriLd, "A and T use the inverse's leading dimension");
-  tri_inv64(sA, sT, scratch, wave, lane);
-  // T Diag(beta) in the MFMA type, lower triangle only, into region 1:
-  // thread = (row, group of TW columns)
-  T* sTb = r1;
+  tri_inv64(sA, sT, nullptr, wave, lane);  // its scratch: T's upper blocks
+  // T Diag(beta) in the MFMA type, lower triangle only, over T in region 2:
+  // thread = (row, group of TW columns).  A is dead: (K o e^G)^T goes to
+  // region 1 meanwhile.
+  T* sTb = r2;
   {
     constexpr int TG = NT / kC, TW = kC / TG;  // threads per row, columns each
     const int r = tid / TG, i0 = (tid % TG) * TW;
@@ -526,9 +638,14 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
       vals[t + 2] = (i0 + t + 2 <= r) ? tv.z * bv.z : 0.f;
       vals[t + 3] = (i0 + t + 3 <= r) ? tv.w * bv.w : 0.f;
     }
-    // region 1 held A: every read of it ended above
 #pragma unroll
-    for (int t = 0; t < TW; t += 8) st8(sTb + r * L::LDT + i0 + t, vals + t);
+    for (int b = 0; b < RPP / 8; ++b) {
+      kgh[b][0].store(r1 + c0 * L::LDT + r0p + 8 * b);
+      kgh[b][1].store(r1 + (c0 + 1) * L::LDT + r0p + 8 * b);
+    }
+    __syncthreads();  // every read of T done
+#pragma unroll
+    for (int t = 0; t < TW; t += 8) st8t(sTb + r * L::LDT + i0 + t, vals + t);
   }
   __syncthreads();
 
@@ -541,14 +658,14 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_min_blocks<T, D>())) void
     const int nb0 = (wave >> 2) * NBW;
     typename M::frag tb[kC / M::KSTEP];
 #pragma unroll
-    for (int ks = 0; ks < kC / M::KSTEP; ++ks) tb[ks] = frag_at<T>(sTb, L::LDT, rb * 16, ks, lane);
+    for (int ks = 0; ks < kC / M::KSTEP; ++ks) tb[ks] = frag_t<T>(sTb, L::LDT, rb * 16, ks, lane);
 #pragma unroll
     for (int nb = nb0; nb < nb0 + NBW; ++nb) {
       f32x4_t u = {0.f, 0.f, 0.f, 0.f}, wk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kC / M::KSTEP; ++ks) {
-        u = M::mma(tb[ks], frag_at<T>(r0, L::LDT, nb * 16, ks, lane), u);   // B = V^T rows
-        wk = M::mma(frag_at<T>(r3, L::LDT, nb * 16, ks, lane), tb[ks], wk);  // A = KG^T rows
+        u = M::mma(tb[ks], frag_t<T>(r0, L::LDT, nb * 16, ks, lane), u);    // B = V^T rows
+        wk = M::mma(frag_t<T>(r1, L::LDT, nb * 16, ks, lane), tb[ks], wk);   // A = KG^T rows
       }
       // u: rows r = rb*16 + 4*(lane/16) + j, column n = nb*16 + lane%16 -> tile (nb, rb)
       st4(wUT + ((nb * (kC / 16) + rb) * 64 + lane) * 4, u[0], u[1], u[2], u[3]);

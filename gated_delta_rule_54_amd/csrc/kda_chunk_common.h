@@ -81,14 +81,23 @@ template <> struct Raw4<bf16> {
 };
 // Two consecutive elements kept as raw bits until use.
 template <typename T> struct Raw2;
+// Buffer-resource forms (load(rsrc, off)): off is the byte offset of the pair;
+// a pair past the resource's bound reads as zero.  aux 2 = non-temporal.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 template <> struct Raw2<float> {
   float2 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
   __device__ __forceinline__ float2 get() const { return v; }
 };
 template <> struct Raw2<bf16> {
   uint32_t v;
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
   __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
 };
 // Two consecutive elements as raw bits through a non-temporal load: for
@@ -101,12 +110,18 @@ template <> struct RawNt2<float> {
   __device__ __forceinline__ void load(const float* p) {
     v = __builtin_nontemporal_load(reinterpret_cast<const f32x2_t*>(p));
   }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
+  }
   __device__ __forceinline__ float2 get() const { return make_float2(v[0], v[1]); }
 };
 template <> struct RawNt2<bf16> {
   uint32_t v;
   __device__ __forceinline__ void load(const bf16* p) {
     v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2);
   }
   __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
 };
@@ -254,7 +269,10 @@ __device__ __forceinline__ void st_tile_f32(float* C, int ldc, f32x4_t v, float 
 // Unit lower triangular inverse T = (I + A)^-1 of a 64 x 64 strictly lower
 // A, both fp32 in LDS with leading dimension kTriLd; uses 1024 floats of
 // LDS scratch and at least 4 waves, and must be reached by every thread of
-// the workgroup (it contains __syncthreads).  The 16 x 16 diagonal blocks are
+// the workgroup (it contains __syncthreads).  With scratch == nullptr the
+// intermediate products are kept in T's blocks above the 16 x 16 diagonal
+// blocks instead, which are then left undefined (T is lower triangular;
+// the caller reads only its lower triangle).  The 16 x 16 diagonal blocks are
 // inverted by forward substitution (wave 0, one lane per block column), then
 // the blocks below the diagonal follow from T_ij = -T_ii (sum_k A_ik T_kj):
 // first within each 32 x 32 half, then the lower-left 32 x 32 quarter.
@@ -279,14 +297,16 @@ __device__ __forceinline__ void tri_inv64(const float* sA, float* sT, float* scr
   // level 1: T_10 = -T_11 A_10 T_00 (wave 0), T_32 = -T_33 A_32 T_22 (wave 1)
   if (wave < 2) {
     const int b0 = wave * 32;  // the 32x32 diagonal block
-    float* xs = scratch + wave * 256;
+    // in place: the block above T_10, rows b0.., columns b0+16..
+    float* xs = scratch ? scratch + wave * 256 : sT + b0 * LD + b0 + 16;
+    const int ldx = scratch ? 16 : LD;
     f32x4_t x = mm16_f32(sA + (b0 + 16) * LD + b0, LD, sT + b0 * LD + b0, LD,
                          f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
-    st_tile_f32(xs, 16, x, 1.f, lane);
+    st_tile_f32(xs, ldx, x, 1.f, lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    f32x4_t y = mm16_f32(sT + (b0 + 16) * LD + b0 + 16, LD, xs, 16,
+    f32x4_t y = mm16_f32(sT + (b0 + 16) * LD + b0 + 16, LD, xs, ldx,
                          f32x4_t{0.f, 0.f, 0.f, 0.f}, lane);
     st_tile_f32(sT + (b0 + 16) * LD + b0, LD, y, -1.f, lane);
   }
@@ -297,21 +317,23 @@ __device__ __forceinline__ void tri_inv64(const float* sA, float* sT, float* scr
   {
     const bool active = wave < 4;
     const int tr = 32 + 16 * ((wave & 3) >> 1), tc = 16 * (wave & 1);
-    float* xs = scratch;  // 32x32 X, leading dim 32
+    // 32x32 X; in place: T's upper-right quarter, rows 0..31, columns 32..63
+    float* xs = scratch ? scratch : sT + 32;
+    const int ldx = scratch ? 32 : LD;
     if (active) {
       f32x4_t x = f32x4_t{0.f, 0.f, 0.f, 0.f};
       // X = A[tr.., 0:32] T_high[0:32, tc..]: T_high is lower triangular, so
       // only k-blocks >= tc/16 contribute
       for (int kb = tc / 16; kb < 2; ++kb)
         x = mm16_f32(sA + tr * LD + kb * 16, LD, sT + (kb * 16) * LD + tc, LD, x, lane);
-      st_tile_f32(xs + (tr - 32) * 32 + tc, 32, x, 1.f, lane);
+      st_tile_f32(xs + (tr - 32) * ldx + tc, ldx, x, 1.f, lane);
     }
     __syncthreads();
     if (active) {
       // Y = T_low[tr.., 32:64] X[0:32, tc..]: T_low lower triangular, k-blocks <= tr
       f32x4_t y = f32x4_t{0.f, 0.f, 0.f, 0.f};
       for (int kb = 0; kb <= (tr - 32) / 16; ++kb)
-        y = mm16_f32(sT + tr * LD + 32 + kb * 16, LD, xs + (kb * 16) * 32 + tc, 32, y, lane);
+        y = mm16_f32(sT + tr * LD + 32 + kb * 16, LD, xs + (kb * 16) * ldx + tc, ldx, y, lane);
       st_tile_f32(sT + tr * LD + tc, LD, y, -1.f, lane);
     }
   }
