@@ -387,9 +387,16 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
       // rows past the chunk's end read as zero (their norms are never used)
-      const float2 qj = qraw[j].get(), kj = kraw[j].get();
-      x[j] = qj.x * qj.x + qj.y * qj.y;
-      x[RPP + j] = kj.x * kj.x + kj.y * kj.y;
+      if constexpr (sizeof(T) == 2) {  // one dot product of the raw bf16 pair
+        const bf16x2_t qv = __builtin_bit_cast(bf16x2_t, qraw[j].v);
+        const bf16x2_t kv = __builtin_bit_cast(bf16x2_t, kraw[j].v);
+        x[j] = __builtin_amdgcn_fdot2_f32_bf16(qv, qv, 0.f, false);
+        x[RPP + j] = __builtin_amdgcn_fdot2_f32_bf16(kv, kv, 0.f, false);
+      } else {
+        const float2 qj = qraw[j].get(), kj = kraw[j].get();
+        x[j] = qj.x * qj.x + qj.y * qj.y;
+        x[RPP + j] = kj.x * kj.x + kj.y * kj.y;
+      }
     }
     int idx = 0;
 #pragma unroll
@@ -415,13 +422,6 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
       const float rn = qk_l2norm ? rsqrtf(x[0] + kNormEps) : 1.f;
       if (idx < RPP) s_rq[r0p + idx] = rn; else s_rk[r0p + idx - RPP] = rn;
     }
-  }
-  // The operands convert q and k from the raw bits again: holding the
-  // converted values instead would double their registers through the scan.
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    __asm__ volatile("" : "+v"(kraw[j].v));
-    __asm__ volatile("" : "+v"(qraw[j].v));
   }
   // ---- in-chunk prefix sum of g ---------------------------------------------
   float* scan = reinterpret_cast<float*>(r2);  // part totals; region 2 is free until the operands
@@ -522,10 +522,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
         float v[8];
         if (b < QB) {  // Q o e^G: rows r, k = channel
           const int r = (b / (D / 32)) * 16 + (L & 15), cb = (b % (D / 32)) * 32 + 4 * g;
-          const T* row = r1 + r * L::LDR;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { v[e] = ld_f(row + cb + e); v[4 + e] = ld_f(row + cb + 16 + e); }
-          st8(wQG + (b * 64 + L) * 8, v);
+          const T* row = r1 + r * L::LDR;  // bf16 already: copied as raw bits
+          const uint2 lo = *reinterpret_cast<const uint2*>(row + cb);
+          const uint2 hi = *reinterpret_cast<const uint2*>(row + cb + 16);
+          *reinterpret_cast<u32x4_t*>(wQG + (b * 64 + L) * 8) = u32x4_t{lo.x, lo.y, hi.x, hi.y};
         } else {       // K~: rows c, k = chunk row i
           const int bk = b - QB;
           const int c = (bk / (kC / 32)) * 16 + (L & 15), ib = (bk % (kC / 32)) * 32 + 4 * g;
