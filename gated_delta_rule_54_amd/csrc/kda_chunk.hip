@@ -690,19 +690,6 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
 // Buffer-resource loads: one resource per head's records, a per-lane 32-bit
 // offset computed once, the slot's record offset in a scalar register and the
 // fragment's constant offset in the instruction -- no per-load address math.
-template <typename T> struct BufFrag;
-template <> struct BufFrag<bf16> {
-  static __device__ __forceinline__ bf16x8_t load(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                                  uint32_t soff) {
-    return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
-  }
-};
-template <> struct BufFrag<float> {
-  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                               uint32_t soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
-  }
-};
 // Four consecutive elements, raw bits.
 template <typename T> struct BufRaw4;
 template <> struct BufRaw4<bf16> {
@@ -821,6 +808,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   __shared__ __align__(16) char lds_raw[(WS * LDS_S + WS * LDS_W) * sizeof(T)];
   T* sSt = reinterpret_cast<T*>(lds_raw);                // S^T slice [n][c]
   T* sWt = sSt + WS * LDS_S;                             // W^T slice [n][i]
+  constexpr int LDF = WS + 4;
+  __shared__ __align__(16) float sSf[D * LDF];           // S slice [c][n] in fp32 (states)
 
   // XCD-aware placement: workgroups of one (sequence, head) share id mod 8.
   const int id = blockIdx.x;
@@ -909,21 +898,24 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   };
 
   auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
-  // For the backward: the state entering chunk slot s0 + j, [slot][H][dk][dv]
-  // fp32.  Written at the end of the step before (after that step's
-  // prefetch loads: the wait counter is in order, so a store issued before
-  // them would hold up every wait for them).
+  // For the backward: the state entering chunk slot s0 + j, [slot][H] of
+  // slice-blocked D x D fp32 (sblk: this workgroup's slice is one
+  // contiguous D x 16 block).  Step j passes S through LDS in fp32 beside the
+  // MFMA copy, and after the barrier the block is stored in 16-byte pieces
+  // -- after the step's first prefetch loads (the wait counter is in order,
+  // so a store issued before them would hold up every wait for them).
+  // Only the pass without o (inside the backward) writes states.
+  const bool want_states = !OUT && states != nullptr;
   auto store_state = [&](int j) {
-    float* sd = states + ((s0 + j) * H + h) * (int64_t)D * D + n0 + (lane & 15);
+    static_assert(WS == 16, "states are stored in 16-column slices");
+    float* sd = states + ((s0 + j) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
 #pragma unroll
-    for (int i = 0; i < CBW; ++i)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sd[((wave * CBW + i) * 16 + 4 * (lane >> 4) + e) * D + nb * 16] = S[i][nb][e];
+    for (int pr = 0; pr < D * 4 / kThreads; ++pr) {
+      const int row = pr * (kThreads / 4) + threadIdx.x / 4, c4 = 4 * (threadIdx.x % 4);
+      *reinterpret_cast<float4*>(sd + row * 16 + c4) =
+          *reinterpret_cast<const float4*>(sSf + row * LDF + c4);
+    }
   };
-  if (states != nullptr) store_state(j0);
   // One chunk step: consumes the fragments in f and fills fn with those of
   // record jn (clamped to the last record), the loads spread over the step.
   auto step = [&](const F& f, F& fn, int j, int jn) {
@@ -939,6 +931,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
         const int c4 = (wave * CBW + i) * 16 + 4 * (lane >> 4);
         const int n = nb * 16 + (lane & 15);
         st_perm4(sSt + n * LDS_S, c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
+        if (want_states) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sSf[(c4 + e) * LDF + n] = S[i][nb][e];
+        }
       }
     __syncthreads();
 
@@ -959,6 +955,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       for (int nb = 0; nb < NB; ++nb) W[nb] = M::mma(f.wn[ks], sfr[nb][ks], W[nb]);
     __builtin_amdgcn_sched_barrier(0);
     fn.template load_part<0>(rsrc, son, offs);
+    // sSf is written again only after this step's second barrier
+    if (want_states) store_state(j);
     if constexpr (OUT) {
       store_o();
 #pragma unroll
@@ -1008,7 +1006,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       fn.template load_part<3>(rsrc, son, offs);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (states != nullptr && j + 1 < j1) store_state(j + 1);
 
     // (e) checkpoint after every ckpt_every tokens (dense, chunk-aligned)
     if (ckpt != nullptr && --ck_left == 0) {
@@ -1170,6 +1167,8 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                          stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
                          s1 - s0, d.qk_l2norm, recs);
     }
+    // (the per-chunk states are written only by the pass without o)
+    if (o != nullptr && states != nullptr) return hipErrorInvalidValue;
     auto k2 = o ? kda_state_pass<T, D, WS, true> : kda_state_pass<T, D, WS, false>;
     hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(kThreads), 0,
                        stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,

@@ -153,23 +153,13 @@ __device__ __forceinline__ typename Mma<T>::frag acc_frag(const f32x4_t* tiles, 
   }
 }
 
-// B operand (k = rows of a row-major fp32 matrix X, n = column n) read from
-// memory: element (k, n) = X[k * ld + n], k natural order.
-template <typename T>
-__device__ __forceinline__ typename Mma<T>::frag gfrag_cm(const float* X, int ld, int n, int ks,
-                                                          int lane) {
+// The KPL consecutive fp32 values of row m at k-step ks (k = column,
+// contiguous) of a slice-blocked D x D state (sblk; KPL <= 8 columns never
+// cross a 16-column slice).
+template <typename T, int D>
+__device__ __forceinline__ void grow_vals(const float* X, int m, int ks, int lane, float* x) {
   using M = Mma<T>;
-  float x[M::KPL];
-#pragma unroll
-  for (int e = 0; e < M::KPL; ++e) x[e] = X[(ks * M::KSTEP + M::KPL * (lane >> 4) + e) * ld + n];
-  return to_frag(x, T{});
-}
-// The KPL consecutive fp32 values of row m at k-step ks (k contiguous).
-template <typename T>
-__device__ __forceinline__ void grow_vals(const float* X, int ld, int m, int ks, int lane,
-                                          float* x) {
-  using M = Mma<T>;
-  const float* p = X + m * ld + ks * M::KSTEP + M::KPL * (lane >> 4);
+  const float* p = X + sblk<D>(m, ks * M::KSTEP + M::KPL * (lane >> 4));
   if constexpr (M::KPL == 8) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -539,17 +529,12 @@ template <typename T, int D>
 struct BwdPassFrags {
   using M = Mma<T>;
   static constexpr int CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
+  // dO slice of the chunk (64 rows x 16 columns): 16 bytes per lane, VE
+  // elements of one row; NO lanes hold the slice, the rest read nothing
+  static constexpr int VE = 16 / (int)sizeof(T), LPR = kBwdSliceW / VE, NO = kC * LPR;
+  static_assert(NO <= kBwdPassThreads, "the dO slice must fit one load per lane");
   typename M::frag mf[CBW][KD], zf[CBW][KC];
-  uint32_t od[KC][M::KPL];  // raw dO elements, packed into fragments at use
-  __device__ __forceinline__ typename M::frag dof(int ks) const {
-    if constexpr (M::KPL == 8) {
-      const u32x4_t u = {od[ks][0] | (od[ks][1] << 16), od[ks][2] | (od[ks][3] << 16),
-                         od[ks][4] | (od[ks][5] << 16), od[ks][6] | (od[ks][7] << 16)};
-      return __builtin_bit_cast(bf16x8_t, u);
-    } else {
-      return __builtin_bit_cast(float, od[ks][0]);
-    }
-  }
+  u32x4_t dov;  // raw dO bits of row tid / LPR, columns VE (tid % LPR) ..
 };
 
 template <typename T, int D>
@@ -561,7 +546,13 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   using RC = BRec<T, D>;
   using F = BwdPassFrags<T, D>;
   constexpr int CBW = F::CBW, KD = F::KD, KC = F::KC, LDS_S = D + 8;
+  constexpr int VE = F::VE, LPR = F::LPR, NO = F::NO;
+  // per chunk, double-buffered: dS' in the MFMA type (the exchange), dO^T
+  // (columns n, rows r), and dS' in fp32 for the store to dstates
+  constexpr int LDO = kC + 16 / (int)sizeof(T), LDF = kBwdSliceW + 4;
   __shared__ __align__(16) T sD[2][kBwdSliceW * LDS_S];
+  __shared__ __align__(16) T sO[2][kBwdSliceW * LDO];
+  __shared__ __align__(16) float sF[2][D * LDF];
   const int id = blockIdx.x;
   const int nh = (id & 7) + 8 * (id / (8 * nslice));
   const int slice = (id >> 3) % nslice;
@@ -590,74 +581,122 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   const int nch = (int)(sp.c1 - sp.c0);
   const int len_last = (int)(sp.ntok - (int64_t)(nch - 1) * kC);
 
-  auto load = [&](F& f, int ci) {
-    const T* rec = reinterpret_cast<const T*>(brec + ((int64_t)h * nslot + sp.c0 + ci) * RC::BYTES);
+  // Record fragments through a buffer resource rebased at each chunk's
+  // record (scalar), a per-lane offset computed once, and the fragment's
+  // offset as a scalar constant: no per-load address math.
+  constexpr uint32_t FBY = 64 * M::KPL * sizeof(T);  // bytes of one fragment
+  const uint32_t lo_m = (uint32_t)((wave * CBW * KD * 64 + lane) * M::KPL * sizeof(T));
+  const uint32_t lo_z = (uint32_t)((wave * CBW * KC * 64 + lane) * M::KPL * sizeof(T));
+  auto rec_of = [&](int ci) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(brec + ((int64_t)h * nslot + sp.c0 + ci) * RC::BYTES), (short)0, (int)RC::BYTES,
+        0x00020000);
+  };
+  auto load_m = [&](F& f, __amdgpu_buffer_rsrc_t r, int i) {
 #pragma unroll
-    for (int i = 0; i < CBW; ++i) {
+    for (int ks = 0; ks < KD; ++ks)
+      f.mf[i][ks] = BufFrag<T>::load(r, lo_m, (uint32_t)(RC::MF * sizeof(T)) + (i * KD + ks) * FBY);
+  };
+  auto load_z = [&](F& f, __amdgpu_buffer_rsrc_t r, int ci) {
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks)
-        f.mf[i][ks] = M::load(rec + RC::MF + (((wave * CBW + i) * KD + ks) * 64 + lane) * M::KPL);
+    for (int i = 0; i < CBW; ++i)
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks)
-        f.zf[i][ks] = M::load(rec + RC::ZF + (((wave * CBW + i) * KC + ks) * 64 + lane) * M::KPL);
-    }
-    // dO rows in kpos order (the k index of Z^T), as raw bits: the buffer's
-    // bound ends after the chunk's last valid row, so rows past a
-    // sequence's end read as zero without a branch
+        f.zf[i][ks] = BufFrag<T>::load(r, lo_z, (uint32_t)(RC::ZF * sizeof(T)) + (i * KC + ks) * FBY);
+    // The chunk's dO slice as raw bits, one 16-byte piece per lane: the
+    // buffer's bound ends after the chunk's last valid row, so rows past a
+    // sequence's end read as zero, and lanes beyond the slice read past the
+    // bound (zero, no memory access) -- every load is unconditional.
     const int len = ci == nch - 1 ? len_last : kC;
     const T* ob = d_o + ((sp.tok0 + (int64_t)ci * kC) * H + h) * D + n0;
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void*)ob, (short)0, (int)(((len - 1) * H * D + kBwdSliceW) * sizeof(T)), 0x00020000);
-#pragma unroll
-    for (int ks = 0; ks < KC; ++ks)
-#pragma unroll
-      for (int e = 0; e < M::KPL; ++e) {
-        int r;
-        if constexpr (M::KPL == 8)
-          r = ks * 32 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-        else
-          r = 16 * (ks >> 2) + 4 * grp + (ks & 3);
-        const uint32_t off = (uint32_t)((r * H * D + (lane & 15)) * sizeof(T));
-        if constexpr (M::KPL == 8)
-          f.od[ks][e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
-        else
-          f.od[ks][e] = __builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0);
-      }
+    const int tid = threadIdx.x;
+    const uint32_t off = tid < NO ? (uint32_t)(((tid / LPR) * H * D + VE * (tid % LPR)) * sizeof(T))
+                                  : 0x80000000u;
+    f.dov = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
   };
-  // dS' of chunk ci (the gradient of the state leaving it) for kda_bwd_intra:
-  // stored once it is formed, after the step's prefetch loads were issued
-  // (the wait counter is in order; an earlier store would hold up the waits)
-  auto store_ds = [&](int ci) {
-    float* dst = dstates + ((sp.c0 + ci) * H + h) * (int64_t)D * D + n;
+  auto load = [&](F& f, int ci) {
+    const __amdgpu_buffer_rsrc_t r = rec_of(ci);
 #pragma unroll
-    for (int i = 0; i < CBW; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[((wave * CBW + i) * 16 + 4 * grp + j) * D] = dS[i][j];
+    for (int i = 0; i < CBW; ++i) load_m(f, r, i);
+    load_z(f, r, ci);
   };
-  auto step = [&](const F& f, int ci, int buf) {
+  // One chunk step: consumes the fragments in f and fills fn with those of
+  // chunk cn, the loads spread over the step (a wave issuing a whole record
+  // at once stalls behind the CU's vector memory queue).  dS on entry is dS'
+  // of chunk ci (the gradient of the state leaving it): it crosses LDS in
+  // the MFMA type for the product and in fp32 for dstates (kda_bwd_intra
+  // reads it), whose slice block is then stored in 16-byte pieces.  The dO
+  // slice crosses LDS transposed, so each lane's fragment is two runs of rows.
+  auto step = [&](const F& f, F& fn, int ci, int cn, int buf) {
     T* sb = sD[buf];
+    float* sf = sF[buf];
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       const int c4 = (wave * CBW + i) * 16 + 4 * grp;
       st_perm4(sb + (lane & 15) * LDS_S, c4, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sf[(c4 + j) * LDF + (lane & 15)] = dS[i][j];
+    }
+    if (threadIdx.x < NO) {
+      const int r = threadIdx.x / LPR, cb = VE * (threadIdx.x % LPR);
+      T* so = sO[buf] + cb * LDO + r;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          reinterpret_cast<uint16_t*>(so)[(2 * e) * LDO] = (uint16_t)(f.dov[e] & 0xffffu);
+          reinterpret_cast<uint16_t*>(so)[(2 * e + 1) * LDO] = (uint16_t)(f.dov[e] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) so[e * LDO] = __uint_as_float(f.dov[e]);
+      }
     }
     __syncthreads();
-    typename M::frag bfr[KD];
+    typename M::frag bfr[KD], dof[KC];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) bfr[ks] = frag_at<T>(sb, LDS_S, 0, ks, lane);
+    const T* sor = sO[buf] + (lane & 15) * LDO;
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) {
+      if constexpr (M::KPL == 8) {  // kpos order: rows 32ks + 4grp.., then 32ks + 16 + 4grp..
+        const uint2 a = *reinterpret_cast<const uint2*>(sor + ks * 32 + 4 * grp);
+        const uint2 b = *reinterpret_cast<const uint2*>(sor + ks * 32 + 16 + 4 * grp);
+        dof[ks] = __builtin_bit_cast(typename M::frag, u32x4_t{a.x, a.y, b.x, b.y});
+      } else {
+        dof[ks] = M::load(sor + 16 * (ks >> 2) + 4 * grp + (ks & 3));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KC; ++ks) acc = M::mma(f.zf[i][ks], f.dof(ks), acc);
+      for (int ks = 0; ks < KC; ++ks) acc = M::mma(f.zf[i][ks], dof[ks], acc);
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) acc = M::mma(f.mf[i][ks], bfr[ks], acc);
       dS[i] = acc;
     }
-    if (ci > 0) store_ds(ci - 1);
-    // No second barrier: the next chunk writes the other buffer, and this
-    // buffer is rewritten only after the next chunk's barrier, which every
-    // wave reaches after its reads of this one.
+    __builtin_amdgcn_sched_barrier(0);
+    const __amdgpu_buffer_rsrc_t rn = rec_of(cn);
+    load_m(fn, rn, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // dS' of chunk ci: this slice's contiguous D x 16 block (sblk), 4
+    // threads per row
+    float* dst = dstates + ((sp.c0 + ci) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
+#pragma unroll
+    for (int pr = 0; pr < D * 4 / kBwdPassThreads; ++pr) {
+      const int row = pr * (kBwdPassThreads / 4) + threadIdx.x / 4, c4 = 4 * (threadIdx.x % 4);
+      *reinterpret_cast<float4*>(dst + row * 16 + c4) =
+          *reinterpret_cast<const float4*>(sf + row * LDF + c4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 1; i < CBW; ++i) load_m(fn, rn, i);
+    load_z(fn, rn, cn);
+    // No second barrier: the next chunk writes the other buffers, and these
+    // are rewritten only after the next chunk's barrier, which every wave
+    // reaches after its reads of them.
   };
   // Three register sets: each chunk's record is prefetched two chunks ahead
   // (clamped at the first chunk, so every load is unconditional), and the
@@ -666,19 +705,15 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   F fa, fb, fc;
   load(fa, nch - 1);
   load(fb, max(nch - 2, 0));
-  store_ds(nch - 1);
   int s = 0;
   for (; s + 3 <= nch; s += 3) {
     const int ci = nch - 1 - s;
-    load(fc, max(ci - 2, 0));
-    step(fa, ci, s & 1);
-    load(fa, max(ci - 3, 0));
-    step(fb, ci - 1, (s + 1) & 1);
-    load(fb, max(ci - 4, 0));
-    step(fc, ci - 2, s & 1);
+    step(fa, fc, ci, max(ci - 2, 0), s & 1);
+    step(fb, fa, ci - 1, max(ci - 3, 0), (s + 1) & 1);
+    step(fc, fb, ci - 2, max(ci - 4, 0), s & 1);
   }
-  if (s < nch) step(fa, nch - 1 - s, s & 1);
-  if (s + 1 < nch) step(fb, nch - 2 - s, (s + 1) & 1);
+  if (s < nch) step(fa, fc, nch - 1 - s, 0, s & 1);
+  if (s + 1 < nch) step(fb, fa, nch - 2 - s, 0, (s + 1) & 1);
   if (dinit != nullptr) {
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
@@ -743,8 +778,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
       const int cc = ks * M::KSTEP + KPL * grp + e;
-      sraw[ks][e] = S[cc * D + c];
-      draw[ks][e] = dS[cc * D + c];
+      sraw[ks][e] = S[sblk<D>(cc, c)];
+      draw[ks][e] = dS[sblk<D>(cc, c)];
     }
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -901,7 +936,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
       float xs[KPL];
-      grow_vals<T>(S, D, c, ks, lane, xs);
+      grow_vals<T, D>(S, c, ks, lane, xs);
       st[ks] = to_frag(xs, T{});
     }
 #pragma unroll
@@ -938,8 +973,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
       float xs[KPL], xd[KPL];
-      grow_vals<T>(S, D, c, ks, lane, xs);
-      grow_vals<T>(dS, D, c, ks, lane, xd);
+      grow_vals<T, D>(S, c, ks, lane, xs);
+      grow_vals<T, D>(dS, c, ks, lane, xd);
 #pragma unroll
       for (int e = 0; e < KPL; ++e) rs += xs[e] * xd[e];
       dst[ks] = to_frag(xd, T{});

@@ -173,6 +173,22 @@ template <> struct Mma<float> {
   }
 };
 
+// One operand fragment (a lane's KPL elements) through a buffer resource:
+// off is the lane's byte offset, soff a scalar byte offset.
+template <typename T> struct BufFrag;
+template <> struct BufFrag<bf16> {
+  static __device__ __forceinline__ bf16x8_t load(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                  uint32_t soff) {
+    return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+  }
+};
+template <> struct BufFrag<float> {
+  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+  }
+};
+
 // Fragment of rows [row0, row0+16) and k-step ks of a row-major buffer.
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag frag_at(const T* base, int ld, int row0, int ks,
@@ -338,6 +354,16 @@ __device__ __forceinline__ void tri_inv64(const float* sA, float* sT, float* scr
     }
   }
   __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk states handed from the forward pass and the reverse pass to the
+// backward's per-chunk kernel are stored slice-blocked: [D/16][D][16], i.e.
+// the 16-column slices one state-pass workgroup owns are contiguous (each
+// step writes whole lines), rows c inside a slice, columns n last.
+template <int D>
+__device__ __forceinline__ int sblk(int c, int n) {
+  return ((n >> 4) * D + c) * 16 + (n & 15);
 }
 
 // ---------------------------------------------------------------------------

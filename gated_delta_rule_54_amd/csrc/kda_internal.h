@@ -15,8 +15,10 @@ hipError_t launch_decode(const kda_desc_t& d, const void* q, const void* k, cons
                          hipStream_t stream);
 
 // Chunkwise prefill.  Workspace size and launch plan live in kda_chunk.hip.
-// chunk_states (or nullptr): the state entering every chunk slot,
-// [slot][H][dk][dv] fp32, for the backward; o may then be nullptr.
+// chunk_states (or nullptr): the state entering every chunk slot, [slot][H]
+// of D x D fp32 slice-blocked as sblk (kda_chunk_common.h) lays it out, for
+// the backward; only with o == nullptr (the
+// pass that writes states produces no output; both set is an invalid value).
 size_t chunk_workspace_bytes(const kda_desc_t& d);
 hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* init_state,
