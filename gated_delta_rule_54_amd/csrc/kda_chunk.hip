@@ -387,16 +387,11 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
       // rows past the chunk's end read as zero (their norms are never used)
-      if constexpr (sizeof(T) == 2) {  // one dot product of the raw bf16 pair
-        const bf16x2_t qv = __builtin_bit_cast(bf16x2_t, qraw[j].v);
-        const bf16x2_t kv = __builtin_bit_cast(bf16x2_t, kraw[j].v);
-        x[j] = __builtin_amdgcn_fdot2_f32_bf16(qv, qv, 0.f, false);
-        x[RPP + j] = __builtin_amdgcn_fdot2_f32_bf16(kv, kv, 0.f, false);
-      } else {
-        const float2 qj = qraw[j].get(), kj = kraw[j].get();
-        x[j] = qj.x * qj.x + qj.y * qj.y;
-        x[RPP + j] = kj.x * kj.x + kj.y * kj.y;
-      }
+      // (plain fp32 arithmetic: the packed bf16 dot-product instruction gave
+      // wrong sums inside a larger kernel here, so it is not used)
+      const float2 qj = qraw[j].get(), kj = kraw[j].get();
+      x[j] = qj.x * qj.x + qj.y * qj.y;
+      x[RPP + j] = kj.x * kj.x + kj.y * kj.y;
     }
     int idx = 0;
 #pragma unroll

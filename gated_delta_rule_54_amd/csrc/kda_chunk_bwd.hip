@@ -303,6 +303,106 @@ __device__ __forceinline__ void load_cols(const T* __restrict__ q, const T* __re
     }
 }
 
+// Prologue loads: the chunk's k, q and g rows in coalesced 16-byte pieces
+// through buffer resources bounded at the chunk's last valid row (rows past
+// it read as zero), the q/k row norms reduced across the lanes that hold each
+// row, and the raw rows staged in LDS for reads in the column layout: k at
+// byte 0, g (fp32) at XB, q at 3 XB -- space no layout uses before the gated
+// operands are written.  NTL: read non-temporally (read once).
+template <typename T, int D, bool GS, bool NTL>
+__device__ __forceinline__ void stage_rows(const T* q, const T* k, const float* g,
+                                           const ChunkLoc& loc, int H, int h, int qk_l2norm,
+                                           char* stage, float* rk, float* rq) {
+  using L = BwdLds<T, D>;
+  constexpr int NT = L::NT, LDX = L::LDX, LDG = D + 4;
+  constexpr int VE = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int PR = D / VE, NPK = kC * PR / NT;    // k, q: pieces per row, per thread
+  constexpr int PRG = D / 4, NPG = kC * PRG / NT;   // g: the same
+  static_assert(kC * PR % NT == 0 && kC * PRG % NT == 0 && PR <= 64 && 64 % PR == 0,
+                "pieces must tile the threads, a row's pieces within one wave");
+  static_assert(64 * LDG * 4 <= 2 * L::XB, "staged g must fit two regions");
+  constexpr int aux = NTL ? 2 : 0;
+  const int tid = threadIdx.x;
+  const int rs = H * D;
+  const int64_t row0 = loc.tok0 * H + h;
+  const int span = (loc.len - 1) * rs + D;
+  auto rsrc = [](const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rkr = rsrc(k + row0 * D, span * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t rqr = rsrc(q + row0 * D, span * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t rgr =
+      rsrc(GS ? g + row0 : g + row0 * D, GS ? ((loc.len - 1) * H + 1) * 4 : span * 4);
+  u32x4_t kv[NPK], qv[NPK], gv[NPG];
+  float gs = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int p = i * NT + tid, row = p / PR, cp = p % PR;
+    kv[i] = __builtin_amdgcn_raw_buffer_load_b128(rkr, (uint32_t)((row * rs + cp * VE) * (int)sizeof(T)), 0, aux);
+  }
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int p = i * NT + tid, row = p / PR, cp = p % PR;
+    qv[i] = __builtin_amdgcn_raw_buffer_load_b128(rqr, (uint32_t)((row * rs + cp * VE) * (int)sizeof(T)), 0, aux);
+  }
+  if constexpr (GS) {
+    gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                       rgr, (uint32_t)((tid % kC) * H * 4), 0, aux));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPG; ++i) {
+      const int p = i * NT + tid, row = p / PRG, cp = p % PRG;
+      gv[i] = __builtin_amdgcn_raw_buffer_load_b128(rgr, (uint32_t)((row * rs + cp * 4) * 4), 0, aux);
+    }
+  }
+  T* sk = reinterpret_cast<T*>(stage);
+  float* sg = reinterpret_cast<float*>(stage + L::XB);
+  T* sq = reinterpret_cast<T*>(stage + 3 * L::XB);
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int p = i * NT + tid, row = p / PR, cp = p % PR;
+    float a = 0.f, b = 0.f;  // this piece's part of |k_row|^2, |q_row|^2
+    // (plain fp32 arithmetic: the packed bf16 dot-product instruction gave
+    // wrong sums in this kernel, so it is not used)
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float k0 = bf_val(kv[i][e] & 0xffffu), k1 = bf_val(kv[i][e] >> 16);
+        const float q0 = bf_val(qv[i][e] & 0xffffu), q1 = bf_val(qv[i][e] >> 16);
+        a += k0 * k0 + k1 * k1;
+        b += q0 * q0 + q1 * q1;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __uint_as_float(kv[i][e]), y = __uint_as_float(qv[i][e]);
+        a += x * x;
+        b += y * y;
+      }
+    }
+#pragma unroll
+    for (int o = PR / 2; o >= 1; o >>= 1) {
+      a += __shfl_xor(a, o);
+      b += __shfl_xor(b, o);
+    }
+    if (cp == 0) {
+      rk[row] = qk_l2norm ? rsqrtf(a + kNormEps) : 1.f;
+      rq[row] = qk_l2norm ? rsqrtf(b + kNormEps) : 1.f;
+    }
+    *reinterpret_cast<u32x4_t*>(sk + row * LDX + cp * VE) = kv[i];
+    *reinterpret_cast<u32x4_t*>(sq + row * LDX + cp * VE) = qv[i];
+  }
+  if constexpr (GS) {
+    if (tid < kC) sg[tid * LDG] = gs;  // the row's one gate, in column 0
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPG; ++i) {
+      const int p = i * NT + tid, row = p / PRG, cp = p % PRG;
+      *reinterpret_cast<u32x4_t*>(sg + row * LDG + cp * 4) = gv[i];
+    }
+  }
+}
+
 // G = prefix sum of gr down the 64 rows of this lane's column -- within the
 // lane's 4 rows, then across the 4 lane groups, then across the tiles -- and
 // gamma = G of the last row.
@@ -346,31 +446,24 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
   float gr[4][4];
-  load_cols<T, D, GS, NTL>(q, k, g, loc, H, h, c, grp, R, gr);
-  if (tid < kC) sm.beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
-  // row norms: over this wave's 16 columns, then over the waves
+  {
+    char* stage = reinterpret_cast<char*>(sm.kp);  // the layout's first byte
+    stage_rows<T, D, GS, NTL>(q, k, g, loc, H, h, qk_l2norm, stage, sm.rk, sm.rq);
+    if (tid < kC) sm.beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
+    __syncthreads();
+    const T* sk = reinterpret_cast<const T*>(stage);
+    const float* sg = reinterpret_cast<const float*>(stage + L::XB);
+    const T* sq = reinterpret_cast<const T*>(stage + 3 * L::XB);
+    constexpr int LDG = D + 4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sk = sum16(R.kh[t][j] * R.kh[t][j]);
-      const float sq = sum16(R.qh[t][j] * R.qh[t][j]);
-      if ((lane & 15) == 0) {
+      for (int j = 0; j < 4; ++j) {
         const int r = 16 * t + 4 * grp + j;
-        sm.red[wave * kC + r] = sk;
-        sm.red[(NW + wave) * kC + r] = sq;
+        R.kh[t][j] = ld_f(sk + r * LDX + c);
+        R.qh[t][j] = ld_f(sq + r * LDX + c);
+        gr[t][j] = GS ? sg[r * LDG] : sg[r * LDG + c];
       }
-    }
-  __syncthreads();
-  if (tid < kC) {
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      sk += sm.red[w * kC + tid];
-      sq += sm.red[(NW + w) * kC + tid];
-    }
-    sm.rk[tid] = qk_l2norm ? rsqrtf(sk + kNormEps) : 1.f;
-    sm.rq[tid] = qk_l2norm ? rsqrtf(sq + kNormEps) : 1.f;
   }
   prefix_G(gr, lane, R);
   __syncthreads();
