@@ -1149,6 +1149,17 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     if (tid < loc.len) st_nt(dbb + tok(tid), sm.x0[tid]);
   }
   __syncthreads();
+  // dk, dq (and dg) leave through LDS: each lane writes its column of the
+  // row-major tiles (the layout's first bytes, free since the barrier
+  // above), and the tiles go out in 16-byte non-temporal pieces through
+  // buffer resources bounded at the chunk's last valid row, whole lines at
+  // a time (rows past the end are dropped by the bound).
+  char* ostage = reinterpret_cast<char*>(sm.kp);
+  T* sdk = reinterpret_cast<T*>(ostage);
+  T* sdq = reinterpret_cast<T*>(ostage + L::XB);
+  float* sdg = reinterpret_cast<float*>(ostage + 2 * L::XB);
+  constexpr int LDG = D + 4;
+  static_assert(2 * L::XB + kC * LDG * 4 <= 4 * L::XB, "staged gradients must fit");
   const T* qrow = q + row0 * D;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -1161,12 +1172,42 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
         gk = sm.rk[r] * (gk - sm.x1[r] * R.kh[t][j]);
         gq = sm.rq[r] * (gq - sm.x2[r] * qn);
       }
-      if (r < loc.len) {
-        st_nt(dkb + tok(r) * D + c, gk);
-        st_nt(dqb + tok(r) * D + c, gq);
-        if (!GS) st_nt(dgb + tok(r) * D + c, dgo[t][j]);
+      st_f(sdk + r * LDX + c, gk);
+      st_f(sdq + r * LDX + c, gq);
+      if constexpr (!GS) sdg[r * LDG + c] = dgo[t][j];
+    }
+  __syncthreads();
+  {
+    constexpr int NT = L::NT;
+    constexpr int VE = 16 / (int)sizeof(T), PR = D / VE, NPK = kC * PR / NT;
+    constexpr int PRG = D / 4, NPG = kC * PRG / NT;
+    constexpr int kNt = 2;  // non-temporal: nothing here reads the gradients again
+    const int rs = H * D, span = (loc.len - 1) * rs + D;
+    auto rsrc = [](void* base, int bytes) {
+      return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rdk = rsrc(dkb, span * (int)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rdq = rsrc(dqb, span * (int)sizeof(T));
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) {
+      const int p = i * NT + tid, row = p / PR, cp = p % PR;
+      const uint32_t off = (uint32_t)((row * rs + cp * VE) * (int)sizeof(T));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          *reinterpret_cast<const u32x4_t*>(sdk + row * LDX + cp * VE), rdk, off, 0, kNt);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          *reinterpret_cast<const u32x4_t*>(sdq + row * LDX + cp * VE), rdq, off, 0, kNt);
+    }
+    if constexpr (!GS) {
+      const __amdgpu_buffer_rsrc_t rdg = rsrc(dgb, span * 4);
+#pragma unroll
+      for (int i = 0; i < NPG; ++i) {
+        const int p = i * NT + tid, row = p / PRG, cp = p % PRG;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            *reinterpret_cast<const u32x4_t*>(sdg + row * LDG + cp * 4), rdg,
+            (uint32_t)((row * rs + cp * 4) * 4), 0, kNt);
       }
     }
+  }
   if constexpr (GS) {
     __syncthreads();
 #pragma unroll
