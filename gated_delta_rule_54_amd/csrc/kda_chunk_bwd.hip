@@ -862,26 +862,45 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // ---- value side: columns n = c --------------------------------------------
   // Every global read of this phase is issued at once, as raw bits converted
   // at use, so the phase waits for memory once: the S and dS' columns of the
-  // two B operands (k = c), and v and dO of this column (rows past the
-  // chunk's end re-read its last row and are masked at use).
+  // two B operands (k = c), and the chunk's v and dO rows.  v and dO come in
+  // coalesced 16-byte pieces through buffer resources bounded at the chunk's
+  // last valid row (rows past it read as zero) and are staged where W and dO'
+  // go (the inverse's region, dead now): each lane then reads its own column
+  // and later overwrites exactly those positions, so no barrier separates
+  // the reads from the W and dO' writes.
   float sraw[KD][KPL], draw[KD][KPL];
-  uint32_t vraw[4][4], oraw[4][4];
+  {
+    constexpr int NT = L::NT;
+    constexpr int VE = 16 / (int)sizeof(T), PR = D / VE, NPK = kC * PR / NT;
+    const int rs = H * D, span = (loc.len - 1) * rs + D;
+    const __amdgpu_buffer_rsrc_t rvr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(vb), (short)0, span * (int)sizeof(T), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ror = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(ob), (short)0, span * (int)sizeof(T), 0x00020000);
+    u32x4_t vv[NPK], ov[NPK];
 #pragma unroll
-  for (int ks = 0; ks < KD; ++ks)
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-      const int cc = ks * M::KSTEP + KPL * grp + e;
-      sraw[ks][e] = S[sblk<D>(cc, c)];
-      draw[ks][e] = dS[sblk<D>(cc, c)];
+    for (int i = 0; i < NPK; ++i) {
+      const int p = i * NT + tid, row = p / PR, cp = p % PR;
+      const uint32_t off = (uint32_t)((row * rs + cp * VE) * (int)sizeof(T));
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(rvr, off, 0, 2);
+      ov[i] = __builtin_amdgcn_raw_buffer_load_b128(ror, off, 0, 2);
     }
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int ks = 0; ks < KD; ++ks)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = tok(min(16 * t + 4 * grp + j, loc.len - 1)) * D + c;
-      vraw[t][j] = ld_raw_nt(vb + off);
-      oraw[t][j] = ld_raw_nt(ob + off);
+      for (int e = 0; e < KPL; ++e) {
+        const int cc = ks * M::KSTEP + KPL * grp + e;
+        sraw[ks][e] = S[sblk<D>(cc, c)];
+        draw[ks][e] = dS[sblk<D>(cc, c)];
+      }
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) {
+      const int p = i * NT + tid, row = p / PR, cp = p % PR;
+      *reinterpret_cast<u32x4_t*>(sm.wb + row * LDX + cp * VE) = vv[i];
+      *reinterpret_cast<u32x4_t*>(sm.dob + row * LDX + cp * VE) = ov[i];
     }
+  }
+  __syncthreads();
   // Kp S, then R = Diag(beta)(V - Kp S) and W = T R
   f32x4_t vmk[4], acc[4], w[4];
   {
@@ -897,7 +916,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * t + 4 * grp + j;
-        const float vv = r < loc.len ? raw_val<T>(vraw[t][j]) : 0.f;
+        const float vv = ld_f(sm.wb + r * LDX + c);  // zero past the chunk's end
         vmk[t][j] = vv - a[j];
         acc[t][j] = sm.beta[r] * vmk[t][j];
       }
@@ -918,7 +937,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      dov[t][j] = r < loc.len ? scale * raw_val<T>(oraw[t][j]) : 0.f;
+      dov[t][j] = scale * ld_f(sm.dob + r * LDX + c);  // zero past the chunk's end
       st_f(sm.wb + r * LDX + c, w[t][j]);
       st_f(sm.dob + r * LDX + c, dov[t][j]);
     }
