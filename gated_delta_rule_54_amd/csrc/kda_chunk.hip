@@ -589,9 +589,12 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
     }
   }
   {
-    // zero blocks of P above the diagonal: (R, I) = (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    // zero blocks of P above the diagonal, (R, I) = (0,1) (0,2) (0,3) (1,2)
+    // (1,3) (2,3): only those inside a k-step the state pass reads for rows
+    // R (its lowest 16-row block <= R; the others it reads as zeros)
     const int zR[6] = {0, 0, 0, 1, 1, 2}, zI[6] = {1, 2, 3, 2, 3, 3};
     for (int z = wave; z < 6; z += NW) {
+      if ((zI[z] * 16 / M::KSTEP) * M::KSTEP / 16 > zR[z]) continue;
       const int r = zR[z] * 16 + (lane & 15), i0 = zI[z] * 16 + 4 * (lane >> 4);
       st_fnat4(wP, kC / M::KSTEP, r, i0, 0.f, 0.f, 0.f, 0.f);
     }
@@ -740,7 +743,7 @@ struct K2Frags {
   BufRaw4<float> eg[CBW];
 
   // lane offsets (bytes within a record), computed once per workgroup
-  struct Offs { uint32_t wn, qg, p, kt, ut, eg; };
+  struct Offs { uint32_t wn, qg, p, kt, ut, eg, pz; };
   static __device__ __forceinline__ Offs offsets(int wave, int lane, int n0) {
     Offs o;
     o.wn = (uint32_t)(R::WN * ES) + ((wave * KD) * 64 + lane) * FB;
@@ -749,6 +752,7 @@ struct K2Frags {
     o.kt = (uint32_t)(R::KT * ES) + ((wave * CBW * KC) * 64 + lane) * FB;
     o.ut = (uint32_t)(R::UT * ES) + (((n0 / 16) * (kC / 16) + wave) * 64 + lane) * 4 * ES;
     o.eg = (uint32_t)R::BYTES_T + (wave * CBW * 16 + 4 * (lane >> 4)) * 4;
+    o.pz = (uint32_t)wave;
     return o;
   }
   // The loads come in four groups so that a step can spread them between
@@ -776,7 +780,13 @@ struct K2Frags {
           kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * KC + ks) * 64 * FB, soff);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KC; ++ks) p[ks] = BufFrag<T>::load(r, o.p + ks * 64 * FB, soff);
+      for (int ks = 0; ks < KC; ++ks) {
+        // a k-step whose lowest 16-row block lies past this wave's rows is
+        // zero (P is lower triangular): read past the bound instead (zeros,
+        // no memory access, the same instruction count in every wave)
+        const bool zero = (ks * M::KSTEP) / 16 > (int)o.pz;
+        p[ks] = BufFrag<T>::load(r, zero ? 0x40000000u : o.p + ks * 64 * FB, soff);
+      }
     }
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
