@@ -101,7 +101,9 @@ __global__ __launch_bounds__(kEpiThreads) void gate_norm_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e)
         x[e] = x[e] * inv * wv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-g[e]));
-      if (r < rows) *reinterpret_cast<u32x4e_t*>(y + off[u]) = V::pack(x);
+      // y is not read here again: stored non-temporally (measured ~2 % faster;
+      // non-temporal loads of o and z measured slower)
+      if (r < rows) __builtin_nontemporal_store(V::pack(x), reinterpret_cast<u32x4e_t*>(y + off[u]));
     }
   }
 }
