@@ -348,7 +348,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
   const int rs = H * D;  // elements between consecutive tokens
   const int span = (loc.len - 1) * rs + D;  // elements from the first to the last valid
   auto rsrc = [](const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
   };
   const __amdgpu_buffer_rsrc_t rq = rsrc(qb, span * (int)sizeof(T));
   const __amdgpu_buffer_rsrc_t rk = rsrc(kb, span * (int)sizeof(T));
@@ -785,7 +785,7 @@ struct K2Frags {
         // zero (P is lower triangular): read past the bound instead (zeros,
         // no memory access, the same instruction count in every wave)
         const bool zero = (ks * M::KSTEP) / 16 > (int)o.pz;
-        p[ks] = BufFrag<T>::load(r, zero ? 0x40000000u : o.p + ks * 64 * FB, soff);
+        p[ks] = BufFrag<T>::load(r, zero ? kPastBound : o.p + ks * 64 * FB, soff);
       }
     }
   }
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       }
 
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(ws + (int64_t)h * nrec * R::BYTES), (short)0, (int)(nrec * R::BYTES), 0x00020000);
+      (void*)(ws + (int64_t)h * nrec * R::BYTES), (short)0, (int)(nrec * R::BYTES), kRsrcWord3);
   const typename F::Offs offs = F::offsets(wave, lane, n0);
 
   // The loop runs over 32-bit record indices j in [j0, j1) relative to the
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
         (o_pend != nullptr && len_pend > 0) ? ((len_pend - 1) * H * D + WS) * (int)sizeof(T) : 0;
     // (a bound of 0 on a real address when there is no o: every store dropped)
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        o_pend ? (void*)o_pend : (void*)ws, (short)0, nbytes, 0x00020000);
+        o_pend ? (void*)o_pend : (void*)ws, (short)0, nbytes, kRsrcWord3);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       BufStore4<T>::store(ro, o_voff + nb * 16 * sizeof(T), scale * O[nb][0], scale * O[nb][1],

@@ -327,7 +327,7 @@ __device__ __forceinline__ void stage_rows(const T* q, const T* k, const float* 
   const int64_t row0 = loc.tok0 * H + h;
   const int span = (loc.len - 1) * rs + D;
   auto rsrc = [](const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
   };
   const __amdgpu_buffer_rsrc_t rkr = rsrc(k + row0 * D, span * (int)sizeof(T));
   const __amdgpu_buffer_rsrc_t rqr = rsrc(q + row0 * D, span * (int)sizeof(T));
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   auto rec_of = [&](int ci) {
     return __builtin_amdgcn_make_buffer_rsrc(
         (void*)(brec + ((int64_t)h * nslot + sp.c0 + ci) * RC::BYTES), (short)0, (int)RC::BYTES,
-        0x00020000);
+        kRsrcWord3);
   };
   auto load_m = [&](F& f, __amdgpu_buffer_rsrc_t r, int i) {
 #pragma unroll
@@ -703,10 +703,10 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     const int len = ci == nch - 1 ? len_last : kC;
     const T* ob = d_o + ((sp.tok0 + (int64_t)ci * kC) * H + h) * D + n0;
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)ob, (short)0, (int)(((len - 1) * H * D + kBwdSliceW) * sizeof(T)), 0x00020000);
+        (void*)ob, (short)0, (int)(((len - 1) * H * D + kBwdSliceW) * sizeof(T)), kRsrcWord3);
     const int tid = threadIdx.x;
     const uint32_t off = tid < NO ? (uint32_t)(((tid / LPR) * H * D + VE * (tid % LPR)) * sizeof(T))
-                                  : 0x80000000u;
+                                  : kPastBound;
     f.dov = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
   };
   auto load = [&](F& f, int ci) {
@@ -874,9 +874,9 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     constexpr int VE = 16 / (int)sizeof(T), PR = D / VE, NPK = kC * PR / NT;
     const int rs = H * D, span = (loc.len - 1) * rs + D;
     const __amdgpu_buffer_rsrc_t rvr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(vb), (short)0, span * (int)sizeof(T), 0x00020000);
+        const_cast<T*>(vb), (short)0, span * (int)sizeof(T), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ror = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(ob), (short)0, span * (int)sizeof(T), 0x00020000);
+        const_cast<T*>(ob), (short)0, span * (int)sizeof(T), kRsrcWord3);
     u32x4_t vv[NPK], ov[NPK];
 #pragma unroll
     for (int i = 0; i < NPK; ++i) {
@@ -1203,7 +1203,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     constexpr int kNt = 2;  // non-temporal: nothing here reads the gradients again
     const int rs = H * D, span = (loc.len - 1) * rs + D;
     auto rsrc = [](void* base, int bytes) {
-      return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+      return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kRsrcWord3);
     };
     const __amdgpu_buffer_rsrc_t rdk = rsrc(dkb, span * (int)sizeof(T));
     const __amdgpu_buffer_rsrc_t rdq = rsrc(dqb, span * (int)sizeof(T));

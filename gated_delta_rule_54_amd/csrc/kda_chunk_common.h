@@ -173,6 +173,14 @@ template <> struct Mma<float> {
   }
 };
 
+// Word 3 of the raw buffer resources used here (untyped 32-bit data).
+constexpr int kRsrcWord3 = 0x00020000;
+// A byte offset (1 GiB) past a resource's bound reads zeros without touching
+// memory.  Where the zeros are relied on (the state pass's record resource)
+// the bound is at most one segment's records, 160 MiB; where they are not
+// (lanes whose value is unused) a larger bound only costs a read.
+constexpr uint32_t kPastBound = 0x40000000u;
+
 // One operand fragment (a lane's KPL elements) through a buffer resource:
 // off is the lane's byte offset, soff a scalar byte offset.
 template <typename T> struct BufFrag;
