@@ -32,7 +32,7 @@ typedef unsigned int u32x4c_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2c_t __attribute__((ext_vector_type(2)));
 constexpr int kConvThreads = 256;
 constexpr int kTB = (int)kConvInPlaceMaxTokens;  // tokens per thread
-constexpr int kGroup = 8;                          // token rows loaded together
+constexpr int kGroup = 4;                          // token rows loaded together
 
 template <typename T> struct CVec;
 template <> struct CVec<float> {
