@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
     const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
     int nseg, int64_t seg_slots, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
     float* __restrict__ fin, float* __restrict__ ckpt, int64_t ckpt_every, int64_t nckpt,
-    float* __restrict__ states, float scale, T* __restrict__ o) {
+    T* __restrict__ states, float scale, T* __restrict__ o) {
   using M = Mma<T>;
   using R = Rec<T, D>;
   using F = K2Frags<T, D, WS, OUT>;
@@ -813,8 +813,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   __shared__ __align__(16) char lds_raw[(WS * LDS_S + WS * LDS_W) * sizeof(T)];
   T* sSt = reinterpret_cast<T*>(lds_raw);                // S^T slice [n][c]
   T* sWt = sSt + WS * LDS_S;                             // W^T slice [n][i]
-  constexpr int LDF = WS + 4;
-  __shared__ __align__(16) float sSf[D * LDF];           // S slice [c][n] in fp32 (states)
+  constexpr int LDF = WS + 16 / (int)sizeof(T);
+  __shared__ __align__(16) T sSf[D * LDF];               // S slice [c][n] (states)
 
   // XCD-aware placement: workgroups of one (sequence, head) share id mod 8.
   const int id = blockIdx.x;
@@ -904,21 +904,25 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
 
   auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
   // For the backward: the state entering chunk slot s0 + j, [slot][H] of
-  // slice-blocked D x D fp32 (sblk: this workgroup's slice is one
-  // contiguous D x 16 block).  Step j passes S through LDS in fp32 beside the
-  // MFMA copy, and after the barrier the block is stored in 16-byte pieces
+  // slice-blocked D x D in the MFMA type (sblk: this workgroup's slice is one
+  // contiguous D x 16 block; the backward uses S only as a product operand,
+  // rounded to that type the same way, and in one fp32 row sum).  Step j
+  // passes S through LDS beside the transposed MFMA copy, and after the
+  // barrier the block is stored in 16-byte pieces
   // -- after the step's first prefetch loads (the wait counter is in order,
   // so a store issued before them would hold up every wait for them).
   // Only the pass without o (inside the backward) writes states.
   const bool want_states = !OUT && states != nullptr;
   auto store_state = [&](int j) {
     static_assert(WS == 16, "states are stored in 16-column slices");
-    float* sd = states + ((s0 + j) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
+    T* sd = states + ((s0 + j) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
+    constexpr int VE = 16 / (int)sizeof(T), PPR = WS / VE;  // 16-byte pieces per row
 #pragma unroll
-    for (int pr = 0; pr < D * 4 / kThreads; ++pr) {
-      const int row = pr * (kThreads / 4) + threadIdx.x / 4, c4 = 4 * (threadIdx.x % 4);
-      *reinterpret_cast<float4*>(sd + row * 16 + c4) =
-          *reinterpret_cast<const float4*>(sSf + row * LDF + c4);
+    for (int pr = 0; pr < (D * PPR + kThreads - 1) / kThreads; ++pr) {
+      const int pc = pr * kThreads + threadIdx.x, row = pc / PPR, cv = VE * (pc % PPR);
+      if (D * PPR % kThreads == 0 || pc < D * PPR)
+        *reinterpret_cast<u32x4_t*>(sd + row * 16 + cv) =
+            *reinterpret_cast<const u32x4_t*>(sSf + row * LDF + cv);
     }
   };
   // One chunk step: consumes the fragments in f and fills fn with those of
@@ -938,7 +942,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
         st_perm4(sSt + n * LDS_S, c4, S[i][nb][0], S[i][nb][1], S[i][nb][2], S[i][nb][3]);
         if (want_states) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sSf[(c4 + e) * LDF + n] = S[i][nb][e];
+          for (int e = 0; e < 4; ++e) st_elem(sSf + (c4 + e) * LDF + n, S[i][nb][e]);
         }
       }
     __syncthreads();
@@ -1130,7 +1134,7 @@ template <typename T, int D>
 hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const void* v,
                      const float* g, const float* beta, const float* init_state,
                      const int32_t* cu, void* o, float* final_state, float* ckpt,
-                     float* states, char* ws, hipStream_t stream) {
+                     void* states, char* ws, hipStream_t stream) {
   const bool varlen = cu != nullptr;
   const Plan p = make_plan(d, varlen);
   const int H = d.heads, NH = d.num_seqs * d.heads;
@@ -1177,7 +1181,7 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
     auto k2 = o ? kda_state_pass<T, D, WS, true> : kda_state_pass<T, D, WS, false>;
     hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(kThreads), 0,
                        stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,
-                       carry, final_state, ckpt, d.ckpt_every, nck, states, d.scale, (T*)o);
+                       carry, final_state, ckpt, d.ckpt_every, nck, (T*)states, d.scale, (T*)o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1202,7 +1206,7 @@ int64_t chunk_slot_bound(const kda_desc_t& d, bool varlen) {
 hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* init_state,
                             const int32_t* cu_seqlens, void* o, float* final_state,
-                            float* state_ckpt, float* chunk_states, void* workspace,
+                            float* state_ckpt, void* chunk_states, void* workspace,
                             hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   const bool bf = d.dtype == KDA_DTYPE_BF16;

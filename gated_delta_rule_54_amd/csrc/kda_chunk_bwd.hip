@@ -153,22 +153,32 @@ __device__ __forceinline__ typename Mma<T>::frag acc_frag(const f32x4_t* tiles, 
   }
 }
 
-// The KPL consecutive fp32 values of row m at k-step ks (k = column,
-// contiguous) of a slice-blocked D x D state (sblk; KPL <= 8 columns never
-// cross a 16-column slice).
+// The operand fragment of row m at k-step ks (k = column, contiguous) of a
+// slice-blocked D x D state stored in the MFMA type (sblk; KPL <= 8 columns
+// never cross a 16-column slice): one 16-byte load (bf16) or one element.
 template <typename T, int D>
-__device__ __forceinline__ void grow_vals(const float* X, int m, int ks, int lane, float* x) {
+__device__ __forceinline__ typename Mma<T>::frag grow_frag(const T* X, int m, int ks, int lane) {
   using M = Mma<T>;
-  const float* p = X + sblk<D>(m, ks * M::KSTEP + M::KPL * (lane >> 4));
+  const T* p = X + sblk<D>(m, ks * M::KSTEP + M::KPL * (lane >> 4));
   if constexpr (M::KPL == 8) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    return __builtin_bit_cast(typename M::frag, *reinterpret_cast<const u32x4_t*>(p));
   } else {
-    x[0] = p[0];
+    return p[0];
   }
 }
+// Element e of a fragment as fp32.
+__device__ __forceinline__ float frag_val(bf16x8_t f, int e) {
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, f);
+  return (e & 1) ? __uint_as_float(u[e >> 1] & 0xffff0000u) : __uint_as_float(u[e >> 1] << 16);
+}
+__device__ __forceinline__ float frag_val(float f, int) { return f; }
+// KPL raw elements (ld_raw bits) to an operand fragment.
+__device__ __forceinline__ bf16x8_t raw_frag(const uint32_t* x, bf16) {
+  const u32x4_t u = {x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16),
+                     x[6] | (x[7] << 16)};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ float raw_frag(const uint32_t* x, float) { return __uint_as_float(x[0]); }
 
 // One element as raw bits (a load whose value is converted only at use does
 // not make the wave wait where it is issued), and its value.
@@ -633,7 +643,7 @@ struct BwdPassFrags {
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     const char* __restrict__ brec, int64_t nslot, ChunkGeom gm, int H, int NH, int nslice,
-    const T* __restrict__ d_o, const float* __restrict__ dfinal, float* __restrict__ dstates,
+    const T* __restrict__ d_o, const float* __restrict__ dfinal, T* __restrict__ dstates,
     float* __restrict__ dinit) {
   using M = Mma<T>;
   using RC = BRec<T, D>;
@@ -641,11 +651,11 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   constexpr int CBW = F::CBW, KD = F::KD, KC = F::KC, LDS_S = D + 8;
   constexpr int VE = F::VE, LPR = F::LPR, NO = F::NO;
   // per chunk, double-buffered: dS' in the MFMA type (the exchange), dO^T
-  // (columns n, rows r), and dS' in fp32 for the store to dstates
-  constexpr int LDO = kC + 16 / (int)sizeof(T), LDF = kBwdSliceW + 4;
+  // (columns n, rows r), and dS' untransposed for the store to dstates
+  constexpr int LDO = kC + 16 / (int)sizeof(T), LDF = kBwdSliceW + 16 / (int)sizeof(T);
   __shared__ __align__(16) T sD[2][kBwdSliceW * LDS_S];
   __shared__ __align__(16) T sO[2][kBwdSliceW * LDO];
-  __shared__ __align__(16) float sF[2][D * LDF];
+  __shared__ __align__(16) T sF[2][D * LDF];
   const int id = blockIdx.x;
   const int nh = (id & 7) + 8 * (id / (8 * nslice));
   const int slice = (id >> 3) % nslice;
@@ -719,18 +729,19 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   // chunk cn, the loads spread over the step (a wave issuing a whole record
   // at once stalls behind the CU's vector memory queue).  dS on entry is dS'
   // of chunk ci (the gradient of the state leaving it): it crosses LDS in
-  // the MFMA type for the product and in fp32 for dstates (kda_bwd_intra
-  // reads it), whose slice block is then stored in 16-byte pieces.  The dO
+  // the MFMA type, transposed for the product and as is for dstates
+  // (kda_bwd_intra reads it only as an operand of that type and in one fp32
+  // row sum), whose slice block is then stored in 16-byte pieces.  The dO
   // slice crosses LDS transposed, so each lane's fragment is two runs of rows.
   auto step = [&](const F& f, F& fn, int ci, int cn, int buf) {
     T* sb = sD[buf];
-    float* sf = sF[buf];
+    T* sf = sF[buf];
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       const int c4 = (wave * CBW + i) * 16 + 4 * grp;
       st_perm4(sb + (lane & 15) * LDS_S, c4, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sf[(c4 + j) * LDF + (lane & 15)] = dS[i][j];
+      for (int j = 0; j < 4; ++j) st_elem(sf + (c4 + j) * LDF + (lane & 15), dS[i][j]);
     }
     if (threadIdx.x < NO) {
       const int r = threadIdx.x / LPR, cb = VE * (threadIdx.x % LPR);
@@ -774,14 +785,18 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     const __amdgpu_buffer_rsrc_t rn = rec_of(cn);
     load_m(fn, rn, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // dS' of chunk ci: this slice's contiguous D x 16 block (sblk), 4
-    // threads per row
-    float* dst = dstates + ((sp.c0 + ci) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
+    // dS' of chunk ci: this slice's contiguous D x 16 block (sblk), in
+    // 16-byte pieces (2 per row in bf16, 4 in fp32)
+    T* dst = dstates + ((sp.c0 + ci) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
+    {
+      constexpr int VEF = 16 / (int)sizeof(T), PPR = kBwdSliceW / VEF, NPC = D * PPR;
 #pragma unroll
-    for (int pr = 0; pr < D * 4 / kBwdPassThreads; ++pr) {
-      const int row = pr * (kBwdPassThreads / 4) + threadIdx.x / 4, c4 = 4 * (threadIdx.x % 4);
-      *reinterpret_cast<float4*>(dst + row * 16 + c4) =
-          *reinterpret_cast<const float4*>(sf + row * LDF + c4);
+      for (int pr = 0; pr < (NPC + kBwdPassThreads - 1) / kBwdPassThreads; ++pr) {
+        const int pc = pr * kBwdPassThreads + threadIdx.x, row = pc / PPR, cv = VEF * (pc % PPR);
+        if (NPC % kBwdPassThreads == 0 || pc < NPC)
+          *reinterpret_cast<u32x4_t*>(dst + row * 16 + cv) =
+              *reinterpret_cast<const u32x4_t*>(sf + row * LDF + cv);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -825,7 +840,7 @@ template <typename T, int D, bool GS>
 __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ d_o,
-    const float* __restrict__ states, const float* __restrict__ dstates, ChunkGeom gm, int H,
+    const T* __restrict__ states, const T* __restrict__ dstates, ChunkGeom gm, int H,
     int64_t slot_base, int qk_l2norm, float scale, T* __restrict__ dq, T* __restrict__ dk,
     T* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta) {
@@ -846,8 +861,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);  // this lane's column (d_k or d_v)
-  const float* S = states + (slot * H + h) * (int64_t)D * D;
-  const float* dS = dstates + (slot * H + h) * (int64_t)D * D;
+  const T* S = states + (slot * H + h) * (int64_t)D * D;
+  const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
   // per-token tensors: uniform bases at the chunk's first row, 32-bit offsets
   const int64_t row0 = loc.tok0 * H + h;
   const T* vb = v + row0 * D;
@@ -868,7 +883,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // go (the inverse's region, dead now): each lane then reads its own column
   // and later overwrites exactly those positions, so no barrier separates
   // the reads from the W and dO' writes.
-  float sraw[KD][KPL], draw[KD][KPL];
+  uint32_t sraw[KD][KPL], draw[KD][KPL];
   {
     constexpr int NT = L::NT;
     constexpr int VE = 16 / (int)sizeof(T), PR = D / VE, NPK = kC * PR / NT;
@@ -890,8 +905,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         const int cc = ks * M::KSTEP + KPL * grp + e;
-        sraw[ks][e] = S[sblk<D>(cc, c)];
-        draw[ks][e] = dS[sblk<D>(cc, c)];
+        sraw[ks][e] = ld_raw(S + sblk<D>(cc, c));
+        draw[ks][e] = ld_raw(dS + sblk<D>(cc, c));
       }
 #pragma unroll
     for (int i = 0; i < NPK; ++i) {
@@ -906,7 +921,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   {
     typename M::frag sb[KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) sb[ks] = to_frag(sraw[ks], T{});
+    for (int ks = 0; ks < KD; ++ks) sb[ks] = raw_frag(sraw[ks], T{});
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
@@ -945,7 +960,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   {
     typename M::frag dsb[KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) dsb[ks] = to_frag(draw[ks], T{});
+    for (int ks = 0; ks < KD; ++ks) dsb[ks] = raw_frag(draw[ks], T{});
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
@@ -1046,11 +1061,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   {
     typename M::frag st[KD], kmc[KC];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) {
-      float xs[KPL];
-      grow_vals<T, D>(S, c, ks, lane, xs);
-      st[ks] = to_frag(xs, T{});
-    }
+    for (int ks = 0; ks < KD; ++ks) st[ks] = grow_frag<T, D>(S, c, ks, lane);
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks) kmc[ks] = frag_cm<T>(sm.km, LDX, 16 * wave, ks, lane);
 #pragma unroll
@@ -1084,12 +1095,10 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     typename M::frag dst[KD], kpc[KC], qpc[KC];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
-      float xs[KPL], xd[KPL];
-      grow_vals<T, D>(S, c, ks, lane, xs);
-      grow_vals<T, D>(dS, c, ks, lane, xd);
+      const typename M::frag xs = grow_frag<T, D>(S, c, ks, lane);
+      dst[ks] = grow_frag<T, D>(dS, c, ks, lane);
 #pragma unroll
-      for (int e = 0; e < KPL; ++e) rs += xs[e] * xd[e];
-      dst[ks] = to_frag(xd, T{});
+      for (int e = 0; e < KPL; ++e) rs += frag_val(xs, e) * frag_val(dst[ks], e);
     }
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks) {
@@ -1261,7 +1270,9 @@ BwdPlan bwd_plan(const kda_desc_t& d) {
   kda_desc_t df = d;
   df.ckpt_every = 0;
   p.fwd = align256((int64_t)chunk_workspace_bytes(df));
-  p.states = align256(p.slots * d.heads * (int64_t)d.dk * d.dv * 4);
+  // S and dS' in the MFMA type (the element type of q/k/v)
+  p.states = align256(p.slots * d.heads * (int64_t)d.dk * d.dv *
+                      (d.dtype == KDA_DTYPE_BF16 ? 2 : 4));
   const int64_t rb = d.dtype == KDA_DTYPE_BF16
                          ? (d.dk == 128 ? BRec<bf16, 128>::BYTES : BRec<bf16, 64>::BYTES)
                          : (d.dk == 128 ? BRec<float, 128>::BYTES : BRec<float, 64>::BYTES);
@@ -1280,8 +1291,8 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   const BwdPlan p = bwd_plan(d);
   const bool varlen = cu != nullptr;
   const int H = d.heads, NH = d.num_seqs * d.heads;
-  float* states = reinterpret_cast<float*>(ws + p.fwd);
-  float* dstates = reinterpret_cast<float*>(ws + p.fwd + p.states);
+  T* states = reinterpret_cast<T*>(ws + p.fwd);
+  T* dstates = reinterpret_cast<T*>(ws + p.fwd + p.states);
   char* recs = ws + p.fwd + 2 * p.states;
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.fwd + 2 * p.states + p.recs);
   int32_t* cu_s = chunk_off + (p.map / 2) / 4;

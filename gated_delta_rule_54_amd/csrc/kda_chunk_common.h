@@ -37,6 +37,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One fp32 value stored as an element of the MFMA type (bf16: rounded to
+// nearest even, as the packed conversion of the operand fragments rounds).
+__device__ __forceinline__ void st_elem(bf16* p, float x) {
+  *reinterpret_cast<uint16_t*>(p) = bf_bits(x);
+}
+__device__ __forceinline__ void st_elem(float* p, float x) { *p = x; }
+
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const bf16* p) {
   return bf_val(*reinterpret_cast<const uint16_t*>(p));

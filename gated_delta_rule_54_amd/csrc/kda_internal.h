@@ -16,14 +16,15 @@ hipError_t launch_decode(const kda_desc_t& d, const void* q, const void* k, cons
 
 // Chunkwise prefill.  Workspace size and launch plan live in kda_chunk.hip.
 // chunk_states (or nullptr): the state entering every chunk slot, [slot][H]
-// of D x D fp32 slice-blocked as sblk (kda_chunk_common.h) lays it out, for
-// the backward; only with o == nullptr (the
-// pass that writes states produces no output; both set is an invalid value).
+// of D x D in the element type of q/k/v (bf16 or fp32), slice-blocked as sblk
+// (kda_chunk_common.h) lays it out, for the backward; only with o == nullptr
+// (the pass that writes states produces no output; both set is an invalid
+// value).
 size_t chunk_workspace_bytes(const kda_desc_t& d);
 hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* init_state,
                             const int32_t* cu_seqlens, void* o, float* final_state,
-                            float* state_ckpt, float* chunk_states, void* workspace,
+                            float* state_ckpt, void* chunk_states, void* workspace,
                             hipStream_t stream);
 // Chunk slots of a batch (dense: B * ceil(T/64); varlen: an upper bound that
 // does not read cu_seqlens, T/64 + N).
