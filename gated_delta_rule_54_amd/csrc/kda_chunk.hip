@@ -287,12 +287,16 @@ __device__ __attribute__((noinline)) void k1_exact_ap(
 }
 
 // GS: one gate per (token, head), broadcast over the key channels (Gated
-// DeltaNet) instead of one per channel.
-template <typename T, int D, bool GS>
+// DeltaNet) instead of one per channel.  RO = false: the records feed a
+// state pass without output (inside the backward), which reads neither
+// Q o e^G nor P, so those blocks are not written (the exact-decay path
+// still writes its P).
+template <typename T, int D, bool GS, bool RO>
 __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) void kda_intra_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
     int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws) {
+  constexpr bool rec_out = RO;
   using L = K1Lds<T, D>;
   using M = Mma<T>;
   using R = Rec<T, D>;
@@ -465,7 +469,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
       // operations as __expf, so the same values)
       const float gsx = G[jj].x * kLog2eF, gsy = G[jj].y * kLog2eF;
       const float egx = __builtin_amdgcn_exp2f(gsx), egy = __builtin_amdgcn_exp2f(gsy);
-      if (direct) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
+      if (direct && rec_out) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
       kgx[e] = khx * egx;
       kgy[e] = khy * egy;
       if (!exact) {
@@ -512,7 +516,8 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
   if constexpr (kStaged) {
     if (!exact) {
       constexpr int QB = (kC / 16) * (D / 32), KB = (D / 16) * (kC / 32);  // blocks
-      for (int sidx = tid; sidx < (QB + KB) * 64; sidx += NT) {
+      // (a pass without output reads no Q o e^G: its blocks are skipped)
+      for (int sidx = tid + (RO ? 0 : QB * 64); sidx < (QB + KB) * 64; sidx += NT) {
         const int b = sidx >> 6, L = sidx & 63, g = L >> 4;
         float v[8];
         if (b < QB) {  // Q o e^G: rows r, k = channel
@@ -585,10 +590,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
         p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
       }
       *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-      st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
+      if (rec_out) st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
     }
   }
-  {
+  if (rec_out) {
     // zero blocks of P above the diagonal, (R, I) = (0,1) (0,2) (0,3) (1,2)
     // (1,3) (2,3): only those inside a k-step the state pass reads for rows
     // R (its lowest 16-row block <= R; the others it reads as zeros)
@@ -1152,8 +1157,10 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   const int k1_lds = K1Lds<T, D>::BYTES;
   static bool attr_set = false;
   if (!attr_set) {
-    for (const void* fn : {(const void*)kda_intra_chunk<T, D, false>,
-                           (const void*)kda_intra_chunk<T, D, true>}) {
+    for (const void* fn : {(const void*)kda_intra_chunk<T, D, false, true>,
+                           (const void*)kda_intra_chunk<T, D, true, true>,
+                           (const void*)kda_intra_chunk<T, D, false, false>,
+                           (const void*)kda_intra_chunk<T, D, true, false>}) {
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
       if (e != hipSuccess) return e;
     }
@@ -1171,7 +1178,10 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   for (int64_t s = 0; s < nseg; ++s) {
     const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
     if (s1 > s0) {
-      auto k1 = d.gate_per_head ? kda_intra_chunk<T, D, true> : kda_intra_chunk<T, D, false>;
+      auto k1 = o != nullptr ? (d.gate_per_head ? kda_intra_chunk<T, D, true, true>
+                                                : kda_intra_chunk<T, D, false, true>)
+                             : (d.gate_per_head ? kda_intra_chunk<T, D, true, false>
+                                                : kda_intra_chunk<T, D, false, false>);
       hipLaunchKernelGGL(k1, dim3(H, (unsigned)(s1 - s0)), dim3(k1_threads<T, D>()), k1_lds,
                          stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
                          s1 - s0, d.qk_l2norm, recs);
