@@ -136,8 +136,10 @@ kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
 /* Bytes of device workspace kda_chunk_bwd needs for this descriptor (an upper
  * bound that does not read cu_seqlens); 0 for an invalid or unsupported
  * descriptor.  It holds a forward workspace plus, per chunk slot and head,
- * the entering state and its gradient (2 x dk x dv x 4 bytes) and the
- * reverse pass's operands ((dk + 64) x dk elements of dtype). */
+ * the entering state and its gradient (2 x dk x dv elements of dtype: they
+ * serve only as operands of products in that type, and in one fp32 row sum
+ * of the gate gradient) and the reverse pass's operands ((dk + 64) x dk
+ * elements of dtype). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
 
 /* Gradients of kda_chunk_fwd (training).  [XT §5: training runs the
