@@ -30,7 +30,7 @@ namespace {
 
 typedef unsigned int u32x4c_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2c_t __attribute__((ext_vector_type(2)));
-constexpr int kConvThreads = 256;
+constexpr int kConvThreads = 64;  // small workgroups spread the few long-lived ones evenly
 constexpr int kTB = (int)kConvInPlaceMaxTokens;  // tokens per thread
 constexpr int kGroup = 4;                          // token rows loaded together
 
