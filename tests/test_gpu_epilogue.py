@@ -72,6 +72,20 @@ def test_gate_norm_prefill_rows_sampled():
     assert_close("sampled rows", y[idx], ref, TOL[torch.bfloat16])
 
 
+def test_gate_norm_grid_stride_sampled():
+    """More rows than one pass of the largest grid covers (16384 one-wave
+    workgroups x 16 rows of 128): the grid-stride loop and a ragged last
+    pass, checked on sampled rows and on the last 64 rows."""
+    rows, dv = 8192 * 32 + 12345, 128
+    o, z, w = _inputs(rows, dv, torch.bfloat16, seed=13)
+    y = kda_output_gate_norm(o, z, w, eps=1e-6)
+    torch.cuda.synchronize()
+    pick = np.random.default_rng(4).choice(rows, 2000, replace=False)
+    idx = torch.from_numpy(np.concatenate([pick, np.arange(rows - 64, rows)])).to(DEV)
+    ref = O.gate_norm(o[idx].cpu(), z[idx].cpu(), w.cpu(), eps=1e-6)
+    assert_close("sampled rows", y[idx], ref, TOL[torch.bfloat16])
+
+
 def test_prefill_then_epilogue():
     """The path as the layer runs it: prefill, then the epilogue on its output,
     against the oracle's prefill followed by the oracle's epilogue."""
