@@ -430,9 +430,171 @@ def cpu_baseline(inp, heads_sample: int, min_seconds: float = 10.0):
     # tokens/s of the whole problem (all heads) at this per-head rate
     full_heads = inp["q"].shape[2]
     return dict(value=reps * B * T * heads_sample / full_heads / dt, unit="tokens/s",
-                cores=threads, kind="oracle",
+                cores=threads, kind="oracle", cpu_model=_cpu_model(),
                 sample=f"all {T} tokens of {heads_sample} of {full_heads} heads, {reps} repetitions "
                        f"(fp64, {dt:.1f} s wall on {threads} threads); value scaled to all heads")
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _rocm_version() -> str:
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            continue
+    return getattr(torch.version, "hip", None) or "unknown"
+
+
+def _git_sha():
+    import subprocess
+    try:
+        return subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                              text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def _source_sha256() -> str:
+    """SHA-256 over the library sources, the binding and this file (the box
+    that runs the benchmark has no git metadata)."""
+    import glob
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_54_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "gated_delta_rule_54_amd", "*.py")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")) + [os.path.abspath(__file__)])
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.relpath(path, ROOT).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _tensor_sha256(t: torch.Tensor) -> str:
+    b = t.detach().contiguous().view(torch.uint8).cpu().numpy().tobytes()
+    return hashlib.sha256(b).hexdigest()
+
+
+def reproducibility(inputs_sha: dict) -> dict:
+    props = torch.cuda.get_device_properties(0)
+    return {"device": torch.cuda.get_device_name(0), "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "cpu_model": _cpu_model(),
+            "host_threads": len(os.sched_getaffinity(0)), "rocm": _rocm_version(),
+            "torch": torch.__version__, "git_sha": _git_sha(), "source_sha256": _source_sha256(),
+            "inputs_sha256": inputs_sha}
+
+
+def _flush(buf: torch.Tensor):
+    """Overwrite a scratch buffer larger than the last-level cache (256 MB)."""
+    buf.fill_(1)
+
+
+def bench_prefill_flushed(inp, steps: int, flush_mb: int = 512):
+    """The prefill call timed one at a time with HIP events, a 512 MB scratch
+    write between calls (outside the events), so no input is served from the
+    last-level cache by an earlier call."""
+    B, T, H, d = inp["q"].shape
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    desc = make_desc(batch=B, num_seqs=B, seqlen=T, heads=H, dk=d, dv=d, dtype=inp["q"].dtype)
+    ws = torch.empty(chunk_fwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    evs = [_events() for _ in range(steps)]
+    for e0, e1 in evs:
+        _flush(scratch)
+        e0.record(stream)
+        kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["init_state"],
+                      out=o, final_state=fs, workspace=ws, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    return ms
+
+
+def bench_varlen(steps: int, warmup: int):
+    """The varlen workload: 16 packed sequences, lengths U[1024, 32768],
+    32 heads, nonzero initial states; calls back to back."""
+    w = W.VARLEN_16
+    inp = W.workload_inputs(w, "cuda")
+    cu = inp["cu_seqlens"]
+    total = int(cu[-1].item())
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty_like(inp["init_state"])
+    desc = make_desc(batch=1, num_seqs=w.num_seqs, seqlen=total, heads=w.heads, dk=w.dk,
+                     dv=w.dv, dtype=w.dtype)
+    ws = torch.empty(chunk_fwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                inp["init_state"], cu, out=o, final_state=fs, workspace=ws,
+                                stream=stream)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    th = total * w.heads
+    sha = {k: _tensor_sha256(inp[k]) for k in ("q", "k", "v", "g", "beta", "init_state",
+                                                 "cu_seqlens")}
+    gbs = PREFILL_BYTES_PER_TH * th / (ms * 1e-3) / 1e9
+    return {"workload": w.describe() + " (nonzero initial states)", "tokens": total,
+            "lengths": torch.diff(cu).tolist(), "us_per_call": ms * 1e3,
+            "value": total / (ms * 1e-3), "unit": "tokens/s",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_token_head": PREFILL_BYTES_PER_TH,
+                         "hbm_floor_us": PREFILL_BYTES_PER_TH * th / (HBM_PEAK_GBS * 1e9) * 1e6}}, sha
+
+
+def bench_prefill_1m(steps: int = 3):
+    """The 1,048,576-token workload (32 heads, checkpoints every 65,536
+    tokens): one warm-up call, then `steps` calls back to back."""
+    w = W.PREFILL_1M
+    inp = W.workload_inputs(w, "cuda")
+    B, T, H, d = inp["q"].shape
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    ck = torch.empty((B, T // w.ckpt_every, H, d, d), dtype=torch.float32, device="cuda")
+    desc = make_desc(batch=B, num_seqs=B, seqlen=T, heads=H, dk=d, dv=d, dtype=w.dtype,
+                     ckpt_every=w.ckpt_every)
+    ws = torch.empty(chunk_fwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                ckpt_every=w.ckpt_every, out=o, final_state=fs, state_ckpt=ck,
+                                workspace=ws, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    th = B * T * H
+    gbs = PREFILL_BYTES_PER_TH * th / (ms * 1e-3) / 1e9
+    # inputs hashed over their first 65,536 tokens (hashing 40 GB would take minutes)
+    sha = {k: _tensor_sha256(inp[k][:, :65536]) for k in ("q", "k", "v", "g", "beta")}
+    del inp
+    return {"workload": w.describe() + ", checkpoints written", "tokens": B * T,
+            "us_per_call": ms * 1e3, "value": B * T / (ms * 1e-3), "unit": "tokens/s",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_token_head": PREFILL_BYTES_PER_TH,
+                         "hbm_floor_us": PREFILL_BYTES_PER_TH * th / (HBM_PEAK_GBS * 1e9) * 1e6}}, sha
 
 
 def main():
@@ -465,12 +627,17 @@ def main():
         probe()
         return
     pf = bench_prefill(args.steps, args.warmup)
+    pf_cold_ms = bench_prefill_flushed(pf["inp"], args.steps)
+    inputs_sha = {"prefill_8k": {k: _tensor_sha256(pf["inp"][k])
+                                 for k in ("q", "k", "v", "g", "beta")}}
     tr_prefill, tr_decode, tr_epi, tr_pro, tr_bwd = measured_traffic()
     dc = bench_decode(min(args.warmup, 8))
     ep = bench_epilogue(args.steps, args.warmup)
     gm = bench_gate_modes()
     pl = bench_prologue(args.steps, args.warmup)
     bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 2))
+    vl, inputs_sha["varlen"] = bench_varlen(max(1, args.steps // 2), 2)
+    m1, inputs_sha["prefill_1m_first_65536_tokens"] = bench_prefill_1m()
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -497,7 +664,11 @@ def main():
                      "kernel": "kda_chunk_fwd (intra-chunk + state-pass launches of one call)",
                      "bytes_per_token_head": PREFILL_BYTES_PER_TH,
                      "mfma_tflops": pf["achieved_tflops"],
-                     "mfma_frac": pf["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS},
+                     "mfma_frac": pf["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                     "us_per_call": pf["ms"] * 1e3,
+                     "hbm_floor_us": PREFILL_BYTES_PER_TH * pf["token_heads"] / (HBM_PEAK_GBS * 1e9) * 1e6,
+                     "flushed_us_per_call": pf_cold_ms * 1e3,
+                     "flushed_frac": PREFILL_BYTES_PER_TH * pf["token_heads"] / (pf_cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "decode": {"workload": dc["w"].describe(), "value": dc["tokens_per_s"],
                    "unit": "tokens/s", "ms_per_step": dc["ms_step"],
                    "roofline": {"bound": "hbm", "achieved": dc["achieved_gbs"],
@@ -542,10 +713,13 @@ def main():
         "gate_modes": {"workload": "prefill B=1 H=16 d=128 bf16, T = 2K..64K: per-channel "
                                    "gates (KDA) vs one gate per token and head (GDN)",
                        "rows": gm},
+        "varlen": vl,
+        "prefill_1m": m1,
         "wall_s_prefill_loop": pf["wall"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf["inp"], args.cpu_heads)
+    line["reproducibility"] = reproducibility(inputs_sha)
     print(json.dumps(line), flush=True)
 
 

@@ -84,6 +84,11 @@ struct Rec {
   static constexpr int64_t BYTES_T = END * (int64_t)sizeof(T);
   static constexpr int64_t BYTES = ((BYTES_T + D * 4 + 255) / 256) * 256;  // + e^gamma
 };
+// The state pass addresses one head's records of a segment through a buffer
+// resource with 32-bit offsets and relies on reads at kPastBound returning
+// zeros: a segment's records per head must stay below that offset.
+static_assert(kSegSlotsMax * Rec<float, 128>::BYTES < (int64_t)kPastBound,
+              "one head's segment records must stay below the past-the-bound offset");
 
 // ---------------------------------------------------------------------------
 // K1: intra-chunk transform.  LDS holds three equal regions, reused by phase:
@@ -1113,7 +1118,8 @@ int64_t seg_slots(const kda_desc_t& d) {
   static const int64_t env = [] {
     const char* e = getenv("KDA_SEG_SLOTS");
     const long long x = e ? atoll(e) : 0;
-    return x >= 8 && x <= (1 << 20) ? (int64_t)x : (int64_t)0;
+    return x > 0 ? std::max<int64_t>(8, std::min<int64_t>(kSegSlotsMax, x)) & ~(int64_t)7
+                 : (int64_t)0;
   }();
   if (env) return env;
   const int64_t per_slot = (int64_t)d.heads * rec_bytes_for(d);
@@ -1155,8 +1161,11 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   const int nslice = D / WS;
   const int nhpad = (NH + 7) / 8 * 8;
   const int k1_lds = K1Lds<T, D>::BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the per-chunk states are written only by the pass without o
+  if (o != nullptr && states != nullptr) return hipErrorInvalidValue;
+  // K1's dynamic LDS limit, once per device
+  static std::atomic<uint64_t> attr_done{0};
+  hipError_t ea = once_per_device(attr_done, [&]() {
     for (const void* fn : {(const void*)kda_intra_chunk<T, D, false, true>,
                            (const void*)kda_intra_chunk<T, D, true, true>,
                            (const void*)kda_intra_chunk<T, D, false, false>,
@@ -1164,8 +1173,9 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
       if (e != hipSuccess) return e;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (ea != hipSuccess) return ea;
   const int64_t nck = d.ckpt_every > 0 ? d.seqlen / d.ckpt_every : 0;
   ChunkGeom gm{nullptr, nullptr, d.seqlen, (d.seqlen + kC - 1) / kC, d.num_seqs};
   if (varlen) {
@@ -1186,8 +1196,6 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                          stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
                          s1 - s0, d.qk_l2norm, recs);
     }
-    // (the per-chunk states are written only by the pass without o)
-    if (o != nullptr && states != nullptr) return hipErrorInvalidValue;
     auto k2 = o ? kda_state_pass<T, D, WS, true> : kda_state_pass<T, D, WS, false>;
     hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(kThreads), 0,
                        stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,

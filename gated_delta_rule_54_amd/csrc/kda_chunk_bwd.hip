@@ -1310,20 +1310,21 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
     gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
   }
   using LP = BwdLds<T, D, true>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<uint64_t> attr_done{0};
+  e = once_per_device(attr_done, [&]() {
     for (const void* fn : {(const void*)kda_bwd_prep<T, D, false>,
                            (const void*)kda_bwd_prep<T, D, true>}) {
-      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LP::BYTES);
-      if (e != hipSuccess) return e;
+      hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LP::BYTES);
+      if (ea != hipSuccess) return ea;
     }
     for (const void* fn : {(const void*)kda_bwd_intra<T, D, false>,
                            (const void*)kda_bwd_intra<T, D, true>}) {
-      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
-      if (e != hipSuccess) return e;
+      hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+      if (ea != hipSuccess) return ea;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (e != hipSuccess) return e;
   // chunk slots go in the grid's y dimension, at most kMaxGridY per launch
   constexpr int64_t kMaxGridY = 32768;
   auto prep = d.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;

@@ -5,9 +5,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kda.h"
 
 namespace kda {
+
+// Runs `set` (kernel attribute calls, idempotent) the first time a call site
+// reaches it on each device; `done` holds one bit per device id.  Two threads
+// may both run `set` for the same device, which is harmless.
+template <typename F>
+hipError_t once_per_device(std::atomic<uint64_t>& done, F&& set) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t e = set();
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Launch the single-token decode kernel.  Shapes are validated by the caller.
 hipError_t launch_decode(const kda_desc_t& d, const void* q, const void* k, const void* v,

@@ -10,7 +10,9 @@ call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -129,6 +131,24 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _on(stream):
+    """Allocation context for a call launched on `stream`: tensors the
+    binding allocates (outputs, workspace) come from that stream's pool, so
+    the caching allocator hands a freed block (the workspace, once the call
+    returns) only to later work on the same stream, which the stream orders
+    after the kernels that still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _stream_scoped(fn):
+    """Run a binding call with its allocations on the call's stream (_on)."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kwargs):
+        with _on(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return wrapped
+
+
 def _stream_handle(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -148,6 +168,7 @@ def chunk_fwd_workspace_bytes(desc: KdaDesc) -> int:
     return int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
 
 
+@_stream_scoped
 def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2norm=True,
                   scale=1.0, ckpt_every=0, out=None, final_state=None, want_final=True,
                   state_ckpt=None, workspace=None, stream=None):
@@ -207,6 +228,7 @@ def chunk_bwd_workspace_bytes(desc: KdaDesc) -> int:
     return int(load_library().kda_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
 
 
+@_stream_scoped
 def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens=None, *,
                   qk_l2norm=True, scale=1.0, want_dinit=True, workspace=None, stream=None):
     """Gradients of the chunkwise KDA prefill through the C ABI.
@@ -257,6 +279,7 @@ def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens
     return dq, dkk, dvv, dg, db, dinit
 
 
+@_stream_scoped
 def kda_decode_step(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, out=None,
                     stream=None):
     """One KDA decode step through the C ABI; `state` [N, H, dk, dv] fp32 is
@@ -284,6 +307,7 @@ def kda_decode_step(q, k, v, g, beta, state, *, qk_l2norm=True, scale=1.0, out=N
     return out
 
 
+@_stream_scoped
 def kda_output_gate_norm(o, z, w=None, *, eps=1e-6, out=None, stream=None):
     """Output epilogue through the C ABI: head-wise RMSNorm of o times
     sigmoid(z).  o, z: [..., dv] (same dtype and shape, contiguous); w: [dv]
@@ -305,6 +329,7 @@ def kda_output_gate_norm(o, z, w=None, *, eps=1e-6, out=None, stream=None):
     return out
 
 
+@_stream_scoped
 def kda_short_conv_swish(x, w, bias=None, state=None, cu_seqlens=None, *, want_state=True,
                          state_out=None, out=None, stream=None):
     """ShortConv + Swish through the C ABI.  x: [B, T, C] (float32 or

@@ -213,3 +213,27 @@ def test_long_needle():
         for h in range(H):
             err = (got[i, h] - vals[i]).abs().max().item()
             assert err < 1e-5, f"needle {i} head {h}: error {err}"
+
+
+def test_prefill_on_side_stream():
+    """Calls launched on a stream other than the current one: the binding
+    allocates the workspace and outputs on that stream, so work queued on
+    the current stream right after (which reuses freed blocks) cannot touch
+    memory the side stream's kernels still use."""
+    side = torch.cuda.Stream()
+    inps = [_inputs(1, 1024, 8, 128, torch.bfloat16, seed=300 + i) for i in range(3)]
+    torch.cuda.synchronize()
+    outs = []
+    for inp in inps:
+        outs.append(kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                  inp["init_state"], stream=side))
+        # current-stream work that would land in any block freed above
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device=DEV)
+        junk.fill_(0xFF)
+        del junk
+    torch.cuda.synchronize()
+    for inp, (o, fs, _) in zip(inps, outs):
+        o_ref, fs_ref, _ = O.kda_fwd(*(inp[k].cpu() for k in ("q", "k", "v", "g", "beta")),
+                                     inp["init_state"].cpu())
+        assert_close("o (side stream)", o, o_ref, TOL[torch.bfloat16])
+        assert_close("final_state (side stream)", fs, fs_ref, TOL[torch.bfloat16])
