@@ -98,12 +98,13 @@ KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(const kda_desc_t* desc) {
   return kda::chunk_workspace_bytes(*desc);
 }
 
-KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
-                                      const void* v, const float* g, const float* beta,
-                                      const float* init_state, const int32_t* cu_seqlens,
-                                      void* o, float* final_state, float* state_ckpt,
-                                      void* workspace, size_t workspace_bytes,
-                                      hipStream_t stream) {
+namespace {
+// Validation shared by kda_chunk_fwd and kda_chunk_fwd_noalloc (everything
+// but the workspace).
+kda_status_t check_chunk_fwd_args(const kda_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta,
+                                  const float* init_state, const int32_t* cu_seqlens, void* o,
+                                  float* final_state, float* state_ckpt) {
   kda_status_t st = check_chunk_desc(desc);
   if (st != KDA_OK) return st;
   const kda_desc_t& d = *desc;
@@ -133,15 +134,29 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i],
                   (int)align[i]);
   }
-  const void* opt[] = {init_state, final_state, state_ckpt, workspace};
-  const char* onames[] = {"init_state", "final_state", "state_ckpt", "workspace"};
-  const uintptr_t oalign[] = {4, 4, 4, 16};
-  for (int i = 0; i < 4; ++i)
-    if (opt[i] && !aligned(opt[i], oalign[i]))
-      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", onames[i],
-                  (int)oalign[i]);
+  const void* opt[] = {init_state, final_state, state_ckpt};
+  const char* onames[] = {"init_state", "final_state", "state_ckpt"};
+  for (int i = 0; i < 3; ++i)
+    if (opt[i] && !aligned(opt[i], 4))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", onames[i]);
   if (o && (o == q || o == k || o == v || o == (const void*)g || o == (const void*)beta))
     return fail(KDA_ERR_INVALID_ARGUMENT, "o must not alias an input");
+  return KDA_OK;
+}
+}  // namespace
+
+KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
+                                      const void* v, const float* g, const float* beta,
+                                      const float* init_state, const int32_t* cu_seqlens,
+                                      void* o, float* final_state, float* state_ckpt,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  kda_status_t st = check_chunk_fwd_args(desc, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                         final_state, state_ckpt);
+  if (st != KDA_OK) return st;
+  const kda_desc_t& d = *desc;
+  if (workspace && !aligned(workspace, 16))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
   const size_t need_ws = kda::chunk_workspace_bytes(d);
   if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu%s", need_ws,
@@ -149,6 +164,30 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
   hipError_t e = kda::launch_chunk_fwd(d, q, k, v, g, beta, init_state, cu_seqlens, o,
                                        final_state, state_ckpt, nullptr, workspace, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_fwd launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+KDA_EXPORT kda_status_t kda_chunk_fwd_noalloc(const kda_desc_t* desc, const void* q,
+                                              const void* k, const void* v, const float* g,
+                                              const float* beta, const float* init_state,
+                                              const int32_t* cu_seqlens, void* o,
+                                              float* final_state, float* state_ckpt,
+                                              hipStream_t stream) {
+  kda_status_t st = check_chunk_fwd_args(desc, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                         final_state, state_ckpt);
+  if (st != KDA_OK) return st;
+  const kda_desc_t& d = *desc;
+  if (kda::noalloc_seg_slots(d) == 0)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                "kda_chunk_fwd_noalloc holds %zu bytes of scratch per device; this descriptor "
+                "needs at least %lld (%d sequences x %d heads of carried states plus one "
+                "8-chunk segment of records): use kda_chunk_fwd with a workspace",
+                (size_t)KDA_NOALLOC_SCRATCH_BYTES, (long long)kda::noalloc_min_bytes(d),
+                d.num_seqs, d.heads);
+  hipError_t e = kda::launch_chunk_fwd_noalloc(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                               final_state, state_ckpt, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_chunk_fwd_noalloc launch: %s", hipGetErrorString(e));
   return ok();
 }
 

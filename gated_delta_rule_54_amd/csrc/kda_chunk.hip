@@ -55,6 +55,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 
 #include "kda_internal.h"
 #include "kda_chunk_common.h"
@@ -1127,27 +1128,38 @@ int64_t seg_slots(const kda_desc_t& d) {
   return std::max<int64_t>(8, std::min<int64_t>(kSegSlotsMax, s));
 }
 
-Plan make_plan(const kda_desc_t& d, bool varlen) {
+// Workspace plan for segments of at most ss chunk slots.
+Plan make_plan(const kda_desc_t& d, bool varlen, int64_t ss) {
   Plan p{};
   const int64_t T = d.seqlen;
   p.slot_bound = varlen ? (T + (int64_t)(kC - 1) * d.num_seqs) / kC
                         : (int64_t)d.batch * ((T + kC - 1) / kC);
-  p.seg_slots = std::min<int64_t>(p.slot_bound, seg_slots(d));
+  p.seg_slots = std::min<int64_t>(p.slot_bound, ss);
   p.rec_bytes = rec_bytes_for(d);
   p.rec_total = p.seg_slots * d.heads * p.rec_bytes;
-  p.carry_bytes = p.slot_bound > seg_slots(d)
-                      ? (int64_t)d.num_seqs * d.heads * d.dk * d.dv * 4 : 0;
+  p.carry_bytes = p.slot_bound > ss ? (int64_t)d.num_seqs * d.heads * d.dk * d.dv * 4 : 0;
   p.map_bytes = varlen ? 2 * align256(((int64_t)d.num_seqs + 1) * 4) : 0;
   return p;
+}
+Plan make_plan(const kda_desc_t& d, bool varlen) { return make_plan(d, varlen, seg_slots(d)); }
+
+// Workspace bytes for segments of at most ss slots: the larger of the dense
+// and varlen layouts (whether cu_seqlens will be passed is not known here;
+// they differ only in the slot bound and the map).
+int64_t workspace_for(const kda_desc_t& d, int64_t ss) {
+  const Plan pv = make_plan(d, true, ss), pd = make_plan(d, false, ss);
+  const int64_t a = pv.rec_total + pv.carry_bytes + pv.map_bytes;
+  const int64_t b = pd.rec_total + pd.carry_bytes + pd.map_bytes;
+  return a > b ? a : b;
 }
 
 template <typename T, int D>
 hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const void* v,
                      const float* g, const float* beta, const float* init_state,
                      const int32_t* cu, void* o, float* final_state, float* ckpt,
-                     void* states, char* ws, hipStream_t stream) {
+                     void* states, char* ws, int64_t SS, hipStream_t stream) {
   const bool varlen = cu != nullptr;
-  const Plan p = make_plan(d, varlen);
+  const Plan p = make_plan(d, varlen, SS);
   const int H = d.heads, NH = d.num_seqs * d.heads;
   char* recs = ws;
   float* carry = p.carry_bytes ? reinterpret_cast<float*>(ws + p.rec_total) : nullptr;
@@ -1183,7 +1195,6 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                        d.seqlen, cu_s, chunk_off);
     gm = ChunkGeom{cu_s, chunk_off, d.seqlen, 0, d.num_seqs};
   }
-  const int64_t SS = seg_slots(d);
   const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + SS - 1) / SS;
   for (int64_t s = 0; s < nseg; ++s) {
     const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
@@ -1208,35 +1219,91 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
 
 }  // namespace
 
-size_t chunk_workspace_bytes(const kda_desc_t& d) {
-  // Whether cu_seqlens will be passed is not known here: size for the larger
-  // of the two layouts (they differ only in the slot bound and the map).
-  const Plan pv = make_plan(d, true), pd = make_plan(d, false);
-  const int64_t a = pv.rec_total + pv.carry_bytes + pv.map_bytes;
-  const int64_t b = pd.rec_total + pd.carry_bytes + pd.map_bytes;
-  return (size_t)(a > b ? a : b);
-}
+size_t chunk_workspace_bytes(const kda_desc_t& d) { return (size_t)workspace_for(d, seg_slots(d)); }
 
 int64_t chunk_slot_bound(const kda_desc_t& d, bool varlen) {
   return make_plan(d, varlen).slot_bound;
 }
+
+namespace {
+hipError_t launch_with(const kda_desc_t& d, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* init_state,
+                       const int32_t* cu_seqlens, void* o, float* final_state, float* state_ckpt,
+                       void* chunk_states, char* ws, int64_t ss, hipStream_t stream) {
+  const bool bf = d.dtype == KDA_DTYPE_BF16;
+  if (d.dk == 128)
+    return bf ? run_typed<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                     final_state, state_ckpt, chunk_states, ws, ss, stream)
+              : run_typed<float, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                      final_state, state_ckpt, chunk_states, ws, ss, stream);
+  return bf ? run_typed<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state,
+                                  state_ckpt, chunk_states, ws, ss, stream)
+            : run_typed<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
+                                   final_state, state_ckpt, chunk_states, ws, ss, stream);
+}
+}  // namespace
 
 hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                             const float* g, const float* beta, const float* init_state,
                             const int32_t* cu_seqlens, void* o, float* final_state,
                             float* state_ckpt, void* chunk_states, void* workspace,
                             hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
-  const bool bf = d.dtype == KDA_DTYPE_BF16;
-  if (d.dk == 128)
-    return bf ? run_typed<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                     final_state, state_ckpt, chunk_states, ws, stream)
-              : run_typed<float, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                      final_state, state_ckpt, chunk_states, ws, stream);
-  return bf ? run_typed<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state,
-                                  state_ckpt, chunk_states, ws, stream)
-            : run_typed<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                   final_state, state_ckpt, chunk_states, ws, stream);
+  return launch_with(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state, state_ckpt,
+                     chunk_states, static_cast<char*>(workspace), seg_slots(d), stream);
+}
+
+// ---------------------------------------------------------------------------
+// The prefill without a caller workspace: the scratch is a fixed device array
+// of the library (one copy per device, held until the process ends), and the
+// chunk records use segments small enough to fit it.  Host code never uses
+// the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+namespace {
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_for_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+}  // namespace
+
+int64_t noalloc_seg_slots(const kda_desc_t& d) {
+  // the segment length the normal path uses, or the largest multiple of 8
+  // below it whose workspace fits the array (records shrink with the segment;
+  // the carried states and the varlen map do not)
+  for (int64_t ss = seg_slots(d); ss >= 8; ss -= 8)
+    if (workspace_for(d, ss) <= (int64_t)kNoAllocScratchBytes) return ss;
+  return workspace_for(d, 8) <= (int64_t)kNoAllocScratchBytes ? 8 : 0;
+}
+
+int64_t noalloc_min_bytes(const kda_desc_t& d) { return workspace_for(d, 8); }
+
+hipError_t launch_chunk_fwd_noalloc(const kda_desc_t& d, const void* q, const void* k,
+                                    const void* v, const float* g, const float* beta,
+                                    const float* init_state, const int32_t* cu_seqlens, void* o,
+                                    float* final_state, float* state_ckpt, hipStream_t stream) {
+  const int64_t ss = noalloc_seg_slots(d);
+  if (ss == 0) return hipErrorInvalidValue;  // the caller checks the size first
+  char* ws = nullptr;
+  hipError_t e = scratch_for_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_with(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state, state_ckpt,
+                     nullptr, ws, ss, stream);
 }
 
 }  // namespace kda

@@ -46,6 +46,18 @@ hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, c
 // does not read cu_seqlens, T/64 + N).
 int64_t chunk_slot_bound(const kda_desc_t& d, bool varlen);
 
+// Prefill without a caller workspace (kda_chunk_fwd_noalloc): scratch in a
+// fixed device array of kNoAllocScratchBytes per device.  noalloc_seg_slots
+// is the segment length (chunk slots) that fits the array, 0 if even the
+// smallest segment does not (then noalloc_min_bytes says what it would need).
+constexpr size_t kNoAllocScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+int64_t noalloc_seg_slots(const kda_desc_t& d);
+int64_t noalloc_min_bytes(const kda_desc_t& d);
+hipError_t launch_chunk_fwd_noalloc(const kda_desc_t& d, const void* q, const void* k,
+                                    const void* v, const float* g, const float* beta,
+                                    const float* init_state, const int32_t* cu_seqlens, void* o,
+                                    float* final_state, float* state_ckpt, hipStream_t stream);
+
 // Chunkwise backward (kda_chunk_bwd.hip).
 size_t chunk_bwd_workspace_bytes(const kda_desc_t& d);
 hipError_t launch_chunk_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,

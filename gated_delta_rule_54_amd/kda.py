@@ -30,7 +30,8 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
 # Names every build of the library must export (the declarations of kda.h).
-EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_bwd_workspace_bytes",
+EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
+            "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_decode_step",
             "kda_output_gate_norm", "kda_short_conv_swish", "kda_status_string",
             "kda_last_error", "kda_abi_version")
@@ -79,6 +80,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [dp]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 16 + [sz, vp]
@@ -171,7 +174,7 @@ def chunk_fwd_workspace_bytes(desc: KdaDesc) -> int:
 @_stream_scoped
 def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2norm=True,
                   scale=1.0, ckpt_every=0, out=None, final_state=None, want_final=True,
-                  state_ckpt=None, workspace=None, stream=None):
+                  state_ckpt=None, workspace=None, stream=None, noalloc=False):
     """Chunkwise KDA prefill through the C ABI.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (float32 or bfloat16); g: [B, T, H, dk]
@@ -179,7 +182,9 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
     Gated DeltaNet); beta: [B, T, H] fp32; init_state: [N, H, dk, dv] fp32 or None;
     cu_seqlens: int32 [N + 1] device tensor (B must be 1) or None.
     Returns (o, final_state, state_ckpt); final_state may be passed in (it may
-    be the init_state tensor itself).
+    be the init_state tensor itself).  noalloc=True calls kda_chunk_fwd_noalloc
+    (no workspace; the library's fixed per-device scratch); pass out,
+    final_state and state_ckpt to keep the whole call free of allocations.
     """
     lib = load_library()
     B, T, H, dk = q.shape
@@ -209,6 +214,13 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
     desc = make_desc(batch=B, num_seqs=N, seqlen=T, heads=H, dk=dk, dv=dv, dtype=dt,
                      qk_l2norm=qk_l2norm, scale=scale, ckpt_every=ckpt_every,
                      gate_per_head=per_head)
+    if noalloc:
+        st = lib.kda_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(init_state), _ptr(cu_seqlens), _ptr(out),
+                                       _ptr(final_state), _ptr(state_ckpt),
+                                       _stream_handle(stream, dev))
+        _check(lib, st, "kda_chunk_fwd_noalloc")
+        return out, final_state, state_ckpt
     ws_bytes = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
     if ws_bytes == 0 and lib.kda_last_error():
         _check(lib, KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_workspace_bytes")

@@ -24,7 +24,8 @@
  *    kda_decode_step needs the state 16-byte aligned and every other pointer
  *    aligned to its element size.  The caller owns every buffer; the
  *    library keeps no pointer after a call returns and never allocates device
- *    memory (scratch comes in through `workspace`).
+ *    memory (scratch comes in through `workspace`, or, for
+ *    kda_chunk_fwd_noalloc, is a fixed device array the library holds).
  *  - Calls are asynchronous on `stream`; outputs are valid once the stream
  *    has reached the point of the call.  Host-side validation never
  *    synchronises the device; on any error nothing is launched, the status is
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -132,6 +133,28 @@ kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
                            const float* init_state, const int32_t* cu_seqlens, void* o,
                            float* final_state, float* state_ckpt, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Scratch (bytes, per device) that kda_chunk_fwd_noalloc holds. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace and allocates nothing: its scratch (chunk records,
+ * carried states, varlen map) is a fixed array of KDA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library holds on every device it runs on until the
+ * process ends, and the chunk records are processed in segments small enough
+ * to fit it.  Arguments, layouts, alignment and results are those of
+ * kda_chunk_fwd, and the outputs are bitwise identical to it.  A descriptor
+ * whose scratch need exceeds the array (the carried states of many
+ * sequences x heads, or records of one 8-chunk segment that do not fit)
+ * returns KDA_ERR_WORKSPACE_TOO_SMALL and launches nothing.  Every call on a
+ * device shares that device's array and leaves its contents behind (nothing
+ * in it needs to start at zero): calls that overlap on one device -- other
+ * streams, other threads -- race and must be serialised by the caller. */
+kda_status_t kda_chunk_fwd_noalloc(const kda_desc_t* desc, const void* q, const void* k,
+                                   const void* v, const float* g, const float* beta,
+                                   const float* init_state, const int32_t* cu_seqlens, void* o,
+                                   float* final_state, float* state_ckpt, hipStream_t stream);
 
 /* Bytes of device workspace kda_chunk_bwd needs for this descriptor (an upper
  * bound that does not read cu_seqlens); 0 for an invalid or unsupported

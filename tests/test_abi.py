@@ -30,7 +30,7 @@ def test_exports_match_header():
 
 def test_abi_version_and_strings():
     lib = K.load_library()
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
     assert lib.kda_status_string(99) == b"KDA_STATUS_UNKNOWN"
@@ -237,3 +237,22 @@ def test_bwd_pointer_errors(case):
     lib = K.load_library()
     st = _call_bwd(_desc(dk=64, dv=64, dtype=1), **case)
     assert st == B.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error()
+
+
+def test_noalloc_rejects_descriptors_beyond_its_scratch():
+    """kda_chunk_fwd_noalloc checks its fixed scratch on the host: carried
+    states of 2048 sequences x 32 heads (d = 128) need 4 GiB, far beyond the
+    64 MiB array, so it returns KDA_ERR_WORKSPACE_TOO_SMALL before any launch;
+    invalid arguments are rejected as kda_chunk_fwd rejects them."""
+    lib = K.load_library()
+    d = K.make_desc(batch=1, num_seqs=2048, seqlen=2048 * 1024, heads=32, dk=128, dv=128,
+                    dtype=1)
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   FAKE, FAKE + 0x100, None, None, None)
+    assert st == B.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert b"kda_chunk_fwd_noalloc holds" in lib.kda_last_error()
+    d2 = _desc()
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d2), FAKE + 4, FAKE, FAKE, FAKE, FAKE, None,
+                                   None, FAKE + 0x100, None, None, None)
+    assert st == B.KDA_ERR_INVALID_ARGUMENT
+    assert b"q is not 16-byte aligned" in lib.kda_last_error()
