@@ -34,7 +34,9 @@
 //   K2 (kda_state_pass): one workgroup per (sequence, head, d_v slice),
 //     sequential over that sequence's chunks.  The fp32 state slice lives in
 //     MFMA accumulators for the whole sequence; per chunk it forms W, the
-//     output and the next state with three MFMA chains.
+//     output and the next state with three MFMA chains.  On the bf16 path two
+//     producer waves bring the chain's record fragments into LDS by
+//     LDS-direct loads beside the four compute waves.
 //   The d_v columns of the state never mix, so splitting d_v across
 //   workgroups lets one head's chain use several CUs; the slices of one head
 //   are placed on one XCD so their shared operand reads hit the same L2.
@@ -743,13 +745,49 @@ template <> struct BufStore4<float> {
 };
 
 // Per-wave fragments of one chunk's record (see kda_state_pass).
+//
+// On the bf16 path the chain's own operands (-Wk and K~ fragments) come by
+// LDS-direct loads: a buffer load with the LDS bit writes each lane's 16
+// bytes straight into LDS (at the wave's M0 base + 16 x lane), bypassing the
+// VGPRs.  Measured on MI355X, a CU takes in ~100 B/ns of L2 or last-level
+// cache data this way against ~60 B/ns through VGPR loads, and the state
+// pass is bound by that intake.  Each fragment is one contiguous 1 KiB block
+// of the record (operand order), so one LDS-direct load moves one fragment
+// into one 1 KiB LDS block, and the wave that uses it reads its 16 bytes
+// back with one ds_read_b128 (no bank conflicts).  The loads are issued by
+// producer waves that do nothing else (see kda_state_pass); the compute
+// waves' fragments of U, e^gamma, Q o e^G and P stay on the VGPR path, so
+// the two paths feed the CU together.  fp32 operands (4 bytes per lane and
+// k-step, twice the bytes) keep every fragment on the VGPR path.
+template <typename T> constexpr bool k2_dma() { return sizeof(T) == 2; }
+constexpr int kK2Producers = 2;  // producer waves of a bf16 state-pass workgroup
+template <typename T> constexpr int k2_threads() {
+  return k2_dma<T>() ? kThreads + 64 * kK2Producers : kThreads;
+}
+
+__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+// s_waitcnt operand that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt is 6 bits: low 4 at [3:0], high 2 at
+// [15:14]) and leaves expcnt and lgkmcnt alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <typename T, int D, int WS, bool OUT>
 struct K2Frags {
   using M = Mma<T>;
   using R = Rec<T, D>;
   static constexpr int NB = WS / 16, CBW = D / 64, KD = D / M::KSTEP, KC = kC / M::KSTEP;
   static constexpr uint32_t ES = sizeof(T), FB = M::KPL * ES;  // bytes of a lane's fragment
-  typename M::frag wn[KD], qg[KD], p[KC], kt[CBW][KC];
+  static constexpr bool DMA = k2_dma<T>();
+  // LDS-direct fragments per wave and chunk: -Wk (KD), then K~ (CBW x KC)
+  static constexpr int NDMA = KD + CBW * KC;
+  static constexpr int WAVE_LDS = DMA ? NDMA * 64 * (int)FB : 0;  // bytes per wave and buffer
+  static_assert(!DMA || (4 * NDMA) % kK2Producers == 0, "fragments split evenly over producers");
+  static constexpr int VW = DMA ? 1 : KD, VC = DMA ? 1 : CBW, VK = DMA ? 1 : KC;
+  typename M::frag wn[VW], qg[KD], p[KC], kt[VC][VK];
   BufRaw4<T> ut[NB];
   BufRaw4<float> eg[CBW];
 
@@ -766,9 +804,24 @@ struct K2Frags {
     o.pz = (uint32_t)wave;
     return o;
   }
+  // -Wk fragment ks and K~ fragment (i, ks) of this wave, from its block of
+  // an LDS record buffer (DMA path) or from registers
+  __device__ __forceinline__ typename M::frag wn_at(const char* wl, int ks, int lane) const {
+    if constexpr (DMA)
+      return M::load(reinterpret_cast<const T*>(wl + ks * 64 * FB) + lane * M::KPL);
+    else
+      return wn[ks];
+  }
+  __device__ __forceinline__ typename M::frag kt_at(const char* wl, int i, int ks, int lane) const {
+    if constexpr (DMA)
+      return M::load(reinterpret_cast<const T*>(wl + (KD + i * KC + ks) * 64 * FB) + lane * M::KPL);
+    else
+      return kt[i][ks];
+  }
   // The loads come in four groups so that a step can spread them between
   // its phases: a CU's vector memory path takes ~1 KiB per 16 cycles, and
-  // a wave that issues a whole record at once stalls behind it.
+  // a wave that issues a whole record at once stalls behind it.  On the DMA
+  // path -Wk and K~ are not loaded here (the producer waves bring them).
   template <int PART>
   __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t r, uint32_t soff, const Offs& o) {
     // in the order a step consumes them: U and -Wk (W), Q o e^G (O), e^gamma
@@ -776,19 +829,23 @@ struct K2Frags {
     if constexpr (PART == 0) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) ut[nb].load(r, o.ut + nb * (kC / 16) * 64 * 4 * ES, soff);
+      if constexpr (!DMA) {
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) wn[ks] = BufFrag<T>::load(r, o.wn + ks * 64 * FB, soff);
+        for (int ks = 0; ks < KD; ++ks) wn[ks] = BufFrag<T>::load(r, o.wn + ks * 64 * FB, soff);
+      }
     } else if constexpr (PART == 1) {
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) qg[ks] = BufFrag<T>::load(r, o.qg + ks * 64 * FB, soff);
     } else if constexpr (PART == 2) {
 #pragma unroll
       for (int i = 0; i < CBW; ++i) eg[i].load(r, o.eg + i * 64, soff);
+      if constexpr (!DMA) {
 #pragma unroll
-      for (int i = 0; i < CBW; ++i)
+        for (int i = 0; i < CBW; ++i)
 #pragma unroll
-        for (int ks = 0; ks < KC; ++ks)
-          kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * KC + ks) * 64 * FB, soff);
+          for (int ks = 0; ks < KC; ++ks)
+            kt[i][ks] = BufFrag<T>::load(r, o.kt + (i * KC + ks) * 64 * FB, soff);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) {
@@ -806,12 +863,45 @@ struct K2Frags {
     load_part<2>(r, soff, o);
     if constexpr (OUT) load_part<3>(r, soff, o);
   }
+  // Producer side: LDS-direct loads of one chunk's -Wk and K~ fragments for
+  // all four compute waves into record buffer `buf` ([wave][fragment][lane]
+  // [16 bytes]); producer wave pw of kK2Producers takes every
+  // kK2Producers-th fragment.  Returns nothing; each call issues PER_PRODUCER
+  // loads.
+  static constexpr int PER_PRODUCER = 4 * NDMA / kK2Producers;
+  static __device__ __forceinline__ void produce(__amdgpu_buffer_rsrc_t r, uint32_t soff,
+                                                 char* buf, int pw, int lane) {
+#pragma unroll
+    for (int t = 0; t < PER_PRODUCER; ++t) {
+      const int f = pw + t * kK2Producers;    // fragment of the workgroup's record share
+      const int cw = f / NDMA, fi = f % NDMA;  // compute wave, its fragment index
+      const uint32_t voff =
+          fi < KD ? (uint32_t)(R::WN * ES) + ((cw * KD + fi) * 64 + lane) * FB
+                  : (uint32_t)(R::KT * ES) + ((cw * CBW * KC + (fi - KD)) * 64 + lane) * FB;
+      dma_load16(r, buf + (cw * NDMA + fi) * 64 * FB, voff, soff);
+    }
+  }
 };
+
+// Workgroup barrier for the state pass.  __syncthreads() carries a workgroup
+// release fence, which in a producer wave must also wait for every
+// LDS-direct load in flight (they write LDS) and would drain its prefetch;
+// here each wave waits only for its own LDS reads and writes (lgkmcnt), the
+// hardware barrier follows, and the empty asm statements keep the compiler
+// from moving LDS accesses across it.  A producer wave waits for the loads
+// the compute waves are about to read with an explicit vmcnt before the
+// barrier (see kda_state_pass).
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left as they are
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 // OUT = false (the forward run inside the backward): no output, so neither
 // Q o e^G nor P is loaded and O is not formed.
 template <typename T, int D, int WS, bool OUT>
-__global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
+__global__ __launch_bounds__(k2_threads<T>(), 1) void kda_state_pass(
     const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
     int nseg, int64_t seg_slots, int nslice, int NH, const float* __restrict__ init, float* __restrict__ carry,
     float* __restrict__ fin, float* __restrict__ ckpt, int64_t ckpt_every, int64_t nckpt,
@@ -826,6 +916,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   T* sWt = sSt + WS * LDS_S;                             // W^T slice [n][i]
   constexpr int LDF = WS + 16 / (int)sizeof(T);
   __shared__ __align__(16) T sSf[D * LDF];               // S slice [c][n] (states)
+  // LDS record buffers for the LDS-direct fragments of chunks j, j + 1 and
+  // j + 2 (bf16 path), each [compute wave][fragment][lane][16 bytes]
+  constexpr int RBB = F::DMA ? (kThreads / 64) * F::WAVE_LDS : 16;
+  __shared__ __align__(16) char rb0[RBB];
+  __shared__ __align__(16) char rb1[RBB];
+  __shared__ __align__(16) char rb2[RBB];
 
   // XCD-aware placement: workgroups of one (sequence, head) share id mod 8.
   const int id = blockIdx.x;
@@ -834,7 +930,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   if (nh >= NH) return;
   const int seq = nh / H, h = nh % H;
   const int n0 = slice * WS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // This sequence's chunks inside the segment's slot range [s0, s1).  The
   // state enters from init_state at the sequence's first chunk, otherwise from
@@ -845,7 +941,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   if (sp.c0 == sp.c1) {  // empty sequence: final = init, once
     if (seg != (int)min<int64_t>(sp.c0 / seg_slots, nseg - 1) || fin == nullptr) return;
     const int64_t base = (int64_t)nh * D * D;
-    for (int e = threadIdx.x; e < D * WS; e += kThreads) {
+    for (int e = threadIdx.x; e < D * WS; e += blockDim.x) {
       const int64_t idx = base + (int64_t)(e / WS) * D + n0 + e % WS;
       fin[idx] = init ? init[idx] : 0.f;
     }
@@ -855,6 +951,42 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   if (slot0 >= slot1) return;
   const float* src = slot0 == sp.c0 ? init : carry;
   float* dst = slot1 == sp.c1 ? fin : carry;
+
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ws + (int64_t)h * nrec * R::BYTES), (short)0, (int)(nrec * R::BYTES), kRsrcWord3);
+  auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
+  // The loop runs over 32-bit record indices j in [j0, j1) relative to the
+  // segment (64-bit scalar compares would need vector temporaries, whose
+  // reuse makes the compiler drain the prefetched loads).
+  const int j0 = (int)(slot0 - s0), j1 = (int)(slot1 - s0);
+
+  // Producer waves (bf16 path): LDS-direct loads of each chunk's -Wk and K~
+  // fragments into three record buffers, two chunks ahead.  A producer
+  // issues nothing but these loads, so its vmcnt counts exactly them: before
+  // a step's first barrier it waits until only the next chunk's loads are in
+  // flight (this chunk's have landed in LDS), and after that barrier -- by
+  // which every compute wave has finished reading the chunk before this
+  // one -- it refills that chunk's buffer with chunk j + 2.  It takes part in
+  // both barriers of every step, as the compute waves do, and ends with no
+  // load in flight.  The compute waves issue no LDS-direct load, so the
+  // compiler's wait tracking never makes them wait for one.
+  if constexpr (F::DMA) {
+    if (wave >= 4) {
+      const int pw = wave - 4;
+      F::produce(rsrc, soff(j0), rb0, pw, lane);
+      F::produce(rsrc, soff(min(j0 + 1, j1 - 1)), rb1, pw, lane);
+      int b2 = 2;  // buffer of chunk j + 2
+      for (int j = j0; j < j1; ++j) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(F::PER_PRODUCER));
+        lds_barrier();
+        F::produce(rsrc, soff(min(j + 2, j1 - 1)), b2 == 0 ? rb0 : b2 == 1 ? rb1 : rb2, pw, lane);
+        b2 = b2 == 2 ? 0 : b2 + 1;
+        lds_barrier();
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
+  }
 
   // state accumulators: wave owns rows (cb = wave*CBW + i) x all NB column blocks
   f32x4_t S[CBW][NB];
@@ -870,14 +1002,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
         S[i][nb][j] = src ? src[sbase + (int64_t)c * D + n] : 0.f;
       }
 
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(ws + (int64_t)h * nrec * R::BYTES), (short)0, (int)(nrec * R::BYTES), kRsrcWord3);
   const typename F::Offs offs = F::offsets(wave, lane, n0);
-
-  // The loop runs over 32-bit record indices j in [j0, j1) relative to the
-  // segment (64-bit scalar compares would need vector temporaries, whose
-  // reuse makes the compiler drain the prefetched loads).
-  const int j0 = (int)(slot0 - s0), j1 = (int)(slot1 - s0);
   const int cdelta = (int)(s0 - sp.c0);             // chunk index = j + cdelta
   const int ci_last = (int)((sp.ntok - 1) / kC);    // the sequence's last chunk
   const int len_last = (int)(sp.ntok - (int64_t)ci_last * kC);
@@ -913,7 +1038,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
                           scale * O[nb][2], scale * O[nb][3]);
   };
 
-  auto soff = [](int j) { return (uint32_t)j * (uint32_t)R::BYTES; };
   // For the backward: the state entering chunk slot s0 + j, [slot][H] of
   // slice-blocked D x D in the MFMA type (sblk: this workgroup's slice is one
   // contiguous D x 16 block; the backward uses S only as a product operand,
@@ -938,8 +1062,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   };
   // One chunk step: consumes the fragments in f and fills fn with those of
   // record jn (clamped to the last record), the loads spread over the step.
-  auto step = [&](const F& f, F& fn, int j, int jn) {
+  auto step = [&](const F& f, F& fn, const char* lcur, int j, int jn) {
     const uint32_t son = soff(min(jn, j1 - 1));
+    const char* wl = lcur + wave * F::WAVE_LDS;   // this wave's -Wk, K~ of chunk j (DMA path)
     const int ci = j + cdelta;  // chunk index within the sequence
     const int len = ci == ci_last ? len_last : kC;
 
@@ -956,7 +1081,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
           for (int e = 0; e < 4; ++e) st_elem(sSf + (c4 + e) * LDF + n, S[i][nb][e]);
         }
       }
-    __syncthreads();
+    lds_barrier();
+    // -Wk fragments: in the chunk's LDS record buffer once the producers have
+    // passed the barrier above
+    typename M::frag wnf[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) wnf[ks] = f.wn_at(wl, ks, lane);
 
     // (b) W = U + (-Wk) S for this wave's 16 rows -- the chain's critical
     // path -- is issued first; then the previous chunk's output store and
@@ -972,7 +1102,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) W[nb] = M::mma(f.wn[ks], sfr[nb][ks], W[nb]);
+      for (int nb = 0; nb < NB; ++nb) W[nb] = M::mma(wnf[ks], sfr[nb][ks], W[nb]);
     __builtin_amdgcn_sched_barrier(0);
     fn.template load_part<0>(rsrc, son, offs);
     // sSf is written again only after this step's second barrier
@@ -996,7 +1126,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
       const int n = nb * 16 + (lane & 15);
       st_perm4(sWt + n * LDS_W, wave * 16 + 4 * (lane >> 4), W[nb][0], W[nb][1], W[nb][2], W[nb][3]);
     }
-    __syncthreads();
+    // K~ fragments (own LDS-direct loads)
+    typename M::frag ktf[CBW][KC];
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) ktf[i][ks] = f.kt_at(wl, i, ks, lane);
+    lds_barrier();
 
     // (d) S = Diag(e^gamma) S + K~^T W first (critical path), then O^T += W^T P^T
     typename M::frag wf[NB][KC];
@@ -1012,7 +1148,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
 #pragma unroll
         for (int j = 0; j < 4; ++j) S[i][nb][j] *= eg[j];
 #pragma unroll
-        for (int ks = 0; ks < KC; ++ks) S[i][nb] = M::mma(f.kt[i][ks], wf[nb][ks], S[i][nb]);
+        for (int ks = 0; ks < KC; ++ks) S[i][nb] = M::mma(ktf[i][ks], wf[nb][ks], S[i][nb]);
       }
     __builtin_amdgcn_sched_barrier(0);
     fn.template load_part<2>(rsrc, son, offs);
@@ -1059,18 +1195,20 @@ __global__ __launch_bounds__(kThreads, 1) void kda_state_pass(
   // unconditional (past the end it re-reads the last record) and the loop
   // has no early exit, so the in-order wait counter only ever waits for the
   // set being consumed.
+  // Register set fa and LDS buffer rb0 hold chunk j, fb / rb1 chunk j + 1,
+  // fc / rb2 chunk j + 2 (the LDS-direct fragments follow the same rotation).
   F fa, fb, fc;
   fa.load(rsrc, soff(j0), offs);
   __asm__ volatile("" ::: "memory");  // issue the first set's loads first
   fb.load(rsrc, soff(min(j0 + 1, j1 - 1)), offs);
   int j = j0;
   for (; j + 3 <= j1; j += 3) {
-    step(fa, fc, j, j + 2);
-    step(fb, fa, j + 1, j + 3);
-    step(fc, fb, j + 2, j + 4);
+    step(fa, fc, rb0, j, j + 2);
+    step(fb, fa, rb1, j + 1, j + 3);
+    step(fc, fb, rb2, j + 2, j + 4);
   }
-  if (j < j1) step(fa, fc, j, j + 2);
-  if (j + 1 < j1) step(fb, fa, j + 1, j + 3);
+  if (j < j1) step(fa, fc, rb0, j, j + 2);
+  if (j + 1 < j1) step(fb, fa, rb1, j + 1, j + 3);
   if constexpr (OUT) store_o();
 
   if (dst != nullptr) {
@@ -1208,7 +1346,7 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                          s1 - s0, d.qk_l2norm, recs);
     }
     auto k2 = o ? kda_state_pass<T, D, WS, true> : kda_state_pass<T, D, WS, false>;
-    hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(k2_threads<T>()), 0,
                        stream, recs, gm, H, s0, s1, (int)s, (int)nseg, SS, nslice, NH, init_state,
                        carry, final_state, ckpt, d.ckpt_every, nck, (T*)states, d.scale, (T*)o);
     hipError_t e = hipGetLastError();
