@@ -41,14 +41,18 @@
 //   workgroups lets one head's chain use several CUs; the slices of one head
 //   are placed on one XCD so their shared operand reads hit the same L2.
 //
-// Exponent handling.  g <= 0 makes G non-increasing inside a chunk.  The fast
-// path factors e^(G_r - G_i) = e^G_r * e^-G_i with the chunk start as the
-// reference: e^G <= 1 and e^-G <= e^80 when every channel's chunk decay
-// gamma >= -80, so nothing overflows fp32/bf16 (both have an 8-bit exponent)
-// and each product keeps the operands' relative precision.  [XT §4] names
-// the precision loss of this division as a design concern; a chunk whose
-// decay exceeds the bound takes an exact path that forms each
-// e^(G_r - G_i) <= 1 from its own difference (slow, but never overflows).
+// Exponent handling.  g <= 0 makes G non-increasing inside a chunk.  A and P
+// factor e^(G_r - G_i) = e^(G_r - m) * e^(m - G_i) around a per-channel
+// reference m.  The fast path takes m = 0 (the chunk start): e^G <= 1 and
+// e^-G <= e^80 when every channel's chunk decay gamma >= -80, so nothing
+// overflows fp32/bf16 (both have an 8-bit exponent) and each product keeps
+// the operands' relative precision.  [XT §4] names the precision loss of this
+// division as a design concern.  A chunk beyond that bound takes m = G at row
+// 31 (k1_mid_ap): every factor that matters then stays within [e^-80, e^80]
+// as long as each half of the chunk decays by at most 80 (gamma down to
+// about -160), and A and P are the same MFMA products of other operand
+// values.  Beyond even that, an exact path forms each e^(G_r - G_i) <= 1 from
+// its own difference (k1_exact_ap; slow, but never overflows).
 //
 // Precision.  MFMA operands are the input dtype (bf16 or fp32); MFMA
 // accumulation, the state, T, G and gamma are fp32.
@@ -220,7 +224,7 @@ constexpr int k1_waves_per_simd() {
 // offset).  Out of line: few chunks take it, and inlined it would set the
 // register budget of the common path.  Every thread of the workgroup calls it.
 template <typename T, int D, bool GS>
-__device__ __attribute__((noinline)) void k1_exact_ap(
+__device__ __forceinline__ void k1_exact_ap(
     const T* khat, const T* qhat, float* stage, float* sA, const float* s_beta, T* wP,
     const float* gb, int64_t rowstride, int H, int len, float offx, float offy) {
   using L = K1Lds<T, D>;
@@ -292,6 +296,118 @@ __device__ __attribute__((noinline)) void k1_exact_ap(
     const int r = e >> 6, i = e & 63;
     if (i > r && (i >> 4) == (r >> 4)) st_f(wP + fnat<T>(r, i, kC / M::KSTEP), 0.f);
   }
+}
+
+// Mid-reference path of A and P, for a chunk some channel of which decays
+// below the fast bound while each half of it stays within it.  Entered with
+// k^ in region 0 and q^ in region 1 (row-major, as the exact path stages
+// them); G is formed again from g (as the kernel forms it: the prefix sum
+// over the thread's rows, plus the part offset), and with m = G of row 31
+// per channel the regions become K o e^(G-m) (0), Q o e^(G-m) (1) and
+// K o e^(m-G) (2): A^T and P^T then come out of the same block-pair MFMA
+// products as on the fast path.  For i <= r the factors e^(G_r - m) and
+// e^(m - G_i) lie in [e^-80, e^80] unless the whole product is below e^-80
+// (r in the second half, i in the first: both factors <= 1), so nothing
+// overflows and nothing that matters underflows.  Writes A (times beta_r,
+// strict lower, fp32) over region 1 and P into the record, as the fast path
+// does.  Out of line, like the exact path, so that its registers do not set
+// the common path's budget.  Every thread of the workgroup calls it.
+template <typename T, int D, bool GS, bool RO>
+__device__ __forceinline__ void k1_mid_ap(T* kop, T* qop, T* kim, const float* s_beta, T* wP,
+                                          const float* gb, int64_t rowstride, int H, int len,
+                                          float offx, float offy, float mx, float my) {
+  using L = K1Lds<T, D>;
+  using M = Mma<T>;
+  constexpr int NCP = L::NCP, RPP = L::RPP, NT = k1_threads<T, D>(), NW = NT / 64;
+  const int tid = threadIdx.x, cp = tid % NCP, part = tid / NCP, lane = tid & 63,
+            wave = tid >> 6;
+  const int c0 = 2 * cp, r0p = part * RPP;
+  float2 run = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const int r = r0p + j, rr = min(r, len - 1);
+    const float2 gj = GS ? make_float2(gb[rr * H], gb[rr * H]) : ld2(gb + rr * rowstride + c0);
+    const float2 gm = r < len ? gj : make_float2(0.f, 0.f);
+    run = make_float2(run.x + gm.x, run.y + gm.y);
+    const float gsx = (run.x + offx - mx) * kLog2eF, gsy = (run.y + offy - my) * kLog2eF;
+    const float erx = __builtin_amdgcn_exp2f(gsx), ery = __builtin_amdgcn_exp2f(gsy);
+    const float enx = __builtin_amdgcn_exp2f(-gsx), eny = __builtin_amdgcn_exp2f(-gsy);
+    const float2 kh = ld2(kop + r * L::LDR + c0), qh = ld2(qop + r * L::LDR + c0);
+    st2(kop + r * L::LDR + c0, kh.x * erx, kh.y * ery);
+    st2(qop + r * L::LDR + c0, qh.x * erx, qh.y * ery);
+    st2(kim + r * L::LDR + c0, kh.x * enx, kh.y * eny);
+  }
+  __syncthreads();
+  // the fast path's block pairs (I <= R), dealt to the waves round-robin
+  constexpr int NPAIR = 10, PMAX = (NPAIR + NW - 1) / NW;
+  auto pair_I = [](int p) { return p < 4 ? 0 : p < 7 ? 1 : p < 9 ? 2 : 3; };
+  auto pair_R = [](int p) { return p < 4 ? p : p < 7 ? p - 3 : p < 9 ? p - 5 : 3; };
+  f32x4_t accA[PMAX], accP[PMAX];
+#pragma unroll
+  for (int t = 0; t < PMAX; ++t) {
+    accA[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accP[t] = accA[t];
+    const int p = wave + t * NW;
+    if (p >= NPAIR) continue;
+    const int I = pair_I(p), Rb = pair_R(p);
+#pragma unroll
+    for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+      const auto a = frag_at<T>(kim, L::LDR, I * 16, ks, lane);
+      accA[t] = M::mma(a, frag_at<T>(kop, L::LDR, Rb * 16, ks, lane), accA[t]);
+      accP[t] = M::mma(a, frag_at<T>(qop, L::LDR, Rb * 16, ks, lane), accP[t]);
+    }
+  }
+  __syncthreads();  // every read of regions 0..2 done; region 1 becomes A
+  float* sA = reinterpret_cast<float*>(qop);
+#pragma unroll
+  for (int t = 0; t < PMAX; ++t) {
+    const int p = wave + t * NW;
+    if (p >= NPAIR) continue;
+    const int I = pair_I(p), Rb = pair_R(p);
+    const int r = Rb * 16 + (lane & 15);
+    const int i0 = I * 16 + 4 * (lane >> 4);
+    const float br = s_beta[r];
+    float a4[4], p4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a4[j] = (i0 + j < r) ? br * accA[t][j] : 0.f;
+      p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
+    }
+    *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+    if (RO) st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
+  }
+}
+
+// A and P of a chunk beyond the fast path's bound, from raw k^ (region 0) and
+// q^ (region 1), with region 2 still holding the kernel's per-part totals of
+// g: the mid-reference path when each half of the chunk decays by at most 80
+// in every channel, the exact path otherwise.  One call site out of line, so
+// that neither path's registers weigh on the common path.  Every thread of
+// the workgroup calls it.
+template <typename T, int D, bool GS, bool RO>
+__device__ __attribute__((noinline)) void k1_slow_ap(T* r0, T* r1, T* r2, const float* s_beta,
+                                                     T* wP, const float* gb, int64_t rowstride,
+                                                     int H, int len, float offx, float offy) {
+  using L = K1Lds<T, D>;
+  constexpr int NCP = L::NCP, NPART = L::NPART, RPP = L::RPP;
+  const int c0 = 2 * (threadIdx.x % NCP);
+  // m = G of row 31 and gamma = G of row 63, per channel, from the part totals
+  float mx = 0.f, my = 0.f, gx = 0.f, gy = 0.f;
+  const float* scan = reinterpret_cast<const float*>(r2);
+#pragma unroll
+  for (int p = 0; p < NPART; ++p) {
+    const float tx = scan[p * D + c0], ty = scan[p * D + c0 + 1];
+    if (p < (kC / 2) / RPP) { mx += tx; my += ty; }
+    gx += tx; gy += ty;
+  }
+  const bool mid = __syncthreads_or(mx < kFastDecayBound || my < kFastDecayBound ||
+                                    gx - mx < kFastDecayBound || gy - my < kFastDecayBound) == 0;
+  // (every read of the part totals is done: region 2 is free)
+  if (mid)
+    k1_mid_ap<T, D, GS, RO>(r0, r1, r2, s_beta, wP, gb, rowstride, H, len, offx, offy, mx, my);
+  else
+    k1_exact_ap<T, D, GS>(r0, r1, reinterpret_cast<float*>(r2), reinterpret_cast<float*>(r1),
+                          s_beta, wP, gb, rowstride, H, len, offx, offy);
 }
 
 // GS: one gate per (token, head), broadcast over the key channels (Gated
@@ -446,6 +562,9 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
   }
 #pragma unroll
   for (int j = 0; j < RPP; ++j) { G[j].x += off.x; G[j].y += off.y; }
+  // Beyond the fast path's bound (some channel's gamma < -80) A and P come
+  // from k1_slow_ap (mid-reference or exact), from the operands staged as
+  // below (raw k^, q^; records written per thread).
   const bool exact =
       __syncthreads_or(gamma.x < kFastDecayBound || gamma.y < kFastDecayBound) != 0;
 
@@ -576,8 +695,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
       }
     }
   } else {
-    k1_exact_ap<T, D, GS>(r0, r1, reinterpret_cast<float*>(r2), reinterpret_cast<float*>(r1),
-                          s_beta, wP, gb, rowstride, H, loc.len, off.x, off.y);
+    k1_slow_ap<T, D, GS, rec_out>(r0, r1, r2, s_beta, wP, gb, rowstride, H, loc.len, off.x, off.y);
     load_v();
   }
   if (!exact) {

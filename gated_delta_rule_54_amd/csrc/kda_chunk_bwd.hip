@@ -54,9 +54,12 @@
 // (the kpos permutation of kda_chunk_common.h); everything else is staged in
 // LDS in the MFMA type.
 //
-// Domain: the split exponentials e^G, e^-G need every chunk's per-channel
-// decay gamma >= -80 (the forward's fast-path bound); beyond it the backward's
-// results are unspecified (no fault, no hang).  fp32 operands at d = 128 do
+// Exponents: the chunk-local products take e^(G_r - G_i) split as
+// e^(G_r - m) e^(m - G_i) around a per-channel reference m, as the forward
+// does: the chunk start while every channel's chunk decay gamma >= -80, else
+// G of row 31 while each half of the chunk decays by at most 80 (gamma down to
+// about -160; see BwdMode).  A chunk beyond that gets NaN gradients, and its
+// NaN state gradient reaches every chunk before it (all but dq).  fp32 operands at d = 128 do
 // not fit one workgroup's LDS and are not supported.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -282,6 +285,26 @@ struct BwdRegs {
   float gam;       // gamma of this lane's column
 };
 
+// Exponent reference of the chunk-local products (A, P, dP Km, dB Km,
+// dB^T Kp + dP^T Qp), chosen per chunk as in the forward: the chunk start
+// while every channel's gamma >= -80 (Kp = K^ o e^G, Km = K^ o e^-G), else
+// m = G of row 31 per channel while each half of the chunk decays by at most
+// 80 (the products then take K^ o e^(G-m), K^ o e^(m-G), Q^ o e^(G-m), whose
+// factors stay within [e^-80, e^80] wherever they matter, and the per-element
+// gate factors become e^(G-m) and e^(m-G)).  Beyond that the gradients of the
+// chunk are NaN.
+enum BwdMode { kBwdFast = 0, kBwdMid = 1, kBwdBeyond = 2 };
+// G of row 31 of this lane's column (the lanes of lane group 3 hold it)
+__device__ __forceinline__ float g_row31(const BwdRegs& R, int lane) {
+  return __shfl(R.G[1][3], 48 + (lane & 15));
+}
+__device__ __forceinline__ int bwd_mode(const BwdRegs& R, int lane) {
+  if (__syncthreads_or(R.gam < kFastDecayBound) == 0) return kBwdFast;
+  const float m = g_row31(R, lane);
+  return __syncthreads_or(m < kFastDecayBound || R.gam - m < kFastDecayBound) ? kBwdBeyond
+                                                                               : kBwdMid;
+}
+
 // Raw k, q, g of this lane's column and rows (zero past the chunk's end).
 // NTL: read non-temporally (the caller reads them once).
 template <typename T, int D, bool GS, bool NTL = false>
@@ -444,12 +467,12 @@ __device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdR
 // and P, T = (I + A)^-1 (times Diag(beta) when TBETA) in the MFMA type.  Bm receives this wave's tiles of Kp Km^T
 // (tile p = wave + NW * tt: rows 16(p/4), columns 16(p%4)).
 template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false>
-__device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
-                                             const float* __restrict__ g,
-                                             const float* __restrict__ beta, const ChunkLoc& loc,
-                                             int H, int h, int qk_l2norm,
-                                             BwdSmem<T, D, COMPACT>& sm, BwdRegs& R,
-                                             f32x4_t* Bm) {
+__device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
+                                            const float* __restrict__ g,
+                                            const float* __restrict__ beta, const ChunkLoc& loc,
+                                            int H, int h, int qk_l2norm,
+                                            BwdSmem<T, D, COMPACT>& sm, BwdRegs& R,
+                                            f32x4_t* Bm) {
   using L = BwdLds<T, D, COMPACT>;
   using M = Mma<T>;
   constexpr int NW = L::NW, NT = L::NT, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
@@ -476,8 +499,9 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
       }
   }
   prefix_G(gr, lane, R);
-  __syncthreads();
-  // gated operands
+  const int mode = bwd_mode(R, lane);  // (its barriers also end the staged reads)
+  const float mr = mode == kBwdFast ? 0.f : g_row31(R, lane);
+  // gated operands: Kp, Km, Qp relative to the mode's reference
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -486,7 +510,7 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
       R.kh[t][j] *= sm.rk[r];
       R.qh[t][j] *= sm.rq[r];
       const float G = R.G[t][j];
-      const float eg = __expf(G), en = __expf(-G), et = __expf(R.gam - G);
+      const float eg = __expf(G - mr), en = __expf(mr - G), et = __expf(R.gam - G);
       st_f(sm.kp + r * LDX + c, R.kh[t][j] * eg);
       st_f(sm.km + r * LDX + c, R.kh[t][j] * en);
       st_f(sm.qp + r * LDX + c, R.qh[t][j] * eg);
@@ -530,6 +554,7 @@ __device__ __forceinline__ void bwd_prologue(const T* __restrict__ q, const T* _
     st_f(sm.tb + r * LDC + i, TBETA ? t * sm.beta[i] : t);
   }
   __syncthreads();
+  return mode;
 }
 
 // ---------------------------------------------------------------------------
@@ -562,9 +587,13 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
   BwdSmem<T, D, true> sm(smem);
   BwdRegs R;
   f32x4_t Bm[NTW];
-  bwd_prologue<T, D, GS, true, true, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  const int mode =
+      bwd_prologue<T, D, GS, true, true, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
+  // beyond the mid reference's range: NaN records, so that the reverse pass
+  // carries NaN into every state gradient before this chunk
+  const float nanf = mode == kBwdBeyond ? __builtin_nanf("") : 0.f;
   // K~ into the region the inverse has finished with
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -597,7 +626,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
       pw = M::mma(frag_rm_perm<T>(sm.pb, LDC, 16 * t, ks, lane), acc_frag<T>(wk, ks), pw);
     float z[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] * __expf(R.G[t][j]) - pw[j]);
+    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] * __expf(R.G[t][j]) - pw[j]) + nanf;
     st_fnat4(rec + RC::ZF, KC, c, 16 * t + 4 * grp, z[0], z[1], z[2], z[3]);
   }
   // M^T tiles (rows c', column c) = Diag(e^gamma) - K~^T Wk, stored as M
@@ -613,7 +642,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c2 = 16 * cb + 4 * grp + j;
-      m[j] = (c2 == c ? egam : 0.f) - mt[j];
+      m[j] = (c2 == c ? egam : 0.f) - mt[j] + nanf;
     }
     st_fnat4(rec + RC::MF, KD, c, 16 * cb + 4 * grp, m[0], m[1], m[2], m[3]);
   }
@@ -855,12 +884,42 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   if (!locate(gm, slot, loc)) return;
   BwdSmem<T, D> sm(smem);
   f32x4_t Bm[NTW];
+  int mode;
   {
     BwdRegs R0;  // recomputed at the end rather than kept live (registers)
-    bwd_prologue<T, D, GS, false, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R0, Bm);
+    mode = bwd_prologue<T, D, GS, false, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R0, Bm);
+    if (mode == kBwdMid) {
+      // W needs the true Kp = K^ o e^G (it multiplies S): this lane's column
+      const int lane0 = threadIdx.x & 63, c0 = 16 * (threadIdx.x >> 6) + (lane0 & 15);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          st_f(sm.kp + (16 * t + 4 * (lane0 >> 4) + j) * LDX + c0,
+               R0.kh[t][j] * __expf(R0.G[t][j]));
+    }
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);  // this lane's column (d_k or d_v)
+  if (mode == kBwdBeyond) {
+    // a half of the chunk decays by more than 80 in some channel: NaN
+    // gradients for its rows (the reverse pass already carries NaN into the
+    // state gradients before it)
+    const float nan = __builtin_nanf("");
+    const int64_t r0 = loc.tok0 * H + h;
+    for (int e = tid; e < loc.len * D; e += L::NT) {
+      const int64_t o = (r0 + (int64_t)(e / D) * H) * D + e % D;
+      st_f(dq + o, nan);
+      st_f(dk + o, nan);
+      st_f(dv + o, nan);
+      if (!GS) dg[o] = nan;
+    }
+    for (int r = tid; r < loc.len; r += L::NT) {
+      dbeta[r0 + (int64_t)r * H] = nan;
+      if (GS) dg[r0 + (int64_t)r * H] = nan;
+    }
+    return;
+  }
   const T* S = states + (slot * H + h) * (int64_t)D * D;
   const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
   // per-token tensors: uniform bases at the chunk's first row, 32-bit offsets
@@ -1014,9 +1073,14 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * rb + 4 * grp + j;
       const float da = i < r ? -aa[j] : 0.f;
-      st_f(sm.pb + r * LDC + i, i <= r ? ap[j] : 0.f);
+      // dP strictly below the diagonal; the diagonal stays in fp32 (x1):
+      // see the key side
+      st_f(sm.pb + r * LDC + i, i < r ? ap[j] : 0.f);
+      if (i == r) sm.x1[r] = ap[j];
       st_f(sm.db + r * LDC + i, sm.beta[r] * da);
-      const float part = sum16(da * Bm[tt][j]);
+      // (a select, not a product with the zero mask: with the mid reference the
+      // masked tiles above the diagonal may hold inf)
+      const float part = sum16(i < r ? da * Bm[tt][j] : 0.f);
       if ((lane & 15) == 0) sm.red[(NW + ib) * kC + r] = part;  // one tile per (ib, r)
     }
   }
@@ -1051,12 +1115,14 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
         R.qh[t][j] *= sm.rq[r];
       }
   }
+  const bool mid = mode == kBwdMid;
+  const float mr = mid ? g_row31(R, lane) : 0.f, em = mid ? __expf(mr) : 1.f;
   // Two passes, each with its own B operands, the gate factors applied per
   // tile so that one tile's accumulators are live at a time:
   //   1. dQp = dO' S^T + dP Km,  dKp = dB Km - Diag(beta) L S^T
   //   2. dKm = dB^T Kp + dP^T Qp,  dK~ = W dS'^T,  rowsum(S o dS')
   // (q^ is read again for the norm's projection at the end rather than kept)
-  float dkh[4][4], dqh[4][4], dG[4][4];  // dkh holds dKp o e^G after pass 1
+  float dkh[4][4], dqh[4][4], dG[4][4];  // dkh holds dKp o e^G (+ P's diagonal) after pass 1
   __builtin_amdgcn_sched_barrier(0);
   {
     typename M::frag st[KD], kmc[KC];
@@ -1073,19 +1139,35 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
         a = M::mma(frag_at<T>(sm.dob, LDX, 16 * t, ks, lane), st[ks], a);  // dO' S^T
         x = M::mma(frag_at<T>(lb, LDX, 16 * t, ks, lane), st[ks], x);      // L S^T
       }
+      // dq^ = (dO' S^T) o e^G + (dP Km) o e^(G-m) = (e^m dO' S^T + dP Km) o e^(G-m)
+      // with m the reference (e^m = 1 on the fast path); dk^ alike
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] *= em;
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) {
         a = M::mma(frag_at<T>(sm.pb, LDC, 16 * t, ks, lane), kmc[ks], a);  // dP Km
         b = M::mma(frag_at<T>(sm.db, LDC, 16 * t, ks, lane), kmc[ks], b);  // dB Km
       }
+      // P's diagonal (dP_rr) enters dq^ as dP_rr k^_r and dk^ as dP_rr q^_r,
+      // and the two cancel in dG exactly.  It is kept out of the MFMA
+      // products (bf16 operands) and added here in fp32, so dG never forms
+      // that cancellation from rounded operands (with fast-forgetting gates
+      // the rest of dG is small beside it).
+      float ddv[4];
+      __asm__ volatile("" ::: "memory");  // this tile's diagonal values only
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ddv[j] = sm.x1[16 * t + 4 * grp + j];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float eg = __expf(R.G[t][j]);
-        dqh[t][j] = a[j] * eg;
-        dkh[t][j] = (b[j] - sm.beta[16 * t + 4 * grp + j] * x[j]) * eg;
-        dG[t][j] = R.qh[t][j] * dqh[t][j];  // q^ is not needed again until the end
+        const int r = 16 * t + 4 * grp + j;
+        const float eg = __expf(R.G[t][j] - mr), dd = ddv[j];
+        const float dqs = a[j] * eg;  // dq^ without the diagonal term
+        dqh[t][j] = dqs + dd * R.kh[t][j];
+        dkh[t][j] = (b[j] - sm.beta[r] * x[j] * em) * eg + dd * R.qh[t][j];
+        // (pass 2 adds k^ dkh to dG: its diagonal term is taken off here)
+        dG[t][j] = R.qh[t][j] * dqs - R.kh[t][j] * (dd * R.qh[t][j]);
         const float qd = sum16(R.qh[t][j] * dqh[t][j]);  // row dot q^ . dq^, this wave's part
-        if ((lane & 15) == 0) sm.red[(NW + wave) * kC + 16 * t + 4 * grp + j] = qd;
+        if ((lane & 15) == 0) sm.red[(NW + wave) * kC + r] = qd;
       }
     }
   }
@@ -1099,6 +1181,19 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       dst[ks] = grow_frag<T, D>(dS, c, ks, lane);
 #pragma unroll
       for (int e = 0; e < KPL; ++e) rs += frag_val(xs, e) * frag_val(dst[ks], e);
+    }
+    if (mid) {
+      // Kp relative to the reference again (W, the only product of the true
+      // Kp, is done); each wave reads back only its own columns, which its
+      // own lanes write: wave-local ordering suffices
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          st_f(sm.kp + (16 * t + 4 * grp + j) * LDX + c, R.kh[t][j] * __expf(R.G[t][j] - mr));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks) {
@@ -1120,7 +1215,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float G = R.G[t][j];
-        const float a = dkh[t][j], bm = m[j] * __expf(-G), e = kt[j] * __expf(R.gam - G);
+        const float a = dkh[t][j], bm = m[j] * __expf(mr - G), e = kt[j] * __expf(R.gam - G);
         dkh[t][j] = a + bm + e;
         dG[t][j] += R.kh[t][j] * (a - bm - e);
         dgam += R.kh[t][j] * e;

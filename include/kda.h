@@ -186,9 +186,13 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
  *   workspace  device scratch of at least kda_chunk_bwd_workspace_bytes().
  * Supported: bf16 with dk = dv = 64 or 128, fp32 with dk = dv = 64
  * (KDA_ERR_UNSUPPORTED otherwise).  Alignment as kda_chunk_fwd (d_o, dq, dk,
- * dv 16-byte; dg, dbeta 4-byte).  Outputs must not alias inputs.  Every
- * chunk's per-channel decay (the sum of its 64 log-gates) must be >= -80;
- * beyond that the results are unspecified (no fault, no hang). */
+ * dv 16-byte; dg, dbeta 4-byte).  Outputs must not alias inputs.  Exponent
+ * range: within each 64-token chunk, each half (32 tokens) may decay by at
+ * most 80 per channel (the sum of its log-gates >= -80; chunk decays down
+ * to about -160).  A chunk beyond that gets NaN gradients for its tokens,
+ * and its NaN state gradient reaches the dk, dv, dg and dbeta of every
+ * earlier token of its sequence and d_init_state (dq of earlier tokens does
+ * not depend on it); no fault, no hang; the forward has no such limit. */
 kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, const void* k,
                            const void* v, const float* g, const float* beta,
                            const float* init_state, const int32_t* cu_seqlens, const void* d_o,

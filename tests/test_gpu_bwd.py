@@ -220,3 +220,48 @@ def test_bwd_more_chunks_than_one_launch():
         for name, x, r in zip(NAMES[:5], got[:5], ref[:5]):
             assert_close(f"{name} window {a}", x[:, a:a + win], r[:, warm:warm + win],
                          TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 64)], ids=["bf16-d128", "bf16-d64", "f32-d64"])
+def test_bwd_strong_gates_mid_reference(dtype, d):
+    """Chunks beyond the fast path's exponent bound: gates logsigmoid(N(0,1) - 1)
+    (chunk decays around -90) and constant gates of -2.34 per token (every
+    chunk decays by ~-150, each half by ~-75)."""
+    inp = _inputs(2, 300, 3, d, dtype, seed=41, gate_shift=-1.0)
+    assert float(inp["g"][0, :64].sum(0).min()) < -80.0  # beyond the fast bound
+    _run(inp, _up(inp, 42), dtype, label="gates logsigmoid(N - 1)")
+    inp = _inputs(1, 320, 2, d, dtype, seed=43)
+    inp["g"] = torch.full_like(inp["g"], -2.34)
+    _run(inp, _up(inp, 44), dtype, label="chunk decay -150")
+
+
+def test_bwd_strong_gates_per_head():
+    inp = _inputs(1, 200, 2, 128, torch.bfloat16, seed=45, gate_shift=-1.2, gate_per_head=True)
+    _run(inp, _up(inp, 46), torch.bfloat16, label="gate per head, strong", per_head=True)
+
+
+def test_bwd_beyond_the_mid_reference_is_nan():
+    """A chunk one half of which decays by more than 80 in some channel (here
+    five tokens at g = -30 in chunk 1): its tokens' gradients are NaN; the NaN
+    state gradient reaches the k, v, g, beta gradients of every earlier token
+    and d_init, while dq of earlier tokens (q only reads the state) and every
+    gradient of later tokens match the oracle."""
+    inp = _inputs(1, 300, 2, 64, torch.float32, seed=47)
+    inp["g"][:, 70:75] = -30.0
+    up = _up(inp, 48)
+    B, T, H, d = inp["q"].shape
+    print("backward beyond the mid reference: NaN below token 128", flush=True)
+    got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                        inp["init_state"], up["dfinal"])
+    torch.cuda.synchronize()
+    ref = O.kda_bwd(*(_host(inp[key]) for key in ("q", "k", "v", "g", "beta")), _host(up["do"]),
+                    _host(inp["init_state"]), _host(up["dfinal"]))
+    for name, a, b in zip(NAMES[:5], got[:5], ref[:5]):
+        nan_from = 64 if name == "dq" else 0
+        assert bool((~torch.isfinite(a[:, nan_from:128].float())).all()), \
+            f"{name}: tokens {nan_from}..127 not NaN"
+        assert_close(f"{name} (tokens >= 128)", a[:, 128:], b[:, 128:], TOL[torch.float32])
+        if name == "dq":
+            assert_close("dq (tokens < 64)", a[:, :64], b[:, :64], TOL[torch.float32])
+    assert bool((~torch.isfinite(got[5])).all()), "d_init not NaN"

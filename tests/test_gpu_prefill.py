@@ -95,6 +95,21 @@ def test_prefill_extreme_gates_exact_path():
     _check(inp, torch.bfloat16, label="extreme gates bf16")
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)],
+                         ids=["bf16-d128", "f32-d64"])
+def test_prefill_strong_gates_mid_reference(dtype, d):
+    """Fast-forgetting channels beyond the fast path's bound: gates drawn as
+    logsigmoid(N(0,1) - 1) (chunk decays around -90) and constant gates of
+    -2.34 per token (every chunk decays by ~-150, each half by ~-75): A and P
+    come from the mid-reference products."""
+    inp = _inputs(2, 300, 3, d, dtype, seed=21, gate_shift=-1.0)
+    assert float(inp["g"][0, :64].sum(0).min()) < -80.0  # beyond the fast bound
+    _check(inp, dtype, label="gates logsigmoid(N - 1)")
+    inp = _inputs(1, 320, 2, d, dtype, seed=22)
+    inp["g"] = torch.full_like(inp["g"], -2.34)
+    _check(inp, dtype, label="chunk decay -150")
+
+
 def test_prefill_varlen_small():
     lens = [1, 63, 64, 65, 0, 130, 7]
     for dtype in (torch.float32, torch.bfloat16):

@@ -66,8 +66,9 @@ def test_random_config(seed):
     assert_close("o", o, o_ref, tol)
     assert_close("final_state", fs, fs_ref, tol)
 
-    # the backward: bf16 at d = 64 or 128, fp32 at d = 64, chunk decay >= -80
-    if (dtype == torch.float32 and d == 128) or c["shift"] < 1.0:
+    # the backward: bf16 at d = 64 or 128, fp32 at d = 64 (every gate strength:
+    # the strong ones take the mid-reference products)
+    if dtype == torch.float32 and d == 128:
         return
     N = B if cu is None else cu.numel() - 1
     up = W.upstream_grads(batch=B, seqlen=T, heads=H, dk=d, dv=d, num_seqs=N, dtype=dtype,
