@@ -215,6 +215,95 @@ def write_traffic(fetch_csv: str, write_csv: str, out: str = TRAFFIC_FILE) -> di
     return t
 
 
+# Counter passes over --probe for the compute-side profile (at most 8 SQ and
+# 2 GRBM counters fit one pass).
+COUNTER_PASSES = (
+    ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU",
+     "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM", "GRBM_GUI_ACTIVE"),
+    ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+     "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+)
+MI355X_SIMDS = 256 * 4
+MI355X_XCDS = 8
+COUNTER_FILE = os.path.join(ROOT, "profiles", "kda_compute_counters.md")
+# token-heads of one probe call of each workload (prefill and backward: 8192 x 32)
+_PROBE_TOKEN_HEADS = {"prefill": 8192 * 32, "backward": 8192 * 32, "decode": 256 * 32}
+
+
+def write_counters(csvs, out: str = COUNTER_FILE, command: str = "") -> str:
+    """Per-kernel compute counters from the passes of COUNTER_PASSES over
+    `--probe` (rocprofv3 --pmc ... --output-format csv): MFMA FLOPs per call
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) and per token-head, MFMA busy share
+    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs)), instructions per
+    wave, LDS bank-conflict cycles per LDS-active cycle."""
+    import csv
+    per = {}   # part -> counter -> summed value
+    disp = {}  # part -> dispatches
+    keys = {}  # part -> workload
+    for path in csvs:
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        ids = sorted({int(r["Dispatch_Id"]) for r in rows})
+        names = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in rows}
+        last_pro = max((i for i in ids if "short_conv_kernel" in names[i]), default=ids[-1] + 1)
+        seen = set()
+        for r in rows:
+            i = int(r["Dispatch_Id"])
+            part, key = _probe_key(r["Kernel_Name"], i > last_pro)
+            if key is None:
+                continue
+            keys[part] = key
+            c = per.setdefault(part, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if path == csvs[0] and i not in seen:
+                seen.add(i)
+                disp[part] = disp.get(part, 0) + 1
+    calls = {key: n for _, key, n in _PROBE_KERNELS}
+    lines = ["# Compute-side counters per kernel", "",
+             "Two `rocprofv3 --pmc` passes over `python3 bench.py --probe` (each kernel",
+             "dispatched for two calls of its workload; counters serialize the dispatches).",
+             "Prefill and backward: B=1 T=8192 H=32 d=128 bf16 (262,144 token-heads per call).",
+             "MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+             f"(GRBM_GUI_ACTIVE / {MI355X_XCDS} x {MI355X_SIMDS} SIMDs; the csv's GRBM_GUI_ACTIVE is the",
+             "sum over the XCDs' GRBM instances, each counting the dispatch: 2.98 M for a 151 us",
+             "fill kernel); LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; VALU active",
+             "and LDS wait = SQ_ACTIVE_INST_VALU, SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES;",
+             "per-wave figures divide by SQ_WAVES.", ""]
+    if command:
+        lines += ["Commands:", "", "```", command, "```", ""]
+    lines += ["| kernel | dispatches | MFMA GFLOP per call | MFMA FLOP per token-head | "
+              "MFMA busy | VALU instr / wave | MFMA instr / wave | LDS instr / wave | "
+              "SALU instr / wave | VMEM instr / wave | LDS bank conflict | VALU active | "
+              "LDS wait share |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for part in sorted(per):
+        c = per[part]
+        key = keys[part]
+        n = calls[key]
+        g = lambda k: c.get(k, float("nan"))
+        waves = g("SQ_WAVES")
+        flop = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / n
+        th = _PROBE_TOKEN_HEADS.get(key)
+        # GRBM_GUI_ACTIVE appears in both passes, each the sum over the XCDs'
+        # GRBM instances (one per XCD, each counting the whole dispatch)
+        gui = g("GRBM_GUI_ACTIVE") / 2 / MI355X_XCDS
+        ratio = lambda a, b: 100 * a / b if b else float("nan")
+        lines.append(
+            f"| {part} | {disp.get(part, 0)} | {flop / 1e9:.2f} | "
+            f"{(flop / th) if th else float('nan'):,.0f} | "
+            f"{ratio(g('SQ_VALU_MFMA_BUSY_CYCLES'), gui * MI355X_SIMDS):.1f} % | "
+            f"{g('SQ_INSTS_VALU') / waves:,.0f} | {g('SQ_INSTS_MFMA') / waves:,.0f} | "
+            f"{g('SQ_INSTS_LDS') / waves:,.0f} | {g('SQ_INSTS_SALU') / waves:,.0f} | "
+            f"{g('SQ_INSTS_VMEM') / waves:,.0f} | "
+            f"{ratio(g('SQ_LDS_BANK_CONFLICT'), g('SQ_LDS_IDX_ACTIVE')):.1f} % | "
+            f"{ratio(g('SQ_ACTIVE_INST_VALU'), g('SQ_WAVE_CYCLES')):.1f} % | "
+            f"{ratio(g('SQ_WAIT_INST_LDS'), g('SQ_WAVE_CYCLES')):.1f} % |")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def epilogue_inputs():
     """Synthetic epilogue operands at the prefill output's size."""
     gen = torch.Generator(device="cuda").manual_seed(1005)
@@ -339,6 +428,64 @@ def bench_gate_modes(reps: int = 5):
         row["kda_over_gdn"] = row["kda_us"] / row["gdn_us"]
         rows.append(row)
     return rows
+
+
+def chunk_exponent_modes(g: torch.Tensor, chunk: int = 64, bound: float = -80.0) -> dict:
+    """Share of (chunk, head) pairs in each exponent mode of the chunk form,
+    from the per-channel log-gates [B, T, H, d] (T a multiple of the chunk):
+    fast while every channel's chunk decay is >= bound, mid while each 32-token
+    half decays by at most -bound, exact beyond."""
+    B, T, H, d = g.shape
+    x = g.float().reshape(B, T // chunk, chunk, H, d)
+    half = chunk // 2
+    gam = x.sum(2).amin(-1)
+    h1 = x[:, :, :half].sum(2).amin(-1)
+    h2 = x[:, :, half:].sum(2).amin(-1)
+    fast = gam >= bound
+    mid = ~fast & (h1 >= bound) & (h2 >= bound)
+    n = gam.numel()
+    return {"fast": fast.sum().item() / n, "mid": mid.sum().item() / n,
+            "exact": (n - fast.sum().item() - mid.sum().item()) / n}
+
+
+def bench_strong_gates(steps: int, warmup: int):
+    """The prefill workload's shapes with fast-forgetting gates,
+    g = logsigmoid(N(0,1) - 1) per channel (mean about -1.3 per token, so most
+    chunks decay far beyond -80): prefill and backward per call."""
+    w = W.PREFILL_8K
+    inp = W.prefill_inputs(batch=w.batch, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
+                           dtype=w.dtype, device="cuda", seed=w.seed, init="normal",
+                           gate_shift=-1.0)
+    up = W.upstream_grads(batch=w.batch, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
+                          num_seqs=w.batch, dtype=w.dtype, device="cuda", seed=w.seed + 7)
+    B, T, H, d = inp["q"].shape
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fwd = lambda: kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                inp["init_state"], out=o, final_state=fs, stream=stream)
+    bwd = lambda: kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
+                                inp["init_state"], up["dfinal"], stream=stream)
+    res = {}
+    for name, run, n in (("prefill", fwd, steps), ("backward", bwd, max(1, steps // 2))):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record(stream)
+        for _ in range(n):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n * 1e3
+    finite = bool(torch.isfinite(o).all().item())
+    return {"workload": "prefill B=1 H=32 T=8192 d=128 bf16 as above, gates g = "
+                        "logsigmoid(N(0,1) - 1) per channel, nonzero initial state",
+            "prefill_us_per_call": res["prefill"],
+            "prefill_tokens_per_s": B * T / (res["prefill"] * 1e-6),
+            "backward_us_per_call": res["backward"],
+            "chunk_modes": chunk_exponent_modes(inp["g"]),
+            "output_finite": finite}
 
 
 def _events():
@@ -610,10 +757,18 @@ def main():
                     help="run the kernels for hardware-counter passes and exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic file from the two counter passes over --probe")
+    ap.add_argument("--write-counters", nargs="+", metavar="PASS_CSV",
+                    help="write the compute-counter summary from the passes of "
+                         "COUNTER_PASSES over --probe")
+    ap.add_argument("--counter-command", default="",
+                    help="the commands that made the passes, quoted in the summary")
     args = ap.parse_args()
     if args.write_traffic:
         t = write_traffic(*args.write_traffic)
         print(json.dumps({k: v for k, v in t.items() if k.endswith("_bytes")}))
+        return
+    if args.write_counters:
+        print(write_counters(args.write_counters, command=args.counter_command))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are "
@@ -638,6 +793,7 @@ def main():
     bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 2))
     vl, inputs_sha["varlen"] = bench_varlen(max(1, args.steps // 2), 2)
     m1, inputs_sha["prefill_1m_first_65536_tokens"] = bench_prefill_1m()
+    sg = bench_strong_gates(max(2, args.steps // 2), 3)
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -715,6 +871,7 @@ def main():
                        "rows": gm},
         "varlen": vl,
         "prefill_1m": m1,
+        "strong_gates": sg,
         "wall_s_prefill_loop": pf["wall"],
     }
     if not args.no_cpu_baseline:

@@ -34,3 +34,18 @@ def test_workload_table():
     assert set(W.ALL) == {W.FP32_SMALL.name, W.PREFILL_8K.name, W.DECODE_256.name,
                           W.VARLEN_16.name, W.PREFILL_1M.name}
     assert W.PREFILL_1M.seqlen == 1 << 20 and W.PREFILL_1M.ckpt_every == 65536
+
+
+def test_chunk_exponent_mode_shares():
+    """The benchmark's count of chunks per exponent mode: constant gates put
+    the chunk decay and the half decays at known values (g = -1: gamma = -64,
+    fast; g = -2: halves -64, mid; one channel at g = -3: halves -96, exact)."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    g = torch.full((1, 192, 2, 4), -1.0)
+    g[:, 64:128] = -2.0
+    g[:, 128:192, 1, 3] = -3.0
+    m = bench.chunk_exponent_modes(g)
+    assert m == {"fast": 3 / 6, "mid": 2 / 6, "exact": 1 / 6}
