@@ -209,6 +209,14 @@ __device__ __forceinline__ void st_nt(bf16* p, float x) {
 }
 __device__ __forceinline__ void st_nt(float* p, float x) { __builtin_nontemporal_store(x, p); }
 
+// A copy of x the compiler cannot see through: lane indices renewed from it
+// at a phase boundary make the phase form its own address arithmetic there,
+// rather than keep an earlier phase's addresses live in registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Sum over the 16 lanes of a lane group (the 16 columns of an accumulator).
 __device__ __forceinline__ float sum16(float x) {
 #pragma unroll
@@ -244,7 +252,14 @@ struct BwdLds {
   static constexpr int SCR = COMPACT ? 2 * FB : DB;
   static constexpr int SM = COMPACT ? PB + CB : DB + CB;
   // small: beta, rk, rq, x0, x1, x2 [kC] and red [2][NW][kC]
-  static constexpr int BYTES = SM + (6 * kC + 2 * NW * kC) * 4;
+  static constexpr int SMALL = (6 * kC + 2 * NW * kC) * 4;
+  // full layout, where it fits: the fp32 tiles of Kp Km^T (for dbeta), kept
+  // from the prologue to the chunk x chunk products in LDS rather than in
+  // registers
+  static constexpr int LDB = kC + 4;
+  static constexpr int BM = SM + SMALL;
+  static constexpr bool BM_LDS = !COMPACT && BM + kC * LDB * 4 <= 160 * 1024;
+  static constexpr int BYTES = BM_LDS ? BM + kC * LDB * 4 : SM + SMALL;
   static_assert(BYTES <= 160 * 1024, "per-chunk backward LDS exceeds a CU");
 };
 
@@ -252,7 +267,7 @@ template <typename T, int D, bool COMPACT = false>
 struct BwdSmem {
   using L = BwdLds<T, D, COMPACT>;
   T *kp, *km, *qp, *kt, *tb, *pb, *db, *wb, *dob;
-  float *sA, *sT, *scratch, *beta, *rk, *rq, *x0, *x1, *x2, *red;
+  float *sA, *sT, *scratch, *beta, *rk, *rq, *x0, *x1, *x2, *red, *bm;
   __device__ explicit BwdSmem(char* s) {
     kp = reinterpret_cast<T*>(s + L::KP);
     km = reinterpret_cast<T*>(s + L::KM);
@@ -273,6 +288,7 @@ struct BwdSmem {
     x1 = x0 + kC;
     x2 = x1 + kC;
     red = x2 + kC;
+    bm = L::BM_LDS ? reinterpret_cast<float*>(s + L::BM) : nullptr;
   }
 };
 
@@ -883,11 +899,25 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   ChunkLoc loc;
   if (!locate(gm, slot, loc)) return;
   BwdSmem<T, D> sm(smem);
-  f32x4_t Bm[NTW];
   int mode;
+  f32x4_t Bm[L::BM_LDS ? 1 : NTW];  // (unused when the tiles live in LDS)
   {
     BwdRegs R0;  // recomputed at the end rather than kept live (registers)
-    mode = bwd_prologue<T, D, GS, false, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R0, Bm);
+    f32x4_t Bp[NTW];
+    mode = bwd_prologue<T, D, GS, false, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R0, Bp);
+    if constexpr (!L::BM_LDS) {
+#pragma unroll
+      for (int tt = 0; tt < NTW; ++tt) Bm[tt] = Bp[tt];
+    } else {
+      const int lane0 = threadIdx.x & 63, w0 = threadIdx.x >> 6;
+#pragma unroll
+      for (int tt = 0; tt < NTW; ++tt) {
+        const int p = w0 + NW * tt, i = 16 * (p & 3) + (lane0 & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sm.bm[(16 * (p >> 2) + 4 * (lane0 >> 4) + j) * L::LDB + i] = Bp[tt][j];
+      }
+    }
     if (mode == kBwdMid) {
       // W needs the true Kp = K^ o e^G (it multiplies S): this lane's column
       const int lane0 = threadIdx.x & 63, c0 = 16 * (threadIdx.x >> 6) + (lane0 & 15);
@@ -899,8 +929,14 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
                R0.kh[t][j] * __expf(R0.G[t][j]));
     }
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
-  const int c = 16 * wave + (lane & 15);  // this lane's column (d_k or d_v)
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int lane = tid & 63, grp = lane >> 4;
+  int c = 16 * wave + (lane & 15);  // this lane's column (d_k or d_v)
+  auto renew = [&]() {
+    lane = opaque(tid) & 63;
+    grp = lane >> 4;
+    c = 16 * wave + (lane & 15);
+  };
   if (mode == kBwdBeyond) {
     // a half of the chunk decays by more than 80 in some channel: NaN
     // gradients for its rows (the reverse pass already carries NaN into the
@@ -920,6 +956,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     }
     return;
   }
+  renew();
   const T* S = states + (slot * H + h) * (int64_t)D * D;
   const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
   // per-token tensors: uniform bases at the chunk's first row, 32-bit offsets
@@ -942,7 +979,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // go (the inverse's region, dead now): each lane then reads its own column
   // and later overwrites exactly those positions, so no barrier separates
   // the reads from the W and dO' writes.
-  uint32_t sraw[KD][KPL], draw[KD][KPL];
+  uint32_t sraw[KD][KPL];
   {
     constexpr int NT = L::NT;
     constexpr int VE = 16 / (int)sizeof(T), PR = D / VE, NPK = kC * PR / NT;
@@ -965,7 +1002,6 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       for (int e = 0; e < KPL; ++e) {
         const int cc = ks * M::KSTEP + KPL * grp + e;
         sraw[ks][e] = ld_raw(S + sblk<D>(cc, c));
-        draw[ks][e] = ld_raw(dS + sblk<D>(cc, c));
       }
 #pragma unroll
     for (int i = 0; i < NPK; ++i) {
@@ -976,11 +1012,19 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   }
   __syncthreads();
   // Kp S, then R = Diag(beta)(V - Kp S) and W = T R
+  uint32_t draw[KD][KPL];
   f32x4_t vmk[4], acc[4], w[4];
   {
     typename M::frag sb[KD];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) sb[ks] = raw_frag(sraw[ks], T{});
+    // the dS' columns (k = c) once S's raw registers are free: their latency
+    // overlaps the Kp S and T R products
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks)
+#pragma unroll
+      for (int e = 0; e < KPL; ++e)
+        draw[ks][e] = ld_raw(dS + sblk<D>(ks * M::KSTEP + KPL * grp + e, c));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);  // one tile at a time (registers)
@@ -1058,6 +1102,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   __syncthreads();
 
   // ---- chunk x chunk: dP = tril(dO' W^T), dA = -tril_-1(L W^T), dB ------------
+  renew();
 #pragma unroll
   for (int tt = 0; tt < NTW; ++tt) {
     const int p = wave + NW * tt, rb = p >> 2, ib = p & 3;
@@ -1080,7 +1125,10 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       st_f(sm.db + r * LDC + i, sm.beta[r] * da);
       // (a select, not a product with the zero mask: with the mid reference the
       // masked tiles above the diagonal may hold inf)
-      const float part = sum16(i < r ? da * Bm[tt][j] : 0.f);
+      float bmv;
+      if constexpr (L::BM_LDS) bmv = sm.bm[r * L::LDB + i];
+      else bmv = Bm[tt][j];
+      const float part = sum16(i < r ? da * bmv : 0.f);
       if ((lane & 15) == 0) sm.red[(NW + ib) * kC + r] = part;  // one tile per (ib, r)
     }
   }
@@ -1101,6 +1149,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // hoisted early, they would hold registers across the phases before)
   __builtin_amdgcn_sched_barrier(0);
   // G, k^, q^ again (the chunk's k, q, g are still in the cache)
+  renew();
   BwdRegs R;
   {
     float gr[4][4];
@@ -1121,8 +1170,12 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // tile so that one tile's accumulators are live at a time:
   //   1. dQp = dO' S^T + dP Km,  dKp = dB Km - Diag(beta) L S^T
   //   2. dKm = dB^T Kp + dP^T Qp,  dK~ = W dS'^T,  rowsum(S o dS')
-  // (q^ is read again for the norm's projection at the end rather than kept)
-  float dkh[4][4], dqh[4][4], dG[4][4];  // dkh holds dKp o e^G (+ P's diagonal) after pass 1
+  // dq^ is complete after pass 1: it goes to LDS at once, into this wave's
+  // own columns of Km (read by no other wave, and by this one only into the
+  // kmc registers before it), which is where the output stage stages dq;
+  // q^ stays in registers for the norm's projection there.
+  float dkh[4][4], dG[4][4];  // dkh holds dKp o e^G (+ P's diagonal) after pass 1
+  T* sdqh = sm.km;
   __builtin_amdgcn_sched_barrier(0);
   {
     typename M::frag st[KD], kmc[KC];
@@ -1162,17 +1215,19 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
         const int r = 16 * t + 4 * grp + j;
         const float eg = __expf(R.G[t][j] - mr), dd = ddv[j];
         const float dqs = a[j] * eg;  // dq^ without the diagonal term
-        dqh[t][j] = dqs + dd * R.kh[t][j];
+        const float dqh = dqs + dd * R.kh[t][j];
+        st_f(sdqh + r * LDX + c, dqh);
         dkh[t][j] = (b[j] - sm.beta[r] * x[j] * em) * eg + dd * R.qh[t][j];
         // (pass 2 adds k^ dkh to dG: its diagonal term is taken off here)
         dG[t][j] = R.qh[t][j] * dqs - R.kh[t][j] * (dd * R.qh[t][j]);
-        const float qd = sum16(R.qh[t][j] * dqh[t][j]);  // row dot q^ . dq^, this wave's part
+        const float qd = sum16(R.qh[t][j] * dqh);  // row dot q^ . dq^, this wave's part
         if ((lane & 15) == 0) sm.red[(NW + wave) * kC + r] = qd;
       }
     }
   }
   float rs = 0.f, dgam = 0.f;  // rowsum(S o dS') of row c
   __builtin_amdgcn_sched_barrier(0);
+  renew();
   {
     typename M::frag dst[KD], kpc[KC], qpc[KC];
 #pragma unroll
@@ -1277,26 +1332,26 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // above), and the tiles go out in 16-byte non-temporal pieces through
   // buffer resources bounded at the chunk's last valid row, whole lines at
   // a time (rows past the end are dropped by the bound).
+  renew();
   char* ostage = reinterpret_cast<char*>(sm.kp);
   T* sdk = reinterpret_cast<T*>(ostage);
-  T* sdq = reinterpret_cast<T*>(ostage + L::XB);
+  T* sdq = reinterpret_cast<T*>(ostage + L::XB);  // = sdqh, dq^ already there
   float* sdg = reinterpret_cast<float*>(ostage + 2 * L::XB);
   constexpr int LDG = D + 4;
   static_assert(2 * L::XB + kC * LDG * 4 <= 4 * L::XB, "staged gradients must fit");
-  const T* qrow = q + row0 * D;
+  static_assert(L::KM == L::KP + L::XB, "dq^ is staged where the output stage reads dq");
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * t + 4 * grp + j;
-      float gk = dkh[t][j], gq = dqh[t][j];
+      float gk = dkh[t][j];
       if (qk_l2norm) {
-        const float qn = r < loc.len ? ld_f(qrow + tok(r) * D + c) * sm.rq[r] : 0.f;
         gk = sm.rk[r] * (gk - sm.x1[r] * R.kh[t][j]);
-        gq = sm.rq[r] * (gq - sm.x2[r] * qn);
+        const float gq = ld_f(sdq + r * LDX + c);
+        st_f(sdq + r * LDX + c, sm.rq[r] * (gq - sm.x2[r] * R.qh[t][j]));
       }
       st_f(sdk + r * LDX + c, gk);
-      st_f(sdq + r * LDX + c, gq);
       if constexpr (!GS) sdg[r * LDG + c] = dgo[t][j];
     }
   __syncthreads();
