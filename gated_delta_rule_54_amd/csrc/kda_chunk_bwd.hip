@@ -217,10 +217,20 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// Sum over the 16 lanes of a lane group (the 16 columns of an accumulator).
+// Sum over the 16 lanes of a lane group (the 16 columns of an accumulator),
+// every lane of the group receiving it.  The lane group is a DPP row: swap
+// neighbours, then pairs (quad permutations), then the quads of each half-row
+// (half-row mirror), then the halves (row mirror) -- four VALU steps with no
+// LDS traffic.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
+  x += dpp_f<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
   return x;
 }
 
@@ -321,12 +331,18 @@ __device__ __forceinline__ int bwd_mode(const BwdRegs& R, int lane) {
                                                                                : kBwdMid;
 }
 
-// Raw k, q, g of this lane's column and rows (zero past the chunk's end).
-// NTL: read non-temporally (the caller reads them once).
-template <typename T, int D, bool GS, bool NTL = false>
-__device__ __forceinline__ void load_cols(const T* __restrict__ q, const T* __restrict__ k,
-                                          const float* __restrict__ g, const ChunkLoc& loc, int H,
-                                          int h, int c, int grp, BwdRegs& R, float (&gr)[4][4]) {
+// Raw k, q, g of this lane's column and rows, as loaded (the loads are
+// issued here and waited for where cols_from_raw uses them, so a caller can
+// put other work between the two); rows past the chunk's end read its last
+// row and are zeroed by cols_from_raw.
+struct ColsRaw {
+  uint32_t k[4][4], q[4][4];
+  float g[4][4];
+};
+template <typename T, int D, bool GS>
+__device__ __forceinline__ void load_cols_raw(const T* __restrict__ q, const T* __restrict__ k,
+                                              const float* __restrict__ g, const ChunkLoc& loc,
+                                              int H, int h, int c, int grp, ColsRaw& X) {
   // uniform bases (the chunk's first row) and 32-bit per-lane offsets
   const int64_t row0 = loc.tok0 * H + h;
   const T* kb = k + row0 * D;
@@ -336,19 +352,25 @@ __device__ __forceinline__ void load_cols(const T* __restrict__ q, const T* __re
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 16 * t + 4 * grp + j;
-      const int off = min(r, loc.len - 1) * H * D + c;
-      const bool ok = r < loc.len;
-      const float* gp = GS ? gb + min(r, loc.len - 1) * H : gb + off;
-      if constexpr (NTL) {
-        R.kh[t][j] = ok ? raw_val<T>(ld_raw_nt(kb + off)) : 0.f;
-        R.qh[t][j] = ok ? raw_val<T>(ld_raw_nt(qb + off)) : 0.f;
-        gr[t][j] = ok ? __builtin_nontemporal_load(gp) : 0.f;
-      } else {
-        R.kh[t][j] = ok ? ld_f(kb + off) : 0.f;
-        R.qh[t][j] = ok ? ld_f(qb + off) : 0.f;
-        gr[t][j] = ok ? *gp : 0.f;
-      }
+      const int r = min(16 * t + 4 * grp + j, loc.len - 1);
+      const int off = r * H * D + c;
+      X.k[t][j] = ld_raw(kb + off);
+      X.q[t][j] = ld_raw(qb + off);
+      X.g[t][j] = GS ? gb[r * H] : gb[off];
+    }
+}
+// k, q (in R) and g (in gr) from the raw loads, zero past the chunk's end.
+template <typename T>
+__device__ __forceinline__ void cols_from_raw(const ColsRaw& X, const ChunkLoc& loc, int grp,
+                                              BwdRegs& R, float (&gr)[4][4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = 16 * t + 4 * grp + j < loc.len;
+      R.kh[t][j] = ok ? raw_val<T>(X.k[t][j]) : 0.f;
+      R.qh[t][j] = ok ? raw_val<T>(X.q[t][j]) : 0.f;
+      gr[t][j] = ok ? X.g[t][j] : 0.f;
     }
 }
 
@@ -1103,6 +1125,10 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 
   // ---- chunk x chunk: dP = tril(dO' W^T), dA = -tril_-1(L W^T), dB ------------
   renew();
+  // the key side's k, q, g columns, loaded while this phase runs (the chunk's
+  // rows are still in the cache; the registers are free here)
+  ColsRaw cols;
+  load_cols_raw<T, D, GS>(q, k, g, loc, H, h, c, grp, cols);
 #pragma unroll
   for (int tt = 0; tt < NTW; ++tt) {
     const int p = wave + NW * tt, rb = p >> 2, ib = p & 3;
@@ -1148,12 +1174,12 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   // (the scheduler fences between phases keep each phase's loads in it:
   // hoisted early, they would hold registers across the phases before)
   __builtin_amdgcn_sched_barrier(0);
-  // G, k^, q^ again (the chunk's k, q, g are still in the cache)
+  // G, k^, q^ again, from the loads issued before the chunk x chunk products
   renew();
   BwdRegs R;
   {
     float gr[4][4];
-    load_cols<T, D, GS>(q, k, g, loc, H, h, c, grp, R, gr);
+    cols_from_raw<T>(cols, loc, grp, R, gr);
     prefix_G(gr, lane, R);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
