@@ -79,19 +79,35 @@ namespace {
 //   frag_cm_perm  element (m, k) = X[k * ld + m], k in kpos order
 //   acc_frag      operand whose k index is the row index of four stacked
 //                 16-row accumulator tiles, in kpos order (no data movement)
+// The bf16 column fragments come from LDS transpose reads
+// (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte pieces named by lanes i / 4 + 4e, e = 0..3.  So if
+// lane j names row k0 + j / 4, columns m0 + 4 (j % 4) .. +3 of a row-major X,
+// lane i receives X[k0 .. k0+3][m0 + i]: four consecutive k of its own
+// column m, half an operand fragment (layout measured on gfx950).
+typedef short tr16_v4 __attribute__((__vector_size__(4 * sizeof(short))));
+__device__ __forceinline__ uint2 ld_tr16(const bf16* p) {
+  const tr16_v4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr16_v4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+// k0: the first of the fragment's two runs of four k; the second starts
+// `gap` rows further.
+__device__ __forceinline__ bf16x8_t frag_tr(const bf16* X, int ld, int m0, int k0, int gap,
+                                            int lane) {
+  const int j = lane & 15;
+  const bf16* p = X + (k0 + (j >> 2)) * ld + m0 + 4 * (j & 3);
+  const uint2 a = ld_tr16(p), b = ld_tr16(p + gap * ld);
+  return __builtin_bit_cast(bf16x8_t, (u32x4_t{a.x, a.y, b.x, b.y}));
+}
+
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag frag_cm(const T* X, int ld, int m0, int ks,
                                                          int lane);
 template <>
 __device__ __forceinline__ bf16x8_t frag_cm<bf16>(const bf16* X, int ld, int m0, int ks,
                                                   int lane) {
-  const uint16_t* p =
-      reinterpret_cast<const uint16_t*>(X) + (ks * 32 + 8 * (lane >> 4)) * ld + m0 + (lane & 15);
-  u32x4_t u;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    u[t] = (uint32_t)p[(2 * t) * ld] | ((uint32_t)p[(2 * t + 1) * ld] << 16);
-  return __builtin_bit_cast(bf16x8_t, u);
+  return frag_tr(X, ld, m0, ks * 32 + 8 * (lane >> 4), 4, lane);
 }
 template <>
 __device__ __forceinline__ float frag_cm<float>(const float* X, int ld, int m0, int ks, int lane) {
@@ -121,14 +137,8 @@ __device__ __forceinline__ typename Mma<T>::frag frag_cm_perm(const T* X, int ld
 template <>
 __device__ __forceinline__ bf16x8_t frag_cm_perm<bf16>(const bf16* X, int ld, int m0, int ks,
                                                        int lane) {
-  const uint16_t* p =
-      reinterpret_cast<const uint16_t*>(X) + (ks * 32 + 4 * (lane >> 4)) * ld + m0 + (lane & 15);
-  u32x4_t u;
-  u[0] = (uint32_t)p[0] | ((uint32_t)p[ld] << 16);
-  u[1] = (uint32_t)p[2 * ld] | ((uint32_t)p[3 * ld] << 16);
-  u[2] = (uint32_t)p[16 * ld] | ((uint32_t)p[17 * ld] << 16);
-  u[3] = (uint32_t)p[18 * ld] | ((uint32_t)p[19 * ld] << 16);
-  return __builtin_bit_cast(bf16x8_t, u);
+  // positions 0..3: k = 32 ks + 4 g + 0..3; 4..7: k = 32 ks + 16 + 4 g + 0..3
+  return frag_tr(X, ld, m0, ks * 32 + 4 * (lane >> 4), 16, lane);
 }
 template <>
 __device__ __forceinline__ float frag_cm_perm<float>(const float* X, int ld, int m0, int ks,
