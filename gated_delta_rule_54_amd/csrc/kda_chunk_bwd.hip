@@ -146,6 +146,17 @@ __device__ __forceinline__ float frag_cm_perm<float>(const float* X, int ld, int
   return X[(16 * (ks >> 2) + 4 * (lane >> 4) + (ks & 3)) * ld + m0 + (lane & 15)];
 }
 
+// One 16-byte piece of the MFMA type from fp32 values (8 bf16 rounded to
+// nearest even, or 4 fp32).
+__device__ __forceinline__ u32x4_t pack16(const float* x, bf16) {
+  return u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                 pack_bf16x2(x[6], x[7])};
+}
+__device__ __forceinline__ u32x4_t pack16(const float* x, float) {
+  return u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                 __float_as_uint(x[3])};
+}
+
 // Eight (bf16) or one (fp32) fp32 values to an operand fragment.
 __device__ __forceinline__ bf16x8_t to_frag(const float* x, bf16) {
   const u32x4_t u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
@@ -514,13 +525,16 @@ __device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdR
 // the gated operands in LDS (K~ left to the caller in the compact layout), A
 // and P, T = (I + A)^-1 (times Diag(beta) when TBETA) in the MFMA type.  Bm receives this wave's tiles of Kp Km^T
 // (tile p = wave + NW * tt: rows 16(p/4), columns 16(p%4)).
-template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false>
+// INV: form T here (else the caller puts T in tb before its next barrier);
+// tout (or nullptr): where T itself (without Diag(beta)) also goes, 64 x 64
+// row-major in the MFMA type.
+template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false, bool INV = true>
 __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
                                             const float* __restrict__ g,
                                             const float* __restrict__ beta, const ChunkLoc& loc,
                                             int H, int h, int qk_l2norm,
                                             BwdSmem<T, D, COMPACT>& sm, BwdRegs& R,
-                                            f32x4_t* Bm) {
+                                            f32x4_t* Bm, T* __restrict__ tout = nullptr) {
   using L = BwdLds<T, D, COMPACT>;
   using M = Mma<T>;
   constexpr int NW = L::NW, NT = L::NT, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
@@ -581,6 +595,10 @@ __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __
 #pragma unroll
     for (int j = 0; j < 4; ++j) st_f(sm.pb + (16 * rb + 4 * grp + j) * LDC + i, i <= 16 * rb + 4 * grp + j ? ap[j] : 0.f);
   }
+  if constexpr (!INV) {
+    __syncthreads();
+    return mode;
+  }
   // A from the kept Bm tiles; in the compact layout A overlays Kp and Km, so
   // every wave must be done reading them first
   if constexpr (COMPACT) __syncthreads();
@@ -600,6 +618,17 @@ __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __
     const int r = e >> 6, i = e & 63;
     const float t = i <= r ? sm.sT[r * kTriLd + i] : 0.f;
     st_f(sm.tb + r * LDC + i, TBETA ? t * sm.beta[i] : t);
+  }
+  if (tout != nullptr) {
+    // 16-byte pieces of T's rows, rounded as the tb copy above
+    constexpr int VE = 16 / (int)sizeof(T), PR = kC / VE;
+    for (int p = tid; p < kC * PR; p += NT) {
+      const int r = p / PR, i0 = VE * (p % PR);
+      float x[VE];
+#pragma unroll
+      for (int u = 0; u < VE; ++u) x[u] = i0 + u <= r ? sm.sT[r * kTriLd + i0 + u] : 0.f;
+      *reinterpret_cast<u32x4_t*>(tout + r * kC + i0) = pack16(x, T{});
+    }
   }
   __syncthreads();
   return mode;
@@ -621,7 +650,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1)
 __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, ChunkGeom gm, int H, int64_t nslot, int64_t slot_base,
-    int qk_l2norm, float scale, char* __restrict__ brec) {
+    int qk_l2norm, float scale, char* __restrict__ brec, T* __restrict__ tinv) {
   using L = BwdLds<T, D, true>;
   using M = Mma<T>;
   using RC = BRec<T, D>;
@@ -635,8 +664,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
   BwdSmem<T, D, true> sm(smem);
   BwdRegs R;
   f32x4_t Bm[NTW];
-  const int mode =
-      bwd_prologue<T, D, GS, true, true, true>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm);
+  const int mode = bwd_prologue<T, D, GS, true, true, true>(
+      q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm, tinv + (slot * H + h) * (int64_t)(kC * kC));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
   // beyond the mid reference's range: NaN records, so that the reverse pass
@@ -920,7 +949,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     const T* __restrict__ states, const T* __restrict__ dstates, ChunkGeom gm, int H,
     int64_t slot_base, int qk_l2norm, float scale, T* __restrict__ dq, T* __restrict__ dk,
     T* __restrict__ dv,
-    float* __restrict__ dg, float* __restrict__ dbeta) {
+    float* __restrict__ dg, float* __restrict__ dbeta, const T* __restrict__ tinv) {
   using L = BwdLds<T, D>;
   using M = Mma<T>;
   constexpr int NW = L::NW, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
@@ -933,10 +962,30 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
   BwdSmem<T, D> sm(smem);
   int mode;
   f32x4_t Bm[L::BM_LDS ? 1 : NTW];  // (unused when the tiles live in LDS)
+  // T = (I + A)^-1 as kda_bwd_prep formed it (the same operations on the same
+  // inputs, so the same values as forming it here), in 16-byte pieces loaded
+  // before the prologue's own loads and put in tb after the prologue
+  constexpr int TVE = 16 / (int)sizeof(T), TPR = kC / TVE, TNP = kC * TPR / L::NT;
+  static_assert(kC * TPR % L::NT == 0, "T's pieces must tile the threads");
+  u32x4_t tpc[TNP];
+  {
+    const T* tb0 = tinv + (slot * H + h) * (int64_t)(kC * kC);
+#pragma unroll
+    for (int u = 0; u < TNP; ++u) {
+      const int p = u * L::NT + threadIdx.x;
+      tpc[u] = *reinterpret_cast<const u32x4_t*>(tb0 + (p / TPR) * kC + TVE * (p % TPR));
+    }
+  }
   {
     BwdRegs R0;  // recomputed at the end rather than kept live (registers)
     f32x4_t Bp[NTW];
-    mode = bwd_prologue<T, D, GS, false, false>(q, k, g, beta, loc, H, h, qk_l2norm, sm, R0, Bp);
+    mode = bwd_prologue<T, D, GS, false, false, false, false>(q, k, g, beta, loc, H, h,
+                                                               qk_l2norm, sm, R0, Bp);
+#pragma unroll
+    for (int u = 0; u < TNP; ++u) {
+      const int p = u * L::NT + threadIdx.x;
+      *reinterpret_cast<u32x4_t*>(sm.tb + (p / TPR) * L::LDC + TVE * (p % TPR)) = tpc[u];
+    }
     if constexpr (!L::BM_LDS) {
 #pragma unroll
       for (int tt = 0; tt < NTW; ++tt) Bm[tt] = Bp[tt];
@@ -1443,11 +1492,12 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 
 // ---------------------------------------------------------------------------
 // Workspace: [forward workspace | S per slot | dS' per slot | M, Z^T records |
-// chunk map].  Slots are sized for the larger of the dense and varlen bounds.
+// T per (slot, head) | chunk map].  Slots are sized for the larger of the
+// dense and varlen bounds.
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdPlan {
-  int64_t slots, fwd, states, recs, map, total;
+  int64_t slots, fwd, states, recs, tinv, map, total;
 };
 
 BwdPlan bwd_plan(const kda_desc_t& d) {
@@ -1463,8 +1513,9 @@ BwdPlan bwd_plan(const kda_desc_t& d) {
                          ? (d.dk == 128 ? BRec<bf16, 128>::BYTES : BRec<bf16, 64>::BYTES)
                          : (d.dk == 128 ? BRec<float, 128>::BYTES : BRec<float, 64>::BYTES);
   p.recs = p.slots * d.heads * rb;
+  p.tinv = align256(p.slots * d.heads * (int64_t)kC * kC * (d.dtype == KDA_DTYPE_BF16 ? 2 : 4));
   p.map = 2 * align256(((int64_t)d.num_seqs + 1) * 4);
-  p.total = p.fwd + 2 * p.states + p.recs + p.map;
+  p.total = p.fwd + 2 * p.states + p.recs + p.tinv + p.map;
   return p;
 }
 
@@ -1480,7 +1531,8 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   T* states = reinterpret_cast<T*>(ws + p.fwd);
   T* dstates = reinterpret_cast<T*>(ws + p.fwd + p.states);
   char* recs = ws + p.fwd + 2 * p.states;
-  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.fwd + 2 * p.states + p.recs);
+  T* tinv = reinterpret_cast<T*>(ws + p.fwd + 2 * p.states + p.recs);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.fwd + 2 * p.states + p.recs + p.tinv);
   int32_t* cu_s = chunk_off + (p.map / 2) / 4;
   const int64_t nslot = chunk_slot_bound(d, varlen);
 
@@ -1517,7 +1569,8 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   for (int64_t sb = 0; sb < nslot; sb += kMaxGridY) {
     const unsigned ny = (unsigned)std::min<int64_t>(kMaxGridY, nslot - sb);
     hipLaunchKernelGGL(prep, dim3(H, ny), dim3(LP::NT), LP::BYTES, stream, (const T*)q,
-                       (const T*)k, g, beta, gm, H, nslot, sb, d.qk_l2norm, d.scale, recs);
+                       (const T*)k, g, beta, gm, H, nslot, sb, d.qk_l2norm, d.scale, recs,
+                       tinv);
   }
   const int nslice = D / kBwdSliceW;
   const int nhpad = (NH + 7) / 8 * 8;
@@ -1529,7 +1582,7 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
     const unsigned ny = (unsigned)std::min<int64_t>(kMaxGridY, nslot - sb);
     hipLaunchKernelGGL(intra, dim3(H, ny), dim3(L::NT), L::BYTES, stream, (const T*)q,
                        (const T*)k, (const T*)v, g, beta, (const T*)d_o, states, dstates, gm, H,
-                       sb, d.qk_l2norm, d.scale, (T*)dq, (T*)dk, (T*)dv, dg, dbeta);
+                       sb, d.qk_l2norm, d.scale, (T*)dq, (T*)dk, (T*)dv, dg, dbeta, tinv);
   }
   return hipGetLastError();
 }
