@@ -247,13 +247,18 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp_f<0xb1>(x);   // quad_perm [1, 0, 3, 2]
-  x += dpp_f<0x4e>(x);   // quad_perm [2, 3, 0, 1]
-  x += dpp_f<0x141>(x);  // row_half_mirror
-  x += dpp_f<0x140>(x);  // row_mirror
+// The sum over aligned groups of N lanes (N = 1, 2, 4, 8, 16), every lane of
+// a group receiving it.
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "DPP row groups only");
+  if constexpr (N >= 2) x += dpp_f<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) x += dpp_f<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp_f<0x140>(x); // row_mirror
   return x;
 }
+__device__ __forceinline__ float sum16(float x) { return sum_lanes<16>(x); }
 
 // ---------------------------------------------------------------------------
 // LDS of the per-chunk backward kernels (bytes).  kda_bwd_intra (COMPACT =
@@ -472,11 +477,8 @@ __device__ __forceinline__ void stage_rows(const T* q, const T* k, const float* 
         b += y * y;
       }
     }
-#pragma unroll
-    for (int o = PR / 2; o >= 1; o >>= 1) {
-      a += __shfl_xor(a, o);
-      b += __shfl_xor(b, o);
-    }
+    a = sum_lanes<PR>(a);  // every thread is active here
+    b = sum_lanes<PR>(b);
     if (cp == 0) {
       rk[row] = qk_l2norm ? rsqrtf(a + kNormEps) : 1.f;
       rq[row] = qk_l2norm ? rsqrtf(b + kNormEps) : 1.f;
