@@ -260,6 +260,43 @@ __device__ __forceinline__ float sum_lanes(float x) {
 }
 __device__ __forceinline__ float sum16(float x) { return sum_lanes<16>(x); }
 
+// Exchanges between the four 16-lane groups (rows) of a wave, on the VALU:
+// permlane16_swap(x, x) returns rows (x0, x0, x2, x2) and (x1, x1, x3, x3),
+// permlane32_swap(x, x) returns (x0, x1, x0, x1) and (x2, x3, x2, x3)
+// (measured on gfx950), so each lane reaches the same lane of row g ^ 1 or
+// g ^ 2 in one instruction.
+__device__ __forceinline__ float row_xor1(float x, int grp) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((grp & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float row_xor2(float x, int grp) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((grp & 2) ? r[0] : r[1]);
+}
+// Row 3's value of this lane's column, in every row.
+__device__ __forceinline__ float row3_bcast(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const auto b = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+  return __uint_as_float(b[1]);
+}
+// Prefix (rows 0..g) and suffix (rows g..3) sums over the rows of each
+// column, and the column's total.
+__device__ __forceinline__ float rows_prefix(float x, int grp, float& total) {
+  const float pair = x + row_xor1(x, grp);
+  const float other = row_xor2(pair, grp);
+  total = pair + other;
+  return ((grp & 1) ? pair : x) + ((grp & 2) ? other : 0.f);
+}
+__device__ __forceinline__ float rows_suffix(float x, int grp, float& total) {
+  const float pair = x + row_xor1(x, grp);
+  const float other = row_xor2(pair, grp);
+  total = pair + other;
+  return ((grp & 1) ? x : pair) + ((grp & 2) ? 0.f : other);
+}
+
 // ---------------------------------------------------------------------------
 // LDS of the per-chunk backward kernels (bytes).  kda_bwd_intra (COMPACT =
 // false) keeps every operand for the whole kernel; kda_bwd_prep (COMPACT)
@@ -348,7 +385,8 @@ struct BwdRegs {
 enum BwdMode { kBwdFast = 0, kBwdMid = 1, kBwdBeyond = 2 };
 // G of row 31 of this lane's column (the lanes of lane group 3 hold it)
 __device__ __forceinline__ float g_row31(const BwdRegs& R, int lane) {
-  return __shfl(R.G[1][3], 48 + (lane & 15));
+  (void)lane;
+  return row3_bcast(R.G[1][3]);
 }
 __device__ __forceinline__ int bwd_mode(const BwdRegs& R, int lane) {
   if (__syncthreads_or(R.gam < kFastDecayBound) == 0) return kBwdFast;
@@ -509,13 +547,8 @@ __device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdR
     float run = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) { run += gr[t][j]; loc4[j] = run; }
-    float x = run;
-    float y = __shfl_up(x, 16);
-    if (grp >= 1) x += y;
-    y = __shfl_up(x, 32);
-    if (grp >= 2) x += y;
-    const float excl = x - run;
-    const float total = __shfl(x, 48 + (lane & 15));
+    float total;
+    const float excl = rows_prefix(run, grp, total) - run;
 #pragma unroll
     for (int j = 0; j < 4; ++j) R.G[t][j] = carry + excl + loc4[j];
     carry += total;
@@ -1364,10 +1397,10 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       }
     }
   }
-  rs += __shfl_xor(rs, 16);
-  rs += __shfl_xor(rs, 32);
-  dgam += __shfl_xor(dgam, 16);
-  dgam += __shfl_xor(dgam, 32);
+  rs += row_xor1(rs, grp);
+  rs += row_xor2(rs, grp);
+  dgam += row_xor1(dgam, grp);
+  dgam += row_xor2(dgam, grp);
   dgam += __expf(R.gam) * rs;
   if (grp == 3) dG[3][3] += dgam;  // gamma = G of row 63
   // dg_r = sum_(s >= r) dG_s: within the lane's 4 rows, across the lane
@@ -1381,13 +1414,8 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
       float run = 0.f;
 #pragma unroll
       for (int j = 3; j >= 0; --j) { run += dG[t][j]; suf[j] = run; }
-      float x = run;
-      float y = __shfl_down(x, 16);
-      if (grp <= 2) x += y;
-      y = __shfl_down(x, 32);
-      if (grp <= 1) x += y;
-      const float excl = x - run;
-      const float total = __shfl(x, lane & 15);
+      float total;
+      const float excl = rows_suffix(run, grp, total) - run;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dgo[t][j] = carry + excl + suf[j];
       carry += total;
