@@ -336,6 +336,9 @@ KDA_EXPORT kda_status_t kda_short_conv_swish(int32_t batch, int64_t seqlen, int3
   if (channels < 1 || channels % (16 / el) != 0)
     return fail(KDA_ERR_UNSUPPORTED, "channels must be a positive multiple of %d (got %d)",
                 16 / el, channels);
+  if ((int64_t)channels * el > KDA_CONV_MAX_ROW_BYTES)
+    return fail(KDA_ERR_UNSUPPORTED, "channels must be at most %d at this dtype (got %d)",
+                (int)(KDA_CONV_MAX_ROW_BYTES / el), channels);
   if (batch < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
   if (seqlen < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
   if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");

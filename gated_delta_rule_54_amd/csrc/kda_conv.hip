@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
+#include <algorithm>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -77,21 +79,28 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int N, int64_t t) {
   return lo;
 }
 
+// One workgroup per (token block, 64 channel groups): the token block is
+// blockIdx.y, uniform over the workgroup, so each row's address is a scalar
+// base plus the lane's channel offset -- no per-element address arithmetic
+// -- and the 32-token loop is unrolled whole, so the window of the previous
+// W-1 inputs lives in renamed registers instead of being shifted.  (The same thread -> memory mapping copies at ~6 TB/s without
+// arithmetic; the kernel had been bound by its address, window and branch
+// instructions on top of the convolution itself.)
 template <typename T, int W>
 __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
     const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     const float* state_in, const int32_t* __restrict__ cu, T* __restrict__ y, float* state_out,
-    int64_t T_, int N, int C, int64_t nblocks_tok) {
+    int64_t T_, int N, int C, int64_t nblocks_tok, int64_t tb_base) {
   using V = CVec<T>;
   constexpr int E = V::E, HW = W - 1;
   const int CG = C / E;  // channel groups per token row
-  const int64_t gid = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
-  const int64_t ntok_threads = nblocks_tok * CG;
-  if (gid >= ntok_threads) {
-    // empty sequences: carried-out state = carried-in state (or zeros)
-    const int64_t e = gid - ntok_threads;
-    if (state_out == nullptr || e >= (int64_t)N * CG) return;
-    const int n = (int)(e / CG), cg = (int)(e % CG);
+  const int cg = blockIdx.x * kConvThreads + threadIdx.x;
+  if (cg >= CG) return;
+  const int64_t tb = tb_base + blockIdx.y;  // token block, or past them: a sequence
+  if (tb >= nblocks_tok) {
+    // rows past the token blocks (launched only with state_out): empty
+    // sequences carry their state out unchanged (or zeros)
+    const int n = (int)(tb - nblocks_tok);
     const int64_t len = cu ? (int64_t)cu[n + 1] - cu[n] : T_;
     if (len > 0) return;
     for (int k = 0; k < E * HW; ++k) {
@@ -100,16 +109,14 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
     }
     return;
   }
-  const int cg = (int)(gid % CG);
-  const int64_t tb = gid / CG;  // token block
   // dense: sequence b = tb / blocks_per_seq; varlen: packed tokens
-  int64_t seq_base, tok0, tok1;  // row of the sequence's token 0; this block's rows
+  int64_t tok0, tok1;      // this block's rows
   int n;
   int64_t s_start, s_end;  // current sequence's rows [s_start, s_end)
   if (cu == nullptr) {
     const int64_t bps = (T_ + kTB - 1) / kTB;
     n = (int)(tb / bps);
-    seq_base = (int64_t)n * T_;
+    const int64_t seq_base = (int64_t)n * T_;
     tok0 = seq_base + (tb % bps) * kTB;
     tok1 = min(tok0 + kTB, seq_base + T_);
     s_start = seq_base;
@@ -158,8 +165,58 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
     }
   };
   seed(tok0);
-  // Tokens in groups of kGroup: the group's rows are loaded first (clamped to
-  // the block, so every load is unconditional), then processed in order.
+  // one token: y_t from x_t and the window, then the window moves on
+  auto token = [&](const u32x4c_t& xraw, float* out) {
+    float xv[E];
+    V::unpack(xraw, xv);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float acc = bv[e] + wv[e][W - 1] * xv[e];
+#pragma unroll
+      for (int j = 0; j < HW; ++j) acc += wv[e][j] * win[e][j];
+      // swish: a * sigmoid(a), the reciprocal in one hardware instruction
+      out[e] = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
+      if constexpr (HW > 0) {
+#pragma unroll
+        for (int j = 0; j + 1 < HW; ++j) win[e][j] = win[e][j + 1];
+        win[e][HW - 1] = xv[e];
+      }
+    }
+  };
+  auto carry_out = [&]() {
+    if (state_out == nullptr) return;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < HW; ++j) state_out[((int64_t)n * C + c0 + e) * HW + j] = win[e][j];
+  };
+  if (tok1 - tok0 == kTB && s_end >= tok1) {
+    // a whole block inside one sequence (every block of a dense batch): each
+    // row through a pointer uniform over the workgroup (a scalar base) and
+    // the lane's channel offset, and the loop unrolled whole so the window
+    // stays in renamed registers.  (Global, not buffer, stores: a buffer
+    // store with a register soffset is not given the wait state that a VALU
+    // write of its data registers right after it needs, and its first data
+    // dword was seen to take the new value.)
+#pragma unroll
+    for (int g0 = 0; g0 < kTB; g0 += kGroup) {
+      u32x4c_t xr[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k)
+        xr[k] = *reinterpret_cast<const u32x4c_t*>(x + (tok0 + g0 + k) * C + c0);
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        float out[E];
+        token(xr[k], out);
+        *reinterpret_cast<u32x4c_t*>(y + (tok0 + g0 + k) * C + c0) = V::pack(out);
+      }
+    }
+    if (tok1 == s_end) carry_out();
+    return;
+  }
+  // A block that ends early or holds a sequence start (varlen): tokens in
+  // groups of kGroup, the group's rows loaded first (clamped to the block, so
+  // every load is unconditional), then processed in order.
   for (int64_t tg = tok0; tg < tok1; tg += kGroup) {
     u32x4c_t xr[kGroup];
 #pragma unroll
@@ -177,29 +234,10 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
         s_end = max(min((int64_t)cu[n + 1], T_), t + 1);
         seed(t);
       }
-      float xv[E], out[E];
-      V::unpack(xr[k], xv);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float acc = bv[e] + wv[e][W - 1] * xv[e];
-#pragma unroll
-        for (int j = 0; j < HW; ++j) acc += wv[e][j] * win[e][j];
-        // swish: a * sigmoid(a), the reciprocal in one hardware instruction
-        out[e] = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
-        if constexpr (HW > 0) {
-#pragma unroll
-          for (int j = 0; j + 1 < HW; ++j) win[e][j] = win[e][j + 1];
-          win[e][HW - 1] = xv[e];
-        }
-      }
+      float out[E];
+      token(xr[k], out);
       *reinterpret_cast<u32x4c_t*>(y + t * C + c0) = V::pack(out);
-      if (t + 1 == s_end && state_out != nullptr) {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-#pragma unroll
-          for (int j = 0; j < HW; ++j)
-            state_out[((int64_t)n * C + c0 + e) * HW + j] = win[e][j];
-      }
+      if (t + 1 == s_end) carry_out();
     }
   }
 }
@@ -209,13 +247,18 @@ hipError_t launch_w(const kda_conv_args& a, hipStream_t stream) {
   const int CG = a.channels / CVec<T>::E;
   const int64_t nblocks_tok = a.cu ? (a.seqlen + kTB - 1) / kTB
                                    : (int64_t)a.batch * ((a.seqlen + kTB - 1) / kTB);
-  const int64_t threads = nblocks_tok * CG + (int64_t)a.num_seqs * CG;
-  const int64_t blocks = (threads + kConvThreads - 1) / kConvThreads;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((short_conv_kernel<T, W>), dim3((unsigned)blocks), dim3(kConvThreads), 0,
-                     stream, static_cast<const T*>(a.x), a.w, a.bias, a.state_in, a.cu,
-                     static_cast<T*>(a.y), a.state_out, a.seqlen, a.num_seqs, a.channels,
-                     nblocks_tok);
+  const unsigned gx = (unsigned)((CG + kConvThreads - 1) / kConvThreads);
+  // token blocks, then one row per sequence for the empty sequences' states,
+  // in the grid's y dimension, at most kMaxY rows per launch
+  const int64_t rows = nblocks_tok + (a.state_out != nullptr ? a.num_seqs : 0);
+  constexpr int64_t kMaxY = 32768;
+  for (int64_t b0 = 0; b0 < rows; b0 += kMaxY) {
+    const unsigned gy = (unsigned)std::min<int64_t>(kMaxY, rows - b0);
+    hipLaunchKernelGGL((short_conv_kernel<T, W>), dim3(gx, gy), dim3(kConvThreads), 0, stream,
+                       static_cast<const T*>(a.x), a.w, a.bias, a.state_in, a.cu,
+                       static_cast<T*>(a.y), a.state_out, a.seqlen, a.num_seqs, a.channels,
+                       nblocks_tok, b0);
+  }
   return hipGetLastError();
 }
 

@@ -137,6 +137,10 @@ kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, const void* k,
 /* Scratch (bytes, per device) that kda_chunk_fwd_noalloc holds. */
 #define KDA_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
+/* Largest token row of kda_short_conv_swish, in bytes (channels x element
+ * size): 8,388,608 fp32 or 16,777,216 bf16 channels. */
+#define KDA_CONV_MAX_ROW_BYTES (1 << 25)
+
 /* kda_chunk_fwd for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * It takes no workspace and allocates nothing: its scratch (chunk records,
@@ -230,8 +234,9 @@ kda_status_t kda_decode_step(const kda_desc_t* desc, const void* q, const void* 
  *   batch, seqlen, num_seqs  as in kda_desc_t: x, y are [B, T, C]; varlen
  *              (cu_seqlens != NULL) needs batch == 1, dense needs
  *              num_seqs == batch
- *   channels   C >= 1, a multiple of 8 (bf16) or 4 (fp32); for q/k/v of H
- *              heads, C = H * d
+ *   channels   C >= 1, a multiple of 8 (bf16) or 4 (fp32), and at most
+ *              KDA_CONV_MAX_ROW_BYTES / element size (a token row's bytes fit
+ *              the kernel's 32-bit offsets); for q/k/v of H heads, C = H * d
  *   width      1 ... 4 (the pages give none; 4 in every workload)
  *   dtype      element type of x and y
  *   x, y       device, 16-byte aligned; y must not overlap x

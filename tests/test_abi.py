@@ -171,6 +171,9 @@ def test_short_conv_errors():
     assert call(width=0) == B.KDA_ERR_UNSUPPORTED
     assert call(width=5) == B.KDA_ERR_UNSUPPORTED
     assert call(channels=12) == B.KDA_ERR_UNSUPPORTED          # bf16 needs a multiple of 8
+    # a token row may hold at most 2^25 bytes (the kernel's 32-bit offsets)
+    assert call(channels=(1 << 24) + 8, seqlen=1) == B.KDA_ERR_UNSUPPORTED
+    assert call(channels=(1 << 23) + 4, seqlen=1, dtype=0) == B.KDA_ERR_UNSUPPORTED
     assert call(batch=0) == B.KDA_ERR_INVALID_ARGUMENT
     assert call(seqlen=-1) == B.KDA_ERR_INVALID_ARGUMENT
     assert call(num_seqs=2) == B.KDA_ERR_INVALID_ARGUMENT      # dense: num_seqs == batch
