@@ -304,6 +304,73 @@ def write_counters(csvs, out: str = COUNTER_FILE, command: str = "") -> str:
     return text
 
 
+KERNEL_STATS_FILE = os.path.join(ROOT, "profiles", "kda_prefill_8k_decode_256x32_kernel_stats.md")
+# (kernel-name fragment, template arguments shown, workload, from the trace?)
+_STATS_ROWS = (
+    ("kda_intra_chunk<__hip_bfloat16, 128, false, true>", "kda_intra_chunk<bf16, 128, false, true>",
+     "prefill 8K, 20 timed calls (trace)", True),
+    ("kda_state_pass<__hip_bfloat16, 128, 16, true>", "kda_state_pass<bf16, 128, 16, true>",
+     "prefill 8K, 20 timed calls (trace)", True),
+    ("decode_step_kernel<__hip_bfloat16, 128>", "decode_step_kernel<bf16, 128>", "decode (stats)", False),
+    ("gate_norm_kernel<__hip_bfloat16, 128>", "gate_norm_kernel<bf16, 128>", "epilogue (stats)", False),
+    ("short_conv_kernel<__hip_bfloat16, 4>", "short_conv_kernel<bf16, 4>", "prologue (stats)", False),
+    ("kda_intra_chunk<__hip_bfloat16, 128, false, false>", "kda_intra_chunk<bf16, 128, false, false>",
+     "backward's forward, per segment (stats)", False),
+    ("kda_state_pass<__hip_bfloat16, 128, 16, false>", "kda_state_pass<bf16, 128, 16, false>",
+     "backward's forward, per segment (stats)", False),
+    ("kda_bwd_prep<__hip_bfloat16, 128, false>", "kda_bwd_prep<bf16, 128, false>", "backward (stats)", False),
+    ("kda_bwd_state_pass<__hip_bfloat16, 128>", "kda_bwd_state_pass<bf16, 128>", "backward (stats)", False),
+    ("kda_bwd_intra<__hip_bfloat16, 128, false>", "kda_bwd_intra<bf16, 128, false>", "backward (stats)", False),
+)
+
+
+def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_FILE,
+                       warmup: int = 50, steps: int = 20) -> str:
+    """Kernel durations from `rocprofv3 --kernel-trace --stats --output-format
+    csv -- python3 bench.py --no-cpu-baseline`: the prefill kernels from the
+    trace (the dispatches of the timed calls: 2 segments per call, after
+    `warmup` warm-up calls), everything else pooled from the stats file."""
+    import csv
+    trace = list(csv.DictReader(open(trace_csv)))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    stats = {r["Name"]: r for r in csv.DictReader(open(stats_csv))}
+
+    def short(name):
+        return name.replace("void kda::(anonymous namespace)::", "").split("(")[0]
+
+    lines = ["# rocprofv3 kernel stats: prefill 8K x 32 heads, decode 256 x 32 heads, "
+             "epilogue, prologue, backward", "",
+             "Command (run from the repository root on one MI355X), then the summary:", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench "
+             "-o bench -- python3 bench.py --no-cpu-baseline",
+             "    python3 bench.py --write-kernel-stats gpurun_out/prof_bench/bench_kernel_trace.csv "
+             "gpurun_out/prof_bench/bench_kernel_stats.csv", "",
+             f"Kernel durations (ns). Prefill rows: the dispatches of the {steps} timed calls "
+             f"(after {warmup} warm-up calls, two segments per call) from the trace; the other "
+             "rows pool every call of the kernel in the run (stats file).", "",
+             "| Kernel | Workload | Calls | Average | Min | Max |", "|---|---|---|---|---|---|"]
+    for frag, label, workload, from_trace in _STATS_ROWS:
+        if from_trace:
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                 for r in trace if short(r["Kernel_Name"]) == frag]
+            d = d[2 * warmup: 2 * (warmup + steps)]
+            if not d:
+                continue
+            lines.append(f"| `{label}` | {workload} | {len(d)} | {sum(d) / len(d):,.0f} | "
+                         f"{min(d):,} | {max(d):,} |")
+        else:
+            r = next((v for k, v in stats.items() if short(k) == frag), None)
+            if r is None:
+                continue
+            lines.append(f"| `{label}` | {workload} | {int(r['Calls'])} | "
+                         f"{float(r['AverageNs']):,.0f} | {int(float(r['MinNs'])):,} | "
+                         f"{int(float(r['MaxNs'])):,} |")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def epilogue_inputs():
     """Synthetic epilogue operands at the prefill output's size."""
     gen = torch.Generator(device="cuda").manual_seed(1005)
@@ -760,6 +827,9 @@ def main():
     ap.add_argument("--write-counters", nargs="+", metavar="PASS_CSV",
                     help="write the compute-counter summary from the passes of "
                          "COUNTER_PASSES over --probe")
+    ap.add_argument("--write-kernel-stats", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
+                    help="write the kernel-duration summary from a kernel-trace run of this "
+                         "benchmark")
     ap.add_argument("--counter-command", default="",
                     help="the commands that made the passes, quoted in the summary")
     args = ap.parse_args()
@@ -769,6 +839,9 @@ def main():
         return
     if args.write_counters:
         print(write_counters(args.write_counters, command=args.counter_command))
+        return
+    if args.write_kernel_stats:
+        print(write_kernel_stats(*args.write_kernel_stats, warmup=args.warmup, steps=args.steps))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are "
@@ -781,19 +854,28 @@ def main():
     if args.probe:
         probe()
         return
+    def progress(what):  # one stderr line per finished section
+        print(f"[bench] {what} done", file=sys.stderr, flush=True)
+
     pf = bench_prefill(args.steps, args.warmup)
+    progress("prefill")
     pf_cold_ms = bench_prefill_flushed(pf["inp"], args.steps)
     inputs_sha = {"prefill_8k": {k: _tensor_sha256(pf["inp"][k])
                                  for k in ("q", "k", "v", "g", "beta")}}
     tr_prefill, tr_decode, tr_epi, tr_pro, tr_bwd = measured_traffic()
     dc = bench_decode(min(args.warmup, 8))
+    progress("decode")
     ep = bench_epilogue(args.steps, args.warmup)
     gm = bench_gate_modes()
     pl = bench_prologue(args.steps, args.warmup)
+    progress("epilogue, gate modes, prologue")
     bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 2))
+    progress("backward")
     vl, inputs_sha["varlen"] = bench_varlen(max(1, args.steps // 2), 2)
     m1, inputs_sha["prefill_1m_first_65536_tokens"] = bench_prefill_1m()
+    progress("varlen, 1M tokens")
     sg = bench_strong_gates(max(2, args.steps // 2), 3)
+    progress("strong gates")
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
     line = {
@@ -876,6 +958,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf["inp"], args.cpu_heads)
+        progress("cpu baseline")
     line["reproducibility"] = reproducibility(inputs_sha)
     print(json.dumps(line), flush=True)
 
