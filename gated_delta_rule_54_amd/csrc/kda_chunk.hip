@@ -883,16 +883,6 @@ template <typename T> constexpr int k2_threads() {
   return k2_dma<T>() ? kThreads + 64 * kK2Producers : kThreads;
 }
 
-__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
-                                           uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
-}
-// s_waitcnt operand that waits until at most n vector-memory operations of
-// this wave are outstanding (vmcnt is 6 bits: low 4 at [3:0], high 2 at
-// [15:14]) and leaves expcnt and lgkmcnt alone.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 template <typename T, int D, int WS, bool OUT>
 struct K2Frags {
   using M = Mma<T>;
@@ -1000,21 +990,6 @@ struct K2Frags {
     }
   }
 };
-
-// Workgroup barrier for the state pass.  __syncthreads() carries a workgroup
-// release fence, which in a producer wave must also wait for every
-// LDS-direct load in flight (they write LDS) and would drain its prefetch;
-// here each wave waits only for its own LDS reads and writes (lgkmcnt), the
-// hardware barrier follows, and the empty asm statements keep the compiler
-// from moving LDS accesses across it.  A producer wave waits for the loads
-// the compute waves are about to read with an explicit vmcnt before the
-// barrier (see kda_state_pass).
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left as they are
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
 
 // OUT = false (the forward run inside the backward): no output, so neither
 // Q o e^G nor P is loaded and O is not formed.

@@ -762,12 +762,18 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
 
 // ---------------------------------------------------------------------------
 // Reverse state pass: dS = M dS' + (scale Z)^T dO chunk by chunk from the last, one
-// workgroup per (sequence, head, 16 columns of d_v).  Wave w owns rows
+// workgroup per (sequence, head, 16 columns of d_v).  Compute wave w owns rows
 // [16 CBW w, 16 CBW (w+1)) of dS in accumulators; dS' crosses LDS once per
 // chunk (double-buffered, so one barrier per chunk).  Each chunk's dS' (the
-// gradient of the state leaving it) goes to dstates for kda_bwd_intra.
+// gradient of the state leaving it) goes to dstates for kda_bwd_intra.  M,
+// two thirds of a chunk's record, comes into a ring of three LDS buffers by
+// LDS-direct loads of two producer waves, two chunks ahead; scale Z^T and
+// the dO slice stay on the compute waves' VGPR path, so the two paths feed
+// the CU together.
 constexpr int kBwdSliceW = 16;
-constexpr int kBwdPassThreads = 256;
+constexpr int kBwdPassCompute = 256;  // compute threads (four waves)
+constexpr int kBwdProducers = 2;
+constexpr int kBwdPassThreads = kBwdPassCompute + 64 * kBwdProducers;
 
 template <typename T, int D>
 struct BwdPassFrags {
@@ -776,9 +782,26 @@ struct BwdPassFrags {
   // dO slice of the chunk (64 rows x 16 columns): 16 bytes per lane, VE
   // elements of one row; NO lanes hold the slice, the rest read nothing
   static constexpr int VE = 16 / (int)sizeof(T), LPR = kBwdSliceW / VE, NO = kC * LPR;
-  static_assert(NO <= kBwdPassThreads, "the dO slice must fit one load per lane");
-  typename M::frag mf[CBW][KD], zf[CBW][KC];
+  static_assert(NO <= kBwdPassCompute, "the dO slice must fit one load per lane");
+  typename M::frag zf[CBW][KC];
   u32x4_t dov;  // raw dO bits of row tid / LPR, columns VE (tid % LPR) ..
+};
+
+// LDS of the reverse pass (bytes): the M ring, then the exchange buffers.
+template <typename T, int D>
+struct BwdPassLds {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int LDS_S = D + 8;                                    // dS' exchange row
+  static constexpr int LDO = kC + 16 / ES, LDF = kBwdSliceW + 16 / ES;  // dO^T, dS' store rows
+  static constexpr int MB = D * D * ES;                                  // M of one chunk
+  static constexpr int NBUF = 3;  // two chunks ahead (the step loop assumes 3)
+  static constexpr int SD = NBUF * MB;
+  static constexpr int SO = SD + 2 * kBwdSliceW * LDS_S * ES;
+  static constexpr int SF = SO + 2 * kBwdSliceW * LDO * ES;
+  static constexpr int BYTES = SF + 2 * D * LDF * ES;
+  static constexpr int PER_PRODUCER = MB / 1024 / kBwdProducers;  // 1 KiB loads per chunk
+  static_assert(MB % (1024 * kBwdProducers) == 0, "M splits into whole 1 KiB loads per producer");
+  static_assert(BYTES <= 160 * 1024, "reverse-pass LDS exceeds a CU");
 };
 
 template <typename T, int D>
@@ -789,14 +812,17 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   using M = Mma<T>;
   using RC = BRec<T, D>;
   using F = BwdPassFrags<T, D>;
-  constexpr int CBW = F::CBW, KD = F::KD, KC = F::KC, LDS_S = D + 8;
+  using PL = BwdPassLds<T, D>;
+  constexpr int CBW = F::CBW, KD = F::KD, KC = F::KC, LDS_S = PL::LDS_S;
   constexpr int VE = F::VE, LPR = F::LPR, NO = F::NO;
   // per chunk, double-buffered: dS' in the MFMA type (the exchange), dO^T
   // (columns n, rows r), and dS' untransposed for the store to dstates
-  constexpr int LDO = kC + 16 / (int)sizeof(T), LDF = kBwdSliceW + 16 / (int)sizeof(T);
-  __shared__ __align__(16) T sD[2][kBwdSliceW * LDS_S];
-  __shared__ __align__(16) T sO[2][kBwdSliceW * LDO];
-  __shared__ __align__(16) T sF[2][D * LDF];
+  constexpr int LDO = PL::LDO, LDF = PL::LDF;
+  extern __shared__ __align__(16) char smem[];
+  char* mring = smem;
+  T (*sD)[kBwdSliceW * LDS_S] = reinterpret_cast<T (*)[kBwdSliceW * LDS_S]>(smem + PL::SD);
+  T (*sO)[kBwdSliceW * LDO] = reinterpret_cast<T (*)[kBwdSliceW * LDO]>(smem + PL::SO);
+  T (*sF)[D * LDF] = reinterpret_cast<T (*)[D * LDF]>(smem + PL::SF);
   const int id = blockIdx.x;
   const int nh = (id & 7) + 8 * (id / (8 * nslice));
   const int slice = (id >> 3) % nslice;
@@ -814,6 +840,41 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     }
     return;
   }
+  const int nch = (int)(sp.c1 - sp.c0);
+  const int len_last = (int)(sp.ntok - (int64_t)(nch - 1) * kC);
+  auto rec_of = [&](int ci) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(brec + ((int64_t)h * nslot + sp.c0 + ci) * RC::BYTES), (short)0, (int)RC::BYTES,
+        kRsrcWord3);
+  };
+  if (wave >= kBwdPassCompute / 64) {
+    // Producer waves: LDS-direct loads of the M block of the chunk of step st
+    // (steps run from the last chunk; clamped at the first, so the tail's
+    // loads stay inside the sequence) into ring buffer st % 3, two steps
+    // ahead.  A producer issues nothing else, so its vmcnt counts exactly
+    // these loads: before step st's barrier it waits until only step
+    // st + 1's are in flight, and after it -- by which the compute waves have
+    // finished reading step st - 1's buffer -- it refills that buffer.
+    const int pw = wave - kBwdPassCompute / 64;
+    auto produce = [&](int st) {
+      const __amdgpu_buffer_rsrc_t rr = rec_of(max(nch - 1 - st, 0));
+      char* b = mring + (st % PL::NBUF) * PL::MB;
+#pragma unroll
+      for (int t = 0; t < PL::PER_PRODUCER; ++t) {
+        const int f = pw + t * kBwdProducers;  // 1 KiB block of M
+        dma_load16(rr, b + f * 1024, (uint32_t)(RC::MF * sizeof(T) + f * 1024 + lane * 16), 0);
+      }
+    };
+    produce(0);
+    produce(1);
+    for (int st = 0; st < nch; ++st) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PL::PER_PRODUCER));
+      lds_barrier();
+      produce(st + 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
   f32x4_t dS[CBW];
 #pragma unroll
   for (int i = 0; i < CBW; ++i)
@@ -822,25 +883,12 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
       const int c = (wave * CBW + i) * 16 + 4 * grp + j;
       dS[i][j] = dfinal ? dfinal[sidx + (int64_t)c * D + n] : 0.f;
     }
-  const int nch = (int)(sp.c1 - sp.c0);
-  const int len_last = (int)(sp.ntok - (int64_t)(nch - 1) * kC);
 
   // Record fragments through a buffer resource rebased at each chunk's
   // record (scalar), a per-lane offset computed once, and the fragment's
   // offset as a scalar constant: no per-load address math.
   constexpr uint32_t FBY = 64 * M::KPL * sizeof(T);  // bytes of one fragment
-  const uint32_t lo_m = (uint32_t)((wave * CBW * KD * 64 + lane) * M::KPL * sizeof(T));
   const uint32_t lo_z = (uint32_t)((wave * CBW * KC * 64 + lane) * M::KPL * sizeof(T));
-  auto rec_of = [&](int ci) {
-    return __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(brec + ((int64_t)h * nslot + sp.c0 + ci) * RC::BYTES), (short)0, (int)RC::BYTES,
-        kRsrcWord3);
-  };
-  auto load_m = [&](F& f, __amdgpu_buffer_rsrc_t r, int i) {
-#pragma unroll
-    for (int ks = 0; ks < KD; ++ks)
-      f.mf[i][ks] = BufFrag<T>::load(r, lo_m, (uint32_t)(RC::MF * sizeof(T)) + (i * KD + ks) * FBY);
-  };
   auto load_z = [&](F& f, __amdgpu_buffer_rsrc_t r, int ci) {
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
@@ -860,12 +908,7 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
                                   : kPastBound;
     f.dov = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
   };
-  auto load = [&](F& f, int ci) {
-    const __amdgpu_buffer_rsrc_t r = rec_of(ci);
-#pragma unroll
-    for (int i = 0; i < CBW; ++i) load_m(f, r, i);
-    load_z(f, r, ci);
-  };
+  auto load = [&](F& f, int ci) { load_z(f, rec_of(ci), ci); };
   // One chunk step: consumes the fragments in f and fills fn with those of
   // chunk cn, the loads spread over the step (a wave issuing a whole record
   // at once stalls behind the CU's vector memory queue).  dS on entry is dS'
@@ -874,9 +917,10 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   // (kda_bwd_intra reads it only as an operand of that type and in one fp32
   // row sum), whose slice block is then stored in 16-byte pieces.  The dO
   // slice crosses LDS transposed, so each lane's fragment is two runs of rows.
-  auto step = [&](const F& f, F& fn, int ci, int cn, int buf) {
+  auto step = [&](const F& f, F& fn, int ci, int cn, int buf, int rb) {
     T* sb = sD[buf];
     T* sf = sF[buf];
+    const T* mr = reinterpret_cast<const T*>(mring + rb * PL::MB);  // this chunk's M
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       const int c4 = (wave * CBW + i) * 16 + 4 * grp;
@@ -898,7 +942,15 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
         for (int e = 0; e < 4; ++e) so[e * LDO] = __uint_as_float(f.dov[e]);
       }
     }
-    __syncthreads();
+    lds_barrier();
+    // this wave's M fragments first (read from the ring once, ahead of the
+    // products), then the exchanged dS' and dO operands
+    typename M::frag mfr[CBW][KD];
+#pragma unroll
+    for (int i = 0; i < CBW; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks)
+        mfr[i][ks] = M::load(mr + (((wave * CBW + i) * KD + ks) * 64 + lane) * M::KPL);
     typename M::frag bfr[KD], dof[KC];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) bfr[ks] = frag_at<T>(sb, LDS_S, 0, ks, lane);
@@ -913,35 +965,32 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
         dof[ks] = M::load(sor + 16 * (ks >> 2) + 4 * grp + (ks & 3));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // (keeps the reads ahead of the products)
 #pragma unroll
     for (int i = 0; i < CBW; ++i) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) acc = M::mma(f.zf[i][ks], dof[ks], acc);
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) acc = M::mma(f.mf[i][ks], bfr[ks], acc);
+      for (int ks = 0; ks < KD; ++ks) acc = M::mma(mfr[i][ks], bfr[ks], acc);
       dS[i] = acc;
     }
     __builtin_amdgcn_sched_barrier(0);
     const __amdgpu_buffer_rsrc_t rn = rec_of(cn);
-    load_m(fn, rn, 0);
-    __builtin_amdgcn_sched_barrier(0);
     // dS' of chunk ci: this slice's contiguous D x 16 block (sblk), in
     // 16-byte pieces (2 per row in bf16, 4 in fp32)
     T* dst = dstates + ((sp.c0 + ci) * H + h) * (int64_t)D * D + sblk<D>(0, n0);
     {
       constexpr int VEF = 16 / (int)sizeof(T), PPR = kBwdSliceW / VEF, NPC = D * PPR;
 #pragma unroll
-      for (int pr = 0; pr < (NPC + kBwdPassThreads - 1) / kBwdPassThreads; ++pr) {
-        const int pc = pr * kBwdPassThreads + threadIdx.x, row = pc / PPR, cv = VEF * (pc % PPR);
-        if (NPC % kBwdPassThreads == 0 || pc < NPC)
+      for (int pr = 0; pr < (NPC + kBwdPassCompute - 1) / kBwdPassCompute; ++pr) {
+        const int pc = pr * kBwdPassCompute + threadIdx.x, row = pc / PPR, cv = VEF * (pc % PPR);
+        if (NPC % kBwdPassCompute == 0 || pc < NPC)
           *reinterpret_cast<u32x4_t*>(dst + row * 16 + cv) =
               *reinterpret_cast<const u32x4_t*>(sf + row * LDF + cv);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 1; i < CBW; ++i) load_m(fn, rn, i);
     load_z(fn, rn, cn);
     // No second barrier: the next chunk writes the other buffers, and these
     // are rewritten only after the next chunk's barrier, which every wave
@@ -957,12 +1006,13 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
   int s = 0;
   for (; s + 3 <= nch; s += 3) {
     const int ci = nch - 1 - s;
-    step(fa, fc, ci, max(ci - 2, 0), s & 1);
-    step(fb, fa, ci - 1, max(ci - 3, 0), (s + 1) & 1);
-    step(fc, fb, ci - 2, max(ci - 4, 0), s & 1);
+    step(fa, fc, ci, max(ci - 2, 0), s & 1, 0);
+    step(fb, fa, ci - 1, max(ci - 3, 0), (s + 1) & 1, 1);
+    step(fc, fb, ci - 2, max(ci - 4, 0), s & 1, 2);
   }
-  if (s < nch) step(fa, fc, nch - 1 - s, 0, s & 1);
-  if (s + 1 < nch) step(fb, fa, nch - 2 - s, 0, (s + 1) & 1);
+  // (s is a multiple of 3 here: steps s and s + 1 use ring buffers 0 and 1)
+  if (s < nch) step(fa, fc, nch - 1 - s, 0, s & 1, 0);
+  if (s + 1 < nch) step(fb, fa, nch - 2 - s, 0, (s + 1) & 1, 1);
   if (dinit != nullptr) {
 #pragma unroll
     for (int i = 0; i < CBW; ++i)
@@ -1590,7 +1640,9 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
       hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
       if (ea != hipSuccess) return ea;
     }
-    return hipSuccess;
+    return hipFuncSetAttribute((const void*)kda_bwd_state_pass<T, D>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               BwdPassLds<T, D>::BYTES);
   });
   if (e != hipSuccess) return e;
   // chunk slots go in the grid's y dimension, at most kMaxGridY per launch
@@ -1604,9 +1656,10 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   }
   const int nslice = D / kBwdSliceW;
   const int nhpad = (NH + 7) / 8 * 8;
-  hipLaunchKernelGGL((kda_bwd_state_pass<T, D>), dim3(nhpad * nslice), dim3(kBwdPassThreads), 0,
-                     stream, recs, nslot, gm, H, NH, nslice, (const T*)d_o, d_final, dstates,
-                     d_init);
+  constexpr int kPassLds = BwdPassLds<T, D>::BYTES;
+  hipLaunchKernelGGL((kda_bwd_state_pass<T, D>), dim3(nhpad * nslice), dim3(kBwdPassThreads),
+                     kPassLds, stream, recs, nslot, gm, H, NH, nslice, (const T*)d_o, d_final,
+                     dstates, d_init);
   auto intra = d.gate_per_head ? kda_bwd_intra<T, D, true> : kda_bwd_intra<T, D, false>;
   for (int64_t sb = 0; sb < nslot; sb += kMaxGridY) {
     const unsigned ny = (unsigned)std::min<int64_t>(kMaxGridY, nslot - sb);

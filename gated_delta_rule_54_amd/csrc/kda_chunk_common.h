@@ -204,6 +204,33 @@ template <> struct BufFrag<float> {
   }
 };
 
+// LDS-direct load: 16 bytes per lane from the buffer into LDS at lds + 16 *
+// lane (one 1 KiB block per wave and instruction).
+__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+// s_waitcnt operand that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt is 6 bits: low 4 at [3:0], high 2 at
+// [15:14]) and leaves expcnt and lgkmcnt alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier for the state passes.  __syncthreads() carries a workgroup
+// release fence, which in a producer wave must also wait for every
+// LDS-direct load in flight (they write LDS) and would drain its prefetch;
+// here each wave waits only for its own LDS reads and writes (lgkmcnt), the
+// hardware barrier follows, and the empty asm statements keep the compiler
+// from moving LDS accesses across it.  A producer wave waits for the loads
+// the compute waves are about to read with an explicit vmcnt before the
+// barrier (see the state passes).
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left as they are
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Fragment of rows [row0, row0+16) and k-step ks of a row-major buffer.
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag frag_at(const T* base, int ld, int row0, int ks,
