@@ -930,14 +930,11 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     }
     if (threadIdx.x < NO) {
       const int r = threadIdx.x / LPR, cb = VE * (threadIdx.x % LPR);
-      T* so = sO[buf] + cb * LDO + r;
       if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          reinterpret_cast<uint16_t*>(so)[(2 * e) * LDO] = (uint16_t)(f.dov[e] & 0xffffu);
-          reinterpret_cast<uint16_t*>(so)[(2 * e + 1) * LDO] = (uint16_t)(f.dov[e] >> 16);
-        }
+        // as loaded: the slice row-major, [64 rows][16], one 16-byte piece
+        *reinterpret_cast<u32x4_t*>(sO[buf] + r * kBwdSliceW + cb) = f.dov;
       } else {
+        T* so = sO[buf] + cb * LDO + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) so[e * LDO] = __uint_as_float(f.dov[e]);
       }
@@ -954,15 +951,14 @@ __global__ __launch_bounds__(kBwdPassThreads, 1) void kda_bwd_state_pass(
     typename M::frag bfr[KD], dof[KC];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) bfr[ks] = frag_at<T>(sb, LDS_S, 0, ks, lane);
-    const T* sor = sO[buf] + (lane & 15) * LDO;
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks) {
-      if constexpr (M::KPL == 8) {  // kpos order: rows 32ks + 4grp.., then 32ks + 16 + 4grp..
-        const uint2 a = *reinterpret_cast<const uint2*>(sor + ks * 32 + 4 * grp);
-        const uint2 b = *reinterpret_cast<const uint2*>(sor + ks * 32 + 16 + 4 * grp);
-        dof[ks] = __builtin_bit_cast(typename M::frag, u32x4_t{a.x, a.y, b.x, b.y});
+      if constexpr (M::KPL == 8) {
+        // kpos order (rows 32ks + 4grp.., then 32ks + 16 + 4grp..) of column
+        // n: transpose reads of the row-major slice
+        dof[ks] = frag_cm_perm<T>(sO[buf], kBwdSliceW, 0, ks, lane);
       } else {
-        dof[ks] = M::load(sor + 16 * (ks >> 2) + 4 * grp + (ks & 3));
+        dof[ks] = M::load(sO[buf] + (lane & 15) * LDO + 16 * (ks >> 2) + 4 * grp + (ks & 3));
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // (keeps the reads ahead of the products)
