@@ -307,18 +307,17 @@ def write_counters(csvs, out: str = COUNTER_FILE, command: str = "") -> str:
 KERNEL_STATS_FILE = os.path.join(ROOT, "profiles", "kda_prefill_8k_decode_256x32_kernel_stats.md")
 # (kernel-name fragment, template arguments shown, workload, from the trace?)
 _STATS_ROWS = (
-    ("kda_intra_chunk<__hip_bfloat16, 128, false, true>", "kda_intra_chunk<bf16, 128, false, true>",
+    ("kda_intra_chunk<__hip_bfloat16, 128, false>", "kda_intra_chunk<bf16, 128, false>",
      "prefill 8K, 20 timed calls (trace)", True),
     ("kda_state_pass<__hip_bfloat16, 128, 16, true>", "kda_state_pass<bf16, 128, 16, true>",
      "prefill 8K, 20 timed calls (trace)", True),
     ("decode_step_kernel<__hip_bfloat16, 128>", "decode_step_kernel<bf16, 128>", "decode (stats)", False),
     ("gate_norm_kernel<__hip_bfloat16, 128>", "gate_norm_kernel<bf16, 128>", "epilogue (stats)", False),
     ("short_conv_kernel<__hip_bfloat16, 4>", "short_conv_kernel<bf16, 4>", "prologue (stats)", False),
-    ("kda_intra_chunk<__hip_bfloat16, 128, false, false>", "kda_intra_chunk<bf16, 128, false, false>",
-     "backward's forward, per segment (stats)", False),
+    ("kda_bwd_prep<__hip_bfloat16, 128, false>", "kda_bwd_prep<bf16, 128, false>",
+     "backward, per segment (stats)", False),
     ("kda_state_pass<__hip_bfloat16, 128, 16, false>", "kda_state_pass<bf16, 128, 16, false>",
      "backward's forward, per segment (stats)", False),
-    ("kda_bwd_prep<__hip_bfloat16, 128, false>", "kda_bwd_prep<bf16, 128, false>", "backward (stats)", False),
     ("kda_bwd_state_pass<__hip_bfloat16, 128>", "kda_bwd_state_pass<bf16, 128>", "backward (stats)", False),
     ("kda_bwd_intra<__hip_bfloat16, 128, false>", "kda_bwd_intra<bf16, 128, false>", "backward (stats)", False),
 )
@@ -945,8 +944,8 @@ def main():
                                   "frac": bw["achieved_gbs"] / HBM_PEAK_GBS,
                                   "traffic": (tr_bwd / (bw["ms"] * 1e-3) / 1e9) if tr_bwd else None,
                                   "traffic_bytes_per_call": tr_bwd,
-                                  "kernel": "kda_chunk_bwd (forward recompute + kda_bwd_prep + "
-                                            "kda_bwd_state_pass + kda_bwd_intra)",
+                                  "kernel": "kda_chunk_bwd (kda_bwd_prep + forward state pass "
+                                            "+ kda_bwd_state_pass + kda_bwd_intra)",
                                   "bytes_per_token_head": BACKWARD_BYTES_PER_TH}},
         "gate_modes": {"workload": "prefill B=1 H=16 d=128 bf16, T = 2K..64K: per-channel "
                                    "gates (KDA) vs one gate per token and head (GDN)",

@@ -75,22 +75,6 @@ namespace {
 constexpr int64_t kSegRecordBudget = 160ll << 20;
 constexpr int64_t kSegSlotsMax = 1024;  // chunk slots per K1/K2 launch pair, at most
 
-// ---------------------------------------------------------------------------
-// Workspace record of one (head, chunk slot): the operands K2 reads.
-template <typename T, int D>
-struct Rec {
-  // element offsets inside a record (in units of T), then gamma (fp32).
-  // QG, KT, WN and P are fragment-native (see fnat) with the k index named;
-  // U is stored as 16x16 accumulator tiles [n/16][r/16][lane][4].
-  static constexpr int64_t QG = 0;                 // rows r, k = channel: q^ o e^G
-  static constexpr int64_t KT = QG + kC * D;       // rows channel, k = r: k^ o e^(gamma-G)
-  static constexpr int64_t WN = KT + D * kC;       // rows r, k = channel: -Wk
-  static constexpr int64_t UT = WN + kC * D;       // U (rows r, columns n) as tiles
-  static constexpr int64_t P = UT + D * kC;        // rows r, k = i: P (zero for i > r)
-  static constexpr int64_t END = P + kC * kC;
-  static constexpr int64_t BYTES_T = END * (int64_t)sizeof(T);
-  static constexpr int64_t BYTES = ((BYTES_T + D * 4 + 255) / 256) * 256;  // + e^gamma
-};
 // The state pass addresses one head's records of a segment through a buffer
 // resource with 32-bit offsets and relies on reads at kPastBound returning
 // zeros: a segment's records per head must stay below that offset.
@@ -312,7 +296,7 @@ __device__ __forceinline__ void k1_exact_ap(
 // strict lower, fp32) over region 1 and P into the record, as the fast path
 // does.  Out of line, like the exact path, so that its registers do not set
 // the common path's budget.  Every thread of the workgroup calls it.
-template <typename T, int D, bool GS, bool RO>
+template <typename T, int D, bool GS>
 __device__ __forceinline__ void k1_mid_ap(T* kop, T* qop, T* kim, const float* s_beta, T* wP,
                                           const float* gb, int64_t rowstride, int H, int len,
                                           float offx, float offy, float mx, float my) {
@@ -374,7 +358,7 @@ __device__ __forceinline__ void k1_mid_ap(T* kop, T* qop, T* kim, const float* s
       p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
     }
     *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-    if (RO) st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
+    st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
   }
 }
 
@@ -384,7 +368,7 @@ __device__ __forceinline__ void k1_mid_ap(T* kop, T* qop, T* kim, const float* s
 // in every channel, the exact path otherwise.  One call site out of line, so
 // that neither path's registers weigh on the common path.  Every thread of
 // the workgroup calls it.
-template <typename T, int D, bool GS, bool RO>
+template <typename T, int D, bool GS>
 __device__ __attribute__((noinline)) void k1_slow_ap(T* r0, T* r1, T* r2, const float* s_beta,
                                                      T* wP, const float* gb, int64_t rowstride,
                                                      int H, int len, float offx, float offy) {
@@ -404,23 +388,19 @@ __device__ __attribute__((noinline)) void k1_slow_ap(T* r0, T* r1, T* r2, const 
                                     gx - mx < kFastDecayBound || gy - my < kFastDecayBound) == 0;
   // (every read of the part totals is done: region 2 is free)
   if (mid)
-    k1_mid_ap<T, D, GS, RO>(r0, r1, r2, s_beta, wP, gb, rowstride, H, len, offx, offy, mx, my);
+    k1_mid_ap<T, D, GS>(r0, r1, r2, s_beta, wP, gb, rowstride, H, len, offx, offy, mx, my);
   else
     k1_exact_ap<T, D, GS>(r0, r1, reinterpret_cast<float*>(r2), reinterpret_cast<float*>(r1),
                           s_beta, wP, gb, rowstride, H, len, offx, offy);
 }
 
 // GS: one gate per (token, head), broadcast over the key channels (Gated
-// DeltaNet) instead of one per channel.  RO = false: the records feed a
-// state pass without output (inside the backward), which reads neither
-// Q o e^G nor P, so those blocks are not written (the exact-decay path
-// still writes its P).
-template <typename T, int D, bool GS, bool RO>
+// DeltaNet) instead of one per channel.
+template <typename T, int D, bool GS>
 __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) void kda_intra_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
     int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws) {
-  constexpr bool rec_out = RO;
   using L = K1Lds<T, D>;
   using M = Mma<T>;
   using R = Rec<T, D>;
@@ -515,8 +495,6 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
 #pragma unroll
     for (int j = 0; j < RPP; ++j) {
       // rows past the chunk's end read as zero (their norms are never used)
-      // (plain fp32 arithmetic: the packed bf16 dot-product instruction gave
-      // wrong sums inside a larger kernel here, so it is not used)
       const float2 qj = qraw[j].get(), kj = kraw[j].get();
       x[j] = qj.x * qj.x + qj.y * qj.y;
       x[RPP + j] = kj.x * kj.x + kj.y * kj.y;
@@ -596,7 +574,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
       // operations as __expf, so the same values)
       const float gsx = G[jj].x * kLog2eF, gsy = G[jj].y * kLog2eF;
       const float egx = __builtin_amdgcn_exp2f(gsx), egy = __builtin_amdgcn_exp2f(gsy);
-      if (direct && rec_out) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
+      if (direct) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
       kgx[e] = khx * egx;
       kgy[e] = khy * egy;
       if (!exact) {
@@ -643,8 +621,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
   if constexpr (kStaged) {
     if (!exact) {
       constexpr int QB = (kC / 16) * (D / 32), KB = (D / 16) * (kC / 32);  // blocks
-      // (a pass without output reads no Q o e^G: its blocks are skipped)
-      for (int sidx = tid + (RO ? 0 : QB * 64); sidx < (QB + KB) * 64; sidx += NT) {
+      for (int sidx = tid; sidx < (QB + KB) * 64; sidx += NT) {
         const int b = sidx >> 6, L = sidx & 63, g = L >> 4;
         float v[8];
         if (b < QB) {  // Q o e^G: rows r, k = channel
@@ -695,7 +672,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
       }
     }
   } else {
-    k1_slow_ap<T, D, GS, rec_out>(r0, r1, r2, s_beta, wP, gb, rowstride, H, loc.len, off.x, off.y);
+    k1_slow_ap<T, D, GS>(r0, r1, r2, s_beta, wP, gb, rowstride, H, loc.len, off.x, off.y);
     load_v();
   }
   if (!exact) {
@@ -716,10 +693,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
         p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
       }
       *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-      if (rec_out) st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
+      st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
     }
   }
-  if (rec_out) {
+  {
     // zero blocks of P above the diagonal, (R, I) = (0,1) (0,2) (0,3) (1,2)
     // (1,3) (2,3): only those inside a k-step the state pass reads for rows
     // R (its lowest 16-row block <= R; the others it reads as zeros)
@@ -991,8 +968,9 @@ struct K2Frags {
   }
 };
 
-// OUT = false (the forward run inside the backward): no output, so neither
-// Q o e^G nor P is loaded and O is not formed.
+// OUT = false (the forward states inside the backward, over records that
+// kda_bwd_prep writes): no output, so neither Q o e^G nor P is loaded and O
+// is not formed.
 template <typename T, int D, int WS, bool OUT>
 __global__ __launch_bounds__(k2_threads<T>(), 1) void kda_state_pass(
     const char* __restrict__ ws, ChunkGeom gm, int H, int64_t s0, int64_t s1, int seg,
@@ -1388,7 +1366,8 @@ template <typename T, int D>
 hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const void* v,
                      const float* g, const float* beta, const float* init_state,
                      const int32_t* cu, void* o, float* final_state, float* ckpt,
-                     void* states, char* ws, int64_t SS, hipStream_t stream) {
+                     void* states, char* ws, int64_t SS, chunk_record_stage_fn stage,
+                     void* stage_ctx, hipStream_t stream) {
   const bool varlen = cu != nullptr;
   const Plan p = make_plan(d, varlen, SS);
   const int H = d.heads, NH = d.num_seqs * d.heads;
@@ -1404,15 +1383,14 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   const int nslice = D / WS;
   const int nhpad = (NH + 7) / 8 * 8;
   const int k1_lds = K1Lds<T, D>::BYTES;
-  // the per-chunk states are written only by the pass without o
-  if (o != nullptr && states != nullptr) return hipErrorInvalidValue;
+  // the per-chunk states are written only by the pass without o, and only
+  // that pass takes its records from a caller's stage
+  if (o != nullptr && (states != nullptr || stage != nullptr)) return hipErrorInvalidValue;
   // K1's dynamic LDS limit, once per device
   static std::atomic<uint64_t> attr_done{0};
   hipError_t ea = once_per_device(attr_done, [&]() {
-    for (const void* fn : {(const void*)kda_intra_chunk<T, D, false, true>,
-                           (const void*)kda_intra_chunk<T, D, true, true>,
-                           (const void*)kda_intra_chunk<T, D, false, false>,
-                           (const void*)kda_intra_chunk<T, D, true, false>}) {
+    for (const void* fn : {(const void*)kda_intra_chunk<T, D, false>,
+                           (const void*)kda_intra_chunk<T, D, true>}) {
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
       if (e != hipSuccess) return e;
     }
@@ -1429,11 +1407,12 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   const int64_t nseg = p.slot_bound == 0 ? 1 : (p.slot_bound + SS - 1) / SS;
   for (int64_t s = 0; s < nseg; ++s) {
     const int64_t s0 = s * SS, s1 = std::min<int64_t>(p.slot_bound, s0 + SS);
-    if (s1 > s0) {
-      auto k1 = o != nullptr ? (d.gate_per_head ? kda_intra_chunk<T, D, true, true>
-                                                : kda_intra_chunk<T, D, false, true>)
-                             : (d.gate_per_head ? kda_intra_chunk<T, D, true, false>
-                                                : kda_intra_chunk<T, D, false, false>);
+    if (s1 > s0 && stage != nullptr) {
+      const hipError_t es = stage(stage_ctx, s0, s1, recs, stream);
+      if (es != hipSuccess) return es;
+    } else if (s1 > s0) {
+      if (o == nullptr) return hipErrorInvalidValue;  // a states-only pass takes a stage
+      auto k1 = d.gate_per_head ? kda_intra_chunk<T, D, true> : kda_intra_chunk<T, D, false>;
       hipLaunchKernelGGL(k1, dim3(H, (unsigned)(s1 - s0)), dim3(k1_threads<T, D>()), k1_lds,
                          stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
                          s1 - s0, d.qk_l2norm, recs);
@@ -1460,17 +1439,21 @@ namespace {
 hipError_t launch_with(const kda_desc_t& d, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, const float* init_state,
                        const int32_t* cu_seqlens, void* o, float* final_state, float* state_ckpt,
-                       void* chunk_states, char* ws, int64_t ss, hipStream_t stream) {
+                       void* chunk_states, char* ws, int64_t ss, hipStream_t stream,
+                       chunk_record_stage_fn stage = nullptr, void* stage_ctx = nullptr) {
   const bool bf = d.dtype == KDA_DTYPE_BF16;
   if (d.dk == 128)
     return bf ? run_typed<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                     final_state, state_ckpt, chunk_states, ws, ss, stream)
+                                     final_state, state_ckpt, chunk_states, ws, ss, stage,
+                                     stage_ctx, stream)
               : run_typed<float, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                      final_state, state_ckpt, chunk_states, ws, ss, stream);
+                                      final_state, state_ckpt, chunk_states, ws, ss, stage,
+                                      stage_ctx, stream);
   return bf ? run_typed<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state,
-                                  state_ckpt, chunk_states, ws, ss, stream)
+                                  state_ckpt, chunk_states, ws, ss, stage, stage_ctx, stream)
             : run_typed<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
-                                   final_state, state_ckpt, chunk_states, ws, ss, stream);
+                                   final_state, state_ckpt, chunk_states, ws, ss, stage,
+                                   stage_ctx, stream);
 }
 }  // namespace
 
@@ -1481,6 +1464,16 @@ hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, c
                             hipStream_t stream) {
   return launch_with(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state, state_ckpt,
                      chunk_states, static_cast<char*>(workspace), seg_slots(d), stream);
+}
+
+hipError_t launch_chunk_states(const kda_desc_t& d, const float* init_state,
+                               const int32_t* cu_seqlens, void* chunk_states, void* workspace,
+                               chunk_record_stage_fn stage, void* stage_ctx,
+                               hipStream_t stream) {
+  if (stage == nullptr || chunk_states == nullptr) return hipErrorInvalidValue;
+  return launch_with(d, nullptr, nullptr, nullptr, nullptr, nullptr, init_state, cu_seqlens,
+                     nullptr, nullptr, nullptr, chunk_states, static_cast<char*>(workspace),
+                     seg_slots(d), stream, stage, stage_ctx);
 }
 
 // ---------------------------------------------------------------------------

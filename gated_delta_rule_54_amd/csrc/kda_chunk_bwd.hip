@@ -35,16 +35,18 @@
 // Gated DeltaNet mode (one gate per token and head) sums dg over channels.
 //
 // Launches, all on the caller's stream:
-//   1. the forward (kda_chunk.hip) with o off and every chunk's entering
-//      state S written to the workspace;
-//   2. kda_bwd_prep, one workgroup per (chunk, head): M and Z^T in operand
-//      order for the reverse pass;
-//   3. kda_bwd_state_pass, one workgroup per (sequence, head, 16 columns of
+//   1. the forward's states, per segment of chunk slots (kda_chunk.hip's
+//      launch_chunk_states): kda_bwd_prep, one workgroup per (chunk, head),
+//      forms the chunk's norms, G, A, P, T and writes the forward state
+//      pass's record (K~, -Wk, U, e^gamma), the reverse pass's record (M and
+//      Z^T in operand order) and T; the forward's state pass (without output)
+//      then writes every chunk's entering state S to the workspace;
+//   2. kda_bwd_state_pass, one workgroup per (sequence, head, 16 columns of
 //      d_v), sequential over the sequence's chunks from the last: dS' of every
 //      chunk to the workspace, dS of the first to d_init_state;
-//   4. kda_bwd_intra, one workgroup per (chunk, head): every gradient above.
-// The per-chunk kernels recompute the chunk's operands (norms, G, A, T, P)
-// rather than store them.
+//   3. kda_bwd_intra, one workgroup per (chunk, head): every gradient above.
+// The intra-chunk kernel recomputes the chunk's operands (norms, G, A, P)
+// rather than store them; T it loads.
 //
 // Operand layouts.  A workgroup of D/16 waves gives wave w the 16 columns
 // [16w, 16w+16) of every chunk x d matrix, all 64 rows, in MFMA accumulator
@@ -59,7 +61,8 @@
 // does: the chunk start while every channel's chunk decay gamma >= -80, else
 // G of row 31 while each half of the chunk decays by at most 80 (gamma down to
 // about -160; see BwdMode).  A chunk beyond that gets NaN gradients, and its
-// NaN state gradient reaches every chunk before it (all but dq).  fp32 operands at d = 128 do
+// NaN state gradient reaches every chunk before it (all but dq); its A (and
+// so the forward states after it) is still formed exactly, by kda_bwd_prep.  fp32 operands at d = 128 do
 // not fit one workgroup's LDS and are not supported.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -229,6 +232,22 @@ __device__ __forceinline__ void st_nt(bf16* p, float x) {
   __builtin_nontemporal_store(bf_bits(x), reinterpret_cast<uint16_t*>(p));
 }
 __device__ __forceinline__ void st_nt(float* p, float x) { __builtin_nontemporal_store(x, p); }
+// st_fnat4 with non-temporal stores: the reverse pass's records are read once,
+// after the forward pass, and allocated in the last-level cache they would
+// push out the state pass's records that the forward reads next.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_fnat4_nt(bf16* base, int nks, int m, int k0, float a, float b,
+                                            float c, float d) {
+  __builtin_nontemporal_store(u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)},
+                              reinterpret_cast<u32x2_t*>(base + fnat<bf16>(m, k0, nks)));
+}
+__device__ __forceinline__ void st_fnat4_nt(float* base, int nks, int m, int k0, float a, float b,
+                                            float c, float d) {
+  __builtin_nontemporal_store(a, base + fnat<float>(m, k0, nks));
+  __builtin_nontemporal_store(b, base + fnat<float>(m, k0 + 1, nks));
+  __builtin_nontemporal_store(c, base + fnat<float>(m, k0 + 2, nks));
+  __builtin_nontemporal_store(d, base + fnat<float>(m, k0 + 3, nks));
+}
 
 // A copy of x the compiler cannot see through: lane indices renewed from it
 // at a phase boundary make the phase form its own address arithmetic there,
@@ -497,8 +516,6 @@ __device__ __forceinline__ void stage_rows(const T* q, const T* k, const float* 
   for (int i = 0; i < NPK; ++i) {
     const int p = i * NT + tid, row = p / PR, cp = p % PR;
     float a = 0.f, b = 0.f;  // this piece's part of |k_row|^2, |q_row|^2
-    // (plain fp32 arithmetic: the packed bf16 dot-product instruction gave
-    // wrong sums in this kernel, so it is not used)
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -563,7 +580,37 @@ __device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdR
 // INV: form T here (else the caller puts T in tb before its next barrier);
 // tout (or nullptr): where T itself (without Diag(beta)) also goes, 64 x 64
 // row-major in the MFMA type.
-template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false, bool INV = true>
+// A of a chunk beyond the mid reference's range, exactly: every entry from
+// its own exponent differences, A_ri = beta_r sum_c k^_rc k^_ic e^(G_rc - G_ic)
+// (i < r), so that T and what follows from it hold for any gate.  Channels
+// come 16 at a time, k^ and G channel-major in `stage`; thread (row r = lane,
+// columns i = wave + NW e) adds their terms to its entries of A in LDS (the
+// first block starts them, the last scales by beta_r and clears i >= r).
+// LDS operands only, so it adds few registers to the common path.
+template <int NW>
+__device__ __forceinline__ void exact_A_block(const float* stage, const float* beta, float* sA,
+                                           int lane, int wave, bool first, bool last) {
+  constexpr int EPT = kC / NW;
+  const float* sk = stage;
+  const float* sg = stage + 16 * kC;
+#pragma unroll 1
+  for (int e = 0; e < EPT; ++e) {
+    const int i = wave + NW * e;  // the same for the whole wave: broadcast reads
+    float a = first ? 0.f : sA[lane * kTriLd + i];
+#pragma unroll 4
+    for (int cc = 0; cc < 16; ++cc) {
+      const float d = i < lane ? sg[cc * kC + lane] - sg[cc * kC + i] : 0.f;
+      a += sk[cc * kC + lane] * sk[cc * kC + i] * __expf(d);
+    }
+    sA[lane * kTriLd + i] = last ? (i < lane ? beta[lane] * a : 0.f) : a;
+  }
+}
+
+// EXA: a chunk beyond the mid reference's range forms A exactly (exact_A),
+// in T's LDS before T is written; otherwise such a chunk's A, T are not
+// meaningful (its results are NaN by the caller's choice).
+template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false, bool INV = true,
+          bool EXA = false>
 __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
                                             const float* __restrict__ g,
                                             const float* __restrict__ beta, const ChunkLoc& loc,
@@ -648,6 +695,28 @@ __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __
     }
   }
   __syncthreads();
+  if constexpr (EXA) {
+    static_assert(2 * 16 * kC * 4 <= L::CB, "exact A's stage must fit T's buffer");
+    if (mode == kBwdBeyond) {  // T's buffer is free until the inverse
+      float* xs = reinterpret_cast<float*>(sm.tb);
+#pragma unroll 1
+      for (int b = 0; b < NW; ++b) {
+        if (wave == b) {  // this wave's 16 channels, channel-major
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 16 * t + 4 * grp + j;
+              xs[(lane & 15) * kC + r] = R.kh[t][j];
+              xs[16 * kC + (lane & 15) * kC + r] = R.G[t][j];
+            }
+        }
+        __syncthreads();
+        exact_A_block<NW>(xs, sm.beta, sm.sA, lane, wave, b == 0, b == NW - 1);
+        __syncthreads();
+      }
+    }
+  }
   tri_inv64(sm.sA, sm.sT, sm.scratch, wave, lane);
   for (int e = tid; e < kC * kC; e += NT) {
     const int r = e >> 6, i = e & 63;
@@ -662,7 +731,7 @@ __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __
       float x[VE];
 #pragma unroll
       for (int u = 0; u < VE; ++u) x[u] = i0 + u <= r ? sm.sT[r * kTriLd + i0 + u] : 0.f;
-      *reinterpret_cast<u32x4_t*>(tout + r * kC + i0) = pack16(x, T{});
+      __builtin_nontemporal_store(pack16(x, T{}), reinterpret_cast<u32x4_t*>(tout + r * kC + i0));
     }
   }
   __syncthreads();
@@ -680,16 +749,28 @@ struct BRec {
   static constexpr int64_t BYTES = (END * (int64_t)sizeof(T) + 255) / 256 * 256;
 };
 
+// kda_bwd_prep, one workgroup per (chunk, head) of one segment of chunk slots:
+// the chunk's norms, G, A, P, T = (I + A)^-1, then
+//  * the reverse pass's record (M and scale Z^T) and T (for the intra-chunk
+//    kernel), indexed by the batch's slot;
+//  * the state pass's record (K~, -Wk, U = T Diag(beta) V, e^gamma), indexed
+//    by the slot within the segment (frec, fnrec slots per head): the
+//    backward's forward pass runs the state pass on these instead of the
+//    intra-chunk kernel's.
+// A chunk beyond the mid reference's range forms A exactly, so its state-pass
+// record (and T) hold; its reverse-pass record is NaN.
 template <typename T, int D, bool GS>
 __global__ __launch_bounds__((BwdLds<T, D>::NT), 1)
 __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, ChunkGeom gm, int H, int64_t nslot, int64_t slot_base,
-    int qk_l2norm, float scale, char* __restrict__ brec, T* __restrict__ tinv) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
+    int64_t nslot, int64_t slot_base, int qk_l2norm, float scale, char* __restrict__ brec,
+    T* __restrict__ tinv, char* __restrict__ frec, int64_t fnrec) {
   using L = BwdLds<T, D, true>;
   using M = Mma<T>;
   using RC = BRec<T, D>;
-  constexpr int NW = L::NW, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
+  using RF = Rec<T, D>;
+  constexpr int NW = L::NW, NT = L::NT, LDX = L::LDX, LDC = L::LDC, NTW = 16 / NW;
   constexpr int KC = kC / M::KSTEP, KD = D / M::KSTEP;
   extern __shared__ __align__(16) char smem[];
   const int h = blockIdx.x;
@@ -699,34 +780,69 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
   BwdSmem<T, D, true> sm(smem);
   BwdRegs R;
   f32x4_t Bm[NTW];
-  const int mode = bwd_prologue<T, D, GS, true, true, true>(
+  const int mode = bwd_prologue<T, D, GS, true, true, true, true, true>(
       q, k, g, beta, loc, H, h, qk_l2norm, sm, R, Bm, tinv + (slot * H + h) * (int64_t)(kC * kC));
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
   const int c = 16 * wave + (lane & 15);
+  // v's rows in 16-byte pieces through a resource bounded at the chunk's last
+  // valid row (rows past it read as zero), non-temporal as k, q, g; staged in
+  // LDS after M, for U
+  constexpr int VE = 16 / (int)sizeof(T), PR = D / VE, NPV = kC * PR / NT;
+  static_assert(kC * PR % NT == 0, "v's pieces must tile the threads");
+  u32x4_t vp[NPV];
+  {
+    const int rs = H * D;
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(v + (loc.tok0 * H + h) * D), (short)0,
+        ((loc.len - 1) * rs + D) * (int)sizeof(T), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int p = i * NT + tid, row = p / PR, cp = p % PR;
+      vp[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rv, (uint32_t)((row * rs + cp * VE) * (int)sizeof(T)), 0, 2);
+    }
+  }
   // beyond the mid reference's range: NaN records, so that the reverse pass
   // carries NaN into every state gradient before this chunk
   const float nanf = mode == kBwdBeyond ? __builtin_nanf("") : 0.f;
-  // K~ into the region the inverse has finished with
+  char* fr = frec + ((int64_t)h * fnrec + blockIdx.y) * RF::BYTES;
+  T* wKT = reinterpret_cast<T*>(fr) + RF::KT;
+  T* wWN = reinterpret_cast<T*>(fr) + RF::WN;
+  T* wUT = reinterpret_cast<T*>(fr) + RF::UT;
+  float* wEG = reinterpret_cast<float*>(fr + RF::BYTES_T);
+  // K~ into the region the inverse has finished with, and into the record;
+  // Kp = K^ o e^G, and Qp = Q^ o e^G in place of Q^ (G is dead after this)
+  f32x4_t kpa[4], wk[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t) {
+    float kt[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      st_f(sm.kt + (16 * t + 4 * grp + j) * LDX + c, R.kh[t][j] * __expf(R.gam - R.G[t][j]));
+    for (int j = 0; j < 4; ++j) {
+      const float eg = __expf(R.G[t][j]);
+      kt[j] = R.kh[t][j] * __expf(R.gam - R.G[t][j]);
+      kpa[t][j] = R.kh[t][j] * eg;
+      R.qh[t][j] *= eg;
+      st_f(sm.kt + (16 * t + 4 * grp + j) * LDX + c, kt[j]);
+    }
+    st_fnat4(wKT, KC, c, 16 * t + 4 * grp, kt[0], kt[1], kt[2], kt[3]);
+  }
+  const float egam = __expf(R.gam);
+  if (grp == 0) wEG[c] = egam;
   __syncthreads();
   T* rec = reinterpret_cast<T*>(brec + ((int64_t)h * nslot + slot) * RC::BYTES);
 
-  // Wk = T Diag(beta) Kp for this wave's columns, B = Kp from registers
-  f32x4_t kpa[4], wk[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kpa[t][j] = R.kh[t][j] * __expf(R.G[t][j]);
+  // Wk = T Diag(beta) Kp for this wave's columns, B = Kp from registers; the
+  // record's -Wk from the transposed product (rows r, four channels a lane)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     wk[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t wt = wk[t];
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks)
+    for (int ks = 0; ks < KC; ++ks) {
       wk[t] = M::mma(frag_rm_perm<T>(sm.tb, LDC, 16 * t, ks, lane), acc_frag<T>(kpa, ks), wk[t]);
+      wt = M::mma(acc_frag<T>(kpa, ks), frag_rm_perm<T>(sm.tb, LDC, 16 * t, ks, lane), wt);
+    }
+    st_fnat4(wWN, KD, 16 * t + (lane & 15), 16 * wave + 4 * grp, -wt[0], -wt[1], -wt[2], -wt[3]);
   }
   // Z = Qp - P Wk, stored as scale Z^T (rows c, k = r; the reverse pass then
   // takes dO as it is): each lane's 4 rows are 4 consecutive k
@@ -738,12 +854,11 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
       pw = M::mma(frag_rm_perm<T>(sm.pb, LDC, 16 * t, ks, lane), acc_frag<T>(wk, ks), pw);
     float z[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] * __expf(R.G[t][j]) - pw[j]) + nanf;
-    st_fnat4(rec + RC::ZF, KC, c, 16 * t + 4 * grp, z[0], z[1], z[2], z[3]);
+    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] - pw[j]) + nanf;
+    st_fnat4_nt(rec + RC::ZF, KC, c, 16 * t + 4 * grp, z[0], z[1], z[2], z[3]);
   }
   // M^T tiles (rows c', column c) = Diag(e^gamma) - K~^T Wk, stored as M
   // (rows c, k = c')
-  const float egam = __expf(R.gam);
 #pragma unroll
   for (int cb = 0; cb < NW; ++cb) {
     f32x4_t mt = {0.f, 0.f, 0.f, 0.f};
@@ -756,7 +871,27 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
       const int c2 = 16 * cb + 4 * grp + j;
       m[j] = (c2 == c ? egam : 0.f) - mt[j] + nanf;
     }
-    st_fnat4(rec + RC::MF, KD, c, 16 * cb + 4 * grp, m[0], m[1], m[2], m[3]);
+    st_fnat4_nt(rec + RC::MF, KD, c, 16 * cb + 4 * grp, m[0], m[1], m[2], m[3]);
+  }
+  // U = T Diag(beta) V: V row-major in the region after K~'s (the inverse's,
+  // free since the prologue), read as column fragments
+  T* sv = reinterpret_cast<T*>(smem + L::XB);
+  static_assert(2 * L::XB <= L::R0, "V must fit region 0 beside K~");
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    const int p = i * NT + tid, row = p / PR, cp = p % PR;
+    *reinterpret_cast<u32x4_t*>(sv + row * LDX + cp * VE) = vp[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks)
+      u = M::mma(frag_rm_perm<T>(sm.tb, LDC, 16 * t, ks, lane),
+                 frag_cm_perm<T>(sv, LDX, 16 * wave, ks, lane), u);
+    // rows 16 t + 4 (lane / 16) + j, column c: tile (c / 16, t)
+    st4(wUT + ((wave * (kC / 16) + t) * 64 + lane) * 4, u[0], u[1], u[2], u[3]);
   }
 }
 
@@ -1595,6 +1730,33 @@ BwdPlan bwd_plan(const kda_desc_t& d) {
   return p;
 }
 
+// The backward's record stage for the forward's state pass (see
+// launch_chunk_states): kda_bwd_prep over one segment of chunk slots.
+template <typename T>
+struct PrepStage {
+  const T *q, *k, *v;
+  const float *g, *beta;
+  ChunkGeom gm;
+  int H;
+  int64_t nslot;
+  int qk_l2norm;
+  float scale;
+  char* brec;
+  T* tinv;
+  bool gate_per_head;
+};
+
+template <typename T, int D>
+hipError_t prep_stage(void* ctx, int64_t s0, int64_t s1, char* recs, hipStream_t stream) {
+  const PrepStage<T>& c = *static_cast<const PrepStage<T>*>(ctx);
+  using LP = BwdLds<T, D, true>;
+  auto prep = c.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
+  hipLaunchKernelGGL(prep, dim3(c.H, (unsigned)(s1 - s0)), dim3(LP::NT), LP::BYTES, stream, c.q,
+                     c.k, c.v, c.g, c.beta, c.gm, c.H, c.nslot, s0, c.qk_l2norm, c.scale, c.brec,
+                     c.tinv, recs, s1 - s0);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                    const float* g, const float* beta, const float* init_state, const int32_t* cu,
@@ -1612,11 +1774,6 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   int32_t* cu_s = chunk_off + (p.map / 2) / 4;
   const int64_t nslot = chunk_slot_bound(d, varlen);
 
-  kda_desc_t df = d;
-  df.ckpt_every = 0;
-  hipError_t e = launch_chunk_fwd(df, q, k, v, g, beta, init_state, cu, nullptr, nullptr,
-                                  nullptr, states, ws, stream);
-  if (e != hipSuccess) return e;
   ChunkGeom gm{nullptr, nullptr, d.seqlen, (d.seqlen + kC - 1) / kC, d.num_seqs};
   if (varlen) {
     hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, stream, cu, d.num_seqs,
@@ -1625,7 +1782,7 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   }
   using LP = BwdLds<T, D, true>;
   static std::atomic<uint64_t> attr_done{0};
-  e = once_per_device(attr_done, [&]() {
+  hipError_t e = once_per_device(attr_done, [&]() {
     for (const void* fn : {(const void*)kda_bwd_prep<T, D, false>,
                            (const void*)kda_bwd_prep<T, D, true>}) {
       hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LP::BYTES);
@@ -1641,15 +1798,17 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
                                BwdPassLds<T, D>::BYTES);
   });
   if (e != hipSuccess) return e;
+  // the forward pass: per segment of chunk slots, kda_bwd_prep writes the
+  // state pass's records (and the reverse pass's records and T of those
+  // slots), then the state pass writes the state entering every chunk
+  PrepStage<T> ps{(const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, nslot,
+                  d.qk_l2norm, d.scale, recs, tinv, d.gate_per_head != 0};
+  kda_desc_t df = d;
+  df.ckpt_every = 0;
+  e = launch_chunk_states(df, init_state, cu, states, ws, prep_stage<T, D>, &ps, stream);
+  if (e != hipSuccess) return e;
   // chunk slots go in the grid's y dimension, at most kMaxGridY per launch
   constexpr int64_t kMaxGridY = 32768;
-  auto prep = d.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
-  for (int64_t sb = 0; sb < nslot; sb += kMaxGridY) {
-    const unsigned ny = (unsigned)std::min<int64_t>(kMaxGridY, nslot - sb);
-    hipLaunchKernelGGL(prep, dim3(H, ny), dim3(LP::NT), LP::BYTES, stream, (const T*)q,
-                       (const T*)k, g, beta, gm, H, nslot, sb, d.qk_l2norm, d.scale, recs,
-                       tinv);
-  }
   const int nslice = D / kBwdSliceW;
   const int nhpad = (NH + 7) / 8 * 8;
   constexpr int kPassLds = BwdPassLds<T, D>::BYTES;

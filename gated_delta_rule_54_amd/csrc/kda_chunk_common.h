@@ -268,6 +268,25 @@ __device__ __forceinline__ int fnat(int m, int k, int nks) {
   return (((m >> 4) * nks + p / M::KSTEP) * 64 + (m & 15) + 16 * (q / M::KPL)) * M::KPL +
          q % M::KPL;
 }
+// Record of one (head, chunk slot): the operands the state pass reads,
+// written by the intra-chunk kernel (or, for the backward's states-only pass,
+// by the backward's per-chunk preparation).
+template <typename T, int D>
+struct Rec {
+  // element offsets inside a record (in units of T), then gamma (fp32).
+  // QG, KT, WN and P are fragment-native (see fnat) with the k index named;
+  // U is stored as 16x16 accumulator tiles [n/16][r/16][lane][4].  A state
+  // pass without output reads only KT, WN, UT and e^gamma.
+  static constexpr int64_t QG = 0;                 // rows r, k = channel: q^ o e^G
+  static constexpr int64_t KT = QG + kC * D;       // rows channel, k = r: k^ o e^(gamma-G)
+  static constexpr int64_t WN = KT + D * kC;       // rows r, k = channel: -Wk
+  static constexpr int64_t UT = WN + kC * D;       // U (rows r, columns n) as tiles
+  static constexpr int64_t P = UT + D * kC;        // rows r, k = i: P (zero for i > r)
+  static constexpr int64_t END = P + kC * kC;
+  static constexpr int64_t BYTES_T = END * (int64_t)sizeof(T);
+  static constexpr int64_t BYTES = ((BYTES_T + D * 4 + 255) / 256) * 256;  // + e^gamma
+};
+
 // Stores of k-runs of row m into a fragment-native matrix (k0 % 4 == 0 for
 // runs of 4, k0 % 8 == 0 for runs of 8, k0 even for pairs).  For bf16 a run
 // of 4 is one 8-byte piece; fp32 scatters.

@@ -42,6 +42,18 @@ hipError_t launch_chunk_fwd(const kda_desc_t& d, const void* q, const void* k, c
                             const int32_t* cu_seqlens, void* o, float* final_state,
                             float* state_ckpt, void* chunk_states, void* workspace,
                             hipStream_t stream);
+// States-only chunkwise pass whose chunk records come from the caller: for
+// each segment of chunk slots [s0, s1), stage(ctx, s0, s1, recs, stream)
+// launches, on `stream`, kernels that write the records of those slots (the
+// blocks a state pass without output reads: K~, -Wk, U, e^gamma) at `recs`,
+// head h and slot s at recs + (h (s1 - s0) + s - s0) record bytes; the state
+// pass then runs over them.  chunk_states and the workspace are as for
+// launch_chunk_fwd without o.
+typedef hipError_t (*chunk_record_stage_fn)(void* ctx, int64_t s0, int64_t s1, char* recs,
+                                            hipStream_t stream);
+hipError_t launch_chunk_states(const kda_desc_t& d, const float* init_state,
+                               const int32_t* cu_seqlens, void* chunk_states, void* workspace,
+                               chunk_record_stage_fn stage, void* stage_ctx, hipStream_t stream);
 // Chunk slots of a batch (dense: B * ceil(T/64); varlen: an upper bound that
 // does not read cu_seqlens, T/64 + N).
 int64_t chunk_slot_bound(const kda_desc_t& d, bool varlen);
