@@ -46,7 +46,7 @@ sys.path.insert(0, ROOT)
 
 from gated_delta_rule_54_amd import (chunk_bwd_workspace_bytes,  # noqa: E402
                                      chunk_fwd_workspace_bytes, kda_chunk_bwd, kda_chunk_fwd,
-                                     kda_decode_step, kda_output_gate_norm,
+                                     kda_chunk_fwd_conv, kda_decode_step, kda_output_gate_norm,
                                      kda_short_conv_swish, make_desc)
 from gated_delta_rule_54_amd import workloads as W  # noqa: E402
 
@@ -428,6 +428,55 @@ def bench_prologue(steps: int, warmup: int):
     ms = e0.elapsed_time(e1) / steps
     nbytes = x.numel() * PROLOGUE_BYTES_PER_EL
     return dict(ms=ms, achieved_gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
+def bench_prologue_fused(inp, steps: int, warmup: int, rounds: int = 3):
+    """The prologue -> operator chain on the 8K x 32-head prefill workload
+    (its q, k, v taken as the prologue's inputs; seeded width-4 filters,
+    biases and carried states): kda_short_conv_swish on each of q, k, v then
+    kda_chunk_fwd, against kda_chunk_fwd_conv, rounds alternating; best
+    round of each, microseconds per call."""
+    B, T, H, d = inp["q"].shape
+    C = H * d
+    gen = torch.Generator(device="cuda").manual_seed(1011)
+    w = [0.5 * torch.randn(C, 4, generator=gen, device="cuda") for _ in range(3)]
+    b = [0.1 * torch.randn(C, generator=gen, device="cuda") for _ in range(3)]
+    s = [torch.randn(B, C, 3, generator=gen, device="cuda") for _ in range(3)]
+    so = [torch.empty_like(t) for t in s]
+    ys = [torch.empty(B, T, C, dtype=inp["q"].dtype, device="cuda") for _ in range(3)]
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    desc = make_desc(batch=B, num_seqs=B, seqlen=T, heads=H, dk=d, dv=d, dtype=inp["q"].dtype)
+    ws = torch.empty(chunk_fwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def two_step():
+        for i, n in enumerate(("q", "k", "v")):
+            kda_short_conv_swish(inp[n].reshape(B, T, C), w[i], b[i], s[i], state_out=so[i],
+                                 out=ys[i], stream=stream)
+        kda_chunk_fwd(ys[0].reshape(B, T, H, d), ys[1].reshape(B, T, H, d),
+                      ys[2].reshape(B, T, H, d), inp["g"], inp["beta"], inp["init_state"],
+                      out=o, final_state=fs, workspace=ws, stream=stream)
+
+    def fused():
+        kda_chunk_fwd_conv(inp["q"], inp["k"], inp["v"], w, inp["g"], inp["beta"],
+                           inp["init_state"], conv_bias=b, conv_state=s, conv_state_out=so,
+                           out=o, final_state=fs, workspace=ws, stream=stream)
+
+    best = {"two_step": float("inf"), "fused": float("inf")}
+    for _ in range(rounds):
+        for name, run in (("two_step", two_step), ("fused", fused)):
+            for _ in range(warmup):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = _events()
+            e0.record(stream)
+            for _ in range(steps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best[name] = min(best[name], e0.elapsed_time(e1) / steps * 1e3)
+    return best
 
 
 def backward_inputs():
@@ -867,6 +916,7 @@ def main():
     ep = bench_epilogue(args.steps, args.warmup)
     gm = bench_gate_modes()
     pl = bench_prologue(args.steps, args.warmup)
+    pfu = bench_prologue_fused(pf["inp"], args.steps, min(args.warmup, 10))
     progress("epilogue, gate modes, prologue")
     bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 2))
     progress("backward")
@@ -934,6 +984,12 @@ def main():
                                   "traffic": (tr_pro / (pl["ms"] * 1e-3) / 1e9) if tr_pro else None,
                                   "kernel": "short_conv_kernel<bf16,4>",
                                   "bytes_per_element": PROLOGUE_BYTES_PER_EL}},
+        "prologue_fused": {"workload": "ShortConv (width 4) + Swish on q, k, v, then the "
+                                       "prefill (B=1 H=32 T=8192 d=128 bf16): three prologue "
+                                       "calls and kda_chunk_fwd, against kda_chunk_fwd_conv",
+                           "two_step_us_per_call": pfu["two_step"],
+                           "fused_us_per_call": pfu["fused"],
+                           "fused_tokens_per_s": pf["tokens"] / (pfu["fused"] * 1e-6)},
         "backward": {"workload": "gradients of the prefill workload (B=1 H=32 T=8192 "
                                  "d=128 bf16, nonzero initial state, seeded do and d_final): "
                                  "dq, dk, dv, dg, dbeta, d_init",

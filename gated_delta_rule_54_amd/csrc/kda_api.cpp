@@ -167,6 +167,66 @@ KDA_EXPORT kda_status_t kda_chunk_fwd(const kda_desc_t* desc, const void* q, con
   return ok();
 }
 
+KDA_EXPORT kda_status_t kda_chunk_fwd_conv(const kda_desc_t* desc, const void* xq,
+                                           const void* xk, const void* xv,
+                                           const float* const* conv_w,
+                                           const float* const* conv_bias,
+                                           const float* const* conv_state_in,
+                                           float* const* conv_state_out, const float* g,
+                                           const float* beta, const float* init_state,
+                                           const int32_t* cu_seqlens, void* o,
+                                           float* final_state, float* state_ckpt,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  kda_status_t st = check_chunk_fwd_args(desc, xq, xk, xv, g, beta, init_state, cu_seqlens, o,
+                                         final_state, state_ckpt);
+  if (st != KDA_OK) return st;
+  const kda_desc_t& d = *desc;
+  static const char* names[3] = {"q", "k", "v"};
+  const float* w[3] = {nullptr, nullptr, nullptr};
+  const float* bias[3] = {nullptr, nullptr, nullptr};
+  const float* sin[3] = {nullptr, nullptr, nullptr};
+  float* sout[3] = {nullptr, nullptr, nullptr};
+  if (!conv_w) return fail(KDA_ERR_INVALID_ARGUMENT, "conv_w is NULL");
+  const size_t state_bytes = (size_t)d.num_seqs * d.heads * d.dk * 3 * sizeof(float);
+  for (int t = 0; t < 3; ++t) {
+    w[t] = conv_w[t];
+    bias[t] = conv_bias ? conv_bias[t] : nullptr;
+    sin[t] = conv_state_in ? conv_state_in[t] : nullptr;
+    sout[t] = conv_state_out ? conv_state_out[t] : nullptr;
+    if (!w[t]) return fail(KDA_ERR_INVALID_ARGUMENT, "conv_w[%d] (%s) is NULL", t, names[t]);
+    if (!aligned(w[t], 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "conv_w[%d] (%s) is not 16-byte aligned", t, names[t]);
+    const void* al[3] = {bias[t], sin[t], sout[t]};
+    const char* an[3] = {"conv_bias", "conv_state_in", "conv_state_out"};
+    for (int i = 0; i < 3; ++i)
+      if (al[i] && !aligned(al[i], 4))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s[%d] (%s) is not 4-byte aligned", an[i], t,
+                    names[t]);
+    if (sin[t] && sout[t] && (const void*)sout[t] != (const void*)sin[t]) {
+      const char* a = reinterpret_cast<const char*>(sin[t]);
+      const char* b = reinterpret_cast<const char*>(sout[t]);
+      if (a < b + state_bytes && b < a + state_bytes)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "conv_state_out[%d] (%s) overlaps conv_state_in[%d] without being it", t,
+                    names[t], t);
+    }
+  }
+  if (workspace && !aligned(workspace, 16))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+  const size_t need_ws = kda::chunk_workspace_bytes(d);
+  if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu%s", need_ws,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  const void* x[3] = {xq, xk, xv};
+  hipError_t e = kda::launch_chunk_fwd_conv(d, x, w, bias, sin, sout, g, beta, init_state,
+                                            cu_seqlens, o, final_state, state_ckpt, workspace,
+                                            stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_chunk_fwd_conv launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 KDA_EXPORT kda_status_t kda_chunk_fwd_noalloc(const kda_desc_t* desc, const void* q,
                                               const void* k, const void* v, const float* g,
                                               const float* beta, const float* init_state,

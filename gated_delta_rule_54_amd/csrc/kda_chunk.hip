@@ -196,9 +196,9 @@ __device__ __forceinline__ void st2(bf16* p, float a, float b) {
 
 // Waves per SIMD the kernel is built for: three workgroups per CU (LDS
 // allows it) except fp32 at d = 128, whose registers fill a CU alone.
-template <typename T, int D>
+template <typename T, int D, bool CONV = false>
 constexpr int k1_waves_per_simd() {
-  return (sizeof(T) == 4 && D == 128) ? 1 : 3 * k1_threads<T, D>() / 256;
+  return (sizeof(T) == 4 && D == 128) ? 1 : (CONV ? 2 : 3) * k1_threads<T, D>() / 256;
 }
 
 // Exact-decay path of A and P: each entry from its own exponent difference
@@ -394,13 +394,93 @@ __device__ __attribute__((noinline)) void k1_slow_ap(T* r0, T* r1, T* r2, const 
                           s_beta, wP, gb, rowstride, H, len, offx, offy);
 }
 
+// The ShortConv + Swish prologue (width 4) fused into K1's loads: per tensor
+// (q, k, v) its [C, 4] fp32 weights (C = H D), its [C] fp32 bias or null, and
+// the [N, C, 3] fp32 inputs carried in before each sequence (oldest first),
+// or null for zeros.
+struct ConvIn {
+  const float* w[3];
+  const float* bias[3];
+  const float* state[3];
+};
+
+// ShortConv + Swish of the thread's RPP rows of channels c0, c0+1, in the
+// separate prologue kernel's order and arithmetic (so the results are the
+// same bits): a = bias + w3 x_t + w0 x_(t-3) + w1 x_(t-2) + w2 x_(t-1),
+// y = a rcp(1 + e^-a); each loaded pair is replaced by its y in the element
+// type (as that kernel stores y).  win holds the three inputs before the
+// thread's first row; rows from nvalid on (past the chunk's end) give 0.
+template <int RPP, typename Raw>
+__device__ __forceinline__ void conv_swish(Raw (&x)[RPP], float2 (&win)[3], const float4 (&w)[2],
+                                           const float (&b)[2], int nvalid) {
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const float2 xt = x[j].get();
+    float a0 = b[0] + w[0].w * xt.x;
+    a0 += w[0].x * win[0].x;
+    a0 += w[0].y * win[1].x;
+    a0 += w[0].z * win[2].x;
+    float a1 = b[1] + w[1].w * xt.y;
+    a1 += w[1].x * win[0].y;
+    a1 += w[1].y * win[1].y;
+    a1 += w[1].z * win[2].y;
+    float y0 = a0 * __builtin_amdgcn_rcpf(1.f + __expf(-a0));
+    float y1 = a1 * __builtin_amdgcn_rcpf(1.f + __expf(-a1));
+    if (j >= nvalid) {
+      y0 = 0.f;
+      y1 = 0.f;
+    }
+    win[0] = win[1];
+    win[1] = win[2];
+    win[2] = xt;
+    x[j].set(y0, y1);
+  }
+}
+
+// The three input rows before the thread's first (row r0p), channels c0,
+// c0+1, of one fused-prologue tensor: from the rows before the chunk (same
+// sequence) when the chunk is not its sequence's first, else, for the rows
+// before the chunk, from the carried state or zero.  `base` is the chunk's
+// first row of this head; the halo loads go through a resource over the
+// chunk's rows plus the three before it (three rows of a sequence's first
+// chunk lie before the sequence: there the resource starts at the chunk and
+// the rows before it, past its bound, read as zero).
+template <typename T, typename Raw>
+__device__ __forceinline__ void conv_halo_load(Raw (&hal)[3], const T* base, bool first, int span,
+                                               int rs, int r0p, int c0) {
+  const int back = first ? 0 : 3;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(base - back * rs), (short)0, (span + back * rs) * (int)sizeof(T), kRsrcWord3);
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    hal[p].load(r, (uint32_t)(((r0p - 3 + p + back) * rs + c0) * (int)sizeof(T)));
+}
+template <typename Raw>
+__device__ __forceinline__ void conv_window(float2 (&win)[3], const Raw (&hal)[3], bool from_state,
+                                            const float* state, int64_t sidx) {
+#pragma unroll
+  for (int p = 0; p < 3; ++p) win[p] = hal[p].get();
+  if (from_state && state != nullptr) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p) win[p] = make_float2(state[sidx + p], state[sidx + 3 + p]);
+  }
+}
+__device__ __forceinline__ void conv_weights(float4 (&w)[2], float (&b)[2], const float* wt,
+                                             const float* bias, int64_t ch) {
+  w[0] = *reinterpret_cast<const float4*>(wt + ch * 4);
+  w[1] = *reinterpret_cast<const float4*>(wt + (ch + 1) * 4);
+  b[0] = bias ? bias[ch] : 0.f;
+  b[1] = bias ? bias[ch + 1] : 0.f;
+}
+
 // GS: one gate per (token, head), broadcast over the key channels (Gated
-// DeltaNet) instead of one per channel.
-template <typename T, int D, bool GS>
-__global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) void kda_intra_chunk(
+// DeltaNet) instead of one per channel.  CONV: q, k, v are the prologue's
+// inputs, convolved on load (ConvIn).
+template <typename T, int D, bool GS, bool CONV = false>
+__global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV>())) void kda_intra_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
-    int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws) {
+    int64_t slot_base, int64_t nrec, int qk_l2norm, char* __restrict__ ws, ConvIn cv) {
   using L = K1Lds<T, D>;
   using M = Mma<T>;
   using R = Rec<T, D>;
@@ -480,7 +560,26 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
   for (int j = 0; j < RPP; ++j) kraw[j].load(rk, offT + (uint32_t)j * rowT);
 #pragma unroll
   for (int j = 0; j < RPP; ++j) qraw[j].load(rq, offT + (uint32_t)j * rowT);
+  // CONV: the chunk is its sequence's first when it starts the sequence
+  const bool first = CONV && seq_span(gm, loc.seq).tok0 == loc.tok0;
+  const int64_t sidx = ((int64_t)loc.seq * rs + h * D + c0) * 3;  // carried state, channel c0
+  Raw2<T> khal[3], qhal[3];
+  if constexpr (CONV) {
+    conv_halo_load(khal, kb, first, span, rs, r0p, c0);
+    conv_halo_load(qhal, qb, first, span, rs, r0p, c0);
+  }
   if (tid < kC) s_beta[tid] = tid < loc.len ? beta[(loc.tok0 + tid) * H + h] : 0.f;
+  if constexpr (CONV) {
+    float4 w[2];
+    float b[2];
+    float2 win[3];
+    conv_weights(w, b, cv.w[1], cv.bias[1], (int64_t)h * D + c0);
+    conv_window(win, khal, first && r0p == 0, cv.state[1], sidx);
+    conv_swish<RPP>(kraw, win, w, b, loc.len - r0p);
+    conv_weights(w, b, cv.w[0], cv.bias[0], (int64_t)h * D + c0);
+    conv_window(win, qhal, first && r0p == 0, cv.state[0], sidx);
+    conv_swish<RPP>(qraw, win, w, b, loc.len - r0p);
+  }
   float2 G[RPP];
 #pragma unroll
   for (int j = 0; j < RPP; ++j) G[j] = GS ? make_float2(gsc[j], gsc[j]) : graw[j].get();
@@ -606,11 +705,13 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
   // (the exact path loads it after its own A and P).  Its row offsets are
   // formed again: they equal the first loads' and would otherwise be held
   // in registers until now.
+  RawNt2<T> vhal[3];
   auto load_v = [&]() {
     uint32_t ov = offT;
     __asm__ volatile("" : "+v"(ov));
 #pragma unroll
     for (int j = 0; j < RPP; ++j) vraw[j].load(rv, ov + (uint32_t)j * rowT);
+    if constexpr (CONV) conv_halo_load(vhal, vb, first, span, rs, r0p, c0);
   };
   if (!exact) load_v();
 
@@ -706,6 +807,14 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D>())) 
       const int r = zR[z] * 16 + (lane & 15), i0 = zI[z] * 16 + 4 * (lane >> 4);
       st_fnat4(wP, kC / M::KSTEP, r, i0, 0.f, 0.f, 0.f, 0.f);
     }
+  }
+  if constexpr (CONV) {
+    float4 w[2];
+    float b[2];
+    float2 win[3];
+    conv_weights(w, b, cv.w[2], cv.bias[2], (int64_t)h * D + c0);
+    conv_window(win, vhal, first && r0p == 0, cv.state[2], sidx);
+    conv_swish<RPP>(vraw, win, w, b, loc.len - r0p);
   }
   // V^T into region 0 (its row-major content is dead now), 8 rows per store
 #pragma unroll
@@ -1367,7 +1476,7 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
                      const float* g, const float* beta, const float* init_state,
                      const int32_t* cu, void* o, float* final_state, float* ckpt,
                      void* states, char* ws, int64_t SS, chunk_record_stage_fn stage,
-                     void* stage_ctx, hipStream_t stream) {
+                     void* stage_ctx, const ConvIn* conv, hipStream_t stream) {
   const bool varlen = cu != nullptr;
   const Plan p = make_plan(d, varlen, SS);
   const int H = d.heads, NH = d.num_seqs * d.heads;
@@ -1390,7 +1499,9 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
   static std::atomic<uint64_t> attr_done{0};
   hipError_t ea = once_per_device(attr_done, [&]() {
     for (const void* fn : {(const void*)kda_intra_chunk<T, D, false>,
-                           (const void*)kda_intra_chunk<T, D, true>}) {
+                           (const void*)kda_intra_chunk<T, D, true>,
+                           (const void*)kda_intra_chunk<T, D, false, true>,
+                           (const void*)kda_intra_chunk<T, D, true, true>}) {
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, k1_lds);
       if (e != hipSuccess) return e;
     }
@@ -1412,10 +1523,13 @@ hipError_t run_typed(const kda_desc_t& d, const void* q, const void* k, const vo
       if (es != hipSuccess) return es;
     } else if (s1 > s0) {
       if (o == nullptr) return hipErrorInvalidValue;  // a states-only pass takes a stage
-      auto k1 = d.gate_per_head ? kda_intra_chunk<T, D, true> : kda_intra_chunk<T, D, false>;
+      auto k1 = conv != nullptr
+                    ? (d.gate_per_head ? kda_intra_chunk<T, D, true, true>
+                                       : kda_intra_chunk<T, D, false, true>)
+                    : (d.gate_per_head ? kda_intra_chunk<T, D, true> : kda_intra_chunk<T, D, false>);
       hipLaunchKernelGGL(k1, dim3(H, (unsigned)(s1 - s0)), dim3(k1_threads<T, D>()), k1_lds,
                          stream, (const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, s0,
-                         s1 - s0, d.qk_l2norm, recs);
+                         s1 - s0, d.qk_l2norm, recs, conv != nullptr ? *conv : ConvIn{});
     }
     auto k2 = o ? kda_state_pass<T, D, WS, true> : kda_state_pass<T, D, WS, false>;
     hipLaunchKernelGGL(k2, dim3(nhpad * nslice), dim3(k2_threads<T>()), 0,
@@ -1440,20 +1554,22 @@ hipError_t launch_with(const kda_desc_t& d, const void* q, const void* k, const 
                        const float* g, const float* beta, const float* init_state,
                        const int32_t* cu_seqlens, void* o, float* final_state, float* state_ckpt,
                        void* chunk_states, char* ws, int64_t ss, hipStream_t stream,
-                       chunk_record_stage_fn stage = nullptr, void* stage_ctx = nullptr) {
+                       chunk_record_stage_fn stage = nullptr, void* stage_ctx = nullptr,
+                       const ConvIn* conv = nullptr) {
   const bool bf = d.dtype == KDA_DTYPE_BF16;
   if (d.dk == 128)
     return bf ? run_typed<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
                                      final_state, state_ckpt, chunk_states, ws, ss, stage,
-                                     stage_ctx, stream)
+                                     stage_ctx, conv, stream)
               : run_typed<float, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
                                       final_state, state_ckpt, chunk_states, ws, ss, stage,
-                                      stage_ctx, stream);
+                                      stage_ctx, conv, stream);
   return bf ? run_typed<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o, final_state,
-                                  state_ckpt, chunk_states, ws, ss, stage, stage_ctx, stream)
+                                  state_ckpt, chunk_states, ws, ss, stage, stage_ctx, conv,
+                                  stream)
             : run_typed<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, o,
                                    final_state, state_ckpt, chunk_states, ws, ss, stage,
-                                   stage_ctx, stream);
+                                   stage_ctx, conv, stream);
 }
 }  // namespace
 
@@ -1474,6 +1590,30 @@ hipError_t launch_chunk_states(const kda_desc_t& d, const float* init_state,
   return launch_with(d, nullptr, nullptr, nullptr, nullptr, nullptr, init_state, cu_seqlens,
                      nullptr, nullptr, nullptr, chunk_states, static_cast<char*>(workspace),
                      seg_slots(d), stream, stage, stage_ctx);
+}
+
+hipError_t launch_chunk_fwd_conv(const kda_desc_t& d, const void* const x[3],
+                                 const float* const w[3], const float* const bias[3],
+                                 const float* const state_in[3], float* const state_out[3],
+                                 const float* g, const float* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state,
+                                 float* state_ckpt, void* workspace, hipStream_t stream) {
+  const ConvIn conv{{w[0], w[1], w[2]}, {bias[0], bias[1], bias[2]},
+                    {state_in[0], state_in[1], state_in[2]}};
+  hipError_t e = launch_with(d, x[0], x[1], x[2], g, beta, init_state, cu_seqlens, o, final_state,
+                             state_ckpt, nullptr, static_cast<char*>(workspace), seg_slots(d),
+                             stream, nullptr, nullptr, &conv);
+  if (e != hipSuccess) return e;
+  // the carried-out inputs, after every read of the carried-in ones (they
+  // may be the same arrays)
+  const int32_t C = d.heads * d.dk;
+  for (int t = 0; t < 3; ++t) {
+    if (state_out[t] == nullptr) continue;
+    e = launch_conv_state_out(d.seqlen, d.num_seqs, C, d.dtype, x[t], state_in[t], cu_seqlens,
+                              state_out[t], stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -235,7 +235,6 @@ __device__ __forceinline__ void st_nt(float* p, float x) { __builtin_nontemporal
 // st_fnat4 with non-temporal stores: the reverse pass's records are read once,
 // after the forward pass, and allocated in the last-level cache they would
 // push out the state pass's records that the forward reads next.
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st_fnat4_nt(bf16* base, int nks, int m, int k0, float a, float b,
                                             float c, float d) {
   __builtin_nontemporal_store(u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)},

@@ -98,6 +98,7 @@ template <> struct Raw2<float> {
     v = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
   }
   __device__ __forceinline__ float2 get() const { return v; }
+  __device__ __forceinline__ void set(float a, float b) { v = make_float2(a, b); }
 };
 template <> struct Raw2<bf16> {
   uint32_t v;
@@ -106,6 +107,8 @@ template <> struct Raw2<bf16> {
     v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
   __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
+  // two values rounded to bf16 (nearest even) in place of the loaded pair
+  __device__ __forceinline__ void set(float a, float b) { v = pack_bf16x2(a, b); }
 };
 // Two consecutive elements as raw bits through a non-temporal load: for
 // inputs read once, so that they do not displace data that is read again
@@ -121,6 +124,7 @@ template <> struct RawNt2<float> {
     v = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
   }
   __device__ __forceinline__ float2 get() const { return make_float2(v[0], v[1]); }
+  __device__ __forceinline__ void set(float a, float b) { v = f32x2_t{a, b}; }
 };
 template <> struct RawNt2<bf16> {
   uint32_t v;
@@ -131,6 +135,7 @@ template <> struct RawNt2<bf16> {
     v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2);
   }
   __device__ __forceinline__ float2 get() const { return make_float2(bf_val(v & 0xffffu), bf_val(v >> 16)); }
+  __device__ __forceinline__ void set(float a, float b) { v = pack_bf16x2(a, b); }
 };
 // Load N consecutive elements (16-byte aligned, N a multiple of 8) as floats.
 template <int N>

@@ -274,6 +274,54 @@ hipError_t launch_t(const kda_conv_args& a, hipStream_t stream) {
 
 }  // namespace
 
+// The inputs each sequence carries out when the prologue is fused into the
+// operator (kda_chunk_fwd_conv, width 4): state_out[n, c, i] = x~[len_n + i],
+// i < 3, where x~ is sequence n's input preceded by state_in[n, c, :] (or
+// zeros) -- what the prologue kernel's carried window ends with.  One thread
+// per (sequence, channel); its reads come before its writes, so state_out
+// may be state_in.
+template <typename T>
+__global__ void conv_state_out_kernel(const T* __restrict__ x, const float* state_in,
+                                      const int32_t* __restrict__ cu, int64_t T_, int N, int C,
+                                      float* state_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)N * C) return;
+  const int n = (int)(i / C), c = (int)(i % C);
+  int64_t tok0 = (int64_t)n * T_, len = T_;
+  if (cu != nullptr) {
+    // clamped as in the prologue kernel: offsets not checked on the host
+    // cannot move a read outside [0, T)
+    tok0 = min(max((int64_t)cu[n], (int64_t)0), T_);
+    len = max(min((int64_t)cu[n + 1], T_) - tok0, (int64_t)0);
+  }
+  float s[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int64_t t = len + j;  // index into x~ (its first three entries carried in)
+    s[j] = t < 3 ? (state_in ? state_in[i * 3 + t] : 0.f)
+                 : static_cast<float>(x[(tok0 + t - 3) * C + c]);
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) state_out[i * 3 + j] = s[j];
+}
+
+hipError_t launch_conv_state_out(int64_t seqlen, int32_t num_seqs, int32_t channels,
+                                 int32_t dtype, const void* x, const float* state_in,
+                                 const int32_t* cu, float* state_out, hipStream_t stream) {
+  const int64_t n = (int64_t)num_seqs * channels;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (dtype == KDA_DTYPE_BF16)
+    hipLaunchKernelGGL(conv_state_out_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const __hip_bfloat16*>(x), state_in, cu, seqlen, num_seqs,
+                       channels, state_out);
+  else
+    hipLaunchKernelGGL(conv_state_out_kernel<float>, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const float*>(x), state_in, cu, seqlen, num_seqs, channels,
+                       state_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_short_conv(const kda_conv_args& a, hipStream_t stream) {
   return a.dtype == KDA_DTYPE_BF16 ? launch_t<__hip_bfloat16>(a, stream)
                                    : launch_t<float>(a, stream);

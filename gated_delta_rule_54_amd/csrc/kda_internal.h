@@ -70,6 +70,24 @@ hipError_t launch_chunk_fwd_noalloc(const kda_desc_t& d, const void* q, const vo
                                     const float* init_state, const int32_t* cu_seqlens, void* o,
                                     float* final_state, float* state_ckpt, hipStream_t stream);
 
+// Prefill with the ShortConv + Swish prologue (width 4) fused into the
+// intra-chunk kernel's loads: x[t] are the prologue inputs of q, k, v
+// ([B, T, H, d] as q, k, v are for launch_chunk_fwd); w, bias, state_in,
+// state_out per tensor as for launch_short_conv at width 4 (C = H d).  The
+// workspace is launch_chunk_fwd's.  Shapes are validated by the caller.
+hipError_t launch_chunk_fwd_conv(const kda_desc_t& d, const void* const x[3],
+                                 const float* const w[3], const float* const bias[3],
+                                 const float* const state_in[3], float* const state_out[3],
+                                 const float* g, const float* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state,
+                                 float* state_ckpt, void* workspace, hipStream_t stream);
+// The carried-out prologue inputs of width 4 (kda_conv.hip): state_out[n, c, :]
+// = the last 3 entries of sequence n's input preceded by state_in[n, c, :]
+// (or zeros); x is [B, T, C] (dense, B = num_seqs) or packed (cu != null).
+hipError_t launch_conv_state_out(int64_t seqlen, int32_t num_seqs, int32_t channels,
+                                 int32_t dtype, const void* x, const float* state_in,
+                                 const int32_t* cu, float* state_out, hipStream_t stream);
+
 // Chunkwise backward (kda_chunk_bwd.hip).
 size_t chunk_bwd_workspace_bytes(const kda_desc_t& d);
 hipError_t launch_chunk_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,

@@ -31,6 +31,7 @@ KDA_DTYPE_BF16 = 1
 
 # Names every build of the library must export (the declarations of kda.h).
 EXPORTED = ("kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
+            "kda_chunk_fwd_conv",
             "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_decode_step",
             "kda_output_gate_norm", "kda_short_conv_swish", "kda_status_string",
@@ -82,6 +83,9 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_chunk_fwd_noalloc.restype = i32
+    lib.kda_chunk_fwd_conv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, sz, vp]
+    lib.kda_chunk_fwd_conv.restype = i32
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [dp]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 16 + [sz, vp]
@@ -233,6 +237,95 @@ def kda_chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, qk_l2no
                            _stream_handle(stream, dev))
     _check(lib, st, "kda_chunk_fwd")
     return out, final_state, state_ckpt
+
+
+def _ptr3(ts):
+    """Three optional tensors as a C array of three pointers (None: NULL array)."""
+    if ts is None:
+        return None
+    return (ctypes.c_void_p * 3)(*[None if t is None else t.data_ptr() for t in ts])
+
+
+@_stream_scoped
+def kda_chunk_fwd_conv(xq, xk, xv, conv_w, g, beta, init_state=None, cu_seqlens=None, *,
+                       conv_bias=None, conv_state=None, conv_state_out=None,
+                       want_conv_state=True, qk_l2norm=True, scale=1.0, ckpt_every=0, out=None,
+                       final_state=None, want_final=True, state_ckpt=None, workspace=None,
+                       stream=None):
+    """Prefill with the ShortConv + Swish prologue (width 4) fused into the
+    operator, through the C ABI (kda_chunk_fwd_conv).
+
+    xq, xk, xv: the prologue's inputs, shaped as q, k, v of kda_chunk_fwd;
+    conv_w: three [H*dk, 4] fp32 filters (q, k, v); conv_bias: None or three
+    [H*dk] fp32 tensors or Nones; conv_state: None or three [N, H*dk, 3] fp32
+    carried-in inputs or Nones (zeros); conv_state_out: None or three tensors
+    (each may be the matching conv_state).  Other arguments as for
+    kda_chunk_fwd.  Returns (o, final_state, state_ckpt, conv_state_out),
+    conv_state_out a list of three [N, H*dk, 3] tensors (None when
+    want_conv_state is False and none were passed).
+    """
+    lib = load_library()
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    dt = xq.dtype
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    C = H * dk
+    _need(xq, "xq", dt, (B, T, H, dk))
+    _need(xk, "xk", dt, (B, T, H, dk))
+    _need(xv, "xv", dt, (B, T, H, dv))
+    per_head = g.dim() == 3
+    _need(g, "g", torch.float32, (B, T, H) if per_head else (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if len(conv_w) != 3:
+        raise ValueError("conv_w: one filter tensor per q, k, v")
+    for i, w in enumerate(conv_w):
+        _need(w, f"conv_w[{i}]", torch.float32, (C, 4))
+    if conv_bias is not None:
+        for i, b in enumerate(conv_bias):
+            if b is not None:
+                _need(b, f"conv_bias[{i}]", torch.float32, (C,))
+    if conv_state is not None:
+        for i, st in enumerate(conv_state):
+            if st is not None:
+                _need(st, f"conv_state[{i}]", torch.float32, (N, C, 3))
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (N, H, dk, dv))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    dev = xq.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _need(out, "out", dt, (B, T, H, dv))
+    if final_state is None and want_final:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    if ckpt_every and state_ckpt is None:
+        state_ckpt = torch.empty((B, T // ckpt_every, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_state_out is None and want_conv_state:
+        conv_state_out = [torch.empty((N, C, 3), dtype=torch.float32, device=dev)
+                          for _ in range(3)]
+    if conv_state_out is not None:
+        for i, st in enumerate(conv_state_out):
+            if st is not None:
+                _need(st, f"conv_state_out[{i}]", torch.float32, (N, C, 3))
+    desc = make_desc(batch=B, num_seqs=N, seqlen=T, heads=H, dk=dk, dv=dv, dtype=dt,
+                     qk_l2norm=qk_l2norm, scale=scale, ckpt_every=ckpt_every,
+                     gate_per_head=per_head)
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
+    if ws_bytes == 0 and lib.kda_last_error():
+        _check(lib, KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_workspace_bytes")
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_fwd_conv(ctypes.byref(desc), _ptr(xq), _ptr(xk), _ptr(xv),
+                                _ptr3(conv_w), _ptr3(conv_bias), _ptr3(conv_state),
+                                _ptr3(conv_state_out), _ptr(g), _ptr(beta), _ptr(init_state),
+                                _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _ptr(state_ckpt),
+                                _ptr(workspace),
+                                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream_handle(stream, dev))
+    _check(lib, st, "kda_chunk_fwd_conv")
+    return out, final_state, state_ckpt, conv_state_out
 
 
 def chunk_bwd_workspace_bytes(desc: KdaDesc) -> int:

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -159,6 +159,41 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_desc_t* desc, const void* q, const 
                                    const void* v, const float* g, const float* beta,
                                    const float* init_state, const int32_t* cu_seqlens, void* o,
                                    float* final_state, float* state_ckpt, hipStream_t stream);
+
+/* Prefill with the ShortConv + Swish prologue fused into the operator's
+ * loads.  [XT §6 layer diagram: the q, k, v projections pass ShortConv ->
+ * Swish before the operator; XT §6.1; XD preprocessing list.]  The results
+ * (o, final_state, state_ckpt, conv_state_out) are bitwise those of
+ * kda_short_conv_swish at width 4 on each of xq, xk, xv followed by
+ * kda_chunk_fwd on its three outputs; the prologue's outputs never go
+ * through memory.  The filter width is 4 (every workload's); for another
+ * width call the two steps.
+ *   desc, g, beta, init_state, cu_seqlens, o, final_state, state_ckpt,
+ *   workspace, workspace_bytes: as for kda_chunk_fwd (the same workspace
+ *              size, kda_chunk_fwd_workspace_bytes)
+ *   xq, xk, xv the prologue's inputs, each laid out as q / k / v of
+ *              kda_chunk_fwd ([B, T, H, dk], dtype, 16-byte aligned), so a
+ *              token row is the prologue's C = H * dk channels
+ *   conv_w     3 pointers (q, k, v), each [C, 4] fp32, 16-byte aligned: the
+ *              filters of kda_short_conv_swish
+ *   conv_bias  NULL, or 3 pointers, each [C] fp32 or NULL (no bias)
+ *   conv_state_in   NULL, or 3 pointers, each [N, C, 3] fp32 (the inputs
+ *              before each sequence, oldest first) or NULL (zeros)
+ *   conv_state_out  NULL, or 3 pointers, each [N, C, 3] fp32 or NULL: the
+ *              last 3 inputs of each sequence, preceded by its carried-in
+ *              ones (what decode continues from); each may equal the
+ *              matching conv_state_in, and must not otherwise overlap it.
+ * o must not alias xq, xk or xv.  Asynchronous on `stream`; on a validation
+ * error nothing is launched.  Not for the backward: kda_chunk_bwd takes the
+ * prologue's outputs q, k, v. */
+kda_status_t kda_chunk_fwd_conv(const kda_desc_t* desc, const void* xq, const void* xk,
+                                const void* xv, const float* const* conv_w,
+                                const float* const* conv_bias,
+                                const float* const* conv_state_in, float* const* conv_state_out,
+                                const float* g, const float* beta, const float* init_state,
+                                const int32_t* cu_seqlens, void* o, float* final_state,
+                                float* state_ckpt, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Bytes of device workspace kda_chunk_bwd needs for this descriptor (an upper
  * bound that does not read cu_seqlens); 0 for an invalid or unsupported

@@ -30,7 +30,7 @@ def test_exports_match_header():
 
 def test_abi_version_and_strings():
     lib = K.load_library()
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
     assert lib.kda_status_string(99) == b"KDA_STATUS_UNKNOWN"
@@ -97,6 +97,33 @@ def test_chunk_pointer_errors():
     assert _call_chunk(_desc(batch=2, num_seqs=3), cu=FAKE) == B.KDA_ERR_INVALID_ARGUMENT
     assert _call_chunk(_desc(num_seqs=3, ckpt_every=64), cu=FAKE, ckpt=FAKE) == \
         B.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_chunk_fwd_conv_errors():
+    """The fused prologue entry point: the prefill's checks, then its own."""
+    lib = K.load_library()
+    desc = _desc()
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc))
+    arr = lambda *a: (ctypes.c_void_p * 3)(*a)
+    w_ok = arr(FAKE, FAKE + 0x40, FAKE + 0x80)
+
+    def call(*, x=FAKE, w=w_ok, bias=None, sin=None, sout=None, o=FAKE + 0x100, ws_bytes=need,
+             d=desc):
+        return lib.kda_chunk_fwd_conv(ctypes.byref(d), x, FAKE, FAKE, w, bias, sin, sout, FAKE,
+                                      FAKE, None, None, o, None, None, FAKE, ws_bytes, None)
+
+    assert call(x=None) == B.KDA_ERR_INVALID_ARGUMENT                       # xq NULL
+    assert call(o=FAKE) == B.KDA_ERR_INVALID_ARGUMENT                       # o aliases xq
+    assert call(d=_desc(dk=96, dv=96)) == B.KDA_ERR_UNSUPPORTED
+    assert call(w=None) == B.KDA_ERR_INVALID_ARGUMENT                       # no filter array
+    assert call(w=arr(FAKE, None, FAKE)) == B.KDA_ERR_INVALID_ARGUMENT      # k's filter NULL
+    assert call(w=arr(FAKE, FAKE + 8, FAKE)) == B.KDA_ERR_INVALID_ARGUMENT  # not 16-byte aligned
+    assert call(bias=arr(None, FAKE + 2, None)) == B.KDA_ERR_INVALID_ARGUMENT
+    assert call(sin=arr(FAKE + 1, None, None)) == B.KDA_ERR_INVALID_ARGUMENT
+    # carried-out inputs overlapping the carried-in ones without being them
+    assert call(sin=arr(FAKE, None, None), sout=arr(FAKE + 4, None, None)) == \
+        B.KDA_ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=16) == B.KDA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_workspace_sizes():
