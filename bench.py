@@ -307,13 +307,17 @@ def write_counters(csvs, out: str = COUNTER_FILE, command: str = "") -> str:
 KERNEL_STATS_FILE = os.path.join(ROOT, "profiles", "kda_prefill_8k_decode_256x32_kernel_stats.md")
 # (kernel-name fragment, template arguments shown, workload, from the trace?)
 _STATS_ROWS = (
-    ("kda_intra_chunk<__hip_bfloat16, 128, false>", "kda_intra_chunk<bf16, 128, false>",
+    ("kda_intra_chunk<__hip_bfloat16, 128, false, false>", "kda_intra_chunk<bf16, 128, false, false>",
      "prefill 8K, 20 timed calls (trace)", True),
     ("kda_state_pass<__hip_bfloat16, 128, 16, true>", "kda_state_pass<bf16, 128, 16, true>",
      "prefill 8K, 20 timed calls (trace)", True),
     ("decode_step_kernel<__hip_bfloat16, 128>", "decode_step_kernel<bf16, 128>", "decode (stats)", False),
     ("gate_norm_kernel<__hip_bfloat16, 128>", "gate_norm_kernel<bf16, 128>", "epilogue (stats)", False),
     ("short_conv_kernel<__hip_bfloat16, 4>", "short_conv_kernel<bf16, 4>", "prologue (stats)", False),
+    ("kda_intra_chunk<__hip_bfloat16, 128, false, true>", "kda_intra_chunk<bf16, 128, false, true>",
+     "prefill with the prologue fused, per segment (stats)", False),
+    ("conv_state_out_kernel<__hip_bfloat16>", "conv_state_out_kernel<bf16>",
+     "prefill with the prologue fused, carried-out inputs (stats)", False),
     ("kda_bwd_prep<__hip_bfloat16, 128, false>", "kda_bwd_prep<bf16, 128, false>",
      "backward, per segment (stats)", False),
     ("kda_state_pass<__hip_bfloat16, 128, 16, false>", "kda_state_pass<bf16, 128, 16, false>",

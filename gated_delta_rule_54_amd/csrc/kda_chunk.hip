@@ -1606,14 +1606,8 @@ hipError_t launch_chunk_fwd_conv(const kda_desc_t& d, const void* const x[3],
   if (e != hipSuccess) return e;
   // the carried-out inputs, after every read of the carried-in ones (they
   // may be the same arrays)
-  const int32_t C = d.heads * d.dk;
-  for (int t = 0; t < 3; ++t) {
-    if (state_out[t] == nullptr) continue;
-    e = launch_conv_state_out(d.seqlen, d.num_seqs, C, d.dtype, x[t], state_in[t], cu_seqlens,
-                              state_out[t], stream);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return launch_conv_state_out(d.seqlen, d.num_seqs, d.heads * d.dk, d.dtype, x, state_in,
+                               state_out, cu_seqlens, stream);
 }
 
 // ---------------------------------------------------------------------------

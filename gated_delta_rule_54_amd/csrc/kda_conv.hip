@@ -272,18 +272,26 @@ hipError_t launch_t(const kda_conv_args& a, hipStream_t stream) {
   }
 }
 
-}  // namespace
-
 // The inputs each sequence carries out when the prologue is fused into the
 // operator (kda_chunk_fwd_conv, width 4): state_out[n, c, i] = x~[len_n + i],
 // i < 3, where x~ is sequence n's input preceded by state_in[n, c, :] (or
 // zeros) -- what the prologue kernel's carried window ends with.  One thread
-// per (sequence, channel); its reads come before its writes, so state_out
-// may be state_in.
+// per (sequence, channel), grid y = the tensor (q, k, v; one launch for the
+// three); its reads come before its writes, so state_out may be state_in.
+struct ConvStateOut {
+  const void* x[3];
+  const float* state_in[3];
+  float* state_out[3];
+};
+
 template <typename T>
-__global__ void conv_state_out_kernel(const T* __restrict__ x, const float* state_in,
-                                      const int32_t* __restrict__ cu, int64_t T_, int N, int C,
-                                      float* state_out) {
+__global__ void conv_state_out_kernel(ConvStateOut a, const int32_t* __restrict__ cu, int64_t T_,
+                                      int N, int C) {
+  const int t = blockIdx.y;
+  float* state_out = a.state_out[t];
+  if (state_out == nullptr) return;
+  const T* __restrict__ x = static_cast<const T*>(a.x[t]);
+  const float* state_in = a.state_in[t];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)N * C) return;
   const int n = (int)(i / C), c = (int)(i % C);
@@ -297,28 +305,32 @@ __global__ void conv_state_out_kernel(const T* __restrict__ x, const float* stat
   float s[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const int64_t t = len + j;  // index into x~ (its first three entries carried in)
-    s[j] = t < 3 ? (state_in ? state_in[i * 3 + t] : 0.f)
-                 : static_cast<float>(x[(tok0 + t - 3) * C + c]);
+    const int64_t u = len + j;  // index into x~ (its first three entries carried in)
+    s[j] = u < 3 ? (state_in ? state_in[i * 3 + u] : 0.f)
+                 : static_cast<float>(x[(tok0 + u - 3) * C + c]);
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j) state_out[i * 3 + j] = s[j];
 }
 
+}  // namespace
+
 hipError_t launch_conv_state_out(int64_t seqlen, int32_t num_seqs, int32_t channels,
-                                 int32_t dtype, const void* x, const float* state_in,
-                                 const int32_t* cu, float* state_out, hipStream_t stream) {
+                                 int32_t dtype, const void* const x[3],
+                                 const float* const state_in[3], float* const state_out[3],
+                                 const int32_t* cu, hipStream_t stream) {
   const int64_t n = (int64_t)num_seqs * channels;
-  if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (n == 0 || (!state_out[0] && !state_out[1] && !state_out[2])) return hipSuccess;
+  const ConvStateOut a{{x[0], x[1], x[2]},
+                       {state_in[0], state_in[1], state_in[2]},
+                       {state_out[0], state_out[1], state_out[2]}};
+  const dim3 grid((unsigned)((n + 255) / 256), 3);
   if (dtype == KDA_DTYPE_BF16)
-    hipLaunchKernelGGL(conv_state_out_kernel<__hip_bfloat16>, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const __hip_bfloat16*>(x), state_in, cu, seqlen, num_seqs,
-                       channels, state_out);
+    hipLaunchKernelGGL(conv_state_out_kernel<__hip_bfloat16>, grid, dim3(256), 0, stream, a, cu,
+                       seqlen, num_seqs, channels);
   else
-    hipLaunchKernelGGL(conv_state_out_kernel<float>, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const float*>(x), state_in, cu, seqlen, num_seqs, channels,
-                       state_out);
+    hipLaunchKernelGGL(conv_state_out_kernel<float>, grid, dim3(256), 0, stream, a, cu, seqlen,
+                       num_seqs, channels);
   return hipGetLastError();
 }
 

@@ -81,12 +81,14 @@ hipError_t launch_chunk_fwd_conv(const kda_desc_t& d, const void* const x[3],
                                  const float* g, const float* beta, const float* init_state,
                                  const int32_t* cu_seqlens, void* o, float* final_state,
                                  float* state_ckpt, void* workspace, hipStream_t stream);
-// The carried-out prologue inputs of width 4 (kda_conv.hip): state_out[n, c, :]
-// = the last 3 entries of sequence n's input preceded by state_in[n, c, :]
-// (or zeros); x is [B, T, C] (dense, B = num_seqs) or packed (cu != null).
+// The carried-out prologue inputs of width 4 (kda_conv.hip), for each of
+// three tensors whose state_out is not null: state_out[n, c, :] = the last 3
+// entries of sequence n's input preceded by state_in[n, c, :] (or zeros); x
+// is [B, T, C] (dense, B = num_seqs) or packed (cu != null).  One launch.
 hipError_t launch_conv_state_out(int64_t seqlen, int32_t num_seqs, int32_t channels,
-                                 int32_t dtype, const void* x, const float* state_in,
-                                 const int32_t* cu, float* state_out, hipStream_t stream);
+                                 int32_t dtype, const void* const x[3],
+                                 const float* const state_in[3], float* const state_out[3],
+                                 const int32_t* cu, hipStream_t stream);
 
 // Chunkwise backward (kda_chunk_bwd.hip).
 size_t chunk_bwd_workspace_bytes(const kda_desc_t& d);
