@@ -49,9 +49,13 @@ def _fused(inp, w, b, s, **kw):
                               **kw)
 
 
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
 def _assert_same(name, a, b):
-    assert a.shape == b.shape, (name, a.shape, b.shape)
-    same = torch.equal(a, b)
+    assert a.shape == b.shape and a.dtype == b.dtype, (name, a.shape, b.shape)
+    same = torch.equal(_bits(a), _bits(b))  # the same bits, NaN patterns included
     if not same:
         diff = (a.float() - b.float()).abs().max().item()
         raise AssertionError(f"{name}: not bitwise equal to the two-step path (max diff {diff})")
@@ -65,6 +69,7 @@ CASES = [
     ("f32-d64-dense", torch.float32, 64, (1, 200), False, True, True),
     ("bf16-d128-varlen-short", torch.bfloat16, 128, [0, 2, 70, 1, 64, 3, 200], False, True, True),
     ("bf16-d64-pergate-varlen", torch.bfloat16, 64, [5, 0, 129], True, True, False),
+    ("f32-d128-dense", torch.float32, 128, (1, 100), False, True, True),
 ]
 
 
@@ -90,6 +95,29 @@ def test_fused_matches_two_steps(case):
     _assert_same("final_state", fs1, fs2)
     for i in range(3):
         _assert_same(f"conv_state_out[{'qkv'[i]}]", so1[i], so2[i])
+
+
+def test_fused_without_norm_with_scale():
+    """qk_l2norm off and a query scale: the same options reach both paths.
+    Small filters keep the unnormalised keys short (|k| < 1), so the
+    recurrence stays bounded."""
+    H, d, T = 2, 64, 150
+    inp = W.prefill_inputs(batch=1, seqlen=T, heads=H, dk=d, dv=d, dtype=torch.bfloat16,
+                           device=DEV, seed=768, init="normal")
+    w, b, s = _conv_params(H * d, 1, 769)
+    w = [0.1 * t for t in w]
+    b = [0.1 * t for t in b]
+    ys = []
+    for i, name in enumerate(("q", "k", "v")):
+        y, _ = kda_short_conv_swish(inp[name].reshape(1, T, H * d), w[i], b[i], s[i])
+        ys.append(y.reshape(1, T, H, d))
+    o2, fs2, _ = kda_chunk_fwd(ys[0], ys[1], ys[2], inp["g"], inp["beta"], inp["init_state"],
+                               qk_l2norm=False, scale=0.5)
+    o1, fs1, _, _ = _fused(inp, w, b, s, qk_l2norm=False, scale=0.5)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o2).all()), "the recurrence diverged: inputs too large"
+    _assert_same("o", o1, o2)
+    _assert_same("final_state", fs1, fs2)
 
 
 def test_fused_conv_state_in_place_and_checkpoints():
