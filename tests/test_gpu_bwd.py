@@ -241,13 +241,16 @@ def test_bwd_strong_gates_per_head():
     _run(inp, _up(inp, 46), torch.bfloat16, label="gate per head, strong", per_head=True)
 
 
-def test_bwd_beyond_the_mid_reference_is_nan():
+@pytest.mark.parametrize("dt,d", [(torch.float32, 64), (torch.bfloat16, 128)],
+                         ids=["f32-d64", "bf16-d128"])
+def test_bwd_beyond_the_mid_reference_is_nan(dt, d):
     """A chunk one half of which decays by more than 80 in some channel (here
     five tokens at g = -30 in chunk 1): its tokens' gradients are NaN; the NaN
     state gradient reaches the k, v, g, beta gradients of every earlier token
     and d_init, while dq of earlier tokens (q only reads the state) and every
-    gradient of later tokens match the oracle."""
-    inp = _inputs(1, 300, 2, 64, torch.float32, seed=47)
+    gradient of later tokens match the oracle (the forward states past the
+    chunk come from its exactly formed A)."""
+    inp = _inputs(1, 300, 2, d, dt, seed=47)
     inp["g"][:, 70:75] = -30.0
     up = _up(inp, 48)
     B, T, H, d = inp["q"].shape
@@ -261,7 +264,7 @@ def test_bwd_beyond_the_mid_reference_is_nan():
         nan_from = 64 if name == "dq" else 0
         assert bool((~torch.isfinite(a[:, nan_from:128].float())).all()), \
             f"{name}: tokens {nan_from}..127 not NaN"
-        assert_close(f"{name} (tokens >= 128)", a[:, 128:], b[:, 128:], TOL[torch.float32])
+        assert_close(f"{name} (tokens >= 128)", a[:, 128:], b[:, 128:], TOL[dt])
         if name == "dq":
-            assert_close("dq (tokens < 64)", a[:, :64], b[:, :64], TOL[torch.float32])
+            assert_close("dq (tokens < 64)", a[:, :64], b[:, :64], TOL[dt])
     assert bool((~torch.isfinite(got[5])).all()), "d_init not NaN"
