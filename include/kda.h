@@ -182,7 +182,8 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_desc_t* desc, const void* q, const 
  *   conv_state_out  NULL, or 3 pointers, each [N, C, 3] fp32 or NULL: the
  *              last 3 inputs of each sequence, preceded by its carried-in
  *              ones (what decode continues from); each may equal the
- *              matching conv_state_in, and must not otherwise overlap it.
+ *              matching conv_state_in (only that overlap is checked) and must
+ *              not otherwise overlap it or any other argument.
  * o must not alias xq, xk or xv.  Asynchronous on `stream`; on a validation
  * error nothing is launched.  Not for the backward: kda_chunk_bwd takes the
  * prologue's outputs q, k, v. */
