@@ -341,13 +341,16 @@ def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_F
     def short(name):
         return name.replace("void kda::(anonymous namespace)::", "").split("(")[0]
 
+    # the commands that produced the two files (rocprofv3 names them after
+    # the -o prefix inside the -d directory)
+    out_dir = os.path.relpath(os.path.dirname(os.path.abspath(trace_csv)), ROOT)
     lines = ["# rocprofv3 kernel stats: prefill 8K x 32 heads, decode 256 x 32 heads, "
              "epilogue, prologue, backward", "",
              "Command (run from the repository root on one MI355X), then the summary:", "",
-             "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench "
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d {out_dir} "
              "-o bench -- python3 bench.py --no-cpu-baseline",
-             "    python3 bench.py --write-kernel-stats gpurun_out/prof_bench/bench_kernel_trace.csv "
-             "gpurun_out/prof_bench/bench_kernel_stats.csv", "",
+             f"    python3 bench.py --write-kernel-stats {os.path.relpath(trace_csv, ROOT)} "
+             f"{os.path.relpath(stats_csv, ROOT)}", "",
              f"Kernel durations (ns). Prefill rows: the dispatches of the {steps} timed calls "
              f"(after {warmup} warm-up calls, two segments per call) from the trace; the other "
              "rows pool every call of the kernel in the run (stats file).", "",
