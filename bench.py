@@ -925,7 +925,7 @@ def main():
     pl = bench_prologue(args.steps, args.warmup)
     pfu = bench_prologue_fused(pf["inp"], args.steps, min(args.warmup, 10))
     progress("epilogue, gate modes, prologue")
-    bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 2))
+    bw = bench_backward(max(1, args.steps // 2), min(args.warmup, 5))
     progress("backward")
     vl, inputs_sha["varlen"] = bench_varlen(max(1, args.steps // 2), 2)
     m1, inputs_sha["prefill_1m_first_65536_tokens"] = bench_prefill_1m()
