@@ -359,7 +359,10 @@ def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_F
         if from_trace:
             d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
                  for r in trace if short(r["Kernel_Name"]) == frag]
-            d = d[2 * warmup: 2 * (warmup + steps)]
+            # the prefill section's zero-token setup call launches the state
+            # pass once (over no chunks) before the warm-up calls
+            lead = 1 if frag.startswith("kda_state_pass") else 0
+            d = d[lead + 2 * warmup: lead + 2 * (warmup + steps)]
             if not d:
                 continue
             lines.append(f"| `{label}` | {workload} | {len(d)} | {sum(d) / len(d):,.0f} | "
