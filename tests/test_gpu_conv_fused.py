@@ -97,6 +97,22 @@ def test_fused_matches_two_steps(case):
         _assert_same(f"conv_state_out[{'qkv'[i]}]", so1[i], so2[i])
 
 
+@pytest.mark.parametrize("shift", [-1.0, -30.0], ids=["mid-reference", "exact"])
+def test_fused_strong_gates(shift):
+    """Fast-forgetting gates send chunks down the intra-chunk kernel's other
+    exponent paths (the mid reference; the exact path past it), which stage
+    the convolved rows and load v on their own."""
+    H, d, T = 2, 128, 200
+    inp = W.prefill_inputs(batch=1, seqlen=T, heads=H, dk=d, dv=d, dtype=torch.bfloat16,
+                           device=DEV, seed=770, init="normal", gate_shift=shift)
+    w, b, s = _conv_params(H * d, 1, 771)
+    o2, fs2, _, so2 = _two_step(inp, w, b, s)
+    o1, fs1, _, so1 = _fused(inp, w, b, s)
+    torch.cuda.synchronize()
+    _assert_same("o", o1, o2)
+    _assert_same("final_state", fs1, fs2)
+
+
 def test_fused_without_norm_with_scale():
     """qk_l2norm off and a query scale: the same options reach both paths.
     Small filters keep the unnormalised keys short (|k| < 1), so the
