@@ -48,11 +48,12 @@
 // overflows fp32/bf16 (both have an 8-bit exponent) and each product keeps
 // the operands' relative precision.  [XT §4] names the precision loss of this
 // division as a design concern.  A chunk beyond that bound takes m = G at row
-// 31 (k1_mid_ap): every factor that matters then stays within [e^-80, e^80]
-// as long as each half of the chunk decays by at most 80 (gamma down to
-// about -160), and A and P are the same MFMA products of other operand
-// values.  Beyond even that, an exact path forms each e^(G_r - G_i) <= 1 from
-// its own difference (k1_exact_ap; slow, but never overflows).
+// 31 (the mid reference, in the same code): every factor that matters then
+// stays within [e^-80, e^80] as long as each half of the chunk decays by at
+// most 80 (gamma down to about -160), and A and P are the same MFMA products
+// of other operand values.  Beyond even that, an exact path forms each
+// e^(G_r - G_i) <= 1 from its own difference (k1_exact_ap; slow, but never
+// overflows).
 //
 // Precision.  MFMA operands are the input dtype (bf16 or fp32); MFMA
 // accumulation, the state, T, G and gamma are fp32.
@@ -122,8 +123,20 @@ struct K1Lds {
   static_assert(RPP % 8 == 0, "transposed stores take 8 rows at a time");
   static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
   static_assert(NPART * D * 4 <= REG, "the scan partials must fit a region");
-  // + per row: 1/|k|, 1/|q|, beta; per channel: e^gamma
+  // + per row: 1/|k|, 1/|q|, beta; per channel: e^(gamma-m).  (Not one
+  // float more: at 512 more bytes three workgroups no longer share a CU --
+  // measured, the intra-chunk kernel then takes ~17 us more per call.)
   static constexpr int BYTES = 3 * REG + (3 * kC + D) * 4;
+  // Under the mid reference e^m per channel is parked in the 16-byte row pads
+  // of region 2 (row-major there until T is written), rows kC/2 .. kC/2 +
+  // D/4 - 1, four channels a row; the Wk phase takes it from the row-norm
+  // arrays (1/|k|, 1/|q|: 2 kC floats, dead after the operands).
+  static_assert((LDR - D) * (int)sizeof(T) == 16 && kC / 2 + D / 4 <= kC,
+                "four floats of pad per row, D/4 rows");
+  static_assert(D <= 2 * kC, "e^m fits the row-norm arrays");
+  static __device__ __forceinline__ float* em_pad(T* r2, int c) {
+    return reinterpret_cast<float*>(r2 + (kC / 2 + c / 4) * LDR + D) + (c & 3);
+  }
 };
 
 constexpr float kLog2eF = 1.44269504088896341f;  // log2(e), rounded to fp32
@@ -282,116 +295,17 @@ __device__ __forceinline__ void k1_exact_ap(
   }
 }
 
-// Mid-reference path of A and P, for a chunk some channel of which decays
-// below the fast bound while each half of it stays within it.  Entered with
-// k^ in region 0 and q^ in region 1 (row-major, as the exact path stages
-// them); G is formed again from g (as the kernel forms it: the prefix sum
-// over the thread's rows, plus the part offset), and with m = G of row 31
-// per channel the regions become K o e^(G-m) (0), Q o e^(G-m) (1) and
-// K o e^(m-G) (2): A^T and P^T then come out of the same block-pair MFMA
-// products as on the fast path.  For i <= r the factors e^(G_r - m) and
-// e^(m - G_i) lie in [e^-80, e^80] unless the whole product is below e^-80
-// (r in the second half, i in the first: both factors <= 1), so nothing
-// overflows and nothing that matters underflows.  Writes A (times beta_r,
-// strict lower, fp32) over region 1 and P into the record, as the fast path
-// does.  Out of line, like the exact path, so that its registers do not set
-// the common path's budget.  Every thread of the workgroup calls it.
-template <typename T, int D, bool GS>
-__device__ __forceinline__ void k1_mid_ap(T* kop, T* qop, T* kim, const float* s_beta, T* wP,
-                                          const float* gb, int64_t rowstride, int H, int len,
-                                          float offx, float offy, float mx, float my) {
-  using L = K1Lds<T, D>;
-  using M = Mma<T>;
-  constexpr int NCP = L::NCP, RPP = L::RPP, NT = k1_threads<T, D>(), NW = NT / 64;
-  const int tid = threadIdx.x, cp = tid % NCP, part = tid / NCP, lane = tid & 63,
-            wave = tid >> 6;
-  const int c0 = 2 * cp, r0p = part * RPP;
-  float2 run = make_float2(0.f, 0.f);
-#pragma unroll
-  for (int j = 0; j < RPP; ++j) {
-    const int r = r0p + j, rr = min(r, len - 1);
-    const float2 gj = GS ? make_float2(gb[rr * H], gb[rr * H]) : ld2(gb + rr * rowstride + c0);
-    const float2 gm = r < len ? gj : make_float2(0.f, 0.f);
-    run = make_float2(run.x + gm.x, run.y + gm.y);
-    const float gsx = (run.x + offx - mx) * kLog2eF, gsy = (run.y + offy - my) * kLog2eF;
-    const float erx = __builtin_amdgcn_exp2f(gsx), ery = __builtin_amdgcn_exp2f(gsy);
-    const float enx = __builtin_amdgcn_exp2f(-gsx), eny = __builtin_amdgcn_exp2f(-gsy);
-    const float2 kh = ld2(kop + r * L::LDR + c0), qh = ld2(qop + r * L::LDR + c0);
-    st2(kop + r * L::LDR + c0, kh.x * erx, kh.y * ery);
-    st2(qop + r * L::LDR + c0, qh.x * erx, qh.y * ery);
-    st2(kim + r * L::LDR + c0, kh.x * enx, kh.y * eny);
-  }
-  __syncthreads();
-  // the fast path's block pairs (I <= R), dealt to the waves round-robin
-  constexpr int NPAIR = 10, PMAX = (NPAIR + NW - 1) / NW;
-  auto pair_I = [](int p) { return p < 4 ? 0 : p < 7 ? 1 : p < 9 ? 2 : 3; };
-  auto pair_R = [](int p) { return p < 4 ? p : p < 7 ? p - 3 : p < 9 ? p - 5 : 3; };
-  f32x4_t accA[PMAX], accP[PMAX];
-#pragma unroll
-  for (int t = 0; t < PMAX; ++t) {
-    accA[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    accP[t] = accA[t];
-    const int p = wave + t * NW;
-    if (p >= NPAIR) continue;
-    const int I = pair_I(p), Rb = pair_R(p);
-#pragma unroll
-    for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-      const auto a = frag_at<T>(kim, L::LDR, I * 16, ks, lane);
-      accA[t] = M::mma(a, frag_at<T>(kop, L::LDR, Rb * 16, ks, lane), accA[t]);
-      accP[t] = M::mma(a, frag_at<T>(qop, L::LDR, Rb * 16, ks, lane), accP[t]);
-    }
-  }
-  __syncthreads();  // every read of regions 0..2 done; region 1 becomes A
-  float* sA = reinterpret_cast<float*>(qop);
-#pragma unroll
-  for (int t = 0; t < PMAX; ++t) {
-    const int p = wave + t * NW;
-    if (p >= NPAIR) continue;
-    const int I = pair_I(p), Rb = pair_R(p);
-    const int r = Rb * 16 + (lane & 15);
-    const int i0 = I * 16 + 4 * (lane >> 4);
-    const float br = s_beta[r];
-    float a4[4], p4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a4[j] = (i0 + j < r) ? br * accA[t][j] : 0.f;
-      p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
-    }
-    *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-    st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
-  }
-}
-
-// A and P of a chunk beyond the fast path's bound, from raw k^ (region 0) and
-// q^ (region 1), with region 2 still holding the kernel's per-part totals of
-// g: the mid-reference path when each half of the chunk decays by at most 80
-// in every channel, the exact path otherwise.  One call site out of line, so
-// that neither path's registers weigh on the common path.  Every thread of
-// the workgroup calls it.
+// A and P of a chunk beyond the mid reference's range (some half of the chunk
+// decays by more than 80 in some channel), from raw k^ (region 0) and q^
+// (region 1): k1_exact_ap, with region 2 free for its staging.  One call site
+// out of line, so that its registers do not weigh on the common path.  Every
+// thread of the workgroup calls it.
 template <typename T, int D, bool GS>
 __device__ __attribute__((noinline)) void k1_slow_ap(T* r0, T* r1, T* r2, const float* s_beta,
                                                      T* wP, const float* gb, int64_t rowstride,
                                                      int H, int len, float offx, float offy) {
-  using L = K1Lds<T, D>;
-  constexpr int NCP = L::NCP, NPART = L::NPART, RPP = L::RPP;
-  const int c0 = 2 * (threadIdx.x % NCP);
-  // m = G of row 31 and gamma = G of row 63, per channel, from the part totals
-  float mx = 0.f, my = 0.f, gx = 0.f, gy = 0.f;
-  const float* scan = reinterpret_cast<const float*>(r2);
-#pragma unroll
-  for (int p = 0; p < NPART; ++p) {
-    const float tx = scan[p * D + c0], ty = scan[p * D + c0 + 1];
-    if (p < (kC / 2) / RPP) { mx += tx; my += ty; }
-    gx += tx; gy += ty;
-  }
-  const bool mid = __syncthreads_or(mx < kFastDecayBound || my < kFastDecayBound ||
-                                    gx - mx < kFastDecayBound || gy - my < kFastDecayBound) == 0;
-  // (every read of the part totals is done: region 2 is free)
-  if (mid)
-    k1_mid_ap<T, D, GS>(r0, r1, r2, s_beta, wP, gb, rowstride, H, len, offx, offy, mx, my);
-  else
-    k1_exact_ap<T, D, GS>(r0, r1, reinterpret_cast<float*>(r2), reinterpret_cast<float*>(r1),
-                          s_beta, wP, gb, rowstride, H, len, offx, offy);
+  k1_exact_ap<T, D, GS>(r0, r1, reinterpret_cast<float*>(r2), reinterpret_cast<float*>(r1),
+                        s_beta, wP, gb, rowstride, H, len, offx, offy);
 }
 
 // The ShortConv + Swish prologue (width 4) fused into K1's loads: per tensor
@@ -493,7 +407,8 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
   float* s_rk = reinterpret_cast<float*>(smem + 3 * L::REG);
   float* s_rq = s_rk + kC;
   float* s_beta = s_rq + kC;
-  float* s_eg = s_beta + kC;  // e^gamma per channel
+  float* s_eg = s_beta + kC;  // e^(gamma-m) per channel (K~'s factor)
+  float* s_em = s_rk;         // e^m per channel for the Wk phase (mid reference)
 
   // heads vary fastest across workgroups: concurrently resident workgroups
   // then read whole token rows (all heads) of neighbouring tokens
@@ -639,25 +554,55 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
   }
 #pragma unroll
   for (int j = 0; j < RPP; ++j) { G[j].x += off.x; G[j].y += off.y; }
-  // Beyond the fast path's bound (some channel's gamma < -80) A and P come
-  // from k1_slow_ap (mid-reference or exact), from the operands staged as
-  // below (raw k^, q^; records written per thread).
-  const bool exact =
+  // Exponent modes (a workgroup vote): the fast path's reference m = 0
+  // while every channel's gamma >= -80; else the mid reference m = G of row
+  // 31 while each half of the chunk decays by at most 80 in every channel --
+  // the same products on MFMA, from K o e^(G-m), Q o e^(G-m), K o e^(m-G),
+  // whose factors stay within [e^-80, e^80] wherever a product's result is
+  // kept; beyond that, k1_slow_ap's exact path (raw k^, q^ staged, records
+  // written per thread).
+  const bool beyond =
       __syncthreads_or(gamma.x < kFastDecayBound || gamma.y < kFastDecayBound) != 0;
+  float2 mref = make_float2(0.f, 0.f);  // G of row 31, from the part totals
+  bool mid = false;
+  if (beyond) {
+#pragma unroll
+    for (int p = 0; p < (kC / 2) / RPP; ++p) {
+      mref.x += scan[p * D + c0];
+      mref.y += scan[p * D + c0 + 1];
+    }
+    mid = __syncthreads_or(mref.x < kFastDecayBound || mref.y < kFastDecayBound ||
+                           gamma.x - mref.x < kFastDecayBound ||
+                           gamma.y - mref.y < kFastDecayBound) == 0;
+    if (mid) {  // G relative to the reference: G - m
+#pragma unroll
+      for (int j = 0; j < RPP; ++j) { G[j].x -= mref.x; G[j].y -= mref.y; }
+    } else {
+      mref = make_float2(0.f, 0.f);
+    }
+  }
+  const bool exact = beyond && !mid;
 
   // ---- operands ---------------------------------------------------------------
+  // e^gamma for the record; K~'s factor e^(gamma-m); e^m rescales the mid
+  // reference's relative Q o e^(G-m) and Wk to their true values (1 off it)
   const float2 eg_gamma = make_float2(__expf(gamma.x), __expf(gamma.y));
-  // bf16 records on the fast path take Q o e^G and K~ from LDS below, in
+  const float2 eg_kt =
+      mid ? make_float2(__expf(gamma.x - mref.x), __expf(gamma.y - mref.y)) : eg_gamma;
+  // bf16 records off the exact path take Q o e^G and K~ from LDS below, in
   // whole operand fragments; otherwise every thread stores its own values
   constexpr bool kStaged = sizeof(T) == 2;
   const bool direct = !kStaged || exact;
+  float2 em = make_float2(1.f, 1.f);
+  if (mid) em = make_float2(__expf(mref.x), __expf(mref.y));
   if (part == 0) {
     wEG[c0] = eg_gamma.x; wEG[c0 + 1] = eg_gamma.y;
-    s_eg[c0] = eg_gamma.x; s_eg[c0 + 1] = eg_gamma.y;
+    s_eg[c0] = eg_kt.x; s_eg[c0 + 1] = eg_kt.y;
+    if (mid) { *L::em_pad(r2, c0) = em.x; *L::em_pad(r2, c0 + 1) = em.y; }
   }
-  // (K o e^G)^T, 8 rows of channels c0 and c0+1 per entry, stored after the
-  // inverse.  Rows are taken in pairs, so that each pair goes straight into
-  // the held tile and K~ leaves as pairs (few values live at a time).
+  // (K o e^(G-m))^T, 8 rows of channels c0 and c0+1 per entry, stored after
+  // the inverse.  Rows are taken in pairs, so that each pair goes straight
+  // into the held tile and K~ leaves as pairs (few values live at a time).
   Tr8<T> kgh[RPP / 8][2];
 #pragma unroll
   for (int j = 0; j < RPP; j += 2) {
@@ -669,21 +614,26 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
       const float2 kk = kraw[jj].get(), qq = qraw[jj].get();  // zero past the end
       const float khx = kk.x * rk, khy = kk.y * rk;
       const float qhx = qq.x * rq, qhy = qq.y * rq;
-      // e^(+-G) as 2^(+-G log2 e): one scaling for both signs (the same
-      // operations as __expf, so the same values)
+      // e^(+-(G-m)) as 2^(+-(G-m) log2 e): one scaling for both signs (the
+      // same operations as __expf, so the same values)
       const float gsx = G[jj].x * kLog2eF, gsy = G[jj].y * kLog2eF;
       const float egx = __builtin_amdgcn_exp2f(gsx), egy = __builtin_amdgcn_exp2f(gsy);
-      if (direct) st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
+      if (direct) {  // the true Q o e^G (bf16 only on the exact path, where m = 0)
+        if constexpr (kStaged)
+          st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx, qhy * egy);
+        else
+          st_fnat2(wQG, D / M::KSTEP, r, c0, qhx * egx * em.x, qhy * egy * em.y);
+      }
       kgx[e] = khx * egx;
       kgy[e] = khy * egy;
       if (!exact) {
         const float enx = __builtin_amdgcn_exp2f(-gsx), eny = __builtin_amdgcn_exp2f(-gsy);
-        st2(r0 + r * L::LDR + c0, khx * egx, khy * egy);     // K o e^G
-        st2(r1 + r * L::LDR + c0, qhx * egx, qhy * egy);     // Q o e^G
-        st2(r2 + r * L::LDR + c0, khx * enx, khy * eny);     // K o e^-G
+        st2(r0 + r * L::LDR + c0, khx * egx, khy * egy);     // K o e^(G-m)
+        st2(r1 + r * L::LDR + c0, qhx * egx, qhy * egy);     // Q o e^(G-m)
+        st2(r2 + r * L::LDR + c0, khx * enx, khy * eny);     // K o e^(m-G)
         if constexpr (!kStaged) {
-          ktx[e] = khx * (eg_gamma.x * enx);
-          kty[e] = khy * (eg_gamma.y * eny);
+          ktx[e] = khx * (eg_kt.x * enx);
+          kty[e] = khy * (eg_kt.y * eny);
         }
       } else {
         st2(r0 + r * L::LDR + c0, khx, khy);                 // k^ (staged later)
@@ -700,6 +650,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
     }
   }
   __syncthreads();
+  if (mid && tid < D) s_em[tid] = *L::em_pad(r2, tid);  // the row norms are dead
   // v is needed only after A and P: loading it here keeps its registers free
   // through the operands, and the staged writes and A, P cover its latency
   // (the exact path loads it after its own A and P).  Its row offsets are
@@ -715,10 +666,11 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
   };
   if (!exact) load_v();
 
-  // Staged record writes (bf16, fast path): Q o e^G is region 1 and
-  // K o e^-G region 2, so every lane slot of the operand-order blocks is
-  // gathered from LDS and each wave writes whole 1 KiB blocks.  K~ = e^gamma
-  // (K o e^-G) per channel (a second bf16 rounding of the region-2 values).
+  // Staged record writes (bf16, off the exact path): Q o e^(G-m) is region 1
+  // and K o e^(m-G) region 2, so every lane slot of the operand-order blocks
+  // is gathered from LDS and each wave writes whole 1 KiB blocks.  K~ =
+  // e^(gamma-m) (K o e^(m-G)) per channel, and under the mid reference
+  // Q o e^G = e^m (Q o e^(G-m)): a second bf16 rounding of the LDS values.
   if constexpr (kStaged) {
     if (!exact) {
       constexpr int QB = (kC / 16) * (D / 32), KB = (D / 16) * (kC / 32);  // blocks
@@ -727,10 +679,22 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
         float v[8];
         if (b < QB) {  // Q o e^G: rows r, k = channel
           const int r = (b / (D / 32)) * 16 + (L & 15), cb = (b % (D / 32)) * 32 + 4 * g;
-          const T* row = r1 + r * L::LDR;  // bf16 already: copied as raw bits
-          const uint2 lo = *reinterpret_cast<const uint2*>(row + cb);
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + cb + 16);
-          *reinterpret_cast<u32x4_t*>(wQG + (b * 64 + L) * 8) = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+          const T* row = r1 + r * L::LDR;
+          if (!mid) {  // bf16 already: copied as raw bits
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + cb);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + cb + 16);
+            *reinterpret_cast<u32x4_t*>(wQG + (b * 64 + L) * 8) = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+          } else {
+            const float4 e0 = *reinterpret_cast<const float4*>(L::em_pad(r2, cb));
+            const float4 e1 = *reinterpret_cast<const float4*>(L::em_pad(r2, cb + 16));
+            const float ea[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = ea[e] * ld_f(row + cb + e);
+              v[4 + e] = ea[4 + e] * ld_f(row + cb + 16 + e);
+            }
+            st8(wQG + (b * 64 + L) * 8, v);
+          }
         } else {       // K~: rows c, k = chunk row i
           const int bk = b - QB;
           const int c = (bk / (kC / 32)) * 16 + (L & 15), ib = (bk % (kC / 32)) * 32 + 4 * g;
@@ -808,6 +772,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
       st_fnat4(wP, kC / M::KSTEP, r, i0, 0.f, 0.f, 0.f, 0.f);
     }
   }
+
   if constexpr (CONV) {
     float4 w[2];
     float b[2];
@@ -865,6 +830,7 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
   __syncthreads();
 
   // ---- U = T Diag(beta) V and Wk^T = (K o e^G)^T (T Diag(beta))^T --------------
+  // (from (K o e^(G-m))^T, then times e^m per channel)
   {
     // wave w: the 16 rows rb = w % 4 of T, and column blocks nb of its
     // share (with 8 waves, waves 4..7 take the second half of the blocks)
@@ -886,6 +852,10 @@ __global__ __launch_bounds__((k1_threads<T, D>()), (k1_waves_per_simd<T, D, CONV
       st4(wUT + ((nb * (kC / 16) + rb) * 64 + lane) * 4, u[0], u[1], u[2], u[3]);
       // wk: rows c = nb*16 + 4*(lane/16) + j of Wk^T, column r = rb*16 + lane%16
       const int c4 = nb * 16 + 4 * (lane >> 4), r = rb * 16 + (lane & 15);
+      if (mid) {  // from K o e^(G-m): times e^m per channel
+        const float4 e4 = *reinterpret_cast<const float4*>(s_em + c4);
+        wk[0] *= e4.x; wk[1] *= e4.y; wk[2] *= e4.z; wk[3] *= e4.w;
+      }
       st_fnat4(wWN, D / M::KSTEP, r, c4, -wk[0], -wk[1], -wk[2], -wk[3]);
     }
   }
