@@ -269,8 +269,15 @@ def write_counters(csvs, out: str = COUNTER_FILE, command: str = "") -> str:
              "fill kernel); LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; VALU active",
              "and LDS wait = SQ_ACTIVE_INST_VALU, SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES;",
              "per-wave figures divide by SQ_WAVES.", ""]
-    if command:
-        lines += ["Commands:", "", "```", command, "```", ""]
+    if not command:  # the passes' commands, from the csv paths (-d DIR -o pmc)
+        rel = lambda x: os.path.relpath(x, ROOT)
+        command = "\n".join(
+            ["cd /tmp && export TMPDIR=/tmp && cd /root/repo"]
+            + [f"rocprofv3 --pmc {' '.join(pas)} --output-format csv "
+               f"-d {rel(os.path.dirname(os.path.abspath(path)))} -o pmc -- python3 bench.py --probe"
+               for pas, path in zip(COUNTER_PASSES, csvs)]
+            + ["python3 bench.py --write-counters " + " ".join(rel(x) for x in csvs)])
+    lines += ["Commands:", "", "```", command, "```", ""]
     lines += ["| kernel | dispatches | MFMA GFLOP per call | MFMA FLOP per token-head | "
               "MFMA busy | VALU instr / wave | MFMA instr / wave | LDS instr / wave | "
               "SALU instr / wave | VMEM instr / wave | LDS bank conflict | VALU active | "
@@ -308,9 +315,9 @@ KERNEL_STATS_FILE = os.path.join(ROOT, "profiles", "kda_prefill_8k_decode_256x32
 # (kernel-name fragment, template arguments shown, workload, from the trace?)
 _STATS_ROWS = (
     ("kda_intra_chunk<__hip_bfloat16, 128, false, false>", "kda_intra_chunk<bf16, 128, false, false>",
-     "prefill 8K, 20 timed calls (trace)", True),
+     "prefill 8K, 20 timed calls (trace)", "prefill"),
     ("kda_state_pass<__hip_bfloat16, 128, 16, true>", "kda_state_pass<bf16, 128, 16, true>",
-     "prefill 8K, 20 timed calls (trace)", True),
+     "prefill 8K, 20 timed calls (trace)", "prefill"),
     ("decode_step_kernel<__hip_bfloat16, 128>", "decode_step_kernel<bf16, 128>", "decode (stats)", False),
     ("gate_norm_kernel<__hip_bfloat16, 128>", "gate_norm_kernel<bf16, 128>", "epilogue (stats)", False),
     ("short_conv_kernel<__hip_bfloat16, 4>", "short_conv_kernel<bf16, 4>", "prologue (stats)", False),
@@ -319,16 +326,19 @@ _STATS_ROWS = (
     ("conv_state_out_kernel<__hip_bfloat16>", "conv_state_out_kernel<bf16>",
      "prefill with the prologue fused, carried-out inputs (stats)", False),
     ("kda_bwd_prep<__hip_bfloat16, 128, false>", "kda_bwd_prep<bf16, 128, false>",
-     "backward, per segment (stats)", False),
+     "backward, 10 timed calls, per segment (trace)", "backward"),
     ("kda_state_pass<__hip_bfloat16, 128, 16, false>", "kda_state_pass<bf16, 128, 16, false>",
-     "backward's forward, per segment (stats)", False),
-    ("kda_bwd_state_pass<__hip_bfloat16, 128>", "kda_bwd_state_pass<bf16, 128>", "backward (stats)", False),
-    ("kda_bwd_intra<__hip_bfloat16, 128, false>", "kda_bwd_intra<bf16, 128, false>", "backward (stats)", False),
+     "backward's forward, 10 timed calls, per segment (trace)", "backward"),
+    ("kda_bwd_state_pass<__hip_bfloat16, 128>", "kda_bwd_state_pass<bf16, 128>",
+     "backward, 10 timed calls (trace)", "backward"),
+    ("kda_bwd_intra<__hip_bfloat16, 128, false>", "kda_bwd_intra<bf16, 128, false>",
+     "backward, 10 timed calls (trace)", "backward"),
 )
 
 
 def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_FILE,
                        warmup: int = 50, steps: int = 20) -> str:
+    bwd_warmup, bwd_steps = min(warmup, 5), max(1, steps // 2)  # as main() runs the backward
     """Kernel durations from `rocprofv3 --kernel-trace --stats --output-format
     csv -- python3 bench.py --no-cpu-baseline`: the prefill kernels from the
     trace (the dispatches of the timed calls: 2 segments per call, after
@@ -352,11 +362,31 @@ def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_F
              f"    python3 bench.py --write-kernel-stats {os.path.relpath(trace_csv, ROOT)} "
              f"{os.path.relpath(stats_csv, ROOT)}", "",
              f"Kernel durations (ns). Prefill rows: the dispatches of the {steps} timed calls "
-             f"(after {warmup} warm-up calls, two segments per call) from the trace; the other "
-             "rows pool every call of the kernel in the run (stats file).", "",
+             f"(after {warmup} warm-up calls, two segments per call) from the trace. Backward "
+             f"rows: the dispatches of the backward section's {bwd_steps} timed calls (after "
+             f"{bwd_warmup} warm-up calls; the window between the ends of their neighbouring "
+             "calls' last kernels) from the trace. The other rows pool every call of the "
+             "kernel in the run (stats file).", "",
              "| Kernel | Workload | Calls | Average | Min | Max |", "|---|---|---|---|---|---|"]
+    # the backward section's timed calls: each call ends with one kda_bwd_intra
+    # dispatch, and the section runs the first backward calls of the run
+    bwd_end = [int(r["End_Timestamp"]) for r in trace
+               if short(r["Kernel_Name"]) == "kda_bwd_intra<__hip_bfloat16, 128, false>"]
+    bwd_window = None
+    if len(bwd_end) >= bwd_warmup + bwd_steps and bwd_warmup >= 1:
+        bwd_window = (bwd_end[bwd_warmup - 1], bwd_end[bwd_warmup + bwd_steps - 1])
     for frag, label, workload, from_trace in _STATS_ROWS:
-        if from_trace:
+        if from_trace == "backward":
+            if bwd_window is None:
+                continue
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+                 if short(r["Kernel_Name"]) == frag
+                 and bwd_window[0] < int(r["Start_Timestamp"]) <= bwd_window[1]]
+            if not d:
+                continue
+            lines.append(f"| `{label}` | {workload} | {len(d)} | {sum(d) / len(d):,.0f} | "
+                         f"{min(d):,} | {max(d):,} |")
+        elif from_trace:
             d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
                  for r in trace if short(r["Kernel_Name"]) == frag]
             # the prefill section's zero-token setup call launches the state
