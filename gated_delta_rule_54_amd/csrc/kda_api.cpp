@@ -272,8 +272,9 @@ KDA_EXPORT kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, con
                                       const float* init_state, const int32_t* cu_seqlens,
                                       const void* d_o, const float* d_final_state, void* dq,
                                       void* dk, void* dv, float* dg, float* dbeta,
-                                      float* d_init_state, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+                                      float* d_init_state, uint32_t* range_flag,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
   kda_status_t st = check_bwd_desc(desc);
   if (st != KDA_OK) return st;
   const kda_desc_t& d = *desc;
@@ -297,10 +298,11 @@ KDA_EXPORT kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, con
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i],
                   (int)align[i]);
   }
-  const void* opt[] = {init_state, d_final_state, d_init_state, workspace};
-  const char* onames[] = {"init_state", "d_final_state", "d_init_state", "workspace"};
-  const uintptr_t oalign[] = {4, 4, 4, 16};
-  for (int i = 0; i < 4; ++i)
+  const void* opt[] = {init_state, d_final_state, d_init_state, range_flag, workspace};
+  const char* onames[] = {"init_state", "d_final_state", "d_init_state", "range_flag",
+                          "workspace"};
+  const uintptr_t oalign[] = {4, 4, 4, 4, 16};
+  for (int i = 0; i < 5; ++i)
     if (opt[i] && !aligned(opt[i], oalign[i]))
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", onames[i],
                   (int)oalign[i]);
@@ -310,13 +312,17 @@ KDA_EXPORT kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, con
   for (const void* o : outs)
     for (const void* in : ins)
       if (o && o == in) return fail(KDA_ERR_INVALID_ARGUMENT, "gradients must not alias inputs");
+  if (range_flag)
+    for (const void* o : outs)
+      if (o == range_flag)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "range_flag must not alias a gradient");
   const size_t need_ws = kda::chunk_bwd_workspace_bytes(d);
   if (!workspace || workspace_bytes < need_ws)
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu%s", need_ws,
                 workspace_bytes, workspace ? "" : " (NULL)");
   hipError_t e = kda::launch_chunk_bwd(d, q, k, v, g, beta, init_state, cu_seqlens, d_o,
                                        d_final_state, dq, dk, dv, dg, dbeta, d_init_state,
-                                       workspace, stream);
+                                       range_flag, workspace, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kda_chunk_bwd launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -61,9 +61,10 @@
 // does: the chunk start while every channel's chunk decay gamma >= -80, else
 // G of row 31 while each half of the chunk decays by at most 80 (gamma down to
 // about -160; see BwdMode).  A chunk beyond that gets NaN gradients, and its
-// NaN state gradient reaches every chunk before it (all but dq); its A (and
-// so the forward states after it) is still formed exactly, by kda_bwd_prep.  fp32 operands at d = 128 do
-// not fit one workgroup's LDS and are not supported.
+// NaN state gradient reaches every chunk before it (all but dq); the caller's
+// range flag (when given) is set.  Its A (and so the forward states after it)
+// is still formed exactly, by kda_bwd_prep.  fp32 operands at d = 128 do not
+// fit one workgroup's LDS and are not supported.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -757,14 +758,15 @@ struct BRec {
 //    backward's forward pass runs the state pass on these instead of the
 //    intra-chunk kernel's.
 // A chunk beyond the mid reference's range forms A exactly, so its state-pass
-// record (and T) hold; its reverse-pass record is NaN.
+// record (and T) hold; its reverse-pass record is NaN, and one lane stores 1
+// into *range_flag (when given).
 template <typename T, int D, bool GS>
 __global__ __launch_bounds__((BwdLds<T, D>::NT), 1)
 __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
     int64_t nslot, int64_t slot_base, int qk_l2norm, float scale, char* __restrict__ brec,
-    T* __restrict__ tinv, char* __restrict__ frec, int64_t fnrec) {
+    T* __restrict__ tinv, char* __restrict__ frec, int64_t fnrec, uint32_t* range_flag) {
   using L = BwdLds<T, D, true>;
   using M = Mma<T>;
   using RC = BRec<T, D>;
@@ -804,6 +806,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
   // beyond the mid reference's range: NaN records, so that the reverse pass
   // carries NaN into every state gradient before this chunk
   const float nanf = mode == kBwdBeyond ? __builtin_nanf("") : 0.f;
+  if (mode == kBwdBeyond && range_flag != nullptr && tid == 0) *range_flag = 1u;
   char* fr = frec + ((int64_t)h * fnrec + blockIdx.y) * RF::BYTES;
   T* wKT = reinterpret_cast<T*>(fr) + RF::KT;
   T* wWN = reinterpret_cast<T*>(fr) + RF::WN;
@@ -1743,6 +1746,7 @@ struct PrepStage {
   char* brec;
   T* tinv;
   bool gate_per_head;
+  uint32_t* range_flag;
 };
 
 template <typename T, int D>
@@ -1752,7 +1756,7 @@ hipError_t prep_stage(void* ctx, int64_t s0, int64_t s1, char* recs, hipStream_t
   auto prep = c.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
   hipLaunchKernelGGL(prep, dim3(c.H, (unsigned)(s1 - s0)), dim3(LP::NT), LP::BYTES, stream, c.q,
                      c.k, c.v, c.g, c.beta, c.gm, c.H, c.nslot, s0, c.qk_l2norm, c.scale, c.brec,
-                     c.tinv, recs, s1 - s0);
+                     c.tinv, recs, s1 - s0, c.range_flag);
   return hipGetLastError();
 }
 
@@ -1760,7 +1764,8 @@ template <typename T, int D>
 hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void* v,
                    const float* g, const float* beta, const float* init_state, const int32_t* cu,
                    const void* d_o, const float* d_final, void* dq, void* dk, void* dv,
-                   float* dg, float* dbeta, float* d_init, char* ws, hipStream_t stream) {
+                   float* dg, float* dbeta, float* d_init, uint32_t* range_flag, char* ws,
+                   hipStream_t stream) {
   using L = BwdLds<T, D>;
   const BwdPlan p = bwd_plan(d);
   const bool varlen = cu != nullptr;
@@ -1801,7 +1806,7 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   // state pass's records (and the reverse pass's records and T of those
   // slots), then the state pass writes the state entering every chunk
   PrepStage<T> ps{(const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, nslot,
-                  d.qk_l2norm, d.scale, recs, tinv, d.gate_per_head != 0};
+                  d.qk_l2norm, d.scale, recs, tinv, d.gate_per_head != 0, range_flag};
   kda_desc_t df = d;
   df.ckpt_every = 0;
   e = launch_chunk_states(df, init_state, cu, states, ws, prep_stage<T, D>, &ps, stream);
@@ -1832,18 +1837,19 @@ hipError_t launch_chunk_bwd(const kda_desc_t& d, const void* q, const void* k, c
                             const float* g, const float* beta, const float* init_state,
                             const int32_t* cu_seqlens, const void* d_o, const float* d_final,
                             void* dq, void* dk, void* dv, float* dg, float* dbeta,
-                            float* d_init, void* workspace, hipStream_t stream) {
+                            float* d_init, uint32_t* range_flag, void* workspace,
+                            hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   if (d.dtype == KDA_DTYPE_BF16) {
     if (d.dk == 128)
       return run_bwd<bf16, 128>(d, q, k, v, g, beta, init_state, cu_seqlens, d_o, d_final, dq,
-                                dk, dv, dg, dbeta, d_init, ws, stream);
+                                dk, dv, dg, dbeta, d_init, range_flag, ws, stream);
     return run_bwd<bf16, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, d_o, d_final, dq, dk,
-                             dv, dg, dbeta, d_init, ws, stream);
+                             dv, dg, dbeta, d_init, range_flag, ws, stream);
   }
   if (d.dk == 64)
     return run_bwd<float, 64>(d, q, k, v, g, beta, init_state, cu_seqlens, d_o, d_final, dq, dk,
-                              dv, dg, dbeta, d_init, ws, stream);
+                              dv, dg, dbeta, d_init, range_flag, ws, stream);
   return hipErrorInvalidValue;  // fp32 at d = 128: rejected by the caller
 }
 

@@ -96,7 +96,8 @@ hipError_t launch_chunk_bwd(const kda_desc_t& d, const void* q, const void* k, c
                             const float* g, const float* beta, const float* init_state,
                             const int32_t* cu_seqlens, const void* d_o, const float* d_final,
                             void* dq, void* dk, void* dv, float* dg, float* dbeta,
-                            float* d_init, void* workspace, hipStream_t stream);
+                            float* d_init, uint32_t* range_flag, void* workspace,
+                            hipStream_t stream);
 
 // ShortConv + Swish prologue.  Shapes are validated by the caller.
 struct kda_conv_args {

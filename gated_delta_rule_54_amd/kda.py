@@ -88,7 +88,7 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_fwd_conv.restype = i32
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [dp]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
-    lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 16 + [sz, vp]
+    lib.kda_chunk_bwd.argtypes = [dp] + [vp] * 17 + [sz, vp]
     lib.kda_chunk_bwd.restype = i32
     lib.kda_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_decode_step.restype = i32
@@ -335,14 +335,18 @@ def chunk_bwd_workspace_bytes(desc: KdaDesc) -> int:
 
 @_stream_scoped
 def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens=None, *,
-                  qk_l2norm=True, scale=1.0, want_dinit=True, workspace=None, stream=None):
+                  qk_l2norm=True, scale=1.0, want_dinit=True, range_flag=None, workspace=None,
+                  stream=None):
     """Gradients of the chunkwise KDA prefill through the C ABI.
 
     Inputs as kda_chunk_fwd, plus do: [B, T, H, dv] (q's dtype), the gradient
     of o, and dfinal: [N, H, dk, dv] fp32 or None (zero), the gradient of the
     final state.  Returns (dq, dk, dv, dg, dbeta, dinit): dq, dk, dv in q's
     dtype, dg fp32 shaped like g, dbeta [B, T, H] fp32, dinit [N, H, dk, dv]
-    fp32 (None unless want_dinit).
+    fp32 (None unless want_dinit).  range_flag: None, or a one-element int32
+    tensor on q's device, set to 1 by the call when some chunk decays beyond
+    the backward's exponent range (its sequence's gradients then hold NaN);
+    the caller clears it.
     """
     lib = load_library()
     B, T, H, dk = q.shape
@@ -360,6 +364,8 @@ def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens
             _need(t, name, torch.float32, (N, H, dk, dv))
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if range_flag is not None:
+        _need(range_flag, "range_flag", torch.int32, (1,))
     dev = q.device
     dq = torch.empty_like(q)
     dkk = torch.empty_like(k)
@@ -378,7 +384,8 @@ def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens
     st = lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(init_state), _ptr(cu_seqlens), _ptr(do), _ptr(dfinal), _ptr(dq),
                            _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dinit),
-                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _ptr(range_flag), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(),
                            _stream_handle(stream, dev))
     _check(lib, st, "kda_chunk_bwd")
     return dq, dkk, dvv, dg, db, dinit

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
   KDA_OK = 0,
@@ -223,6 +223,11 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
  *              the sum over the key channels)
  *   dbeta      [B, T, H]      fp32, output
  *   d_init_state [N, H, dk, dv] fp32 output or NULL
+ *   range_flag NULL, or one device uint32 (4-byte aligned): the call stores 1
+ *              into it when some chunk lies beyond the exponent range below
+ *              (the gradients then hold NaN as described there) and leaves
+ *              it untouched otherwise; the caller clears it and reads it
+ *              after the call (no host synchronisation inside the call)
  *   workspace  device scratch of at least kda_chunk_bwd_workspace_bytes().
  * Supported: bf16 with dk = dv = 64 or 128, fp32 with dk = dv = 64
  * (KDA_ERR_UNSUPPORTED otherwise).  Alignment as kda_chunk_fwd (d_o, dq, dk,
@@ -232,13 +237,14 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
  * to about -160).  A chunk beyond that gets NaN gradients for its tokens,
  * and its NaN state gradient reaches the dk, dv, dg and dbeta of every
  * earlier token of its sequence and d_init_state (dq of earlier tokens does
- * not depend on it); no fault, no hang; the forward has no such limit. */
+ * not depend on it), and range_flag is set; no fault, no hang; the forward
+ * has no such limit. */
 kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, const void* k,
                            const void* v, const float* g, const float* beta,
                            const float* init_state, const int32_t* cu_seqlens, const void* d_o,
                            const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
-                           float* dbeta, float* d_init_state, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream);
+                           float* dbeta, float* d_init_state, uint32_t* range_flag,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One decode step for N independent sequences, state updated in place.
  * [XT §3 decay-then-correct split; XT §5 recurrent form "S_(t-1) + current

@@ -30,7 +30,7 @@ def test_exports_match_header():
 
 def test_abi_version_and_strings():
     lib = K.load_library()
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
     assert lib.kda_status_string(99) == b"KDA_STATUS_UNKNOWN"
@@ -225,19 +225,20 @@ def _call_bwd(desc, *, ws=None, ws_bytes=None, nulls=(), misalign=None, alias=No
     """Backward calls that must fail host validation (nothing launched)."""
     lib = K.load_library()
     need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc))
-    names = ("q", "k", "v", "g", "beta", "d_o", "dq", "dk", "dv", "dg", "dbeta")
+    names = ("q", "k", "v", "g", "beta", "d_o", "dq", "dk", "dv", "dg", "dbeta", "range_flag")
     ptrs = {n: FAKE + 0x1000 * i for i, n in enumerate(names)}
     for n in nulls:
         ptrs[n] = None
     if misalign:
-        ptrs[misalign] += 4
+        ptrs[misalign] += 2 if misalign == "range_flag" else 4  # its alignment is 4
     if alias:
         ptrs[alias[0]] = ptrs[alias[1]]
     wsp = FAKE + 0x100000 if ws is None else ws
     wsb = need if ws_bytes is None else ws_bytes
     return lib.kda_chunk_bwd(ctypes.byref(desc), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"],
                              ptrs["beta"], None, None, ptrs["d_o"], None, ptrs["dq"], ptrs["dk"],
-                             ptrs["dv"], ptrs["dg"], ptrs["dbeta"], None, wsp, wsb, None)
+                             ptrs["dv"], ptrs["dg"], ptrs["dbeta"], None, ptrs["range_flag"], wsp,
+                             wsb, None)
 
 
 def test_bwd_workspace_and_support():
@@ -261,7 +262,7 @@ def test_bwd_workspace_and_support():
 @pytest.mark.parametrize("case", [
     dict(nulls=("d_o",)), dict(nulls=("dg",)), dict(nulls=("dbeta",)),
     dict(misalign="dq"), dict(misalign="d_o"), dict(alias=("dq", "q")),
-    dict(alias=("dv", "d_o")),
+    dict(alias=("dv", "d_o")), dict(misalign="range_flag"), dict(alias=("range_flag", "dg")),
 ])
 def test_bwd_pointer_errors(case):
     lib = K.load_library()

@@ -22,9 +22,12 @@ def _run(inp, up, dtype, *, qk_l2norm=True, scale=1.0, label="", per_head=False)
     B, T, H, d = inp["q"].shape
     print(f"backward {label}: B,T,H,d = {(B, T, H, d)} {dtype}", flush=True)
     cu = inp["cu_seqlens"]
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
-                        inp["init_state"], up["dfinal"], cu, qk_l2norm=qk_l2norm, scale=scale)
+                        inp["init_state"], up["dfinal"], cu, qk_l2norm=qk_l2norm, scale=scale,
+                        range_flag=flag)
     torch.cuda.synchronize()
+    assert int(flag.item()) == 0, "range flag set for inputs within the exponent range"
     g = inp["g"]
     g_full = g.unsqueeze(-1).expand(B, T, H, d).contiguous() if per_head else g
     ref = O.kda_bwd(*(_host(inp[key]) for key in ("q", "k", "v")), _host(g_full),
@@ -245,7 +248,8 @@ def test_bwd_strong_gates_per_head():
                          ids=["f32-d64", "bf16-d128"])
 def test_bwd_beyond_the_mid_reference_is_nan(dt, d):
     """A chunk one half of which decays by more than 80 in some channel (here
-    five tokens at g = -30 in chunk 1): its tokens' gradients are NaN; the NaN
+    five tokens at g = -30 in chunk 1): the range flag is set; its tokens'
+    gradients are NaN; the NaN
     state gradient reaches the k, v, g, beta gradients of every earlier token
     and d_init, while dq of earlier tokens (q only reads the state) and every
     gradient of later tokens match the oracle (the forward states past the
@@ -255,9 +259,11 @@ def test_bwd_beyond_the_mid_reference_is_nan(dt, d):
     up = _up(inp, 48)
     B, T, H, d = inp["q"].shape
     print("backward beyond the mid reference: NaN below token 128", flush=True)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
-                        inp["init_state"], up["dfinal"])
+                        inp["init_state"], up["dfinal"], range_flag=flag)
     torch.cuda.synchronize()
+    assert int(flag.item()) == 1, "range flag not set"
     ref = O.kda_bwd(*(_host(inp[key]) for key in ("q", "k", "v", "g", "beta")), _host(up["do"]),
                     _host(inp["init_state"]), _host(up["dfinal"]))
     for name, a, b in zip(NAMES[:5], got[:5], ref[:5]):
