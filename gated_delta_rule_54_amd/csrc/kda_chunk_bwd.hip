@@ -580,16 +580,19 @@ __device__ __forceinline__ void prefix_G(const float (&gr)[4][4], int lane, BwdR
 // INV: form T here (else the caller puts T in tb before its next barrier);
 // tout (or nullptr): where T itself (without Diag(beta)) also goes, 64 x 64
 // row-major in the MFMA type.
-// A of a chunk beyond the mid reference's range, exactly: every entry from
-// its own exponent differences, A_ri = beta_r sum_c k^_rc k^_ic e^(G_rc - G_ic)
-// (i < r), so that T and what follows from it hold for any gate.  Channels
-// come 16 at a time, k^ and G channel-major in `stage`; thread (row r = lane,
-// columns i = wave + NW e) adds their terms to its entries of A in LDS (the
-// first block starts them, the last scales by beta_r and clears i >= r).
+// A and P of a chunk beyond the mid reference's range, exactly: every entry
+// from its own exponent differences, A_ri = beta_r sum_c k^_rc k^_ic
+// e^(G_rc - G_ic) (i < r) and P_ri = sum_c q^_rc k^_ic e^(G_rc - G_ic) (i <= r),
+// so that T, the forward states and the reverse pass's record (Z = Qp - P Wk)
+// hold for any gate.  Channels come 16 at a time, k^ and G channel-major in
+// `stage`, q^ in `sqs`; thread (row r = lane, columns i = wave + NW e) adds
+// their terms to its entries of A and P in LDS (the first block starts them,
+// the last scales A by beta_r and clears the entries above the diagonals).
 // LDS operands only, so it adds few registers to the common path.
 template <int NW>
-__device__ __forceinline__ void exact_A_block(const float* stage, const float* beta, float* sA,
-                                           int lane, int wave, bool first, bool last) {
+__device__ __forceinline__ void exact_AP_block(const float* stage, const float* sqs,
+                                               const float* beta, float* sA, float* sP, int lane,
+                                               int wave, bool first, bool last) {
   constexpr int EPT = kC / NW;
   const float* sk = stage;
   const float* sg = stage + 16 * kC;
@@ -597,18 +600,24 @@ __device__ __forceinline__ void exact_A_block(const float* stage, const float* b
   for (int e = 0; e < EPT; ++e) {
     const int i = wave + NW * e;  // the same for the whole wave: broadcast reads
     float a = first ? 0.f : sA[lane * kTriLd + i];
+    float p = first ? 0.f : sP[lane * kTriLd + i];
 #pragma unroll 4
     for (int cc = 0; cc < 16; ++cc) {
       const float d = i < lane ? sg[cc * kC + lane] - sg[cc * kC + i] : 0.f;
-      a += sk[cc * kC + lane] * sk[cc * kC + i] * __expf(d);
+      const float x = sk[cc * kC + i] * __expf(d);
+      a += sk[cc * kC + lane] * x;
+      p += sqs[cc * kC + lane] * x;
     }
     sA[lane * kTriLd + i] = last ? (i < lane ? beta[lane] * a : 0.f) : a;
+    sP[lane * kTriLd + i] = last ? (i <= lane ? p : 0.f) : p;
   }
 }
 
-// EXA: a chunk beyond the mid reference's range forms A exactly (exact_A),
-// in T's LDS before T is written; otherwise such a chunk's A, T are not
-// meaningful (its results are NaN by the caller's choice).
+// EXA: a chunk beyond the mid reference's range forms A and P exactly
+// (exact_AP_block), staged in T's and P's LDS, with P accumulated in fp32
+// T's space, before T is written; otherwise such a chunk's A, T and P are not
+// meaningful (the intra-chunk kernel leaves its gradients to the exact
+// kernel).
 template <typename T, int D, bool GS, bool TBETA, bool COMPACT, bool NTL = false, bool INV = true,
           bool EXA = false>
 __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __restrict__ k,
@@ -697,8 +706,10 @@ __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __
   __syncthreads();
   if constexpr (EXA) {
     static_assert(2 * 16 * kC * 4 <= L::CB, "exact A's stage must fit T's buffer");
-    if (mode == kBwdBeyond) {  // T's buffer is free until the inverse
+    static_assert(16 * kC * 4 <= L::CB, "exact P's q stage must fit P's buffer");
+    if (mode == kBwdBeyond) {  // T's and P's buffers and fp32 T are free until the inverse
       float* xs = reinterpret_cast<float*>(sm.tb);
+      float* xq = reinterpret_cast<float*>(sm.pb);
 #pragma unroll 1
       for (int b = 0; b < NW; ++b) {
         if (wave == b) {  // this wave's 16 channels, channel-major
@@ -709,12 +720,18 @@ __device__ __forceinline__ int bwd_prologue(const T* __restrict__ q, const T* __
               const int r = 16 * t + 4 * grp + j;
               xs[(lane & 15) * kC + r] = R.kh[t][j];
               xs[16 * kC + (lane & 15) * kC + r] = R.G[t][j];
+              xq[(lane & 15) * kC + r] = R.qh[t][j];
             }
         }
         __syncthreads();
-        exact_A_block<NW>(xs, sm.beta, sm.sA, lane, wave, b == 0, b == NW - 1);
+        exact_AP_block<NW>(xs, xq, sm.beta, sm.sA, sm.sT, lane, wave, b == 0, b == NW - 1);
         __syncthreads();
       }
+      for (int e = tid; e < kC * kC; e += NT) {
+        const int r = e >> 6, i = e & 63;
+        st_f(sm.pb + r * LDC + i, sm.sT[r * kTriLd + i]);
+      }
+      __syncthreads();
     }
   }
   tri_inv64(sm.sA, sm.sT, sm.scratch, wave, lane);
@@ -757,16 +774,18 @@ struct BRec {
 //    by the slot within the segment (frec, fnrec slots per head): the
 //    backward's forward pass runs the state pass on these instead of the
 //    intra-chunk kernel's.
-// A chunk beyond the mid reference's range forms A exactly, so its state-pass
-// record (and T) hold; its reverse-pass record is NaN, and one lane stores 1
-// into *range_flag (when given).
+// A chunk beyond the mid reference's range forms A and P exactly, so its
+// state-pass record, T and its reverse-pass record hold; xflag[slot H + h]
+// tells kda_bwd_exact whether the chunk is one (1) or not (0), and one lane
+// stores 1 into *range_flag (when given) for such a chunk.
 template <typename T, int D, bool GS>
 __global__ __launch_bounds__((BwdLds<T, D>::NT), 1)
 __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, ChunkGeom gm, int H,
     int64_t nslot, int64_t slot_base, int qk_l2norm, float scale, char* __restrict__ brec,
-    T* __restrict__ tinv, char* __restrict__ frec, int64_t fnrec, uint32_t* range_flag) {
+    T* __restrict__ tinv, char* __restrict__ frec, int64_t fnrec, uint32_t* __restrict__ xflag,
+    uint32_t* range_flag) {
   using L = BwdLds<T, D, true>;
   using M = Mma<T>;
   using RC = BRec<T, D>;
@@ -803,10 +822,10 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
           rv, (uint32_t)((row * rs + cp * VE) * (int)sizeof(T)), 0, 2);
     }
   }
-  // beyond the mid reference's range: NaN records, so that the reverse pass
-  // carries NaN into every state gradient before this chunk
-  const float nanf = mode == kBwdBeyond ? __builtin_nanf("") : 0.f;
-  if (mode == kBwdBeyond && range_flag != nullptr && tid == 0) *range_flag = 1u;
+  if (tid == 0) {
+    xflag[slot * H + h] = mode == kBwdBeyond ? 1u : 0u;
+    if (mode == kBwdBeyond && range_flag != nullptr) *range_flag = 1u;
+  }
   char* fr = frec + ((int64_t)h * fnrec + blockIdx.y) * RF::BYTES;
   T* wKT = reinterpret_cast<T*>(fr) + RF::KT;
   T* wWN = reinterpret_cast<T*>(fr) + RF::WN;
@@ -856,7 +875,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
       pw = M::mma(frag_rm_perm<T>(sm.pb, LDC, 16 * t, ks, lane), acc_frag<T>(wk, ks), pw);
     float z[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] - pw[j]) + nanf;
+    for (int j = 0; j < 4; ++j) z[j] = scale * (R.qh[t][j] - pw[j]);
     st_fnat4_nt(rec + RC::ZF, KC, c, 16 * t + 4 * grp, z[0], z[1], z[2], z[3]);
   }
   // M^T tiles (rows c', column c) = Diag(e^gamma) - K~^T Wk, stored as M
@@ -871,7 +890,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_prep(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c2 = 16 * cb + 4 * grp + j;
-      m[j] = (c2 == c ? egam : 0.f) - mt[j] + nanf;
+      m[j] = (c2 == c ? egam : 0.f) - mt[j];
     }
     st_fnat4_nt(rec + RC::MF, KD, c, 16 * cb + 4 * grp, m[0], m[1], m[2], m[3]);
   }
@@ -1237,9 +1256,9 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
     c = 16 * wave + (lane & 15);
   };
   if (mode == kBwdBeyond) {
-    // a half of the chunk decays by more than 80 in some channel: NaN
-    // gradients for its rows (the reverse pass already carries NaN into the
-    // state gradients before it)
+    // a half of the chunk decays by more than 80 in some channel: its
+    // gradients come from kda_bwd_exact, launched after this kernel, which
+    // overwrites these placeholders
     const float nan = __builtin_nanf("");
     const int64_t r0 = loc.tok0 * H + h;
     for (int e = tid; e < loc.len * D; e += L::NT) {
@@ -1704,13 +1723,295 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 }
 
 // ---------------------------------------------------------------------------
+// kda_bwd_exact: the gradients of the chunks beyond the mid reference's
+// exponent range (xflag set by kda_bwd_prep), in plain fp32 arithmetic with
+// every gate factor formed from its own exponent difference, so no factor
+// exceeds 1 for any gate ([XT §4] names the chunk form's e^(-G) division as
+// its precision concern).  The same closed forms as the file header, each
+// e^(G_r - G_i) product summed entry by entry:
+//   (Kp Km^T)_ri = sum_c k^_rc k^_ic e^(G_rc - G_ic)   P_ri = sum_c q^_rc k^_ic e^(...)
+//   dq^_rc = e^G_rc (dO' S^T)_rc + sum_(i<=r) dP_ri k^_ic e^(G_rc - G_ic)
+//   dKp o e^G  = -beta_r e^G_rc (L S^T)_rc + sum_(i<r) dB_ri k^_ic e^(G_rc - G_ic)
+//   dKm o e^-G = sum_(s>r) dB_sr k^_sc e^(G_sc - G_rc) + sum_(s>=r) dP_sr q^_sc e^(G_sc - G_rc)
+//   dK~ o e^(gamma-G) = e^(gamma_c - G_rc) (W dS'^T)_rc
+// S, dS' and T are the stored copies the other kernels read (S, dS'
+// slice-blocked, T row-major, in the MFMA type); S and dS' are also copied
+// transposed, in fp32, so that lanes over key channels read them coalesced.  A persistent grid walks
+// every (slot, head) and skips the unflagged ones (one word each).  k^, q^, G
+// live in LDS; the chunk's other intermediates in this workgroup's part of
+// `scr` (ExScr<D>: fp32, L2-resident).  Slow (each workgroup one chunk at a
+// time, no MFMA) and only for chunks the fast kernels cannot represent.
+constexpr int kExactThreads = 512;
+constexpr int kExactMaxGroups = 128;
+template <int D>
+struct ExScr {
+  static constexpr int64_t CD = (int64_t)kC * D, CC = (int64_t)kC * kC;
+  static constexpr int64_t X = 0, W = X + CD, OP = W + CD, DW = OP + CD, LM = DW + CD;
+  static constexpr int64_t DQ = LM + CD, DK = DQ + CD, DG = DK + CD, TT = DG + CD;
+  static constexpr int64_t KPM = TT + CD, PM = KPM + CC, TM = PM + CC, DA = TM + CC, DP = DA + CC;
+  // S and dS' in fp32, transposed ([n][c]: consecutive c contiguous)
+  static constexpr int64_t ST = DP + CC, DST = ST + (int64_t)D * D;
+  static constexpr int64_t END = DST + (int64_t)D * D;
+  static constexpr int64_t BYTES = (END * 4 + 255) / 256 * 256;
+  // LDS: k^, q^, G [kC][D]; beta, rk, rq, dot products [kC]; gamma [D]
+  static constexpr int LDS = (3 * kC * D + 5 * kC + D) * 4;
+};
+
+template <typename T, int D, bool GS>
+__global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ d_o,
+    const T* __restrict__ states, const T* __restrict__ dstates, const T* __restrict__ tinv,
+    const uint32_t* __restrict__ xflag, ChunkGeom gm, int H, int64_t nslot, int qk_l2norm,
+    float scale, float* __restrict__ scr, T* __restrict__ dq, T* __restrict__ dk,
+    T* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
+  using X = ExScr<D>;
+  constexpr int NT = kExactThreads;
+  extern __shared__ __align__(16) char smem[];
+  float* sk = reinterpret_cast<float*>(smem);
+  float* sq = sk + kC * D;
+  float* sg = sq + kC * D;
+  float* sb = sg + kC * D;
+  float* rk = sb + kC;
+  float* rq = rk + kC;
+  float* dotq = rq + kC;
+  float* dotk = dotq + kC;
+  float* gam = dotk + kC;
+  float* w = scr + blockIdx.x * (X::BYTES / 4);
+  float *xm = w + X::X, *wm = w + X::W, *op = w + X::OP, *dw = w + X::DW, *lm = w + X::LM;
+  float *dqh = w + X::DQ, *dkh = w + X::DK, *dG = w + X::DG, *tt = w + X::TT;
+  float *kpm = w + X::KPM, *pm = w + X::PM, *tm = w + X::TM, *da = w + X::DA, *dp = w + X::DP;
+  float *st = w + X::ST, *dst = w + X::DST;
+  const int tid = threadIdx.x;
+  for (int64_t item = blockIdx.x; item < nslot * H; item += gridDim.x) {
+    const int64_t slot = item / H;
+    const int h = (int)(item % H);
+    ChunkLoc loc;
+    if (!locate(gm, slot, loc)) continue;
+    if (xflag[slot * H + h] == 0u) continue;
+    const int len = loc.len;
+    const int64_t row0 = loc.tok0 * H + h;
+    const T* S = states + (slot * H + h) * (int64_t)D * D;
+    const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
+    const T* tb = tinv + (slot * H + h) * (int64_t)(kC * kC);
+    auto Sv = [&](int c, int n) { return ld_f(S + sblk<D>(c, n)); };
+    auto dSv = [&](int c, int n) { return ld_f(dS + sblk<D>(c, n)); };
+    // raw rows (zero past the chunk's end), beta, V and dO' = scale dO
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, c = e % D;
+      const bool ok = r < len;
+      const int64_t o = (row0 + (int64_t)r * H) * D + c;
+      sk[e] = ok ? ld_f(k + o) : 0.f;
+      sq[e] = ok ? ld_f(q + o) : 0.f;
+      sg[e] = ok ? (GS ? g[row0 + (int64_t)r * H] : g[o]) : 0.f;
+      xm[e] = ok ? ld_f(v + o) : 0.f;
+      op[e] = ok ? scale * ld_f(d_o + o) : 0.f;
+    }
+    if (tid < kC) sb[tid] = tid < len ? beta[row0 + (int64_t)tid * H] : 0.f;
+    for (int e = tid; e < D * D; e += NT) {  // e = n D + c
+      const int n = e / D, c = e % D;
+      st[e] = Sv(c, n);
+      dst[e] = dSv(c, n);
+    }
+    __syncthreads();
+    if (tid < kC) {
+      float a = 0.f, b = 0.f;
+      #pragma unroll 4
+      for (int c = 0; c < D; ++c) {
+        a += sk[tid * D + c] * sk[tid * D + c];
+        b += sq[tid * D + c] * sq[tid * D + c];
+      }
+      rk[tid] = qk_l2norm ? rsqrtf(a + kNormEps) : 1.f;
+      rq[tid] = qk_l2norm ? rsqrtf(b + kNormEps) : 1.f;
+    } else if (tid < kC + D) {  // in-chunk cumulative gate of channel c
+      const int c = tid - kC;
+      float run = 0.f;
+      #pragma unroll 4
+      for (int r = 0; r < kC; ++r) {
+        run += sg[r * D + c];
+        sg[r * D + c] = run;
+      }
+      gam[c] = run;
+    }
+    __syncthreads();
+    for (int e = tid; e < kC * D; e += NT) {
+      sk[e] *= rk[e / D];
+      sq[e] *= rq[e / D];
+    }
+    __syncthreads();
+    // X = V - Kp S; Kp Km^T, P and T (lower triangles)
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, n = e % D;
+      float a = 0.f;
+      #pragma unroll 4
+      for (int c = 0; c < D; ++c) a += sk[r * D + c] * __expf(sg[r * D + c]) * Sv(c, n);
+      xm[e] -= a;
+    }
+    for (int e = tid; e < kC * kC; e += NT) {
+      const int r = e / kC, i = e % kC;
+      float a = 0.f, p = 0.f;
+      if (i <= r) {
+        #pragma unroll 4
+        for (int c = 0; c < D; ++c) {
+          const float x = sk[i * D + c] * __expf(sg[r * D + c] - sg[i * D + c]);
+          a += sk[r * D + c] * x;
+          p += sq[r * D + c] * x;
+        }
+      }
+      kpm[e] = i < r ? a : 0.f;
+      pm[e] = p;
+      tm[e] = i <= r ? ld_f(tb + e) : 0.f;
+    }
+    __syncthreads();
+    // W = T Diag(beta) X
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, n = e % D;
+      float a = 0.f;
+      #pragma unroll 4
+      for (int i = 0; i <= r; ++i) a += tm[r * kC + i] * sb[i] * xm[i * D + n];
+      wm[e] = a;
+    }
+    __syncthreads();
+    // dW = P^T dO' + K~ dS'
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, n = e % D;
+      float a = 0.f;
+      #pragma unroll 4
+      for (int s2 = r; s2 < kC; ++s2) a += pm[s2 * kC + r] * op[s2 * D + n];
+      #pragma unroll 4
+      for (int c = 0; c < D; ++c)
+        a += sk[r * D + c] * __expf(gam[c] - sg[r * D + c]) * dSv(c, n);
+      dw[e] = a;
+    }
+    __syncthreads();
+    // L = T^T dW
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, n = e % D;
+      float a = 0.f;
+      #pragma unroll 4
+      for (int s2 = r; s2 < kC; ++s2) a += tm[s2 * kC + r] * dw[s2 * D + n];
+      lm[e] = a;
+    }
+    __syncthreads();
+    // dV = Diag(beta) L; dA = -tril_-1(L W^T); dP = tril(dO' W^T)
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, n = e % D;
+      if (r < len) st_f(dv + (row0 + (int64_t)r * H) * D + n, sb[r] * lm[e]);
+    }
+    for (int e = tid; e < kC * kC; e += NT) {
+      const int r = e / kC, i = e % kC;
+      float a = 0.f, p = 0.f;
+      if (i <= r)
+        #pragma unroll 4
+        for (int n = 0; n < D; ++n) {
+          a += lm[r * D + n] * wm[i * D + n];
+          p += op[r * D + n] * wm[i * D + n];
+        }
+      da[e] = i < r ? -a : 0.f;
+      dp[e] = p;
+    }
+    __syncthreads();
+    // dbeta = rowsum(L o X) + rowsum(dA o Kp Km^T)
+    if (tid < len) {
+      const int r = tid;
+      float a = 0.f;
+      #pragma unroll 4
+      for (int n = 0; n < D; ++n) a += lm[r * D + n] * xm[r * D + n];
+      #pragma unroll 4
+      for (int i = 0; i < r; ++i) a += da[r * kC + i] * kpm[r * kC + i];
+      dbeta[row0 + (int64_t)r * H] = a;
+    }
+    // per element: dq^, dk^ and dG
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, c = e % D;
+      const float gr = sg[e], eg = __expf(gr);
+      float dos = 0.f, ls = 0.f, wds = 0.f;
+      #pragma unroll 4
+      for (int n = 0; n < D; ++n) {
+        const float sv = st[n * D + c];
+        dos += op[r * D + n] * sv;
+        ls += lm[r * D + n] * sv;
+        wds += wm[r * D + n] * dst[n * D + c];
+      }
+      float dqv = eg * dos, tp = -sb[r] * eg * ls, tmv = 0.f;
+      #pragma unroll 4
+      for (int i = 0; i < kC; ++i) {
+        const float gi = sg[i * D + c];
+        if (i <= r) {
+          const float x = __expf(gr - gi);
+          dqv += dp[r * kC + i] * sk[i * D + c] * x;
+          if (i < r) tp += sb[r] * da[r * kC + i] * sk[i * D + c] * x;
+        }
+        if (i >= r) {
+          const float x = __expf(gi - gr);
+          tmv += dp[i * kC + r] * sq[i * D + c] * x;
+          if (i > r) tmv += sb[i] * da[i * kC + r] * sk[i * D + c] * x;
+        }
+      }
+      const float ttv = __expf(gam[c] - gr) * wds;
+      dqh[e] = dqv;
+      dkh[e] = tp + tmv + ttv;
+      dG[e] = sk[e] * (tp - tmv - ttv) + sq[e] * dqv;
+      tt[e] = ttv;
+    }
+    __syncthreads();
+    // dgamma = colsum(dK~ o K~) + e^gamma o rowsum(S o dS'), on the last row;
+    // then the in-chunk prefix sum reversed; the norms' row dot products
+    if (tid < D) {
+      const int c = tid;
+      float a = 0.f, b = 0.f;
+      #pragma unroll 4
+      for (int r = 0; r < kC; ++r) a += sk[r * D + c] * tt[r * D + c];
+      #pragma unroll 4
+      for (int n = 0; n < D; ++n) b += st[n * D + c] * dst[n * D + c];
+      float run = a + __expf(gam[c]) * b;
+      #pragma unroll 4
+      for (int r = kC - 1; r >= 0; --r) {
+        run += dG[r * D + c];
+        dG[r * D + c] = run;
+      }
+    } else if (tid < D + kC) {
+      const int r = tid - D;
+      float a = 0.f, b = 0.f;
+      #pragma unroll 4
+      for (int c = 0; c < D; ++c) {
+        a += sq[r * D + c] * dqh[r * D + c];
+        b += sk[r * D + c] * dkh[r * D + c];
+      }
+      dotq[r] = a;
+      dotk[r] = b;
+    }
+    __syncthreads();
+    // outputs: dg, and dq, dk through the norm (dx = r (dx^ - (x^ . dx^) x^))
+    for (int e = tid; e < kC * D; e += NT) {
+      const int r = e / D, c = e % D;
+      if (r >= len) continue;
+      const int64_t o = (row0 + (int64_t)r * H) * D + c;
+      const float vq = qk_l2norm ? rq[r] * (dqh[e] - dotq[r] * sq[e]) : dqh[e];
+      const float vk = qk_l2norm ? rk[r] * (dkh[e] - dotk[r] * sk[e]) : dkh[e];
+      st_f(dq + o, vq);
+      st_f(dk + o, vk);
+      if (!GS) dg[o] = dG[e];
+    }
+    if (GS && tid < len) {
+      float a = 0.f;
+      #pragma unroll 4
+      for (int c = 0; c < D; ++c) a += dG[tid * D + c];
+      dg[row0 + (int64_t)tid * H] = a;
+    }
+    __syncthreads();  // LDS and scratch are reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Workspace: [forward workspace | S per slot | dS' per slot | M, Z^T records |
-// T per (slot, head) | chunk map].  Slots are sized for the larger of the
-// dense and varlen bounds.
+// T per (slot, head) | chunk map | exact-path flag per (slot, head) | exact
+// kernel's scratch].  Slots are sized for the larger of the dense and varlen
+// bounds.
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdPlan {
-  int64_t slots, fwd, states, recs, tinv, map, total;
+  int64_t slots, fwd, states, recs, tinv, map, xflag, xgroups, xscr, total;
 };
 
 BwdPlan bwd_plan(const kda_desc_t& d) {
@@ -1728,7 +2029,10 @@ BwdPlan bwd_plan(const kda_desc_t& d) {
   p.recs = p.slots * d.heads * rb;
   p.tinv = align256(p.slots * d.heads * (int64_t)kC * kC * (d.dtype == KDA_DTYPE_BF16 ? 2 : 4));
   p.map = 2 * align256(((int64_t)d.num_seqs + 1) * 4);
-  p.total = p.fwd + 2 * p.states + p.recs + p.tinv + p.map;
+  p.xflag = align256(p.slots * d.heads * 4);
+  p.xgroups = std::max<int64_t>(1, std::min<int64_t>(kExactMaxGroups, p.slots * d.heads));
+  p.xscr = p.xgroups * (d.dk == 128 ? ExScr<128>::BYTES : ExScr<64>::BYTES);
+  p.total = p.fwd + 2 * p.states + p.recs + p.tinv + p.map + p.xflag + p.xscr;
   return p;
 }
 
@@ -1746,6 +2050,7 @@ struct PrepStage {
   char* brec;
   T* tinv;
   bool gate_per_head;
+  uint32_t* xflag;
   uint32_t* range_flag;
 };
 
@@ -1756,7 +2061,7 @@ hipError_t prep_stage(void* ctx, int64_t s0, int64_t s1, char* recs, hipStream_t
   auto prep = c.gate_per_head ? kda_bwd_prep<T, D, true> : kda_bwd_prep<T, D, false>;
   hipLaunchKernelGGL(prep, dim3(c.H, (unsigned)(s1 - s0)), dim3(LP::NT), LP::BYTES, stream, c.q,
                      c.k, c.v, c.g, c.beta, c.gm, c.H, c.nslot, s0, c.qk_l2norm, c.scale, c.brec,
-                     c.tinv, recs, s1 - s0, c.range_flag);
+                     c.tinv, recs, s1 - s0, c.xflag, c.range_flag);
   return hipGetLastError();
 }
 
@@ -1776,6 +2081,9 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   T* tinv = reinterpret_cast<T*>(ws + p.fwd + 2 * p.states + p.recs);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + p.fwd + 2 * p.states + p.recs + p.tinv);
   int32_t* cu_s = chunk_off + (p.map / 2) / 4;
+  char* xbase = ws + p.fwd + 2 * p.states + p.recs + p.tinv + p.map;
+  uint32_t* xflag = reinterpret_cast<uint32_t*>(xbase);
+  float* xscr = reinterpret_cast<float*>(xbase + p.xflag);
   const int64_t nslot = chunk_slot_bound(d, varlen);
 
   ChunkGeom gm{nullptr, nullptr, d.seqlen, (d.seqlen + kC - 1) / kC, d.num_seqs};
@@ -1797,6 +2105,12 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
       hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
       if (ea != hipSuccess) return ea;
     }
+    for (const void* fn : {(const void*)kda_bwd_exact<T, D, false>,
+                           (const void*)kda_bwd_exact<T, D, true>}) {
+      hipError_t ea = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          ExScr<D>::LDS);
+      if (ea != hipSuccess) return ea;
+    }
     return hipFuncSetAttribute((const void*)kda_bwd_state_pass<T, D>,
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                BwdPassLds<T, D>::BYTES);
@@ -1806,7 +2120,7 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
   // state pass's records (and the reverse pass's records and T of those
   // slots), then the state pass writes the state entering every chunk
   PrepStage<T> ps{(const T*)q, (const T*)k, (const T*)v, g, beta, gm, H, nslot,
-                  d.qk_l2norm, d.scale, recs, tinv, d.gate_per_head != 0, range_flag};
+                  d.qk_l2norm, d.scale, recs, tinv, d.gate_per_head != 0, xflag, range_flag};
   kda_desc_t df = d;
   df.ckpt_every = 0;
   e = launch_chunk_states(df, init_state, cu, states, ws, prep_stage<T, D>, &ps, stream);
@@ -1826,6 +2140,13 @@ hipError_t run_bwd(const kda_desc_t& d, const void* q, const void* k, const void
                        (const T*)k, (const T*)v, g, beta, (const T*)d_o, states, dstates, gm, H,
                        sb, d.qk_l2norm, d.scale, (T*)dq, (T*)dk, (T*)dv, dg, dbeta, tinv);
   }
+  // the chunks beyond the mid reference's range (prep's flags), exactly
+  auto exact = d.gate_per_head ? kda_bwd_exact<T, D, true> : kda_bwd_exact<T, D, false>;
+  const unsigned ngx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(p.xgroups, nslot * H));
+  hipLaunchKernelGGL(exact, dim3(ngx), dim3(kExactThreads), ExScr<D>::LDS, stream, (const T*)q,
+                     (const T*)k, (const T*)v, g, beta, (const T*)d_o, states, dstates, tinv,
+                     xflag, gm, H, nslot, d.qk_l2norm, d.scale, xscr, (T*)dq, (T*)dk, (T*)dv,
+                     dg, dbeta);
   return hipGetLastError();
 }
 

@@ -345,8 +345,8 @@ def kda_chunk_bwd(q, k, v, g, beta, do, init_state=None, dfinal=None, cu_seqlens
     dtype, dg fp32 shaped like g, dbeta [B, T, H] fp32, dinit [N, H, dk, dv]
     fp32 (None unless want_dinit).  range_flag: None, or a one-element int32
     tensor on q's device, set to 1 by the call when some chunk decays beyond
-    the backward's exponent range (its sequence's gradients then hold NaN);
-    the caller clears it.
+    the fast kernels' exponent range (that chunk's gradients then come from
+    the slow exact kernel); the caller clears it.
     """
     lib = load_library()
     B, T, H, dk = q.shape

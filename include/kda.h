@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum {
   KDA_OK = 0,
@@ -224,21 +224,22 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
  *   dbeta      [B, T, H]      fp32, output
  *   d_init_state [N, H, dk, dv] fp32 output or NULL
  *   range_flag NULL, or one device uint32 (4-byte aligned): the call stores 1
- *              into it when some chunk lies beyond the exponent range below
- *              (the gradients then hold NaN as described there) and leaves
- *              it untouched otherwise; the caller clears it and reads it
- *              after the call (no host synchronisation inside the call)
+ *              into it when some chunk lies beyond the fast exponent range
+ *              below (its gradients then came from the slow exact kernel)
+ *              and leaves it untouched otherwise; the caller clears it and
+ *              reads it after the call (no host synchronisation inside the
+ *              call)
  *   workspace  device scratch of at least kda_chunk_bwd_workspace_bytes().
  * Supported: bf16 with dk = dv = 64 or 128, fp32 with dk = dv = 64
  * (KDA_ERR_UNSUPPORTED otherwise).  Alignment as kda_chunk_fwd (d_o, dq, dk,
- * dv 16-byte; dg, dbeta 4-byte).  Outputs must not alias inputs.  Exponent
- * range: within each 64-token chunk, each half (32 tokens) may decay by at
- * most 80 per channel (the sum of its log-gates >= -80; chunk decays down
- * to about -160).  A chunk beyond that gets NaN gradients for its tokens,
- * and its NaN state gradient reaches the dk, dv, dg and dbeta of every
- * earlier token of its sequence and d_init_state (dq of earlier tokens does
- * not depend on it), and range_flag is set; no fault, no hang; the forward
- * has no such limit. */
+ * dv 16-byte; dg, dbeta 4-byte).  Outputs must not alias inputs.  Any
+ * finite log-gates g <= 0 are supported ([XT §4] names the precision of the
+ * chunk form's e^(-G) division as its concern).  Fast exponent range: within
+ * each 64-token chunk, each half (32 tokens) decays by at most 80 per channel
+ * (the sum of its log-gates >= -80; chunk decays down to about -160).  A
+ * chunk beyond that takes an exact path (every gate factor from its own
+ * exponent difference, fp32 arithmetic without matrix cores: much slower per
+ * chunk) and range_flag is set. */
 kda_status_t kda_chunk_bwd(const kda_desc_t* desc, const void* q, const void* k,
                            const void* v, const float* g, const float* beta,
                            const float* init_state, const int32_t* cu_seqlens, const void* d_o,

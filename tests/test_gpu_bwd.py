@@ -244,33 +244,62 @@ def test_bwd_strong_gates_per_head():
     _run(inp, _up(inp, 46), torch.bfloat16, label="gate per head, strong", per_head=True)
 
 
-@pytest.mark.parametrize("dt,d", [(torch.float32, 64), (torch.bfloat16, 128)],
-                         ids=["f32-d64", "bf16-d128"])
-def test_bwd_beyond_the_mid_reference_is_nan(dt, d):
-    """A chunk one half of which decays by more than 80 in some channel (here
-    five tokens at g = -30 in chunk 1): the range flag is set; its tokens'
-    gradients are NaN; the NaN
-    state gradient reaches the k, v, g, beta gradients of every earlier token
-    and d_init, while dq of earlier tokens (q only reads the state) and every
-    gradient of later tokens match the oracle (the forward states past the
-    chunk come from its exactly formed A)."""
-    inp = _inputs(1, 300, 2, d, dt, seed=47)
-    inp["g"][:, 70:75] = -30.0
-    up = _up(inp, 48)
+def _run_beyond(inp, up, dtype, label, per_head=False, cu=None, **kw):
+    """Gradients where some chunk is beyond the mid reference's exponent
+    range: the range flag is set and every gradient matches the oracle."""
     B, T, H, d = inp["q"].shape
-    print("backward beyond the mid reference: NaN below token 128", flush=True)
+    print(f"backward beyond the mid reference, {label}: {(B, T, H, d)} {dtype}", flush=True)
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     got = kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], up["do"],
-                        inp["init_state"], up["dfinal"], range_flag=flag)
+                        inp["init_state"], up["dfinal"], inp["cu_seqlens"], range_flag=flag,
+                        **kw)
     torch.cuda.synchronize()
     assert int(flag.item()) == 1, "range flag not set"
-    ref = O.kda_bwd(*(_host(inp[key]) for key in ("q", "k", "v", "g", "beta")), _host(up["do"]),
-                    _host(inp["init_state"]), _host(up["dfinal"]))
-    for name, a, b in zip(NAMES[:5], got[:5], ref[:5]):
-        nan_from = 64 if name == "dq" else 0
-        assert bool((~torch.isfinite(a[:, nan_from:128].float())).all()), \
-            f"{name}: tokens {nan_from}..127 not NaN"
-        assert_close(f"{name} (tokens >= 128)", a[:, 128:], b[:, 128:], TOL[dt])
-        if name == "dq":
-            assert_close("dq (tokens < 64)", a[:, :64], b[:, :64], TOL[dt])
-    assert bool((~torch.isfinite(got[5])).all()), "d_init not NaN"
+    g = inp["g"]
+    g_full = g.unsqueeze(-1).expand(B, T, H, d).contiguous() if per_head else g
+    cu = inp["cu_seqlens"]
+    ref = list(O.kda_bwd(*(_host(inp[key]) for key in ("q", "k", "v")), _host(g_full),
+                         _host(inp["beta"]), _host(up["do"]), _host(inp["init_state"]),
+                         _host(up["dfinal"]), None if cu is None else cu.cpu().numpy(), **kw))
+    if per_head:
+        ref[3] = ref[3].sum(axis=-1)
+    for name, a, b in zip(NAMES, got, ref):
+        assert torch.isfinite(a).all(), name
+        assert_close(name, a, b, TOL[dtype])
+
+
+@pytest.mark.parametrize("dt,d", [(torch.float32, 64), (torch.bfloat16, 128),
+                                  (torch.bfloat16, 64)], ids=["f32-d64", "bf16-d128", "bf16-d64"])
+def test_bwd_beyond_the_mid_reference(dt, d):
+    """One chunk, one half of which decays by more than 80 in every channel
+    (five tokens at g = -30 in chunk 1): the exact kernel's gradients for its
+    tokens, and through its exactly formed reverse-pass record every earlier
+    token's and d_init, all match the oracle."""
+    inp = _inputs(1, 300, 2, d, dt, seed=47)
+    inp["g"][:, 70:75] = -30.0
+    _run_beyond(inp, _up(inp, 48), dt, "one chunk at g = -30")
+
+
+@pytest.mark.parametrize("dt,d", [(torch.float32, 64), (torch.bfloat16, 128)],
+                         ids=["f32-d64", "bf16-d128"])
+def test_bwd_every_chunk_beyond(dt, d):
+    """Constant g = -6 per token: every full chunk decays by 384 per channel
+    (each half by 192), so every chunk takes the exact kernel; two sequences,
+    a ragged last chunk, a nonzero initial state, with and without the norm."""
+    inp = _inputs(2, 200, 3, d, dt, seed=51)
+    inp["g"] = torch.full_like(inp["g"], -6.0)
+    _run_beyond(inp, _up(inp, 52), dt, "g = -6 everywhere")
+    _run_beyond(inp, _up(inp, 53), dt, "g = -6, no norm, scale 0.5", qk_l2norm=False,
+                scale=0.5)
+
+
+def test_bwd_beyond_varlen_and_per_head():
+    """Beyond-range chunks in varlen packing (an empty and a one-token
+    sequence beside them) and with one gate per (token, head)."""
+    lens = [70, 0, 1, 130, 64]
+    inp = _inputs(1, sum(lens), 2, 128, torch.bfloat16, seed=55, lengths=lens)
+    inp["g"][:, 100:140] = -9.0  # the second long sequence's first chunk and part of its next
+    _run_beyond(inp, _up(inp, 56), torch.bfloat16, "varlen")
+    inp = _inputs(1, 260, 2, 128, torch.bfloat16, seed=57, gate_per_head=True)
+    inp["g"][:, 150:] = -7.0
+    _run_beyond(inp, _up(inp, 58), torch.bfloat16, "gate per head", per_head=True)

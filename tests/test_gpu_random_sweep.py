@@ -2,7 +2,7 @@
 oracle over configurations drawn from a fixed seed per case -- batch, length
 (ragged, varlen with empty and single-token sequences), head count, head
 width, element type, gate mode (per channel or per head), gate strength
-(slow, normal and exact-path decay), initial state, final-state gradient,
+(slow, normal, mid-reference and exact-path decay), initial state, final-state gradient,
 norm and scale.  Each case names its configuration in its output."""
 import random
 
@@ -33,6 +33,8 @@ def _config(seed):
                         for _ in range(rng.randint(1, 5))]
     else:
         c["B"], c["T"] = rng.randint(1, 3), rng.choice([1, 17, 64, 65, 127, 128, 129, 300])
+    if rng.random() < 0.25:  # beyond the mid reference: the exact kernels
+        c["shift"] = -4.0
     return c
 
 
@@ -67,7 +69,8 @@ def test_random_config(seed):
     assert_close("final_state", fs, fs_ref, tol)
 
     # the backward: bf16 at d = 64 or 128, fp32 at d = 64 (every gate strength:
-    # the strong ones take the mid-reference products)
+    # the strong ones take the mid-reference products, the strongest the
+    # exact kernel)
     if dtype == torch.float32 and d == 128:
         return
     N = B if cu is None else cu.numel() - 1
