@@ -1735,27 +1735,63 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 //   dKm o e^-G = sum_(s>r) dB_sr k^_sc e^(G_sc - G_rc) + sum_(s>=r) dP_sr q^_sc e^(G_sc - G_rc)
 //   dK~ o e^(gamma-G) = e^(gamma_c - G_rc) (W dS'^T)_rc
 // S, dS' and T are the stored copies the other kernels read (S, dS'
-// slice-blocked, T row-major, in the MFMA type); S and dS' are also copied
-// transposed, in fp32, so that lanes over key channels read them coalesced.  A persistent grid walks
-// every (slot, head) and skips the unflagged ones (one word each).  k^, q^, G
-// live in LDS; the chunk's other intermediates in this workgroup's part of
-// `scr` (ExScr<D>: fp32, L2-resident).  Slow (each workgroup one chunk at a
-// time, no MFMA) and only for chunks the fast kernels cannot represent.
-constexpr int kExactThreads = 512;
+// slice-blocked, T row-major, in the MFMA type).  A persistent grid walks
+// every (slot, head) and skips the unflagged ones (one word each).  k^, q^,
+// G, dA and dP live in LDS; the chunk's other intermediates (fp32, among
+// them transposed copies of S and dS') in this workgroup's part of `scr`
+// (ExScr<D>, L2-resident).  Each thread owns a 4 x 4 tile of every product
+// (16-byte loads of the operand that is contiguous along the tile's columns,
+// four broadcast loads of the other), and of the per-element terms, whose
+// sums over the chunk rows carry a factor e^(G_rc - G_ic) per (r, i, c).
+// No MFMA and one chunk per workgroup: only for chunks the fast kernels
+// cannot represent.
+constexpr int kExactThreads = 256;
 constexpr int kExactMaxGroups = 128;
 template <int D>
 struct ExScr {
   static constexpr int64_t CD = (int64_t)kC * D, CC = (int64_t)kC * kC;
-  static constexpr int64_t X = 0, W = X + CD, OP = W + CD, DW = OP + CD, LM = DW + CD;
-  static constexpr int64_t DQ = LM + CD, DK = DQ + CD, DG = DK + CD, TT = DG + CD;
-  static constexpr int64_t KPM = TT + CD, PM = KPM + CC, TM = PM + CC, DA = TM + CC, DP = DA + CC;
-  // S and dS' in fp32, transposed ([n][c]: consecutive c contiguous)
-  static constexpr int64_t ST = DP + CC, DST = ST + (int64_t)D * D;
+  // [kC][D]: Kp = K^ o e^G, K~ = K^ o e^(gamma-G), X = V - Kp S (V first),
+  // W, dO', dW (then dG), L, dO' S^T (then dq^), L S^T (then dk^terms),
+  // W dS'^T (then dK~ o K~ / K^)
+  static constexpr int64_t KP = 0, KT = KP + CD, X = KT + CD, W = X + CD, OP = W + CD;
+  static constexpr int64_t DW = OP + CD, LM = DW + CD, DOS = LM + CD, LS = DOS + CD;
+  static constexpr int64_t WDS = LS + CD;
+  // [kC][kC]: Kp Km^T, P, T
+  static constexpr int64_t KPM = WDS + CD, PM = KPM + CC, TM = PM + CC;
+  // [D][D]: S and dS' transposed ([n][c])
+  static constexpr int64_t ST = TM + CC, DST = ST + (int64_t)D * D;
   static constexpr int64_t END = DST + (int64_t)D * D;
   static constexpr int64_t BYTES = (END * 4 + 255) / 256 * 256;
-  // LDS: k^, q^, G [kC][D]; beta, rk, rq, dot products [kC]; gamma [D]
-  static constexpr int LDS = (3 * kC * D + 5 * kC + D) * 4;
+  // LDS: k^, q^, G [kC][D]; dA, dP [kC][kC]; beta, rk, rq, two dot products [kC]; gamma [D]
+  static constexpr int LDS = (3 * kC * D + 2 * kC * kC + 5 * kC + D) * 4;
 };
+
+__device__ __forceinline__ void ex_ld4(const float* p, float (&x)[4]) {
+  const float4 t = *reinterpret_cast<const float4*>(p);
+  x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+}
+__device__ __forceinline__ void ex_ld4(const bf16* p, float (&x)[4]) {
+  const uint2 t = *reinterpret_cast<const uint2*>(p);
+  x[0] = bf_val(t.x & 0xffffu); x[1] = bf_val(t.x >> 16);
+  x[2] = bf_val(t.y & 0xffffu); x[3] = bf_val(t.y >> 16);
+}
+__device__ __forceinline__ void ex_st4(float* p, const float (&x)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+// acc[i][j] += sum_(kk in [k0, k1)) a(kk)[i] b(kk)[j]
+template <typename FA, typename FB>
+__device__ __forceinline__ void ex_mm(float (&acc)[4][4], int k0, int k1, FA fa, FB fb) {
+#pragma unroll 2
+  for (int kk = k0; kk < k1; ++kk) {
+    float a[4], b[4];
+    fa(kk, a);
+    fb(kk, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+  }
+}
 
 template <typename T, int D, bool GS>
 __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
@@ -1767,21 +1803,23 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
     T* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
   using X = ExScr<D>;
   constexpr int NT = kExactThreads;
+  constexpr int TD = kC / 4 * (D / 4), TC = kC / 4 * (kC / 4);  // 4 x 4 tiles of C x D, C x C
   extern __shared__ __align__(16) char smem[];
   float* sk = reinterpret_cast<float*>(smem);
   float* sq = sk + kC * D;
   float* sg = sq + kC * D;
-  float* sb = sg + kC * D;
+  float* lda = sg + kC * D;
+  float* ldp = lda + kC * kC;
+  float* sb = ldp + kC * kC;
   float* rk = sb + kC;
   float* rq = rk + kC;
   float* dotq = rq + kC;
   float* dotk = dotq + kC;
   float* gam = dotk + kC;
   float* w = scr + blockIdx.x * (X::BYTES / 4);
-  float *xm = w + X::X, *wm = w + X::W, *op = w + X::OP, *dw = w + X::DW, *lm = w + X::LM;
-  float *dqh = w + X::DQ, *dkh = w + X::DK, *dG = w + X::DG, *tt = w + X::TT;
-  float *kpm = w + X::KPM, *pm = w + X::PM, *tm = w + X::TM, *da = w + X::DA, *dp = w + X::DP;
-  float *st = w + X::ST, *dst = w + X::DST;
+  float *kp = w + X::KP, *kt = w + X::KT, *xm = w + X::X, *wm = w + X::W, *op = w + X::OP;
+  float *dw = w + X::DW, *lm = w + X::LM, *dos = w + X::DOS, *ls = w + X::LS, *wds = w + X::WDS;
+  float *kpm = w + X::KPM, *pm = w + X::PM, *tm = w + X::TM, *st = w + X::ST, *dst = w + X::DST;
   const int tid = threadIdx.x;
   for (int64_t item = blockIdx.x; item < nslot * H; item += gridDim.x) {
     const int64_t slot = item / H;
@@ -1794,9 +1832,8 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
     const T* S = states + (slot * H + h) * (int64_t)D * D;
     const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
     const T* tb = tinv + (slot * H + h) * (int64_t)(kC * kC);
-    auto Sv = [&](int c, int n) { return ld_f(S + sblk<D>(c, n)); };
-    auto dSv = [&](int c, int n) { return ld_f(dS + sblk<D>(c, n)); };
-    // raw rows (zero past the chunk's end), beta, V and dO' = scale dO
+    // raw rows (zero past the chunk's end), beta, V and dO' = scale dO, T,
+    // S and dS' transposed
     for (int e = tid; e < kC * D; e += NT) {
       const int r = e / D, c = e % D;
       const bool ok = r < len;
@@ -1808,15 +1845,16 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
       op[e] = ok ? scale * ld_f(d_o + o) : 0.f;
     }
     if (tid < kC) sb[tid] = tid < len ? beta[row0 + (int64_t)tid * H] : 0.f;
+    for (int e = tid; e < kC * kC; e += NT) tm[e] = (e % kC) <= (e / kC) ? ld_f(tb + e) : 0.f;
     for (int e = tid; e < D * D; e += NT) {  // e = n D + c
       const int n = e / D, c = e % D;
-      st[e] = Sv(c, n);
-      dst[e] = dSv(c, n);
+      st[e] = ld_f(S + sblk<D>(c, n));
+      dst[e] = ld_f(dS + sblk<D>(c, n));
     }
     __syncthreads();
     if (tid < kC) {
       float a = 0.f, b = 0.f;
-      #pragma unroll 4
+#pragma unroll 4
       for (int c = 0; c < D; ++c) {
         a += sk[tid * D + c] * sk[tid * D + c];
         b += sq[tid * D + c] * sq[tid * D + c];
@@ -1826,7 +1864,6 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
     } else if (tid < kC + D) {  // in-chunk cumulative gate of channel c
       const int c = tid - kC;
       float run = 0.f;
-      #pragma unroll 4
       for (int r = 0; r < kC; ++r) {
         run += sg[r * D + c];
         sg[r * D + c] = run;
@@ -1834,125 +1871,216 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
       gam[c] = run;
     }
     __syncthreads();
+    // k^, q^; Kp = K^ o e^G, K~ = K^ o e^(gamma-G) (every exponent <= 0)
     for (int e = tid; e < kC * D; e += NT) {
-      sk[e] *= rk[e / D];
-      sq[e] *= rq[e / D];
+      const int r = e / D, c = e % D;
+      const float kh = sk[e] * rk[r];
+      sk[e] = kh;
+      sq[e] *= rq[r];
+      kp[e] = kh * __expf(sg[e]);
+      kt[e] = kh * __expf(gam[c] - sg[e]);
     }
     __syncthreads();
-    // X = V - Kp S; Kp Km^T, P and T (lower triangles)
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, n = e % D;
-      float a = 0.f;
-      #pragma unroll 4
-      for (int c = 0; c < D; ++c) a += sk[r * D + c] * __expf(sg[r * D + c]) * Sv(c, n);
-      xm[e] -= a;
+    // X = V - Kp S; Kp Km^T and P, each entry from its own exponents
+    for (int t = tid; t < TD; t += NT) {
+      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+      float acc[4][4] = {};
+      ex_mm(acc, 0, D, [&](int c, float (&a)[4]) {
+        for (int i = 0; i < 4; ++i) a[i] = kp[(r0 + i) * D + c];
+      }, [&](int c, float (&b)[4]) { ex_ld4(S + sblk<D>(c, n0), b); });
+      for (int i = 0; i < 4; ++i) {
+        float x[4];
+        ex_ld4(xm + (r0 + i) * D + n0, x);
+        for (int j = 0; j < 4; ++j) x[j] -= acc[i][j];
+        ex_st4(xm + (r0 + i) * D + n0, x);
+      }
     }
-    for (int e = tid; e < kC * kC; e += NT) {
-      const int r = e / kC, i = e % kC;
-      float a = 0.f, p = 0.f;
-      if (i <= r) {
-        #pragma unroll 4
+    for (int t = tid; t < TC; t += NT) {
+      const int r0 = 4 * (t / (kC / 4)), i0 = 4 * (t % (kC / 4));
+      float a[4][4] = {}, pp[4][4] = {};
+      if (i0 <= r0 + 3) {
+#pragma unroll 2
         for (int c = 0; c < D; ++c) {
-          const float x = sk[i * D + c] * __expf(sg[r * D + c] - sg[i * D + c]);
-          a += sk[r * D + c] * x;
-          p += sq[r * D + c] * x;
+          float kr[4], qr[4], gr[4], ki[4], gi[4];
+          for (int u = 0; u < 4; ++u) {
+            kr[u] = sk[(r0 + u) * D + c];
+            qr[u] = sq[(r0 + u) * D + c];
+            gr[u] = sg[(r0 + u) * D + c];
+            ki[u] = sk[(i0 + u) * D + c];
+            gi[u] = sg[(i0 + u) * D + c];
+          }
+          for (int u = 0; u < 4; ++u)
+            for (int j = 0; j < 4; ++j) {
+              const float x = i0 + j <= r0 + u ? ki[j] * __expf(gr[u] - gi[j]) : 0.f;
+              a[u][j] += kr[u] * x;
+              pp[u][j] += qr[u] * x;
+            }
         }
       }
-      kpm[e] = i < r ? a : 0.f;
-      pm[e] = p;
-      tm[e] = i <= r ? ld_f(tb + e) : 0.f;
+      for (int u = 0; u < 4; ++u)
+        for (int j = 0; j < 4; ++j) {
+          const int r = r0 + u, i = i0 + j;
+          kpm[r * kC + i] = i < r ? a[u][j] : 0.f;
+          pm[r * kC + i] = i <= r ? pp[u][j] : 0.f;
+        }
     }
     __syncthreads();
     // W = T Diag(beta) X
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, n = e % D;
-      float a = 0.f;
-      #pragma unroll 4
-      for (int i = 0; i <= r; ++i) a += tm[r * kC + i] * sb[i] * xm[i * D + n];
-      wm[e] = a;
+    for (int t = tid; t < TD; t += NT) {
+      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+      float acc[4][4] = {};
+      ex_mm(acc, 0, r0 + 4, [&](int i, float (&a)[4]) {
+        for (int u = 0; u < 4; ++u) a[u] = tm[(r0 + u) * kC + i] * sb[i];
+      }, [&](int i, float (&b)[4]) { ex_ld4(xm + i * D + n0, b); });
+      for (int i = 0; i < 4; ++i) ex_st4(wm + (r0 + i) * D + n0, acc[i]);
     }
     __syncthreads();
     // dW = P^T dO' + K~ dS'
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, n = e % D;
-      float a = 0.f;
-      #pragma unroll 4
-      for (int s2 = r; s2 < kC; ++s2) a += pm[s2 * kC + r] * op[s2 * D + n];
-      #pragma unroll 4
-      for (int c = 0; c < D; ++c)
-        a += sk[r * D + c] * __expf(gam[c] - sg[r * D + c]) * dSv(c, n);
-      dw[e] = a;
+    for (int t = tid; t < TD; t += NT) {
+      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+      float acc[4][4] = {};
+      ex_mm(acc, r0, kC, [&](int s2, float (&a)[4]) { ex_ld4(pm + s2 * kC + r0, a); },
+            [&](int s2, float (&b)[4]) { ex_ld4(op + s2 * D + n0, b); });
+      ex_mm(acc, 0, D, [&](int c, float (&a)[4]) {
+        for (int u = 0; u < 4; ++u) a[u] = kt[(r0 + u) * D + c];
+      }, [&](int c, float (&b)[4]) { ex_ld4(dS + sblk<D>(c, n0), b); });
+      for (int i = 0; i < 4; ++i) ex_st4(dw + (r0 + i) * D + n0, acc[i]);
     }
     __syncthreads();
     // L = T^T dW
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, n = e % D;
-      float a = 0.f;
-      #pragma unroll 4
-      for (int s2 = r; s2 < kC; ++s2) a += tm[s2 * kC + r] * dw[s2 * D + n];
-      lm[e] = a;
+    for (int t = tid; t < TD; t += NT) {
+      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+      float acc[4][4] = {};
+      ex_mm(acc, r0, kC, [&](int s2, float (&a)[4]) { ex_ld4(tm + s2 * kC + r0, a); },
+            [&](int s2, float (&b)[4]) { ex_ld4(dw + s2 * D + n0, b); });
+      for (int i = 0; i < 4; ++i) ex_st4(lm + (r0 + i) * D + n0, acc[i]);
     }
     __syncthreads();
-    // dV = Diag(beta) L; dA = -tril_-1(L W^T); dP = tril(dO' W^T)
+    // dV = Diag(beta) L; dA = -tril_-1(L W^T), dP = tril(dO' W^T) (LDS);
+    // dO' S^T, L S^T, W dS'^T
     for (int e = tid; e < kC * D; e += NT) {
       const int r = e / D, n = e % D;
       if (r < len) st_f(dv + (row0 + (int64_t)r * H) * D + n, sb[r] * lm[e]);
     }
-    for (int e = tid; e < kC * kC; e += NT) {
-      const int r = e / kC, i = e % kC;
-      float a = 0.f, p = 0.f;
-      if (i <= r)
-        #pragma unroll 4
-        for (int n = 0; n < D; ++n) {
-          a += lm[r * D + n] * wm[i * D + n];
-          p += op[r * D + n] * wm[i * D + n];
+    for (int t = tid; t < TC; t += NT) {
+      const int r0 = 4 * (t / (kC / 4)), i0 = 4 * (t % (kC / 4));
+      float a[4][4] = {}, pp[4][4] = {};
+      if (i0 <= r0 + 3) {
+#pragma unroll 1
+        for (int n = 0; n < D; n += 4) {
+          float lr[4][4], orow[4][4], wi[4][4];
+          for (int u = 0; u < 4; ++u) {
+            ex_ld4(lm + (r0 + u) * D + n, lr[u]);
+            ex_ld4(op + (r0 + u) * D + n, orow[u]);
+            ex_ld4(wm + (i0 + u) * D + n, wi[u]);
+          }
+          for (int u = 0; u < 4; ++u)
+            for (int j = 0; j < 4; ++j)
+              for (int e = 0; e < 4; ++e) {
+                a[u][j] += lr[u][e] * wi[j][e];
+                pp[u][j] += orow[u][e] * wi[j][e];
+              }
         }
-      da[e] = i < r ? -a : 0.f;
-      dp[e] = p;
+      }
+      for (int u = 0; u < 4; ++u)
+        for (int j = 0; j < 4; ++j) {
+          const int r = r0 + u, i = i0 + j;
+          lda[r * kC + i] = i < r ? -a[u][j] : 0.f;
+          ldp[r * kC + i] = i <= r ? pp[u][j] : 0.f;
+        }
+    }
+    for (int t = tid; t < TD; t += NT) {
+      const int r0 = 4 * (t / (D / 4)), c0 = 4 * (t % (D / 4));
+      float a1[4][4] = {}, a2[4][4] = {}, a3[4][4] = {};
+#pragma unroll 1
+      for (int n = 0; n < D; ++n) {
+        float o4[4], l4[4], w4[4], s4[4], d4[4];
+        for (int u = 0; u < 4; ++u) {
+          o4[u] = op[(r0 + u) * D + n];
+          l4[u] = lm[(r0 + u) * D + n];
+          w4[u] = wm[(r0 + u) * D + n];
+        }
+        ex_ld4(st + n * D + c0, s4);
+        ex_ld4(dst + n * D + c0, d4);
+        for (int u = 0; u < 4; ++u)
+          for (int j = 0; j < 4; ++j) {
+            a1[u][j] += o4[u] * s4[j];
+            a2[u][j] += l4[u] * s4[j];
+            a3[u][j] += w4[u] * d4[j];
+          }
+      }
+      for (int u = 0; u < 4; ++u) {
+        ex_st4(dos + (r0 + u) * D + c0, a1[u]);
+        ex_st4(ls + (r0 + u) * D + c0, a2[u]);
+        ex_st4(wds + (r0 + u) * D + c0, a3[u]);
+      }
     }
     __syncthreads();
     // dbeta = rowsum(L o X) + rowsum(dA o Kp Km^T)
     if (tid < len) {
       const int r = tid;
       float a = 0.f;
-      #pragma unroll 4
+#pragma unroll 4
       for (int n = 0; n < D; ++n) a += lm[r * D + n] * xm[r * D + n];
-      #pragma unroll 4
-      for (int i = 0; i < r; ++i) a += da[r * kC + i] * kpm[r * kC + i];
+      for (int i = 0; i < r; ++i) a += lda[r * kC + i] * kpm[r * kC + i];
       dbeta[row0 + (int64_t)r * H] = a;
     }
-    // per element: dq^, dk^ and dG
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, c = e % D;
-      const float gr = sg[e], eg = __expf(gr);
-      float dos = 0.f, ls = 0.f, wds = 0.f;
-      #pragma unroll 4
-      for (int n = 0; n < D; ++n) {
-        const float sv = st[n * D + c];
-        dos += op[r * D + n] * sv;
-        ls += lm[r * D + n] * sv;
-        wds += wm[r * D + n] * dst[n * D + c];
+    // per element: dq^ (into dos), dk^ (into ls), dK~ o K~ / k^ (into wds)
+    // and dG (into dw)
+    for (int t = tid; t < TD; t += NT) {
+      const int r0 = 4 * (t / (D / 4)), c0 = 4 * (t % (D / 4));
+      float gr[4][4], dqv[4][4], tp[4][4], tmv[4][4];
+      for (int u = 0; u < 4; ++u) {
+        ex_ld4(sg + (r0 + u) * D + c0, gr[u]);
+        float a1[4], a2[4];
+        ex_ld4(dos + (r0 + u) * D + c0, a1);
+        ex_ld4(ls + (r0 + u) * D + c0, a2);
+        for (int j = 0; j < 4; ++j) {
+          const float eg = __expf(gr[u][j]);
+          dqv[u][j] = eg * a1[j];
+          tp[u][j] = -sb[r0 + u] * eg * a2[j];
+          tmv[u][j] = 0.f;
+        }
       }
-      float dqv = eg * dos, tp = -sb[r] * eg * ls, tmv = 0.f;
-      #pragma unroll 4
+#pragma unroll 1
       for (int i = 0; i < kC; ++i) {
-        const float gi = sg[i * D + c];
-        if (i <= r) {
-          const float x = __expf(gr - gi);
-          dqv += dp[r * kC + i] * sk[i * D + c] * x;
-          if (i < r) tp += sb[r] * da[r * kC + i] * sk[i * D + c] * x;
-        }
-        if (i >= r) {
-          const float x = __expf(gi - gr);
-          tmv += dp[i * kC + r] * sq[i * D + c] * x;
-          if (i > r) tmv += sb[i] * da[i * kC + r] * sk[i * D + c] * x;
+        float ki[4], qi[4], gi[4], pc[4], ac[4];
+        ex_ld4(sk + i * D + c0, ki);
+        ex_ld4(sq + i * D + c0, qi);
+        ex_ld4(sg + i * D + c0, gi);
+        ex_ld4(ldp + i * kC + r0, pc);  // dP_(i, r0..r0+3)
+        ex_ld4(lda + i * kC + r0, ac);  // dA_(i, r0..r0+3)
+        const float bi = sb[i];
+        for (int u = 0; u < 4; ++u) {
+          const int r = r0 + u;
+          const float pr = ldp[r * kC + i], br = sb[r] * lda[r * kC + i];
+          for (int j = 0; j < 4; ++j) {
+            // i <= r: e^(G_rc - G_ic) <= 1; i >= r: e^(G_ic - G_rc) <= 1
+            const float x = i <= r ? __expf(gr[u][j] - gi[j]) : 0.f;
+            const float y = i >= r ? __expf(gi[j] - gr[u][j]) : 0.f;
+            dqv[u][j] += pr * ki[j] * x;
+            tp[u][j] += br * ki[j] * x;
+            tmv[u][j] += (pc[u] * qi[j] + bi * ac[u] * ki[j]) * y;
+          }
         }
       }
-      const float ttv = __expf(gam[c] - gr) * wds;
-      dqh[e] = dqv;
-      dkh[e] = tp + tmv + ttv;
-      dG[e] = sk[e] * (tp - tmv - ttv) + sq[e] * dqv;
-      tt[e] = ttv;
+      for (int u = 0; u < 4; ++u) {
+        float w4[4], kr[4], qr[4], o1[4], o2[4], o3[4], o4[4];
+        ex_ld4(wds + (r0 + u) * D + c0, w4);
+        ex_ld4(sk + (r0 + u) * D + c0, kr);
+        ex_ld4(sq + (r0 + u) * D + c0, qr);
+        for (int j = 0; j < 4; ++j) {
+          const float ttv = __expf(gam[c0 + j] - gr[u][j]) * w4[j];
+          o1[j] = dqv[u][j];
+          o2[j] = tp[u][j] + tmv[u][j] + ttv;
+          o3[j] = kr[j] * ttv;  // dK~ o K~, summed over rows for dgamma
+          o4[j] = kr[j] * (tp[u][j] - tmv[u][j] - ttv) + qr[j] * dqv[u][j];
+        }
+        ex_st4(dos + (r0 + u) * D + c0, o1);
+        ex_st4(ls + (r0 + u) * D + c0, o2);
+        ex_st4(wds + (r0 + u) * D + c0, o3);
+        ex_st4(dw + (r0 + u) * D + c0, o4);
+      }
     }
     __syncthreads();
     // dgamma = colsum(dK~ o K~) + e^gamma o rowsum(S o dS'), on the last row;
@@ -1960,23 +2088,21 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
     if (tid < D) {
       const int c = tid;
       float a = 0.f, b = 0.f;
-      #pragma unroll 4
-      for (int r = 0; r < kC; ++r) a += sk[r * D + c] * tt[r * D + c];
-      #pragma unroll 4
+      for (int r = 0; r < kC; ++r) a += wds[r * D + c];
+#pragma unroll 4
       for (int n = 0; n < D; ++n) b += st[n * D + c] * dst[n * D + c];
       float run = a + __expf(gam[c]) * b;
-      #pragma unroll 4
       for (int r = kC - 1; r >= 0; --r) {
-        run += dG[r * D + c];
-        dG[r * D + c] = run;
+        run += dw[r * D + c];
+        dw[r * D + c] = run;
       }
     } else if (tid < D + kC) {
       const int r = tid - D;
       float a = 0.f, b = 0.f;
-      #pragma unroll 4
+#pragma unroll 4
       for (int c = 0; c < D; ++c) {
-        a += sq[r * D + c] * dqh[r * D + c];
-        b += sk[r * D + c] * dkh[r * D + c];
+        a += sq[r * D + c] * dos[r * D + c];
+        b += sk[r * D + c] * ls[r * D + c];
       }
       dotq[r] = a;
       dotk[r] = b;
@@ -1987,16 +2113,15 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
       const int r = e / D, c = e % D;
       if (r >= len) continue;
       const int64_t o = (row0 + (int64_t)r * H) * D + c;
-      const float vq = qk_l2norm ? rq[r] * (dqh[e] - dotq[r] * sq[e]) : dqh[e];
-      const float vk = qk_l2norm ? rk[r] * (dkh[e] - dotk[r] * sk[e]) : dkh[e];
+      const float vq = qk_l2norm ? rq[r] * (dos[e] - dotq[r] * sq[e]) : dos[e];
+      const float vk = qk_l2norm ? rk[r] * (ls[e] - dotk[r] * sk[e]) : ls[e];
       st_f(dq + o, vq);
       st_f(dk + o, vk);
-      if (!GS) dg[o] = dG[e];
+      if (!GS) dg[o] = dw[e];
     }
     if (GS && tid < len) {
       float a = 0.f;
-      #pragma unroll 4
-      for (int c = 0; c < D; ++c) a += dG[tid * D + c];
+      for (int c = 0; c < D; ++c) a += dw[tid * D + c];
       dg[row0 + (int64_t)tid * H] = a;
     }
     __syncthreads();  // LDS and scratch are reused by the next item
