@@ -121,7 +121,7 @@ struct K1Lds {
   static constexpr int NPART = k1_threads<T, D>() / NCP;   // row parts
   static constexpr int RPP = kC / NPART;                   // rows per part (8 or 16)
   static_assert(RPP % 8 == 0, "transposed stores take 8 rows at a time");
-  static_assert(3 * kC * 16 * 4 <= REG, "exact-path staging must fit a region");
+  static_assert(3 * kC * 17 * 4 <= REG, "exact-path staging must fit a region");
   static_assert(NPART * D * 4 <= REG, "the scan partials must fit a region");
   // + per row: 1/|k|, 1/|q|, beta; per channel: e^(gamma-m).  (Not one
   // float more: at 512 more bytes three workgroups no longer share a CU --
@@ -243,9 +243,12 @@ __device__ __forceinline__ void k1_exact_ap(
   float ea[NE], ep[NE];
 #pragma unroll
   for (int m = 0; m < NE; ++m) { ea[m] = 0.f; ep[m] = 0.f; }
+  // rows of 16 channels at a stride of 17 floats: the lanes of a wave read
+  // consecutive rows i of one channel, which a stride of 16 put in one bank
+  constexpr int SL = 17;
   float* stG = stage;
-  float* stK = stG + kC * 16;
-  float* stQ = stK + kC * 16;
+  float* stK = stG + kC * SL;
+  float* stQ = stK + kC * SL;
   for (int cb = 0; cb < D / 16; ++cb) {
     if (c0 / 16 == cb) {
       float2 run = make_float2(0.f, 0.f);
@@ -256,11 +259,11 @@ __device__ __forceinline__ void k1_exact_ap(
         const float2 gj = GS ? make_float2(gb[rr * H], gb[rr * H]) : ld2(gb + rr * rowstride + c0);
         const float2 gm = r < len ? gj : make_float2(0.f, 0.f);
         run = j == 0 ? gm : make_float2(gm.x + run.x, gm.y + run.y);
-        stG[r * 16 + cc] = run.x + offx;
-        stG[r * 16 + cc + 1] = run.y + offy;
+        stG[r * SL + cc] = run.x + offx;
+        stG[r * SL + cc + 1] = run.y + offy;
         const float2 kh = ld2(khat + r * L::LDR + c0), qh = ld2(qhat + r * L::LDR + c0);
-        stK[r * 16 + cc] = kh.x; stK[r * 16 + cc + 1] = kh.y;
-        stQ[r * 16 + cc] = qh.x; stQ[r * 16 + cc + 1] = qh.y;
+        stK[r * SL + cc] = kh.x; stK[r * SL + cc + 1] = kh.y;
+        stQ[r * SL + cc] = qh.x; stQ[r * SL + cc + 1] = qh.y;
       }
     }
     __syncthreads();
@@ -271,10 +274,10 @@ __device__ __forceinline__ void k1_exact_ap(
       const int i = entry_i(m, r);
 #pragma unroll 1
       for (int c = 0; c < 16; ++c) {
-        const float e = __expf(stG[r * 16 + c] - stG[i * 16 + c]);
-        const float ki = stK[i * 16 + c] * e;
-        ea[m] += stK[r * 16 + c] * ki;
-        ep[m] += stQ[r * 16 + c] * ki;
+        const float e = __expf(stG[r * SL + c] - stG[i * SL + c]);
+        const float ki = stK[i * SL + c] * e;
+        ea[m] += stK[r * SL + c] * ki;
+        ep[m] += stQ[r * SL + c] * ki;
       }
     }
     __syncthreads();
