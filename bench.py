@@ -603,14 +603,16 @@ def chunk_exponent_modes(g: torch.Tensor, chunk: int = 64, bound: float = -80.0)
             "exact": (n - fast.sum().item() - mid.sum().item()) / n}
 
 
-def bench_strong_gates(steps: int, warmup: int):
+def bench_strong_gates(steps: int, warmup: int, shift: float = -1.0):
     """The prefill workload's shapes with fast-forgetting gates,
-    g = logsigmoid(N(0,1) - 1) per channel (mean about -1.3 per token, so most
-    chunks decay far beyond -80): prefill and backward per call."""
+    g = logsigmoid(N(0,1) + shift) per channel: shift -1 (mean about -1.3 per
+    token, so most chunks decay far beyond -80 and take the mid-chunk
+    reference) or -4 (about -4 per token: every chunk beyond the mid
+    reference's range, on the exact paths): prefill and backward per call."""
     w = W.PREFILL_8K
     inp = W.prefill_inputs(batch=w.batch, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
                            dtype=w.dtype, device="cuda", seed=w.seed, init="normal",
-                           gate_shift=-1.0)
+                           gate_shift=shift)
     up = W.upstream_grads(batch=w.batch, seqlen=w.seqlen, heads=w.heads, dk=w.dk, dv=w.dv,
                           num_seqs=w.batch, dtype=w.dtype, device="cuda", seed=w.seed + 7)
     B, T, H, d = inp["q"].shape
@@ -635,7 +637,7 @@ def bench_strong_gates(steps: int, warmup: int):
         res[name] = e0.elapsed_time(e1) / n * 1e3
     finite = bool(torch.isfinite(o).all().item())
     return {"workload": "prefill B=1 H=32 T=8192 d=128 bf16 as above, gates g = "
-                        "logsigmoid(N(0,1) - 1) per channel, nonzero initial state",
+                        f"logsigmoid(N(0,1) {shift:+g}) per channel, nonzero initial state",
             "prefill_us_per_call": res["prefill"],
             "prefill_tokens_per_s": B * T / (res["prefill"] * 1e-6),
             "backward_us_per_call": res["backward"],
@@ -989,6 +991,7 @@ def main():
     m1, inputs_sha["prefill_1m_first_65536_tokens"] = bench_prefill_1m()
     progress("varlen, 1M tokens")
     sg = bench_strong_gates(max(2, args.steps // 2), 3)
+    xg = bench_strong_gates(2, 1, shift=-4.0)
     progress("strong gates")
     w = pf["w"]
     value = pf["tokens"] / (pf["ms"] * 1e-3)
@@ -1074,6 +1077,7 @@ def main():
         "varlen": vl,
         "prefill_1m": m1,
         "strong_gates": sg,
+        "exact_gates": xg,
         "wall_s_prefill_loop": pf["wall"],
     }
     if not args.no_cpu_baseline:
