@@ -153,7 +153,8 @@ def probe():
 _PROBE_KERNELS = (("kda_intra_chunk", "prefill", 2), ("kda_state_pass", "prefill", 2),
                   ("decode_step_kernel", "decode", 2), ("gate_norm_kernel", "epilogue", 2),
                   ("short_conv_kernel", "prologue", 2), ("kda_bwd_prep", "backward", 2),
-                  ("kda_bwd_state_pass", "backward", 2), ("kda_bwd_intra", "backward", 2))
+                  ("kda_bwd_state_pass", "backward", 2), ("kda_bwd_intra", "backward", 2),
+                  ("kda_bwd_exact", "backward", 2))
 
 
 def _probe_key(name: str, after_prologue: bool):
@@ -333,16 +334,18 @@ _STATS_ROWS = (
      "backward, 10 timed calls (trace)", "backward"),
     ("kda_bwd_intra<__hip_bfloat16, 128, false>", "kda_bwd_intra<bf16, 128, false>",
      "backward, 10 timed calls (trace)", "backward"),
+    ("kda_bwd_exact<__hip_bfloat16, 128, false>", "kda_bwd_exact<bf16, 128, false>",
+     "backward, 10 timed calls (trace; no chunk beyond the mid reference)", "backward"),
 )
 
 
 def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_FILE,
                        warmup: int = 50, steps: int = 20) -> str:
-    bwd_warmup, bwd_steps = min(warmup, 5), max(1, steps // 2)  # as main() runs the backward
     """Kernel durations from `rocprofv3 --kernel-trace --stats --output-format
     csv -- python3 bench.py --no-cpu-baseline`: the prefill kernels from the
     trace (the dispatches of the timed calls: 2 segments per call, after
     `warmup` warm-up calls), everything else pooled from the stats file."""
+    bwd_warmup, bwd_steps = min(warmup, 5), max(1, steps // 2)  # as main() runs the backward
     import csv
     trace = list(csv.DictReader(open(trace_csv)))
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
@@ -368,10 +371,10 @@ def write_kernel_stats(trace_csv: str, stats_csv: str, out: str = KERNEL_STATS_F
              "calls' last kernels) from the trace. The other rows pool every call of the "
              "kernel in the run (stats file).", "",
              "| Kernel | Workload | Calls | Average | Min | Max |", "|---|---|---|---|---|---|"]
-    # the backward section's timed calls: each call ends with one kda_bwd_intra
+    # the backward section's timed calls: each call ends with one kda_bwd_exact
     # dispatch, and the section runs the first backward calls of the run
     bwd_end = [int(r["End_Timestamp"]) for r in trace
-               if short(r["Kernel_Name"]) == "kda_bwd_intra<__hip_bfloat16, 128, false>"]
+               if short(r["Kernel_Name"]) == "kda_bwd_exact<__hip_bfloat16, 128, false>"]
     bwd_window = None
     if len(bwd_end) >= bwd_warmup + bwd_steps and bwd_warmup >= 1:
         bwd_window = (bwd_end[bwd_warmup - 1], bwd_end[bwd_warmup + bwd_steps - 1])
