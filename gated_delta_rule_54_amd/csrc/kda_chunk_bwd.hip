@@ -1821,310 +1821,330 @@ __global__ __launch_bounds__(kExactThreads) void kda_bwd_exact(
   float *dw = w + X::DW, *lm = w + X::LM, *dos = w + X::DOS, *ls = w + X::LS, *wds = w + X::WDS;
   float *kpm = w + X::KPM, *pm = w + X::PM, *tm = w + X::TM, *st = w + X::ST, *dst = w + X::DST;
   const int tid = threadIdx.x;
-  for (int64_t item = blockIdx.x; item < nslot * H; item += gridDim.x) {
-    const int64_t slot = item / H;
-    const int h = (int)(item % H);
-    ChunkLoc loc;
-    if (!locate(gm, slot, loc)) continue;
-    if (xflag[slot * H + h] == 0u) continue;
-    const int len = loc.len;
-    const int64_t row0 = loc.tok0 * H + h;
-    const T* S = states + (slot * H + h) * (int64_t)D * D;
-    const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
-    const T* tb = tinv + (slot * H + h) * (int64_t)(kC * kC);
-    // raw rows (zero past the chunk's end), beta, V and dO' = scale dO, T,
-    // S and dS' transposed
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, c = e % D;
-      const bool ok = r < len;
-      const int64_t o = (row0 + (int64_t)r * H) * D + c;
-      sk[e] = ok ? ld_f(k + o) : 0.f;
-      sq[e] = ok ? ld_f(q + o) : 0.f;
-      sg[e] = ok ? (GS ? g[row0 + (int64_t)r * H] : g[o]) : 0.f;
-      xm[e] = ok ? ld_f(v + o) : 0.f;
-      op[e] = ok ? scale * ld_f(d_o + o) : 0.f;
-    }
-    if (tid < kC) sb[tid] = tid < len ? beta[row0 + (int64_t)tid * H] : 0.f;
-    for (int e = tid; e < kC * kC; e += NT) tm[e] = (e % kC) <= (e / kC) ? ld_f(tb + e) : 0.f;
-    for (int e = tid; e < D * D; e += NT) {  // e = n D + c
-      const int n = e / D, c = e % D;
-      st[e] = ld_f(S + sblk<D>(c, n));
-      dst[e] = ld_f(dS + sblk<D>(c, n));
+  // Items (slot, head) = slot H + h.  Each pass looks at NT items at once,
+  // thread t at item base + t gridDim.x (its flag, after locating the slot),
+  // and lists the flagged ones in LDS; then the workgroup takes them one by
+  // one.  (Walking the items one flag load at a time cost ~25 us per call
+  // with nothing flagged.)
+  __shared__ int s_list[NT];
+  __shared__ int s_cnt;
+  const int64_t nitem = nslot * H;
+  for (int64_t base = blockIdx.x; base < nitem; base += (int64_t)gridDim.x * NT) {
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    {
+      const int64_t it = base + (int64_t)tid * gridDim.x;
+      ChunkLoc l0;
+      if (it < nitem && locate(gm, it / H, l0) && xflag[it] != 0u) s_list[atomicAdd(&s_cnt, 1)] = tid;
     }
     __syncthreads();
-    if (tid < kC) {
-      float a = 0.f, b = 0.f;
+    const int nflag = s_cnt;
+    for (int jf = 0; jf < nflag; ++jf) {
+      const int64_t item = base + (int64_t)s_list[jf] * gridDim.x;
+      const int64_t slot = item / H;
+      const int h = (int)(item % H);
+      ChunkLoc loc;
+      locate(gm, slot, loc);
+      const int len = loc.len;
+      const int64_t row0 = loc.tok0 * H + h;
+      const T* S = states + (slot * H + h) * (int64_t)D * D;
+      const T* dS = dstates + (slot * H + h) * (int64_t)D * D;
+      const T* tb = tinv + (slot * H + h) * (int64_t)(kC * kC);
+      // raw rows (zero past the chunk's end), beta, V and dO' = scale dO, T,
+      // S and dS' transposed
+      for (int e = tid; e < kC * D; e += NT) {
+        const int r = e / D, c = e % D;
+        const bool ok = r < len;
+        const int64_t o = (row0 + (int64_t)r * H) * D + c;
+        sk[e] = ok ? ld_f(k + o) : 0.f;
+        sq[e] = ok ? ld_f(q + o) : 0.f;
+        sg[e] = ok ? (GS ? g[row0 + (int64_t)r * H] : g[o]) : 0.f;
+        xm[e] = ok ? ld_f(v + o) : 0.f;
+        op[e] = ok ? scale * ld_f(d_o + o) : 0.f;
+      }
+      if (tid < kC) sb[tid] = tid < len ? beta[row0 + (int64_t)tid * H] : 0.f;
+      for (int e = tid; e < kC * kC; e += NT) tm[e] = (e % kC) <= (e / kC) ? ld_f(tb + e) : 0.f;
+      for (int e = tid; e < D * D; e += NT) {  // e = n D + c
+        const int n = e / D, c = e % D;
+        st[e] = ld_f(S + sblk<D>(c, n));
+        dst[e] = ld_f(dS + sblk<D>(c, n));
+      }
+      __syncthreads();
+      if (tid < kC) {
+        float a = 0.f, b = 0.f;
 #pragma unroll 4
-      for (int c = 0; c < D; ++c) {
-        a += sk[tid * D + c] * sk[tid * D + c];
-        b += sq[tid * D + c] * sq[tid * D + c];
-      }
-      rk[tid] = qk_l2norm ? rsqrtf(a + kNormEps) : 1.f;
-      rq[tid] = qk_l2norm ? rsqrtf(b + kNormEps) : 1.f;
-    } else if (tid < kC + D) {  // in-chunk cumulative gate of channel c
-      const int c = tid - kC;
-      float run = 0.f;
-      for (int r = 0; r < kC; ++r) {
-        run += sg[r * D + c];
-        sg[r * D + c] = run;
-      }
-      gam[c] = run;
-    }
-    __syncthreads();
-    // k^, q^; Kp = K^ o e^G, K~ = K^ o e^(gamma-G) (every exponent <= 0)
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, c = e % D;
-      const float kh = sk[e] * rk[r];
-      sk[e] = kh;
-      sq[e] *= rq[r];
-      kp[e] = kh * __expf(sg[e]);
-      kt[e] = kh * __expf(gam[c] - sg[e]);
-    }
-    __syncthreads();
-    // X = V - Kp S; Kp Km^T and P, each entry from its own exponents
-    for (int t = tid; t < TD; t += NT) {
-      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
-      float acc[4][4] = {};
-      ex_mm(acc, 0, D, [&](int c, float (&a)[4]) {
-        for (int i = 0; i < 4; ++i) a[i] = kp[(r0 + i) * D + c];
-      }, [&](int c, float (&b)[4]) { ex_ld4(S + sblk<D>(c, n0), b); });
-      for (int i = 0; i < 4; ++i) {
-        float x[4];
-        ex_ld4(xm + (r0 + i) * D + n0, x);
-        for (int j = 0; j < 4; ++j) x[j] -= acc[i][j];
-        ex_st4(xm + (r0 + i) * D + n0, x);
-      }
-    }
-    for (int t = tid; t < TC; t += NT) {
-      const int r0 = 4 * (t / (kC / 4)), i0 = 4 * (t % (kC / 4));
-      float a[4][4] = {}, pp[4][4] = {};
-      if (i0 <= r0 + 3) {
-#pragma unroll 2
         for (int c = 0; c < D; ++c) {
-          float kr[4], qr[4], gr[4], ki[4], gi[4];
-          for (int u = 0; u < 4; ++u) {
-            kr[u] = sk[(r0 + u) * D + c];
-            qr[u] = sq[(r0 + u) * D + c];
-            gr[u] = sg[(r0 + u) * D + c];
-            ki[u] = sk[(i0 + u) * D + c];
-            gi[u] = sg[(i0 + u) * D + c];
-          }
-          for (int u = 0; u < 4; ++u)
-            for (int j = 0; j < 4; ++j) {
-              const float x = i0 + j <= r0 + u ? ki[j] * __expf(gr[u] - gi[j]) : 0.f;
-              a[u][j] += kr[u] * x;
-              pp[u][j] += qr[u] * x;
+          a += sk[tid * D + c] * sk[tid * D + c];
+          b += sq[tid * D + c] * sq[tid * D + c];
+        }
+        rk[tid] = qk_l2norm ? rsqrtf(a + kNormEps) : 1.f;
+        rq[tid] = qk_l2norm ? rsqrtf(b + kNormEps) : 1.f;
+      } else if (tid < kC + D) {  // in-chunk cumulative gate of channel c
+        const int c = tid - kC;
+        float run = 0.f;
+        for (int r = 0; r < kC; ++r) {
+          run += sg[r * D + c];
+          sg[r * D + c] = run;
+        }
+        gam[c] = run;
+      }
+      __syncthreads();
+      // k^, q^; Kp = K^ o e^G, K~ = K^ o e^(gamma-G) (every exponent <= 0)
+      for (int e = tid; e < kC * D; e += NT) {
+        const int r = e / D, c = e % D;
+        const float kh = sk[e] * rk[r];
+        sk[e] = kh;
+        sq[e] *= rq[r];
+        kp[e] = kh * __expf(sg[e]);
+        kt[e] = kh * __expf(gam[c] - sg[e]);
+      }
+      __syncthreads();
+      // X = V - Kp S; Kp Km^T and P, each entry from its own exponents
+      for (int t = tid; t < TD; t += NT) {
+        const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+        float acc[4][4] = {};
+        ex_mm(acc, 0, D, [&](int c, float (&a)[4]) {
+          for (int i = 0; i < 4; ++i) a[i] = kp[(r0 + i) * D + c];
+        }, [&](int c, float (&b)[4]) { ex_ld4(S + sblk<D>(c, n0), b); });
+        for (int i = 0; i < 4; ++i) {
+          float x[4];
+          ex_ld4(xm + (r0 + i) * D + n0, x);
+          for (int j = 0; j < 4; ++j) x[j] -= acc[i][j];
+          ex_st4(xm + (r0 + i) * D + n0, x);
+        }
+      }
+      for (int t = tid; t < TC; t += NT) {
+        const int r0 = 4 * (t / (kC / 4)), i0 = 4 * (t % (kC / 4));
+        float a[4][4] = {}, pp[4][4] = {};
+        if (i0 <= r0 + 3) {
+#pragma unroll 2
+          for (int c = 0; c < D; ++c) {
+            float kr[4], qr[4], gr[4], ki[4], gi[4];
+            for (int u = 0; u < 4; ++u) {
+              kr[u] = sk[(r0 + u) * D + c];
+              qr[u] = sq[(r0 + u) * D + c];
+              gr[u] = sg[(r0 + u) * D + c];
+              ki[u] = sk[(i0 + u) * D + c];
+              gi[u] = sg[(i0 + u) * D + c];
             }
-        }
-      }
-      for (int u = 0; u < 4; ++u)
-        for (int j = 0; j < 4; ++j) {
-          const int r = r0 + u, i = i0 + j;
-          kpm[r * kC + i] = i < r ? a[u][j] : 0.f;
-          pm[r * kC + i] = i <= r ? pp[u][j] : 0.f;
-        }
-    }
-    __syncthreads();
-    // W = T Diag(beta) X
-    for (int t = tid; t < TD; t += NT) {
-      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
-      float acc[4][4] = {};
-      ex_mm(acc, 0, r0 + 4, [&](int i, float (&a)[4]) {
-        for (int u = 0; u < 4; ++u) a[u] = tm[(r0 + u) * kC + i] * sb[i];
-      }, [&](int i, float (&b)[4]) { ex_ld4(xm + i * D + n0, b); });
-      for (int i = 0; i < 4; ++i) ex_st4(wm + (r0 + i) * D + n0, acc[i]);
-    }
-    __syncthreads();
-    // dW = P^T dO' + K~ dS'
-    for (int t = tid; t < TD; t += NT) {
-      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
-      float acc[4][4] = {};
-      ex_mm(acc, r0, kC, [&](int s2, float (&a)[4]) { ex_ld4(pm + s2 * kC + r0, a); },
-            [&](int s2, float (&b)[4]) { ex_ld4(op + s2 * D + n0, b); });
-      ex_mm(acc, 0, D, [&](int c, float (&a)[4]) {
-        for (int u = 0; u < 4; ++u) a[u] = kt[(r0 + u) * D + c];
-      }, [&](int c, float (&b)[4]) { ex_ld4(dS + sblk<D>(c, n0), b); });
-      for (int i = 0; i < 4; ++i) ex_st4(dw + (r0 + i) * D + n0, acc[i]);
-    }
-    __syncthreads();
-    // L = T^T dW
-    for (int t = tid; t < TD; t += NT) {
-      const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
-      float acc[4][4] = {};
-      ex_mm(acc, r0, kC, [&](int s2, float (&a)[4]) { ex_ld4(tm + s2 * kC + r0, a); },
-            [&](int s2, float (&b)[4]) { ex_ld4(dw + s2 * D + n0, b); });
-      for (int i = 0; i < 4; ++i) ex_st4(lm + (r0 + i) * D + n0, acc[i]);
-    }
-    __syncthreads();
-    // dV = Diag(beta) L; dA = -tril_-1(L W^T), dP = tril(dO' W^T) (LDS);
-    // dO' S^T, L S^T, W dS'^T
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, n = e % D;
-      if (r < len) st_f(dv + (row0 + (int64_t)r * H) * D + n, sb[r] * lm[e]);
-    }
-    for (int t = tid; t < TC; t += NT) {
-      const int r0 = 4 * (t / (kC / 4)), i0 = 4 * (t % (kC / 4));
-      float a[4][4] = {}, pp[4][4] = {};
-      if (i0 <= r0 + 3) {
-#pragma unroll 1
-        for (int n = 0; n < D; n += 4) {
-          float lr[4][4], orow[4][4], wi[4][4];
-          for (int u = 0; u < 4; ++u) {
-            ex_ld4(lm + (r0 + u) * D + n, lr[u]);
-            ex_ld4(op + (r0 + u) * D + n, orow[u]);
-            ex_ld4(wm + (i0 + u) * D + n, wi[u]);
-          }
-          for (int u = 0; u < 4; ++u)
-            for (int j = 0; j < 4; ++j)
-              for (int e = 0; e < 4; ++e) {
-                a[u][j] += lr[u][e] * wi[j][e];
-                pp[u][j] += orow[u][e] * wi[j][e];
+            for (int u = 0; u < 4; ++u)
+              for (int j = 0; j < 4; ++j) {
+                const float x = i0 + j <= r0 + u ? ki[j] * __expf(gr[u] - gi[j]) : 0.f;
+                a[u][j] += kr[u] * x;
+                pp[u][j] += qr[u] * x;
               }
+          }
         }
-      }
-      for (int u = 0; u < 4; ++u)
-        for (int j = 0; j < 4; ++j) {
-          const int r = r0 + u, i = i0 + j;
-          lda[r * kC + i] = i < r ? -a[u][j] : 0.f;
-          ldp[r * kC + i] = i <= r ? pp[u][j] : 0.f;
-        }
-    }
-    for (int t = tid; t < TD; t += NT) {
-      const int r0 = 4 * (t / (D / 4)), c0 = 4 * (t % (D / 4));
-      float a1[4][4] = {}, a2[4][4] = {}, a3[4][4] = {};
-#pragma unroll 1
-      for (int n = 0; n < D; ++n) {
-        float o4[4], l4[4], w4[4], s4[4], d4[4];
-        for (int u = 0; u < 4; ++u) {
-          o4[u] = op[(r0 + u) * D + n];
-          l4[u] = lm[(r0 + u) * D + n];
-          w4[u] = wm[(r0 + u) * D + n];
-        }
-        ex_ld4(st + n * D + c0, s4);
-        ex_ld4(dst + n * D + c0, d4);
         for (int u = 0; u < 4; ++u)
           for (int j = 0; j < 4; ++j) {
-            a1[u][j] += o4[u] * s4[j];
-            a2[u][j] += l4[u] * s4[j];
-            a3[u][j] += w4[u] * d4[j];
+            const int r = r0 + u, i = i0 + j;
+            kpm[r * kC + i] = i < r ? a[u][j] : 0.f;
+            pm[r * kC + i] = i <= r ? pp[u][j] : 0.f;
           }
       }
-      for (int u = 0; u < 4; ++u) {
-        ex_st4(dos + (r0 + u) * D + c0, a1[u]);
-        ex_st4(ls + (r0 + u) * D + c0, a2[u]);
-        ex_st4(wds + (r0 + u) * D + c0, a3[u]);
+      __syncthreads();
+      // W = T Diag(beta) X
+      for (int t = tid; t < TD; t += NT) {
+        const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+        float acc[4][4] = {};
+        ex_mm(acc, 0, r0 + 4, [&](int i, float (&a)[4]) {
+          for (int u = 0; u < 4; ++u) a[u] = tm[(r0 + u) * kC + i] * sb[i];
+        }, [&](int i, float (&b)[4]) { ex_ld4(xm + i * D + n0, b); });
+        for (int i = 0; i < 4; ++i) ex_st4(wm + (r0 + i) * D + n0, acc[i]);
       }
-    }
-    __syncthreads();
-    // dbeta = rowsum(L o X) + rowsum(dA o Kp Km^T)
-    if (tid < len) {
-      const int r = tid;
-      float a = 0.f;
-#pragma unroll 4
-      for (int n = 0; n < D; ++n) a += lm[r * D + n] * xm[r * D + n];
-      for (int i = 0; i < r; ++i) a += lda[r * kC + i] * kpm[r * kC + i];
-      dbeta[row0 + (int64_t)r * H] = a;
-    }
-    // per element: dq^ (into dos), dk^ (into ls), dK~ o K~ / k^ (into wds)
-    // and dG (into dw)
-    for (int t = tid; t < TD; t += NT) {
-      const int r0 = 4 * (t / (D / 4)), c0 = 4 * (t % (D / 4));
-      float gr[4][4], dqv[4][4], tp[4][4], tmv[4][4];
-      for (int u = 0; u < 4; ++u) {
-        ex_ld4(sg + (r0 + u) * D + c0, gr[u]);
-        float a1[4], a2[4];
-        ex_ld4(dos + (r0 + u) * D + c0, a1);
-        ex_ld4(ls + (r0 + u) * D + c0, a2);
-        for (int j = 0; j < 4; ++j) {
-          const float eg = __expf(gr[u][j]);
-          dqv[u][j] = eg * a1[j];
-          tp[u][j] = -sb[r0 + u] * eg * a2[j];
-          tmv[u][j] = 0.f;
-        }
+      __syncthreads();
+      // dW = P^T dO' + K~ dS'
+      for (int t = tid; t < TD; t += NT) {
+        const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+        float acc[4][4] = {};
+        ex_mm(acc, r0, kC, [&](int s2, float (&a)[4]) { ex_ld4(pm + s2 * kC + r0, a); },
+              [&](int s2, float (&b)[4]) { ex_ld4(op + s2 * D + n0, b); });
+        ex_mm(acc, 0, D, [&](int c, float (&a)[4]) {
+          for (int u = 0; u < 4; ++u) a[u] = kt[(r0 + u) * D + c];
+        }, [&](int c, float (&b)[4]) { ex_ld4(dS + sblk<D>(c, n0), b); });
+        for (int i = 0; i < 4; ++i) ex_st4(dw + (r0 + i) * D + n0, acc[i]);
       }
+      __syncthreads();
+      // L = T^T dW
+      for (int t = tid; t < TD; t += NT) {
+        const int r0 = 4 * (t / (D / 4)), n0 = 4 * (t % (D / 4));
+        float acc[4][4] = {};
+        ex_mm(acc, r0, kC, [&](int s2, float (&a)[4]) { ex_ld4(tm + s2 * kC + r0, a); },
+              [&](int s2, float (&b)[4]) { ex_ld4(dw + s2 * D + n0, b); });
+        for (int i = 0; i < 4; ++i) ex_st4(lm + (r0 + i) * D + n0, acc[i]);
+      }
+      __syncthreads();
+      // dV = Diag(beta) L; dA = -tril_-1(L W^T), dP = tril(dO' W^T) (LDS);
+      // dO' S^T, L S^T, W dS'^T
+      for (int e = tid; e < kC * D; e += NT) {
+        const int r = e / D, n = e % D;
+        if (r < len) st_f(dv + (row0 + (int64_t)r * H) * D + n, sb[r] * lm[e]);
+      }
+      for (int t = tid; t < TC; t += NT) {
+        const int r0 = 4 * (t / (kC / 4)), i0 = 4 * (t % (kC / 4));
+        float a[4][4] = {}, pp[4][4] = {};
+        if (i0 <= r0 + 3) {
 #pragma unroll 1
-      for (int i = 0; i < kC; ++i) {
-        float ki[4], qi[4], gi[4], pc[4], ac[4];
-        ex_ld4(sk + i * D + c0, ki);
-        ex_ld4(sq + i * D + c0, qi);
-        ex_ld4(sg + i * D + c0, gi);
-        ex_ld4(ldp + i * kC + r0, pc);  // dP_(i, r0..r0+3)
-        ex_ld4(lda + i * kC + r0, ac);  // dA_(i, r0..r0+3)
-        const float bi = sb[i];
-        for (int u = 0; u < 4; ++u) {
-          const int r = r0 + u;
-          const float pr = ldp[r * kC + i], br = sb[r] * lda[r * kC + i];
-          for (int j = 0; j < 4; ++j) {
-            // i <= r: e^(G_rc - G_ic) <= 1; i >= r: e^(G_ic - G_rc) <= 1
-            const float x = i <= r ? __expf(gr[u][j] - gi[j]) : 0.f;
-            const float y = i >= r ? __expf(gi[j] - gr[u][j]) : 0.f;
-            dqv[u][j] += pr * ki[j] * x;
-            tp[u][j] += br * ki[j] * x;
-            tmv[u][j] += (pc[u] * qi[j] + bi * ac[u] * ki[j]) * y;
+          for (int n = 0; n < D; n += 4) {
+            float lr[4][4], orow[4][4], wi[4][4];
+            for (int u = 0; u < 4; ++u) {
+              ex_ld4(lm + (r0 + u) * D + n, lr[u]);
+              ex_ld4(op + (r0 + u) * D + n, orow[u]);
+              ex_ld4(wm + (i0 + u) * D + n, wi[u]);
+            }
+            for (int u = 0; u < 4; ++u)
+              for (int j = 0; j < 4; ++j)
+                for (int e = 0; e < 4; ++e) {
+                  a[u][j] += lr[u][e] * wi[j][e];
+                  pp[u][j] += orow[u][e] * wi[j][e];
+                }
           }
         }
+        for (int u = 0; u < 4; ++u)
+          for (int j = 0; j < 4; ++j) {
+            const int r = r0 + u, i = i0 + j;
+            lda[r * kC + i] = i < r ? -a[u][j] : 0.f;
+            ldp[r * kC + i] = i <= r ? pp[u][j] : 0.f;
+          }
       }
-      for (int u = 0; u < 4; ++u) {
-        float w4[4], kr[4], qr[4], o1[4], o2[4], o3[4], o4[4];
-        ex_ld4(wds + (r0 + u) * D + c0, w4);
-        ex_ld4(sk + (r0 + u) * D + c0, kr);
-        ex_ld4(sq + (r0 + u) * D + c0, qr);
-        for (int j = 0; j < 4; ++j) {
-          const float ttv = __expf(gam[c0 + j] - gr[u][j]) * w4[j];
-          o1[j] = dqv[u][j];
-          o2[j] = tp[u][j] + tmv[u][j] + ttv;
-          o3[j] = kr[j] * ttv;  // dK~ o K~, summed over rows for dgamma
-          o4[j] = kr[j] * (tp[u][j] - tmv[u][j] - ttv) + qr[j] * dqv[u][j];
+      for (int t = tid; t < TD; t += NT) {
+        const int r0 = 4 * (t / (D / 4)), c0 = 4 * (t % (D / 4));
+        float a1[4][4] = {}, a2[4][4] = {}, a3[4][4] = {};
+#pragma unroll 1
+        for (int n = 0; n < D; ++n) {
+          float o4[4], l4[4], w4[4], s4[4], d4[4];
+          for (int u = 0; u < 4; ++u) {
+            o4[u] = op[(r0 + u) * D + n];
+            l4[u] = lm[(r0 + u) * D + n];
+            w4[u] = wm[(r0 + u) * D + n];
+          }
+          ex_ld4(st + n * D + c0, s4);
+          ex_ld4(dst + n * D + c0, d4);
+          for (int u = 0; u < 4; ++u)
+            for (int j = 0; j < 4; ++j) {
+              a1[u][j] += o4[u] * s4[j];
+              a2[u][j] += l4[u] * s4[j];
+              a3[u][j] += w4[u] * d4[j];
+            }
         }
-        ex_st4(dos + (r0 + u) * D + c0, o1);
-        ex_st4(ls + (r0 + u) * D + c0, o2);
-        ex_st4(wds + (r0 + u) * D + c0, o3);
-        ex_st4(dw + (r0 + u) * D + c0, o4);
+        for (int u = 0; u < 4; ++u) {
+          ex_st4(dos + (r0 + u) * D + c0, a1[u]);
+          ex_st4(ls + (r0 + u) * D + c0, a2[u]);
+          ex_st4(wds + (r0 + u) * D + c0, a3[u]);
+        }
       }
-    }
-    __syncthreads();
-    // dgamma = colsum(dK~ o K~) + e^gamma o rowsum(S o dS'), on the last row;
-    // then the in-chunk prefix sum reversed; the norms' row dot products
-    if (tid < D) {
-      const int c = tid;
-      float a = 0.f, b = 0.f;
-      for (int r = 0; r < kC; ++r) a += wds[r * D + c];
+      __syncthreads();
+      // dbeta = rowsum(L o X) + rowsum(dA o Kp Km^T)
+      if (tid < len) {
+        const int r = tid;
+        float a = 0.f;
 #pragma unroll 4
-      for (int n = 0; n < D; ++n) b += st[n * D + c] * dst[n * D + c];
-      float run = a + __expf(gam[c]) * b;
-      for (int r = kC - 1; r >= 0; --r) {
-        run += dw[r * D + c];
-        dw[r * D + c] = run;
+        for (int n = 0; n < D; ++n) a += lm[r * D + n] * xm[r * D + n];
+        for (int i = 0; i < r; ++i) a += lda[r * kC + i] * kpm[r * kC + i];
+        dbeta[row0 + (int64_t)r * H] = a;
       }
-    } else if (tid < D + kC) {
-      const int r = tid - D;
-      float a = 0.f, b = 0.f;
+      // per element: dq^ (into dos), dk^ (into ls), dK~ o K~ / k^ (into wds)
+      // and dG (into dw)
+      for (int t = tid; t < TD; t += NT) {
+        const int r0 = 4 * (t / (D / 4)), c0 = 4 * (t % (D / 4));
+        float gr[4][4], dqv[4][4], tp[4][4], tmv[4][4];
+        for (int u = 0; u < 4; ++u) {
+          ex_ld4(sg + (r0 + u) * D + c0, gr[u]);
+          float a1[4], a2[4];
+          ex_ld4(dos + (r0 + u) * D + c0, a1);
+          ex_ld4(ls + (r0 + u) * D + c0, a2);
+          for (int j = 0; j < 4; ++j) {
+            const float eg = __expf(gr[u][j]);
+            dqv[u][j] = eg * a1[j];
+            tp[u][j] = -sb[r0 + u] * eg * a2[j];
+            tmv[u][j] = 0.f;
+          }
+        }
+#pragma unroll 1
+        for (int i = 0; i < kC; ++i) {
+          float ki[4], qi[4], gi[4], pc[4], ac[4];
+          ex_ld4(sk + i * D + c0, ki);
+          ex_ld4(sq + i * D + c0, qi);
+          ex_ld4(sg + i * D + c0, gi);
+          ex_ld4(ldp + i * kC + r0, pc);  // dP_(i, r0..r0+3)
+          ex_ld4(lda + i * kC + r0, ac);  // dA_(i, r0..r0+3)
+          const float bi = sb[i];
+          for (int u = 0; u < 4; ++u) {
+            const int r = r0 + u;
+            const float pr = ldp[r * kC + i], br = sb[r] * lda[r * kC + i];
+            for (int j = 0; j < 4; ++j) {
+              // i <= r: e^(G_rc - G_ic) <= 1; i >= r: e^(G_ic - G_rc) <= 1
+              const float x = i <= r ? __expf(gr[u][j] - gi[j]) : 0.f;
+              const float y = i >= r ? __expf(gi[j] - gr[u][j]) : 0.f;
+              dqv[u][j] += pr * ki[j] * x;
+              tp[u][j] += br * ki[j] * x;
+              tmv[u][j] += (pc[u] * qi[j] + bi * ac[u] * ki[j]) * y;
+            }
+          }
+        }
+        for (int u = 0; u < 4; ++u) {
+          float w4[4], kr[4], qr[4], o1[4], o2[4], o3[4], o4[4];
+          ex_ld4(wds + (r0 + u) * D + c0, w4);
+          ex_ld4(sk + (r0 + u) * D + c0, kr);
+          ex_ld4(sq + (r0 + u) * D + c0, qr);
+          for (int j = 0; j < 4; ++j) {
+            const float ttv = __expf(gam[c0 + j] - gr[u][j]) * w4[j];
+            o1[j] = dqv[u][j];
+            o2[j] = tp[u][j] + tmv[u][j] + ttv;
+            o3[j] = kr[j] * ttv;  // dK~ o K~, summed over rows for dgamma
+            o4[j] = kr[j] * (tp[u][j] - tmv[u][j] - ttv) + qr[j] * dqv[u][j];
+          }
+          ex_st4(dos + (r0 + u) * D + c0, o1);
+          ex_st4(ls + (r0 + u) * D + c0, o2);
+          ex_st4(wds + (r0 + u) * D + c0, o3);
+          ex_st4(dw + (r0 + u) * D + c0, o4);
+        }
+      }
+      __syncthreads();
+      // dgamma = colsum(dK~ o K~) + e^gamma o rowsum(S o dS'), on the last row;
+      // then the in-chunk prefix sum reversed; the norms' row dot products
+      if (tid < D) {
+        const int c = tid;
+        float a = 0.f, b = 0.f;
+        for (int r = 0; r < kC; ++r) a += wds[r * D + c];
 #pragma unroll 4
-      for (int c = 0; c < D; ++c) {
-        a += sq[r * D + c] * dos[r * D + c];
-        b += sk[r * D + c] * ls[r * D + c];
+        for (int n = 0; n < D; ++n) b += st[n * D + c] * dst[n * D + c];
+        float run = a + __expf(gam[c]) * b;
+        for (int r = kC - 1; r >= 0; --r) {
+          run += dw[r * D + c];
+          dw[r * D + c] = run;
+        }
+      } else if (tid < D + kC) {
+        const int r = tid - D;
+        float a = 0.f, b = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < D; ++c) {
+          a += sq[r * D + c] * dos[r * D + c];
+          b += sk[r * D + c] * ls[r * D + c];
+        }
+        dotq[r] = a;
+        dotk[r] = b;
       }
-      dotq[r] = a;
-      dotk[r] = b;
+      __syncthreads();
+      // outputs: dg, and dq, dk through the norm (dx = r (dx^ - (x^ . dx^) x^))
+      for (int e = tid; e < kC * D; e += NT) {
+        const int r = e / D, c = e % D;
+        if (r >= len) continue;
+        const int64_t o = (row0 + (int64_t)r * H) * D + c;
+        const float vq = qk_l2norm ? rq[r] * (dos[e] - dotq[r] * sq[e]) : dos[e];
+        const float vk = qk_l2norm ? rk[r] * (ls[e] - dotk[r] * sk[e]) : ls[e];
+        st_f(dq + o, vq);
+        st_f(dk + o, vk);
+        if (!GS) dg[o] = dw[e];
+      }
+      if (GS && tid < len) {
+        float a = 0.f;
+        for (int c = 0; c < D; ++c) a += dw[tid * D + c];
+        dg[row0 + (int64_t)tid * H] = a;
+      }
+      __syncthreads();  // LDS and scratch are reused by the next item
     }
-    __syncthreads();
-    // outputs: dg, and dq, dk through the norm (dx = r (dx^ - (x^ . dx^) x^))
-    for (int e = tid; e < kC * D; e += NT) {
-      const int r = e / D, c = e % D;
-      if (r >= len) continue;
-      const int64_t o = (row0 + (int64_t)r * H) * D + c;
-      const float vq = qk_l2norm ? rq[r] * (dos[e] - dotq[r] * sq[e]) : dos[e];
-      const float vk = qk_l2norm ? rk[r] * (ls[e] - dotk[r] * sk[e]) : ls[e];
-      st_f(dq + o, vq);
-      st_f(dk + o, vk);
-      if (!GS) dg[o] = dw[e];
-    }
-    if (GS && tid < len) {
-      float a = 0.f;
-      for (int c = 0; c < D; ++c) a += dw[tid * D + c];
-      dg[row0 + (int64_t)tid * H] = a;
-    }
-    __syncthreads();  // LDS and scratch are reused by the next item
+    __syncthreads();  // s_cnt and s_list are rewritten by the next pass
   }
 }
 
