@@ -121,7 +121,7 @@ struct K1Lds {
   static constexpr int NPART = k1_threads<T, D>() / NCP;   // row parts
   static constexpr int RPP = kC / NPART;                   // rows per part (8 or 16)
   static_assert(RPP % 8 == 0, "transposed stores take 8 rows at a time");
-  static_assert(3 * kC * 17 * 4 <= REG, "exact-path staging must fit a region");
+  static_assert(3 * 16 * (kC + 4) * 4 <= REG, "exact-path staging must fit a region");
   static_assert(NPART * D * 4 <= REG, "the scan partials must fit a region");
   // + per row: 1/|k|, 1/|q|, beta; per channel: e^(gamma-m).  (Not one
   // float more: at 512 more bytes three workgroups no longer share a CU --
@@ -215,11 +215,15 @@ constexpr int k1_waves_per_simd() {
 }
 
 // Exact-decay path of A and P: each entry from its own exponent difference
-// (<= 0), with G, k^ and q^ staged in blocks of 16 channels.  k^ and q^ are
-// the row-major LDS tiles khat and qhat; G is formed again from g (as the
-// kernel forms it: the prefix sum over the thread's rows, plus the part
-// offset).  Out of line: few chunks take it, and inlined it would set the
-// register budget of the common path.  Every thread of the workgroup calls it.
+// (<= 0), with G, k^ and q^ staged in blocks of 16 channels, channel-major
+// (a row of 64 chunk rows per channel).  k^ and q^ are the row-major LDS
+// tiles khat and qhat; G is formed again from g (as the kernel forms it: the
+// prefix sum over the thread's rows, plus the part offset), once, before the
+// blocks.  Thread t < 136 owns the 4 x 4 tile t of the lower triangle
+// (row block rb, column block ib <= rb, t = rb (rb + 1) / 2 + ib) and reads
+// its four rows and four columns of a channel as 16-byte pieces.  Out of
+// line: few chunks take it, and inlined it would set the register budget of
+// the common path.  Every thread of the workgroup calls it.
 template <typename T, int D, bool GS>
 __device__ __forceinline__ void k1_exact_ap(
     const T* khat, const T* qhat, float* stage, float* sA, const float* s_beta, T* wP,
@@ -227,69 +231,85 @@ __device__ __forceinline__ void k1_exact_ap(
   using L = K1Lds<T, D>;
   using M = Mma<T>;
   constexpr int NCP = L::NCP, RPP = L::RPP, NT = k1_threads<T, D>();
+  constexpr int NTILE = (kC / 4) * (kC / 4 + 1) / 2;  // 4 x 4 tiles of the lower triangle
+  static_assert(NTILE <= NT, "one lower-triangle tile per thread");
   const int tid = threadIdx.x, cp = tid % NCP, part = tid / NCP;
   const int c0 = 2 * cp, r0p = part * RPP;
-  // Thread tid takes the lower-triangle entries e = tid + m NT, e = r(r+1)/2 + i
-  // (row and column are formed again at each use, to keep registers free).
-  constexpr int NE = (kC * (kC + 1) / 2 + NT - 1) / NT;
-  auto entry_r = [&](int m) {
-    const int e = tid + m * NT;
-    int r = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
-    while ((r + 1) * (r + 2) / 2 <= e) ++r;
-    while (r * (r + 1) / 2 > e) --r;
-    return e < kC * (kC + 1) / 2 ? r : -1;
-  };
-  auto entry_i = [&](int m, int r) { return tid + m * NT - r * (r + 1) / 2; };
-  float ea[NE], ep[NE];
-#pragma unroll
-  for (int m = 0; m < NE; ++m) { ea[m] = 0.f; ep[m] = 0.f; }
-  // rows of 16 channels at a stride of 17 floats: the lanes of a wave read
-  // consecutive rows i of one channel, which a stride of 16 put in one bank
-  constexpr int SL = 17;
+  // channel-major rows of 64 chunk rows, 16-byte aligned
+  constexpr int SR = kC + 4;
   float* stG = stage;
-  float* stK = stG + kC * SL;
-  float* stQ = stK + kC * SL;
+  float* stK = stG + 16 * SR;
+  float* stQ = stK + 16 * SR;
+  // this thread's G (channels c0, c0 + 1, rows r0p ..), all loads issued at once
+  float2 G[RPP];
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const int rr = min(r0p + j, len - 1);
+    const float2 gj = GS ? make_float2(gb[rr * H], gb[rr * H]) : ld2(gb + rr * rowstride + c0);
+    G[j] = r0p + j < len ? gj : make_float2(0.f, 0.f);
+  }
+#pragma unroll
+  for (int j = 1; j < RPP; ++j) { G[j].x += G[j - 1].x; G[j].y += G[j - 1].y; }
+  // this thread's tile
+  int rb = 0;
+  while ((rb + 1) * (rb + 2) / 2 <= tid) ++rb;
+  const int ib = tid - rb * (rb + 1) / 2;
+  const bool owner = tid < NTILE, diag = rb == ib;
+  float ea[4][4], ep[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { ea[u][j] = 0.f; ep[u][j] = 0.f; }
   for (int cb = 0; cb < D / 16; ++cb) {
     if (c0 / 16 == cb) {
-      float2 run = make_float2(0.f, 0.f);
+      const int cc = c0 % 16;
 #pragma unroll
       for (int j = 0; j < RPP; ++j) {
-        const int r = r0p + j, cc = c0 % 16;
-        const int rr = min(r, len - 1);
-        const float2 gj = GS ? make_float2(gb[rr * H], gb[rr * H]) : ld2(gb + rr * rowstride + c0);
-        const float2 gm = r < len ? gj : make_float2(0.f, 0.f);
-        run = j == 0 ? gm : make_float2(gm.x + run.x, gm.y + run.y);
-        stG[r * SL + cc] = run.x + offx;
-        stG[r * SL + cc + 1] = run.y + offy;
+        const int r = r0p + j;
+        stG[cc * SR + r] = G[j].x + offx;
+        stG[(cc + 1) * SR + r] = G[j].y + offy;
         const float2 kh = ld2(khat + r * L::LDR + c0), qh = ld2(qhat + r * L::LDR + c0);
-        stK[r * SL + cc] = kh.x; stK[r * SL + cc + 1] = kh.y;
-        stQ[r * SL + cc] = qh.x; stQ[r * SL + cc + 1] = qh.y;
+        stK[cc * SR + r] = kh.x; stK[(cc + 1) * SR + r] = kh.y;
+        stQ[cc * SR + r] = qh.x; stQ[(cc + 1) * SR + r] = qh.y;
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < NE; ++m) {
-      const int r = entry_r(m);
-      if (r < 0) continue;
-      const int i = entry_i(m, r);
-#pragma unroll 1
+    if (owner) {
+#pragma unroll 2
       for (int c = 0; c < 16; ++c) {
-        const float e = __expf(stG[r * SL + c] - stG[i * SL + c]);
-        const float ki = stK[i * SL + c] * e;
-        ea[m] += stK[r * SL + c] * ki;
-        ep[m] += stQ[r * SL + c] * ki;
+        const float4 gr = *reinterpret_cast<const float4*>(stG + c * SR + 4 * rb);
+        const float4 gi = *reinterpret_cast<const float4*>(stG + c * SR + 4 * ib);
+        const float4 kr = *reinterpret_cast<const float4*>(stK + c * SR + 4 * rb);
+        const float4 ki = *reinterpret_cast<const float4*>(stK + c * SR + 4 * ib);
+        const float4 qr = *reinterpret_cast<const float4*>(stQ + c * SR + 4 * rb);
+        const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, giv[4] = {gi.x, gi.y, gi.z, gi.w};
+        const float krv[4] = {kr.x, kr.y, kr.z, kr.w}, kiv[4] = {ki.x, ki.y, ki.z, ki.w};
+        const float qrv[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // above the diagonal G_r - G_i >= 0 may overflow: not formed
+            const float x = (!diag || j <= u) ? kiv[j] * __expf(grv[u] - giv[j]) : 0.f;
+            ea[u][j] += krv[u] * x;
+            ep[u][j] += qrv[u] * x;
+          }
       }
     }
     __syncthreads();
   }
   // sA aliases qhat: every read of it ended at the barrier above
+  if (owner) {
 #pragma unroll
-  for (int m = 0; m < NE; ++m) {
-    const int r = entry_r(m);
-    if (r < 0) continue;
-    const int i = entry_i(m, r);
-    sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[m] : 0.f;
-    st_f(wP + fnat<T>(r, i, kC / M::KSTEP), ep[m]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * rb + u, i = 4 * ib + j;
+        if (i <= r) {
+          sA[r * L::LDA + i] = i < r ? s_beta[r] * ea[u][j] : 0.f;
+          st_f(wP + fnat<T>(r, i, kC / M::KSTEP), ep[u][j]);
+        }
+      }
   }
   // the exact path writes no upper-triangle entries of the diagonal blocks
   for (int e = tid; e < kC * kC; e += NT) {

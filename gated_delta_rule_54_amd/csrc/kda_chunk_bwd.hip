@@ -1746,7 +1746,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 // No MFMA and one chunk per workgroup: only for chunks the fast kernels
 // cannot represent.
 constexpr int kExactThreads = 256;
-constexpr int kExactMaxGroups = 128;
+constexpr int kExactMaxGroups = 256;  // one per CU (132 KB of LDS each)
 template <int D>
 struct ExScr {
   static constexpr int64_t CD = (int64_t)kC * D, CC = (int64_t)kC * kC;

@@ -202,7 +202,7 @@ kda_status_t kda_chunk_fwd_conv(const kda_desc_t* desc, const void* xq, const vo
  * the entering state and its gradient (2 x dk x dv elements of dtype: they
  * serve only as operands of products in that type, and in one fp32 row sum
  * of the gate gradient) and the reverse pass's operands ((dk + 64) x dk
- * elements of dtype), plus the exact path's fp32 scratch (at most 62 MB at
+ * elements of dtype), plus the exact path's fp32 scratch (at most 124 MB at
  * dk = 128). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_desc_t* desc);
 
