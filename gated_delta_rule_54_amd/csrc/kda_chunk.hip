@@ -214,6 +214,98 @@ constexpr int k1_waves_per_simd() {
   return (sizeof(T) == 4 && D == 128) ? 1 : (CONV ? 2 : 3) * k1_threads<T, D>() / 256;
 }
 
+// One operand fragment from KPL floats (bf16: rounded to nearest even).
+template <typename T> __device__ __forceinline__ typename Mma<T>::frag frag_of(const float* x);
+template <> __device__ __forceinline__ bf16x8_t frag_of<bf16>(const float* x) {
+  return __builtin_bit_cast(bf16x8_t, (u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                               pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])}));
+}
+template <> __device__ __forceinline__ float frag_of<float>(const float* x) { return x[0]; }
+
+// A and P of a chunk beyond the mid reference's range on MFMA, block pair by
+// block pair with a reference per pair (see k1_exact_ap, which checks that
+// the reference rows keep every kept factor in range).  G is staged 32
+// channels at a time; each wave forms its pairs' operand fragments from k^,
+// q^ (LDS) and the staged G in registers, the same 10 pairs per wave as the
+// common path, and writes A and P as the common path does.
+template <typename T, int D, int RPP>
+__device__ __forceinline__ void k1_blocked_ap(const T* khat, const T* qhat, float* stage,
+                                              float* sA, const float* s_beta, T* wP,
+                                              const float2 (&G)[RPP], float offx, float offy) {
+  using L = K1Lds<T, D>;
+  using M = Mma<T>;
+  constexpr int NCP = L::NCP, NT = k1_threads<T, D>(), NW = NT / 64;
+  constexpr int NPAIR = 10, PMAX = (NPAIR + NW - 1) / NW, SG = 32 + 4, KPL = M::KPL;
+  static_assert(kC * SG * 4 <= L::REG, "the G stage must fit a region");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cp = tid % NCP, part = tid / NCP, c0 = 2 * cp, r0p = part * RPP;
+  auto pair_I = [](int p) { return p < 4 ? 0 : p < 7 ? 1 : p < 9 ? 2 : 3; };
+  auto pair_R = [](int p) { return p < 4 ? p : p < 7 ? p - 3 : p < 9 ? p - 5 : 3; };
+  f32x4_t accA[PMAX], accP[PMAX];
+#pragma unroll
+  for (int t = 0; t < PMAX; ++t) {
+    accA[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accP[t] = accA[t];
+  }
+  for (int cb = 0; cb < D / 32; ++cb) {
+    if (c0 / 32 == cb) {
+#pragma unroll
+      for (int j = 0; j < RPP; ++j) {
+        stage[(r0p + j) * SG + c0 % 32] = G[j].x + offx;
+        stage[(r0p + j) * SG + c0 % 32 + 1] = G[j].y + offy;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < PMAX; ++t) {
+      const int p = wave + t * NW;
+      if (p >= NPAIR) continue;
+      const int I = pair_I(p), R = pair_R(p);
+      const int ri = 16 * I + (lane & 15), rr = 16 * R + (lane & 15);
+      const int mrow = I == R ? 16 * I + 7 : 16 * I + 15;
+#pragma unroll 1
+      for (int ks = 0; ks < 32 / M::KSTEP; ++ks) {
+        const int cl = ks * M::KSTEP + KPL * (lane >> 4);  // channel within the block
+        const int cg = 32 * cb + cl;
+        float m[KPL], x[KPL], y[KPL];
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) m[e] = stage[mrow * SG + cl + e];
+#pragma unroll
+        for (int e = 0; e < KPL; ++e)
+          x[e] = ld_f(khat + ri * L::LDR + cg + e) * __expf(m[e] - stage[ri * SG + cl + e]);
+        const auto fa = frag_of<T>(x);
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          const float f = __expf(stage[rr * SG + cl + e] - m[e]);
+          x[e] = ld_f(khat + rr * L::LDR + cg + e) * f;
+          y[e] = ld_f(qhat + rr * L::LDR + cg + e) * f;
+        }
+        accA[t] = M::mma(fa, frag_of<T>(x), accA[t]);
+        accP[t] = M::mma(fa, frag_of<T>(y), accP[t]);
+      }
+    }
+    __syncthreads();
+  }
+  // sA aliases qhat: every read of it ended at the barrier above
+#pragma unroll
+  for (int t = 0; t < PMAX; ++t) {
+    const int p = wave + t * NW;
+    if (p >= NPAIR) continue;
+    const int I = pair_I(p), R = pair_R(p);
+    const int r = R * 16 + (lane & 15);
+    const int i0 = I * 16 + 4 * (lane >> 4);
+    const float br = s_beta[r];
+    float a4[4], p4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // above the diagonal the products may overflow: not kept
+      a4[j] = (i0 + j < r) ? br * accA[t][j] : 0.f;
+      p4[j] = (i0 + j <= r) ? accP[t][j] : 0.f;
+    }
+    *reinterpret_cast<float4*>(sA + r * L::LDA + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+    st_fnat4(wP, kC / M::KSTEP, r, i0, p4[0], p4[1], p4[2], p4[3]);
+  }
+}
+
 // Exact-decay path of A and P: each entry from its own exponent difference
 // (<= 0), with G, k^ and q^ staged in blocks of 16 channels, channel-major
 // (a row of 64 chunk rows per channel).  k^ and q^ are the row-major LDS
@@ -250,6 +342,27 @@ __device__ __forceinline__ void k1_exact_ap(
   }
 #pragma unroll
   for (int j = 1; j < RPP; ++j) { G[j].x += G[j - 1].x; G[j].y += G[j - 1].y; }
+  // Blocked form, on MFMA, when each 8-row half of every 16-row block decays
+  // by at most 80 per channel: block pair (R, I) of A and P is
+  // (K_I o e^(m - G_I)) (K_R o e^(G_R - m))^T (and Q_R for P) with m = G of
+  // row 16 I + 15 when R > I (both factors <= 1 for any gate) and of row
+  // 16 I + 7 when R = I (factors within [e^-80, e^80] wherever the result is
+  // kept).  The halves' decays are sums of this thread's own g: rows 16 I ..
+  // 16 I + 7 and 16 I + 8 .. 16 I + 15 each lie inside one thread's rows.
+  bool wide = false;
+#pragma unroll
+  for (int j = 0; j < RPP; ++j) {
+    const int b = r0p + j;
+    if ((b & 7) == 7) {
+      const int a = (b & 15) == 7 ? b - 7 : b - 8;  // the span's first row, or the row before it
+      const float2 ga = a - r0p >= 0 ? G[a - r0p] : make_float2(0.f, 0.f);
+      wide |= G[j].x - ga.x < kFastDecayBound || G[j].y - ga.y < kFastDecayBound;
+    }
+  }
+  if (__syncthreads_or(wide) == 0) {
+    k1_blocked_ap<T, D>(khat, qhat, stage, sA, s_beta, wP, G, offx, offy);
+    return;
+  }
   // this thread's tile
   int rb = 0;
   while ((rb + 1) * (rb + 2) / 2 <= tid) ++rb;

@@ -95,6 +95,23 @@ def test_prefill_extreme_gates_exact_path():
     _check(inp, torch.bfloat16, label="extreme gates bf16")
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 64), (torch.float32, 128)],
+                         ids=["bf16-d128", "bf16-d64", "f32-d64", "f32-d128"])
+def test_prefill_gates_beyond_the_mid_reference(dtype, d):
+    """Chunks beyond the mid reference's range.  Constant g = -6 per token:
+    every 32-token half decays by 192 (beyond the mid reference) while every
+    8-token span decays by 48, so A and P come from the block-pair products
+    on MFMA; then the same with one token at g = -100 in chunk 2 (an 8-token
+    span beyond 80: that chunk takes the per-entry path) and a ragged tail,
+    two sequences and a nonzero initial state."""
+    inp = _inputs(2, 200, 3, d, dtype, seed=31)
+    inp["g"] = torch.full_like(inp["g"], -6.0)
+    _check(inp, dtype, label="g = -6 everywhere")
+    inp["g"][:, 150] = -100.0
+    _check(inp, dtype, label="g = -6, one token at -100")
+
+
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)],
                          ids=["bf16-d128", "f32-d64"])
 def test_prefill_strong_gates_mid_reference(dtype, d):
