@@ -1745,7 +1745,7 @@ __global__ __launch_bounds__((BwdLds<T, D>::NT), 1) void kda_bwd_intra(
 // sums over the chunk rows carry a factor e^(G_rc - G_ic) per (r, i, c).
 // No MFMA and one chunk per workgroup: only for chunks the fast kernels
 // cannot represent.
-constexpr int kExactThreads = 512;
+constexpr int kExactThreads = 256;
 constexpr int kExactMaxGroups = 256;  // one per CU (132 KB of LDS each)
 template <int D>
 struct ExScr {
