@@ -653,11 +653,14 @@ def _events():
 
 
 def device_warm_up(seconds: float = 0.2):
-    """Bring the GPU to steady clocks: plain 1 GiB device-to-device copies,
-    back to back, for `seconds` of wall time, none of the benchmarked kernels.
-    From idle, the first calls run at lower clocks: the 8K prefill timed after
-    5 warm-up calls measured ~13 % slower than after 50, and within ~3 % of
-    the latter with this load (and the code object loaded) just before the 5."""
+    """Bring the GPU to steady clocks with none of the benchmarked kernels:
+    plain 1 GiB device-to-device copies back to back for `seconds` of wall
+    time, then bf16 8192 x 8192 matrix products (torch) for as long.  From
+    idle, the first calls run at lower clocks: the 8K prefill timed after 5
+    warm-up calls measured ~13 % slower than after 50 with no load before
+    them, 234-239 us per call after the copies alone and 229 us (twice, one
+    process each) after copies and products, against ~228 us after 50
+    warm-up calls."""
     src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     dst = torch.empty_like(src)
     t0 = time.perf_counter()
@@ -666,6 +669,14 @@ def device_warm_up(seconds: float = 0.2):
             dst.copy_(src)
         torch.cuda.synchronize()
     del src, dst
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn_like(a)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            c = a @ b
+        torch.cuda.synchronize()
+    del a, b, c
 
 
 def bench_prefill(steps: int, warmup: int):
