@@ -51,9 +51,12 @@
 // 31 (the mid reference, in the same code): every factor that matters then
 // stays within [e^-80, e^80] as long as each half of the chunk decays by at
 // most 80 (gamma down to about -160), and A and P are the same MFMA products
-// of other operand values.  Beyond even that, an exact path forms each
-// e^(G_r - G_i) <= 1 from its own difference (k1_exact_ap; slow, but never
-// overflows).
+// of other operand values.  Beyond even that, each 16-row block pair of A
+// and P takes its own reference (k1_blocked_ap, still on MFMA: the last row
+// of the column block when the blocks differ, so both factors are <= 1 for
+// any gate; row 7 of a diagonal block, while each 8-row half of it decays by
+// at most 80), and past that an exact path forms each e^(G_r - G_i) <= 1
+// from its own difference (k1_exact_ap; slow, but never overflows).
 //
 // Precision.  MFMA operands are the input dtype (bf16 or fp32); MFMA
 // accumulation, the state, T, G and gamma are fp32.

@@ -44,7 +44,9 @@
 //   2. kda_bwd_state_pass, one workgroup per (sequence, head, 16 columns of
 //      d_v), sequential over the sequence's chunks from the last: dS' of every
 //      chunk to the workspace, dS of the first to d_init_state;
-//   3. kda_bwd_intra, one workgroup per (chunk, head): every gradient above.
+//   3. kda_bwd_intra, one workgroup per (chunk, head): every gradient above;
+//   4. kda_bwd_exact, a persistent grid: the gradients of the chunks prep
+//      flagged as beyond the mid reference's exponent range (none, usually).
 // The intra-chunk kernel recomputes the chunk's operands (norms, G, A, P)
 // rather than store them; T it loads.
 //
@@ -60,10 +62,11 @@
 // e^(G_r - m) e^(m - G_i) around a per-channel reference m, as the forward
 // does: the chunk start while every channel's chunk decay gamma >= -80, else
 // G of row 31 while each half of the chunk decays by at most 80 (gamma down to
-// about -160; see BwdMode).  A chunk beyond that gets NaN gradients, and its
-// NaN state gradient reaches every chunk before it (all but dq); the caller's
-// range flag (when given) is set.  Its A (and so the forward states after it)
-// is still formed exactly, by kda_bwd_prep.  fp32 operands at d = 128 do not
+// about -160; see BwdMode).  For a chunk beyond that, kda_bwd_prep forms A
+// and P exactly (so the forward states after it and its reverse-pass record
+// hold) and flags it, kda_bwd_intra leaves its gradients to kda_bwd_exact,
+// which forms every gate factor from its own exponent difference, and the
+// caller's range flag (when given) is set.  fp32 operands at d = 128 do not
 // fit one workgroup's LDS and are not supported.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -399,8 +402,8 @@ struct BwdRegs {
 // m = G of row 31 per channel while each half of the chunk decays by at most
 // 80 (the products then take K^ o e^(G-m), K^ o e^(m-G), Q^ o e^(G-m), whose
 // factors stay within [e^-80, e^80] wherever they matter, and the per-element
-// gate factors become e^(G-m) and e^(m-G)).  Beyond that the gradients of the
-// chunk are NaN.
+// gate factors become e^(G-m) and e^(m-G)).  Beyond that the chunk's
+// gradients come from kda_bwd_exact.
 enum BwdMode { kBwdFast = 0, kBwdMid = 1, kBwdBeyond = 2 };
 // G of row 31 of this lane's column (the lanes of lane group 3 hold it)
 __device__ __forceinline__ float g_row31(const BwdRegs& R, int lane) {
